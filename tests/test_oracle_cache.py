@@ -1,0 +1,107 @@
+"""Pins for the oracle's refinement cache (CPU only).
+
+Reuse across decode steps follows the rag-lover.com StrataFlux summary's
+explainer dialogue; the miss fallback its limitations section.  Pins: a hand trace
+with known outcome, and a second, independently structured LRU (slot array with
+stamps, linear scan) on random traces.
+"""
+import numpy as np
+import pytest
+
+from oracle.cache import LRUPool
+
+
+def test_hand_trace():
+    p = LRUPool(3)
+    assert p.lookup([5, 2, 9], 0) == [False, False, False]
+    assert p.fill(0) == [5, 2, 9]
+    assert p.lookup([2, 7], 1) == [True, False]
+    # victim among last_use < 1: units 5 and 9 (last used at 0) -> smallest id 5
+    assert p.fill(1) == [7]
+    assert p.resident() == {2, 7, 9}
+    assert p.lookup([9, 2, 7, 4, 1], 2) == [True, True, True, False, False]
+    # every resident unit used at step 2: misses dropped
+    assert p.fill(2) == []
+    assert p.resident() == {2, 7, 9}
+    assert p.lookup([4], 3) == [False]
+    # oldest: 9, 2, 7 all used at 2 -> smallest id 2
+    assert p.fill(3) == [4]
+    assert p.resident() == {4, 7, 9}
+
+
+def test_capacity_zero_and_cap():
+    p = LRUPool(0)
+    p.lookup([1, 2], 0)
+    assert p.fill(0) == [] and p.resident() == set()
+    p = LRUPool(10)
+    p.lookup([3, 1, 2, 3], 0)
+    assert p.fill(0, max_fill=2) == [3, 1]
+    assert p.lookup([2], 1) == [False]
+
+
+class SlotLRU:
+    """Independent model: fixed slot array of [unit, stamp], linear scans."""
+
+    def __init__(self, cap):
+        self.slots = [None] * cap
+        self.queue = []
+
+    def lookup(self, units, t):
+        res = []
+        for u in units:
+            idx = [i for i, s in enumerate(self.slots) if s is not None and s[0] == u]
+            if idx:
+                self.slots[idx[0]][1] = t
+                res.append(True)
+            else:
+                if u not in self.queue:
+                    self.queue.append(u)
+                res.append(False)
+        return res
+
+    def fill(self, t, cap=None):
+        q = self.queue if cap is None else self.queue[:cap]
+        self.queue = []
+        for u in q:
+            free = [i for i, s in enumerate(self.slots) if s is None]
+            if free:
+                self.slots[free[0]] = [u, t]
+                continue
+            cands = [(s[1], s[0], i) for i, s in enumerate(self.slots) if s[1] < t]
+            if cands:
+                _, _, i = min(cands)
+                self.slots[i] = [u, t]
+
+    def resident(self):
+        return {s[0] for s in self.slots if s is not None}
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_matches_slot_model(seed):
+    g = np.random.default_rng(seed)
+    cap = int(g.integers(0, 12))
+    a, b = LRUPool(cap), SlotLRU(cap)
+    for t in range(40):
+        for _ in range(int(g.integers(1, 3))):
+            units = g.integers(0, 25, size=int(g.integers(0, 9))).tolist()
+            assert a.lookup(units, t) == b.lookup(units, t)
+        c = None if g.random() < 0.5 else int(g.integers(0, 5))
+        a.fill(t, c)
+        b.fill(t, c)
+        assert a.resident() == b.resident()
+
+
+def test_warm_full_capacity_all_hits():
+    p = LRUPool(100)
+    g = np.random.default_rng(3)
+    seen = set()
+    for t in range(6):
+        sel = g.choice(100, 20, replace=False).tolist()
+        hits = p.lookup(sel, t)
+        # with room for every unit, exactly the units seen at earlier steps hit
+        assert hits == [u in seen for u in sel]
+        p.fill(t)
+        seen |= set(sel)
+    p.lookup(list(range(100)), 6)
+    p.fill(6)
+    assert all(p.lookup(list(range(100)), 7))
