@@ -1,0 +1,451 @@
+"""ctypes binding of libstrataflux.so (C ABI in include/strataflux.h).
+
+Argument marshalling only: every step of the decode path runs in the library's HIP
+kernels.  PyTorch provides device memory, pinned host memory and streams.  If the
+library has not been built, ``lib()`` raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstrataflux.so")
+_lib = None
+_lock = threading.Lock()
+
+SF_REFINE_CHANNEL_MAJOR = 0
+SF_REFINE_ROW_MAJOR = 1
+SF_CACHE_DETERMINISTIC = 0
+SF_CACHE_ASYNC = 1
+
+
+class SFError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"strataflux status {status}: {msg}")
+        self.status = status
+
+
+class sf_qfmt(C.Structure):
+    _fields_ = [("b", C.c_int32), ("r", C.c_int32), ("group", C.c_int32)]
+
+
+class sf_qweight(C.Structure):
+    _fields_ = [
+        ("resident", C.c_void_p),
+        ("sz", C.c_void_p),
+        ("n_out", C.c_int64),
+        ("k_in", C.c_int64),
+        ("fmt", sf_qfmt),
+    ]
+
+
+class sf_qkv(C.Structure):
+    _fields_ = [
+        ("k_res", C.c_void_p),
+        ("k_sz", C.c_void_p),
+        ("v_res", C.c_void_p),
+        ("v_sz", C.c_void_p),
+        ("batch", C.c_int32),
+        ("n_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32),
+        ("t_len", C.c_int32),
+        ("t_cap", C.c_int32),
+        ("fmt", sf_qfmt),
+    ]
+
+
+class sf_pool_desc(C.Structure):
+    _fields_ = [
+        ("unit_bytes", C.c_int64),
+        ("n_units", C.c_int64),
+        ("capacity", C.c_int64),
+        ("host_store", C.c_void_p),
+        ("device_store", C.c_void_p),
+        ("max_lookup", C.c_int32),
+    ]
+
+
+class sf_gemv_op(C.Structure):
+    _fields_ = [
+        ("w", sf_qweight),
+        ("pool", C.c_int32),
+        ("y", C.c_void_p),
+        ("hit_out", C.c_void_p),
+    ]
+
+
+VP, I32, I64, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_PROTOS = {
+    "sf_abi_version": (I32, []),
+    "sf_status_string": (C.c_char_p, [I32]),
+    "sf_last_error": (C.c_char_p, []),
+    "sf_workspace_create": (I32, [SZ, C.POINTER(VP)]),
+    "sf_workspace_destroy": (I32, [VP]),
+    "sf_workspace_bytes_gemv": (SZ, [I32, I64, I32]),
+    "sf_workspace_bytes_attn": (SZ, [I32, I32, I32, I32, I32]),
+    "sf_workspace_check": (I32, [VP]),
+    "sf_quantize_nested": (I32, [VP, I64, I64, sf_qfmt, I32, VP, VP, VP, VP]),
+    "sf_debug_dequantize": (I32, [VP, VP, VP, I64, I64, sf_qfmt, I32, I32, VP, VP]),
+    "sf_kv_append": (I32, [VP, VP, I32, I32, C.POINTER(sf_qkv), VP, VP]),
+    "sf_refine_cache_create": (I32, [C.POINTER(sf_pool_desc), I32, I32, I32, C.POINTER(VP)]),
+    "sf_refine_cache_destroy": (I32, [VP]),
+    "sf_refine_cache_lookup": (I32, [VP, I32, VP, I32, VP, VP]),
+    "sf_refine_cache_fill": (I32, [VP, VP, VP, C.POINTER(I64)]),
+    "sf_refine_cache_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(I64), C.POINTER(I64)]),
+    "sf_refine_cache_resident": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64)]),
+    "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
+    "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
+}
+EXPORTS = tuple(_PROTOS)
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+                    "(there is no CPU fallback)"
+                )
+            L = C.CDLL(LIB_PATH)
+            for name, (res, args) in _PROTOS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+        return _lib
+
+
+def reload():
+    global _lib
+    with _lock:
+        _lib = None
+    return lib()
+
+
+def check(status):
+    if status != 0:
+        L = lib()
+        raise SFError(status, f"{L.sf_status_string(status).decode()}: {L.sf_last_error().decode()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def _dev_tensor(a, dtype, device):
+    torch = _torch()
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
+
+
+def _f16_bits(a, device):
+    """fp16 values (numpy or torch) -> device int16 tensor holding the bit patterns."""
+    torch = _torch()
+    t = _dev_tensor(a, torch.float16, device)
+    return t.view(torch.int16)
+
+
+# ---- workspace ------------------------------------------------------------------
+class Workspace:
+    def __init__(self, nbytes):
+        h = C.c_void_p()
+        check(lib().sf_workspace_create(int(nbytes), C.byref(h)))
+        self.handle = h
+        self.nbytes = int(nbytes)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.sf_workspace_destroy(self.handle)
+            self.handle = None
+
+    def check(self):
+        check(lib().sf_workspace_check(self.handle))
+
+
+_ws = {}
+
+
+def workspace(nbytes, device=None):
+    """A per-device workspace at least ``nbytes`` large (grown on demand)."""
+    torch = _torch()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    w = _ws.get(dev.index)
+    if w is None or w.nbytes < nbytes:
+        torch.cuda.synchronize(dev)
+        with torch.cuda.device(dev):
+            w = Workspace(max(nbytes, 1 << 20))
+        _ws[dev.index] = w
+    return w
+
+
+# ---- nested weights ---------------------------------------------------------------
+class QuantWeight:
+    """A nested-quantised weight [n_out][k_in] on the device."""
+
+    def __init__(self, resident, sz, refine, n_out, k_in, b, r):
+        self.resident, self.sz, self.refine = resident, sz, refine
+        self.n_out, self.k_in, self.b, self.r = n_out, k_in, b, r
+
+    @classmethod
+    def from_device(cls, W, b, r, stream=None):
+        torch = _torch()
+        W = W.contiguous().to(torch.float32)
+        n, k = W.shape
+        dev = W.device
+        res = torch.empty((n, k * b // 8), dtype=torch.uint8, device=dev)
+        sz = torch.empty((n, k // 128), dtype=torch.int32, device=dev)
+        ref = torch.empty((k, n * r // 8), dtype=torch.uint8, device=dev) if r > 0 else None
+        check(
+            lib().sf_quantize_nested(
+                _ptr(W), n, k, sf_qfmt(b, r, 128), SF_REFINE_CHANNEL_MAJOR, _ptr(res), _ptr(sz), _ptr(ref),
+                _stream(stream),
+            )
+        )
+        return cls(res, sz, ref, n, k, b, r)
+
+    @classmethod
+    def from_host(cls, W, b, r, device="cuda"):
+        return cls.from_device(_dev_tensor(W, _torch().float32, device), b, r)
+
+    def desc(self):
+        return sf_qweight(self.resident.data_ptr(), self.sz.data_ptr(), self.n_out, self.k_in, sf_qfmt(self.b, self.r, 128))
+
+    @property
+    def unit_bytes(self):
+        return self.n_out * self.r // 8
+
+    def resident_pool_desc(self, max_lookup=0):
+        """A pool holding every refinement unit of this matrix on the device."""
+        return sf_pool_desc(self.unit_bytes, self.k_in, self.k_in, None, self.refine.data_ptr(), max_lookup)
+
+    def host_store(self):
+        """Pinned host copy of the refinement units [k_in][unit_bytes]."""
+        return self.refine.to("cpu").pin_memory()
+
+    def dequantize(self, which, stream=None):
+        torch = _torch()
+        out = torch.empty((self.n_out, self.k_in), dtype=torch.float32, device=self.resident.device)
+        check(
+            lib().sf_debug_dequantize(
+                _ptr(self.resident), _ptr(self.sz), _ptr(self.refine), self.n_out, self.k_in,
+                sf_qfmt(self.b, self.r, 128), SF_REFINE_CHANNEL_MAJOR, which, _ptr(out), _stream(stream),
+            )
+        )
+        return out
+
+
+def quantize_rows(X, b, r, device="cuda", stream=None):
+    """Row-major nested quantisation of X [rows][cols]: (resident, sz, refine) device tensors."""
+    torch = _torch()
+    X = _dev_tensor(X, torch.float32, device)
+    n, k = X.shape
+    res = torch.empty((n, k * b // 8), dtype=torch.uint8, device=X.device)
+    sz = torch.empty((n, k // 128), dtype=torch.int32, device=X.device)
+    ref = torch.empty((n, k * r // 8), dtype=torch.uint8, device=X.device) if r > 0 else None
+    check(
+        lib().sf_quantize_nested(
+            _ptr(X), n, k, sf_qfmt(b, r, 128), SF_REFINE_ROW_MAJOR, _ptr(res), _ptr(sz), _ptr(ref), _stream(stream)
+        )
+    )
+    return res, sz, ref
+
+
+def dequantize_rows(res, sz, ref, rows, cols, b, r, which, stream=None):
+    torch = _torch()
+    out = torch.empty((rows, cols), dtype=torch.float32, device=res.device)
+    check(
+        lib().sf_debug_dequantize(
+            _ptr(res), _ptr(sz), _ptr(ref), rows, cols, sf_qfmt(b, r, 128), SF_REFINE_ROW_MAJOR, which,
+            _ptr(out), _stream(stream),
+        )
+    )
+    return out
+
+
+# ---- nested KV cache ---------------------------------------------------------------
+class QuantKV:
+    """Nested-quantised KV cache [batch][n_kv][t_cap][head_dim] on the device, plus a
+    device copy of every token's refinement unit (unit id (b*n_kv + h)*t_cap + t)."""
+
+    def __init__(self, batch, n_kv, t_cap, b, r, device="cuda", head_dim=128):
+        torch = _torch()
+        self.batch, self.n_kv, self.t_cap, self.b, self.r, self.d = batch, n_kv, t_cap, b, r, head_dim
+        self.t_len = 0
+        dev = torch.device(device)
+        self.k_res = torch.zeros((batch, n_kv, t_cap, head_dim * b // 8), dtype=torch.uint8, device=dev)
+        self.v_res = torch.zeros_like(self.k_res)
+        self.k_sz = torch.zeros((batch, n_kv, t_cap), dtype=torch.int32, device=dev)
+        self.v_sz = torch.zeros_like(self.k_sz)
+        self.refine = torch.zeros((batch, n_kv, t_cap, self.unit_bytes), dtype=torch.uint8, device=dev)
+
+    @property
+    def unit_bytes(self):
+        return 2 * self.d * self.r // 8
+
+    @property
+    def n_units(self):
+        return self.batch * self.n_kv * self.t_cap
+
+    def desc(self, t_len=None):
+        return sf_qkv(
+            self.k_res.data_ptr(), self.k_sz.data_ptr(), self.v_res.data_ptr(), self.v_sz.data_ptr(),
+            self.batch, self.n_kv, self.d, self.t_len if t_len is None else t_len, self.t_cap,
+            sf_qfmt(self.b, self.r, 128),
+        )
+
+    def append(self, K_new, V_new, stream=None):
+        """Quantise n_tok new tokens (fp32 [batch][n_kv][n_tok][d]) at t_len.."""
+        torch = _torch()
+        dev = self.k_res.device
+        K_new = _dev_tensor(K_new, torch.float32, dev)
+        V_new = _dev_tensor(V_new, torch.float32, dev)
+        n_tok = K_new.shape[2]
+        staged = torch.empty((self.batch, self.n_kv, n_tok, self.unit_bytes), dtype=torch.uint8, device=dev)
+        d = self.desc()
+        check(lib().sf_kv_append(_ptr(K_new), _ptr(V_new), n_tok, self.t_len, C.byref(d), _ptr(staged), _stream(stream)))
+        self.refine[:, :, self.t_len : self.t_len + n_tok] = staged
+        self.t_len += n_tok
+        return staged
+
+    @classmethod
+    def from_host(cls, K, V, b, r, device="cuda", t_cap=None):
+        batch, n_kv, T, d = K.shape
+        kv = cls(batch, n_kv, t_cap or T, b, r, device=device, head_dim=d)
+        kv.append(K, V)
+        return kv
+
+    def resident_pool_desc(self, max_lookup=0):
+        return sf_pool_desc(self.unit_bytes, self.n_units, self.n_units, None, self.refine.data_ptr(), max_lookup)
+
+    def host_store(self):
+        return self.refine.reshape(self.n_units, self.unit_bytes).to("cpu").pin_memory()
+
+
+# ---- refinement cache ---------------------------------------------------------------
+class RefineCache:
+    def __init__(self, pools, mode=SF_CACHE_DETERMINISTIC, max_fill=0, device=None, keep=()):
+        torch = _torch()
+        arr = (sf_pool_desc * len(pools))(*pools)
+        h = C.c_void_p()
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        with torch.cuda.device(dev):
+            check(lib().sf_refine_cache_create(arr, len(pools), mode, max_fill, C.byref(h)))
+        self.handle = h
+        self.n_pools = len(pools)
+        self._keep = list(keep)  # host stores etc. that must outlive the cache
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.sf_refine_cache_destroy(self.handle)
+            self.handle = None
+
+    def lookup(self, pool, ids, stream=None):
+        torch = _torch()
+        ids = ids.to(torch.int32).contiguous()
+        out = torch.empty_like(ids)
+        check(lib().sf_refine_cache_lookup(self.handle, pool, _ptr(ids), ids.numel(), _ptr(out), _stream(stream)))
+        return out
+
+    def fill(self, stream=None, side=None):
+        torch = _torch()
+        if side is None:
+            side = getattr(self, "_side", None)
+            if side is None:
+                side = self._side = torch.cuda.Stream()
+        n = C.c_int64(0)
+        check(lib().sf_refine_cache_fill(self.handle, _stream(stream), _stream(side), C.byref(n)))
+        return n.value
+
+    def stats(self, pool=-1):
+        v = [C.c_int64(0) for _ in range(4)]
+        check(lib().sf_refine_cache_stats(self.handle, pool, *[C.byref(x) for x in v]))
+        return dict(zip(("lookups", "hits", "installed", "h2d_bytes"), [x.value for x in v]))
+
+    def resident(self, pool, capacity):
+        ids = (C.c_int64 * max(1, capacity))()
+        n = C.c_int64(0)
+        check(lib().sf_refine_cache_resident(self.handle, pool, ids, C.byref(n)))
+        return set(ids[i] for i in range(n.value))
+
+
+def host_pool_desc(host_store, capacity, max_lookup=0):
+    """Pool over a pinned host store tensor [n_units][unit_bytes] with `capacity` slots."""
+    n, ub = host_store.shape
+    return sf_pool_desc(ub, n, capacity, host_store.data_ptr(), None, max_lookup)
+
+
+# ---- refined GEMV -------------------------------------------------------------------
+def refined_gemv(ops, x, k_sel, cache=None, sel_in=None, stream=None, ys=None, want_hits=True):
+    """ops: list of (QuantWeight, pool index or -1); x fp16 [batch][k_in].
+    Returns (list of y [batch][n_out] fp32, sel int32 [k_sel], list of hit tensors)."""
+    torch = _torch()
+    w0 = ops[0][0]
+    dev = w0.resident.device
+    xb = _f16_bits(x, dev)
+    if xb.dim() == 1:
+        xb = xb[None]
+    batch = xb.shape[0]
+    n = len(ops)
+    arr = (sf_gemv_op * n)()
+    outs, hits = [], []
+    for i, (w, pool) in enumerate(ops):
+        y = ys[i] if ys is not None else torch.empty((batch, w.n_out), dtype=torch.float32, device=dev)
+        h = torch.empty(max(1, k_sel), dtype=torch.int32, device=dev) if want_hits else None
+        arr[i] = sf_gemv_op(w.desc(), pool if cache is not None else -1, y.data_ptr(), h.data_ptr() if h is not None else None)
+        outs.append(y)
+        hits.append(h[:k_sel] if h is not None else None)
+    sel = torch.empty(max(1, k_sel), dtype=torch.int32, device=dev)
+    sin = _dev_tensor(sel_in, torch.int32, dev) if sel_in is not None else None
+    ws = workspace(lib().sf_workspace_bytes_gemv(n, w0.k_in, k_sel), dev)
+    check(
+        lib().sf_refined_gemv(
+            arr, n, _ptr(xb), batch, k_sel, _ptr(sin), _ptr(sel), cache.handle if cache else None, ws.handle,
+            _stream(stream),
+        )
+    )
+    return outs, sel[:k_sel], hits
+
+
+# ---- refined attention ----------------------------------------------------------------
+def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stream=None, out=None, t_len=None):
+    """q fp16 [batch][n_q][d].  Returns (out fp32 [batch][n_q][d], sel [batch][n_kv][k_sel],
+    hits [batch][n_kv][k_sel])."""
+    torch = _torch()
+    dev = kv.k_res.device
+    qb = _f16_bits(q, dev)
+    batch, n_q, d = qb.shape
+    o = out if out is not None else torch.empty((batch, n_q, d), dtype=torch.float32, device=dev)
+    ks = max(1, k_sel)
+    sel = torch.empty((batch, kv.n_kv, ks), dtype=torch.int32, device=dev)
+    hit = torch.empty((batch, kv.n_kv, ks), dtype=torch.int32, device=dev)
+    sin = _dev_tensor(sel_in, torch.int32, dev) if sel_in is not None else None
+    tl = kv.t_len if t_len is None else t_len
+    ws = workspace(lib().sf_workspace_bytes_attn(batch, n_q, kv.n_kv, tl, k_sel), dev)
+    d_ = kv.desc(tl)
+    check(
+        lib().sf_refined_attn_decode(
+            _ptr(qb), n_q, C.byref(d_), float(scale), k_sel, _ptr(sin), cache.handle if cache else None, pool,
+            _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream),
+        )
+    )
+    return o, sel[:, :, :k_sel], hit[:, :, :k_sel]

@@ -1,0 +1,283 @@
+// Nested quantisation (resident + refinement codes), KV append, and the test-only
+// dequantisation export.
+//
+// Representation: rag-lover.com StrataFlux summary, explainer dialogue (解説) --
+// the fetched refinement bits subdivide the interval between resident low-bit
+// levels.  Format fixed by this library: per group of 128 values, one (b+r)-bit
+// asymmetric uniform code; fp16 offset z = fp16(min) and step s = fp16((max-min)/Q),
+// each one round-to-nearest-even of the fp64 value; c = clamp(rint((x-z)/s), 0, Q)
+// in fp64; resident = c >> r, refinement = c & (2^r - 1); LSB-first bit streams.
+//
+// Every code decision is taken in fp64 with IEEE-exact operations (subtract,
+// divide, round-to-nearest-even), so the codes are reproducible bit for bit by any
+// IEEE fp64 implementation of the same formula.
+#include "sf_internal.h"
+
+namespace {
+
+// Correctly rounded (nearest-even) fp64 -> fp16 conversion, bit pattern result.
+// Done with integer arithmetic so there is no intermediate fp32 rounding.
+__device__ uint32_t f64_to_f16_rne(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  const int ex = (int)((u >> 52) & 0x7FF);
+  const uint64_t mant = u & 0xFFFFFFFFFFFFFull;
+  if (ex == 0x7FF) return sign | 0x7C00u | (mant ? 0x200u : 0u);
+  if (ex == 0) return sign;  // zero, or an fp64 subnormal (far below fp16's range)
+  const int e = ex - 1023;
+  if (e > 15) return sign | 0x7C00u;
+  const uint64_t m = mant | (1ull << 52);
+  // fp16 quantum is 2^(max(e,-14) - 10); m carries 2^(e - 52).
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  if (shift > 63) return sign;
+  uint64_t q = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  uint32_t bits = (e >= -14) ? (uint32_t)(((e + 14) << 10) + q) : (uint32_t)q;
+  if (bits >= 0x7C00u) bits = 0x7C00u;
+  return sign | bits;
+}
+
+__device__ __forceinline__ double h2d(uint32_t bits16) { return (double)sf_h2f(bits16); }
+
+__device__ __forceinline__ uint32_t code_of(float x, double z, double s, uint32_t s16, int Q) {
+  if ((s16 & 0x7FFFu) == 0) return 0;
+  double t = __builtin_rint(((double)x - z) / s);
+  if (t < 0.0) t = 0.0;
+  if (t > (double)Q) t = (double)Q;
+  return (uint32_t)t;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Builds stream word w (0 <= w < 4*width) of a 128-code group from codes in LDS.
+__device__ __forceinline__ uint32_t stream_word(const uint8_t* codes, int width, int w) {
+  uint32_t word = 0;
+  for (int p = 0; p < 32; ++p) {
+    const int P = 32 * w + p;
+    const int i = P / width, j = P - i * width;
+    word |= (uint32_t)((codes[i] >> j) & 1u) << p;
+  }
+  return word;
+}
+
+// One wave quantises one group of 128 fp32 values at `src`.  Writes the group's
+// 4*b resident words, its sz word, and (if ref_dst) its 4*r refinement words.
+__device__ void quantize_group_wave(const float* src, int b, int r, uint8_t* lds_hi,
+                                    uint8_t* lds_lo, uint32_t* res_dst, uint32_t* sz_dst,
+                                    uint32_t* ref_dst) {
+  const int lane = threadIdx.x & 63;
+  const float v0 = src[lane], v1 = src[lane + 64];
+  const float mn = wave_min(fminf(v0, v1));
+  const float mx = wave_max(fmaxf(v0, v1));
+  const int Q = (1 << (b + r)) - 1;
+  const uint32_t z16 = f64_to_f16_rne((double)mn);
+  const uint32_t s16 = f64_to_f16_rne(((double)mx - (double)mn) / (double)Q);
+  const double z = h2d(z16), s = h2d(s16);
+  const uint32_t c0 = code_of(v0, z, s, s16, Q), c1 = code_of(v1, z, s, s16, Q);
+  const uint32_t lo_mask = (1u << r) - 1u;
+  lds_hi[lane] = (uint8_t)(c0 >> r);
+  lds_hi[lane + 64] = (uint8_t)(c1 >> r);
+  lds_lo[lane] = (uint8_t)(c0 & lo_mask);
+  lds_lo[lane + 64] = (uint8_t)(c1 & lo_mask);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < 4 * b) res_dst[lane] = stream_word(lds_hi, b, lane);
+  if (ref_dst && r > 0 && lane >= 32 && lane - 32 < 4 * r)
+    ref_dst[lane - 32] = stream_word(lds_lo, r, lane - 32);
+  if (lane == 0) *sz_dst = s16 | (z16 << 16);
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restrict__ x,
+                                                            int64_t rows, int64_t cols, int b,
+                                                            int r, uint8_t* __restrict__ resident,
+                                                            uint32_t* __restrict__ sz,
+                                                            uint8_t* __restrict__ refine_rows) {
+  __shared__ uint8_t lds[4][256];
+  const int wave = threadIdx.x >> 6;
+  const int64_t ngr = cols / 128;
+  const int64_t gid = (int64_t)blockIdx.x * 4 + wave;
+  if (gid >= rows * ngr) return;  // whole wave leaves together
+  const int64_t row = gid / ngr, g = gid - row * ngr;
+  uint32_t* res = (uint32_t*)(resident + row * (cols * b / 8) + g * 16 * b);
+  uint32_t* ref = refine_rows ? (uint32_t*)(refine_rows + row * (cols * r / 8) + g * 16 * r) : nullptr;
+  quantize_group_wave(x + row * cols + g * 128, b, r, lds[wave], lds[wave] + 128, res,
+                      sz + row * ngr + g, ref);
+}
+
+// Channel-major refinement: unit k = refinement bits of column k over all rows.
+// One thread per (column k, 32-bit word w of unit k); the codes are recomputed from
+// x and the group's s, z with the same fp64 formula as quantize_rows_kernel.
+__global__ __launch_bounds__(256) void refine_channel_major_kernel(
+    const float* __restrict__ x, int64_t rows, int64_t cols, int b, int r,
+    const uint32_t* __restrict__ sz, uint8_t* __restrict__ refine) {
+  const int64_t words_per_unit = rows * r / 32;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t k = idx % cols, w = idx / cols;
+  if (w >= words_per_unit) return;
+  const int Q = (1 << (b + r)) - 1;
+  const int64_t ngr = cols / 128;
+  uint32_t word = 0;
+  int64_t prev_n = -1;
+  uint32_t clo = 0;
+  for (int p = 0; p < 32; ++p) {
+    const int64_t P = 32 * w + p;
+    const int64_t n = P / r;
+    const int j = (int)(P - n * r);
+    if (n != prev_n) {
+      const uint32_t szw = sz[n * ngr + k / 128];
+      const uint32_t s16 = szw & 0xFFFFu;
+      const uint32_t c = code_of(x[n * cols + k], h2d(szw >> 16), h2d(s16), s16, Q);
+      clo = c & ((1u << r) - 1u);
+      prev_n = n;
+    }
+    word |= ((clo >> j) & 1u) << p;
+  }
+  ((uint32_t*)(refine + k * (rows * r / 8)))[w] = word;
+}
+
+// KV append: one wave per (batch, head, token, K|V) group.
+__global__ __launch_bounds__(256) void kv_append_kernel(const float* __restrict__ k_new,
+                                                        const float* __restrict__ v_new,
+                                                        int batch, int n_kv, int n_tok, int t0,
+                                                        int t_cap, int b, int r,
+                                                        uint8_t* k_res, uint32_t* k_sz,
+                                                        uint8_t* v_res, uint32_t* v_sz,
+                                                        uint8_t* refine_out) {
+  __shared__ uint8_t lds[4][256];
+  const int wave = threadIdx.x >> 6;
+  const int64_t gid = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t total = (int64_t)batch * n_kv * n_tok * 2;
+  if (gid >= total) return;
+  const int which = (int)(gid & 1);  // 0 = K, 1 = V
+  const int64_t e = gid >> 1;        // (bh, tok)
+  const int64_t tok = e % n_tok, bh = e / n_tok;
+  const float* src = (which ? v_new : k_new) + e * 128;
+  const int64_t pos = bh * t_cap + t0 + tok;
+  uint8_t* res_base = which ? v_res : k_res;
+  uint32_t* sz_base = which ? v_sz : k_sz;
+  const int64_t unit_bytes = 2 * 16 * r;
+  uint32_t* ref = (refine_out && r > 0)
+                      ? (uint32_t*)(refine_out + e * unit_bytes + which * 16 * r)
+                      : nullptr;
+  quantize_group_wave(src, b, r, lds[wave], lds[wave] + 128,
+                      (uint32_t*)(res_base + pos * 16 * b), sz_base + pos, ref);
+}
+
+__device__ __forceinline__ uint32_t read_bits(const uint8_t* base, int64_t bitpos, int width) {
+  // width <= 8: the field lies in at most two consecutive bytes
+  const int64_t byte = bitpos >> 3;
+  const int off = (int)(bitpos & 7);
+  uint32_t v = base[byte];
+  if (off + width > 8) v |= (uint32_t)base[byte + 1] << 8;
+  return (v >> off) & ((1u << width) - 1u);
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ resident,
+                                                      const uint32_t* __restrict__ sz,
+                                                      const uint8_t* __restrict__ refine,
+                                                      int64_t rows, int64_t cols, int b, int r,
+                                                      int layout, int which,
+                                                      float* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * cols) return;
+  const int64_t n = idx / cols, k = idx - n * cols;
+  const uint32_t hi = read_bits(resident + n * (cols * b / 8), k * b, b);
+  const uint32_t szw = sz[n * (cols / 128) + k / 128];
+  const float s = sf_h2f(szw), z = sf_h2f(szw >> 16);
+  float v;
+  if (which == 0) {
+    v = fmaf(s * (float)(1u << r), (float)hi, z);
+  } else {
+    uint32_t lo = 0;
+    if (r > 0) {
+      if (layout == SF_REFINE_CHANNEL_MAJOR)
+        lo = read_bits(refine + k * (rows * r / 8), n * r, r);
+      else
+        lo = read_bits(refine + n * (cols * r / 8), k * r, r);
+    }
+    v = fmaf(s, (float)((hi << r) | lo), z);
+  }
+  out[idx] = v;
+}
+
+bool fmt_ok(const sf_qfmt& f) {
+  return f.b >= 1 && f.r >= 0 && f.b + f.r <= 8 && f.group == 128;
+}
+
+}  // namespace
+
+extern "C" sf_status sf_quantize_nested(const float* x, int64_t rows, int64_t cols, sf_qfmt fmt,
+                                        int32_t refine_layout, uint8_t* resident, uint32_t* sz,
+                                        uint8_t* refine, sf_stream stream) {
+  SF_REQUIRE(fmt_ok(fmt), SF_EUNSUPPORTED, "need 1<=b, 0<=r, b+r<=8, group 128");
+  SF_REQUIRE(x && resident && sz, SF_EINVAL, "null tensor");
+  SF_REQUIRE(rows > 0 && cols > 0 && cols % 128 == 0, SF_EINVAL, "cols must be a positive multiple of 128");
+  SF_REQUIRE(refine_layout == SF_REFINE_CHANNEL_MAJOR || refine_layout == SF_REFINE_ROW_MAJOR,
+             SF_EINVAL, "bad refine_layout");
+  const bool want_ref = refine != nullptr && fmt.r > 0;
+  if (want_ref && refine_layout == SF_REFINE_CHANNEL_MAJOR)
+    SF_REQUIRE((rows * fmt.r) % 32 == 0, SF_EINVAL, "channel-major refinement needs rows*r % 32 == 0");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t groups = rows * (cols / 128);
+  const int64_t blocks = (groups + 3) / 4;
+  uint8_t* row_ref = (want_ref && refine_layout == SF_REFINE_ROW_MAJOR) ? refine : nullptr;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols,
+                     fmt.b, fmt.r, resident, sz, row_ref);
+  SF_LAUNCH_CHECK();
+  if (want_ref && refine_layout == SF_REFINE_CHANNEL_MAJOR) {
+    const int64_t threads = cols * (rows * fmt.r / 32);
+    hipLaunchKernelGGL(refine_channel_major_kernel, dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, x, rows, cols, fmt.b, fmt.r, (const uint32_t*)sz, refine);
+    SF_LAUNCH_CHECK();
+  }
+  return SF_OK;
+}
+
+extern "C" sf_status sf_debug_dequantize(const uint8_t* resident, const uint32_t* sz,
+                                         const uint8_t* refine, int64_t rows, int64_t cols,
+                                         sf_qfmt fmt, int32_t refine_layout, int32_t which,
+                                         float* out, sf_stream stream) {
+  SF_REQUIRE(fmt_ok(fmt), SF_EUNSUPPORTED, "bad format");
+  SF_REQUIRE(resident && sz && out, SF_EINVAL, "null tensor");
+  SF_REQUIRE(rows > 0 && cols > 0 && cols % 128 == 0, SF_EINVAL, "bad shape");
+  SF_REQUIRE(which == 0 || which == 1, SF_EINVAL, "which must be 0 or 1");
+  SF_REQUIRE(which == 0 || fmt.r == 0 || refine, SF_EINVAL, "full value needs refine");
+  const int64_t n = rows * cols;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, resident, sz, refine, rows, cols, fmt.b, fmt.r,
+                     refine_layout, which, out);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok,
+                                  int32_t t0, const sf_qkv* kv, uint8_t* refine_out,
+                                  sf_stream stream) {
+  SF_REQUIRE(kv && k_new && v_new, SF_EINVAL, "null argument");
+  SF_REQUIRE(fmt_ok(kv->fmt), SF_EUNSUPPORTED, "bad format");
+  SF_REQUIRE(kv->head_dim == 128, SF_EUNSUPPORTED, "head_dim must be 128");
+  SF_REQUIRE(kv->k_res && kv->k_sz && kv->v_res && kv->v_sz, SF_EINVAL, "null cache tensor");
+  SF_REQUIRE(n_tok >= 0 && t0 >= 0 && (int64_t)t0 + n_tok <= kv->t_cap, SF_EINVAL,
+             "positions beyond t_cap");
+  SF_REQUIRE(kv->batch > 0 && kv->n_kv_heads > 0, SF_EINVAL, "bad shape");
+  if (n_tok == 0) return SF_OK;
+  const int64_t waves = (int64_t)kv->batch * kv->n_kv_heads * n_tok * 2;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)stream, k_new, v_new, kv->batch, kv->n_kv_heads, n_tok, t0,
+                     kv->t_cap, kv->fmt.b, kv->fmt.r, kv->k_res, kv->k_sz, kv->v_res, kv->v_sz,
+                     refine_out);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}

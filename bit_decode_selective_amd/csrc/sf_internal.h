@@ -1,0 +1,81 @@
+// Internal declarations shared by the libstrataflux sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/strataflux.h"
+
+// ---- error reporting -------------------------------------------------------------
+void sf_set_error(const std::string& msg);
+
+#define SF_REQUIRE(cond, code, msg)            \
+  do {                                         \
+    if (!(cond)) {                             \
+      sf_set_error(std::string(__func__) + ": " + (msg)); \
+      return (code);                           \
+    }                                          \
+  } while (0)
+
+#define SF_HIP(call)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      sf_set_error(std::string(__func__) + ": " #call ": " + hipGetErrorString(e_)); \
+      return SF_EHIP;                                                             \
+    }                                                                             \
+  } while (0)
+
+#define SF_LAUNCH_CHECK() SF_HIP(hipGetLastError())
+
+// ---- workspace -------------------------------------------------------------------
+// Control words at the start of every workspace (device memory).
+struct WsControl {
+  uint32_t sel_state;  // 0 idle, 1 selection in progress, 2 published
+  uint32_t done;       // workgroups finished (last one resets the words)
+  uint32_t timeout;    // set when a bounded device wait gave up
+  uint32_t pad[61];    // keeps the data area 256-byte aligned
+};
+
+struct sf_workspace {
+  uint8_t* base = nullptr;  // device
+  size_t bytes = 0;
+  int device = 0;
+};
+
+// ---- cache (device view used by kernels) ------------------------------------------
+struct PoolDev {
+  const int32_t* unit2slot;  // [n_units], -1 = absent
+  const uint8_t* slots;      // [capacity][unit_bytes]
+  int32_t* log_units;        // lookup log: unit ids, in lookup order
+  int32_t* log_slots;        // slot seen by each logged lookup (-1 = miss)
+  uint32_t* log_count;       // entries used this step
+  int32_t log_cap;           // entries available
+  int32_t unit_bytes;
+  int64_t n_units;
+};
+
+// Returns the device view of a pool, or a pool that misses everything if c is
+// NULL or pool < 0.  Fails with SF_EINVAL for a bad pool index.
+sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out);
+
+// ---- fp16 helpers ------------------------------------------------------------------
+__device__ __forceinline__ float sf_h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
+}
+
+// Bounded spin on a device word written by another workgroup of the same launch.
+// Returns false if it gave up.
+__device__ __forceinline__ bool sf_wait_word(uint32_t* p, uint32_t want, uint32_t* timeout_flag) {
+  for (uint32_t it = 0; it < (1u << 24); ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+static inline size_t sf_align256(size_t v) { return (v + 255) & ~size_t(255); }

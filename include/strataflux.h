@@ -1,0 +1,241 @@
+/*
+ * strataflux.h -- C ABI of libstrataflux.so: the refined low-bit decode step on
+ * AMD MI355X (gfx950).
+ *
+ * What is computed (the method, per the pages gathered about StrataFlux):
+ *   - rag-lover.com StrataFlux summary, explainer dialogue (解説): weights and the
+ *     KV cache stay on the GPU in low-bit form; extra precision is fetched from
+ *     host memory as a few additional bits that subdivide the interval between
+ *     resident low-bit levels ("nested refinement"), not as a full FP16 copy;
+ *     weight refinements are chosen by input-activation magnitude, KV refinements
+ *     by the attention weight computed from the low-bit keys; fetched precision
+ *     is cached on the GPU and reused across decode steps.
+ *   - the same page, limitations section (限界と未検証の範囲): on a cache miss the
+ *     value stays at its resident low-bit precision.
+ *   - "StrataFlux: Memory-Hierarchy-Native Low-Bit LLM Inference" (arXiv
+ *     2611.08363), abstract: only selected precision is streamed, delivery
+ *     overlaps computation, and fetched precision is reused across steps.
+ *
+ * Number format (the pages leave it open; this library fixes it):
+ *   per group of 128 consecutive values, an asymmetric uniform code of B = b + r
+ *   bits: z = fp16(min), s = fp16((max - min) / (2^B - 1)) (one round-to-nearest-
+ *   even of the fp64 quotient), c = clamp(rint((x - z) / s), 0, 2^B - 1) in fp64,
+ *   c = 0 for a group whose s is 0.  The resident code is c >> r, dequantised as
+ *   z + (s * 2^r) * (c >> r); the refinement code is c & (2^r - 1), and with it the
+ *   value is z + s * c.  Codes are packed as LSB-first little-endian bit streams.
+ *   The per-group parameters are stored as one 32-bit word per group:
+ *   bits 0..15 = s (fp16), bits 16..31 = z (fp16).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller (allocated by the
+ *     caller, e.g. with PyTorch), unless the argument says "host".  The library
+ *     never frees caller memory.  Library objects (sf_refine_cache, sf_workspace)
+ *     are opaque handles with create/destroy.
+ *   - Calls are stream-ordered: they enqueue work on the given HIP stream
+ *     (sf_stream = hipStream_t, NULL = the default stream) and return.
+ *   - Calls that take a workspace or a cache allocate no memory; only the
+ *     *_create calls allocate.  A workspace must not be used by two calls that
+ *     can run at the same time (one stream at a time).
+ *   - Errors: argument and shape checks are synchronous and return SF_EINVAL /
+ *     SF_EUNSUPPORTED / SF_ENOMEM; a failed HIP call returns SF_EHIP.  Details
+ *     are in sf_last_error() (per thread).  Device-side faults surface at the
+ *     caller's next synchronisation.  A refinement miss is not an error.
+ */
+#ifndef STRATAFLUX_H
+#define STRATAFLUX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SF_ABI_VERSION 1
+
+typedef int32_t sf_status;
+#define SF_OK 0
+#define SF_EINVAL 1
+#define SF_EUNSUPPORTED 2
+#define SF_ENOMEM 3
+#define SF_EHIP 4
+#define SF_ESTATE 5
+
+typedef void* sf_stream; /* hipStream_t */
+
+/* b resident bits, r refinement bits, group size (must be 128 on the GPU). */
+typedef struct {
+  int32_t b, r, group;
+} sf_qfmt;
+
+/* Layouts of the refinement codes written by sf_quantize_nested. */
+#define SF_REFINE_CHANNEL_MAJOR 0 /* weights: [cols][rows*r/8]; unit k = refinement
+                                     bits of input channel k over all rows */
+#define SF_REFINE_ROW_MAJOR 1     /* [rows][cols*r/8]; unit = one row */
+
+/* A nested-quantised weight matrix, torch layout [n_out][k_in], groups along k_in. */
+typedef struct {
+  const uint8_t* resident; /* [n_out][k_in*b/8] packed resident codes */
+  const uint32_t* sz;      /* [n_out][k_in/128] (scale fp16 | zero fp16 << 16) */
+  int64_t n_out, k_in;
+  sf_qfmt fmt;
+} sf_qweight;
+
+/* A nested-quantised KV cache, one group per token-head (head_dim = 128).
+ * k_res, v_res: [batch][n_kv_heads][t_cap][head_dim*b/8]; k_sz, v_sz:
+ * [batch][n_kv_heads][t_cap] words as above.  Tokens [0, t_len) are valid.
+ * KV refinement unit of (batch i, kv head h, token t): unit id
+ * (i*n_kv_heads + h)*t_cap + t, bytes = K refinement stream (head_dim*r/8) followed
+ * by the V refinement stream (head_dim*r/8). */
+typedef struct {
+  uint8_t* k_res;
+  uint32_t* k_sz;
+  uint8_t* v_res;
+  uint32_t* v_sz;
+  int32_t batch, n_kv_heads, head_dim, t_len, t_cap;
+  sf_qfmt fmt;
+} sf_qkv;
+
+typedef struct sf_refine_cache sf_refine_cache;
+typedef struct sf_workspace sf_workspace;
+
+/* ---- misc ------------------------------------------------------------------ */
+int32_t sf_abi_version(void);
+const char* sf_status_string(sf_status s);
+const char* sf_last_error(void);
+
+/* Device workspace for the refined GEMV and attention calls.  `bytes` from
+ * sf_workspace_bytes_gemv / sf_workspace_bytes_attn (take the maximum over the
+ * calls that share it). */
+sf_status sf_workspace_create(size_t bytes, sf_workspace** out);
+sf_status sf_workspace_destroy(sf_workspace* ws);
+size_t sf_workspace_bytes_gemv(int32_t n_ops, int64_t k_in, int32_t k_sel);
+size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t t_len, int32_t k_sel);
+/* Returns SF_ESTATE (and clears the flag) if a device-side wait timed out in a
+ * call that used this workspace since the last check; the affected rows then
+ * carry no refinement.  Synchronises the device. */
+sf_status sf_workspace_check(sf_workspace* ws);
+
+/* ---- a1: nested quantisation ----------------------------------------------- */
+/* Quantise x fp32 [rows][cols] (cols % 128 == 0) to the nested format above.
+ * Writes resident [rows][cols*b/8], sz [rows][cols/128] and the refinement codes in
+ * `refine_layout`; for SF_REFINE_CHANNEL_MAJOR rows*r must be a multiple of 32.
+ * `refine` may be NULL (r == 0, or refinement not wanted).  Format: see top. */
+sf_status sf_quantize_nested(const float* x, int64_t rows, int64_t cols, sf_qfmt fmt,
+                             int32_t refine_layout, uint8_t* resident, uint32_t* sz,
+                             uint8_t* refine, sf_stream stream);
+
+/* Test helper: dequantise to fp32 [rows][cols].  which = 0: resident value
+ * z + (s*2^r)*(c>>r); which = 1: full value z + s*c (needs `refine` in
+ * `refine_layout`).  Each value is one round-to-nearest-even of the exact value. */
+sf_status sf_debug_dequantize(const uint8_t* resident, const uint32_t* sz,
+                              const uint8_t* refine, int64_t rows, int64_t cols,
+                              sf_qfmt fmt, int32_t refine_layout, int32_t which,
+                              float* out, sf_stream stream);
+
+/* ---- a7: KV append --------------------------------------------------------- */
+/* Quantise n_tok new tokens of K and V (fp32 [batch][n_kv_heads][n_tok][head_dim])
+ * into positions [t0, t0 + n_tok) of `kv` (t0 + n_tok <= t_cap; kv->t_len is not
+ * changed by the call).  Their refinement units (layout of sf_qkv) are written
+ * to refine_out [batch][n_kv_heads][n_tok][unit bytes] (device), for the caller to
+ * copy into its host refinement store.  Per (batch, head, token) the K row and
+ * the V row are one group each. */
+sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok, int32_t t0,
+                       const sf_qkv* kv, uint8_t* refine_out, sf_stream stream);
+
+/* ---- a3, a13: refinement slot cache ---------------------------------------- */
+/* One pool per refined tensor.  Units are fixed-size byte strings, unit ids
+ * 0..n_units-1; host_store (pinned host memory, from hipHostMalloc or torch
+ * pin_memory, kept alive by the caller) holds every unit, [n_units][unit_bytes].
+ * If device_store is non-NULL, the pool is a resident pool: capacity must equal
+ * n_units, device_store [n_units][unit_bytes] (caller device memory) already
+ * holds every unit, unit u lives in slot u, and the pool never misses. */
+typedef struct {
+  int64_t unit_bytes; /* multiple of 4 */
+  int64_t n_units;
+  int64_t capacity; /* device slots, 0 <= capacity <= n_units */
+  const uint8_t* host_store;
+  uint8_t* device_store;
+  int32_t max_lookup; /* most unit ids one step looks up in this pool */
+} sf_pool_desc;
+
+#define SF_CACHE_DETERMINISTIC 0 /* fill completes before the next step's lookups */
+#define SF_CACHE_ASYNC 1         /* fills land when their copy has finished */
+
+/* Creates the cache on the current device.  Lookups at step t mark hits as used
+ * at t and queue misses; sf_refine_cache_fill (end of step t) installs the queued
+ * misses in the order they were looked up: into a free slot, else in place of the
+ * resident unit with the smallest (last use, unit id) among those last used
+ * before t, else the miss is dropped; at most max_fill units per pool per fill
+ * (0 = no cap).  Installed units count as used at t. */
+sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n_pools, int32_t mode,
+                                 int32_t max_fill, sf_refine_cache** out);
+sf_status sf_refine_cache_destroy(sf_refine_cache* c);
+
+/* Looks up n device unit ids of `pool`; writes the slot of each (or -1) to
+ * slot_out (device, may be NULL) and records the lookup for the next fill. */
+sf_status sf_refine_cache_lookup(sf_refine_cache* c, int32_t pool, const int32_t* unit_ids,
+                                 int32_t n, int32_t* slot_out, sf_stream compute);
+
+/* End of a decode step: reads the step's lookups, runs the replacement policy,
+ * gathers the missed units from the host stores into pinned staging and copies
+ * them with one hipMemcpyAsync per pool on `side`, then installs them.
+ * Deterministic mode: returns after the new units are visible to work enqueued
+ * later on `compute`.  Async mode: returns after enqueueing; units whose copy
+ * finished are published at a later fill call.  n_filled (host, may be NULL):
+ * units installed or queued for install by this call. */
+sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream side,
+                               int64_t* n_filled);
+
+/* Host-side statistics since creation: lookups, hits, units installed, bytes
+ * copied host-to-device; per pool if pool >= 0, all pools if pool < 0. */
+sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int64_t* lookups,
+                                int64_t* hits, int64_t* installed, int64_t* h2d_bytes);
+
+/* Test helper: writes the resident unit ids of `pool` (ascending) to ids (host,
+ * room for capacity entries) and their count to *n. */
+sf_status sf_refine_cache_resident(sf_refine_cache* c, int32_t pool, int64_t* ids, int64_t* n);
+
+/* ---- a2-a6: refined GEMV ----------------------------------------------------- */
+/* One matrix of a fused GEMV call.  All ops of a call share x, k_in and fmt. */
+typedef struct {
+  sf_qweight w;
+  int32_t pool;     /* cache pool of this matrix (unit k = input channel k), -1 = none */
+  float* y;         /* [batch][n_out] fp32 */
+  int32_t* hit_out; /* optional [k_sel]: slot of each selected channel, -1 = miss */
+} sf_gemv_op;
+
+/* y = x W_eff^T for each op, x fp16 [batch][k_in] (batch >= 1), where W_eff uses
+ * the full (b+r)-bit value on the selected channels whose refinement unit is in
+ * the cache (a hit) and the resident value everywhere else.
+ * Selection: if sel_in (device [k_sel], ascending, distinct) is NULL, the k_sel
+ * channels of largest max-over-batch |x|, ties to the lower index.  sel_out
+ * (device [k_sel], may be NULL) receives the selection, ascending.  k_sel = 0 is
+ * the unrefined low-bit GEMV.  cache may be NULL (every selection misses). */
+sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
+                          int32_t batch, int32_t k_sel, const int32_t* sel_in,
+                          int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
+                          sf_stream stream);
+
+/* ---- a8-a12: refined GQA decode attention ------------------------------------ */
+/* out fp32 [batch][n_q_heads][head_dim] for q fp16 [batch][n_q_heads][head_dim]
+ * over tokens [0, kv->t_len).  Query head h reads KV head h / (n_q/n_kv).
+ * Per (batch, kv head): logits from the resident keys, softmax per query head,
+ * token score = that softmax summed over the kv head's query heads; the k_sel
+ * tokens of largest score (ties to the lower token) are selected (or sel_in,
+ * device [batch][n_kv][k_sel], ascending), looked up in `pool`, and for the hits
+ * both the key and the value use the full (b+r)-bit value; the output softmax is
+ * over all tokens after that replacement.  sel_out / hit_out (device
+ * [batch][n_kv][k_sel], may be NULL) receive the selection and slots. */
+sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
+                                 float softmax_scale, int32_t k_sel, const int32_t* sel_in,
+                                 sf_refine_cache* cache, int32_t pool, float* out,
+                                 int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
+                                 sf_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STRATAFLUX_H */
