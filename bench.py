@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Refined low-bit decode-step benchmark on one MI355X.
+
+One step = one decode step of a Llama-3.1-8B-shaped model at batch 1 through the
+whole refined path, for each of the 32 layers:
+  KV append (the new token's K and V quantised into the 2+2-bit cache),
+  q/k/v refined GEMV (one fused launch, top 3% input channels refined),
+  refined GQA attention over the 32768-token context (32 query / 8 KV heads,
+  head dim 128, top 2% tokens refined),
+  o refined GEMV, gate/up refined GEMV (fused), down refined GEMV,
+plus the refinement-cache fill at the end of the step.  Weights and KV are 2-bit
+resident + 2-bit refinement, group 128.  Every refinement pool holds all of its
+units on the device (no capacity limit is set for this workload), so every
+selected unit hits.  Inputs are seeded synthetic data with the pages' shapes and
+distributions (no trained weights or datasets): W ~ N(0, 0.02), activations
+N(0, 1) with 1% of channels x20, K and V ~ N(0, 1) with 4 dims of K x8, q ~ N(0,1).
+
+Timing: the step is captured once as a HIP graph and replayed; inputs are resident
+in HBM before the timed region.  The dominant kernel (the fused gate/up GEMV) is
+timed with HIP events around each of its launches in an eager pass over the same
+step.  The CPU baseline is the fp64 oracle on a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+HIDDEN, FFN, NQ, NKV, HD = 4096, 14336, 32, 8, 128
+
+
+def k_select(percent, n):
+    return (percent * n + 99) // 100
+
+
+def gemv_bytes(shapes, k_in, k_sel, b, r, batch):
+    """Algorithmic bytes of one fused refined GEMV call: resident codes, scale/zero
+    words, refinement bits of the applied (hit) channels, x, y, selected indices."""
+    tot = 0
+    for n_out in shapes:
+        tot += n_out * k_in * b // 8 + n_out * (k_in // 128) * 4 + k_sel * n_out * r // 8 + n_out * 4 * batch
+    return tot + k_in * 2 * batch + k_sel * 4
+
+
+def attn_bytes(T, k_sel, b, r, batch):
+    """Algorithmic bytes of one refined attention call: resident K and V codes and
+    their scale/zero words, refinement units of the applied tokens, q, out, indices."""
+    per_th = 2 * (HD * b // 8 + 4)
+    return batch * (NKV * T * per_th + NKV * k_sel * (2 * HD * r // 8) + NQ * HD * 2 + NQ * HD * 4 + NKV * k_sel * 4)
+
+
+def append_bytes(b, r, batch):
+    return batch * NKV * (2 * HD * 4 + 2 * (HD * b // 8 + 4) + 2 * HD * r // 8)
+
+
+class Model:
+    def __init__(self, layers, T, batch, b, r, ch_pct, tok_pct, seed=1234):
+        import torch
+
+        from bit_decode_selective_amd import binding, inputs
+
+        self.torch, self.binding, self.inputs = torch, binding, inputs
+        self.layers, self.T, self.batch, self.b, self.r = layers, T, batch, b, r
+        dev = torch.device("cuda", 0)
+        self.dev = dev
+        g = torch.Generator(device=dev)
+        self.groups = []  # per layer: list of (name, [QuantWeight], k_in)
+        pools = []
+        self.kvs = []
+        for li in range(layers):
+            g.manual_seed(seed + li)
+            mats = {}
+            for name, (n, k) in (("q", (HIDDEN, HIDDEN)), ("k", (NKV * HD, HIDDEN)), ("v", (NKV * HD, HIDDEN)),
+                                 ("o", (HIDDEN, NQ * HD)), ("gate", (FFN, HIDDEN)), ("up", (FFN, HIDDEN)),
+                                 ("down", (HIDDEN, FFN))):
+                W = inputs.torch_weight(g, n, k, device=dev)
+                mats[name] = binding.QuantWeight.from_device(W, b, r)
+                del W
+            grp = []
+            for gname, names in (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))):
+                ws = [mats[n] for n in names]
+                ops = []
+                for w in ws:
+                    ops.append((w, len(pools)))
+                    pools.append(w.resident_pool_desc())
+                grp.append((gname, ops, ws[0].k_in))
+            self.groups.append(grp)
+            kv = binding.QuantKV(batch, NKV, T, b, r, device=dev)
+            for t0 in range(0, T - 1, 8192):
+                n = min(8192, T - 1 - t0)
+                K, V = inputs.torch_kv(g, batch, NKV, n, HD, device=dev)
+                kv.append(K, V)
+                del K, V
+            self.kvs.append((kv, len(pools)))
+            pools.append(kv.resident_pool_desc())
+            torch.cuda.synchronize()
+        self.cache = binding.RefineCache(pools, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        # per-layer synthetic inputs and outputs
+        self.x = []
+        self.y = []
+        self.q = []
+        self.knew = []
+        self.out = []
+        for li in range(layers):
+            g.manual_seed(seed + 1000 + li)
+            xs, ys = [], []
+            for gname, ops, k_in in self.groups[li]:
+                outl = torch.randperm(k_in, generator=g, device=dev)[: (k_in + 99) // 100].cpu().numpy()
+                xs.append(binding._f16_bits(inputs.torch_activation(g, batch, k_in, outl, device=dev), dev))
+                ys.append([torch.empty((batch, w.n_out), dtype=torch.float32, device=dev) for w, _ in ops])
+            self.x.append(xs)
+            self.y.append(ys)
+            self.q.append(binding._f16_bits(torch.randn((batch, NQ, HD), generator=g, device=dev).half(), dev))
+            K, V = inputs.torch_kv(g, batch, NKV, 1, HD, device=dev)
+            self.knew.append((K.contiguous(), V.contiguous()))
+            self.out.append(torch.empty((batch, NQ, HD), dtype=torch.float32, device=dev))
+        self.ch_pct, self.tok_pct = ch_pct, tok_pct
+        ws_bytes = max(
+            [binding.lib().sf_workspace_bytes_gemv(len(ops), k_in, k_select(ch_pct, k_in))
+             for grp in self.groups for _, ops, k_in in grp]
+            + [binding.lib().sf_workspace_bytes_attn(batch, NQ, NKV, T, k_select(tok_pct, T))]
+        )
+        self.ws = binding.workspace(ws_bytes, dev)
+        torch.cuda.synchronize()
+
+    def build_calls(self, refined=True):
+        """Prebuilt ctypes argument tuples for every launch of one step."""
+        b = self.binding
+        L = b.lib()
+        calls = []  # (fn, args, tag)
+        for li in range(self.layers):
+            kv, kv_pool = self.kvs[li]
+            T = self.T
+            Kn, Vn = self.knew[li]
+            dsc_app = kv.desc(T - 1)
+            dst = kv.refine.data_ptr() + (T - 1) * kv.unit_bytes
+            calls.append((L.sf_kv_append, (C.c_void_p(Kn.data_ptr()), C.c_void_p(Vn.data_ptr()), 1, T - 1,
+                                           C.byref(dsc_app), C.c_void_p(dst), kv.t_cap, None), "append", dsc_app))
+            for gi, (gname, ops, k_in) in enumerate(self.groups[li]):
+                ks = k_select(self.ch_pct, k_in) if refined else 0
+                arr = (b.sf_gemv_op * len(ops))()
+                for i, (w, pool) in enumerate(ops):
+                    arr[i] = b.sf_gemv_op(w.desc(), pool, self.y[li][gi][i].data_ptr(), None)
+                args = (arr, len(ops), C.c_void_p(self.x[li][gi].data_ptr()), self.batch, ks, None, None,
+                        self.cache.handle, self.ws.handle, None)
+                calls.append((L.sf_refined_gemv, args, gname, arr))
+                if gname == "qkv":
+                    dsc = kv.desc(T)
+                    kt = k_select(self.tok_pct, T) if refined else 0
+                    aargs = (C.c_void_p(self.q[li].data_ptr()), NQ, C.byref(dsc), 1.0 / math.sqrt(HD), kt, None,
+                             self.cache.handle, kv_pool, C.c_void_p(self.out[li].data_ptr()), None, None,
+                             self.ws.handle, None)
+                    calls.append((L.sf_refined_attn_decode, aargs, "attn", dsc))
+        return calls
+
+    def enqueue(self, calls, stream, events=None, tag=None):
+        """Launch every kernel of one step on `stream` (no host synchronisation)."""
+        s = C.c_void_p(stream.cuda_stream)
+        for fn, args, t, _keep in calls:
+            a = list(args)
+            a[-1] = s
+            if events is not None and t == tag:
+                e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st = fn(*a)
+                e1.record(stream)
+                events.append((e0, e1))
+            else:
+                st = fn(*a)
+            if st != 0:
+                self.binding.check(st)
+
+    def fill(self, stream):
+        """End-of-step refinement-cache fill (host side; enqueues copies if needed)."""
+        st = self.binding.lib().sf_refine_cache_fill(self.cache.handle, C.c_void_p(stream.cuda_stream),
+                                                     C.c_void_p(self.side.cuda_stream), None)
+        self.binding.check(st)
+
+    def step_bytes(self, refined=True):
+        tot = 0
+        for li in range(self.layers):
+            for gname, ops, k_in in self.groups[li]:
+                ks = k_select(self.ch_pct, k_in) if refined else 0
+                tot += gemv_bytes([w.n_out for w, _ in ops], k_in, ks, self.b, self.r, self.batch)
+            tot += attn_bytes(self.T, k_select(self.tok_pct, self.T) if refined else 0, self.b, self.r, self.batch)
+            tot += append_bytes(self.b, self.r, self.batch)
+        return tot
+
+    def dominant_bytes(self):
+        gname, ops, k_in = self.groups[0][2]
+        return gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(self.ch_pct, k_in), self.b, self.r, self.batch)
+
+
+def time_steps(model, calls, steps, warmup, use_graph):
+    """Average ms per step over `steps` timed steps after `warmup` untimed ones."""
+    torch = model.torch
+    stream = torch.cuda.Stream(device=model.dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            model.enqueue(calls, stream)
+            model.fill(stream)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            model.enqueue(calls, stream)
+
+        def step():
+            g.replay()
+            model.fill(stream)
+    else:
+        def step():
+            model.enqueue(calls, stream)
+            model.fill(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, batch):
+    """The fp64 oracle on a bounded sample: one 4096 x 4096 refined GEMV and refined
+    attention over 2 KV heads (8 query heads) at the full context; rates scaled to
+    the whole step by algorithmic bytes."""
+    import numpy as np
+
+    from bit_decode_selective_amd import inputs
+    from oracle import attention as o_attn
+    from oracle import gemv as o_gemv
+    from oracle import nested, selection
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = inputs.weight(2, 0, inputs.Q_PROJ, HIDDEN, HIDDEN)
+    q = nested.quantize(W, b, r, 128)
+    x = inputs.activation(2, 0, inputs.Q_PROJ, 0, batch, HIDDEN)
+    ks = selection.k_select(ch_pct, HIDDEN)
+    t0 = time.perf_counter()
+    sel = selection.select_channels(x, ks)
+    o_gemv.refined_gemv(q, x, sel)
+    tg = time.perf_counter() - t0
+    gb = gemv_bytes([HIDDEN], HIDDEN, ks, b, r, batch)
+    nkv = 2
+    K, V = inputs.kv(3, 0, 1, nkv, T, HD)
+    qh = inputs.query(3, 0, 0, 1, nkv * NQ // NKV, HD)
+    qk, qv = o_attn.quantize_kv(K, b, r), o_attn.quantize_kv(V, b, r)
+    kt = selection.k_select(tok_pct, T)
+    t0 = time.perf_counter()
+    o_attn.refined_attention(qh, qk, qv, (1, nkv, T, HD), 1 / math.sqrt(HD), kt)
+    ta = time.perf_counter() - t0
+    ab = attn_bytes(T, kt, b, r, 1) * nkv / NKV
+    step_s = gemv_step_bytes / (gb / tg) + attn_step_bytes / (ab / ta)
+    return {
+        "value": batch / step_s,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: one {HIDDEN}x{HIDDEN} {b}+{r}-bit refined GEMV ({tg:.2f} s) and refined "
+                   f"attention over {nkv} KV heads x {T} tokens ({ta:.2f} s); scaled to the full step by "
+                   f"algorithmic bytes (GEMV {gb / tg / 1e6:.1f} MB/s, attention {ab / ta / 1e6:.1f} MB/s); "
+                   f"host cpu_count={os.cpu_count()}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unrefined", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the refined decode path runs on a single device; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    b = r = 2
+    ch_pct, tok_pct = 3, 2
+    t_setup = time.time()
+    model = Model(args.layers, args.context, args.batch, b, r, ch_pct, tok_pct)
+    print(f"# setup {time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    calls = model.build_calls(refined=True)
+
+    use_graph = not args.no_graph
+    ms = time_steps(model, calls, args.steps, args.warmup, use_graph)
+    print(f"# refined step {ms:.3f} ms", file=sys.stderr, flush=True)
+    unref_ms = None
+    if not args.no_unrefined:
+        calls0 = model.build_calls(refined=False)
+        unref_ms = time_steps(model, calls0, args.steps, args.warmup, use_graph)
+        print(f"# unrefined step {unref_ms:.3f} ms", file=sys.stderr, flush=True)
+    # dominant kernel: fused gate/up GEMV, HIP events around each launch (eager pass)
+    stream = torch.cuda.Stream(device=model.dev)
+    evs = []
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.steps // 4)):
+            model.enqueue(calls, stream, events=evs, tag="gateup")
+            model.fill(stream)
+    torch.cuda.synchronize()
+    dom_us = 1000.0 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    dom_bytes = model.dominant_bytes()
+    step_bytes = model.step_bytes(True)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    res = {
+        "metric": "refined decode tokens/s + achieved HBM GB/s (% peak), Llama-8B-shape 2-bit",
+        "value": args.batch / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 x int-code -> fp32 (fp64 attention partials)",
+        "data": "synthetic (seeded random weights/KV/activations of the model shapes; no trained weights)",
+        "config": {
+            "workload": (f"Llama-3.1-8B-shape refined decode step, batch {args.batch}: {args.layers} layers x "
+                         f"(KV append, q/k/v + o + gate/up + down GEMVs {b}+{r}-bit top {ch_pct}% channels, "
+                         f"GQA attention 32q/8kv d128 T={args.context} KV {b}+{r}-bit top {tok_pct}% tokens)"),
+            "layers": args.layers,
+            "batch": args.batch,
+            "context": args.context,
+            "weight_bits": f"{b}+{r}",
+            "kv_bits": f"{b}+{r}",
+            "refine_channels_pct": ch_pct,
+            "refine_tokens_pct": tok_pct,
+            "refinement_pools": "all units resident on the device",
+            "hip_graph": use_graph,
+        },
+        "hbm_gbps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel (fused gate/up, 2 x 14336 x 4096)",
+            "achieved": dom_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": dom_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "launch_us": dom_us,
+            "bytes_per_launch": dom_bytes,
+        },
+    }
+    if unref_ms is not None:
+        res["unrefined_tokens_per_s"] = args.batch / (unref_ms * 1e-3)
+        res["refined_over_unrefined"] = unref_ms / ms
+    if not args.no_cpu_baseline:
+        gsb = sum(gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(ch_pct, k_in), b, r, args.batch)
+                  for grp in model.groups for _, ops, k_in in grp)
+        asb = args.layers * attn_bytes(args.context, k_select(tok_pct, args.context), b, r, args.batch)
+        res["cpu_baseline"] = cpu_baseline(args.context, ch_pct, tok_pct, b, r, gsb, asb, args.batch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,7 +90,7 @@ _PROTOS = {
     "sf_workspace_check": (I32, [VP]),
     "sf_quantize_nested": (I32, [VP, I64, I64, sf_qfmt, I32, VP, VP, VP, VP]),
     "sf_debug_dequantize": (I32, [VP, VP, VP, I64, I64, sf_qfmt, I32, I32, VP, VP]),
-    "sf_kv_append": (I32, [VP, VP, I32, I32, C.POINTER(sf_qkv), VP, VP]),
+    "sf_kv_append": (I32, [VP, VP, I32, I32, C.POINTER(sf_qkv), VP, I64, VP]),
     "sf_refine_cache_create": (I32, [C.POINTER(sf_pool_desc), I32, I32, I32, C.POINTER(VP)]),
     "sf_refine_cache_destroy": (I32, [VP]),
     "sf_refine_cache_lookup": (I32, [VP, I32, VP, I32, VP, VP]),
@@ -320,12 +320,13 @@ class QuantKV:
         K_new = _dev_tensor(K_new, torch.float32, dev)
         V_new = _dev_tensor(V_new, torch.float32, dev)
         n_tok = K_new.shape[2]
-        staged = torch.empty((self.batch, self.n_kv, n_tok, self.unit_bytes), dtype=torch.uint8, device=dev)
         d = self.desc()
-        check(lib().sf_kv_append(_ptr(K_new), _ptr(V_new), n_tok, self.t_len, C.byref(d), _ptr(staged), _stream(stream)))
-        self.refine[:, :, self.t_len : self.t_len + n_tok] = staged
+        # refinement units land in place in the device store
+        dst = self.refine.data_ptr() + self.t_len * self.unit_bytes
+        check(lib().sf_kv_append(_ptr(K_new), _ptr(V_new), n_tok, self.t_len, C.byref(d), C.c_void_p(dst),
+                                 self.t_cap, _stream(stream)))
         self.t_len += n_tok
-        return staged
+        return self.refine[:, :, self.t_len - n_tok : self.t_len]
 
     @classmethod
     def from_host(cls, K, V, b, r, device="cuda", t_cap=None):

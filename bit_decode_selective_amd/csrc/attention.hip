@@ -8,46 +8,37 @@
 // over the kv head's query heads; for selected tokens that hit, both key and value
 // use the (b+r)-bit value; the output softmax runs over all tokens after that.
 //
-// The refinement is additive, so the refined output is the unrefined flash-decoding
-// result plus a correction over the (few) hit tokens:
-//   l'_t = l_t + scale * s_K,t * (q . cK_lo,t)           (t in E)
-//   Z'   = Z + sum_E (e^{l'-m} - e^{l-m})
-//   N'   = N + sum_E ((e^{l'-m} - e^{l-m}) * V_b,t + e^{l'-m} * s_V,t * cV_lo,t)
-//   out  = N' / Z'
-// Kernel A streams the resident K and V once (split over T) and writes the logits
-// and per-split (m, Z, N) partials.  Kernel B, one workgroup per (batch, kv head),
-// merges the partials, forms the selection scores, radix-selects the top-k tokens
-// (ties to the lower token), looks them up in the refinement cache and applies the
-// correction.
+// Three launches per call:
+//   qk     : streams the resident keys (T split over workgroups), logits of the G
+//            query heads of each KV head on MFMA (codes expanded into fp16
+//            mantissas, value 1 + c/2^b, times q), per-split softmax max / sum;
+//   select : merges the split statistics, forms the selection scores, builds a
+//            2048-bin histogram of their bit patterns (many workgroups); the last
+//            workgroup of each KV head finishes an exact radix select (ties to the
+//            lower token), compacts the selection in token order, looks it up in
+//            the refinement cache and overwrites the logits of the hit tokens with
+//            their refined values l' = l + scale * s_K * (q . cK_lo);
+//   pv     : streams the resident values with the final weights exp(l - m'),
+//            adds s_V * cV_lo for the hit tokens of its split, and the last
+//            workgroup of each KV head merges the split sums into the output.
+// All weights are positive and final before they are accumulated, so fp32 sums
+// carry no cancellation.
 #include "block_scan.h"
 #include "sf_internal.h"
 
 namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 128;       // head dim
-constexpr int MAX_G = 8;      // query heads per kv head
-constexpr int MAX_SPLITS = 256;
-
-// b in {1,2,4,8}: codes i and i + P/2 of a word share one and-or into fp16 lanes.
-template <int B>
-struct KCodec {
-  static constexpr int P = 32 / B, HP = P / 2;
-  static constexpr int WORDS = HD * B / 32;  // words per token-head
-  static constexpr int PAIRS = HD / 2;
-  __device__ static int pair_k0(int j) { return (j / HP) * P + (j % HP); }
-  __device__ static int pair_k1(int j) { return pair_k0(j) + HP; }
-  __device__ static __forceinline__ uint32_t pair(const uint32_t* w, int j) {
-    const int wi = j / HP, i = j % HP;
-    const int sh = (10 - B) - i * B;
-    const uint32_t t = sh >= 0 ? (w[wi] << sh) : (w[wi] >> (-sh));
-    constexpr uint32_t m = ((1u << B) - 1u) << (10 - B);
-    return (t & (m | (m << 16))) | 0x3C003C00u;
-  }
-};
+constexpr int SPLIT1 = 256;   // tokens per qk workgroup (4 waves x 4 MFMA tiles of 16)
+constexpr int SPLIT2 = 2048;  // tokens per select workgroup
+constexpr int SPLIT3 = 256;   // tokens per pv workgroup
+constexpr int NBINS = 2048;   // first-level radix bins (top 11 bits of the score)
 
 __device__ __forceinline__ uint32_t field(const uint32_t* w, int bit, int width) {
   const int wi = bit >> 5, off = bit & 31;
@@ -56,454 +47,556 @@ __device__ __forceinline__ uint32_t field(const uint32_t* w, int bit, int width)
   return v & ((1u << width) - 1u);
 }
 
+__device__ __forceinline__ float h2f16(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
+
 struct AttnArgs {
   const uint16_t* q;  // [batch][n_q][HD] fp16 bits
   const uint8_t* k_res;
   const uint32_t* k_sz;
   const uint8_t* v_res;
   const uint32_t* v_sz;
-  int batch, n_q, n_kv, G, T, t_cap, b, r, splits, split_len, k_sel;
+  int batch, n_q, n_kv, G, T, t_cap, b, r, k_sel, s1, s2, s3;
   float scale;
-  float* logits;  // [batch][n_q][T]
-  float* scores;  // [batch][n_kv][T]
-  double* part;   // [batch*n_kv][splits][G][2 + HD]: m, Z, N[HD] (fp64)
+  float* logits;    // [batch*n_q][T]
+  float* scores;    // [batch*n_kv][T]
+  float* k1part;    // [bh][s1][G][2]: split max, split sum of exp
+  uint32_t* hist;   // [bh][NBINS]
+  uint32_t* cnt;    // [bh][2]: select, pv workgroups done
+  int32_t* sel;     // [bh][KS]
+  int32_t* hit_t;   // [bh][KS]
+  int32_t* hit_s;   // [bh][KS]
+  int32_t* n_hit;   // [bh]
+  float* mref;      // [bh][G]: max logit after refinement
+  float* k3part;    // [bh][s3][G][1 + HD]
   const int32_t* sel_in;
   int32_t* sel_out;
   int32_t* hit_out;
-  int32_t* lists;   // per (batch, kv head): sel, hit token, hit slot [k_sel] each
-  double* ee;       // per (batch, kv head): [k_sel][G][2]: weight added by the stream pass, e'
   float* out;       // [batch][n_q][HD]
   PoolDev pool;
 };
 
-// ---- kernel A: logits + per-split flash partials ---------------------------------
-template <int B, int G>
-__global__ __launch_bounds__(256) void attn_stream_kernel(AttnArgs a) {
-  extern __shared__ float sm[];
-  float* lg = sm;  // [G][split_len]
-  __shared__ uint32_t qs[G][KCodec<B>::PAIRS];
-  __shared__ float qsum[G];
-  __shared__ float red[4][G];
-  __shared__ double dred[4][G][2];
-  __shared__ double acc_red[4][G][HD];
+// ---- block helpers (256 threads) ------------------------------------------------
+__device__ __forceinline__ float wg_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
 
-  using C = KCodec<B>;
+__device__ __forceinline__ float wg_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Suffix sums in place over n bins (n a multiple of 256) held in LDS.
+__device__ void wg_suffix_sum(uint32_t* h, int n, int* lds4) {
+  const int per = n / 256, t = threadIdx.x;
+  const int hi = n - per * t;  // this thread sums bins [hi - per, hi)
+  int s = 0;
+  for (int i = hi - 1; i >= hi - per; --i) s += (int)h[i];
+  int tot;
+  int run = wg_exclusive_scan(s, lds4, &tot);
+  for (int i = hi - 1; i >= hi - per; --i) {
+    run += (int)h[i];
+    h[i] = (uint32_t)run;
+  }
+  __syncthreads();
+}
+
+// ---- qk: logits + per-split softmax statistics -----------------------------------
+template <int B, int G>
+__global__ __launch_bounds__(256) void attn_qk_kernel(AttnArgs a) {
+  __shared__ float st[4][16][2];
+  constexpr int P = 32 / B, HP = P / 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
-  const int L = a.split_len;
-  const int t_begin = split * L;
-  const int t_end = min(a.T, t_begin + L);
-  const int n_here = max(0, t_end - t_begin);
-  const uint16_t* qg = a.q + ((size_t)bi * a.n_q + (size_t)kvh * G) * HD;
+  const int T = a.T;
+  const int t_begin = split * SPLIT1, t_end = min(T, t_begin + SPLIT1);
 
-  for (int p = tid; p < G * C::PAIRS; p += 256) {
-    const int h = p / C::PAIRS, j = p - h * C::PAIRS;
-    qs[h][j] = (uint32_t)qg[h * HD + C::pair_k0(j)] | ((uint32_t)qg[h * HD + C::pair_k1(j)] << 16);
-  }
-  if (tid < G) {
-    float s = 0.f;
-    for (int i = 0; i < HD; ++i) s += (float)__builtin_bit_cast(_Float16, qg[tid * HD + i]);
-    qsum[tid] = s;
-  }
-  __syncthreads();
+  // this call's selection histogram and counters start at zero
+  for (int i = split * 256 + tid; i < NBINS; i += a.s1 * 256) a.hist[(size_t)bh * NBINS + i] = 0;
+  if (split == 0 && tid < 2) a.cnt[bh * 2 + tid] = 0;
+
+  // B operand: q of head n = lane % 16 (zero for n >= G) over the 32 dims of lane
+  // group qg = lane / 16, in the same pair order as the key codes
+  const int n = lane & 15, qg = lane >> 4;
+  const uint16_t* qrow = a.q + ((size_t)bi * a.n_q + (size_t)kvh * G + (n < G ? n : 0)) * HD;
+  h8_t bq[4];
+  float qpart = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = 4 * j + (e >> 1), h = e & 1;
+      const int w = p / HP, i = p % HP;
+      const int dim = 32 * qg + P * w + i + h * HP;
+      const float v = n < G ? h2f16(qrow[dim]) : 0.f;
+      bq[j][e] = (_Float16)v;
+      qpart += v;
+    }
+  qpart += __shfl_xor(qpart, 16, 64);
+  qpart += __shfl_xor(qpart, 32, 64);
+  const float qsum = qpart;  // sum of q_n over all 128 dims
 
   const size_t tok0 = (size_t)bh * a.t_cap;
   const float scl = (float)(1u << (a.r + B));
-  // A1: logits, one token per thread
-  for (int tl = tid; tl < n_here; tl += 256) {
-    const size_t tok = tok0 + t_begin + tl;
-    uint32_t w[C::WORDS];
-    const u32x4* src = (const u32x4*)(a.k_res + tok * (HD * B / 8));
+  constexpr uint32_t m1 = ((1u << B) - 1u) << (10 - B);
+  float run_m = -INFINITY, run_z = 0.f;
+  // each wave: 4 tiles of 16 tokens
+  const int tw = t_begin + wave * 64;
+  uint32_t wv[4][B];
 #pragma unroll
-    for (int i = 0; i < C::WORDS / 4; ++i) {
-      const u32x4 v = __builtin_nontemporal_load(src + i);
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  for (int u = 0; u < 4; ++u) {
+    const int tm = tw + 16 * u + (lane & 15);
+    if (tm < t_end) {
+      const uint32_t* src = (const uint32_t*)(a.k_res + (tok0 + tm) * (HD * B / 8)) + qg * B;
+      if constexpr (B == 1) {
+        wv[u][0] = __builtin_nontemporal_load(src);
+      } else if constexpr (B == 2) {
+        const u32x2 v = __builtin_nontemporal_load((const u32x2*)src);
+        wv[u][0] = v.x; wv[u][1] = v.y;
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < B / 4; ++q4) {
+          const u32x4 v = __builtin_nontemporal_load((const u32x4*)src + q4);
+          wv[u][4 * q4] = v.x; wv[u][4 * q4 + 1] = v.y; wv[u][4 * q4 + 2] = v.z; wv[u][4 * q4 + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < B; ++w) wv[u][w] = 0;
     }
-    const uint32_t szw = a.k_sz[tok];
-    const float s = sf_h2f(szw), z = sf_h2f(szw >> 16);
-    float d[G];
+  }
 #pragma unroll
-    for (int h = 0; h < G; ++h) d[h] = 0.f;
+  for (int u = 0; u < 4; ++u) {
+    f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < C::PAIRS; ++j) {
-      const uint32_t pr = C::pair(w, j);
+    for (int j = 0; j < 4; ++j) {
+      uint32_t pr[4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) d[h] = __builtin_amdgcn_fdot2(as_h2(pr), as_h2(qs[h][j]), d[h], false);
+      for (int v = 0; v < 4; ++v) {
+        const int p = 4 * j + v, w = p / HP, i = p % HP;
+        const int sh = (10 - B) - i * B;
+        const uint32_t t = sh >= 0 ? (wv[u][w] << sh) : (wv[u][w] >> (-sh));
+        pr[v] = (t & (m1 | (m1 << 16))) | 0x3C003C00u;
+      }
+      const u32x4 pv = {pr[0], pr[1], pr[2], pr[3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, pv), bq[j], acc, 0, 0, 0);
     }
+    if (n < G) {
+      const int tb = tw + 16 * u + 4 * qg;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float l = a.scale * (z * qsum[h] + (s * scl) * (d[h] - qsum[h]));
-      lg[h * L + tl] = l;
-      a.logits[((size_t)bi * a.n_q + kvh * G + h) * a.T + t_begin + tl] = l;
+      for (int v = 0; v < 4; ++v) {
+        const int t = tb + v;
+        if (t < t_end) {
+          const uint32_t szw = a.k_sz[tok0 + t];
+          const float s = sf_h2f(szw), z = sf_h2f(szw >> 16);
+          const float l = a.scale * (z * qsum + (s * scl) * (acc[v] - qsum));
+          a.logits[((size_t)bi * a.n_q + kvh * G + n) * T + t] = l;
+          const float nm = fmaxf(run_m, l);
+          run_z = run_z * __expf(run_m - nm) + __expf(l - nm);
+          run_m = nm;
+        }
+      }
     }
+  }
+  // combine (m, z) over the 4 lane groups of each head, then over the waves
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float om = __shfl_xor(run_m, o, 64), oz = __shfl_xor(run_z, o, 64);
+    const float nm = fmaxf(run_m, om);
+    run_z = (run_m > -INFINITY ? run_z * __expf(run_m - nm) : 0.f) + (om > -INFINITY ? oz * __expf(om - nm) : 0.f);
+    run_m = nm;
+  }
+  if (lane < 16) {
+    st[wave][lane][0] = run_m;
+    st[wave][lane][1] = run_z;
   }
   __syncthreads();
-  // A2: split max; exponentials; Z and sum_t e_t z_t in fp64 (token-parallel)
-  float m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v = -INFINITY;
-    for (int tl = tid; tl < n_here; tl += 256) v = fmaxf(v, lg[h * L + tl]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    if (lane == 0) red[wave][h] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) m[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-  double zs[G], zz[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) zs[h] = zz[h] = 0.0;
-  for (int tl = tid; tl < n_here; tl += 256) {
-    const double zv = (double)sf_h2f(a.v_sz[tok0 + t_begin + tl] >> 16);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float e = __expf(lg[h * L + tl] - m[h]);
-      lg[h * L + tl] = e;
-      zs[h] += (double)e;
-      zz[h] = fma((double)e, zv, zz[h]);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    double v = zs[h], w = zz[h];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      v += __shfl_xor(v, o, 64);
-      w += __shfl_xor(w, o, 64);
-    }
-    if (lane == 0) {
-      dred[wave][h][0] = v;
-      dred[wave][h][1] = w;
-    }
-  }
-  __syncthreads();
-  // A3: sum_t (e_t * s'_t) * c_t[d] in fp64; lane owns dims 2*lane, 2*lane+1
-  double acc0[G], acc1[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) acc0[h] = acc1[h] = 0.0;
-  const float sres = (float)(1u << a.r);
-  const int bit0 = 2 * lane * B;
-  for (int tl = wave; tl < n_here; tl += 4) {
-    const size_t tok = tok0 + t_begin + tl;
-    const uint32_t* vw = (const uint32_t*)(a.v_res + tok * (HD * B / 8));
-    const uint32_t word = vw[bit0 >> 5];
-    const double sv = (double)(sf_h2f(a.v_sz[tok]) * sres);
-    const double c0 = (double)((word >> (bit0 & 31)) & ((1u << B) - 1u));
-    const double c1 = (double)((word >> ((bit0 & 31) + B)) & ((1u << B) - 1u));
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const double we = (double)lg[h * L + tl] * sv;
-      acc0[h] = fma(we, c0, acc0[h]);
-      acc1[h] = fma(we, c1, acc1[h]);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    acc_red[wave][h][2 * lane] = acc0[h];
-    acc_red[wave][h][2 * lane + 1] = acc1[h];
-  }
-  __syncthreads();
-  double* P = a.part + (((size_t)bh * a.splits + split) * G) * (2 + HD);
-  for (int i = tid; i < G * HD; i += 256) {
-    const int h = i / HD, dd = i - h * HD;
-    const double zt = (dred[0][h][1] + dred[1][h][1]) + (dred[2][h][1] + dred[3][h][1]);
-    P[h * (2 + HD) + 2 + dd] =
-        ((acc_red[0][h][dd] + acc_red[1][h][dd]) + (acc_red[2][h][dd] + acc_red[3][h][dd])) + zt;
-  }
   if (tid < G) {
-    P[tid * (2 + HD) + 0] = (double)m[tid];
-    P[tid * (2 + HD) + 1] = (dred[0][tid][0] + dred[1][tid][0]) + (dred[2][tid][0] + dred[3][tid][0]);
+    float m = -INFINITY;
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, st[w][tid][0]);
+    float z = 0.f;
+    for (int w = 0; w < 4; ++w)
+      if (st[w][tid][0] > -INFINITY) z += st[w][tid][1] * __expf(st[w][tid][0] - m);
+    float* P2 = a.k1part + (((size_t)bh * a.s1 + split) * G + tid) * 2;
+    P2[0] = m;
+    P2[1] = z;
   }
 }
 
-// ---- kernel B: merge, select, look up, correct ------------------------------------
-constexpr int BT = 1024;  // threads of kernel B
-
-__device__ __forceinline__ int wg1024_exclusive_scan(int v, int* lds, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) lds[wave] = incl;
-  __syncthreads();
-  int base = 0, sum = 0;
-  for (int w = 0; w < BT / 64; ++w) {
-    const int t = lds[w];
-    if (w < wave) base += t;
-    sum += t;
-  }
-  __syncthreads();
-  *total = sum;
-  return base + incl - v;
-}
-
-template <int B, int G>
-__global__ __launch_bounds__(BT) void attn_select_correct_kernel(AttnArgs a) {
-  __shared__ float s_m[G];
-  __shared__ double s_Z[G], s_dZ[G];
-  __shared__ double s_num[G][HD];
-  __shared__ uint32_t hist[2048];
-  __shared__ int lds[32];
+// ---- select ------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(256) void attn_select_kernel(AttnArgs a) {
+  __shared__ uint32_t lh[NBINS];
+  __shared__ float s_m[G], s_iz[G], s_mref[G];
+  __shared__ float red[4];
+  __shared__ int lds[16];
   __shared__ float qf[G][HD];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
+  const int chunk = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
   const int T = a.T, ks = a.k_sel;
   const int KS = ks > 0 ? ks : 1;
-  int* sel = a.lists + (size_t)bh * 3 * KS;
-  int* hit_t = sel + KS;
-  int* hit_s = sel + 2 * KS;
-  double* ee = a.ee + (size_t)bh * KS * G * 2;
 
-  // 1. merge split partials (fp64); split s is scaled by f_s = exp(m_s - m)
-  const double* P = a.part + (size_t)bh * a.splits * G * (2 + HD);
-  if (tid < G) {
+  // global softmax statistics of the resident logits
+  for (int h = 0; h < G; ++h) {
     float m = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) m = fmaxf(m, (float)P[(s * G + tid) * (2 + HD)]);
-    double z = 0.0;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ms = (float)P[(s * G + tid) * (2 + HD)];
-      if (ms > -INFINITY) z += (double)__expf(ms - m) * P[(s * G + tid) * (2 + HD) + 1];
+    for (int s = tid; s < a.s1; s += 256) m = fmaxf(m, a.k1part[(((size_t)bh * a.s1 + s) * G + h) * 2]);
+    m = wg_max(m, red);
+    float z = 0.f;
+    for (int s = tid; s < a.s1; s += 256) {
+      const float* P2 = a.k1part + (((size_t)bh * a.s1 + s) * G + h) * 2;
+      if (P2[0] > -INFINITY) z += P2[1] * __expf(P2[0] - m);
     }
-    s_m[tid] = m;
-    s_Z[tid] = z;
-    s_dZ[tid] = 0.0;
-  }
-  for (int i = tid; i < G * HD; i += BT) {
-    const int h = i / HD, d = i - h * HD;
-    qf[h][d] = (float)__builtin_bit_cast(_Float16, a.q[((size_t)bi * a.n_q + kvh * G + h) * HD + d]);
-  }
-  __syncthreads();
-  for (int i = tid; i < G * HD; i += BT) {
-    const int h = i / HD, d = i - h * HD;
-    double n = 0.0;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ms = (float)P[(s * G + h) * (2 + HD)];
-      if (ms > -INFINITY) n += (double)__expf(ms - s_m[h]) * P[(s * G + h) * (2 + HD) + 2 + d];
-    }
-    s_num[h][d] = n;
-  }
-  __syncthreads();
-
-  if (ks > 0) {
-    // 2. selection
-    if (a.sel_in) {
-      for (int j = tid; j < ks; j += BT) sel[j] = a.sel_in[(size_t)bh * ks + j];
-    } else {
-      float* sc = a.scores + (size_t)bh * T;
-      float inv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) inv[h] = (float)(1.0 / s_Z[h]);
-      for (int t = tid; t < T; t += BT) {
-        float v = 0.f;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          v += expf(a.logits[((size_t)bi * a.n_q + kvh * G + h) * T + t] - s_m[h]) * inv[h];
-        sc[t] = v;
-      }
-      __threadfence();
-      __syncthreads();
-      __threadfence();
-      // radix select over the fp32 bit patterns (scores are >= 0): 11 + 11 + 10 bits
-      uint32_t prefix = 0, above = 0;
-      int need = ks;
-      const int shifts[3] = {21, 10, 0};
-      const int widths[3] = {11, 11, 10};
-      for (int pass = 0; pass < 3; ++pass) {
-        const int sh = shifts[pass], nb = 1 << widths[pass];
-        for (int i = tid; i < 2048; i += BT) hist[i] = 0;
-        __syncthreads();
-        const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (sh + widths[pass]));
-        for (int t = tid; t < T; t += BT) {
-          const uint32_t key = __float_as_uint(sc[t]);
-          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        // suffix sums over nb bins: thread i takes bins 2i, 2i+1 in reverse order
-        int v0 = 0, v1 = 0;
-        const int i0 = nb - 1 - 2 * tid, i1 = i0 - 1;
-        if (i0 >= 0) v0 = (int)hist[i0];
-        if (i1 >= 0) v1 = (int)hist[i1];
-        int tot;
-        const int ex = wg1024_exclusive_scan(v0 + v1, lds, &tot);
-        if (i0 >= 0) hist[i0] = (uint32_t)(ex + v0);
-        if (i1 >= 0) hist[i1] = (uint32_t)(ex + v0 + v1);
-        __syncthreads();
-        if (tid == 0) lds[31] = 0;
-        __syncthreads();
-        for (int i = tid; i < nb; i += BT) {
-          if ((int)hist[i] >= need && (i + 1 == nb || (int)hist[i + 1] < need)) lds[31] = i;
-        }
-        __syncthreads();
-        const int bin = lds[31];
-        const int more = (bin + 1 < nb) ? (int)hist[bin + 1] : 0;
-        __syncthreads();
-        above += more;
-        need -= more;
-        prefix |= (uint32_t)bin << sh;
-      }
-      const uint32_t thr = prefix;  // exact key of the k-th largest score
-      // ordered compaction: thread owns tokens [tid*tpt, (tid+1)*tpt)
-      const int tpt = (T + BT - 1) / BT;
-      const int t0 = tid * tpt, t1 = min(T, t0 + tpt);
-      int gt = 0, eq = 0;
-      for (int t = t0; t < t1; ++t) {
-        const uint32_t key = __float_as_uint(sc[t]);
-        gt += key > thr;
-        eq += key == thr;
-      }
-      int tot;
-      const int eq_before = wg1024_exclusive_scan(eq, lds, &tot);
-      const int take_eq = max(0, min(eq, need - eq_before));
-      int off = wg1024_exclusive_scan(gt + take_eq, lds, &tot);
-      int seen = 0;
-      for (int t = t0; t < t1; ++t) {
-        const uint32_t key = __float_as_uint(sc[t]);
-        if (key > thr) sel[off++] = t;
-        else if (key == thr) {
-          if (seen < take_eq) sel[off++] = t;
-          ++seen;
-        }
-      }
-    }
-    __threadfence();
-    __syncthreads();
-    __threadfence();
-    // 3. lookup (units of this (batch, kv head)), in selection order
-    const size_t unit0 = (size_t)bh * a.t_cap;
+    z = wg_sum(z, red);
     if (tid == 0) {
-      int base = -1;
-      if (a.pool.log_count) {
-        const uint32_t bse = atomicAdd(a.pool.log_count, (uint32_t)ks);
-        base = (bse + (uint32_t)ks <= (uint32_t)a.pool.log_cap) ? (int)bse : -1;
-      }
-      lds[30] = base;
+      s_m[h] = m;
+      s_iz[h] = 1.f / z;
+    }
+  }
+  __syncthreads();
+
+  if (ks == 0) {
+    if (chunk == 0 && tid < G) a.mref[bh * G + tid] = s_m[tid];
+    if (chunk == 0 && tid == 0) a.n_hit[bh] = 0;
+    return;
+  }
+
+  int* sel = a.sel + (size_t)bh * KS;
+  if (a.sel_in == nullptr) {
+    // scores of this chunk + first-level histogram
+    for (int i = tid; i < NBINS; i += 256) lh[i] = 0;
+    __syncthreads();
+    const int c0 = chunk * SPLIT2, c1 = min(T, c0 + SPLIT2);
+    float* sc = a.scores + (size_t)bh * T;
+    for (int t = c0 + tid; t < c1; t += 256) {
+      float v = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        v += expf(a.logits[((size_t)bi * a.n_q + kvh * G + h) * T + t] - s_m[h]) * s_iz[h];
+      sc[t] = v;
+      atomicAdd(&lh[__float_as_uint(v) >> 21], 1u);
     }
     __syncthreads();
-    const int base = lds[30];
-    const int jpt = (ks + BT - 1) / BT;
-    const int j0 = tid * jpt, j1 = min(ks, j0 + jpt);
-    int nh = 0;
-    for (int j = j0; j < j1; ++j) {
-      const int t = sel[j];
-      const bool ok = t >= 0 && t < T;
-      const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
-      nh += slot >= 0;
-    }
-    int n_hits;
-    int pos = wg1024_exclusive_scan(nh, lds, &n_hits);
-    for (int j = j0; j < j1; ++j) {
-      const int t = sel[j];
-      const bool ok = t >= 0 && t < T;
-      const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
-      if (a.sel_out) a.sel_out[(size_t)bh * ks + j] = t;
-      if (a.hit_out) a.hit_out[(size_t)bh * ks + j] = slot;
-      if (base >= 0) {
-        a.pool.log_units[base + j] = ok ? (int)(unit0 + t) : -1;
-        a.pool.log_slots[base + j] = slot;
-      }
-      if (slot >= 0) {
-        hit_t[pos] = t;
-        hit_s[pos] = slot;
-        ++pos;
-      }
-    }
+    for (int i = tid; i < NBINS; i += 256)
+      if (lh[i]) atomicAdd(&a.hist[(size_t)bh * NBINS + i], lh[i]);
     __threadfence();
     __syncthreads();
-    __threadfence();
-    // 4. per hit: logit change from the K refinement, e and e'
+    if (tid == 0) lds[8] = atomicAdd(&a.cnt[bh * 2], 1u) == (uint32_t)(a.s2 - 1);
+    __syncthreads();
+    if (!lds[8]) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // ---- last workgroup of this KV head: exact threshold ----
+    for (int i = tid; i < NBINS; i += 256) lh[i] = a.hist[(size_t)bh * NBINS + i];
+    __syncthreads();
+    wg_suffix_sum(lh, NBINS, lds);
+    uint32_t prefix = 0;
+    int need = ks;
+    {
+      const int bin = wg_find_threshold(lh, NBINS, (uint32_t)need, lds + 4);
+      need -= bin + 1 < NBINS ? (int)lh[bin + 1] : 0;
+      prefix = (uint32_t)bin << 21;
+      __syncthreads();
+    }
+    // levels 2 and 3: bits 20..10 and 9..0 of the keys that share the prefix
+    for (int level = 0; level < 2; ++level) {
+      const int sh = level == 0 ? 10 : 0, nb = level == 0 ? 2048 : 1024;
+      const uint32_t pmask = level == 0 ? 0xFFE00000u : 0xFFFFFC00u;
+      for (int i = tid; i < NBINS; i += 256) lh[i] = 0;
+      __syncthreads();
+      for (int t = tid; t < T; t += 256) {
+        const uint32_t key = __float_as_uint(sc[t]);
+        if ((key & pmask) == prefix) atomicAdd(&lh[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      wg_suffix_sum(lh, NBINS, lds);
+      const int bin = wg_find_threshold(lh, nb, (uint32_t)need, lds + 4);
+      need -= bin + 1 < nb ? (int)lh[bin + 1] : 0;
+      prefix |= (uint32_t)bin << sh;
+      __syncthreads();
+    }
+    const uint32_t thr = prefix;
+    // ordered compaction: thread owns tokens [tid*tpt, (tid+1)*tpt)
+    const int tpt = (T + 255) / 256;
+    const int t0 = tid * tpt, t1 = min(T, t0 + tpt);
+    int gt = 0, eq = 0;
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t key = __float_as_uint(sc[t]);
+      gt += key > thr;
+      eq += key == thr;
+    }
+    int tot;
+    const int eq_before = wg_exclusive_scan(eq, lds, &tot);
+    const int take_eq = max(0, min(eq, need - eq_before));
+    int off = wg_exclusive_scan(gt + take_eq, lds, &tot);
+    int seen = 0;
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t key = __float_as_uint(sc[t]);
+      if (key > thr) {
+        sel[off++] = t;
+      } else if (key == thr) {
+        if (seen < take_eq) sel[off++] = t;
+        ++seen;
+      }
+    }
+  } else {
+    if (chunk != 0) return;
+    for (int j = tid; j < ks; j += 256) sel[j] = a.sel_in[(size_t)bh * ks + j];
+  }
+  __threadfence();
+  __syncthreads();
+  __threadfence();
+
+  // ---- lookup in selection order ----
+  const size_t unit0 = (size_t)bh * a.t_cap;
+  int* hit_t = a.hit_t + (size_t)bh * KS;
+  int* hit_s = a.hit_s + (size_t)bh * KS;
+  if (tid == 0) {
+    int base = -1;
+    if (a.pool.log_count) {
+      const uint32_t bse = atomicAdd(a.pool.log_count, (uint32_t)ks);
+      base = (bse + (uint32_t)ks <= (uint32_t)a.pool.log_cap) ? (int)bse : -1;
+    }
+    lds[9] = base;
+  }
+  __syncthreads();
+  const int base = lds[9];
+  const int jpt = (ks + 255) / 256;
+  const int j0 = tid * jpt, j1 = min(ks, j0 + jpt);
+  int nh = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int t = sel[j];
+    const int slot = (a.pool.unit2slot && t >= 0 && t < T) ? a.pool.unit2slot[unit0 + t] : -1;
+    nh += slot >= 0;
+  }
+  int n_hits;
+  int pos = wg_exclusive_scan(nh, lds, &n_hits);
+  for (int j = j0; j < j1; ++j) {
+    const int t = sel[j];
+    const bool ok = t >= 0 && t < T;
+    const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
+    if (a.sel_out) a.sel_out[(size_t)bh * ks + j] = t;
+    if (a.hit_out) a.hit_out[(size_t)bh * ks + j] = slot;
+    if (base >= 0) {
+      a.pool.log_units[base + j] = ok ? (int)(unit0 + t) : -1;
+      a.pool.log_slots[base + j] = slot;
+    }
+    if (slot >= 0) {
+      hit_t[pos] = t;
+      hit_s[pos] = slot;
+      ++pos;
+    }
+  }
+  for (int i = tid; i < G * HD; i += 256) {
+    const int h = i / HD, d = i - h * HD;
+    qf[h][d] = h2f16(a.q[((size_t)bi * a.n_q + kvh * G + h) * HD + d]);
+  }
+  if (tid < G) s_mref[tid] = s_m[tid];
+  __threadfence();
+  __syncthreads();
+  __threadfence();
+  // ---- refined logits of the hit tokens: l' = l + scale * s_K * (q . cK_lo) ----
+  const int r = a.r;
+  float mloc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
+  for (int m = tid; m < n_hits * G; m += 256) {
+    const int hh = m % G, mi = m / G;
+    const int t = hit_t[mi];
+    const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)hit_s[mi] * a.pool.unit_bytes);
+    float dot = 0.f;
+    for (int i = 0; i < HD; ++i) dot = fmaf(qf[hh][i], (float)field(unit, i * r, r), dot);
+    const float s = sf_h2f(a.k_sz[unit0 + t]);
+    float* lp = a.logits + ((size_t)bi * a.n_q + kvh * G + hh) * T + t;
+    const float l2 = *lp + a.scale * (s * dot);
+    *lp = l2;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (h == hh) mloc[h] = fmaxf(mloc[h], l2);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float v = wg_max(mloc[h], red);
+    if (tid == 0) s_mref[h] = fmaxf(s_mref[h], v);
+  }
+  __syncthreads();
+  if (tid < G) a.mref[bh * G + tid] = s_mref[tid];
+  if (tid == 0) a.n_hit[bh] = n_hits;
+}
+
+// ---- pv: weighted value sums with the final weights ------------------------------
+template <int B, int G>
+__global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
+  __shared__ float w[G][SPLIT3];
+  __shared__ float accr[4][G][HD];
+  __shared__ float red[4];
+  __shared__ float s_z[G], s_zz[G], s_m[G];
+  __shared__ int flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
+  const int T = a.T;
+  const int t_begin = split * SPLIT3, t_end = min(T, t_begin + SPLIT3);
+  const int n_here = max(0, t_end - t_begin);
+  const size_t tok0 = (size_t)bh * a.t_cap;
+  if (tid < G) s_m[tid] = a.mref[bh * G + tid];
+  __syncthreads();
+  // weights, their sum, and the sum of weight * zero-point per head
+  float zs[G], zz[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) zs[h] = zz[h] = 0.f;
+  for (int tl = tid; tl < n_here; tl += 256) {
+    const int t = t_begin + tl;
+    const float zv = sf_h2f(a.v_sz[tok0 + t] >> 16);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float e = __expf(a.logits[((size_t)bi * a.n_q + kvh * G + h) * T + t] - s_m[h]);
+      w[h][tl] = e;
+      zs[h] += e;
+      zz[h] = fmaf(e, zv, zz[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float v1 = wg_sum(zs[h], red);
+    if (tid == 0) s_z[h] = v1;
+    const float v2 = wg_sum(zz[h], red);
+    if (tid == 0) s_zz[h] = v2;
+  }
+  __syncthreads();
+  // sum_t (w_t * s'_t) * c_t[d]; lane owns dims 2*lane, 2*lane+1; wave w takes tokens w, w+4, ...
+  float acc0[G], acc1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc0[h] = acc1[h] = 0.f;
+  const float sres = (float)(1u << a.r);
+  const int bit0 = 2 * lane * B;
+  constexpr int U = 8;
+  for (int tl0 = wave; tl0 < n_here; tl0 += 4 * U) {
+    uint32_t word[U], szw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tl = tl0 + 4 * u;
+      if (tl < n_here) {
+        const size_t tok = tok0 + t_begin + tl;
+        word[u] = ((const uint32_t*)(a.v_res + tok * (HD * B / 8)))[bit0 >> 5];
+        szw[u] = a.v_sz[tok];
+      } else {
+        word[u] = 0;
+        szw[u] = 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tl = tl0 + 4 * u;
+      if (tl < n_here) {
+        const float sv = sf_h2f(szw[u]) * sres;
+        const float c0 = (float)((word[u] >> (bit0 & 31)) & ((1u << B) - 1u));
+        const float c1 = (float)((word[u] >> ((bit0 & 31) + B)) & ((1u << B) - 1u));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float we = w[h][tl] * sv;
+          acc0[h] = fmaf(we, c0, acc0[h]);
+          acc1[h] = fmaf(we, c1, acc1[h]);
+        }
+      }
+    }
+  }
+  // refinement of the hit tokens that fall in this split: + w * s_V * cV_lo
+  if (wave == 0 && a.k_sel > 0) {
+    const int nh = a.n_hit[bh];
+    const int KS = a.k_sel;
+    const int* hit_t = a.hit_t + (size_t)bh * KS;
+    const int* hit_s = a.hit_s + (size_t)bh * KS;
     const int r = a.r;
-    for (int m = tid; m < n_hits * G; m += BT) {
-      const int hh = m / n_hits, mi = m - hh * n_hits;
-      const int t = hit_t[mi];
-      const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)hit_s[mi] * a.pool.unit_bytes);
-      float dot = 0.f;
-      for (int i = 0; i < HD; ++i) dot = fmaf(qf[hh][i], (float)field(unit, i * r, r), dot);
-      const uint32_t szk = a.k_sz[unit0 + t];
-      const float l = a.logits[((size_t)bi * a.n_q + kvh * G + hh) * T + t];
-      const float l2 = l + a.scale * (sf_h2f(szk) * dot);
-      // the weight the stream pass gave t: exp(l - m_split) scaled by exp(m_split - m)
-      const int sp = t / a.split_len;
-      const float ms = (float)P[(sp * G + hh) * (2 + HD)];
-      const double w_old = (double)__expf(ms - s_m[hh]) * (double)__expf(l - ms);
-      ee[2 * (mi * G + hh)] = w_old;
-      ee[2 * (mi * G + hh) + 1] = (double)__expf(l2 - s_m[hh]);
-    }
-    __threadfence();
-    __syncthreads();
-    __threadfence();
-    if (tid < G) {
-      double dz = 0.0;
-      for (int mi = 0; mi < n_hits; ++mi) dz += ee[2 * (mi * G + tid) + 1] - ee[2 * (mi * G + tid)];
-      s_dZ[tid] = dz;
-    }
-    // 5. numerator correction, thread per (head, dim):
-    //    N' = N - w_old * V_b,t + e' * V_B,t  over the hit tokens t
-    const double sres = (double)(1u << r);
-    for (int i = tid; i < G * HD; i += BT) {
-      const int hh = i / HD, d = i - hh * HD;
-      double dn = 0.0;
-      for (int mi = 0; mi < n_hits; ++mi) {
-        const int t = hit_t[mi];
-        const uint32_t* vw = (const uint32_t*)(a.v_res + (unit0 + t) * (HD * B / 8));
-        const uint32_t szv = a.v_sz[unit0 + t];
-        const double sv = (double)sf_h2f(szv), zv = (double)sf_h2f(szv >> 16);
-        const double chi = (double)field(vw, d * B, B);
-        const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)hit_s[mi] * a.pool.unit_bytes);
-        const double clo = (double)field(unit, HD * r + d * r, r);
-        const double w_old = ee[2 * (mi * G + hh)], e2 = ee[2 * (mi * G + hh) + 1];
-        const double vb = zv + (sv * sres) * chi;
-        dn += e2 * (vb + sv * clo) - w_old * vb;
+    for (int m = 0; m < nh; ++m) {
+      const int t = hit_t[m];
+      if (t < t_begin || t >= t_end) continue;
+      const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)hit_s[m] * a.pool.unit_bytes);
+      const float sv = sf_h2f(a.v_sz[tok0 + t]);
+      const float c0 = (float)field(unit, HD * r + 2 * lane * r, r);
+      const float c1 = (float)field(unit, HD * r + (2 * lane + 1) * r, r);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float we = w[h][t - t_begin] * sv;
+        acc0[h] = fmaf(we, c0, acc0[h]);
+        acc1[h] = fmaf(we, c1, acc1[h]);
       }
-      s_num[hh][d] += dn;
     }
-    __syncthreads();
   }
-  // 6. output
-  for (int i = tid; i < G * HD; i += BT) {
-    const int hh = i / HD, d = i - hh * HD;
-    a.out[((size_t)bi * a.n_q + kvh * G + hh) * HD + d] = (float)(s_num[hh][d] / (s_Z[hh] + s_dZ[hh]));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    accr[wave][h][2 * lane] = acc0[h];
+    accr[wave][h][2 * lane + 1] = acc1[h];
+  }
+  __syncthreads();
+  float* P3 = a.k3part + (((size_t)bh * a.s3 + split) * G) * (1 + HD);
+  for (int i = tid; i < G * HD; i += 256) {
+    const int h = i / HD, d = i - h * HD;
+    P3[h * (1 + HD) + 1 + d] = ((accr[0][h][d] + accr[1][h][d]) + (accr[2][h][d] + accr[3][h][d])) + s_zz[h];
+  }
+  if (tid < G) P3[tid * (1 + HD)] = s_z[tid];
+  // last workgroup of this KV head: out = sum_s N_s / sum_s Z_s
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) flag = atomicAdd(&a.cnt[bh * 2 + 1], 1u) == (uint32_t)(a.s3 - 1);
+  __syncthreads();
+  if (!flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const float* Pb = a.k3part + (size_t)bh * a.s3 * G * (1 + HD);
+  for (int i = tid; i < G * HD; i += 256) {
+    const int h = i / HD, d = i - h * HD;
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < a.s3; ++s) {
+      num += Pb[(s * G + h) * (1 + HD) + 1 + d];
+      den += Pb[(s * G + h) * (1 + HD)];
+    }
+    a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
   }
 }
 
-int choose_splits(int T) {
-  int s = (T + 511) / 512;
-  if (s < 1) s = 1;
-  if (s > MAX_SPLITS) s = MAX_SPLITS;
-  return s;
-}
-
-size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t* o_log, size_t* o_sc,
-                   size_t* o_part, size_t* o_lists, size_t* o_ee) {
+size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12]) {
   const int G = n_kv > 0 ? n_q / n_kv : 1;
-  const int S = choose_splits(T);
-  size_t off = sf_align256(sizeof(WsControl));
-  *o_log = off;
-  off += sf_align256((size_t)batch * n_q * T * 4);
-  *o_sc = off;
-  off += sf_align256((size_t)batch * n_kv * T * 4);
-  *o_part = off;
-  off += sf_align256((size_t)batch * n_kv * S * G * (2 + HD) * 8);
+  const int bh = batch * n_kv;
+  const size_t s1 = (T + SPLIT1 - 1) / SPLIT1, s3 = (T + SPLIT3 - 1) / SPLIT3;
   const size_t KS = k_sel > 0 ? k_sel : 1;
-  *o_lists = off;
-  off += sf_align256((size_t)batch * n_kv * 3 * KS * 4);
-  *o_ee = off;
-  off += sf_align256((size_t)batch * n_kv * KS * G * 2 * 8);
-  return off;
+  const size_t sizes[12] = {
+      (size_t)batch * n_q * T * 4,    // logits
+      (size_t)bh * T * 4,             // scores
+      (size_t)bh * s1 * G * 2 * 4,    // k1part
+      (size_t)bh * NBINS * 4,         // hist
+      (size_t)bh * 2 * 4,             // cnt
+      (size_t)bh * KS * 4,            // sel
+      (size_t)bh * KS * 4,            // hit_t
+      (size_t)bh * KS * 4,            // hit_s
+      (size_t)bh * 4,                 // n_hit
+      (size_t)bh * G * 4,             // mref
+      (size_t)bh * s3 * G * (1 + HD) * 4,  // k3part
+      0};
+  size_t o = sf_align256(sizeof(WsControl));
+  for (int i = 0; i < 12; ++i) {
+    off[i] = o;
+    o += sf_align256(sizes[i]);
+  }
+  return o;
 }
 
 template <int B, int G>
 sf_status launch_attn(AttnArgs& a, hipStream_t s) {
-  const size_t lds_a = (size_t)G * a.split_len * 4;
-  SF_REQUIRE(lds_a + (size_t)4 * G * HD * 8 <= 60 * 1024, SF_EUNSUPPORTED, "split too long");
-  hipLaunchKernelGGL((attn_stream_kernel<B, G>), dim3(a.splits, a.batch * a.n_kv), dim3(256), lds_a, s, a);
+  const int bh = a.batch * a.n_kv;
+  hipLaunchKernelGGL((attn_qk_kernel<B, G>), dim3(a.s1, bh), dim3(256), 0, s, a);
   SF_LAUNCH_CHECK();
-  hipLaunchKernelGGL((attn_select_correct_kernel<B, G>), dim3(a.batch * a.n_kv), dim3(BT), 0, s, a);
+  hipLaunchKernelGGL((attn_select_kernel<G>), dim3(a.s2, bh), dim3(256), 0, s, a);
+  SF_LAUNCH_CHECK();
+  hipLaunchKernelGGL((attn_pv_kernel<B, G>), dim3(a.s3, bh), dim3(256), 0, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }
@@ -525,8 +618,8 @@ sf_status dispatch_g(AttnArgs& a, hipStream_t s) {
 
 extern "C" size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                           int32_t t_len, int32_t k_sel) {
-  size_t a, b, c, d, e;
-  return attn_layout(batch, n_q_heads, n_kv_heads, t_len, k_sel, &a, &b, &c, &d, &e);
+  size_t off[12];
+  return attn_layout(batch, n_q_heads, n_kv_heads, t_len, k_sel, off);
 }
 
 extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
@@ -557,18 +650,26 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
   a.t_cap = kv->t_cap;
   a.b = kv->fmt.b;
   a.r = kv->fmt.r;
-  a.splits = choose_splits(a.T);
-  a.split_len = ((a.T + a.splits - 1) / a.splits + 63) / 64 * 64;
   a.k_sel = k_sel;
   a.scale = softmax_scale;
-  size_t o_log, o_sc, o_part, o_lists, o_ee;
-  const size_t need = attn_layout(a.batch, a.n_q, a.n_kv, a.T, k_sel, &o_log, &o_sc, &o_part, &o_lists, &o_ee);
+  a.s1 = (a.T + SPLIT1 - 1) / SPLIT1;
+  a.s2 = (a.T + SPLIT2 - 1) / SPLIT2;
+  a.s3 = (a.T + SPLIT3 - 1) / SPLIT3;
+  size_t off[12];
+  const size_t need = attn_layout(a.batch, a.n_q, a.n_kv, a.T, k_sel, off);
   SF_REQUIRE(ws->bytes >= need, SF_ENOMEM, "workspace too small");
-  a.logits = (float*)(ws->base + o_log);
-  a.scores = (float*)(ws->base + o_sc);
-  a.part = (double*)(ws->base + o_part);
-  a.lists = (int32_t*)(ws->base + o_lists);
-  a.ee = (double*)(ws->base + o_ee);
+  uint8_t* w = ws->base;
+  a.logits = (float*)(w + off[0]);
+  a.scores = (float*)(w + off[1]);
+  a.k1part = (float*)(w + off[2]);
+  a.hist = (uint32_t*)(w + off[3]);
+  a.cnt = (uint32_t*)(w + off[4]);
+  a.sel = (int32_t*)(w + off[5]);
+  a.hit_t = (int32_t*)(w + off[6]);
+  a.hit_s = (int32_t*)(w + off[7]);
+  a.n_hit = (int32_t*)(w + off[8]);
+  a.mref = (float*)(w + off[9]);
+  a.k3part = (float*)(w + off[10]);
   a.sel_in = sel_in;
   a.sel_out = sel_out;
   a.hit_out = hit_out;

@@ -207,9 +207,11 @@ sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out) {
   HostPool& p = c->pools[pool];
   out->unit2slot = p.d_unit2slot;
   out->slots = p.d_slots;
-  out->log_units = p.d_log_units;
-  out->log_slots = p.d_log_slots;
-  out->log_count = p.d_log_count;
+  if (!p.resident) {  // a resident pool never misses: nothing to record
+    out->log_units = p.d_log_units;
+    out->log_slots = p.d_log_slots;
+    out->log_count = p.d_log_count;
+  }
   out->log_cap = p.log_cap;
   out->unit_bytes = (int32_t)p.d.unit_bytes;
   out->n_units = p.d.n_units;
@@ -333,6 +335,13 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
   SF_REQUIRE(c, SF_EINVAL, "null cache");
   hipStream_t compute = (hipStream_t)compute_, side = (hipStream_t)side_;
   const int64_t t = c->step;
+  bool any = false;
+  for (const auto& p : c->pools) any = any || !p.resident;
+  if (!any) {  // only resident pools: nothing is ever missing
+    c->step = t + 1;
+    if (n_filled) *n_filled = 0;
+    return SF_OK;
+  }
   const int np = (int)c->pools.size();
   int64_t filled = 0;
   bool overflow = false;

@@ -49,7 +49,7 @@ struct GemvArgs {
   int32_t* ws_hit_k;     // [n_ops][k_sel]
   int32_t* ws_hit_slot;  // [n_ops][k_sel]
   int32_t* ws_nhit;      // [n_ops]
-  int32_t n_ops, k_in, batch, batch_off, k_sel, r, total_wg, do_log;
+  int32_t n_ops, k_in, batch, batch_off, k_sel, r, total_tiles, do_log;
 };
 
 // ---- code layouts ----------------------------------------------------------------
@@ -228,8 +228,10 @@ __device__ void gemv_select_and_lookup(const GemvArgs& a, uint32_t* hist, int* l
 }
 
 // ---- the GEMV kernel -------------------------------------------------------------
-// Workgroup = 4 waves; wave w owns rows [tile*4R + w*R, +R); lane l owns chunks
-// l, l+64, ...  NB batch rows [batch_off, batch_off + NB) per launch.
+// Persistent workgroups of 4 waves.  Row tiles of 4R rows (R per wave) are dealt to
+// workgroups round-robin: workgroup g takes tiles g, g + grid, ...  Within a tile,
+// lane l of a wave owns chunks l, l+64, ... of each of the wave's R rows.  x is
+// staged once per workgroup.  NB batch rows [batch_off, batch_off + NB) per launch.
 template <class C, int B, int R, int NB>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
@@ -242,37 +244,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int K = a.k_in;
   const int nchunks = K / C::CODES;
   const int xpairs = K / 2;
-  uint32_t* xs = smem;                              // [NB][K/2] fp16 pairs
-  float* xsum = (float*)(smem + NB * xpairs);       // [NB][nchunks]
-
-  int op = 0;
-  for (int i = 1; i < a.n_ops; ++i)
-    if ((int)blockIdx.x >= a.ops[i].tile_begin) op = i;
-  const GemvOpDev o = a.ops[op];
-  const int tile = (int)blockIdx.x - o.tile_begin;
+  uint32_t* xs = smem;                         // [NB][K/2] fp16 pairs
+  float* xsum = (float*)(smem + NB * xpairs);  // [NB][nchunks]
   const bool refine = a.k_sel > 0;
+  const int rows_wg = 4 * R;
 
   if (tid == 0) s_lds[7] = refine ? (atomicCAS(&a.ctl->sel_state, 0u, 1u) == 0u) : 0;
 
-  // stage x in pair order and the per-chunk sums of x
+  // stage x in pair order; per-chunk sums of x by the lanes holding the chunk's pairs
   for (int bb = 0; bb < NB; ++bb) {
     const uint16_t* xr = a.x + (size_t)(a.batch_off + bb) * K;
-    for (int p = tid; p < xpairs; p += 256) {
-      const int c = p / C::PAIRS, j = p - c * C::PAIRS;
-      const int kb = c * C::CODES;
-      xs[bb * xpairs + p] = (uint32_t)xr[kb + C::pair_k0(j)] | ((uint32_t)xr[kb + C::pair_k1(j)] << 16);
+    for (int p0 = 0; p0 < xpairs; p0 += 256) {
+      const int p = p0 + tid;
+      float v = 0.f;
+      if (p < xpairs) {
+        const int c = p / C::PAIRS, j = p - c * C::PAIRS;
+        const int kb = c * C::CODES;
+        const uint32_t pr = (uint32_t)xr[kb + C::pair_k0(j)] | ((uint32_t)xr[kb + C::pair_k1(j)] << 16);
+        xs[bb * xpairs + p] = pr;
+        const h2_t h = as_h2(pr);
+        v = (float)h.x + (float)h.y;
+      }
+#pragma unroll
+      for (int o = C::PAIRS / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, C::PAIRS);
+      if (p < xpairs && (p % C::PAIRS) == 0) xsum[bb * nchunks + p / C::PAIRS] = v;
     }
   }
-  __syncthreads();
-  for (int bb = 0; bb < NB; ++bb)
-    for (int c = tid; c < nchunks; c += 256) {
-      float s = 0.f;
-      for (int j = 0; j < C::PAIRS; ++j) {
-        const h2_t h = as_h2(xs[bb * xpairs + c * C::PAIRS + j]);
-        s += (float)h.x + (float)h.y;
-      }
-      xsum[bb * nchunks + c] = s;
-    }
   __syncthreads();
 
   const bool selector = s_lds[7] != 0;
@@ -283,136 +280,151 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     if (tid == 0) __hip_atomic_store(&a.ctl->sel_state, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // resident GEMV
-  const int rows_wg = 4 * R;
-  const int row0 = tile * rows_wg + wave * R;
   const size_t rowbytes = (size_t)K * B / 8;
   const int ngr = K / 128;
   const float scl = (float)(1u << (a.r + B));
-  float acc[NB][R];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[bb][r] = 0.f;
 
-  for (int c = lane; c < nchunks; c += 64) {
-    uint32_t cw[R][C::WORDS];
-    uint32_t szw[R];
+  // resident GEMV over this workgroup's tiles; y = x W_res^T written per tile
+  for (int tile_g = blockIdx.x; tile_g < a.total_tiles; tile_g += gridDim.x) {
+    int op = 0;
+    for (int i = 1; i < a.n_ops; ++i)
+      if (tile_g >= a.ops[i].tile_begin) op = i;
+    const GemvOpDev& o = a.ops[op];
+    const int tile = tile_g - o.tile_begin;
+    const int row0 = tile * rows_wg + wave * R;
+    float acc[NB][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = row0 + r;
-      if (row < o.n_out) {
-        const uint32_t* src = (const uint32_t*)(o.res + row * rowbytes + (size_t)c * (4 * C::WORDS));
-        if constexpr (C::WORDS == 4) {
-          const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
-          cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[bb][r] = 0.f;
+
+    for (int c = lane; c < nchunks; c += 64) {
+      uint32_t cw[R][C::WORDS];
+      uint32_t szw[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row < o.n_out) {
+          const uint32_t* src = (const uint32_t*)(o.res + row * rowbytes + (size_t)c * (4 * C::WORDS));
+          if constexpr (C::WORDS == 4) {
+            const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
+            cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
+          } else {
+#pragma unroll
+            for (int w = 0; w < C::WORDS; ++w) cw[r][w] = __builtin_nontemporal_load(src + w);
+          }
+          szw[r] = o.sz[(size_t)row * ngr + (c * C::CODES) / 128];
         } else {
 #pragma unroll
-          for (int w = 0; w < C::WORDS; ++w) cw[r][w] = __builtin_nontemporal_load(src + w);
+          for (int w = 0; w < C::WORDS; ++w) cw[r][w] = 0;
+          szw[r] = 0;
         }
-        szw[r] = o.sz[(size_t)row * ngr + (c * C::CODES) / 128];
-      } else {
+      }
 #pragma unroll
-        for (int w = 0; w < C::WORDS; ++w) cw[r][w] = 0;
-        szw[r] = 0;
+      for (int bb = 0; bb < NB; ++bb) {
+        uint32_t xv[C::PAIRS];
+        const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
+#pragma unroll
+        for (int j = 0; j < C::PAIRS / 4; ++j) {
+          const u32x4 v = xp[j];
+          xv[4 * j] = v.x; xv[4 * j + 1] = v.y; xv[4 * j + 2] = v.z; xv[4 * j + 3] = v.w;
+        }
+        const float X = xsum[bb * nchunks + c];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float d = 0.f;
+#pragma unroll
+          for (int j = 0; j < C::PAIRS; ++j)
+            d = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[r], j)), as_h2(xv[j]), d, false);
+          const float s = sf_h2f(szw[r]), z = sf_h2f(szw[r] >> 16);
+          acc[bb][r] += (s * scl) * (d - X) + z * X;
+        }
       }
     }
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      uint32_t xv[C::PAIRS];
-      const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
-#pragma unroll
-      for (int j = 0; j < C::PAIRS / 4; ++j) {
-        const u32x4 v = xp[j];
-        xv[4 * j] = v.x; xv[4 * j + 1] = v.y; xv[4 * j + 2] = v.z; xv[4 * j + 3] = v.w;
-      }
-      const float X = xsum[bb * nchunks + c];
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        float d = 0.f;
+        float v = acc[bb][r];
 #pragma unroll
-        for (int j = 0; j < C::PAIRS; ++j)
-          d = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[r], j)), as_h2(xv[j]), d, false);
-        const float s = sf_h2f(szw[r]), z = sf_h2f(szw[r] >> 16);
-        acc[bb][r] += (s * scl) * (d - X) + z * X;
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        acc[bb][r] = v;
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        if (row < o.n_out)
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][r];
       }
     }
   }
-  // lane reduction
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float v = acc[bb][r];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      if (lane == 0) s_y[bb][wave * R + r] = v;
-    }
-  __syncthreads();
 
-  // sparse refinement delta over this workgroup's rows
+  // sparse refinement delta over this workgroup's tiles: y += sum over hit
+  // channels of x_k * s * c_lo (each row is read back by the lane that wrote it)
   if (refine) {
     int ok = 1;
     if (!selector) {
       if (tid == 0) s_lds[5] = sf_wait_word(&a.ctl->sel_state, 2u, &a.ctl->timeout) ? 1 : 0;
       __syncthreads();
       ok = s_lds[5];
-      __threadfence();
     }
+    // y rows written above by lane 0 of each wave are read back below by other
+    // threads of this workgroup
+    __threadfence();
+    __syncthreads();
     if (ok) {
-      const int nh = a.ws_nhit[op];
-      const int i = tid % rows_wg, mstep = 256 / rows_wg;
-      const int row = tile * rows_wg + i;
-      float part[NB];
+      for (int tile_g = blockIdx.x; tile_g < a.total_tiles; tile_g += gridDim.x) {
+        int op = 0;
+        for (int i = 1; i < a.n_ops; ++i)
+          if (tile_g >= a.ops[i].tile_begin) op = i;
+        const GemvOpDev& o = a.ops[op];
+        const int tile = tile_g - o.tile_begin;
+        const int nh = a.ws_nhit[op];
+        const int i = tid % rows_wg, mstep = 256 / rows_wg;
+        const int row = tile * rows_wg + i;
+        float part[NB];
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) part[bb] = 0.f;
-      if (row < o.n_out) {
-        const int* hk = a.ws_hit_k + op * a.k_sel;
-        const int* hs = a.ws_hit_slot + op * a.k_sel;
-        for (int m = tid / rows_wg; m < nh; m += mstep) {
-          const int k = hk[m];
-          const uint8_t* unit = o.pool.slots + (size_t)hs[m] * o.pool.unit_bytes;
-          const float clo = (float)read_field(unit, (uint32_t)row * a.r, a.r);
-          const float sv = sf_h2f(o.sz[(size_t)row * ngr + k / 128]);
-          const int c = k / C::CODES, kk = k - c * C::CODES;
-          // position of channel k in the pair-ordered x staging
-          int jj, hi;
-          C::locate(kk, &jj, &hi);
+        for (int bb = 0; bb < NB; ++bb) part[bb] = 0.f;
+        if (row < o.n_out) {
+          const int* hk = a.ws_hit_k + op * a.k_sel;
+          const int* hs = a.ws_hit_slot + op * a.k_sel;
+          for (int m = tid / rows_wg; m < nh; m += mstep) {
+            const int k = hk[m];
+            const uint8_t* unit = o.pool.slots + (size_t)hs[m] * o.pool.unit_bytes;
+            const float clo = (float)read_field(unit, (uint32_t)row * a.r, a.r);
+            const float sv = sf_h2f(o.sz[(size_t)row * ngr + k / 128]);
+            const int c = k / C::CODES, kk = k - c * C::CODES;
+            int jj, hi;
+            C::locate(kk, &jj, &hi);
 #pragma unroll
-          for (int bb = 0; bb < NB; ++bb) {
-            const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
-            const float xk = hi ? (float)xh.y : (float)xh.x;
-            part[bb] += (xk * sv) * clo;
+            for (int bb = 0; bb < NB; ++bb) {
+              const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
+              const float xk = hi ? (float)xh.y : (float)xh.x;
+              part[bb] += (xk * sv) * clo;
+            }
           }
         }
-      }
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) s_red[bb][tid] = part[bb];
-      __syncthreads();
-      if (tid < rows_wg) {
+        for (int bb = 0; bb < NB; ++bb) s_red[bb][tid] = part[bb];
+        __syncthreads();
+        if (tid < rows_wg && row < o.n_out) {
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          float sum = 0.f;
-          for (int j = tid; j < 256; j += rows_wg) sum += s_red[bb][j];
-          s_y[bb][tid] += sum;
+          for (int bb = 0; bb < NB; ++bb) {
+            float sum = 0.f;
+            for (int j = tid; j < 256; j += rows_wg) sum += s_red[bb][j];
+            float* yp = o.y + (size_t)(a.batch_off + bb) * o.n_out + row;
+            *yp = *yp + sum;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
-
-  if (tid < rows_wg) {
-    const int row = tile * rows_wg + tid;
-    if (row < o.n_out)
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = s_y[bb][tid];
-  }
-
-  if (refine) {
     __syncthreads();
     if (tid == 0) {
       const uint32_t prev = atomicAdd(&a.ctl->done, 1u);
-      if (prev == (uint32_t)a.total_wg - 1u) {
+      if (prev == gridDim.x - 1u) {
         __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&a.ctl->sel_state, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -420,20 +432,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 }
 
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
 template <class C, int B, int R, int NB>
-sf_status launch_gemv(GemvArgs& a, int rows_per_wg_unused, hipStream_t s) {
-  (void)rows_per_wg_unused;
+sf_status launch_gemv(GemvArgs& a, hipStream_t s) {
   const size_t lds = (size_t)NB * (a.k_in / 2) * 4 + (size_t)NB * (a.k_in / C::CODES) * 4;
   SF_REQUIRE(lds <= 64 * 1024, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
-  hipLaunchKernelGGL((gemv_kernel<C, B, R, NB>), dim3((unsigned)a.total_wg), dim3(256), lds, s, a);
+  // persistent grid: about SF_GEMV_WGS_PER_CU workgroups per CU, each taking an
+  // equal number of tiles
+  const int per_cu = env_int("SF_GEMV_WGS_PER_CU", 4);
+  const int cap = 256 * (per_cu > 0 ? per_cu : 4);
+  const int tiles_per_wg = (a.total_tiles + cap - 1) / cap;
+  const int grid = (a.total_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  hipLaunchKernelGGL((gemv_kernel<C, B, R, NB>), dim3((unsigned)grid), dim3(256), lds, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }
 
 template <class C, int B, int R>
 sf_status dispatch_nb(GemvArgs& a, int nb, hipStream_t s) {
-  if (nb == 2) return launch_gemv<C, B, R, 2>(a, 0, s);
-  return launch_gemv<C, B, R, 1>(a, 0, s);
+  if (nb == 2) return launch_gemv<C, B, R, 2>(a, s);
+  return launch_gemv<C, B, R, 1>(a, s);
 }
 
 template <class C, int B>
@@ -456,13 +478,6 @@ sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, hipStream_t s) {
       sf_set_error("sf_refined_gemv: resident width b must be 1, 2, 3, 4 or 8");
       return SF_EUNSUPPORTED;
   }
-}
-
-// Rows per wave: 1 for small launches (more waves in flight), 2 above 16K rows.
-// SF_GEMV_ROWS_PER_WAVE (1, 2 or 4) overrides the choice.
-int env_rows_per_wave() {
-  const char* e = getenv("SF_GEMV_ROWS_PER_WAVE");
-  return e ? atoi(e) : 0;
 }
 
 }  // namespace
@@ -501,10 +516,11 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   SF_REQUIRE(k_sel >= 0 && k_sel <= K, SF_EINVAL, "k_sel out of range");
   SF_REQUIRE(k_sel == 0 || f.r > 0, SF_EINVAL, "k_sel > 0 needs r > 0");
   GemvArgs a = {};
-  int rpw = env_rows_per_wave();
+  // rows per wave (SF_GEMV_ROWS_PER_WAVE = 1, 2 or 4 overrides the default)
+  int rpw = env_int("SF_GEMV_ROWS_PER_WAVE", 0);
   int64_t rows_total = 0;
   for (int i = 0; i < n_ops; ++i) rows_total += ops[i].w.n_out;
-  if (rpw != 1 && rpw != 2 && rpw != 4) rpw = rows_total <= 16384 ? 1 : 2;
+  if (rpw != 1 && rpw != 2 && rpw != 4) rpw = rows_total <= 8192 ? 1 : (rows_total <= 16384 ? 2 : 4);
   const int rows_wg = 4 * rpw;
   int tiles = 0;
   for (int i = 0; i < n_ops; ++i) {
@@ -546,7 +562,7 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.batch = batch;
   a.k_sel = k_sel;
   a.r = f.r;
-  a.total_wg = tiles;
+  a.total_tiles = tiles;
   hipStream_t s = (hipStream_t)stream;
   for (int b0 = 0; b0 < batch; b0 += 2) {
     const int nb = (batch - b0) >= 2 ? 2 : 1;

@@ -60,15 +60,30 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Builds stream word w (0 <= w < 4*width) of a 128-code group from codes in LDS.
-__device__ __forceinline__ uint32_t stream_word(const uint8_t* codes, int width, int w) {
+// Builds stream word w (0 <= w < 4*W) of a 128-code group of W-bit codes in LDS.
+template <int W>
+__device__ __forceinline__ uint32_t stream_word_t(const uint8_t* codes, int w) {
   uint32_t word = 0;
+#pragma unroll
   for (int p = 0; p < 32; ++p) {
     const int P = 32 * w + p;
-    const int i = P / width, j = P - i * width;
+    const int i = P / W, j = P % W;
     word |= (uint32_t)((codes[i] >> j) & 1u) << p;
   }
   return word;
+}
+
+__device__ __forceinline__ uint32_t stream_word(const uint8_t* codes, int width, int w) {
+  switch (width) {
+    case 1: return stream_word_t<1>(codes, w);
+    case 2: return stream_word_t<2>(codes, w);
+    case 3: return stream_word_t<3>(codes, w);
+    case 4: return stream_word_t<4>(codes, w);
+    case 5: return stream_word_t<5>(codes, w);
+    case 6: return stream_word_t<6>(codes, w);
+    case 7: return stream_word_t<7>(codes, w);
+    default: return stream_word_t<8>(codes, w);
+  }
 }
 
 // One wave quantises one group of 128 fp32 values at `src`.  Writes the group's
@@ -154,7 +169,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float* __restrict_
                                                         int t_cap, int b, int r,
                                                         uint8_t* k_res, uint32_t* k_sz,
                                                         uint8_t* v_res, uint32_t* v_sz,
-                                                        uint8_t* refine_out) {
+                                                        uint8_t* refine_out, int64_t refine_ld) {
   __shared__ uint8_t lds[4][256];
   const int wave = threadIdx.x >> 6;
   const int64_t gid = (int64_t)blockIdx.x * 4 + wave;
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float* __restrict_
   uint32_t* sz_base = which ? v_sz : k_sz;
   const int64_t unit_bytes = 2 * 16 * r;
   uint32_t* ref = (refine_out && r > 0)
-                      ? (uint32_t*)(refine_out + e * unit_bytes + which * 16 * r)
+                      ? (uint32_t*)(refine_out + (bh * refine_ld + tok) * unit_bytes + which * 16 * r)
                       : nullptr;
   quantize_group_wave(src, b, r, lds[wave], lds[wave] + 128,
                       (uint32_t*)(res_base + pos * 16 * b), sz_base + pos, ref);
@@ -264,7 +279,7 @@ extern "C" sf_status sf_debug_dequantize(const uint8_t* resident, const uint32_t
 
 extern "C" sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok,
                                   int32_t t0, const sf_qkv* kv, uint8_t* refine_out,
-                                  sf_stream stream) {
+                                  int64_t refine_ld, sf_stream stream) {
   SF_REQUIRE(kv && k_new && v_new, SF_EINVAL, "null argument");
   SF_REQUIRE(fmt_ok(kv->fmt), SF_EUNSUPPORTED, "bad format");
   SF_REQUIRE(kv->head_dim == 128, SF_EUNSUPPORTED, "head_dim must be 128");
@@ -272,12 +287,13 @@ extern "C" sf_status sf_kv_append(const float* k_new, const float* v_new, int32_
   SF_REQUIRE(n_tok >= 0 && t0 >= 0 && (int64_t)t0 + n_tok <= kv->t_cap, SF_EINVAL,
              "positions beyond t_cap");
   SF_REQUIRE(kv->batch > 0 && kv->n_kv_heads > 0, SF_EINVAL, "bad shape");
+  SF_REQUIRE(refine_out == nullptr || refine_ld >= n_tok, SF_EINVAL, "refine_ld must be >= n_tok");
   if (n_tok == 0) return SF_OK;
   const int64_t waves = (int64_t)kv->batch * kv->n_kv_heads * n_tok * 2;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
                      (hipStream_t)stream, k_new, v_new, kv->batch, kv->n_kv_heads, n_tok, t0,
                      kv->t_cap, kv->fmt.b, kv->fmt.r, kv->k_res, kv->k_sz, kv->v_res, kv->v_sz,
-                     refine_out);
+                     refine_out, (int64_t)refine_ld);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }

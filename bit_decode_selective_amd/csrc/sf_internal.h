@@ -68,11 +68,16 @@ __device__ __forceinline__ float sf_h2f(uint32_t bits16) {
 }
 
 // Bounded spin on a device word written by another workgroup of the same launch.
-// Returns false if it gave up.
+// Polls with relaxed loads (no cache invalidation per poll) and issues one
+// acquire fence once the word has the wanted value.  Returns false if it gave up
+// (after about a second); the caller then skips the work that needed the word.
 __device__ __forceinline__ bool sf_wait_word(uint32_t* p, uint32_t want, uint32_t* timeout_flag) {
-  for (uint32_t it = 0; it < (1u << 24); ++it) {
-    if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
-    __builtin_amdgcn_s_sleep(2);
+  for (uint32_t it = 0; it < (1u << 22); ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(8);
   }
   __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;

@@ -138,11 +138,14 @@ sf_status sf_debug_dequantize(const uint8_t* resident, const uint32_t* sz,
 /* Quantise n_tok new tokens of K and V (fp32 [batch][n_kv_heads][n_tok][head_dim])
  * into positions [t0, t0 + n_tok) of `kv` (t0 + n_tok <= t_cap; kv->t_len is not
  * changed by the call).  Their refinement units (layout of sf_qkv) are written
- * to refine_out [batch][n_kv_heads][n_tok][unit bytes] (device), for the caller to
- * copy into its host refinement store.  Per (batch, head, token) the K row and
- * the V row are one group each. */
+ * to refine_out (device, may be NULL): the unit of (batch i, head h, new token j)
+ * at refine_out + ((i*n_kv_heads + h)*refine_ld + j) * unit_bytes.  refine_ld =
+ * n_tok packs them; refine_ld = t_cap with refine_out pointing at unit t0 of a
+ * store laid out like the cache writes them in place.  Per (batch, head, token)
+ * the K row and the V row are one group each. */
 sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok, int32_t t0,
-                       const sf_qkv* kv, uint8_t* refine_out, sf_stream stream);
+                       const sf_qkv* kv, uint8_t* refine_out, int64_t refine_ld,
+                       sf_stream stream);
 
 /* ---- a3, a13: refinement slot cache ---------------------------------------- */
 /* One pool per refined tensor.  Units are fixed-size byte strings, unit ids
