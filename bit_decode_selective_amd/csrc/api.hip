@@ -14,6 +14,18 @@ __global__ void ws_zero_kernel(uint32_t* p, int n) {
 
 void sf_set_error(const std::string& msg) { g_last_error = msg; }
 
+#ifdef SF_PROBE
+static std::vector<void (*)(long long*)>& sf_probe_installers() {
+  static std::vector<void (*)(long long*)> v;
+  return v;
+}
+void sf_probe_register(void (*install)(long long*)) { sf_probe_installers().push_back(install); }
+extern "C" int sf_probe_set_buffer(long long* p) {
+  for (auto f : sf_probe_installers()) f(p);
+  return 0;
+}
+#endif
+
 extern "C" int32_t sf_abi_version(void) { return SF_ABI_VERSION; }
 
 extern "C" const char* sf_last_error(void) { return g_last_error.c_str(); }

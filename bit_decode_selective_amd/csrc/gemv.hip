@@ -116,74 +116,100 @@ __device__ __forceinline__ uint32_t read_field(const uint8_t* unit, uint32_t bit
 }
 
 // ---- channel selection + lookup (one workgroup) ---------------------------------
-__device__ __forceinline__ uint32_t chan_key(const uint16_t* x, int batch, int K, int k) {
-  uint32_t m = 0;
-  for (int bb = 0; bb < batch; ++bb) {
-    const uint32_t v = x[(size_t)bb * K + k] & 0x7FFFu;
-    m = v > m ? v : m;
-  }
-  return m;
-}
+// Thread t owns channels [t*cpt, (t+1)*cpt), cpt = 2*ceil(K/512) <= 64; their keys
+// (max over the batch of |x| as 15-bit fp16 patterns, which order like the values)
+// are read once, kept two per register, and radix-selected in two histogram passes
+// (top 8 bits, then the low 7; one LDS histogram per wave), then compacted in
+// channel order into `sel` (LDS when it fits, else the workspace).
+constexpr int KEYW = 32;
 
-__device__ void gemv_select_and_lookup(const GemvArgs& a, uint32_t* hist, int* lds) {
-  const int K = a.k_in, ks = a.k_sel, tid = threadIdx.x;
-  int32_t* sel = a.ws_sel;
+__device__ void gemv_select_and_lookup(const GemvArgs& a, uint32_t* hist4, int* lds, int32_t* sel) {
+  const int K = a.k_in, ks = a.k_sel, tid = threadIdx.x, wave = tid >> 6;
   if (a.sel_in) {
     for (int j = tid; j < ks; j += 256) sel[j] = a.sel_in[j];
   } else if (ks >= K) {
     for (int j = tid; j < ks; j += 256) sel[j] = j;
   } else {
-    // radix select on 15-bit keys |x| (fp16 bit patterns order like the values)
-    for (int i = tid; i < 256; i += 256) hist[i] = 0;
-    __syncthreads();
-    for (int k = tid; k < K; k += 256) atomicAdd(&hist[chan_key(a.x, a.batch, K, k) >> 7], 1u);
-    __syncthreads();
-    wg_suffix_sum256(hist, lds);
-    const int b1 = wg_find_threshold(hist, 256, (uint32_t)ks, lds + 4);
-    const uint32_t above1 = b1 < 255 ? hist[b1 + 1] : 0u;
-    __syncthreads();
-    hist[tid] = 0;
-    __syncthreads();
-    for (int k = tid; k < K; k += 256) {
-      const uint32_t kk = chan_key(a.x, a.batch, K, k);
-      if ((int)(kk >> 7) == b1) atomicAdd(&hist[kk & 127u], 1u);
+    const int cpt = 2 * ((K + 511) / 512);
+    const int k0 = tid * cpt;
+    uint32_t kw[KEYW];
+#pragma unroll
+    for (int i = 0; i < KEYW; ++i) kw[i] = 0;
+    for (int bb = 0; bb < a.batch; ++bb) {
+      const uint32_t* xr = (const uint32_t*)(a.x + (size_t)bb * K);
+#pragma unroll
+      for (int i = 0; i < KEYW; ++i) {
+        if (2 * i < cpt && k0 + 2 * i < K) {
+          const uint32_t v = xr[(k0 >> 1) + i] & 0x7FFF7FFFu;
+          const uint32_t lo = max(kw[i] & 0xFFFFu, v & 0xFFFFu), hi = max(kw[i] >> 16, v >> 16);
+          kw[i] = lo | (hi << 16);
+        }
+      }
     }
-    __syncthreads();
-    wg_suffix_sum256(hist, lds);
-    const int lo = wg_find_threshold(hist, 128, (uint32_t)ks - above1, lds + 4);
-    const uint32_t above = above1 + (lo < 127 ? hist[lo + 1] : 0u);
-    const uint32_t T = ((uint32_t)b1 << 7) | (uint32_t)lo;
-    const int need = ks - (int)above;
-    __syncthreads();
-    // ordered compaction: thread t owns channels [t*cpt, (t+1)*cpt)
-    const int cpt = (K + 255) / 256;
-    const int k0 = tid * cpt, k1 = min(K, k0 + cpt);
+    SF_TS(8);
+    // T = the ks-th largest key: the largest v with count(key >= v) >= ks, found by
+    // binary search over the 15-bit key range (15 block-wide counts)
+    (void)hist4;
+    int lo_v = 0, hi_v = 32768;  // count(>= lo_v) >= ks > count(>= hi_v)
+    while (hi_v - lo_v > 1) {
+      const int mid = (lo_v + hi_v) >> 1;
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < KEYW; ++i)
+        if (2 * i < cpt && k0 + 2 * i < K) c += ((int)(kw[i] & 0xFFFFu) >= mid) + ((int)(kw[i] >> 16) >= mid);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+      __syncthreads();
+      if ((tid & 63) == 0) lds[wave] = c;
+      __syncthreads();
+      const int tot4 = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+      if (tot4 >= ks) lo_v = mid; else hi_v = mid;
+    }
+    const uint32_t T = (uint32_t)lo_v;
+    SF_TS(9);
+    int above_l = 0;
+#pragma unroll
+    for (int i = 0; i < KEYW; ++i)
+      if (2 * i < cpt && k0 + 2 * i < K) above_l += ((kw[i] & 0xFFFFu) > T) + ((kw[i] >> 16) > T);
+    int above;
+    (void)wg_exclusive_scan(above_l, lds, &above);
+    const int need = ks - above;
     int gt = 0, eq = 0;
-    for (int k = k0; k < k1; ++k) {
-      const uint32_t kk = chan_key(a.x, a.batch, K, k);
-      gt += kk > T;
-      eq += kk == T;
-    }
+#pragma unroll
+    for (int i = 0; i < KEYW; ++i)
+      if (2 * i < cpt && k0 + 2 * i < K) {
+        const uint32_t lo = kw[i] & 0xFFFFu, hi = kw[i] >> 16;
+        gt += (lo > T) + (hi > T);
+        eq += (lo == T) + (hi == T);
+      }
     int tot;
     const int eq_before = wg_exclusive_scan(eq, lds, &tot);
     const int take_eq = max(0, min(eq, need - eq_before));
     int off = wg_exclusive_scan(gt + take_eq, lds, &tot);
-    int eq_seen = 0;
-    for (int k = k0; k < k1; ++k) {
-      const uint32_t kk = chan_key(a.x, a.batch, K, k);
-      if (kk > T) {
-        sel[off++] = k;
-      } else if (kk == T) {
-        if (eq_seen < take_eq) sel[off++] = k;
-        ++eq_seen;
+    int seen = 0;
+#pragma unroll
+    for (int i = 0; i < KEYW; ++i)
+      if (2 * i < cpt && k0 + 2 * i < K) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t key = h ? (kw[i] >> 16) : (kw[i] & 0xFFFFu);
+          const int k = k0 + 2 * i + h;
+          if (key > T) {
+            sel[off++] = k;
+          } else if (key == T) {
+            if (seen < take_eq) sel[off++] = k;
+            ++seen;
+          }
+        }
       }
-    }
   }
-  __threadfence();
+  // sel[] is read back below by other threads of this workgroup
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   if (a.sel_out && a.do_log)
     for (int j = tid; j < ks; j += 256) a.sel_out[j] = sel[j];
+  SF_TS(10);
   // lookups, per op, in selection order
   const int jpt = (ks + 255) / 256;
   const int j0 = tid * jpt, j1 = min(ks, j0 + jpt);
@@ -217,78 +243,149 @@ __device__ void gemv_select_and_lookup(const GemvArgs& a, uint32_t* hist, int* l
         pool.log_slots[base + j] = slot;
       }
       if (slot >= 0) {
-        a.ws_hit_k[op * ks + pos] = k;
-        a.ws_hit_slot[op * ks + pos] = slot;
+        sf_put(a.ws_hit_k + op * ks + pos, k);
+        sf_put(a.ws_hit_slot + op * ks + pos, slot);
         ++pos;
       }
     }
-    if (tid == 0) a.ws_nhit[op] = tot;
+    if (tid == 0) sf_put(a.ws_nhit + op, tot);
     __syncthreads();
   }
 }
 
 // ---- the GEMV kernel -------------------------------------------------------------
-// Persistent workgroups of 4 waves.  Row tiles of 4R rows (R per wave) are dealt to
-// workgroups round-robin: workgroup g takes tiles g, g + grid, ...  Within a tile,
-// lane l of a wave owns chunks l, l+64, ... of each of the wave's R rows.  x is
-// staged once per workgroup.  NB batch rows [batch_off, batch_off + NB) per launch.
+// When refining, workgroup 0 only selects, looks up and publishes the hit lists.
+// The other (tile) workgroups are persistent, 4 waves each: row tiles of 4R rows
+// (R per wave) are dealt round-robin; lane l of a wave owns chunks l, l+64, ... of
+// each of the wave's R rows.  The first chunk is requested before x is staged, and
+// the next tile's first chunk before the current tile is reduced.  x is staged
+// once per workgroup (16-byte loads scattered into pair order in LDS, chunk sums
+// by shuffles).  NB batch rows [batch_off, batch_off + NB) per launch.
+// Dynamic LDS: x pairs [NB][K/2] | x chunk sums [NB][nchunks] | delta staging:
+// tile scale words [4R][K/128] and per-hit refinement words [HIT_CAP][SW].
+constexpr int HIT_CAP = 512;  // hits staged in LDS per batch of the delta
+constexpr int SW = 4;         // refinement words staged per hit (a tile's rows)
+
+template <class C, int R>
+__device__ __forceinline__ void load_chunk(const GemvOpDev& o, int row0, int c, size_t rowbytes, int ngr,
+                                           uint32_t (&cw)[R][C::WORDS], uint32_t (&szw)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    if (row < o.n_out) {
+      const uint32_t* src = (const uint32_t*)(o.res + row * rowbytes + (size_t)c * (4 * C::WORDS));
+      if constexpr (C::WORDS == 4) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
+        cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
+      } else {
+#pragma unroll
+        for (int w = 0; w < C::WORDS; ++w) cw[r][w] = __builtin_nontemporal_load(src + w);
+      }
+      szw[r] = o.sz[(size_t)row * ngr + (c * C::CODES) / 128];
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::WORDS; ++w) cw[r][w] = 0;
+      szw[r] = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ int op_of_tile(const GemvArgs& a, int tile_g) {
+  int op = 0;
+  for (int i = 1; i < a.n_ops; ++i)
+    if (tile_g >= a.ops[i].tile_begin) op = i;
+  return op;
+}
+
 template <class C, int B, int R, int NB>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[1024];
   __shared__ int s_lds[8];
-  __shared__ float s_y[NB][4 * R];
   __shared__ float s_red[NB][256];
+  __shared__ int s_hk[HIT_CAP], s_hs[HIT_CAP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.k_in;
   const int nchunks = K / C::CODES;
   const int xpairs = K / 2;
-  uint32_t* xs = smem;                         // [NB][K/2] fp16 pairs
-  float* xsum = (float*)(smem + NB * xpairs);  // [NB][nchunks]
-  const bool refine = a.k_sel > 0;
   const int rows_wg = 4 * R;
+  const int ngr = K / 128;
+  uint32_t* xs = smem;                              // [NB][K/2] fp16 pairs
+  float* xsum = (float*)(smem + NB * xpairs);       // [NB][nchunks]
+  uint32_t* s_sz = smem + NB * xpairs + NB * nchunks;  // [rows_wg][ngr]
+  uint32_t* s_w = s_sz + rows_wg * ngr;                // [HIT_CAP][SW]
+  const bool refine = a.k_sel > 0;
+  const size_t rowbytes = (size_t)K * B / 8;
 
-  if (tid == 0) s_lds[7] = refine ? (atomicCAS(&a.ctl->sel_state, 0u, 1u) == 0u) : 0;
-
-  // stage x in pair order; per-chunk sums of x by the lanes holding the chunk's pairs
-  for (int bb = 0; bb < NB; ++bb) {
-    const uint16_t* xr = a.x + (size_t)(a.batch_off + bb) * K;
-    for (int p0 = 0; p0 < xpairs; p0 += 256) {
-      const int p = p0 + tid;
-      float v = 0.f;
-      if (p < xpairs) {
-        const int c = p / C::PAIRS, j = p - c * C::PAIRS;
-        const int kb = c * C::CODES;
-        const uint32_t pr = (uint32_t)xr[kb + C::pair_k0(j)] | ((uint32_t)xr[kb + C::pair_k1(j)] << 16);
-        xs[bb * xpairs + p] = pr;
-        const h2_t h = as_h2(pr);
-        v = (float)h.x + (float)h.y;
+  SF_TS(0);
+  if (refine && blockIdx.x == 0) {
+    // the selecting workgroup: its sel list lives in the (otherwise unused) LDS
+    // staging area when it fits
+    int32_t* sel = (a.k_sel <= NB * xpairs) ? (int32_t*)smem : a.ws_sel;
+    gemv_select_and_lookup(a, s_hist, s_lds, sel);
+    SF_TS(2);
+    sf_drain();
+    __syncthreads();
+    if (tid == 0) {
+      sf_put(&a.ctl->sel_state, 2u);
+      const uint32_t prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1u) {
+        sf_put(&a.ctl->done, 0u);
+        sf_put(&a.ctl->sel_state, 0u);
       }
+    }
+    return;
+  }
+  const int twg = (int)blockIdx.x - (refine ? 1 : 0);  // tile workgroup index
+  const int n_twg = (int)gridDim.x - (refine ? 1 : 0);
+
+  // request the first chunk of this wave before anything else
+  uint32_t cw[R][C::WORDS];
+  uint32_t szw[R];
+  bool have = false;
+  if (twg < a.total_tiles && lane < nchunks) {
+    const int op = op_of_tile(a, twg);
+    load_chunk<C, R>(a.ops[op], (twg - a.ops[op].tile_begin) * rows_wg + wave * R, lane, rowbytes, ngr, cw, szw);
+    have = true;
+  }
+
+  // stage x in pair order (16-byte loads, 2-byte LDS stores); the CODES/8 threads
+  // that load one chunk sum it with shuffles
+  {
+    uint16_t* xh = (uint16_t*)xs;
+    constexpr int TPC = C::CODES / 8;  // threads per chunk
+    for (int bb = 0; bb < NB; ++bb) {
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+      for (int m0 = 0; m0 < K / 8; m0 += 256) {
+        const int m = m0 + tid;
+        float part = 0.f;
+        if (m < K / 8) {
+          const u32x4 v = xr[m];
+          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int o = C::PAIRS / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, C::PAIRS);
-      if (p < xpairs && (p % C::PAIRS) == 0) xsum[bb * nchunks + p / C::PAIRS] = v;
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * m + e;
+            const int c = k / C::CODES, kk = k - c * C::CODES;
+            int j, hi;
+            C::locate(kk, &j, &hi);
+            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
+            part += (float)__builtin_bit_cast(_Float16, hb);
+          }
+        }
+#pragma unroll
+        for (int o = TPC / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, TPC);
+        if (m < K / 8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
+      }
     }
   }
   __syncthreads();
 
-  const bool selector = s_lds[7] != 0;
-  if (selector) {
-    gemv_select_and_lookup(a, s_hist, s_lds);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&a.ctl->sel_state, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  const size_t rowbytes = (size_t)K * B / 8;
-  const int ngr = K / 128;
+  SF_TS(1);
   const float scl = (float)(1u << (a.r + B));
-
-  // resident GEMV over this workgroup's tiles; y = x W_res^T written per tile
-  for (int tile_g = blockIdx.x; tile_g < a.total_tiles; tile_g += gridDim.x) {
-    int op = 0;
-    for (int i = 1; i < a.n_ops; ++i)
-      if (tile_g >= a.ops[i].tile_begin) op = i;
+  for (int tile_g = twg; tile_g < a.total_tiles; tile_g += n_twg) {
+    const int op = op_of_tile(a, tile_g);
     const GemvOpDev& o = a.ops[op];
     const int tile = tile_g - o.tile_begin;
     const int row0 = tile * rows_wg + wave * R;
@@ -297,29 +394,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[bb][r] = 0.f;
-
     for (int c = lane; c < nchunks; c += 64) {
-      uint32_t cw[R][C::WORDS];
-      uint32_t szw[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
-        if (row < o.n_out) {
-          const uint32_t* src = (const uint32_t*)(o.res + row * rowbytes + (size_t)c * (4 * C::WORDS));
-          if constexpr (C::WORDS == 4) {
-            const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
-            cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
-          } else {
-#pragma unroll
-            for (int w = 0; w < C::WORDS; ++w) cw[r][w] = __builtin_nontemporal_load(src + w);
-          }
-          szw[r] = o.sz[(size_t)row * ngr + (c * C::CODES) / 128];
-        } else {
-#pragma unroll
-          for (int w = 0; w < C::WORDS; ++w) cw[r][w] = 0;
-          szw[r] = 0;
-        }
-      }
+      if (!have) load_chunk<C, R>(o, row0, c, rowbytes, ngr, cw, szw);
+      have = false;
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         uint32_t xv[C::PAIRS];
@@ -341,6 +418,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         }
       }
     }
+    // request the next tile's first chunk before reducing this one
+    const int next = tile_g + n_twg;
+    if (next < a.total_tiles && lane < nchunks) {
+      const int op2 = op_of_tile(a, next);
+      load_chunk<C, R>(a.ops[op2], (next - a.ops[op2].tile_begin) * rows_wg + wave * R, lane, rowbytes, ngr,
+                       cw, szw);
+      have = true;
+    }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
@@ -361,40 +446,69 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
   }
 
+  SF_TS(3);
   // sparse refinement delta over this workgroup's tiles: y += sum over hit
-  // channels of x_k * s * c_lo (each row is read back by the lane that wrote it)
-  if (refine) {
-    int ok = 1;
-    if (!selector) {
-      if (tid == 0) s_lds[5] = sf_wait_word(&a.ctl->sel_state, 2u, &a.ctl->timeout) ? 1 : 0;
-      __syncthreads();
-      ok = s_lds[5];
-    }
-    // y rows written above by lane 0 of each wave are read back below by other
-    // threads of this workgroup
-    __threadfence();
-    __syncthreads();
-    if (ok) {
-      for (int tile_g = blockIdx.x; tile_g < a.total_tiles; tile_g += gridDim.x) {
-        int op = 0;
-        for (int i = 1; i < a.n_ops; ++i)
-          if (tile_g >= a.ops[i].tile_begin) op = i;
-        const GemvOpDev& o = a.ops[op];
-        const int tile = tile_g - o.tile_begin;
-        const int nh = a.ws_nhit[op];
-        const int i = tid % rows_wg, mstep = 256 / rows_wg;
-        const int row = tile * rows_wg + i;
-        float part[NB];
+  // channels k of x_k * s[row][k/128] * c_lo[row][k]
+  if (!refine) return;
+  int ok = 1;
+  if (tid == 0) s_lds[5] = sf_wait_word(&a.ctl->sel_state, 2u, &a.ctl->timeout) ? 1 : 0;
+  __syncthreads();
+  ok = s_lds[5];
+  SF_TS(4);
+  if (ok) {
+    const int r = a.r;
+    // the refinement bits of a tile's rows: rows_wg * r bits from bit tile*rows_wg*r
+    // of each unit; staged in LDS when they span at most SW words
+    const int nw = (rows_wg * r + 31) / 32 + 1;
+    const bool staged = nw <= SW;
+    for (int tile_g = twg; tile_g < a.total_tiles; tile_g += n_twg) {
+      const int op = op_of_tile(a, tile_g);
+      const GemvOpDev& o = a.ops[op];
+      const int tile = tile_g - o.tile_begin;
+      const int nh = sf_get(a.ws_nhit + op);
+      const int* ghk = a.ws_hit_k + op * a.k_sel;
+      const int* ghs = a.ws_hit_slot + op * a.k_sel;
+      const uint32_t w0 = ((uint32_t)(tile * rows_wg) * r) >> 5;
+      const int wpu = o.pool.unit_bytes / 4;
+      // scale words of the tile's rows
+      for (int i = tid; i < rows_wg * ngr; i += 256) {
+        const int rr = i / ngr, g = i - rr * ngr;
+        const int row = tile * rows_wg + rr;
+        s_sz[i] = row < o.n_out ? o.sz[(size_t)row * ngr + g] : 0u;
+      }
+      const int i = tid % rows_wg, mstep = 256 / rows_wg;
+      const int row = tile * rows_wg + i;
+      float part[NB];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) part[bb] = 0.f;
+      for (int bb = 0; bb < NB; ++bb) part[bb] = 0.f;
+      for (int m0 = 0; m0 < nh; m0 += HIT_CAP) {
+        const int mn = min(HIT_CAP, nh - m0);
+        __syncthreads();
+        for (int m = tid; m < mn; m += 256) {
+          const int k = sf_get(ghk + m0 + m), slot = sf_get(ghs + m0 + m);
+          s_hk[m] = k;
+          s_hs[m] = slot;
+          if (staged) {
+            const uint32_t* u = (const uint32_t*)(o.pool.slots + (size_t)slot * o.pool.unit_bytes);
+#pragma unroll
+            for (int q = 0; q < SW; ++q)
+              s_w[SW * m + q] = (q < nw && (int)w0 + q < wpu) ? u[w0 + q] : 0u;
+          }
+        }
+        __syncthreads();
         if (row < o.n_out) {
-          const int* hk = a.ws_hit_k + op * a.k_sel;
-          const int* hs = a.ws_hit_slot + op * a.k_sel;
-          for (int m = tid / rows_wg; m < nh; m += mstep) {
-            const int k = hk[m];
-            const uint8_t* unit = o.pool.slots + (size_t)hs[m] * o.pool.unit_bytes;
-            const float clo = (float)read_field(unit, (uint32_t)row * a.r, a.r);
-            const float sv = sf_h2f(o.sz[(size_t)row * ngr + k / 128]);
+          for (int m = tid / rows_wg; m < mn; m += mstep) {
+            const int k = s_hk[m];
+            uint32_t clo_u;
+            if (staged) {
+              const uint32_t p = (uint32_t)row * r - (w0 << 5);  // bit within the staged words
+              const uint32_t q = p >> 5;
+              const uint64_t w2 = (uint64_t)s_w[SW * m + q] | ((uint64_t)(q + 1 < (uint32_t)SW ? s_w[SW * m + q + 1] : 0u) << 32);
+              clo_u = (uint32_t)(w2 >> (p & 31)) & ((1u << r) - 1u);
+            } else {
+              clo_u = read_field(o.pool.slots + (size_t)s_hs[m] * o.pool.unit_bytes, (uint32_t)row * r, r);
+            }
+            const float sv = sf_h2f(s_sz[i * ngr + (k >> 7)]);
             const int c = k / C::CODES, kk = k - c * C::CODES;
             int jj, hi;
             C::locate(kk, &jj, &hi);
@@ -402,32 +516,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             for (int bb = 0; bb < NB; ++bb) {
               const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
               const float xk = hi ? (float)xh.y : (float)xh.x;
-              part[bb] += (xk * sv) * clo;
+              part[bb] += (xk * sv) * (float)clo_u;
             }
           }
         }
+      }
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) s_red[bb][tid] = part[bb];
-        __syncthreads();
-        if (tid < rows_wg && row < o.n_out) {
+      for (int bb = 0; bb < NB; ++bb) s_red[bb][tid] = part[bb];
+      __syncthreads();
+      // lane 0 of wave w wrote rows [w*R, w*R + R) of the tile: it adds their deltas
+      if (lane == 0) {
 #pragma unroll
-          for (int bb = 0; bb < NB; ++bb) {
-            float sum = 0.f;
-            for (int j = tid; j < 256; j += rows_wg) sum += s_red[bb][j];
-            float* yp = o.y + (size_t)(a.batch_off + bb) * o.n_out + row;
-            *yp = *yp + sum;
+        for (int rr = 0; rr < R; ++rr) {
+          const int ii = wave * R + rr;
+          const int rrow = tile * rows_wg + ii;
+          if (rrow < o.n_out) {
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+              float sum = 0.f;
+              for (int j = ii; j < 256; j += rows_wg) sum += s_red[bb][j];
+              float* yp = o.y + (size_t)(a.batch_off + bb) * o.n_out + rrow;
+              *yp = *yp + sum;
+            }
           }
         }
-        __syncthreads();
       }
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = atomicAdd(&a.ctl->done, 1u);
-      if (prev == gridDim.x - 1u) {
-        __hip_atomic_store(&a.ctl->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctl->sel_state, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
+  }
+  __syncthreads();
+  SF_TS(5);
+  if (tid == 0) {
+    // the last workgroup to finish resets the words for the next launch
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1u) {
+      sf_put(&a.ctl->done, 0u);
+      sf_put(&a.ctl->sel_state, 0u);
     }
   }
 }
@@ -439,14 +563,26 @@ int env_int(const char* name, int dflt) {
 
 template <class C, int B, int R, int NB>
 sf_status launch_gemv(GemvArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)NB * (a.k_in / 2) * 4 + (size_t)NB * (a.k_in / C::CODES) * 4;
-  SF_REQUIRE(lds <= 64 * 1024, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
-  // persistent grid: about SF_GEMV_WGS_PER_CU workgroups per CU, each taking an
-  // equal number of tiles
-  const int per_cu = env_int("SF_GEMV_WGS_PER_CU", 4);
-  const int cap = 256 * (per_cu > 0 ? per_cu : 4);
+  const size_t lds = ((size_t)NB * (a.k_in / 2) + (size_t)NB * (a.k_in / C::CODES) +
+                      (size_t)4 * R * (a.k_in / 128) + (size_t)SW * HIT_CAP) * 4;
+  SF_REQUIRE(lds <= 52 * 1024, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  // persistent tile workgroups: as many as are resident at once (at most
+  // SF_GEMV_WGS_PER_CU per CU if set), each with an equal number of tiles
+  static int occ = 0, n_cu = 0;
+  if (occ == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, (const void*)gemv_kernel<C, B, R, NB>, 256, lds) != hipSuccess || v < 1)
+      v = 2;
+    int dev = 0, cus = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    occ = v;
+    n_cu = cus;
+  }
+  const int per_cu = env_int("SF_GEMV_WGS_PER_CU", occ);
+  const int cap = n_cu * (per_cu > 0 ? min(per_cu, occ) : occ) - (a.k_sel > 0 ? 1 : 0);
   const int tiles_per_wg = (a.total_tiles + cap - 1) / cap;
-  const int grid = (a.total_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  const int grid = (a.total_tiles + tiles_per_wg - 1) / tiles_per_wg + (a.k_sel > 0 ? 1 : 0);
   hipLaunchKernelGGL((gemv_kernel<C, B, R, NB>), dim3((unsigned)grid), dim3(256), lds, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
@@ -463,7 +599,8 @@ sf_status dispatch_r(GemvArgs& a, int R, int nb, hipStream_t s) {
   switch (R) {
     case 1: return dispatch_nb<C, B, 1>(a, nb, s);
     case 2: return dispatch_nb<C, B, 2>(a, nb, s);
-    default: return dispatch_nb<C, B, 4>(a, nb, s);
+    case 4: return dispatch_nb<C, B, 4>(a, nb, s);
+    default: return dispatch_nb<C, B, 8>(a, nb, s);
   }
 }
 
@@ -516,11 +653,12 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   SF_REQUIRE(k_sel >= 0 && k_sel <= K, SF_EINVAL, "k_sel out of range");
   SF_REQUIRE(k_sel == 0 || f.r > 0, SF_EINVAL, "k_sel > 0 needs r > 0");
   GemvArgs a = {};
-  // rows per wave (SF_GEMV_ROWS_PER_WAVE = 1, 2 or 4 overrides the default)
+  // rows per wave (SF_GEMV_ROWS_PER_WAVE = 1, 2, 4 or 8 overrides the default)
   int rpw = env_int("SF_GEMV_ROWS_PER_WAVE", 0);
   int64_t rows_total = 0;
   for (int i = 0; i < n_ops; ++i) rows_total += ops[i].w.n_out;
-  if (rpw != 1 && rpw != 2 && rpw != 4) rpw = rows_total <= 8192 ? 1 : (rows_total <= 16384 ? 2 : 4);
+  if (rpw != 1 && rpw != 2 && rpw != 4 && rpw != 8)
+    rpw = rows_total <= 8192 ? 2 : (rows_total <= 16384 ? 4 : 8);
   const int rows_wg = 4 * rpw;
   int tiles = 0;
   for (int i = 0; i < n_ops; ++i) {
@@ -564,8 +702,10 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.r = f.r;
   a.total_tiles = tiles;
   hipStream_t s = (hipStream_t)stream;
-  for (int b0 = 0; b0 < batch; b0 += 2) {
-    const int nb = (batch - b0) >= 2 ? 2 : 1;
+  // two batch rows per launch when both fit the LDS staging of x, else one
+  const int max_nb = ((size_t)2 * K * 2 + 2 * K * 4 / 16 + 32 * (K / 128) * 4 + SW * HIT_CAP * 4) <= 52 * 1024 ? 2 : 1;
+  for (int b0 = 0; b0 < batch; b0 += max_nb) {
+    const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;
     a.do_log = b0 == 0;
     sf_status st = dispatch_b(a, f.b, rpw, nb, s);

@@ -67,20 +67,66 @@ __device__ __forceinline__ float sf_h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
 }
 
-// Bounded spin on a device word written by another workgroup of the same launch.
-// Polls with relaxed loads (no cache invalidation per poll) and issues one
-// acquire fence once the word has the wanted value.  Returns false if it gave up
-// (after about a second); the caller then skips the work that needed the word.
+// Cross-workgroup hand-off inside one launch.  Data published by one workgroup for
+// others is written with agent-scope atomic stores and read with agent-scope
+// atomic loads, which are performed at the device coherence point (no L2 writeback
+// or invalidation, which on a multi-XCD device would be needed for plain accesses
+// and are costly).  The writer waits for its stores to complete (s_waitcnt) and
+// passes a workgroup barrier before one thread raises the flag.
+__device__ __forceinline__ void sf_put(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sf_put(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sf_put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sf_get(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t sf_get(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float sf_get(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this thread's memory operations have completed.
+__device__ __forceinline__ void sf_drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Bounded spin on a flag raised by another workgroup of the same launch.  Returns
+// false if it gave up (after about a second); the caller then skips the work that
+// needed the flag.
 __device__ __forceinline__ bool sf_wait_word(uint32_t* p, uint32_t want, uint32_t* timeout_flag) {
   for (uint32_t it = 0; it < (1u << 22); ++it) {
-    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      return true;
-    }
-    __builtin_amdgcn_s_sleep(8);
+    if (sf_get(p) == want) return true;
+    __builtin_amdgcn_s_sleep(4);
   }
-  __hip_atomic_store(timeout_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sf_put(timeout_flag, 1u);
   return false;
 }
+
+// Phase timestamps for performance analysis.  Compiled in only with -DSF_PROBE
+// (a separate build); SF_TS(i) records the wall clock of thread 0 of each
+// workgroup in slot i (0..15) of that workgroup's row of the probe buffer.
+#ifdef SF_PROBE
+// one copy of the buffer pointer per translation unit (no relocatable device code)
+static __device__ long long* sf_probe_buf = nullptr;
+void sf_probe_register(void (*install)(long long*));
+namespace {
+struct SfProbeInstaller {
+  static void install(long long* p) { (void)hipMemcpyToSymbol(HIP_SYMBOL(sf_probe_buf), &p, sizeof(p)); }
+  SfProbeInstaller() { sf_probe_register(&install); }
+};
+static SfProbeInstaller sf_probe_installer;
+}  // namespace
+#define SF_TS(i)                                                                          \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && sf_probe_buf)                                                 \
+      sf_probe_buf[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + (i)] = wall_clock64(); \
+  } while (0)
+#else
+#define SF_TS(i) ((void)0)
+#endif
 
 static inline size_t sf_align256(size_t v) { return (v + 255) & ~size_t(255); }

@@ -30,7 +30,7 @@ def _run(qws, x, k_sel, sel_in=None, cache="resident"):
     return [y.cpu().numpy() for y in ys], sel.cpu().numpy().tolist(), [h.cpu().numpy() for h in hits]
 
 
-@pytest.mark.parametrize("rpw", ["1", "2", "4"])
+@pytest.mark.parametrize("rpw", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("b,r", [(2, 2), (3, 1), (4, 4), (1, 3), (8, 0), (2, 0)])
 @pytest.mark.parametrize("batch", [1, 2, 3])
 def test_small_shapes(b, r, batch, rpw, monkeypatch):
