@@ -35,6 +35,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# The kernel whose launches are timed for the roofline line: the step's largest share
+# of time.  `traffic` is its HBM bytes per launch from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE), each divided by what the same counter reads per byte
+# for a plain copy kernel of known size (bench.py --copy-calibration); it is reported
+# only while the kernel source still has the hash it was measured on.
+DOMINANT = {
+    "tag": "gateup",
+    "kernel": "gemv_kernel (fused gate/up, 2 x 14336 x 4096)",
+    "source": "bit_decode_selective_amd/csrc/gemv.hip",
+}
+TRAFFIC = {
+    "source_sha256": "b79993cf88aee4cc1a4ab517df91f368adfc06cb0d5058f8aac2c8274668fd3b",
+    "fetch_bytes": 40645820,
+    "write_bytes": 143565,
+}
+COPY_CALIBRATION_BYTES = 256 << 20
 HIDDEN, FFN, NQ, NKV, HD = 4096, 14336, 32, 8, 128
 
 
@@ -196,9 +213,15 @@ class Model:
             tot += append_bytes(self.b, self.r, self.batch)
         return tot
 
-    def dominant_bytes(self):
-        gname, ops, k_in = self.groups[0][2]
-        return gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(self.ch_pct, k_in), self.b, self.r, self.batch)
+    def dominant_bytes(self, tag):
+        """Algorithmic bytes of one launch of the call tagged `tag` (refined)."""
+        if tag == "attn":
+            return attn_bytes(self.T, k_select(self.tok_pct, self.T), self.b, self.r, self.batch)
+        for gname, ops, k_in in self.groups[0]:
+            if gname == tag:
+                return gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(self.ch_pct, k_in), self.b, self.r,
+                                  self.batch)
+        raise KeyError(tag)
 
 
 def time_steps(model, calls, steps, warmup, use_graph):
@@ -237,12 +260,24 @@ def time_steps(model, calls, steps, warmup, use_graph):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, batch):
-    """The fp64 oracle on a bounded sample: one 4096 x 4096 refined GEMV and refined
-    attention over 2 KV heads (8 query heads) at the full context; rates scaled to
-    the whole step by algorithmic bytes."""
-    import numpy as np
+def _timed_reps(fn, budget_s):
+    """One untimed warm-up call, then timed calls until `budget_s` seconds have
+    been spent (at least three); returns (median seconds per call, reps)."""
+    fn()
+    times = []
+    while len(times) < 3 or sum(times) < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    return times[len(times) // 2], len(times)
 
+
+def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, batch, budget_s=8.0):
+    """The fp64 oracle on a bounded sample: a 4096 x 4096 refined GEMV and refined
+    attention over all 8 KV heads (32 query heads) at the full context, each repeated
+    for about `budget_s` seconds (median per call); rates are scaled to the whole step
+    by algorithmic bytes."""
     from bit_decode_selective_amd import inputs
     from oracle import attention as o_attn
     from oracle import gemv as o_gemv
@@ -258,19 +293,21 @@ def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, bat
     q = nested.quantize(W, b, r, 128)
     x = inputs.activation(2, 0, inputs.Q_PROJ, 0, batch, HIDDEN)
     ks = selection.k_select(ch_pct, HIDDEN)
-    t0 = time.perf_counter()
-    sel = selection.select_channels(x, ks)
-    o_gemv.refined_gemv(q, x, sel)
-    tg = time.perf_counter() - t0
+
+    def gemv():
+        sel = selection.select_channels(x, ks)
+        o_gemv.refined_gemv(q, x, sel)
+
+    tg, ng = _timed_reps(gemv, budget_s)
     gb = gemv_bytes([HIDDEN], HIDDEN, ks, b, r, batch)
-    nkv = 2
+    nkv = NKV
     K, V = inputs.kv(3, 0, 1, nkv, T, HD)
     qh = inputs.query(3, 0, 0, 1, nkv * NQ // NKV, HD)
     qk, qv = o_attn.quantize_kv(K, b, r), o_attn.quantize_kv(V, b, r)
+    del K, V
     kt = selection.k_select(tok_pct, T)
-    t0 = time.perf_counter()
-    o_attn.refined_attention(qh, qk, qv, (1, nkv, T, HD), 1 / math.sqrt(HD), kt)
-    ta = time.perf_counter() - t0
+    ta, na = _timed_reps(lambda: o_attn.refined_attention(qh, qk, qv, (1, nkv, T, HD), 1 / math.sqrt(HD), kt),
+                         budget_s)
     ab = attn_bytes(T, kt, b, r, 1) * nkv / NKV
     step_s = gemv_step_bytes / (gb / tg) + attn_step_bytes / (ab / ta)
     return {
@@ -278,11 +315,25 @@ def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, bat
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: one {HIDDEN}x{HIDDEN} {b}+{r}-bit refined GEMV ({tg:.2f} s) and refined "
-                   f"attention over {nkv} KV heads x {T} tokens ({ta:.2f} s); scaled to the full step by "
-                   f"algorithmic bytes (GEMV {gb / tg / 1e6:.1f} MB/s, attention {ab / ta / 1e6:.1f} MB/s); "
-                   f"host cpu_count={os.cpu_count()}"),
+        "sample": (f"fp64 numpy oracle, median of {ng} calls of one {HIDDEN}x{HIDDEN} {b}+{r}-bit refined GEMV "
+                   f"with top-{ks} channel selection ({tg:.3f} s each) and of {na} calls of refined attention, "
+                   f"batch 1, {NQ} query / {nkv} KV heads x {T} tokens, top-{kt} tokens ({ta:.3f} s each); "
+                   f"scaled to the full step by algorithmic bytes (GEMV {gb / tg / 1e6:.1f} MB/s, attention "
+                   f"{ab / ta / 1e6:.1f} MB/s); host cpu_count={os.cpu_count()}"),
     }
+
+
+def traffic_bytes():
+    """Measured HBM bytes per launch of the dominant kernel, or None when unmeasured or
+    when its source changed since the counters were taken."""
+    if TRAFFIC is None:
+        return None
+    import hashlib
+
+    with open(os.path.join(ROOT, DOMINANT["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["source_sha256"]:
+            return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
 
 
 def main():
@@ -296,6 +347,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unrefined", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain device copy kernel (256 MiB read + 256 MiB written) "
+                         "whose HBM counters scale those of the other kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -304,6 +358,14 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: 3 x torch.neg over {COPY_CALIBRATION_BYTES} bytes", file=sys.stderr, flush=True)
+        del src, dst
     b = r = 2
     ch_pct, tok_pct = 3, 2
     t_setup = time.time()
@@ -324,11 +386,11 @@ def main():
     evs = []
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.steps // 4)):
-            model.enqueue(calls, stream, events=evs, tag="gateup")
+            model.enqueue(calls, stream, events=evs, tag=DOMINANT["tag"])
             model.fill(stream)
     torch.cuda.synchronize()
     dom_us = 1000.0 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-    dom_bytes = model.dominant_bytes()
+    dom_bytes = model.dominant_bytes(DOMINANT["tag"])
     step_bytes = model.step_bytes(True)
     gbps = step_bytes / (ms * 1e-3) / 1e9
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -343,7 +405,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 x int-code -> fp32 (fp64 attention partials)",
+        "dtype": "fp16 x int2 -> fp32",
         "data": "synthetic (seeded random weights/KV/activations of the model shapes; no trained weights)",
         "config": {
             "workload": (f"Llama-3.1-8B-shape refined decode step, batch {args.batch}: {args.layers} layers x "
@@ -364,12 +426,12 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel (fused gate/up, 2 x 14336 x 4096)",
+            "kernel": DOMINANT["kernel"],
             "achieved": dom_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": dom_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": traffic_bytes(),
             "launch_us": dom_us,
             "bytes_per_launch": dom_bytes,
         },
