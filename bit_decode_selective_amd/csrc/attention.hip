@@ -8,43 +8,51 @@
 // over the kv head's query heads; for selected tokens that hit, both key and value
 // use the (b+r)-bit value; the output softmax runs over all tokens after that.
 //
-// Three launches per call:
-//   qk     : streams the resident keys (T split over workgroups), logits of the G
-//            query heads of each KV head on MFMA (codes expanded into fp16
-//            mantissas, value 1 + c/2^b, times q), per-split softmax max / sum;
-//   select : merges the split statistics, forms the selection scores, builds a
-//            2048-bin histogram of their bit patterns (many workgroups); the last
-//            workgroup of each KV head finishes an exact radix select (ties to the
-//            lower token), compacts the selection in token order, looks it up in
-//            the refinement cache and overwrites the logits of the hit tokens with
-//            their refined values l' = l + scale * s_K * (q . cK_lo);
-//   pv     : streams the resident values with the final weights exp(l - m'),
-//            adds s_V * cV_lo for the hit tokens of its split, and the last
-//            workgroup of each KV head merges the split sums into the output.
-// All weights are positive and final before they are accumulated, so fp32 sums
-// carry no cancellation.
-#include "block_scan.h"
+// Kernels (per call, one KV head = one (batch, kv head) pair):
+//   split  : a workgroup per 256 tokens streams the resident keys: logits of the G
+//            query heads on MFMA (key codes expanded into fp16 mantissas, value
+//            1 + c/2^b, times q), split-local softmax max m_s and sum z_s.  Without
+//            refinement it also streams the values and forms the split's value sum
+//            N_s = sum_t e^(l - m_s) V_b[t] (flash-decoding partials).
+//   select : a 1024-thread workgroup per 4096-token chunk.  Merges the split
+//            statistics into the softmax max / sum of each head.  Without
+//            refinement it merges the partials and the last chunk writes the output.
+//            With refinement it scores its chunk (softmax weight summed over the G
+//            heads) and, with the other chunks of the KV head, finds the exact k-th
+//            score by a radix select over shared histograms (ties to the lower
+//            token); each chunk writes its part of the ascending selection, looks it
+//            up in the refinement cache and replaces the logits of its hits by
+//            l' = l + scale * s_K * (q . cK_lo); the last chunk records the max
+//            logit after replacement.
+//   pv     : (refinement only) a workgroup per 512 tokens (256 for b = 8) forms
+//            the final weights e^(l - max), sums weight * V_b on MFMA
+//            and adds weight * s_V * cV_lo for its hits; the last workgroup of the
+//            KV head divides numerator by denominator.
+// Weights are final and positive before anything is accumulated, so no sum
+// cancels a large term.  Value sums on MFMA use the weight as an fp16 high part
+// plus an fp16 low part (about 22 bits) times codes in the 1 + c/2^b form.
+// The chunks of one KV head in `select` wait for each other at up to four points
+// (bounded spins).  Workgroups are dispatched in order and a KV head has at most
+// 256 chunks, so the chunks of a KV head are resident together.
 #include "sf_internal.h"
 
 namespace {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int HD = 128;       // head dim
-constexpr int SPLIT2 = 4096;  // tokens per select workgroup
-constexpr int SEL_T = 1024;   // threads of a select workgroup
-constexpr int SPR = 32;       // scores per thread per round in the finishing workgroup
-constexpr int NBINS = 2048;   // first-level radix bins (top 11 bits of the score)
+constexpr int HD = 128;          // head dim
+constexpr int SA = 256;          // tokens per split workgroup
+constexpr int CB = 4096;         // tokens per select workgroup (chunk)
+constexpr int SEL_T = 1024;      // threads of a select workgroup
+constexpr int TPT = CB / SEL_T;  // tokens per select thread
+constexpr int PW = HD + 4;       // partial record: N[HD], max, sum, pad
+constexpr int NBIN = 2048;       // histogram bins (levels: key bits 30..20, 19..10, 9..0)
+constexpr int MAX_CHUNKS = 256;
 
-// qk: 16-token MFMA tiles; each wave loads TPW tiles up front
-__host__ __device__ constexpr int qk_tpw(int b) { return b <= 2 ? 8 : (b == 4 ? 8 : 4); }
-__host__ __device__ constexpr int qk_split(int b) { return 4 * 16 * qk_tpw(b); }
-// pv: tokens per workgroup, their codes staged in LDS (16 KB)
-__host__ __device__ constexpr int pv_split(int b) { return 1024 / b; }
+__host__ __device__ constexpr int pv_tokens(int b) { return b <= 4 ? 512 : 256; }
 
 __device__ __forceinline__ uint32_t field(const uint32_t* w, int bit, int width) {
   const int wi = bit >> 5, off = bit & 31;
@@ -61,83 +69,135 @@ struct AttnArgs {
   const uint32_t* k_sz;
   const uint8_t* v_res;
   const uint32_t* v_sz;
-  int batch, n_q, n_kv, G, T, t_cap, b, r, k_sel, s1, s2, s3;
+  int batch, n_q, n_kv, G, T, LT, t_cap, b, r, k_sel, nsa, s2, nsp;
   float scale;
-  float* logits;    // [batch*n_q][T]
-  float* scores;    // [batch*n_kv][T rounded up to 4]
-  float* k1part;    // [bh][s1][G][2]: split max, split sum of exp
-  uint32_t* hist;   // [bh][NBINS]
-  uint32_t* cnt;    // [bh][2]: select, pv workgroups done
-  int32_t* sel;     // [bh][KS]
-  int32_t* hit_t;   // [bh][KS]
-  int32_t* hit_s;   // [bh][KS]
-  int32_t* n_hit;   // [bh]
-  float* mref;      // [bh][G]: max logit after refinement
-  float* k3part;    // [bh][s3][G][1 + HD]
+  float* logits;    // [batch*n_q][LT] (rows padded to 4 floats)
+  float* part_a;    // [bh][nsa][G][PW]: split max / sum (+ value sums without refinement)
+  float* part_c;    // [bh][s2][G][PW]: chunk sums (without refinement)
+  float* part_p;    // [bh][nsp][G][PW]: pv sums (with refinement)
+  float* cmax;      // [bh][s2][G]: chunk max of the replaced logits
+  float* mref;      // [bh][G]: max logit after replacement
+  int32_t* sel_ws;  // [bh][KS]: selection
+  int32_t* slot_ws; // [bh][KS]: slot of each selected token, -1 = miss
+  uint32_t* hist;   // [bh][3][NBIN]
+  uint32_t* ctl;    // [bh][8]: arrival counters 0..4 and 6; word 5 of KV head 0: lookup-log base
+  uint32_t* cnts;   // [bh][s2][2]: per chunk (above, equal) counts
   const int32_t* sel_in;
   int32_t* sel_out;
   int32_t* hit_out;
   float* out;       // [batch][n_q][HD]
+  uint32_t* timeout;
   PoolDev pool;
 };
 
-// ---- block helpers (256 threads) ------------------------------------------------
-__device__ __forceinline__ float wg_max(float v, float* red) {
+__device__ __forceinline__ void merge_ms(float& m, float& z, float om, float oz) {
+  const float nm = fmaxf(m, om);
+  if (nm == -INFINITY) return;
+  z = (m > -INFINITY ? z * __expf(m - nm) : 0.f) + (om > -INFINITY ? oz * __expf(om - nm) : 0.f);
+  m = nm;
+}
+
+// B operand of a value-sum MFMA: the codes of dim d for this lane's 8 tokens
+// tk0..tk0+7 (rows of the LDS-staged codes, stride WPTP words), each as the fp16
+// value 1 + c/2^B, two per word.
+template <int B, int WPTP>
+__device__ __forceinline__ u32x4 code_operand(const uint32_t* s_vc, int tk0, int d) {
+  constexpr uint32_t cmask = (1u << B) - 1u;
+  const int bit = d * B, wi = bit >> 5, sh = bit & 31;
+  uint32_t c[8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__device__ __forceinline__ float wg_sum(float v, float* red) {
+  for (int e = 0; e < 8; ++e) c[e] = (s_vc[(tk0 + e) * WPTP + wi] >> sh) & cmask;
+  u32x4 bv;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  for (int e = 0; e < 4; ++e) bv[e] = (((c[2 * e + 1] << 16) | c[2 * e]) << (10 - B)) | 0x3C003C00u;
+  return bv;
 }
 
-// Suffix sums in place over n bins (n a multiple of 256) held in LDS.
-__device__ void wg_suffix_sum(uint32_t* h, int n, int* lds4) {
-  const int per = n / 256, t = threadIdx.x;
-  const int hi = n - per * t;  // this thread sums bins [hi - per, hi)
-  int s = 0;
-  for (int i = hi - 1; i >= hi - per; --i) s += (int)h[i];
-  int tot;
-  int run = wg_exclusive_scan(s, lds4, &tot);
-  for (int i = hi - 1; i >= hi - per; --i) {
-    run += (int)h[i];
-    h[i] = (uint32_t)run;
-  }
-  __syncthreads();
-}
-
-// ---- qk: logits + per-split softmax statistics -----------------------------------
-template <int B, int G>
-__global__ __launch_bounds__(256) void attn_qk_kernel(AttnArgs a) {
-  __shared__ float st[4][16][2];
-  __shared__ uint32_t s_ksz[qk_split(B)];
+// ---- split: logits, split softmax statistics (and value sums) --------------------
+template <int B, int G, bool PV>
+__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+  constexpr int WPT = HD * B / 32;  // code words per token
+  constexpr int WPTP = WPT + 1;     // padded LDS row (conflict-free column reads)
+  constexpr int UP = SA + 8;        // padded A-operand row (halves)
   constexpr int P = 32 / B, HP = P / 2;
+  __shared__ uint32_t s_vc[PV ? SA * WPTP : 1];
+  __shared__ uint32_t s_ksz[SA], s_vsz[PV ? SA : 1];
+  __shared__ float s_l[G][SA];
+  __shared__ _Float16 s_u[PV ? 2 * G : 1][UP];
+  __shared__ float s_red[4][3 * G + 1];
+  __shared__ float s_st[3 * G + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
   const int T = a.T;
-  constexpr int TPW = qk_tpw(B);
-  const int t_begin = split * qk_split(B), t_end = min(T, t_begin + qk_split(B));
+  const int t_begin = split * SA, n_here = min(SA, T - t_begin);
+  const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
+  SF_TS(0);
 
-  // this call's selection histogram and counters start at zero
-  for (int i = split * 256 + tid; i < NBINS; i += a.s1 * 256) a.hist[(size_t)bh * NBINS + i] = 0;
-  if (split == 0 && tid < 2) a.cnt[bh * 2 + tid] = 0;
+  // this call's selection histograms, counters and lookup-log base
+  if (a.k_sel > 0) {
+    uint32_t* h = a.hist + (size_t)bh * 3 * NBIN;
+    for (int i = split * 256 + tid; i < 3 * NBIN; i += a.nsa * 256) h[i] = 0;
+    if (split == 0 && tid == 0) {
+      for (int i = 0; i < 8; ++i)
+        if (i != 5) a.ctl[bh * 8 + i] = 0;
+      if (bh == 0) {
+        int base = -1;
+        if (a.pool.log_count) {
+          const uint32_t n = (uint32_t)(a.batch * a.n_kv) * (uint32_t)a.k_sel;
+          const uint32_t bse = atomicAdd(a.pool.log_count, n);
+          base = (bse + n <= (uint32_t)a.pool.log_cap) ? (int)bse : -1;
+        }
+        a.ctl[5] = (uint32_t)base;
+      }
+    }
+  } else if (split == 0 && tid == 0) {
+    a.ctl[bh * 8 + 4] = 0;
+  }
 
-  // B operand: q of head n = lane % 16 (zero for n >= G) over the 32 dims of lane
-  // group qg = lane / 16, in the same pair order as the key codes
+  // loads: (value codes -> LDS), scale words -> LDS, key codes -> registers
+  if constexpr (PV) {
+    const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
+    const int nv = n_here * WPT / 4;
+    for (int i = tid; i < nv; i += 256) {
+      const u32x4 v = __builtin_nontemporal_load(src + i);
+      const int w = 4 * i, tk = w / WPT, c = w - tk * WPT;
+      uint32_t* d = s_vc + tk * WPTP + c;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    s_vsz[tid] = tid < n_here ? a.v_sz[tok0 + tid] : 0u;
+  }
+  s_ksz[tid] = tid < n_here ? a.k_sz[tok0 + tid] : 0u;
   const int n = lane & 15, qg = lane >> 4;
-  const uint16_t* qrow = a.q + ((size_t)bi * a.n_q + (size_t)kvh * G + (n < G ? n : 0)) * HD;
-  uint16_t q32[32];
+  uint32_t kw[4][B];  // wave: 4 tiles of 16 tokens; lane: token n of each tile, dims 32qg..
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int tl = wave * 64 + 16 * u + n;
+    if (tl < n_here) {
+      const uint32_t* src = (const uint32_t*)(a.k_res + (tok0 + tl) * (HD * B / 8)) + qg * B;
+      if constexpr (B == 1) {
+        kw[u][0] = __builtin_nontemporal_load(src);
+      } else if constexpr (B == 2) {
+        const u32x2 v = __builtin_nontemporal_load((const u32x2*)src);
+        kw[u][0] = v.x; kw[u][1] = v.y;
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < B / 4; ++q4) {
+          const u32x4 v = __builtin_nontemporal_load((const u32x4*)src + q4);
+          kw[u][4 * q4] = v.x; kw[u][4 * q4 + 1] = v.y; kw[u][4 * q4 + 2] = v.z; kw[u][4 * q4 + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < B; ++w) kw[u][w] = 0;
+    }
+  }
+  // B operand: q of head n (zero for n >= G) over dims 32qg.., in the codes' pair order
+  h8_t bq[4];
+  float qsum;
   {
+    const uint16_t* qrow = a.q + ((size_t)bi * a.n_q + (size_t)kvh * G + (n < G ? n : 0)) * HD;
+    uint16_t q32[32];
     const u32x4* qv = (const u32x4*)(qrow + 32 * qg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -146,58 +206,30 @@ __global__ __launch_bounds__(256) void attn_qk_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) q32[8 * i + e] = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
     }
-  }
-  h8_t bq[4];
-  float qpart = 0.f;
+    float qpart = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int p = 4 * j + (e >> 1), h = e & 1;
-      const int w = p / HP, i = p % HP;
-      const float v = n < G ? h2f16(q32[P * w + i + h * HP]) : 0.f;
-      bq[j][e] = (_Float16)v;
-      qpart += v;
-    }
-  qpart += __shfl_xor(qpart, 16, 64);
-  qpart += __shfl_xor(qpart, 32, 64);
-  const float qsum = qpart;  // sum of q_n over all 128 dims
-
-  const size_t tok0 = (size_t)bh * a.t_cap;
-  const float scl = (float)(1u << (a.r + B));
-  constexpr uint32_t m1 = ((1u << B) - 1u) << (10 - B);
-  float run_m = -INFINITY, run_z = 0.f;
-  SF_TS(0);
-  for (int i = tid; i < t_end - t_begin; i += 256) s_ksz[i] = a.k_sz[tok0 + t_begin + i];
-  // each wave: TPW tiles of 16 tokens, all loads issued first
-  const int tw = t_begin + wave * 16 * TPW;
-  uint32_t wv[TPW][B];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tm = tw + 16 * u + (lane & 15);
-    if (tm < t_end) {
-      const uint32_t* src = (const uint32_t*)(a.k_res + (tok0 + tm) * (HD * B / 8)) + qg * B;
-      if constexpr (B == 1) {
-        wv[u][0] = __builtin_nontemporal_load(src);
-      } else if constexpr (B == 2) {
-        const u32x2 v = __builtin_nontemporal_load((const u32x2*)src);
-        wv[u][0] = v.x; wv[u][1] = v.y;
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < B / 4; ++q4) {
-          const u32x4 v = __builtin_nontemporal_load((const u32x4*)src + q4);
-          wv[u][4 * q4] = v.x; wv[u][4 * q4 + 1] = v.y; wv[u][4 * q4 + 2] = v.z; wv[u][4 * q4 + 3] = v.w;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int p = 4 * j + (e >> 1), hh = e & 1;
+        const int w = p / HP, i = p % HP;
+        const float v = n < G ? h2f16(q32[P * w + i + hh * HP]) : 0.f;
+        bq[j][e] = (_Float16)v;
+        qpart += v;
       }
-    } else {
-#pragma unroll
-      for (int w = 0; w < B; ++w) wv[u][w] = 0;
-    }
+    qpart += __shfl_xor(qpart, 16, 64);
+    qpart += __shfl_xor(qpart, 32, 64);
+    qsum = qpart;
   }
-  __syncthreads();  // s_ksz
+  __syncthreads();  // s_ksz (s_vsz, s_vc)
+
+  // ---- logits on MFMA ----
+  const float kscl = (float)(1u << (a.r + B));
+  constexpr uint32_t m1 = ((1u << B) - 1u) << (10 - B);
+  const bool want_logits = a.k_sel > 0;
+  float* lrow = a.logits + ((size_t)bi * a.n_q + kvh * G + (n < G ? n : 0)) * a.LT + t_begin;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    if (tw + 16 * u >= t_end) break;
+  for (int u = 0; u < 4; ++u) {
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -206,58 +238,212 @@ __global__ __launch_bounds__(256) void attn_qk_kernel(AttnArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int p = 4 * j + v, w = p / HP, i = p % HP;
         const int sh = (10 - B) - i * B;
-        const uint32_t t = sh >= 0 ? (wv[u][w] << sh) : (wv[u][w] >> (-sh));
+        const uint32_t t = sh >= 0 ? (kw[u][w] << sh) : (kw[u][w] >> (-sh));
         pr[v] = (t & (m1 | (m1 << 16))) | 0x3C003C00u;
       }
       const u32x4 pv = {pr[0], pr[1], pr[2], pr[3]};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, pv), bq[j], acc, 0, 0, 0);
     }
     if (n < G) {
-      const int tb = tw + 16 * u + 4 * qg;
+      const int tb = wave * 64 + 16 * u + 4 * qg;
+      float l4[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int t = tb + v;
-        if (t < t_end) {
-          const uint32_t szw = s_ksz[t - t_begin];
-          const float s = sf_h2f(szw), z = sf_h2f(szw >> 16);
-          const float l = a.scale * (z * qsum + (s * scl) * (acc[v] - qsum));
-          a.logits[((size_t)bi * a.n_q + kvh * G + n) * T + t] = l;
-          const float nm = fmaxf(run_m, l);
-          run_z = run_z * __expf(run_m - nm) + __expf(l - nm);
-          run_m = nm;
+        const uint32_t szw = s_ksz[tb + v];
+        const float s = sf_h2f(szw), z = sf_h2f(szw >> 16);
+        l4[v] = tb + v < n_here ? a.scale * (z * qsum + (s * kscl) * (acc[v] - qsum)) : -INFINITY;
+        s_l[n][tb + v] = l4[v];
+      }
+      if (want_logits) {
+        if (tb + 3 < n_here) {
+          *(f4_t*)(lrow + tb) = f4_t{l4[0], l4[1], l4[2], l4[3]};
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (tb + v < n_here) lrow[tb + v] = l4[v];
         }
       }
     }
   }
+  __syncthreads();  // s_l
   SF_TS(1);
-  // combine (m, z) over the 4 lane groups of each head, then over the waves
+
+  // ---- split max per head (and the largest value scale) ----
+  const int t = tid;  // this thread's token within the split
+  float sv = 0.f, zv = 0.f;
+  if constexpr (PV) {
+    const uint32_t vsz = s_vsz[t];
+    sv = sf_h2f(vsz);
+    zv = sf_h2f(vsz >> 16);
+  }
+  {
+    float mx[G + 1];
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float om = __shfl_xor(run_m, o, 64), oz = __shfl_xor(run_z, o, 64);
-    const float nm = fmaxf(run_m, om);
-    run_z = (run_m > -INFINITY ? run_z * __expf(run_m - nm) : 0.f) + (om > -INFINITY ? oz * __expf(om - nm) : 0.f);
-    run_m = nm;
+    for (int h = 0; h < G; ++h) mx[h] = s_l[h][t];
+    mx[G] = t < n_here ? sv : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int h = 0; h <= G; ++h) mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], o, 64));
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h <= G; ++h) s_red[wave][h] = mx[h];
+    __syncthreads();
+    if (tid <= G) s_st[tid] = fmaxf(fmaxf(s_red[0][tid], s_red[1][tid]), fmaxf(s_red[2][tid], s_red[3][tid]));
+    __syncthreads();
   }
-  if (lane < 16) {
-    st[wave][lane][0] = run_m;
-    st[wave][lane][1] = run_z;
+  // fp16 A operand scaled by 2^shift so that the largest weight * scale is below 2^14
+  const float smax = s_st[G] * (float)(1u << a.r);
+  int e2 = 0;
+  if (smax > 0.f) (void)frexpf(smax, &e2);
+  const int shift = smax > 0.f ? 14 - e2 : 0;
+  const float uscale = ldexpf((float)(1u << a.r), shift);
+  float ms[G], acc3[3 * G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) ms[h] = s_st[h];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float w = t < n_here ? __expf(s_l[h][t] - ms[h]) : 0.f;
+    acc3[3 * h] = w;
+    acc3[3 * h + 1] = acc3[3 * h + 2] = 0.f;
+    if constexpr (PV) {
+      const float u = w * sv * uscale;
+      const _Float16 hi = (_Float16)u;
+      const _Float16 lo = (_Float16)(u - (float)hi);
+      s_u[2 * h][t] = hi;
+      s_u[2 * h + 1][t] = lo;
+      acc3[3 * h + 1] = w * zv;
+      acc3[3 * h + 2] = (float)hi + (float)lo;
+    }
   }
+  __syncthreads();  // s_u written; s_red free
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int i = 0; i < 3 * G; ++i) acc3[i] += __shfl_xor(acc3[i], o, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
+
+  f4_t pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if constexpr (PV) {
+    // value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks; A rows
+    // 2h / 2h+1 = high / low part of head h's scaled weights
+#pragma unroll 2
+    for (int kb = 0; kb < SA / 32; ++kb) {
+      const int tk0 = 32 * kb + 8 * qg;
+      h8_t av;
+      if (n < 2 * G) {
+        av = *(const h8_t*)(&s_u[n][tk0]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = (_Float16)0.f;
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const u32x4 bv = code_operand<B, WPTP>(s_vc, tk0, 32 * wave + 16 * db + n);
+        pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // s_red
+  if (tid < 3 * G) s_st[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
   __syncthreads();
-  if (tid < G) {
-    float m = -INFINITY;
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, st[w][tid][0]);
-    float z = 0.f;
-    for (int w = 0; w < 4; ++w)
-      if (st[w][tid][0] > -INFINITY) z += st[w][tid][1] * __expf(st[w][tid][0] - m);
-    float* P2 = a.k1part + (((size_t)bh * a.s1 + split) * G + tid) * 2;
-    P2[0] = m;
-    P2[1] = z;
+  float* PS = a.part_a + ((size_t)bh * a.nsa + split) * G * PW;
+  if constexpr (PV) {
+    // lane group qg holds rows 4qg..4qg+3 = head 2qg (rows 0, 1) and head 2qg+1 (rows 2, 3)
+    const float back = ldexpf(1.f, B - shift);  // 2^B undoes the 1 + c/2^B form, 2^-shift the scaling
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * wave + 16 * db + n;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * qg + hh;
+        if (h < G) {
+          const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
+          PS[h * PW + d] = s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]);
+        }
+      }
+    }
   }
+  if (tid < G) {
+    PS[tid * PW + HD] = ms[tid];
+    PS[tid * PW + HD + 1] = s_st[3 * tid];
+  }
+  SF_TS(2);
 }
 
-// ---- select ------------------------------------------------------------------------
-// q_h . cK_lo for one head, cK_lo = the HD r-bit K refinement codes at the start of
-// a KV unit (16-byte aligned); r = 1 and 2 keep the unit's words in registers.
+// ---- select / merge ----------------------------------------------------------------
+__device__ __forceinline__ int blk_exclusive_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = SEL_T / 64;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) lds[wave] = incl;
+  __syncthreads();
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = lds[w];
+    if (w < wave) base += t;
+    sum += t;
+  }
+  *total = sum;
+  return base + incl - v;
+}
+
+// Over nb bins in LDS (nb = 1024 or 2048): the largest bin whose suffix count
+// reaches `need`.  Returns the bin; *above = count of the bins after it, *inbin =
+// its own count.  Every thread gets the answer.
+__device__ int blk_threshold(const uint32_t* h, int nb, int need, int* lds, int* above, int* inbin) {
+  const int per = nb / SEL_T;  // 1 or 2
+  const int t = threadIdx.x;
+  const int top = nb - 1 - per * t;  // this thread's bins: top, top-1, ..
+  if (t == 0) {
+    lds[32] = 0;
+    lds[33] = 0;
+    lds[34] = 0;
+  }
+  int s = 0;
+  for (int i = 0; i < per; ++i) s += (int)h[top - i];
+  int tot;
+  const int ex = blk_exclusive_scan(s, lds, &tot);
+  int run = ex;
+  for (int i = 0; i < per; ++i) {
+    const int c = (int)h[top - i];
+    if (run < need && run + c >= need) {
+      lds[32] = top - i;
+      lds[33] = run;
+      lds[34] = c;
+    }
+    run += c;
+  }
+  __syncthreads();
+  const int bin = lds[32];
+  *above = lds[33];
+  *inbin = lds[34];
+  __syncthreads();
+  return bin;
+}
+
+// This workgroup's contribution is written; count it and wait until all n chunks
+// of the KV head have arrived.
+__device__ __forceinline__ void chunk_barrier(uint32_t* ctr, uint32_t n, uint32_t* timeout) {
+  sf_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    (void)sf_wait_word(ctr, n, timeout);
+  }
+  __syncthreads();
+}
+
+// q_h . cK_lo for the HD r-bit key refinement codes at the start of a unit
 template <int R>
 __device__ __forceinline__ float kref_dot_r(const uint8_t* unit, const float* qh) {
   constexpr int NW = HD * R / 32;
@@ -283,291 +469,269 @@ __device__ __forceinline__ float kref_dot(const uint8_t* unit, int r, const floa
   return dot;
 }
 
-__device__ __forceinline__ float wgN_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float m = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
-  return m;
-}
-
-__device__ __forceinline__ float wgN_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float m = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m += red[w];
-  return m;
-}
-
-__device__ __forceinline__ int wgN_exclusive_scan(int v, int* lds, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  __syncthreads();
-  if (lane == 63) lds[wave] = incl;
-  __syncthreads();
-  int base = 0, sum = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int t = lds[w];
-    if (w < wave) base += t;
-    sum += t;
-  }
-  *total = sum;
-  return base + incl - v;
-}
-
-// Suffix sums over NBINS bins with SEL_T threads (2 bins each), then the largest
-// bin whose suffix count is >= need; *above = suffix count of the next bin.
-__device__ int sel_threshold_bin(uint32_t* h, int nb, int need, int* lds, int* above) {
-  const int t = threadIdx.x;
-  const int i0 = NBINS - 1 - 2 * t, i1 = i0 - 1;
-  const int v0 = (int)h[i0], v1 = (int)h[i1];
-  int tot;
-  const int ex = wgN_exclusive_scan(v0 + v1, lds, &tot);
-  __syncthreads();
-  h[i0] = (uint32_t)(ex + v0);
-  h[i1] = (uint32_t)(ex + v0 + v1);
-  if (t == 0) lds[40] = 0;
-  __syncthreads();
-  for (int i = t; i < nb; i += SEL_T)
-    if ((int)h[i] >= need && (i + 1 == nb || (int)h[i + 1] < need)) lds[40] = i;
-  __syncthreads();
-  const int bin = lds[40];
-  *above = bin + 1 < nb ? (int)h[bin + 1] : 0;
-  __syncthreads();
-  return bin;
-}
-
 template <int G>
 __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
-  __shared__ uint32_t lh[NBINS];
-  __shared__ float s_m[G], s_iz[G], s_mref[G];
-  __shared__ float red[16];
-  __shared__ int lds[48];
+  __shared__ uint32_t lh[NBIN];
+  __shared__ int s_tok[CB];
   __shared__ float qf[G][HD];
-  const int tid = threadIdx.x;
+  __shared__ float s_m[G], s_iz[G];
+  __shared__ float s_wm[SEL_T / 64][G][2];
+  __shared__ int lds[40];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
-  const int T = a.T, ks = a.k_sel;
+  const int T = a.T, ks = a.k_sel, s2 = a.s2;
   const int KS = ks > 0 ? ks : 1;
-
+  const int c0 = chunk * CB;
+  uint32_t* ctl = a.ctl + bh * 8;
   SF_TS(4);
-  // global softmax statistics of the resident logits: split partials -> LDS,
-  // then one thread per head combines them
+  if (ks > 0)
+    for (int i = tid; i < G * HD; i += SEL_T) {
+      const int h = i / HD, d = i - h * HD;
+      qf[h][d] = h2f16(a.q[((size_t)bi * a.n_q + kvh * G + h) * HD + d]);
+    }
+
+  // ---- softmax max / sum per head from the split statistics ----
   {
-    float* pm = (float*)lh;  // reuse the histogram area: [G][s1] max, then sums
-    const int n = G * a.s1;
-    for (int i = tid; i < n && i < NBINS / 2; i += SEL_T) {
-      const float* P2 = a.k1part + ((size_t)bh * a.s1 * G + i) * 2;  // (split, head) order
-      pm[i] = P2[0];
-      pm[NBINS / 2 + i] = P2[1];
+    constexpr int NJ = SEL_T / G;
+    const int h = tid % G, j = tid / G;
+    float m = -INFINITY, z = 0.f;
+    const float* PA = a.part_a + (size_t)bh * a.nsa * G * PW;
+    for (int s = j; s < a.nsa; s += NJ) merge_ms(m, z, PA[(s * G + h) * PW + HD], PA[(s * G + h) * PW + HD + 1]);
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) merge_ms(m, z, __shfl_xor(m, o, 64), __shfl_xor(z, o, 64));
+    if (lane < G) {
+      s_wm[wave][lane][0] = m;
+      s_wm[wave][lane][1] = z;
     }
     __syncthreads();
     if (tid < G) {
-      float m = -INFINITY;
-      for (int sp = 0; sp < a.s1; ++sp) m = fmaxf(m, pm[sp * G + tid]);
-      float z = 0.f;
-      for (int sp = 0; sp < a.s1; ++sp) {
-        const float ms = pm[sp * G + tid];
-        if (ms > -INFINITY) z += pm[NBINS / 2 + sp * G + tid] * __expf(ms - m);
-      }
-      s_m[tid] = m;
-      s_iz[tid] = 1.f / z;
+      float mm = -INFINITY, zz = 0.f;
+      for (int w = 0; w < SEL_T / 64; ++w) merge_ms(mm, zz, s_wm[w][tid][0], s_wm[w][tid][1]);
+      s_m[tid] = mm;
+      s_iz[tid] = 1.f / zz;
     }
     __syncthreads();
   }
+  SF_TS(5);
 
   if (ks == 0) {
-    if (chunk == 0 && tid < G) a.mref[bh * G + tid] = s_m[tid];
-    if (chunk == 0 && tid == 0) a.n_hit[bh] = 0;
-    return;
-  }
-
-  int* sel = a.sel + (size_t)bh * KS;
-  float* sc = a.scores + (size_t)bh * ((T + 3) & ~3);  // rows padded to 16 bytes
-  if (a.sel_in == nullptr) {
-    SF_TS(5);
-    // scores of this chunk + first-level histogram
-    for (int i = tid; i < NBINS; i += SEL_T) lh[i] = 0;
-    __syncthreads();
-    const int c0 = chunk * SPLIT2, c1 = min(T, c0 + SPLIT2);
-    for (int t = c0 + tid; t < c1; t += SEL_T) {
-      float v = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        v += expf(a.logits[((size_t)bi * a.n_q + kvh * G + h) * T + t] - s_m[h]) * s_iz[h];
-      sf_put(sc + t, v);
-      atomicAdd(&lh[__float_as_uint(v) >> 21], 1u);
+    // ---- no refinement: this chunk's value sums relative to the global max ----
+    float* PC = a.part_c + ((size_t)bh * s2 + chunk) * G * PW;
+    if (tid < G * HD) {
+      const int s_lo = c0 / SA, s_hi = min(a.nsa, (c0 + CB) / SA);
+      const int h = tid / HD, d = tid - h * HD;
+      const float* PA = a.part_a + (size_t)bh * a.nsa * G * PW;
+      float nc = 0.f, zc = 0.f;
+      const float mh = s_m[h];
+      for (int s = s_lo; s < s_hi; ++s) {
+        const float* r = PA + (s * G + h) * PW;
+        const float f = __expf(r[HD] - mh);
+        nc = fmaf(f, r[d], nc);
+        if (d == 0) zc = fmaf(f, r[HD + 1], zc);
+      }
+      sf_put(PC + h * PW + d, nc);
+      if (d == 0) sf_put(PC + h * PW + HD + 1, zc);
     }
-    __syncthreads();
-    for (int i = tid; i < NBINS; i += SEL_T)
-      if (lh[i]) atomicAdd(&a.hist[(size_t)bh * NBINS + i], lh[i]);
     sf_drain();
     __syncthreads();
     if (tid == 0)
-      lds[44] = __hip_atomic_fetch_add(&a.cnt[bh * 2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)(a.s2 - 1);
+      lds[36] = __hip_atomic_fetch_add(ctl + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(s2 - 1);
     __syncthreads();
-    SF_TS(6);
-    if (!lds[44]) return;
+    if (!lds[36]) return;
+    // last chunk: out = sum_c N_c / sum_c z_c (all relative to the same max)
+    if (tid < G * HD) {
+      const int h = tid / HD, d = tid - h * HD;
+      const float* PB = a.part_c + (size_t)bh * s2 * G * PW;
+      float num = 0.f, den = 0.f;
+      for (int c0_ = 0; c0_ < s2; c0_ += 8) {
+        float vn[8], vd[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = min(c0_ + k, s2 - 1);
+          vn[k] = sf_get(PB + (c * G + h) * PW + d);
+          vd[k] = sf_get(PB + (c * G + h) * PW + HD + 1);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (c0_ + k < s2) {
+            num += vn[k];
+            den += vd[k];
+          }
+      }
+      a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
+    }
+    return;
+  }
 
-    // ---- last workgroup of this KV head: exact threshold by radix select ----
-    // thread t holds tokens [round*SEL_T*SPR + t*SPR, +SPR) of each round
-    const int rounds = (T + SEL_T * SPR - 1) / (SEL_T * SPR);
-    float sv[SPR];
-#define SF_LOAD_ROUND(rd)                                                                 \
-  do {                                                                                    \
-    const int base_ = (rd) * SEL_T * SPR + tid * SPR;                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < SPR; i_ += 4) {                               \
-      _Pragma("unroll") for (int e_ = 0; e_ < 4; ++e_) sv[i_ + e_] = base_ + i_ + e_ < T ? sf_get(sc + base_ + i_ + e_) : -1.f; \
-    }                                                                                     \
-  } while (0)
-    for (int i = tid; i < NBINS; i += SEL_T) lh[i] = sf_get(a.hist + (size_t)bh * NBINS + i);
-    __syncthreads();
-    int above;
-    uint32_t prefix;
-    int need = ks;
+  int off = 0, cnt = 0;  // this chunk's range of selection positions
+  if (a.sel_in == nullptr) {
+    // ---- scores of this chunk's tokens (TPT consecutive per thread) ----
+    uint32_t key[TPT];
+    const int tb = c0 + TPT * tid;
     {
-      const int bin = sel_threshold_bin(lh, NBINS, need, lds, &above);
-      need -= above;
-      prefix = (uint32_t)bin << 21;
-    }
-    if (rounds == 1) SF_LOAD_ROUND(0);
-    for (int level = 0; level < 2; ++level) {
-      const int sh = level == 0 ? 10 : 0, nb = level == 0 ? 2048 : 1024;
-      const uint32_t pmask = level == 0 ? 0xFFE00000u : 0xFFFFFC00u;
-      for (int i = tid; i < NBINS; i += SEL_T) lh[i] = 0;
-      __syncthreads();
-      for (int rd = 0; rd < rounds; ++rd) {
-        if (rounds > 1) SF_LOAD_ROUND(rd);
+      float sc[TPT] = {};
 #pragma unroll
-        for (int i = 0; i < SPR; ++i) {
-          const uint32_t key = __float_as_uint(sv[i]);
-          if (sv[i] >= 0.f && (key & pmask) == prefix) atomicAdd(&lh[(key >> sh) & (uint32_t)(nb - 1)], 1u);
+      for (int h = 0; h < G; ++h) {
+        const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + tb;
+        f4_t l4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (tb + 3 < T) {
+          l4 = *(const f4_t*)lr;
+        } else {
+#pragma unroll
+          for (int i = 0; i < TPT; ++i)
+            if (tb + i < T) l4[i] = lr[i];
         }
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) sc[i] += __expf(l4[i] - s_m[h]) * s_iz[h];
       }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) key[i] = __float_as_uint(sc[i]);
+    }
+    // ---- radix select of the k-th key over all chunks of this KV head ----
+    // selected: (key >> sh) > tv, or (key >> sh) == tv within the first `need`
+    uint32_t* gh = a.hist + (size_t)bh * 3 * NBIN;
+    int need = ks, sh = 31;
+    uint32_t tv = 0;
+    for (int level = 0; level < 3; ++level) {
+      const int lsh = level == 0 ? 20 : (level == 1 ? 10 : 0);
+      const int nb = level == 0 ? 2048 : 1024;
+      for (int i = tid; i < nb; i += SEL_T) lh[i] = 0;
       __syncthreads();
-      const int bin = sel_threshold_bin(lh, nb, need, lds, &above);
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+        if (tb + i < T && (level == 0 || (key[i] >> sh) == tv))
+          atomicAdd(&lh[(key[i] >> lsh) & (uint32_t)(nb - 1)], 1u);
+      __syncthreads();
+      uint32_t* g = gh + level * NBIN;
+      for (int i = tid; i < nb; i += SEL_T)
+        if (lh[i]) atomicAdd(&g[i], lh[i]);
+      chunk_barrier(ctl + level, (uint32_t)s2, a.timeout);
+      for (int i = tid; i < nb; i += SEL_T) lh[i] = sf_get(g + i);
+      __syncthreads();
+      int above, inbin;
+      const uint32_t bin = (uint32_t)blk_threshold(lh, nb, need, lds, &above, &inbin);
       need -= above;
-      prefix |= (uint32_t)bin << sh;
+      tv = level == 0 ? bin : ((tv << 10) | bin);
+      sh = lsh;
+      if (need == inbin) break;  // the whole bin is taken: no finer level needed
     }
-    SF_TS(7);
-    const uint32_t thr = prefix;
-    // ordered compaction, round by round
-    int written = 0, eq_seen_total = 0;
-    for (int rd = 0; rd < rounds; ++rd) {
-      if (rounds > 1) SF_LOAD_ROUND(rd);
-      int gt = 0, eq = 0;
+    SF_TS(6);
+    // ---- counts above / at the threshold, exchanged between the chunks ----
+    int gt = 0, eq = 0;
 #pragma unroll
-      for (int i = 0; i < SPR; ++i) {
-        const uint32_t key = __float_as_uint(sv[i]);
-        const bool valid = sv[i] >= 0.f;
-        gt += valid && key > thr;
-        eq += valid && key == thr;
-      }
-      int tot_eq, tot;
-      const int eq_before = eq_seen_total + wgN_exclusive_scan(eq, lds, &tot_eq);
-      const int take_eq = max(0, min(eq, need - eq_before));
-      int off = written + wgN_exclusive_scan(gt + take_eq, lds, &tot);
-      int seen = 0;
-      const int base = rd * SEL_T * SPR + tid * SPR;
-#pragma unroll
-      for (int i = 0; i < SPR; ++i) {
-        const uint32_t key = __float_as_uint(sv[i]);
-        if (!(sv[i] >= 0.f)) continue;
-        if (key > thr) {
-          sel[off++] = base + i;
-        } else if (key == thr) {
-          if (seen < take_eq) sel[off++] = base + i;
-          ++seen;
+    for (int i = 0; i < TPT; ++i) {
+      const bool valid = tb + i < T;
+      gt += valid && (key[i] >> sh) > tv;
+      eq += valid && (key[i] >> sh) == tv;
+    }
+    int gt_c, eq_c;
+    (void)blk_exclusive_scan(gt, lds, &gt_c);
+    const int eq_before = blk_exclusive_scan(eq, lds, &eq_c);
+    if (tid == 0) {
+      sf_put(a.cnts + ((size_t)bh * s2 + chunk) * 2, (uint32_t)gt_c);
+      sf_put(a.cnts + ((size_t)bh * s2 + chunk) * 2 + 1, (uint32_t)eq_c);
+    }
+    chunk_barrier(ctl + 3, (uint32_t)s2, a.timeout);
+    if (wave == 0) {
+      // prefix over chunks; equal keys are taken in token (= chunk) order
+      int run_sel = 0, run_eq = 0;
+      for (int cb = 0; cb < s2; cb += 64) {
+        const int c = cb + lane;
+        int g_ = 0, e_ = 0;
+        if (c < s2) {
+          g_ = (int)sf_get(a.cnts + ((size_t)bh * s2 + c) * 2);
+          e_ = (int)sf_get(a.cnts + ((size_t)bh * s2 + c) * 2 + 1);
         }
+        int ie = e_;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(ie, o, 64);
+          if (lane >= o) ie += v;
+        }
+        const int eb = run_eq + ie - e_;  // equal keys before chunk c
+        const int tk = max(0, min(e_, need - eb));
+        int is = g_ + tk;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(is, o, 64);
+          if (lane >= o) is += v;
+        }
+        if (c == chunk) {
+          lds[37] = run_sel + is - (g_ + tk);
+          lds[38] = g_ + tk;
+          lds[39] = eb;
+        }
+        run_sel += __shfl(is, 63, 64);
+        run_eq += __shfl(ie, 63, 64);
       }
-      written += tot;
-      eq_seen_total += tot_eq;
     }
-#undef SF_LOAD_ROUND
+    __syncthreads();
+    off = lds[37];
+    cnt = lds[38];
+    const int eq_chunk_before = lds[39];
+    // ---- ordered compaction of this chunk's selection into LDS ----
+    int nsel = 0;
+    bool take[TPT];
+    {
+      int eseen = eq_chunk_before + eq_before;
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const bool valid = tb + i < T;
+        const bool g_ = valid && (key[i] >> sh) > tv;
+        const bool e_ = valid && (key[i] >> sh) == tv;
+        take[i] = g_ || (e_ && eseen < need);
+        eseen += e_;
+        nsel += take[i];
+      }
+    }
+    int tot;
+    int pos = blk_exclusive_scan(nsel, lds, &tot);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+      if (take[i] && pos < CB) s_tok[pos++] = tb + i;
   } else {
-    if (chunk != 0) return;
-    for (int j = tid; j < ks; j += SEL_T) sel[j] = a.sel_in[(size_t)bh * ks + j];
+    // external selection: chunk c takes positions [c*ks/s2, (c+1)*ks/s2)
+    off = (int)(((long long)chunk * ks) / s2);
+    cnt = (int)(((long long)(chunk + 1) * ks) / s2) - off;
+    for (int j = tid; j < cnt; j += SEL_T) s_tok[j] = a.sel_in[(size_t)bh * ks + off + j];
   }
-  // sel[] is read back by other threads of this workgroup
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // (off, cnt) are only out of range after a timed-out wait
+  off = min(max(off, 0), ks);
+  cnt = min(max(cnt, 0), min(CB, ks - off));
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  SF_TS(7);
 
-  SF_TS(8);
-  // ---- lookup in selection order ----
+  // ---- lookups (in selection order) and, for the hits, the logits become
+  //      l' = l + scale * s_K * (q . cK_lo); item m = (selected j, head m % G) ----
   const size_t unit0 = (size_t)bh * a.t_cap;
-  const int r = a.r;
-  (void)r;
-  int* hit_t = a.hit_t + (size_t)bh * KS;
-  int* hit_s = a.hit_s + (size_t)bh * KS;
-  if (tid == 0) {
-    int base = -1;
-    if (a.pool.log_count) {
-      const uint32_t bse = atomicAdd(a.pool.log_count, (uint32_t)ks);
-      base = (bse + (uint32_t)ks <= (uint32_t)a.pool.log_cap) ? (int)bse : -1;
-    }
-    lds[45] = base;
-  }
-  __syncthreads();
-  const int base = lds[45];
-  const int jpt = (ks + SEL_T - 1) / SEL_T;
-  const int j0 = tid * jpt, j1 = min(ks, j0 + jpt);
-  int nh = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int t = sel[j];
-    const int slot = (a.pool.unit2slot && t >= 0 && t < T) ? a.pool.unit2slot[unit0 + t] : -1;
-    nh += slot >= 0;
-  }
-  int n_hits;
-  int pos = wgN_exclusive_scan(nh, lds, &n_hits);
-  for (int j = j0; j < j1; ++j) {
-    const int t = sel[j];
-    const bool ok = t >= 0 && t < T;
-    const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
-    if (a.sel_out) a.sel_out[(size_t)bh * ks + j] = t;
-    if (a.hit_out) a.hit_out[(size_t)bh * ks + j] = slot;
-    if (base >= 0) {
-      a.pool.log_units[base + j] = ok ? (int)(unit0 + t) : -1;
-      a.pool.log_slots[base + j] = slot;
-    }
-    if (slot >= 0) {
-      hit_t[pos] = t;
-      hit_s[pos] = slot;
-      ++pos;
-    }
-  }
-  for (int i = tid; i < G * HD; i += SEL_T) {
-    const int h = i / HD, d = i - h * HD;
-    qf[h][d] = h2f16(a.q[((size_t)bi * a.n_q + kvh * G + h) * HD + d]);
-  }
-  if (tid < G) s_mref[tid] = s_m[tid];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  SF_TS(9);
-  // ---- refined logits of the hit tokens: l' = l + scale * s_K * (q . cK_lo) ----
+  const int base = a.pool.log_count ? (int)sf_get(a.ctl + 5) : -1;
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-  for (int m = tid; m < n_hits * G; m += SEL_T) {
-    const int hh = m % G, mi = m / G;
-    const int t = hit_t[mi];
-    const float dot = kref_dot(a.pool.slots + (size_t)hit_s[mi] * a.pool.unit_bytes, a.r, qf[hh]);
-    const float s = sf_h2f(a.k_sz[unit0 + t]);
-    float* lp = a.logits + ((size_t)bi * a.n_q + kvh * G + hh) * T + t;
-    const float l2 = *lp + a.scale * (s * dot);
+#pragma nounroll
+  for (int m = tid; m < cnt * G; m += SEL_T) {
+    const int j = m / G, hh = m - j * G;
+    const int t = s_tok[j];
+    const bool ok = t >= 0 && t < T;
+    const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
+    float* lp = a.logits + ((size_t)bi * a.n_q + kvh * G + hh) * a.LT + (ok ? t : 0);
+    const float l = *lp;
+    const float s = sf_h2f(a.k_sz[unit0 + (ok ? t : 0)]);
+    if (hh == 0) {
+      const size_t p = (size_t)bh * ks + off + j;
+      a.sel_ws[(size_t)bh * KS + off + j] = t;
+      a.slot_ws[(size_t)bh * KS + off + j] = slot;
+      if (a.sel_out) a.sel_out[p] = t;
+      if (a.hit_out) a.hit_out[p] = slot;
+      if (base >= 0) {
+        a.pool.log_units[base + p] = ok ? (int)(unit0 + t) : -1;
+        a.pool.log_slots[base + p] = slot;
+      }
+    }
+    if (slot < 0) continue;
+    const float dot = kref_dot(a.pool.slots + (size_t)slot * a.pool.unit_bytes, a.r, qf[hh]);
+    const float l2 = l + a.scale * (s * dot);
     *lp = l2;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -575,148 +739,268 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float v = wgN_max(mloc[h], red);
-    if (tid == 0) s_mref[h] = fmaxf(s_mref[h], v);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mloc[h] = fmaxf(mloc[h], __shfl_xor(mloc[h], o, 64));
   }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_wm[wave][h][0] = mloc[h];
   __syncthreads();
-  if (tid < G) a.mref[bh * G + tid] = s_mref[tid];
-  if (tid == 0) a.n_hit[bh] = n_hits;
-  SF_TS(10);
+  if (tid < G) {
+    float mm = s_m[tid];
+    for (int w = 0; w < SEL_T / 64; ++w) mm = fmaxf(mm, s_wm[w][tid][0]);
+    sf_put(a.cmax + ((size_t)bh * s2 + chunk) * G + tid, mm);
+  }
+  SF_TS(8);
+  sf_drain();
+  __syncthreads();
+  if (tid == 0)
+    lds[36] = __hip_atomic_fetch_add(ctl + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(s2 - 1);
+  __syncthreads();
+  if (!lds[36]) return;
+  // last chunk: the max logit after replacement
+  if (tid < G) {
+    float mm = -INFINITY;
+    for (int c0_ = 0; c0_ < s2; c0_ += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = sf_get(a.cmax + ((size_t)bh * s2 + min(c0_ + k, s2 - 1)) * G + tid);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mm = fmaxf(mm, v[k]);
+    }
+    a.mref[bh * G + tid] = mm;
+  }
+  SF_TS(9);
 }
 
-// ---- pv: weighted value sums with the final weights ------------------------------
+// ---- pv: final weights, value sums, hit refinements, merge ---------------------------
 template <int B, int G>
 __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
-  constexpr int SPLIT3 = pv_split(B);
-  constexpr int WPT = HD * B / 32;  // code words per token
-  __shared__ float w[G][SPLIT3];
-  __shared__ uint32_t s_vsz[SPLIT3];
-  __shared__ uint32_t s_code[SPLIT3 * WPT];
-  __shared__ float accr[4][G][HD];
-  __shared__ float red[4];
-  __shared__ float s_z[G], s_zz[G], s_m[G];
-  __shared__ int flag;
+  constexpr int SP = pv_tokens(B);
+  constexpr int WPT = HD * B / 32, WPTP = WPT + 1, UP = SP + 8;
+  constexpr int TPW = SP / 256;  // tokens per thread in the weight phase
+  __shared__ uint32_t s_vc[SP * WPTP];
+  __shared__ _Float16 s_u[2 * G][UP];
+  __shared__ uint32_t s_vsz[SP];
+  __shared__ float s_w[G][SP];
+  __shared__ float s_acc[4][G][HD];
+  __shared__ float s_red[4][3 * G + 1];
+  __shared__ float s_st[3 * G + 1];
+  __shared__ int s_rng[4][2];
+  __shared__ int s_flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
   const int T = a.T;
-  const int t_begin = split * SPLIT3, t_end = min(T, t_begin + SPLIT3);
-  const int n_here = max(0, t_end - t_begin);
-  const size_t tok0 = (size_t)bh * a.t_cap;
-  SF_TS(11);
-  // stage this split's value codes (16-byte loads) and scale words
+  const int t_begin = split * SP, n_here = min(SP, T - t_begin);
+  const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
+  SF_TS(12);
+  // loads: value codes -> LDS, this thread's scale words and final logits -> registers
   {
-    const u32x4* src = (const u32x4*)(a.v_res + (tok0 + t_begin) * (HD * B / 8));
+    const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
     const int nv = n_here * WPT / 4;
     for (int i = tid; i < nv; i += 256) {
       const u32x4 v = __builtin_nontemporal_load(src + i);
-      s_code[4 * i] = v.x; s_code[4 * i + 1] = v.y; s_code[4 * i + 2] = v.z; s_code[4 * i + 3] = v.w;
+      const int w = 4 * i, tk = w / WPT, c = w - tk * WPT;
+      uint32_t* d = s_vc + tk * WPTP + c;
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
   }
-  if (tid < G) s_m[tid] = a.mref[bh * G + tid];
-  __syncthreads();
-  // weights, their sum, and the sum of weight * zero-point per head
-  float zs[G], zz[G];
+  const int tl0 = TPW * tid;  // this thread's first token within the split
+  uint32_t vsz[TPW];
+  float lg[G][TPW];
 #pragma unroll
-  for (int h = 0; h < G; ++h) zs[h] = zz[h] = 0.f;
-  for (int tl = tid; tl < n_here; tl += 256) {
-    const int t = t_begin + tl;
-    const uint32_t vsz = a.v_sz[tok0 + t];
-    s_vsz[tl] = vsz;
-    const float zv = sf_h2f(vsz >> 16);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float e = __expf(a.logits[((size_t)bi * a.n_q + kvh * G + h) * T + t] - s_m[h]);
-      w[h][tl] = e;
-      zs[h] += e;
-      zz[h] = fmaf(e, zv, zz[h]);
-    }
-  }
+  for (int i = 0; i < TPW; ++i) vsz[i] = tl0 + i < n_here ? a.v_sz[tok0 + tl0 + i] : 0u;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float v1 = wg_sum(zs[h], red);
-    if (tid == 0) s_z[h] = v1;
-    const float v2 = wg_sum(zz[h], red);
-    if (tid == 0) s_zz[h] = v2;
+    const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + t_begin + tl0;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) lg[h][i] = tl0 + i < n_here ? lr[i] : -INFINITY;
+  }
+  float mh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mh[h] = a.mref[bh * G + h];
+  // selected positions of this split's tokens: [#sel < t_begin, #sel < t_end)
+  const int* sel = a.sel_ws + (size_t)bh * a.k_sel;
+  int below0 = 0, below1 = 0;
+  for (int j = tid; j < a.k_sel; j += 256) {
+    const int t = sel[j];
+    below0 += t < t_begin;
+    below1 += t < t_begin + n_here;
+  }
+  // largest value scale of the split
+  float smx = 0.f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    s_vsz[tl0 + i] = vsz[i];
+    smx = fmaxf(smx, sf_h2f(vsz[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    smx = fmaxf(smx, __shfl_xor(smx, o, 64));
+    below0 += __shfl_xor(below0, o, 64);
+    below1 += __shfl_xor(below1, o, 64);
+  }
+  if (lane == 0) {
+    s_red[wave][0] = smx;
+    s_rng[wave][0] = below0;
+    s_rng[wave][1] = below1;
   }
   __syncthreads();
-  SF_TS(12);
-  // sum_t (w_t * s'_t) * c_t[d]; lane owns dims 2*lane, 2*lane+1; wave w takes tokens w, w+4, ...
-  float acc0[G], acc1[G];
+  const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
+  const int hit_hi = (s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]);
+  smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
+  const float smax = smx * (float)(1u << a.r);
+  int e2 = 0;
+  if (smax > 0.f) (void)frexpf(smax, &e2);
+  const int shift = smax > 0.f ? 14 - e2 : 0;
+  const float uscale = ldexpf((float)(1u << a.r), shift);
+  float acc3[3 * G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc0[h] = acc1[h] = 0.f;
-  const float sres = (float)(1u << a.r);
-  const int bit0 = 2 * lane * B;
-#pragma unroll 4
-  for (int tl = wave; tl < n_here; tl += 4) {
-    const uint32_t word = s_code[tl * WPT + (bit0 >> 5)];
-    const float sv = sf_h2f(s_vsz[tl]) * sres;
-    const float c0 = (float)((word >> (bit0 & 31)) & ((1u << B) - 1u));
-    const float c1 = (float)((word >> ((bit0 & 31) + B)) & ((1u << B) - 1u));
+  for (int i = 0; i < 3 * G; ++i) acc3[i] = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float we = w[h][tl] * sv;
-      acc0[h] = fmaf(we, c0, acc0[h]);
-      acc1[h] = fmaf(we, c1, acc1[h]);
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const float w = __expf(lg[h][i] - mh[h]);
+      s_w[h][tl0 + i] = w;
+      const float u = w * sf_h2f(vsz[i]) * uscale;
+      const _Float16 hi = (_Float16)u;
+      const _Float16 lo = (_Float16)(u - (float)hi);
+      s_u[2 * h][tl0 + i] = hi;
+      s_u[2 * h + 1][tl0 + i] = lo;
+      acc3[3 * h] += w;
+      acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
+      acc3[3 * h + 2] += (float)hi + (float)lo;
+    }
+  __syncthreads();  // s_u, s_vc, s_vsz written; s_red free
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int i = 0; i < 3 * G; ++i) acc3[i] += __shfl_xor(acc3[i], o, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
+  SF_TS(13);
+
+  // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
+  const int n = lane & 15, qg = lane >> 4;
+  f4_t pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 2
+  for (int kb = 0; kb < SP / 32; ++kb) {
+    const int tk0 = 32 * kb + 8 * qg;
+    h8_t av;
+    if (n < 2 * G) {
+      av = *(const h8_t*)(&s_u[n][tk0]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = (_Float16)0.f;
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const u32x4 bv = code_operand<B, WPTP>(s_vc, tk0, 32 * wave + 16 * db + n);
+      pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
     }
   }
-  // refinement of the hit tokens that fall in this split: + w * s_V * cV_lo
-  if (wave == 0 && a.k_sel > 0) {
-    const int nh = a.n_hit[bh];
-    const int KS = a.k_sel;
-    const int* hit_t = a.hit_t + (size_t)bh * KS;
-    const int* hit_s = a.hit_s + (size_t)bh * KS;
+
+  // ---- hits in this split: + w * s_V * cV_lo; wave w takes hits w, w+4, ..; lane: dims 2l, 2l+1 ----
+  float hacc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) hacc[h][0] = hacc[h][1] = 0.f;
+  {
+    // the selection ascends, so this split's hits are positions [hit_lo, hit_hi)
+    const int* slots = a.slot_ws + (size_t)bh * a.k_sel;
     const int r = a.r;
-    int lo = 0, hi = nh;  // first hit with token >= t_begin (hit tokens ascend)
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (hit_t[mid] < t_begin) lo = mid + 1; else hi = mid;
-    }
-    for (int m = lo; m < nh; ++m) {
-      const int t = hit_t[m];
-      if (t >= t_end) break;
-      const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)hit_s[m] * a.pool.unit_bytes);
-      const float sv = sf_h2f(s_vsz[t - t_begin]);
-      const float c0 = (float)field(unit, HD * r + 2 * lane * r, r);
-      const float c1 = (float)field(unit, HD * r + (2 * lane + 1) * r, r);
+    for (int j = hit_lo + wave; j < hit_hi; j += 4) {
+      const int t = sel[j] - t_begin;
+      const int slot = slots[j];
+      if (slot < 0 || t < 0 || t >= n_here) continue;
+      const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
+      const float s = sf_h2f(s_vsz[t]);
+      const float c0 = s * (float)field(unit, HD * r + 2 * lane * r, r);
+      const float c1 = s * (float)field(unit, HD * r + (2 * lane + 1) * r, r);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float we = w[h][t - t_begin] * sv;
-        acc0[h] = fmaf(we, c0, acc0[h]);
-        acc1[h] = fmaf(we, c1, acc1[h]);
+        hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
+        hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
       }
     }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    accr[wave][h][2 * lane] = acc0[h];
-    accr[wave][h][2 * lane + 1] = acc1[h];
+    s_acc[wave][h][2 * lane] = hacc[h][0];
+    s_acc[wave][h][2 * lane + 1] = hacc[h][1];
   }
+  __syncthreads();  // s_red, s_acc
+  if (tid < 3 * G) s_st[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
   __syncthreads();
-  float* P3 = a.k3part + (((size_t)bh * a.s3 + split) * G) * (1 + HD);
-  for (int i = tid; i < G * HD; i += 256) {
-    const int h = i / HD, d = i - h * HD;
-    sf_put(P3 + h * (1 + HD) + 1 + d, ((accr[0][h][d] + accr[1][h][d]) + (accr[2][h][d] + accr[3][h][d])) + s_zz[h]);
+  float* PP = a.part_p + ((size_t)bh * a.nsp + split) * G * PW;
+  const float back = ldexpf(1.f, B - shift);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int d = 32 * wave + 16 * db + n;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = 2 * qg + hh;
+      if (h < G) {
+        const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
+        const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
+        sf_put(PP + h * PW + d, s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr);
+      }
+    }
   }
-  if (tid < G) sf_put(P3 + tid * (1 + HD), s_z[tid]);
-  SF_TS(13);
-  // last workgroup of this KV head: out = sum_s N_s / sum_s Z_s
+  if (tid < G) sf_put(PP + tid * PW + HD + 1, s_st[3 * tid]);
+  SF_TS(14);
+  // merge in two levels: the last of each group of 8 splits sums the group into
+  // the group's first record, the last group to finish sums the groups
+  const int grp = split >> 3, ngrp = (a.nsp + 7) >> 3;
+  const int gsize = min(8, a.nsp - 8 * grp);
+  uint32_t* gctr = a.hist + (size_t)bh * 3 * NBIN + 2 * NBIN + 1024;  // words the select kernel leaves at zero
   sf_drain();
   __syncthreads();
   if (tid == 0)
-    flag = __hip_atomic_fetch_add(&a.cnt[bh * 2 + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           (uint32_t)(a.s3 - 1);
+    s_flag = __hip_atomic_fetch_add(gctr + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(gsize - 1);
   __syncthreads();
-  if (!flag) return;
-  SF_TS(14);
-  const float* Pb = a.k3part + (size_t)bh * a.s3 * G * (1 + HD);
+  if (!s_flag) return;
+  float* PB = a.part_p + (size_t)bh * a.nsp * G * PW;
+  for (int i = tid; i < G * (HD + 1); i += 256) {
+    const int h = i / (HD + 1), d = i - h * (HD + 1);
+    const int col = d < HD ? d : HD + 1;  // value sums, then the weight sum
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = sf_get(PB + ((8 * grp + min(k, gsize - 1)) * G + h) * PW + col);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < gsize) sum += v[k];
+    sf_put(PB + ((8 * grp) * G + h) * PW + col, sum);
+  }
+  sf_drain();
+  __syncthreads();
+  if (tid == 0)
+    s_flag = __hip_atomic_fetch_add(a.ctl + bh * 8 + 6, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(ngrp - 1);
+  __syncthreads();
+  if (!s_flag) return;
+  // last group of this KV head: out = sum N / sum z (one common max)
   for (int i = tid; i < G * HD; i += 256) {
     const int h = i / HD, d = i - h * HD;
     float num = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < a.s3; ++s) {
-      num += sf_get(Pb + (s * G + h) * (1 + HD) + 1 + d);
-      den += sf_get(Pb + (s * G + h) * (1 + HD));
+    for (int g0 = 0; g0 < ngrp; g0 += 16) {
+      float vn[16], vd[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int g = min(g0 + k, ngrp - 1);
+        vn[k] = sf_get(PB + ((8 * g) * G + h) * PW + d);
+        vd[k] = sf_get(PB + ((8 * g) * G + h) * PW + HD + 1);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (g0 + k < ngrp) {
+          num += vn[k];
+          den += vd[k];
+        }
     }
     a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
   }
@@ -725,21 +1009,22 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 
 size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12]) {
   const int G = n_kv > 0 ? n_q / n_kv : 1;
-  const int bh = batch * n_kv;
-  const size_t s1 = (T + 255) / 256, s3 = (T + 127) / 128;  // bounds for every b
+  const size_t bh = (size_t)batch * n_kv;
+  const size_t nsa = (T + SA - 1) / SA, s2 = (T + CB - 1) / CB, nsp = (T + 255) / 256;  // nsp: bound for every b
   const size_t KS = k_sel > 0 ? k_sel : 1;
+  const size_t LT = ((size_t)T + 3) & ~size_t(3);
   const size_t sizes[12] = {
-      (size_t)batch * n_q * T * 4,    // logits
-      (size_t)bh * ((T + 3) & ~3) * 4,  // scores (rows padded to 16 bytes)
-      (size_t)bh * s1 * G * 2 * 4,    // k1part
-      (size_t)bh * NBINS * 4,         // hist
-      (size_t)bh * 2 * 4,             // cnt
-      (size_t)bh * KS * 4,            // sel
-      (size_t)bh * KS * 4,            // hit_t
-      (size_t)bh * KS * 4,            // hit_s
-      (size_t)bh * 4,                 // n_hit
-      (size_t)bh * G * 4,             // mref
-      (size_t)bh * s3 * G * (1 + HD) * 4,  // k3part
+      (size_t)batch * n_q * LT * 4,  // logits
+      bh * nsa * G * PW * 4,         // split partials
+      bh * s2 * G * PW * 4,          // chunk partials
+      bh * nsp * G * PW * 4,         // pv partials
+      bh * s2 * G * 4,               // chunk max
+      bh * G * 4,                    // max after replacement
+      bh * KS * 4,                   // selection
+      bh * KS * 4,                   // slots
+      bh * 3 * NBIN * 4,             // histograms
+      bh * 8 * 4,                    // control words
+      bh * s2 * 2 * 4,               // chunk counts
       0};
   size_t o = sf_align256(sizeof(WsControl));
   for (int i = 0; i < 12; ++i) {
@@ -752,11 +1037,18 @@ size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12
 template <int B, int G>
 sf_status launch_attn(AttnArgs& a, hipStream_t s) {
   const int bh = a.batch * a.n_kv;
-  hipLaunchKernelGGL((attn_qk_kernel<B, G>), dim3(a.s1, bh), dim3(256), 0, s, a);
+  if (a.k_sel == 0) {
+    hipLaunchKernelGGL((attn_split_kernel<B, G, true>), dim3(a.nsa, bh), dim3(256), 0, s, a);
+    SF_LAUNCH_CHECK();
+    hipLaunchKernelGGL((attn_select_kernel<G>), dim3(a.s2, bh), dim3(SEL_T), 0, s, a);
+    SF_LAUNCH_CHECK();
+    return SF_OK;
+  }
+  hipLaunchKernelGGL((attn_split_kernel<B, G, false>), dim3(a.nsa, bh), dim3(256), 0, s, a);
   SF_LAUNCH_CHECK();
   hipLaunchKernelGGL((attn_select_kernel<G>), dim3(a.s2, bh), dim3(SEL_T), 0, s, a);
   SF_LAUNCH_CHECK();
-  hipLaunchKernelGGL((attn_pv_kernel<B, G>), dim3(a.s3, bh), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_pv_kernel<B, G>), dim3(a.nsp, bh), dim3(256), 0, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }
@@ -794,6 +1086,7 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
   SF_REQUIRE(kv->batch > 0 && kv->n_kv_heads > 0 && n_q_heads % kv->n_kv_heads == 0, SF_EINVAL,
              "n_q_heads must be a multiple of n_kv_heads");
   SF_REQUIRE(kv->t_len >= 1 && kv->t_len <= kv->t_cap, SF_EINVAL, "need 1 <= t_len <= t_cap");
+  SF_REQUIRE((int64_t)kv->t_len <= (int64_t)MAX_CHUNKS * CB, SF_EUNSUPPORTED, "t_len above 1048576");
   SF_REQUIRE(k_sel >= 0 && k_sel <= kv->t_len, SF_EINVAL, "k_sel out of range");
   SF_REQUIRE(k_sel == 0 || kv->fmt.r > 0, SF_EINVAL, "k_sel > 0 needs r > 0");
   AttnArgs a = {};
@@ -807,29 +1100,31 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
   a.n_kv = kv->n_kv_heads;
   a.G = n_q_heads / kv->n_kv_heads;
   a.T = kv->t_len;
+  a.LT = (a.T + 3) & ~3;
   a.t_cap = kv->t_cap;
   a.b = kv->fmt.b;
   a.r = kv->fmt.r;
   a.k_sel = k_sel;
   a.scale = softmax_scale;
-  a.s1 = (a.T + qk_split(a.b) - 1) / qk_split(a.b);
-  a.s2 = (a.T + SPLIT2 - 1) / SPLIT2;
-  a.s3 = (a.T + pv_split(a.b) - 1) / pv_split(a.b);
+  a.nsa = (a.T + SA - 1) / SA;
+  a.s2 = (a.T + CB - 1) / CB;
+  a.nsp = (a.T + pv_tokens(a.b) - 1) / pv_tokens(a.b);
   size_t off[12];
   const size_t need = attn_layout(a.batch, a.n_q, a.n_kv, a.T, k_sel, off);
   SF_REQUIRE(ws->bytes >= need, SF_ENOMEM, "workspace too small");
   uint8_t* w = ws->base;
   a.logits = (float*)(w + off[0]);
-  a.scores = (float*)(w + off[1]);
-  a.k1part = (float*)(w + off[2]);
-  a.hist = (uint32_t*)(w + off[3]);
-  a.cnt = (uint32_t*)(w + off[4]);
-  a.sel = (int32_t*)(w + off[5]);
-  a.hit_t = (int32_t*)(w + off[6]);
-  a.hit_s = (int32_t*)(w + off[7]);
-  a.n_hit = (int32_t*)(w + off[8]);
-  a.mref = (float*)(w + off[9]);
-  a.k3part = (float*)(w + off[10]);
+  a.part_a = (float*)(w + off[1]);
+  a.part_c = (float*)(w + off[2]);
+  a.part_p = (float*)(w + off[3]);
+  a.cmax = (float*)(w + off[4]);
+  a.mref = (float*)(w + off[5]);
+  a.sel_ws = (int32_t*)(w + off[6]);
+  a.slot_ws = (int32_t*)(w + off[7]);
+  a.hist = (uint32_t*)(w + off[8]);
+  a.ctl = (uint32_t*)(w + off[9]);
+  a.cnts = (uint32_t*)(w + off[10]);
+  a.timeout = (uint32_t*)(w + offsetof(WsControl, timeout));
   a.sel_in = sel_in;
   a.sel_out = sel_out;
   a.hit_out = hit_out;
