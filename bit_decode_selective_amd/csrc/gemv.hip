@@ -9,15 +9,18 @@
 //
 // Because the refinement is additive (W_eff = W_res + s * c_lo on refined
 // channels), y = x W_res^T + sum over hit channels k of x_k * s[:, g(k)] * c_lo[:, k].
-// One launch computes, for up to SF_MAX_OPS matrices that share x:
-//   * the channel selection (top-k of max-over-batch |x|, ties to the lower index)
-//     and its cache lookup, done once by whichever workgroup starts first and
-//     published to the others through the workspace;
-//   * the resident GEMV, streamed from HBM with 16-byte loads, codes expanded into
-//     fp16 lanes by mask-and-or into the mantissa (value 1 + c/2^b) and reduced with
-//     v_dot2_f32_f16; sum_k c*x = 2^b * (dot - sum_k x) per chunk;
-//   * the sparse refinement delta for each workgroup's rows.
-#include "block_scan.h"
+// A call computes, for up to SF_MAX_OPS matrices that share x:
+//   * select (one 1024-thread workgroup, its own launch): the channel selection
+//     (top-k of max-over-batch |x|, ties to the lower index) by a two-pass LDS
+//     radix select, and its cache lookup per matrix, into the workspace.  On its
+//     own the workgroup has the CU to itself; inside the streaming launch the same
+//     few thousand dependent LDS steps run several times slower;
+//   * gemv: the resident GEMV, streamed from HBM with 16-byte loads, codes
+//     expanded into fp16 lanes by mask-and-or into the mantissa (value 1 + c/2^b)
+//     and reduced with v_dot2_f32_f16 (sum_k c*x = 2^b * (dot - sum_k x) per
+//     chunk), plus the sparse refinement delta of each row tile before it is
+//     written: the refinement words of the tile's rows in every hit slot are
+//     requested when the tile starts and consumed after its chunks.
 #include "sf_internal.h"
 
 #define SF_MAX_OPS 4
@@ -28,6 +31,9 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+constexpr int SEL_NT = 1024;          // threads of the selection workgroup
+constexpr int MAX_SEL_K = 8 * SEL_NT * 4;  // k_in with a computed selection: 4 x 8 channels per thread
 
 struct GemvOpDev {
   const uint8_t* res;
@@ -44,12 +50,9 @@ struct GemvArgs {
   const uint16_t* x;
   const int32_t* sel_in;
   int32_t* sel_out;
-  WsControl* ctl;
-  int32_t* ws_sel;       // [k_sel]
-  int32_t* ws_hit_k;     // [n_ops][k_sel]
-  int32_t* ws_hit_slot;  // [n_ops][k_sel]
-  int32_t* ws_nhit;      // [n_ops]
-  int32_t n_ops, k_in, batch, batch_off, k_sel, r, total_tiles, do_log;
+  int32_t* ws_sel;   // [k_sel]: selection, ascending
+  int32_t* ws_slot;  // [n_ops][k_sel]: slot per op, -1 = miss
+  int32_t n_ops, k_in, batch, batch_off, k_sel, r, total_tiles, hits_in_lds;
 };
 
 // ---- code layouts ----------------------------------------------------------------
@@ -65,8 +68,6 @@ struct CodecPow2 {
   static constexpr int CODES = 32 * WORDS / B;
   static constexpr int PAIRS = CODES / 2;
   static constexpr int P = 32 / B, HP = P / 2;
-  __device__ static int pair_k0(int j) { return (j / HP) * P + (j % HP); }
-  __device__ static int pair_k1(int j) { return pair_k0(j) + HP; }
   // pair index and half of channel kk (0 <= kk < CODES) of a chunk
   __device__ static __forceinline__ void locate(int kk, int* j, int* hi) {
     const int w = kk / P, q = kk % P;
@@ -89,8 +90,6 @@ struct CodecStream {
   static constexpr int WORDS = B;
   static constexpr int CODES = 32;
   static constexpr int PAIRS = 16;
-  __device__ static int pair_k0(int j) { return 2 * j; }
-  __device__ static int pair_k1(int j) { return 2 * j + 1; }
   __device__ static __forceinline__ void locate(int kk, int* j, int* hi) {
     *j = kk >> 1;
     *hi = kk & 1;
@@ -107,164 +106,240 @@ struct CodecStream {
   }
 };
 
-__device__ __forceinline__ uint32_t read_field(const uint8_t* unit, uint32_t bitpos, int width) {
-  const uint32_t* w = (const uint32_t*)unit;
-  const uint32_t wi = bitpos >> 5, off = bitpos & 31;
-  uint32_t v = w[wi] >> off;
-  if (off + width > 32) v |= w[wi + 1] << (32 - off);
-  return v & ((1u << width) - 1u);
+// ---- selection + lookup (one 1024-thread workgroup) ----------------------------------
+// Wave 0 scans NBIN = 64 * PER histogram bins from the top: the largest bin whose
+// suffix count reaches `need`; lds[20] = bin, lds[21] = count above it.
+template <int PER>
+__device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int* lds) {
+  constexpr int NBIN = 64 * PER;
+  const int lane = threadIdx.x & 63;
+  int c[PER], s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = (int)h[NBIN - 1 - PER * lane - i];
+    s += c[i];
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  int run = incl - s;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (run < need && run + c[i] >= need) {
+      lds[20] = NBIN - 1 - PER * lane - i;
+      lds[21] = run;
+    }
+    run += c[i];
+  }
 }
 
-// ---- channel selection + lookup (one workgroup) ---------------------------------
-// Thread t owns channels [t*cpt, (t+1)*cpt), cpt = 2*ceil(K/512) <= 64; their keys
-// (max over the batch of |x| as 15-bit fp16 patterns, which order like the values)
-// are read once, kept two per register, and radix-selected in two histogram passes
-// (top 8 bits, then the low 7; one LDS histogram per wave), then compacted in
-// channel order into `sel` (LDS when it fits, else the workspace).
-constexpr int KEYW = 32;
+// number of set bits of m in the lanes below this one
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
-__device__ void gemv_select_and_lookup(const GemvArgs& a, uint32_t* hist4, int* lds, int32_t* sel) {
-  const int K = a.k_in, ks = a.k_sel, tid = threadIdx.x, wave = tid >> 6;
+// Channel-order prefix of per-channel flags f[q] (q = 0..7: this thread's 8
+// consecutive channels) over the whole workgroup: returns the number of flags in
+// earlier channels; *total = all flags.  One LDS round (lds[0..15]).
+__device__ __forceinline__ int blk_flag_prefix(const bool (&f)[8], int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = SEL_NT / 64;
+  int below = 0, wtot = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint64_t m = __ballot(f[q]);
+    below += lanes_below(m);
+    wtot += __popcll(m);
+  }
+  __syncthreads();
+  if (lane == 0) lds[wave] = wtot;
+  __syncthreads();
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = lds[w];
+    if (w < wave) base += t;
+    sum += t;
+  }
+  *total = sum;
+  return base + below;
+}
+
+// Keys are max over the batch of |x| as 15-bit fp16 patterns, which order like the
+// values.  Thread t holds channels 8m..8m+7 for m = t + 1024 i, two per register
+// (word 4i + q: channel 8m + 2q low half, 8m + 2q + 1 high half).  The k-th largest
+// key T comes from two histogram passes (top 8 bits, then the low 7), each wave
+// counting into its own LDS histogram (the keys concentrate in a few bins, so one
+// shared histogram would serialise the atomics) before the 16 are summed; then,
+// per i, ballots place the keys above T and the first `need` keys equal to T
+// (lowest channels first) in channel order.
+__global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
+  constexpr int NW = SEL_NT / 64;
+  __shared__ uint32_t whist[NW][256];
+  __shared__ uint32_t hist[384];
+  __shared__ int lds[24];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.k_in, ks = a.k_sel;
+  int32_t* sel = a.ws_sel;
+  SF_TS(6);
   if (a.sel_in) {
-    for (int j = tid; j < ks; j += 256) sel[j] = a.sel_in[j];
+    for (int j = tid; j < ks; j += SEL_NT) sel[j] = a.sel_in[j];
   } else if (ks >= K) {
-    for (int j = tid; j < ks; j += 256) sel[j] = j;
+    for (int j = tid; j < ks; j += SEL_NT) sel[j] = j;
   } else {
-    const int cpt = 2 * ((K + 511) / 512);
-    const int k0 = tid * cpt;
-    uint32_t kw[KEYW];
+    constexpr int MI = 4;
+    uint32_t kw[4 * MI];
 #pragma unroll
-    for (int i = 0; i < KEYW; ++i) kw[i] = 0;
+    for (int i = 0; i < 4 * MI; ++i) kw[i] = 0;
     for (int bb = 0; bb < a.batch; ++bb) {
-      const uint32_t* xr = (const uint32_t*)(a.x + (size_t)bb * K);
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)bb * K);
 #pragma unroll
-      for (int i = 0; i < KEYW; ++i) {
-        if (2 * i < cpt && k0 + 2 * i < K) {
-          const uint32_t v = xr[(k0 >> 1) + i] & 0x7FFF7FFFu;
-          const uint32_t lo = max(kw[i] & 0xFFFFu, v & 0xFFFFu), hi = max(kw[i] >> 16, v >> 16);
-          kw[i] = lo | (hi << 16);
-        }
-      }
-    }
-    SF_TS(8);
-    // T = the ks-th largest key: the largest v with count(key >= v) >= ks, found by
-    // binary search over the 15-bit key range (15 block-wide counts)
-    (void)hist4;
-    int lo_v = 0, hi_v = 32768;  // count(>= lo_v) >= ks > count(>= hi_v)
-    while (hi_v - lo_v > 1) {
-      const int mid = (lo_v + hi_v) >> 1;
-      int c = 0;
+      for (int i = 0; i < MI; ++i) {
+        const int m = tid + SEL_NT * i;
+        if (m < K / 8) {
+          const u32x4 v = xr[m];
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int i = 0; i < KEYW; ++i)
-        if (2 * i < cpt && k0 + 2 * i < K) c += ((int)(kw[i] & 0xFFFFu) >= mid) + ((int)(kw[i] >> 16) >= mid);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
-      __syncthreads();
-      if ((tid & 63) == 0) lds[wave] = c;
-      __syncthreads();
-      const int tot4 = (lds[0] + lds[1]) + (lds[2] + lds[3]);
-      if (tot4 >= ks) lo_v = mid; else hi_v = mid;
-    }
-    const uint32_t T = (uint32_t)lo_v;
-    SF_TS(9);
-    int above_l = 0;
-#pragma unroll
-    for (int i = 0; i < KEYW; ++i)
-      if (2 * i < cpt && k0 + 2 * i < K) above_l += ((kw[i] & 0xFFFFu) > T) + ((kw[i] >> 16) > T);
-    int above;
-    (void)wg_exclusive_scan(above_l, lds, &above);
-    const int need = ks - above;
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < KEYW; ++i)
-      if (2 * i < cpt && k0 + 2 * i < K) {
-        const uint32_t lo = kw[i] & 0xFFFFu, hi = kw[i] >> 16;
-        gt += (lo > T) + (hi > T);
-        eq += (lo == T) + (hi == T);
-      }
-    int tot;
-    const int eq_before = wg_exclusive_scan(eq, lds, &tot);
-    const int take_eq = max(0, min(eq, need - eq_before));
-    int off = wg_exclusive_scan(gt + take_eq, lds, &tot);
-    int seen = 0;
-#pragma unroll
-    for (int i = 0; i < KEYW; ++i)
-      if (2 * i < cpt && k0 + 2 * i < K) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t key = h ? (kw[i] >> 16) : (kw[i] & 0xFFFFu);
-          const int k = k0 + 2 * i + h;
-          if (key > T) {
-            sel[off++] = k;
-          } else if (key == T) {
-            if (seen < take_eq) sel[off++] = k;
-            ++seen;
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x2 = wv[q] & 0x7FFF7FFFu;
+            kw[4 * i + q] = max(kw[4 * i + q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kw[4 * i + q] >> 16, x2 >> 16) << 16);
           }
         }
       }
+    }
+    uint32_t* wh = whist[wave];
+    for (int i = lane; i < 256; i += 64) wh[i] = 0;
+    __syncthreads();
+    SF_TS(7);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      if (tid + SEL_NT * i < K / 8)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          atomicAdd(&wh[(kw[4 * i + q] & 0xFFFFu) >> 7], 1u);
+          atomicAdd(&wh[kw[4 * i + q] >> 23], 1u);
+        }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c += whist[w][tid];
+      hist[tid] = c;
+    }
+    __syncthreads();
+    for (int i = lane; i < 128; i += 64) wh[i] = 0;  // every wave has been summed
+    if (tid < 64) wave_threshold<4>(hist, ks, lds);
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)lds[20];
+    int need = ks - lds[21];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      if (tid + SEL_NT * i < K / 8)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = kw[4 * i + q] & 0xFFFFu, hi = kw[4 * i + q] >> 16;
+          if ((lo >> 7) == b1) atomicAdd(&wh[lo & 127u], 1u);
+          if ((hi >> 7) == b1) atomicAdd(&wh[hi & 127u], 1u);
+        }
+    __syncthreads();
+    if (tid < 128) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c += whist[w][tid];
+      hist[256 + tid] = c;
+    }
+    __syncthreads();
+    if (tid < 64) wave_threshold<2>(hist + 256, need, lds);
+    __syncthreads();
+    const uint32_t T = (b1 << 7) | (uint32_t)lds[20];
+    need -= lds[21];  // keys equal to T that are taken, lowest channels first
+    SF_TS(11);
+    int written = 0, eq_seen = 0;
+    for (int i = 0; i < MI; ++i) {
+      if (SEL_NT * 8 * i >= K) break;
+      const bool ok = tid + SEL_NT * i < K / 8;
+      bool gt[8], eq[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = kw[4 * i + q] & 0xFFFFu, hi = kw[4 * i + q] >> 16;
+        gt[2 * q] = ok && lo > T;
+        gt[2 * q + 1] = ok && hi > T;
+        eq[2 * q] = ok && lo == T;
+        eq[2 * q + 1] = ok && hi == T;
+      }
+      // equal keys before each of this thread's channels, then the taken ones
+      int tot_eq;
+      int eb = eq_seen + blk_flag_prefix(eq, lds, &tot_eq);
+      bool take[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        take[q] = gt[q] || (eq[q] && eb < need);
+        eb += eq[q];
+      }
+      int tot;
+      int pos = written + blk_flag_prefix(take, lds, &tot);
+      const int k0 = 8 * (tid + SEL_NT * i);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (take[q]) {
+          if (pos < ks) sel[pos] = k0 + q;
+          ++pos;
+        }
+      written += tot;
+      eq_seen += tot_eq;
+    }
   }
   // sel[] is read back below by other threads of this workgroup
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  if (a.sel_out && a.do_log)
-    for (int j = tid; j < ks; j += 256) a.sel_out[j] = sel[j];
-  SF_TS(10);
-  // lookups, per op, in selection order
-  const int jpt = (ks + 255) / 256;
-  const int j0 = tid * jpt, j1 = min(ks, j0 + jpt);
-  for (int op = 0; op < a.n_ops; ++op) {
-    const PoolDev pool = a.ops[op].pool;
-    int32_t* hit_out = a.ops[op].hit_out;
-    if (tid == 0) {
-      int base = -1;
-      if (pool.log_count && a.do_log) {
-        const uint32_t bse = atomicAdd(pool.log_count, (uint32_t)ks);
-        base = (bse + (uint32_t)ks <= (uint32_t)pool.log_cap) ? (int)bse : -1;
-      }
-      lds[6] = base;
+  SF_TS(12);
+  // lookups, per op, in selection order (with the report and the lookup log)
+  if (tid < a.n_ops) {
+    const PoolDev& pool = a.ops[tid].pool;
+    int base = -1;
+    if (pool.log_count) {
+      const uint32_t bse = atomicAdd(pool.log_count, (uint32_t)ks);
+      base = (bse + (uint32_t)ks <= (uint32_t)pool.log_cap) ? (int)bse : -1;
     }
-    __syncthreads();
-    const int base = lds[6];
-    int nh = 0;
-    for (int j = j0; j < j1; ++j) {
-      const int k = sel[j];
-      const int slot = (pool.unit2slot && k >= 0 && k < K) ? pool.unit2slot[k] : -1;
-      nh += slot >= 0;
-    }
-    int tot;
-    int pos = wg_exclusive_scan(nh, lds, &tot);
-    for (int j = j0; j < j1; ++j) {
-      const int k = sel[j];
-      const int slot = (pool.unit2slot && k >= 0 && k < K) ? pool.unit2slot[k] : -1;
-      if (hit_out && a.do_log) hit_out[j] = slot;
-      if (base >= 0) {
-        pool.log_units[base + j] = k;
-        pool.log_slots[base + j] = slot;
-      }
-      if (slot >= 0) {
-        sf_put(a.ws_hit_k + op * ks + pos, k);
-        sf_put(a.ws_hit_slot + op * ks + pos, slot);
-        ++pos;
-      }
-    }
-    if (tid == 0) sf_put(a.ws_nhit + op, tot);
-    __syncthreads();
+    lds[tid] = base;
   }
+  __syncthreads();
+  for (int j = tid; j < ks; j += SEL_NT) {
+    const int k = sel[j];
+    if (a.sel_out) a.sel_out[j] = k;
+    int slot[SF_MAX_OPS];
+#pragma unroll
+    for (int op = 0; op < SF_MAX_OPS; ++op)  // all loads first
+      slot[op] = (op < a.n_ops && a.ops[op].pool.unit2slot && k >= 0 && k < K) ? a.ops[op].pool.unit2slot[k] : -1;
+#pragma unroll
+    for (int op = 0; op < SF_MAX_OPS; ++op) {
+      if (op >= a.n_ops) break;
+      a.ws_slot[op * ks + j] = slot[op];
+      if (a.ops[op].hit_out) a.ops[op].hit_out[j] = slot[op];
+      if (lds[op] >= 0) {
+        a.ops[op].pool.log_units[lds[op] + j] = k;
+        a.ops[op].pool.log_slots[lds[op] + j] = slot[op];
+      }
+    }
+  }
+  SF_TS(13);
 }
 
 // ---- the GEMV kernel -------------------------------------------------------------
-// When refining, workgroup 0 only selects, looks up and publishes the hit lists.
-// The other (tile) workgroups are persistent, 4 waves each: row tiles of 4R rows
-// (R per wave) are dealt round-robin; lane l of a wave owns chunks l, l+64, ... of
-// each of the wave's R rows.  The first chunk is requested before x is staged, and
-// the next tile's first chunk before the current tile is reduced.  x is staged
-// once per workgroup (16-byte loads scattered into pair order in LDS, chunk sums
-// by shuffles).  NB batch rows [batch_off, batch_off + NB) per launch.
-// Dynamic LDS: x pairs [NB][K/2] | x chunk sums [NB][nchunks] | delta staging:
-// tile scale words [4R][K/128] and per-hit refinement words [HIT_CAP][SW].
-constexpr int HIT_CAP = 512;  // hits staged in LDS per batch of the delta
-constexpr int SW = 4;         // refinement words staged per hit (a tile's rows)
+// Persistent workgroups, 4 waves each: row tiles of 4R rows (R per wave) are dealt
+// round-robin; lane l of a wave owns chunks l, l+64, ... of each of the wave's R
+// rows.  The first chunk is requested before x is staged in LDS (16-byte loads
+// scattered into pair order, chunk sums by shuffles), the next tile's first chunk
+// before the current tile is reduced.  With refinement the hit list (selection
+// and slots, from the select launch) is copied to LDS with the staging; each tile
+// requests the refinement words of its rows in HPF hits per lane when it starts,
+// records its rows' scale words per group while streaming, and adds the deltas
+// before the wave reduction.  NB batch rows [batch_off, batch_off + NB) per launch.
+// Dynamic LDS: x pairs [NB][K/2] | x chunk sums [NB][nchunks] | scale words
+// [4][R][K/128] | (selection [k_sel] | slots [n_ops][k_sel] when they fit).
+constexpr int HPF = 8;  // hits per lane whose refinement words are requested at tile start
 
 template <class C, int R>
 __device__ __forceinline__ void load_chunk(const GemvOpDev& o, int row0, int c, size_t rowbytes, int ngr,
@@ -297,13 +372,14 @@ __device__ __forceinline__ int op_of_tile(const GemvArgs& a, int tile_g) {
   return op;
 }
 
+// bits [p, p + width) of the 64-bit (w1:w0)
+__device__ __forceinline__ uint32_t bits64(uint32_t w0, uint32_t w1, int p, int width) {
+  return (uint32_t)((((uint64_t)w1 << 32) | w0) >> p) & ((1u << width) - 1u);
+}
+
 template <class C, int B, int R, int NB>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
-  __shared__ uint32_t s_hist[1024];
-  __shared__ int s_lds[8];
-  __shared__ float s_red[NB][256];
-  __shared__ int s_hk[HIT_CAP], s_hs[HIT_CAP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.k_in;
@@ -311,115 +387,194 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int xpairs = K / 2;
   const int rows_wg = 4 * R;
   const int ngr = K / 128;
-  uint32_t* xs = smem;                              // [NB][K/2] fp16 pairs
-  float* xsum = (float*)(smem + NB * xpairs);       // [NB][nchunks]
-  uint32_t* s_sz = smem + NB * xpairs + NB * nchunks;  // [rows_wg][ngr]
-  uint32_t* s_w = s_sz + rows_wg * ngr;                // [HIT_CAP][SW]
-  const bool refine = a.k_sel > 0;
+  const int ks = a.k_sel;
+  uint32_t* xs = smem;                                   // [NB][K/2] fp16 pairs
+  float* xsum = (float*)(smem + NB * xpairs);            // [NB][nchunks]
+  uint32_t* s_szw = (uint32_t*)(xsum + NB * nchunks);    // [4][R][ngr]
+  int32_t* l_sel = (int32_t*)(s_szw + (ks > 0 ? 4 * R * ngr : 0));  // [k_sel] if hits_in_lds
+  int32_t* l_slot = l_sel + ks;                                     // [n_ops][k_sel]
+  const bool refine = ks > 0;
+  const int32_t* hsel = a.hits_in_lds ? l_sel : a.ws_sel;
+  const int32_t* hslot = a.hits_in_lds ? l_slot : a.ws_slot;
   const size_t rowbytes = (size_t)K * B / 8;
 
   SF_TS(0);
-  if (refine && blockIdx.x == 0) {
-    // the selecting workgroup: its sel list lives in the (otherwise unused) LDS
-    // staging area when it fits
-    int32_t* sel = (a.k_sel <= NB * xpairs) ? (int32_t*)smem : a.ws_sel;
-    gemv_select_and_lookup(a, s_hist, s_lds, sel);
-    SF_TS(2);
-    sf_drain();
-    __syncthreads();
-    if (tid == 0) {
-      sf_put(&a.ctl->sel_state, 2u);
-      const uint32_t prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == gridDim.x - 1u) {
-        sf_put(&a.ctl->done, 0u);
-        sf_put(&a.ctl->sel_state, 0u);
-      }
-    }
-    return;
-  }
-  const int twg = (int)blockIdx.x - (refine ? 1 : 0);  // tile workgroup index
-  const int n_twg = (int)gridDim.x - (refine ? 1 : 0);
-
-  // request the first chunk of this wave before anything else
+  // request the first chunk of this wave
   uint32_t cw[R][C::WORDS];
   uint32_t szw[R];
   bool have = false;
-  if (twg < a.total_tiles && lane < nchunks) {
-    const int op = op_of_tile(a, twg);
-    load_chunk<C, R>(a.ops[op], (twg - a.ops[op].tile_begin) * rows_wg + wave * R, lane, rowbytes, ngr, cw, szw);
+  if ((int)blockIdx.x < a.total_tiles && lane < nchunks) {
+    const int op = op_of_tile(a, blockIdx.x);
+    load_chunk<C, R>(a.ops[op], (blockIdx.x - a.ops[op].tile_begin) * rows_wg + wave * R, lane, rowbytes, ngr,
+                     cw, szw);
     have = true;
   }
-
-  // stage x in pair order (16-byte loads, 2-byte LDS stores); the CODES/8 threads
-  // that load one chunk sum it with shuffles
+  // the hit list, when it fits in LDS
+  if (refine && a.hits_in_lds) {
+    for (int j = tid; j < ks * (1 + a.n_ops); j += 256) l_sel[j] = j < ks ? a.ws_sel[j] : a.ws_slot[j - ks];
+  }
+  // stage x in pair order (16-byte loads, all issued first; 2-byte LDS stores); the
+  // CODES/8 threads that load one chunk sum it with shuffles
   {
     uint16_t* xh = (uint16_t*)xs;
     constexpr int TPC = C::CODES / 8;  // threads per chunk
-    for (int bb = 0; bb < NB; ++bb) {
-      const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
-      for (int m0 = 0; m0 < K / 8; m0 += 256) {
-        const int m = m0 + tid;
-        float part = 0.f;
-        if (m < K / 8) {
-          const u32x4 v = xr[m];
-          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+    constexpr int XB = 8;              // 16-byte x loads in flight per thread
+    for (int m0 = 0; m0 < K / 8; m0 += 256 * XB) {
+      u32x4 xv[NB][XB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int k = 8 * m + e;
-            const int c = k / C::CODES, kk = k - c * C::CODES;
-            int j, hi;
-            C::locate(kk, &j, &hi);
-            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
-            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
-            part += (float)__builtin_bit_cast(_Float16, hb);
-          }
+      for (int bb = 0; bb < NB; ++bb) {
+        const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+#pragma unroll
+        for (int i = 0; i < XB; ++i) {
+          const int m = m0 + 256 * i + tid;
+          if (m < K / 8) xv[bb][i] = xr[m];
         }
+      }
 #pragma unroll
-        for (int o = TPC / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, TPC);
-        if (m < K / 8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
+      for (int i = 0; i < XB; ++i) {
+        const int m = m0 + 256 * i + tid;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          float part = 0.f;
+          if (m < K / 8) {
+            const uint32_t wds[4] = {xv[bb][i].x, xv[bb][i].y, xv[bb][i].z, xv[bb][i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int k = 8 * m + e;
+              const int c = k / C::CODES, kk = k - c * C::CODES;
+              int j, hi;
+              C::locate(kk, &j, &hi);
+              const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+              xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
+              part += (float)__builtin_bit_cast(_Float16, hb);
+            }
+          }
+#pragma unroll
+          for (int o = TPC / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, TPC);
+          if (m < K / 8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
+        }
       }
     }
   }
   __syncthreads();
-
   SF_TS(1);
+
   const float scl = (float)(1u << (a.r + B));
-  for (int tile_g = twg; tile_g < a.total_tiles; tile_g += n_twg) {
+  const int r = a.r;
+  uint32_t* szrow = s_szw + wave * R * ngr;  // this wave's rows' scale words, [R][ngr]
+  for (int tile_g = blockIdx.x; tile_g < a.total_tiles; tile_g += gridDim.x) {
     const int op = op_of_tile(a, tile_g);
     const GemvOpDev& o = a.ops[op];
     const int tile = tile_g - o.tile_begin;
     const int row0 = tile * rows_wg + wave * R;
+    // the wave's R rows occupy bits [row0 * r, (row0 + R) * r) of every unit
+    const int ubit = row0 * r, uwi = ubit >> 5, uoff = ubit & 31;
+    const int wpu = o.pool.unit_bytes >> 2;
+    const uint32_t* units = (const uint32_t*)o.pool.slots;
+    const int32_t* slots = hslot + op * ks;
+    // refinement words of the first HPF hits per lane, requested now, used after
+    // the chunks
+    int pslot[HPF];
+    uint32_t pw0[HPF], pw1[HPF];
+    if (refine) {
+#pragma unroll
+      for (int i = 0; i < HPF; ++i) {
+        const int j = lane + 64 * i;
+        pslot[i] = j < ks ? slots[j] : -1;
+        pw0[i] = pw1[i] = 0u;
+        if (pslot[i] >= 0) {
+          const uint32_t* u = units + (size_t)pslot[i] * wpu;
+          if (uwi < wpu) pw0[i] = u[uwi];
+          if (uwi + 1 < wpu) pw1[i] = u[uwi + 1];
+        }
+      }
+    }
     float acc[NB][R];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[bb][r] = 0.f;
+      for (int rr = 0; rr < R; ++rr) acc[bb][rr] = 0.f;
     for (int c = lane; c < nchunks; c += 64) {
       if (!have) load_chunk<C, R>(o, row0, c, rowbytes, ngr, cw, szw);
       have = false;
+      if (refine && (c * C::CODES) % 128 == 0)
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[rr];
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        uint32_t xv[C::PAIRS];
         const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
+        float d[R];
 #pragma unroll
-        for (int j = 0; j < C::PAIRS / 4; ++j) {
-          const u32x4 v = xp[j];
-          xv[4 * j] = v.x; xv[4 * j + 1] = v.y; xv[4 * j + 2] = v.z; xv[4 * j + 3] = v.w;
+        for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < C::PAIRS / 4; ++jb) {
+          const u32x4 xv = xp[jb];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[rr], 4 * jb + q)), as_h2(xv[q]), d[rr], false);
         }
         const float X = xsum[bb * nchunks + c];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float d = 0.f;
+        for (int rr = 0; rr < R; ++rr) {
+          const float s = sf_h2f(szw[rr]), z = sf_h2f(szw[rr] >> 16);
+          acc[bb][rr] += (s * scl) * (d[rr] - X) + z * X;
+        }
+      }
+    }
+    // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
+    if (refine) {
+      // the rows' scale words were recorded by other lanes of this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int j = lane; j < ks; j += 64) {
+        const int i = (j - lane) >> 6;
+        int slot;
+        uint32_t w0, w1, w2 = 0u;
+        if (i < HPF) {
+          slot = pslot[0];
+          w0 = pw0[0];
+          w1 = pw1[0];
 #pragma unroll
-          for (int j = 0; j < C::PAIRS; ++j)
-            d = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[r], j)), as_h2(xv[j]), d, false);
-          const float s = sf_h2f(szw[r]), z = sf_h2f(szw[r] >> 16);
-          acc[bb][r] += (s * scl) * (d - X) + z * X;
+          for (int q = 1; q < HPF; ++q)
+            if (q == i) {
+              slot = pslot[q];
+              w0 = pw0[q];
+              w1 = pw1[q];
+            }
+          if (slot >= 0 && uoff + R * r > 64 && uwi + 2 < wpu) w2 = units[(size_t)slot * wpu + uwi + 2];
+        } else {
+          slot = slots[j];
+          w0 = w1 = 0u;
+          if (slot >= 0) {
+            const uint32_t* u = units + (size_t)slot * wpu;
+            if (uwi < wpu) w0 = u[uwi];
+            if (uwi + 1 < wpu) w1 = u[uwi + 1];
+            if (uwi + 2 < wpu) w2 = u[uwi + 2];
+          }
+        }
+        if (slot < 0) continue;
+        const int k = hsel[j];
+        const int c = k / C::CODES, kk = k - c * C::CODES;
+        int jj, hi;
+        C::locate(kk, &jj, &hi);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const int p = uoff + rr * r;
+          const uint32_t clo = p + r <= 64 ? bits64(w0, w1, p, r) : bits64(w1, w2, p - 32, r);
+          const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
+            acc[bb][rr] = fmaf(hi ? (float)xh.y : (float)xh.x, sv, acc[bb][rr]);
+          }
         }
       }
     }
     // request the next tile's first chunk before reducing this one
-    const int next = tile_g + n_twg;
+    const int next = tile_g + gridDim.x;
     if (next < a.total_tiles && lane < nchunks) {
       const int op2 = op_of_tile(a, next);
       load_chunk<C, R>(a.ops[op2], (next - a.ops[op2].tile_begin) * rows_wg + wave * R, lane, rowbytes, ngr,
@@ -429,131 +584,29 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float v = acc[bb][r];
+      for (int rr = 0; rr < R; ++rr) {
+        float v = acc[bb][rr];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        acc[bb][r] = v;
+        acc[bb][rr] = v;
       }
     if (lane == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
+      for (int rr = 0; rr < R; ++rr) {
+        const int row = row0 + rr;
         if (row < o.n_out)
 #pragma unroll
-          for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][r];
+          for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][rr];
       }
     }
+    // the next tile records its scale words over this one's
+    if (refine) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
-
   SF_TS(3);
-  // sparse refinement delta over this workgroup's tiles: y += sum over hit
-  // channels k of x_k * s[row][k/128] * c_lo[row][k]
-  if (!refine) return;
-  int ok = 1;
-  if (tid == 0) s_lds[5] = sf_wait_word(&a.ctl->sel_state, 2u, &a.ctl->timeout) ? 1 : 0;
-  __syncthreads();
-  ok = s_lds[5];
-  SF_TS(4);
-  if (ok) {
-    const int r = a.r;
-    // the refinement bits of a tile's rows: rows_wg * r bits from bit tile*rows_wg*r
-    // of each unit; staged in LDS when they span at most SW words
-    const int nw = (rows_wg * r + 31) / 32 + 1;
-    const bool staged = nw <= SW;
-    for (int tile_g = twg; tile_g < a.total_tiles; tile_g += n_twg) {
-      const int op = op_of_tile(a, tile_g);
-      const GemvOpDev& o = a.ops[op];
-      const int tile = tile_g - o.tile_begin;
-      const int nh = sf_get(a.ws_nhit + op);
-      const int* ghk = a.ws_hit_k + op * a.k_sel;
-      const int* ghs = a.ws_hit_slot + op * a.k_sel;
-      const uint32_t w0 = ((uint32_t)(tile * rows_wg) * r) >> 5;
-      const int wpu = o.pool.unit_bytes / 4;
-      // scale words of the tile's rows
-      for (int i = tid; i < rows_wg * ngr; i += 256) {
-        const int rr = i / ngr, g = i - rr * ngr;
-        const int row = tile * rows_wg + rr;
-        s_sz[i] = row < o.n_out ? o.sz[(size_t)row * ngr + g] : 0u;
-      }
-      const int i = tid % rows_wg, mstep = 256 / rows_wg;
-      const int row = tile * rows_wg + i;
-      float part[NB];
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) part[bb] = 0.f;
-      for (int m0 = 0; m0 < nh; m0 += HIT_CAP) {
-        const int mn = min(HIT_CAP, nh - m0);
-        __syncthreads();
-        for (int m = tid; m < mn; m += 256) {
-          const int k = sf_get(ghk + m0 + m), slot = sf_get(ghs + m0 + m);
-          s_hk[m] = k;
-          s_hs[m] = slot;
-          if (staged) {
-            const uint32_t* u = (const uint32_t*)(o.pool.slots + (size_t)slot * o.pool.unit_bytes);
-#pragma unroll
-            for (int q = 0; q < SW; ++q)
-              s_w[SW * m + q] = (q < nw && (int)w0 + q < wpu) ? u[w0 + q] : 0u;
-          }
-        }
-        __syncthreads();
-        if (row < o.n_out) {
-          for (int m = tid / rows_wg; m < mn; m += mstep) {
-            const int k = s_hk[m];
-            uint32_t clo_u;
-            if (staged) {
-              const uint32_t p = (uint32_t)row * r - (w0 << 5);  // bit within the staged words
-              const uint32_t q = p >> 5;
-              const uint64_t w2 = (uint64_t)s_w[SW * m + q] | ((uint64_t)(q + 1 < (uint32_t)SW ? s_w[SW * m + q + 1] : 0u) << 32);
-              clo_u = (uint32_t)(w2 >> (p & 31)) & ((1u << r) - 1u);
-            } else {
-              clo_u = read_field(o.pool.slots + (size_t)s_hs[m] * o.pool.unit_bytes, (uint32_t)row * r, r);
-            }
-            const float sv = sf_h2f(s_sz[i * ngr + (k >> 7)]);
-            const int c = k / C::CODES, kk = k - c * C::CODES;
-            int jj, hi;
-            C::locate(kk, &jj, &hi);
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-              const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
-              const float xk = hi ? (float)xh.y : (float)xh.x;
-              part[bb] += (xk * sv) * (float)clo_u;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) s_red[bb][tid] = part[bb];
-      __syncthreads();
-      // lane 0 of wave w wrote rows [w*R, w*R + R) of the tile: it adds their deltas
-      if (lane == 0) {
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          const int ii = wave * R + rr;
-          const int rrow = tile * rows_wg + ii;
-          if (rrow < o.n_out) {
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-              float sum = 0.f;
-              for (int j = ii; j < 256; j += rows_wg) sum += s_red[bb][j];
-              float* yp = o.y + (size_t)(a.batch_off + bb) * o.n_out + rrow;
-              *yp = *yp + sum;
-            }
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-  SF_TS(5);
-  if (tid == 0) {
-    // the last workgroup to finish resets the words for the next launch
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ctl->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1u) {
-      sf_put(&a.ctl->done, 0u);
-      sf_put(&a.ctl->sel_state, 0u);
-    }
-  }
 }
 
 int env_int(const char* name, int dflt) {
@@ -561,28 +614,37 @@ int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
+size_t gemv_lds_bytes(int k_in, int codes, int nb, int n_ops, int k_sel, int rpw, bool hits_in_lds) {
+  size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (k_in / codes);
+  if (k_sel > 0) w += (size_t)4 * rpw * (k_in / 128) + (hits_in_lds ? (size_t)k_sel * (1 + n_ops) : 0);
+  return w * 4;
+}
+
+constexpr size_t MAX_DYN_LDS = 96 * 1024;
+constexpr size_t HIT_LDS = 16 * 1024;  // hit lists up to this size are copied to LDS
+
 template <class C, int B, int R, int NB>
 sf_status launch_gemv(GemvArgs& a, hipStream_t s) {
-  const size_t lds = ((size_t)NB * (a.k_in / 2) + (size_t)NB * (a.k_in / C::CODES) +
-                      (size_t)4 * R * (a.k_in / 128) + (size_t)SW * HIT_CAP) * 4;
-  SF_REQUIRE(lds <= 52 * 1024, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
-  // persistent tile workgroups: as many as are resident at once (at most
+  a.hits_in_lds = a.k_sel > 0 && (size_t)a.k_sel * (1 + a.n_ops) * 4 <= HIT_LDS;
+  const size_t lds = gemv_lds_bytes(a.k_in, C::CODES, NB, a.n_ops, a.k_sel, R, a.hits_in_lds);
+  SF_REQUIRE(lds <= MAX_DYN_LDS, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  // persistent workgroups: as many as are resident at once (at most
   // SF_GEMV_WGS_PER_CU per CU if set), each with an equal number of tiles
-  static int occ = 0, n_cu = 0;
-  if (occ == 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, (const void*)gemv_kernel<C, B, R, NB>, 256, lds) != hipSuccess || v < 1)
-      v = 2;
+  static int n_cu = 0;
+  if (n_cu == 0) {
     int dev = 0, cus = 0;
     (void)hipGetDevice(&dev);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    occ = v;
     n_cu = cus;
   }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)gemv_kernel<C, B, R, NB>, 256, lds) != hipSuccess ||
+      occ < 1)
+    occ = 1;
   const int per_cu = env_int("SF_GEMV_WGS_PER_CU", occ);
-  const int cap = n_cu * (per_cu > 0 ? min(per_cu, occ) : occ) - (a.k_sel > 0 ? 1 : 0);
+  const int cap = n_cu * (per_cu > 0 ? min(per_cu, occ) : occ);
   const int tiles_per_wg = (a.total_tiles + cap - 1) / cap;
-  const int grid = (a.total_tiles + tiles_per_wg - 1) / tiles_per_wg + (a.k_sel > 0 ? 1 : 0);
+  const int grid = (a.total_tiles + tiles_per_wg - 1) / tiles_per_wg;
   hipLaunchKernelGGL((gemv_kernel<C, B, R, NB>), dim3((unsigned)grid), dim3(256), lds, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
@@ -617,26 +679,24 @@ sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, hipStream_t s) {
   }
 }
 
-}  // namespace
+int codes_per_chunk(int b) { return (b == 1 || b == 2 || b == 4 || b == 8) ? 128 / b : 32; }
 
-size_t sf_gemv_ws_layout(int32_t n_ops, int64_t k_in, int32_t k_sel, size_t* off_sel,
-                         size_t* off_hk, size_t* off_hs, size_t* off_nh) {
-  size_t off = sf_align256(sizeof(WsControl));
-  *off_sel = off;
-  off += sf_align256((size_t)(k_sel > 0 ? k_sel : 1) * 4);
-  *off_hk = off;
-  off += sf_align256((size_t)n_ops * (k_sel > 0 ? k_sel : 1) * 4);
-  *off_hs = off;
-  off += sf_align256((size_t)n_ops * (k_sel > 0 ? k_sel : 1) * 4);
-  *off_nh = off;
-  off += sf_align256((size_t)n_ops * 4);
-  (void)k_in;
-  return off;
+size_t gemv_ws_layout(int32_t n_ops, int32_t k_sel, size_t* off_sel, size_t* off_slot) {
+  const size_t ks = k_sel > 0 ? (size_t)k_sel : 1;
+  size_t o = sf_align256(sizeof(WsControl));
+  *off_sel = o;
+  o += sf_align256(ks * 4);
+  *off_slot = o;
+  o += sf_align256((size_t)(n_ops > 0 ? n_ops : 1) * ks * 4);
+  return o;
 }
 
+}  // namespace
+
 extern "C" size_t sf_workspace_bytes_gemv(int32_t n_ops, int64_t k_in, int32_t k_sel) {
-  size_t a, b, c, d;
-  return sf_gemv_ws_layout(n_ops, k_in, k_sel, &a, &b, &c, &d);
+  (void)k_in;
+  size_t a, b;
+  return gemv_ws_layout(n_ops, k_sel, &a, &b);
 }
 
 extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
@@ -652,6 +712,8 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   SF_REQUIRE(K > 0 && K % 128 == 0 && K <= (1 << 20), SF_EINVAL, "k_in must be a multiple of 128");
   SF_REQUIRE(k_sel >= 0 && k_sel <= K, SF_EINVAL, "k_sel out of range");
   SF_REQUIRE(k_sel == 0 || f.r > 0, SF_EINVAL, "k_sel > 0 needs r > 0");
+  SF_REQUIRE(k_sel == 0 || sel_in || k_sel == K || K <= MAX_SEL_K, SF_EUNSUPPORTED,
+             "computed selection needs k_in <= 32768");
   GemvArgs a = {};
   // rows per wave (SF_GEMV_ROWS_PER_WAVE = 1, 2, 4 or 8 overrides the default)
   int rpw = env_int("SF_GEMV_ROWS_PER_WAVE", 0);
@@ -684,17 +746,13 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     }
     tiles += (int)((o.w.n_out + rows_wg - 1) / rows_wg);
   }
-  size_t o_sel, o_hk, o_hs, o_nh;
-  const size_t need = sf_gemv_ws_layout(n_ops, K, k_sel, &o_sel, &o_hk, &o_hs, &o_nh);
-  SF_REQUIRE(ws->bytes >= need, SF_ENOMEM, "workspace too small");
+  size_t o_sel, o_slot;
+  SF_REQUIRE(ws->bytes >= gemv_ws_layout(n_ops, k_sel, &o_sel, &o_slot), SF_ENOMEM, "workspace too small");
   a.x = x_f16;
   a.sel_in = sel_in;
   a.sel_out = sel_out;
-  a.ctl = (WsControl*)ws->base;
   a.ws_sel = (int32_t*)(ws->base + o_sel);
-  a.ws_hit_k = (int32_t*)(ws->base + o_hk);
-  a.ws_hit_slot = (int32_t*)(ws->base + o_hs);
-  a.ws_nhit = (int32_t*)(ws->base + o_nh);
+  a.ws_slot = (int32_t*)(ws->base + o_slot);
   a.n_ops = n_ops;
   a.k_in = (int32_t)K;
   a.batch = batch;
@@ -702,12 +760,16 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.r = f.r;
   a.total_tiles = tiles;
   hipStream_t s = (hipStream_t)stream;
+  if (k_sel > 0) {
+    hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(SEL_NT), 0, s, a);
+    SF_LAUNCH_CHECK();
+  }
   // two batch rows per launch when both fit the LDS staging of x, else one
-  const int max_nb = ((size_t)2 * K * 2 + 2 * K * 4 / 16 + 32 * (K / 128) * 4 + SW * HIT_CAP * 4) <= 52 * 1024 ? 2 : 1;
+  const int cpc = codes_per_chunk(f.b);
+  const int max_nb = gemv_lds_bytes((int)K, cpc, 2, n_ops, k_sel, rpw, false) <= 64 * 1024 ? 2 : 1;
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;
-    a.do_log = b0 == 0;
     sf_status st = dispatch_b(a, f.b, rpw, nb, s);
     if (st != SF_OK) return st;
   }

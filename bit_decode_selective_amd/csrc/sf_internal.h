@@ -125,8 +125,15 @@ static SfProbeInstaller sf_probe_installer;
     if (threadIdx.x == 0 && sf_probe_buf)                                                 \
       sf_probe_buf[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + (i)] = wall_clock64(); \
   } while (0)
+// the same, recorded by thread t of the workgroup
+#define SF_TS_T(i, t)                                                                     \
+  do {                                                                                    \
+    if (threadIdx.x == (t) && sf_probe_buf)                                               \
+      sf_probe_buf[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + (i)] = wall_clock64(); \
+  } while (0)
 #else
 #define SF_TS(i) ((void)0)
+#define SF_TS_T(i, t) ((void)0)
 #endif
 
 static inline size_t sf_align256(size_t v) { return (v + 255) & ~size_t(255); }

@@ -215,7 +215,10 @@ typedef struct {
  * Selection: if sel_in (device [k_sel], ascending, distinct) is NULL, the k_sel
  * channels of largest max-over-batch |x|, ties to the lower index.  sel_out
  * (device [k_sel], may be NULL) receives the selection, ascending.  k_sel = 0 is
- * the unrefined low-bit GEMV.  cache may be NULL (every selection misses). */
+ * the unrefined low-bit GEMV.  cache may be NULL (every selection misses).
+ * A computed selection (sel_in NULL, 0 < k_sel < k_in) needs k_in <= 32768
+ * (SF_EUNSUPPORTED otherwise).  Two launches: the selection with its lookups,
+ * then the GEMV. */
 sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
                           int32_t batch, int32_t k_sel, const int32_t* sel_in,
                           int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
@@ -227,10 +230,13 @@ sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* 
  * Per (batch, kv head): logits from the resident keys, softmax per query head,
  * token score = that softmax summed over the kv head's query heads; the k_sel
  * tokens of largest score (ties to the lower token) are selected (or sel_in,
- * device [batch][n_kv][k_sel], ascending), looked up in `pool`, and for the hits
+ * device [batch][n_kv][k_sel], ascending and distinct per KV head), looked up
+ * in `pool`, and for the hits
  * both the key and the value use the full (b+r)-bit value; the output softmax is
  * over all tokens after that replacement.  sel_out / hit_out (device
- * [batch][n_kv][k_sel], may be NULL) receive the selection and slots. */
+ * [batch][n_kv][k_sel], may be NULL) receive the selection and slots.
+ * t_len <= 1048576.  Workspaces may be shared by calls on one stream, not by
+ * calls that can run at the same time. */
 sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
                                  float softmax_scale, int32_t k_sel, const int32_t* sel_in,
                                  sf_refine_cache* cache, int32_t pool, float* out,
