@@ -774,12 +774,20 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 }
 
 // ---- pv: final weights, value sums, hit refinements, merge ---------------------------
+// Every load of the workgroup is issued first: its V codes (16 bytes a thread per
+// step), scale words, final logits, the KV head's max, and the selection words that
+// locate this split's hits.  V codes are staged column-major ([code word][token],
+// padded), so a lane's B operand -- one dim of 8 consecutive tokens -- is two
+// 16-byte LDS reads.  The last workgroup of the KV head sums every split's record.
 template <int B, int G>
 __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   constexpr int SP = pv_tokens(B);
-  constexpr int WPT = HD * B / 32, WPTP = WPT + 1, UP = SP + 8;
-  constexpr int TPW = SP / 256;  // tokens per thread in the weight phase
-  __shared__ uint32_t s_vc[SP * WPTP];
+  constexpr int WPT = HD * B / 32;       // code words per token
+  constexpr int CST = SP + 4;            // column stride (words), keeps 16-byte alignment
+  constexpr int UP = SP + 8;
+  constexpr int TPW = SP / 256;          // tokens per thread in the weight phase
+  constexpr int NV = SP * WPT / 4 / 256; // 16-byte code loads per thread
+  __shared__ uint32_t s_vc[WPT * CST];
   __shared__ _Float16 s_u[2 * G][UP];
   __shared__ uint32_t s_vsz[SP];
   __shared__ float s_w[G][SP];
@@ -795,15 +803,14 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   const int t_begin = split * SP, n_here = min(SP, T - t_begin);
   const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
   SF_TS(12);
-  // loads: value codes -> LDS, this thread's scale words and final logits -> registers
+  // ---- loads ----
+  u32x4 vc[NV];
   {
     const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
-    const int nv = n_here * WPT / 4;
-    for (int i = tid; i < nv; i += 256) {
-      const u32x4 v = __builtin_nontemporal_load(src + i);
-      const int w = 4 * i, tk = w / WPT, c = w - tk * WPT;
-      uint32_t* d = s_vc + tk * WPTP + c;
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = tid + 256 * i;
+      vc[i] = idx < n_here * WPT / 4 ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   const int tl0 = TPW * tid;  // this thread's first token within the split
@@ -828,7 +835,14 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     below0 += t < t_begin;
     below1 += t < t_begin + n_here;
   }
-  // largest value scale of the split
+  // ---- V codes into LDS, column-major ----
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int w = 4 * (tid + 256 * i), tk = w / WPT, c = w - tk * WPT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_vc[(c + e) * CST + tk] = vc[i][e];
+  }
+  // largest value scale of the split, and the hit range
   float smx = 0.f;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -847,9 +861,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     s_rng[wave][1] = below1;
   }
   __syncthreads();
+  smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
   const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
   const int hit_hi = (s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]);
-  smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
   const float smax = smx * (float)(1u << a.r);
   int e2 = 0;
   if (smax > 0.f) (void)frexpf(smax, &e2);
@@ -873,7 +887,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
       acc3[3 * h + 2] += (float)hi + (float)lo;
     }
-  __syncthreads();  // s_u, s_vc, s_vsz written; s_red free
+  __syncthreads();  // s_u, s_vc, s_vsz, s_w written; s_red free
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1)
 #pragma unroll
@@ -885,6 +899,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 
   // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
   const int n = lane & 15, qg = lane >> 4;
+  constexpr uint32_t cmask = (1u << B) - 1u;
   f4_t pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
   for (int kb = 0; kb < SP / 32; ++kb) {
@@ -898,7 +913,15 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const u32x4 bv = code_operand<B, WPTP>(s_vc, tk0, 32 * wave + 16 * db + n);
+      const int d = 32 * wave + 16 * db + n;
+      const int bit = d * B, wi = bit >> 5, sh = bit & 31;
+      const u32x4 w0 = *(const u32x4*)(s_vc + wi * CST + tk0);
+      const u32x4 w1 = *(const u32x4*)(s_vc + wi * CST + tk0 + 4);
+      const uint32_t c[8] = {(w0.x >> sh) & cmask, (w0.y >> sh) & cmask, (w0.z >> sh) & cmask, (w0.w >> sh) & cmask,
+                             (w1.x >> sh) & cmask, (w1.y >> sh) & cmask, (w1.z >> sh) & cmask, (w1.w >> sh) & cmask};
+      u32x4 bv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = (((c[2 * e + 1] << 16) | c[2 * e]) << (10 - B)) | 0x3C003C00u;
       pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
     }
   }
@@ -916,9 +939,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       const int slot = slots[j];
       if (slot < 0 || t < 0 || t >= n_here) continue;
       const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
-      const float s = sf_h2f(s_vsz[t]);
-      const float c0 = s * (float)field(unit, HD * r + 2 * lane * r, r);
-      const float c1 = s * (float)field(unit, HD * r + (2 * lane + 1) * r, r);
+      const float sv = sf_h2f(s_vsz[t]);
+      const float c0 = sv * (float)field(unit, HD * r + 2 * lane * r, r);
+      const float c1 = sv * (float)field(unit, HD * r + (2 * lane + 1) * r, r);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
@@ -951,53 +974,30 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   }
   if (tid < G) sf_put(PP + tid * PW + HD + 1, s_st[3 * tid]);
   SF_TS(14);
-  // merge in two levels: the last of each group of 8 splits sums the group into
-  // the group's first record, the last group to finish sums the groups
-  const int grp = split >> 3, ngrp = (a.nsp + 7) >> 3;
-  const int gsize = min(8, a.nsp - 8 * grp);
-  uint32_t* gctr = a.hist + (size_t)bh * 3 * NBIN + 2 * NBIN + 1024;  // words the select kernel leaves at zero
-  sf_drain();
-  __syncthreads();
-  if (tid == 0)
-    s_flag = __hip_atomic_fetch_add(gctr + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(gsize - 1);
-  __syncthreads();
-  if (!s_flag) return;
-  float* PB = a.part_p + (size_t)bh * a.nsp * G * PW;
-  for (int i = tid; i < G * (HD + 1); i += 256) {
-    const int h = i / (HD + 1), d = i - h * (HD + 1);
-    const int col = d < HD ? d : HD + 1;  // value sums, then the weight sum
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = sf_get(PB + ((8 * grp + min(k, gsize - 1)) * G + h) * PW + col);
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < gsize) sum += v[k];
-    sf_put(PB + ((8 * grp) * G + h) * PW + col, sum);
-  }
   sf_drain();
   __syncthreads();
   if (tid == 0)
     s_flag = __hip_atomic_fetch_add(a.ctl + bh * 8 + 6, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(ngrp - 1);
+             (uint32_t)(a.nsp - 1);
   __syncthreads();
   if (!s_flag) return;
-  // last group of this KV head: out = sum N / sum z (one common max)
+  // last workgroup of this KV head: out = sum N / sum z (one common max); every
+  // thread issues a batch of coherent loads before adding any of them
+  const float* PB = a.part_p + (size_t)bh * a.nsp * G * PW;
   for (int i = tid; i < G * HD; i += 256) {
     const int h = i / HD, d = i - h * HD;
     float num = 0.f, den = 0.f;
-    for (int g0 = 0; g0 < ngrp; g0 += 16) {
-      float vn[16], vd[16];
+    for (int s0 = 0; s0 < a.nsp; s0 += 32) {
+      float vn[32], vd[32];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int g = min(g0 + k, ngrp - 1);
-        vn[k] = sf_get(PB + ((8 * g) * G + h) * PW + d);
-        vd[k] = sf_get(PB + ((8 * g) * G + h) * PW + HD + 1);
+      for (int k = 0; k < 32; ++k) {
+        const int sp = min(s0 + k, a.nsp - 1);
+        vn[k] = sf_get(PB + (sp * G + h) * PW + d);
+        vd[k] = sf_get(PB + (sp * G + h) * PW + HD + 1);
       }
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (g0 + k < ngrp) {
+      for (int k = 0; k < 32; ++k)
+        if (s0 + k < a.nsp) {
           num += vn[k];
           den += vd[k];
         }
