@@ -143,12 +143,19 @@ class Model:
             self.out.append(torch.empty((batch, NQ, HD), dtype=torch.float32, device=dev))
         self.ch_pct, self.tok_pct = ch_pct, tok_pct
         ws_bytes = max(
-            [binding.lib().sf_workspace_bytes_gemv(len(ops), k_in, k_select(ch_pct, k_in))
+            [self._gemv_ws_bytes(ops, batch, k_select(ch_pct, k_in))
              for grp in self.groups for _, ops, k_in in grp]
             + [binding.lib().sf_workspace_bytes_attn(batch, NQ, NKV, T, k_select(tok_pct, T))]
         )
         self.ws = binding.workspace(ws_bytes, dev)
         torch.cuda.synchronize()
+
+    def _gemv_ws_bytes(self, ops, batch, ks):
+        b = self.binding
+        arr = (b.sf_gemv_op * len(ops))()
+        for i, (w, pool) in enumerate(ops):
+            arr[i] = b.sf_gemv_op(w.desc(), pool, None, None)
+        return b.lib().sf_workspace_bytes_gemv(arr, len(ops), batch, ks)
 
     def build_calls(self, refined=True):
         """Prebuilt ctypes argument tuples for every launch of one step."""

@@ -85,7 +85,7 @@ _PROTOS = {
     "sf_last_error": (C.c_char_p, []),
     "sf_workspace_create": (I32, [SZ, C.POINTER(VP)]),
     "sf_workspace_destroy": (I32, [VP]),
-    "sf_workspace_bytes_gemv": (SZ, [I32, I64, I32]),
+    "sf_workspace_bytes_gemv": (SZ, [C.POINTER(sf_gemv_op), I32, I32, I32]),
     "sf_workspace_bytes_attn": (SZ, [I32, I32, I32, I32, I32]),
     "sf_workspace_check": (I32, [VP]),
     "sf_quantize_nested": (I32, [VP, I64, I64, sf_qfmt, I32, VP, VP, VP, VP]),
@@ -417,7 +417,7 @@ def refined_gemv(ops, x, k_sel, cache=None, sel_in=None, stream=None, ys=None, w
         hits.append(h[:k_sel] if h is not None else None)
     sel = torch.empty(max(1, k_sel), dtype=torch.int32, device=dev)
     sin = _dev_tensor(sel_in, torch.int32, dev) if sel_in is not None else None
-    ws = workspace(lib().sf_workspace_bytes_gemv(n, w0.k_in, k_sel), dev)
+    ws = workspace(lib().sf_workspace_bytes_gemv(arr, n, batch, k_sel), dev)
     check(
         lib().sf_refined_gemv(
             arr, n, _ptr(xb), batch, k_sel, _ptr(sin), _ptr(sel), cache.handle if cache else None, ws.handle,

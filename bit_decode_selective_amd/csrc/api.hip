@@ -7,8 +7,7 @@ namespace {
 thread_local std::string g_last_error;
 
 __global__ void ws_zero_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 }  // namespace
 
@@ -57,7 +56,7 @@ extern "C" sf_status sf_workspace_create(size_t bytes, sf_workspace** out) {
   }
   w->bytes = bytes;
   const int words = (int)(sizeof(WsControl) / 4);
-  hipLaunchKernelGGL(ws_zero_kernel, dim3(1), dim3(64), 0, 0, (uint32_t*)w->base, words);
+  hipLaunchKernelGGL(ws_zero_kernel, dim3(8), dim3(256), 0, 0, (uint32_t*)w->base, words);
   e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     hipFree(w->base);

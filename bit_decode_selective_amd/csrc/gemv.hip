@@ -21,6 +21,9 @@
 //     chunk), plus the sparse refinement delta of each row tile before it is
 //     written: the refinement words of the tile's rows in every hit slot are
 //     requested when the tile starts and consumed after its chunks.
+#include <algorithm>
+#include <cstddef>
+
 #include "sf_internal.h"
 
 #define SF_MAX_OPS 4
@@ -29,6 +32,9 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
@@ -53,6 +59,12 @@ struct GemvArgs {
   int32_t* ws_sel;   // [k_sel]: selection, ascending
   int32_t* ws_slot;  // [n_ops][k_sel]: slot per op, -1 = miss
   int32_t n_ops, k_in, batch, batch_off, k_sel, r, total_tiles, hits_in_lds;
+  // batched (MFMA) variant: channel slices per row block, groups per slice, hit
+  // capacity per slice, padded rows, slice partials [ns][batch][rows_pad], and one
+  // counter per row block
+  int32_t ns, gs, nhp, rows_pad;
+  float* part;
+  uint32_t* ctr;
 };
 
 // ---- code layouts ----------------------------------------------------------------
@@ -609,6 +621,338 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   SF_TS(3);
 }
 
+
+// ---- batched GEMV on MFMA (batch 3..16 per launch) --------------------------------
+// With several batch rows the GEMV is a real contraction.  v_mfma_f32_16x16x32_f16
+// takes A = x (row = batch row, fp16, exact) and B = codes expanded to fp16
+// 1 + c/2^b (exact), giving C[batch][row] = X + sum_k c x / 2^b over its 32 k-slots.
+// The 32 k-slots of one MFMA come from one group of 128 channels: lane (q, n)
+// supplies 8 codes of weight row n from channels [32q, 32q + 32) of the group,
+// four MFMAs cover the group, and the group's scale words are applied to the
+// fp32 result: y += s' D + (z - s') X with s' = s 2^(r+b).  x is staged in LDS
+// once per workgroup, in the order in which a word's half-pairs come out.  Hit
+// refinements of the workgroup's channel slice are compacted, 32 to an MFMA:
+// A = x at the hit channels, B = s * c_lo as a sum of two fp16 terms (exact), so
+// the fp32 sum sees the full-precision value on hits.  A workgroup covers 64*RT
+// rows (RT 16-row tiles per wave) by one channel slice; the slices of a row block
+// are summed in slice order by the workgroup that finishes last.
+constexpr int MPFG = 4;         // groups of codes in flight per tile
+constexpr int MAX_ROW_BLOCKS = 1024;  // counters in the workspace control block
+
+template <int W>
+__device__ __forceinline__ void load_words(const uint8_t* src, uint32_t (&w)[W]) {
+  if constexpr (W == 1) {
+    w[0] = __builtin_nontemporal_load((const uint32_t*)src);
+  } else if constexpr (W == 2) {
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)src);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)src + i);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  }
+}
+
+__host__ __device__ constexpr size_t mfma_lds_words(int nb, int gs, int rows_wg, int nhp) {
+  return (size_t)nb * (gs * 64 + 4) + (size_t)gs * 16 + (size_t)rows_wg * (gs + 1) * 2 +
+         ((size_t)nb * (nhp + 8) + 1) / 2 + (size_t)nhp * 2;
+}
+
+template <int B, int RT>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
+  using C = CodecPow2<B>;
+  constexpr int WQ = B;  // words holding one lane's 32 codes of a group
+  extern __shared__ uint32_t smem[];
+  __shared__ int s_cnt[4][2];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int ns = a.ns, GS = a.gs;
+  const int slice = blockIdx.x % ns, tile_g = blockIdx.x / ns;
+  const int op = op_of_tile(a, tile_g);
+  const GemvOpDev& o = a.ops[op];
+  constexpr int rows_wg = 64 * RT;
+  const int row_wg0 = (tile_g - o.tile_begin) * rows_wg;
+  const int K = a.k_in, ngr = K / 128;
+  const int g0 = slice * GS, k0 = g0 * 128, KS = GS * 128;
+  const int nb = min(16, a.batch - a.batch_off);
+  const size_t rowbytes = (size_t)K * B / 8;
+  const int XSTR = GS * 64 + 4;  // words per batch row of staged x
+  const int SSTR = GS + 1;       // scale pairs per row
+  const int HSTR = a.nhp + 8;    // fp16 per batch row of hit x
+  uint32_t* xs = smem;                                  // [nb][XSTR]
+  float* xsum = (float*)(xs + nb * XSTR);               // [GS][16]
+  float2* sp = (float2*)(xsum + GS * 16);               // [rows_wg][SSTR]: (s', z - s')
+  _Float16* hx = (_Float16*)(sp + rows_wg * SSTR);      // [nb][HSTR]
+  int32_t* hk = (int32_t*)(xs + (mfma_lds_words(nb, GS, rows_wg, a.nhp) - 2 * a.nhp));  // [nhp]
+  int32_t* hs = hk + a.nhp;                                                            // [nhp]
+  const int wrow0 = wave * 16 * RT;  // this wave's first row within the block
+
+  // codes of the first MPFG groups of every tile
+  uint32_t cw[MPFG][RT][WQ];
+  auto issue = [&](int u, int gl) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int row = row_wg0 + wrow0 + 16 * t + n;
+      if (gl < GS && row < o.n_out) {
+        load_words<WQ>(o.res + (size_t)row * rowbytes + (size_t)(g0 + gl) * (16 * B) + q * (4 * B), cw[u][t]);
+      } else {
+#pragma unroll
+        for (int w = 0; w < WQ; ++w) cw[u][t][w] = 0u;
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < MPFG; ++u) issue(u, u);
+
+  // x slice -> LDS in half-pair order, with its group sums
+  {
+    const int per_row = KS / 8;  // 16-byte loads per batch row (a multiple of 16)
+    const int items = nb * per_row;
+    constexpr int XB = 4;
+    for (int i0 = 0; i0 < items; i0 += 256 * XB) {
+      u32x4 xv[XB];
+#pragma unroll
+      for (int it = 0; it < XB; ++it) {
+        const int i = i0 + 256 * it + tid;
+        if (i < items) {
+          const int bc = i / per_row, c8 = i - bc * per_row;
+          xv[it] = *(const u32x4*)(a.x + (size_t)(a.batch_off + bc) * K + k0 + 8 * c8);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < XB; ++it) {
+        const int i = i0 + 256 * it + tid;
+        float part = 0.f;
+        int bc = 0, c8 = 0;
+        if (i < items) {
+          bc = i / per_row;
+          c8 = i - bc * per_row;
+          const uint32_t wds[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
+          uint16_t* xh = (uint16_t*)(xs + bc * XSTR);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kl = 8 * c8 + e, gl = kl >> 7, kg = kl & 127;
+            int j, hi;
+            C::locate(kg & 31, &j, &hi);
+            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+            xh[2 * ((gl * 4 + (kg >> 5)) * 16 + j) + hi] = hb;
+            part += (float)__builtin_bit_cast(_Float16, hb);
+          }
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) part += __shfl_xor(part, off, 16);
+        if (i < items && (c8 & 15) == 0) xsum[(c8 >> 4) * 16 + bc] = part;
+      }
+    }
+    for (int i = tid; i < GS * 16; i += 256)
+      if ((i & 15) >= nb) xsum[i] = 0.f;
+  }
+  // scale words of the block's rows in the slice -> (s 2^(r+b), z - s 2^(r+b))
+  {
+    const float scl = (float)(1u << (a.r + B));
+    constexpr int SB = 8;
+    for (int i0 = 0; i0 < rows_wg * GS; i0 += 256 * SB) {
+      uint32_t w[SB];
+#pragma unroll
+      for (int it = 0; it < SB; ++it) {
+        const int i = i0 + 256 * it + tid;
+        const int rl = i / GS, gl = i - rl * GS, row = row_wg0 + rl;
+        w[it] = (i < rows_wg * GS && row < o.n_out) ? o.sz[(size_t)row * ngr + g0 + gl] : 0u;
+      }
+#pragma unroll
+      for (int it = 0; it < SB; ++it) {
+        const int i = i0 + 256 * it + tid;
+        if (i < rows_wg * GS) {
+          const int rl = i / GS, gl = i - rl * GS;
+          const float sv = sf_h2f(w[it]) * scl, zv = sf_h2f(w[it] >> 16);
+          sp[rl * SSTR + gl] = make_float2(sv, zv - sv);
+        }
+      }
+    }
+  }
+  // selected channels inside the slice: positions [h0, h1) of the ascending list
+  const int ks = a.k_sel;
+  int h0 = 0, nh = 0;
+  if (ks > 0) {
+    int c0 = 0, c1 = 0;
+    for (int j = tid; j < ks; j += 256) {
+      const int k = a.ws_sel[j];
+      c0 += k < k0;
+      c1 += k < k0 + KS;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      c0 += __shfl_xor(c0, off, 64);
+      c1 += __shfl_xor(c1, off, 64);
+    }
+    if (lane == 0) {
+      s_cnt[wave][0] = c0;
+      s_cnt[wave][1] = c1;
+    }
+  }
+  __syncthreads();
+  if (ks > 0) {
+    h0 = (s_cnt[0][0] + s_cnt[1][0]) + (s_cnt[2][0] + s_cnt[3][0]);
+    nh = (s_cnt[0][1] + s_cnt[1][1]) + (s_cnt[2][1] + s_cnt[3][1]) - h0;
+    const int nhp = (nh + 31) & ~31;
+    const int32_t* slots = a.ws_slot + (size_t)op * ks;
+    for (int j = tid; j < nhp; j += 256) {
+      const bool valid = j < nh;
+      const int k = valid ? a.ws_sel[h0 + j] : k0;
+      hk[j] = k;
+      hs[j] = valid ? slots[h0 + j] : -1;
+      for (int bc = 0; bc < nb; ++bc)
+        hx[bc * HSTR + j] = valid ? __builtin_bit_cast(_Float16, a.x[(size_t)(a.batch_off + bc) * K + k])
+                                  : (_Float16)0.f;
+    }
+  }
+
+  // resident GEMV
+  f4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+  const bool arow = n < nb;  // this lane's A row is a real batch row
+  for (int gb = 0; gb < GS; gb += MPFG) {
+#pragma unroll
+    for (int u = 0; u < MPFG; ++u) {
+      const int gl = gb + u;
+      if (gl < GS) {
+        h8_t ax[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (arow) {
+            ax[m] = *(const h8_t*)(xs + n * XSTR + (gl * 4 + q) * 16 + 4 * m);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ax[m][e] = (_Float16)0.f;
+          }
+        }
+        const f4_t X4 = *(const f4_t*)(xsum + gl * 16 + 4 * q);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x4 bv = {C::pair(cw[u][t], 4 * m), C::pair(cw[u][t], 4 * m + 1), C::pair(cw[u][t], 4 * m + 2),
+                              C::pair(cw[u][t], 4 * m + 3)};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[m], __builtin_bit_cast(h8_t, bv), d, 0, 0, 0);
+          }
+          const float2 sc = sp[(wrow0 + 16 * t + n) * SSTR + gl];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc.x, d[v], fmaf(sc.y, X4[v], acc[t][v]));
+        }
+      }
+      issue(u, gl + MPFG);
+    }
+  }
+
+  // refinements of the hit channels in the slice, 32 channels per MFMA
+  if (ks > 0 && nh > 0) {
+    __syncthreads();  // hit lists staged
+    const uint32_t* units = (const uint32_t*)o.pool.slots;
+    const int wpu = o.pool.unit_bytes >> 2;
+    const int r = a.r;
+    const float sdown = 1.f / (float)(1u << (r + B));
+    for (int blk = 0; blk * 32 < nh; ++blk) {
+      h8_t ah;
+      if (arow) {
+        ah = *(const h8_t*)(hx + n * HSTR + blk * 32 + 8 * q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ah[e] = (_Float16)0.f;
+      }
+      int kk[8], sl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kk[e] = hk[blk * 32 + 8 * q + e];
+        sl[e] = hs[blk * 32 + 8 * q + e];
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int rl = wrow0 + 16 * t + n, row = row_wg0 + rl;
+        const int bit = row * r, wi = bit >> 5, off = bit & 31;
+        uint32_t w0[8], w1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w0[e] = w1[e] = 0u;
+          if (sl[e] >= 0 && row < o.n_out) {
+            const uint32_t* u = units + (size_t)sl[e] * wpu;
+            w0[e] = u[wi];
+            if (off + r > 32 && wi + 1 < wpu) w1[e] = u[wi + 1];
+          }
+        }
+        u32x4 hb, lb;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          uint32_t hp = 0u, lp = 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e = 2 * f + h;
+            const float val = sp[rl * SSTR + ((kk[e] - k0) >> 7)].x * sdown * (float)bits64(w0[e], w1[e], off, r);
+            const _Float16 vh = (_Float16)val;
+            const _Float16 vl = (_Float16)(val - (float)vh);
+            hp |= (uint32_t)__builtin_bit_cast(uint16_t, vh) << (16 * h);
+            lp |= (uint32_t)__builtin_bit_cast(uint16_t, vl) << (16 * h);
+          }
+          hb[f] = hp;
+          lb[f] = lp;
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(h8_t, hb), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(h8_t, lb), acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane (q, n) holds batch rows 4q .. 4q+3 of weight row n of each tile
+  if (ns == 1) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int row = row_wg0 + wrow0 + 16 * t + n;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int bc = 4 * q + v;
+        if (bc < nb && row < o.n_out) o.y[(size_t)(a.batch_off + bc) * o.n_out + row] = acc[t][v];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int prow = tile_g * rows_wg + wrow0 + 16 * t + n;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int bc = 4 * q + v;
+      if (bc < nb) sf_put(a.part + (size_t)(slice * nb + bc) * a.rows_pad + prow, acc[t][v]);
+    }
+  }
+  sf_drain();
+  __syncthreads();
+  if (tid == 0)
+    s_last = __builtin_amdgcn_atomic_inc32(a.ctr + tile_g, (uint32_t)(ns - 1), __ATOMIC_RELAXED, "agent") ==
+             (uint32_t)(ns - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // last slice of this row block: y = sum of the slices' partials, in slice order
+  for (int i = tid; i < nb * rows_wg; i += 256) {
+    const int bc = i / rows_wg, rl = i - bc * rows_wg, row = row_wg0 + rl;
+    if (row >= o.n_out) continue;
+    const float* pp = a.part + (size_t)bc * a.rows_pad + tile_g * rows_wg + rl;
+    const size_t sstride = (size_t)nb * a.rows_pad;
+    float sum = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = s0 + k < ns ? sf_get(pp + (size_t)(s0 + k) * sstride) : 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sum += v[k];
+    }
+    o.y[(size_t)(a.batch_off + bc) * o.n_out + row] = sum;
+  }
+}
+
 int env_int(const char* name, int dflt) {
   const char* e = getenv(name);
   return e ? atoi(e) : dflt;
@@ -681,22 +1025,121 @@ sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, hipStream_t s) {
 
 int codes_per_chunk(int b) { return (b == 1 || b == 2 || b == 4 || b == 8) ? 128 / b : 32; }
 
-size_t gemv_ws_layout(int32_t n_ops, int32_t k_sel, size_t* off_sel, size_t* off_slot) {
+size_t gemv_ws_layout(int32_t n_ops, int32_t k_sel, size_t part_bytes, size_t* off_sel, size_t* off_slot,
+                      size_t* off_part) {
   const size_t ks = k_sel > 0 ? (size_t)k_sel : 1;
   size_t o = sf_align256(sizeof(WsControl));
   *off_sel = o;
   o += sf_align256(ks * 4);
   *off_slot = o;
   o += sf_align256((size_t)(n_ops > 0 ? n_ops : 1) * ks * 4);
+  *off_part = o;
+  o += sf_align256(part_bytes);
   return o;
+}
+
+int device_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, cus = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    n_cu = cus;
+  }
+  return n_cu;
+}
+
+// The batched MFMA kernel serves b in {1, 2, 4, 8} from three batch rows up
+// (SF_GEMV_MFMA=0 / 1 forces it off / on).
+bool mfma_wanted(int b, int batch) {
+  if (b != 1 && b != 2 && b != 4 && b != 8) return false;
+  const int e = env_int("SF_GEMV_MFMA", -1);
+  if (e >= 0) return e != 0;
+  return batch >= 3;
+}
+
+constexpr size_t MAX_MFMA_LDS = 64 * 1024;
+
+struct MfmaPlan {
+  int rt = 0, ns = 1, gs = 0, nhp = 0, tiles = 0;
+  size_t part_bytes = 0;
+};
+
+// Rows per workgroup: 256 when that still gives a quarter of the CUs a row block,
+// else 128, else 64.  Channel slices: the fewest (a divisor of the group count,
+// at most 16 groups each, LDS within 64 KB) that give 1.5 workgroups per CU.
+// SF_GEMV_MFMA_RT and SF_GEMV_MFMA_SLICES override the choices.
+MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel) {
+  MfmaPlan p;
+  const int n_cu = device_cus();
+  const int nb = batch < 16 ? batch : 16;
+  auto tiles_for = [&](int rows) {
+    int t = 0;
+    for (int i = 0; i < n_ops; ++i) t += (int)((n_out[i] + rows - 1) / rows);
+    return t;
+  };
+  int rt = env_int("SF_GEMV_MFMA_RT", 0);
+  if (rt != 1 && rt != 2 && rt != 4) rt = tiles_for(256) >= n_cu / 4 ? 4 : (tiles_for(128) >= n_cu / 4 ? 2 : 1);
+  const int rows_wg = 64 * rt, tiles = tiles_for(rows_wg), ngr = K / 128;
+  const int want_ns = env_int("SF_GEMV_MFMA_SLICES", 0);
+  int best = -1;
+  for (int ns = 1; ns <= ngr; ++ns) {
+    if (ngr % ns) continue;
+    const int gs = ngr / ns;
+    if (gs > 16 || (ns > 1 && tiles > MAX_ROW_BLOCKS)) continue;
+    const int nhp = k_sel > 0 ? ((std::min(k_sel, gs * 128) + 31) & ~31) : 0;
+    if (mfma_lds_words(nb, gs, rows_wg, nhp) * 4 > MAX_MFMA_LDS) continue;
+    best = ns;
+    if (want_ns > 0 ? ns >= want_ns : (long)tiles * ns >= 3L * n_cu / 2) break;
+  }
+  if (best < 0) return p;
+  p.rt = rt;
+  p.ns = best;
+  p.gs = ngr / best;
+  p.nhp = k_sel > 0 ? ((std::min(k_sel, p.gs * 128) + 31) & ~31) : 0;
+  p.tiles = tiles;
+  p.part_bytes = best > 1 ? (size_t)best * nb * tiles * rows_wg * 4 : 0;
+  return p;
+}
+
+template <int B>
+sf_status launch_mfma_rt(GemvArgs& a, int rt, size_t lds, hipStream_t s) {
+  const dim3 grid((unsigned)(a.total_tiles * a.ns));
+  switch (rt) {
+    case 1: hipLaunchKernelGGL((gemv_mfma_kernel<B, 1>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<B, 2>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((gemv_mfma_kernel<B, 4>), grid, dim3(256), lds, s, a); break;
+  }
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+sf_status launch_mfma(GemvArgs& a, int b, int rt, size_t lds, hipStream_t s) {
+  switch (b) {
+    case 1: return launch_mfma_rt<1>(a, rt, lds, s);
+    case 2: return launch_mfma_rt<2>(a, rt, lds, s);
+    case 4: return launch_mfma_rt<4>(a, rt, lds, s);
+    default: return launch_mfma_rt<8>(a, rt, lds, s);
+  }
+}
+
+// The plan sf_refined_gemv uses for these ops (rt = 0: the per-row-pair kernel).
+MfmaPlan plan_for(const sf_gemv_op* ops, int n_ops, int batch, int k_sel) {
+  MfmaPlan p;
+  if (!mfma_wanted(ops[0].w.fmt.b, batch)) return p;
+  int64_t no[SF_MAX_OPS];
+  for (int i = 0; i < n_ops; ++i) no[i] = ops[i].w.n_out;
+  return mfma_plan(no, n_ops, (int)ops[0].w.k_in, batch, k_sel);
 }
 
 }  // namespace
 
-extern "C" size_t sf_workspace_bytes_gemv(int32_t n_ops, int64_t k_in, int32_t k_sel) {
-  (void)k_in;
-  size_t a, b;
-  return gemv_ws_layout(n_ops, k_sel, &a, &b);
+extern "C" size_t sf_workspace_bytes_gemv(const sf_gemv_op* ops, int32_t n_ops, int32_t batch, int32_t k_sel) {
+  size_t part = 0;
+  if (ops && n_ops >= 1 && n_ops <= SF_MAX_OPS && batch >= 1 && ops[0].w.k_in > 0 && ops[0].w.k_in % 128 == 0)
+    part = plan_for(ops, n_ops, batch, k_sel).part_bytes;
+  size_t a, b, c;
+  return gemv_ws_layout(n_ops, k_sel, part, &a, &b, &c);
 }
 
 extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
@@ -721,7 +1164,9 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   for (int i = 0; i < n_ops; ++i) rows_total += ops[i].w.n_out;
   if (rpw != 1 && rpw != 2 && rpw != 4 && rpw != 8)
     rpw = rows_total <= 8192 ? 2 : (rows_total <= 16384 ? 4 : 8);
-  const int rows_wg = 4 * rpw;
+  const MfmaPlan mp = plan_for(ops, n_ops, batch, k_sel);
+  const bool mfma = mp.rt > 0;
+  const int rows_wg = mfma ? 64 * mp.rt : 4 * rpw;
   int tiles = 0;
   for (int i = 0; i < n_ops; ++i) {
     const sf_gemv_op& o = ops[i];
@@ -746,8 +1191,9 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     }
     tiles += (int)((o.w.n_out + rows_wg - 1) / rows_wg);
   }
-  size_t o_sel, o_slot;
-  SF_REQUIRE(ws->bytes >= gemv_ws_layout(n_ops, k_sel, &o_sel, &o_slot), SF_ENOMEM, "workspace too small");
+  size_t o_sel, o_slot, o_part;
+  SF_REQUIRE(ws->bytes >= gemv_ws_layout(n_ops, k_sel, mp.part_bytes, &o_sel, &o_slot, &o_part), SF_ENOMEM,
+             "workspace too small");
   a.x = x_f16;
   a.sel_in = sel_in;
   a.sel_out = sel_out;
@@ -763,6 +1209,21 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   if (k_sel > 0) {
     hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(SEL_NT), 0, s, a);
     SF_LAUNCH_CHECK();
+  }
+  if (mfma) {
+    a.ns = mp.ns;
+    a.gs = mp.gs;
+    a.nhp = mp.nhp;
+    a.rows_pad = tiles * rows_wg;
+    a.part = (float*)(ws->base + o_part);
+    a.ctr = (uint32_t*)(ws->base + offsetof(WsControl, row_ctr));
+    for (int b0 = 0; b0 < batch; b0 += 16) {
+      const int nb = batch - b0 < 16 ? batch - b0 : 16;
+      a.batch_off = b0;
+      sf_status st = launch_mfma(a, f.b, mp.rt, mfma_lds_words(nb, mp.gs, rows_wg, mp.nhp) * 4, s);
+      if (st != SF_OK) return st;
+    }
+    return SF_OK;
   }
   // two batch rows per launch when both fit the LDS staging of x, else one
   const int cpc = codes_per_chunk(f.b);

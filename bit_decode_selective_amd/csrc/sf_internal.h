@@ -38,6 +38,7 @@ struct WsControl {
   uint32_t done;       // workgroups finished (last one resets the words)
   uint32_t timeout;    // set when a bounded device wait gave up
   uint32_t pad[61];    // keeps the data area 256-byte aligned
+  uint32_t row_ctr[1024];  // batched GEMV: slices finished per row block (last one resets)
 };
 
 struct sf_workspace {

@@ -106,10 +106,10 @@ const char* sf_last_error(void);
 
 /* Device workspace for the refined GEMV and attention calls.  `bytes` from
  * sf_workspace_bytes_gemv / sf_workspace_bytes_attn (take the maximum over the
- * calls that share it). */
+ * calls that share it).  Its control block is zeroed at creation; every call
+ * leaves it as it found it. */
 sf_status sf_workspace_create(size_t bytes, sf_workspace** out);
 sf_status sf_workspace_destroy(sf_workspace* ws);
-size_t sf_workspace_bytes_gemv(int32_t n_ops, int64_t k_in, int32_t k_sel);
 size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t t_len, int32_t k_sel);
 /* Returns SF_ESTATE (and clears the flag) if a device-side wait timed out in a
@@ -209,6 +209,12 @@ typedef struct {
   int32_t* hit_out; /* optional [k_sel]: slot of each selected channel, -1 = miss */
 } sf_gemv_op;
 
+/* Workspace bytes for sf_refined_gemv(ops, n_ops, ..., batch, k_sel, ...): the
+ * selection, the slot lists and, for the batched kernel, the partial outputs of
+ * its channel slices ([slices][min(batch, 16)][padded rows] fp32).  The batched
+ * kernel's plan depends on the CU count of the current device. */
+size_t sf_workspace_bytes_gemv(const sf_gemv_op* ops, int32_t n_ops, int32_t batch, int32_t k_sel);
+
 /* y = x W_eff^T for each op, x fp16 [batch][k_in] (batch >= 1), where W_eff uses
  * the full (b+r)-bit value on the selected channels whose refinement unit is in
  * the cache (a hit) and the resident value everywhere else.
@@ -217,8 +223,9 @@ typedef struct {
  * (device [k_sel], may be NULL) receives the selection, ascending.  k_sel = 0 is
  * the unrefined low-bit GEMV.  cache may be NULL (every selection misses).
  * A computed selection (sel_in NULL, 0 < k_sel < k_in) needs k_in <= 32768
- * (SF_EUNSUPPORTED otherwise).  Two launches: the selection with its lookups,
- * then the GEMV. */
+ * (SF_EUNSUPPORTED otherwise).  Launches: the selection with its lookups (k_sel
+ * > 0), then the GEMV: for b in {1, 2, 4, 8} and batch >= 3 the batched MFMA
+ * kernel, one launch per 16 batch rows; otherwise one launch per 2 batch rows. */
 sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
                           int32_t batch, int32_t k_sel, const int32_t* sel_in,
                           int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,

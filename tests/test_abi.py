@@ -63,10 +63,20 @@ def test_host_only_calls(built):
     assert lib.sf_status_string(0) == b"ok"
     assert lib.sf_status_string(1) == b"invalid argument"
     # size queries are host arithmetic
+    from bit_decode_selective_amd.binding import sf_gemv_op, sf_qfmt, sf_qweight
+
     lib.sf_workspace_bytes_gemv.restype = ctypes.c_size_t
-    lib.sf_workspace_bytes_gemv.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    lib.sf_workspace_bytes_gemv.argtypes = [ctypes.POINTER(sf_gemv_op), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    ops = (sf_gemv_op * 3)()
+    for i, n_out in enumerate((4096, 1024, 1024)):
+        ops[i] = sf_gemv_op(sf_qweight(None, None, n_out, 4096, sf_qfmt(2, 2, 128)), i, None, None)
     # selection and per-op slots of the GEMV live in the workspace
-    assert lib.sf_workspace_bytes_gemv(3, 4096, 123) >= 123 * 4 * (1 + 3)
+    one = lib.sf_workspace_bytes_gemv(ops, 3, 1, 123)
+    assert one >= 123 * 4 * (1 + 3)
+    # batch 8 adds the partial outputs of the channel slices: at most
+    # [32 slices][8 rows][6144 rows padded to 256] fp32
+    eight = lib.sf_workspace_bytes_gemv(ops, 3, 8, 123)
+    assert one <= eight <= one + 32 * 8 * 6144 * 4 + 4096
     lib.sf_workspace_bytes_attn.restype = ctypes.c_size_t
     lib.sf_workspace_bytes_attn.argtypes = [ctypes.c_int32] * 5
     assert lib.sf_workspace_bytes_attn(1, 32, 8, 32768, 656) >= 32 * 32768 * 4

@@ -131,3 +131,67 @@ def test_llama8b_layer_shapes(batch):
             assert_close(y, o_gemv.refined_gemv(q, x, want), what=name)
         del qs
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rt,slices", [("1", "1"), ("2", "0"), ("4", "5"), ("0", "0")])
+@pytest.mark.parametrize("b,r", [(2, 2), (4, 4), (1, 3), (8, 0)])
+@pytest.mark.parametrize("batch", [1, 3, 8, 16, 19])
+def test_batched_mfma(b, r, batch, rt, slices, monkeypatch):
+    """The batched (MFMA) kernel: 16-row tiles, 1/2/4 tiles per wave, one or several
+    channel slices summed by the last workgroup, batch rows beyond 16 in a second
+    launch; ragged rows; no, one, a few and all channels refined."""
+    monkeypatch.setenv("SF_GEMV_MFMA", "1")
+    monkeypatch.setenv("SF_GEMV_MFMA_RT", rt)
+    monkeypatch.setenv("SF_GEMV_MFMA_SLICES", slices)
+    n_out = 200 if r in (0, 4) else 224
+    k_in = 640
+    W, qw, q = _setup(16, n_out, k_in, b, r)
+    x = inputs.activation(16, 0, 0, 0, batch, k_in)
+    for k_sel in ([0] if r == 0 else [0, 1, 17, k_in]):
+        (y,), sel, (hit,) = _run([qw], x, k_sel)
+        want_sel = selection.select_channels(x, k_sel)
+        assert sel == want_sel
+        assert_close(y, o_gemv.refined_gemv(q, x, want_sel), what=f"b{b} r{r} batch{batch} k{k_sel}")
+
+
+@pytest.mark.parametrize("slices", ["0", "1", "4"])
+def test_batched_mfma_fused_ragged_ops(slices, monkeypatch):
+    """Three fused matrices with ragged row counts, 20 groups (more than one slice
+    must hold them by default), an external selection and a pool with misses."""
+    monkeypatch.setenv("SF_GEMV_MFMA_SLICES", slices)
+    k_in = 2560
+    qs = [_setup(17, n, k_in, 2, 2, tensor=i) for i, n in enumerate((336, 64, 96))]
+    x = inputs.activation(17, 0, 0, 0, 8, k_in)
+    ks = selection.k_select(3, k_in)
+    ys, sel, hits = _run([t[1] for t in qs], x, ks)
+    want = selection.select_channels(x, ks)
+    assert sel == want
+    for (W, qw, q), y in zip(qs, ys):
+        assert_close(y, o_gemv.refined_gemv(q, x, want))
+    # empty pools: every selected channel misses and keeps its resident value
+    stores = [t[1].host_store() for t in qs]
+    cache = binding.RefineCache([binding.host_pool_desc(s, 0) for s in stores], keep=stores)
+    ext = sorted(np.random.default_rng(1).choice(k_in, ks, replace=False).tolist())
+    ys, sel, hits = _run([t[1] for t in qs], x, ks, sel_in=np.array(ext, dtype=np.int32), cache=cache)
+    assert sel == ext
+    for (W, qw, q), y, h in zip(qs, ys, hits):
+        assert np.all(h == -1)
+        assert_close(y, o_gemv.refined_gemv(q, x, []))
+
+
+def test_batched_mfma_repeated_calls():
+    """Slice counters return to zero after every call: alternate shapes and batch
+    sizes on one workspace."""
+    a = _setup(18, 512, 4096, 2, 2, tensor=0)
+    bq = _setup(18, 4096, 1024, 2, 2, tensor=1)
+    cache_a = binding.RefineCache([a[1].resident_pool_desc()])
+    cache_b = binding.RefineCache([bq[1].resident_pool_desc()])
+    for step in range(6):
+        W, qw, q = a if step % 2 == 0 else bq
+        batch = (8, 5, 16, 8, 3, 12)[step]
+        x = inputs.activation(18, 0, step, 0, batch, qw.k_in)
+        ks = selection.k_select(3, qw.k_in)
+        (y,), sel, _ = _run([qw], x, ks, cache=cache_a if step % 2 == 0 else cache_b)
+        want = selection.select_channels(x, ks)
+        assert sel == want
+        assert_close(y, o_gemv.refined_gemv(q, x, want), what=f"step {step}")
