@@ -213,6 +213,7 @@ sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out) {
     out->log_count = p.d_log_count;
   }
   out->log_cap = p.log_cap;
+  out->resident = p.resident ? 1 : 0;
   out->unit_bytes = (int32_t)p.d.unit_bytes;
   out->n_units = p.d.n_units;
   return SF_OK;

@@ -63,6 +63,7 @@ struct GemvArgs {
   // capacity per slice, padded rows, slice partials [ns][batch][rows_pad], and one
   // counter per row block
   int32_t ns, gs, nhp, rows_pad;
+  int32_t report;  // fused kernel: report the selection, hits and lookup log
   float* part;
   uint32_t* ctr;
 };
@@ -156,9 +157,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // Channel-order prefix of per-channel flags f[q] (q = 0..7: this thread's 8
 // consecutive channels) over the whole workgroup: returns the number of flags in
 // earlier channels; *total = all flags.  One LDS round (lds[0..15]).
+template <int NW = SEL_NT / 64>
 __device__ __forceinline__ int blk_flag_prefix(const bool (&f)[8], int* lds, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NW = SEL_NT / 64;
   int below = 0, wtot = 0;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -374,6 +375,26 @@ __device__ __forceinline__ void load_chunk(const GemvOpDev& o, int row0, int c, 
       for (int w = 0; w < C::WORDS; ++w) cw[r][w] = 0;
       szw[r] = 0;
     }
+  }
+}
+
+// The same, unconditionally: rows past the matrix read its last row (their sums
+// are never written); the caller clamps c.
+template <class C, int R>
+__device__ __forceinline__ void load_chunk_clamped(const GemvOpDev& o, int row0, int c, size_t rowbytes, int ngr,
+                                                   uint32_t (&cw)[R][C::WORDS], uint32_t (&szw)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, o.n_out - 1);
+    const uint32_t* src = (const uint32_t*)(o.res + row * rowbytes + (size_t)c * (4 * C::WORDS));
+    if constexpr (C::WORDS == 4) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)src);
+      cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
+    } else {
+#pragma unroll
+      for (int w = 0; w < C::WORDS; ++w) cw[r][w] = __builtin_nontemporal_load(src + w);
+    }
+    szw[r] = o.sz[(size_t)row * ngr + (c * C::CODES) / 128];
   }
 }
 
@@ -622,6 +643,456 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 }
 
 
+
+
+// Largest bin b of the sum of four per-wave histograms h[w][0..nbin) whose suffix
+// count (bins >= b) reaches `need`; *above = count in bins above b.  Every wave
+// computes it from the histograms itself.  nbin = 256 or 128.
+__device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[256], int nbin, int need, int* bin,
+                                                int* above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbin / 64;
+  int c[4] = {0, 0, 0, 0}, s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < per) {
+      const int b = nbin - 1 - per * lane - i;
+      c[i] = (int)((h[0][b] + h[1][b]) + (h[2][b] + h[3][b]));
+      s += c[i];
+    }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  int run = incl - s, hit = -1, hab = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < per) {
+      if (run < need && run + c[i] >= need) {
+        hit = nbin - 1 - per * lane - i;
+        hab = run;
+      }
+      run += c[i];
+    }
+  const uint64_t m = __ballot(hit >= 0);
+  const int src = m ? __builtin_ctzll(m) : 0;
+  *bin = __shfl(hit, src, 64);
+  *above = __shfl(hab, src, 64);
+}
+__device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[128], int nbin, int need, int* bin,
+                                                int* above) {
+  const int lane = threadIdx.x & 63;
+  int c[2], s = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = 127 - 2 * lane - i;
+    c[i] = (int)((h[0][b] + h[1][b]) + (h[2][b] + h[3][b]));
+    s += c[i];
+  }
+  (void)nbin;
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  int run = incl - s, hit = -1, hab = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (run < need && run + c[i] >= need) {
+      hit = 127 - 2 * lane - i;
+      hab = run;
+    }
+    run += c[i];
+  }
+  const uint64_t m = __ballot(hit >= 0);
+  const int src = m ? __builtin_ctzll(m) : 0;
+  *bin = __shfl(hit, src, 64);
+  *above = __shfl(hab, src, 64);
+}
+
+// Keys of 8 channels (4 words of two 15-bit keys): (#keys > T) | (#keys == T) << 16.
+__device__ __forceinline__ uint32_t gt_eq_count(const uint32_t* kp, uint32_t T) {
+  const u32x4 kv = *(const u32x4*)kp;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = kv[q] & 0xFFFFu, hi = kv[q] >> 16;
+    gt += (lo > T) + (hi > T);
+    eq += (lo == T) + (hi == T);
+  }
+  return gt | (eq << 16);
+}
+
+// Sum of c (0 <= c < 16) over the lanes below this one, by ballots of its bits;
+// *total = the sum over the wave.
+__device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t* total) {
+  uint32_t ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t m = __ballot((c >> b) & 1u);
+    ex += (uint32_t)lanes_below(m) << b;
+    tot += (uint32_t)__popcll(m) << b;
+  }
+  *total = tot;
+  return ex;
+}
+
+// ---- batch-1/2 GEMV with the selection in every workgroup ----------------------
+// One row tile per workgroup (4 waves x R rows).  All code loads of the tile are
+// issued first (a window of D chunks per lane when a row has more than 64 chunks).
+// While they are in flight the workgroup stages x in LDS and selects the channels
+// itself, exactly as the selection workgroup does: keys max-over-batch |x| as
+// 15-bit fp16 patterns (kept in LDS in channel order), the k-th largest by two
+// histogram passes (one histogram per wave), the selected channels in channel
+// order by ballot prefixes.  Each lane then looks up the slots of its hits and
+// requests their refinement words for its wave's rows; the resident dot products
+// run meanwhile and the deltas are added before the row sums are written.  The
+// first workgroup of each matrix reports its hits and lookup log, workgroup 0 the
+// selection.
+template <class C, int B, int R, int NB, int D, int XB>
+__global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t whist[4][256];
+  __shared__ uint32_t whist2[4][128];
+  __shared__ uint32_t s_cnt[4 * (MAX_SEL_K / 2048)];
+  __shared__ int lds[24];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) (&whist[0][0])[i] = 0u;
+  for (int i = tid; i < 4 * 128; i += 256) (&whist2[0][0])[i] = 0u;
+  const int K = a.k_in, nchunks = K / C::CODES, xpairs = K / 2, ngr = K / 128, n8 = K / 8;
+  const int ks = a.k_sel;
+  const bool refine = ks > 0;
+  uint32_t* xs = smem;                                         // [NB][K/2] fp16 pairs
+  float* xsum = (float*)(smem + NB * xpairs);                  // [NB][nchunks]
+  uint32_t* keys = (uint32_t*)(xsum + NB * ((nchunks + 3) & ~3));  // [K/2]: channel-order key pairs
+  uint32_t* s_szw = keys + (refine ? xpairs : 0);              // [4][R][ngr]
+  int32_t* l_sel = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [ks]
+  const int tile_g = blockIdx.x;
+  const int op = op_of_tile(a, tile_g);
+  const GemvOpDev& o = a.ops[op];
+  const int row0 = (tile_g - o.tile_begin) * 4 * R + wave * R;
+  const size_t rowbytes = (size_t)K * B / 8;
+  SF_TS(0);
+
+  // x first (the selection needs it early; loads complete in order), then the
+  // tile's codes; both unconditional (clamped addresses, unused values), so that
+  // staging x waits for the x loads only
+  u32x4 xv0[NB][XB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+#pragma unroll
+    for (int i = 0; i < XB; ++i) xv0[bb][i] = xr[min(256 * i + tid, n8 - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code loads
+  // the first D chunks of every row of this lane
+  uint32_t cw[D][R][C::WORDS];
+  uint32_t szw[D][R];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_chunk_clamped<C, R>(o, row0, min(lane + 64 * u, nchunks - 1), rowbytes, ngr, cw[u], szw[u]);
+
+  // x in pair order; chunk sums; selection keys in channel order
+  uint16_t* xh = (uint16_t*)xs;
+  auto stage = [&](const u32x4 (&xv)[NB][XB], int m0) {
+    constexpr int TPC = C::CODES / 8;  // threads per chunk
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int m = m0 + 256 * i + tid;
+      u32x4 kv = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        float part = 0.f;
+        if (m < n8) {
+          const uint32_t wds[4] = {xv[bb][i].x, xv[bb][i].y, xv[bb][i].z, xv[bb][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x2 = wds[q] & 0x7FFF7FFFu;
+            kv[q] = max(kv[q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[q] >> 16, x2 >> 16) << 16);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * m + e;
+            const int c = k / C::CODES, kk = k - c * C::CODES;
+            int j, hi;
+            C::locate(kk, &j, &hi);
+            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
+            part += (float)__builtin_bit_cast(_Float16, hb);
+          }
+        }
+#pragma unroll
+        for (int o2 = TPC / 2; o2 >= 1; o2 >>= 1) part += __shfl_xor(part, o2, TPC);
+        if (m < n8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
+      }
+      if (refine && m < n8) *(u32x4*)(keys + 4 * m) = kv;
+    }
+  };
+  stage(xv0, 0);
+  for (int m0 = 256 * XB; m0 < n8; m0 += 256 * XB) {  // x longer than XB loads a thread
+    u32x4 xv[NB][XB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+#pragma unroll
+      for (int i = 0; i < XB; ++i) xv[bb][i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
+    }
+    stage(xv, m0);
+  }
+  SF_TS(1);
+
+  // the selection, ascending, into l_sel
+  if (refine) {
+    if (a.sel_in) {
+      for (int j = tid; j < ks; j += 256) l_sel[j] = a.sel_in[j];
+    } else if (ks >= K) {
+      for (int j = tid; j < ks; j += 256) l_sel[j] = j;
+    } else {
+      lds_barrier();  // keys, zeroed histograms
+      // pass 1: top 8 key bits, one histogram per wave
+      for (int m = tid; m < n8; m += 256) {
+        const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
+          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
+        }
+      }
+      lds_barrier();
+      // every wave finds the bin itself (no further barrier)
+      int b1, above1;
+      wave_threshold4(whist, 256, ks, &b1, &above1);
+      SF_TS(5);
+      int need = ks - above1;
+      // pass 2: low 7 bits of the keys in bin b1
+      for (int m = tid; m < n8; m += 256) {
+        const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = kv[q] & 0xFFFFu, hi = kv[q] >> 16;
+          if ((int)(lo >> 7) == b1) atomicAdd(&whist2[wave][lo & 127u], 1u);
+          if ((int)(hi >> 7) == b1) atomicAdd(&whist2[wave][hi & 127u], 1u);
+        }
+      }
+      lds_barrier();
+      int b2, above2;
+      wave_threshold4(whist2, 128, need, &b2, &above2);
+      SF_TS(8);
+      const uint32_t T = ((uint32_t)b1 << 7) | (uint32_t)b2;
+      need -= above2;  // keys equal to T that are taken, lowest channels first
+      // compaction in channel order: per (round, wave) counts of keys above T and
+      // equal to T, one barrier, then every thread places its taken channels at
+      // (#above before) + min(#equal before, need)
+      const int rounds = (n8 + 255) / 256;
+      for (int it = 0; it < rounds; ++it) {
+        const int m = tid + 256 * it;
+        const uint32_t cnt = m < n8 ? gt_eq_count(keys + 4 * m, T) : 0u;
+        uint32_t tg, te;
+        (void)wave_excl_small(cnt & 0xFFFFu, &tg);
+        (void)wave_excl_small(cnt >> 16, &te);
+        if (lane == 0) s_cnt[it * 4 + wave] = tg | (te << 16);
+      }
+      lds_barrier();
+      uint32_t base = 0;  // packed (#above | #equal << 16) before this round
+      for (int it = 0; it < rounds; ++it) {
+        const int m = tid + 256 * it;
+        const uint32_t cnt = m < n8 ? gt_eq_count(keys + 4 * m, T) : 0u;
+        uint32_t tg, te;
+        uint32_t before = base + wave_excl_small(cnt & 0xFFFFu, &tg) + (wave_excl_small(cnt >> 16, &te) << 16);
+        for (int w = 0; w < wave; ++w) before += s_cnt[it * 4 + w];
+        base += (s_cnt[it * 4] + s_cnt[it * 4 + 1]) + (s_cnt[it * 4 + 2] + s_cnt[it * 4 + 3]);
+        if (cnt) {
+          const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+          uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const bool gt = key > T, eq = key == T;
+            if (gt || (eq && eqb < (uint32_t)need)) l_sel[gtb + min(eqb, (uint32_t)need)] = 8 * m + e;
+            gtb += gt;
+            eqb += eq;
+          }
+        }
+      }
+    }
+  }
+  lds_barrier();  // x, chunk sums and the selection
+  SF_TS(2);
+
+  const float scl = (float)(1u << (a.r + B));
+  const int r = a.r;
+  uint32_t* szrow = s_szw + wave * R * ngr;  // this wave's rows' scale words, [R][ngr]
+  // the wave's R rows occupy bits [row0 * r, (row0 + R) * r) of every unit
+  const int ubit = row0 * r, uwi = ubit >> 5, uoff = ubit & 31;
+  const int wpu = o.pool.unit_bytes >> 2;
+  const uint32_t* units = (const uint32_t*)o.pool.slots;
+  const int32_t* u2s = o.pool.unit2slot;
+  // slots of this lane's first HPF hits and their refinement words for the wave's rows
+  int pslot[HPF];
+  uint32_t pw0[HPF], pw1[HPF];
+  if (refine) {
+#pragma unroll
+    for (int i = 0; i < HPF; ++i) {
+      const int j = lane + 64 * i;
+      pslot[i] = j < ks ? (o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1)) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < HPF; ++i) {
+      pw0[i] = pw1[i] = 0u;
+      if (pslot[i] >= 0) {
+        const uint32_t* u = units + (size_t)pslot[i] * wpu;
+        if (uwi < wpu) pw0[i] = u[uwi];
+        if (uwi + 1 < wpu) pw1[i] = u[uwi + 1];
+      }
+    }
+  }
+
+  float acc[NB][R];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = 0.f;
+  for (int c0 = 0; c0 < nchunks; c0 += 64 * D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int c = c0 + 64 * u + lane;
+      if (c < nchunks) {
+        if (refine && (c * C::CODES) % 128 == 0)
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[u][rr];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
+          float d[R];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
+#pragma unroll 2
+          for (int jb = 0; jb < C::PAIRS / 4; ++jb) {
+            const u32x4 xv = xp[jb];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q)), as_h2(xv[q]), d[rr], false);
+          }
+          const float X = xsum[bb * nchunks + c];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+            const float sv = sf_h2f(szw[u][rr]), zv = sf_h2f(szw[u][rr] >> 16);
+            acc[bb][rr] += (sv * scl) * (d[rr] - X) + zv * X;
+          }
+        }
+        const int cn = c + 64 * D;
+        if (cn < nchunks) load_chunk_clamped<C, R>(o, row0, cn, rowbytes, ngr, cw[u], szw[u]);
+      }
+    }
+  }
+  SF_TS(3);
+  // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
+  if (refine) {
+    // the rows' scale words were recorded by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = lane; j < ks; j += 64) {
+      const int i = (j - lane) >> 6;
+      int slot;
+      uint32_t w0, w1, w2 = 0u;
+      if (i < HPF) {
+        slot = pslot[0];
+        w0 = pw0[0];
+        w1 = pw1[0];
+#pragma unroll
+        for (int q = 1; q < HPF; ++q)
+          if (q == i) {
+            slot = pslot[q];
+            w0 = pw0[q];
+            w1 = pw1[q];
+          }
+        if (slot >= 0 && uoff + R * r > 64 && uwi + 2 < wpu) w2 = units[(size_t)slot * wpu + uwi + 2];
+      } else {
+        slot = o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1);
+        w0 = w1 = 0u;
+        if (slot >= 0) {
+          const uint32_t* u = units + (size_t)slot * wpu;
+          if (uwi < wpu) w0 = u[uwi];
+          if (uwi + 1 < wpu) w1 = u[uwi + 1];
+          if (uwi + 2 < wpu) w2 = u[uwi + 2];
+        }
+      }
+      if (slot < 0) continue;
+      const int k = l_sel[j];
+      const int c = k / C::CODES, kk = k - c * C::CODES;
+      int jj, hi;
+      C::locate(kk, &jj, &hi);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int p = uoff + rr * r;
+        const uint32_t clo = p + r <= 64 ? bits64(w0, w1, p, r) : bits64(w1, w2, p - 32, r);
+        const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
+          acc[bb][rr] = fmaf(hi ? (float)xh.y : (float)xh.x, sv, acc[bb][rr]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      float v = acc[bb][rr];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+      acc[bb][rr] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int row = row0 + rr;
+      if (row < o.n_out)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][rr];
+    }
+  }
+  // reports (once per call): the selection, each matrix's hits and lookup log
+  if (refine && a.report) {
+    if (tile_g == 0 && a.sel_out)
+      for (int j = tid; j < ks; j += 256) a.sel_out[j] = l_sel[j];
+    if (tile_g == o.tile_begin && (o.hit_out || o.pool.log_count)) {
+      if (tid == 0) {
+        int base = -1;
+        if (o.pool.log_count) {
+          const uint32_t bse = atomicAdd(o.pool.log_count, (uint32_t)ks);
+          base = (bse + (uint32_t)ks <= (uint32_t)o.pool.log_cap) ? (int)bse : -1;
+        }
+        lds[22] = base;
+      }
+      lds_barrier();
+      const int base = lds[22];
+      for (int j = tid; j < ks; j += 256) {
+        const int k = l_sel[j];
+        const int slot = o.pool.resident ? k : (u2s ? u2s[k] : -1);
+        if (o.hit_out) o.hit_out[j] = slot;
+        if (base >= 0) {
+          o.pool.log_units[base + j] = k;
+          o.pool.log_slots[base + j] = slot;
+        }
+      }
+    }
+  }
+  SF_TS(4);
+}
+
+size_t fused_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
+  size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
+  if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel;
+  return w * 4;
+}
+
 // ---- batched GEMV on MFMA (batch 3..16 per launch) --------------------------------
 // With several batch rows the GEMV is a real contraction.  v_mfma_f32_16x16x32_f16
 // takes A = x (row = batch row, fp16, exact) and B = codes expanded to fp16
@@ -793,7 +1264,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       s_cnt[wave][1] = c1;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (ks > 0) {
     h0 = (s_cnt[0][0] + s_cnt[1][0]) + (s_cnt[2][0] + s_cnt[3][0]);
     nh = (s_cnt[0][1] + s_cnt[1][1]) + (s_cnt[2][1] + s_cnt[3][1]) - h0;
@@ -851,7 +1322,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
 
   // refinements of the hit channels in the slice, 32 channels per MFMA
   if (ks > 0 && nh > 0) {
-    __syncthreads();  // hit lists staged
+    lds_barrier();  // hit lists staged
     const uint32_t* units = (const uint32_t*)o.pool.slots;
     const int wpu = o.pool.unit_bytes >> 2;
     const int r = a.r;
@@ -994,29 +1465,43 @@ sf_status launch_gemv(GemvArgs& a, hipStream_t s) {
   return SF_OK;
 }
 
+template <class C, int B, int R, int NB>
+sf_status launch_fused(GemvArgs& a, hipStream_t s) {
+  constexpr int D = R >= 8 ? 1 : (R >= 4 ? 2 : 4);
+  const size_t lds = fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);
+  SF_REQUIRE(lds <= MAX_DYN_LDS, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  if (a.k_in <= 256 * 8 * 2)
+    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 2>), dim3((unsigned)a.total_tiles), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 8>), dim3((unsigned)a.total_tiles), dim3(256), lds, s, a);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
 template <class C, int B, int R>
-sf_status dispatch_nb(GemvArgs& a, int nb, hipStream_t s) {
+sf_status dispatch_nb(GemvArgs& a, int nb, bool fused, hipStream_t s) {
+  if (fused) return nb == 2 ? launch_fused<C, B, R, 2>(a, s) : launch_fused<C, B, R, 1>(a, s);
   if (nb == 2) return launch_gemv<C, B, R, 2>(a, s);
   return launch_gemv<C, B, R, 1>(a, s);
 }
 
 template <class C, int B>
-sf_status dispatch_r(GemvArgs& a, int R, int nb, hipStream_t s) {
+sf_status dispatch_r(GemvArgs& a, int R, int nb, bool fused, hipStream_t s) {
   switch (R) {
-    case 1: return dispatch_nb<C, B, 1>(a, nb, s);
-    case 2: return dispatch_nb<C, B, 2>(a, nb, s);
-    case 4: return dispatch_nb<C, B, 4>(a, nb, s);
-    default: return dispatch_nb<C, B, 8>(a, nb, s);
+    case 1: return dispatch_nb<C, B, 1>(a, nb, fused, s);
+    case 2: return dispatch_nb<C, B, 2>(a, nb, fused, s);
+    case 4: return dispatch_nb<C, B, 4>(a, nb, fused, s);
+    default: return dispatch_nb<C, B, 8>(a, nb, fused, s);
   }
 }
 
-sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, hipStream_t s) {
+sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, bool fused, hipStream_t s) {
   switch (b) {
-    case 1: return dispatch_r<CodecPow2<1>, 1>(a, R, nb, s);
-    case 2: return dispatch_r<CodecPow2<2>, 2>(a, R, nb, s);
-    case 3: return dispatch_r<CodecStream<3>, 3>(a, R, nb, s);
-    case 4: return dispatch_r<CodecPow2<4>, 4>(a, R, nb, s);
-    case 8: return dispatch_r<CodecPow2<8>, 8>(a, R, nb, s);
+    case 1: return dispatch_r<CodecPow2<1>, 1>(a, R, nb, fused, s);
+    case 2: return dispatch_r<CodecPow2<2>, 2>(a, R, nb, fused, s);
+    case 3: return dispatch_r<CodecStream<3>, 3>(a, R, nb, fused, s);
+    case 4: return dispatch_r<CodecPow2<4>, 4>(a, R, nb, fused, s);
+    case 8: return dispatch_r<CodecPow2<8>, 8>(a, R, nb, fused, s);
     default:
       sf_set_error("sf_refined_gemv: resident width b must be 1, 2, 3, 4 or 8");
       return SF_EUNSUPPORTED;
@@ -1162,8 +1647,12 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   int rpw = env_int("SF_GEMV_ROWS_PER_WAVE", 0);
   int64_t rows_total = 0;
   for (int i = 0; i < n_ops; ++i) rows_total += ops[i].w.n_out;
-  if (rpw != 1 && rpw != 2 && rpw != 4 && rpw != 8)
-    rpw = rows_total <= 8192 ? 2 : (rows_total <= 16384 ? 4 : 8);
+  if (rpw != 1 && rpw != 2 && rpw != 4 && rpw != 8) {
+    if (env_int("SF_GEMV_FUSED", 1) != 0)  // one row tile per workgroup: about one per CU, 8 rows a wave at most
+      rpw = rows_total <= 8192 ? 4 : 8;
+    else
+      rpw = rows_total <= 8192 ? 2 : (rows_total <= 16384 ? 4 : 8);
+  }
   const MfmaPlan mp = plan_for(ops, n_ops, batch, k_sel);
   const bool mfma = mp.rt > 0;
   const int rows_wg = mfma ? 64 * mp.rt : 4 * rpw;
@@ -1206,7 +1695,17 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.r = f.r;
   a.total_tiles = tiles;
   hipStream_t s = (hipStream_t)stream;
-  if (k_sel > 0) {
+  const int cpc = codes_per_chunk(f.b);
+  // Batch 1-2 without the batched kernel: the fused kernel selects the channels in
+  // every workgroup (SF_GEMV_FUSED=0 selects the separate selection launch and the
+  // persistent kernel).  With more rows than one launch takes, the selection over
+  // all rows comes from the selection launch.
+  const bool fused = !mfma && env_int("SF_GEMV_FUSED", 1) != 0 &&
+                     fused_lds_bytes((int)K, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS;
+  const int max_nb = fused ? (fused_lds_bytes((int)K, cpc, 2, k_sel, rpw) <= 64 * 1024 ? 2 : 1)
+                           : (gemv_lds_bytes((int)K, cpc, 2, n_ops, k_sel, rpw, false) <= 64 * 1024 ? 2 : 1);
+  const bool one_launch = fused && batch <= max_nb;
+  if (k_sel > 0 && !one_launch) {
     hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(SEL_NT), 0, s, a);
     SF_LAUNCH_CHECK();
   }
@@ -1226,12 +1725,14 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     return SF_OK;
   }
   // two batch rows per launch when both fit the LDS staging of x, else one
-  const int cpc = codes_per_chunk(f.b);
-  const int max_nb = gemv_lds_bytes((int)K, cpc, 2, n_ops, k_sel, rpw, false) <= 64 * 1024 ? 2 : 1;
+  if (fused) {
+    a.report = one_launch ? 1 : 0;
+    if (!one_launch && k_sel > 0) a.sel_in = a.ws_sel;
+  }
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;
-    sf_status st = dispatch_b(a, f.b, rpw, nb, s);
+    sf_status st = dispatch_b(a, f.b, rpw, nb, fused, s);
     if (st != SF_OK) return st;
   }
   return SF_OK;

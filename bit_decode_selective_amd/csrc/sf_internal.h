@@ -55,6 +55,7 @@ struct PoolDev {
   int32_t* log_slots;        // slot seen by each logged lookup (-1 = miss)
   uint32_t* log_count;       // entries used this step
   int32_t log_cap;           // entries available
+  int32_t resident;          // every unit u is in slot u (unit2slot is the identity)
   int32_t unit_bytes;
   int64_t n_units;
 };
@@ -92,6 +93,14 @@ __device__ __forceinline__ int32_t sf_get(const int32_t* p) {
 __device__ __forceinline__ float sf_get(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Workgroup barrier that orders LDS accesses only: this thread's global loads stay
+// in flight (a plain __syncthreads() waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // All of this thread's memory operations have completed.
 __device__ __forceinline__ void sf_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -111,8 +120,9 @@ __device__ __forceinline__ bool sf_wait_word(uint32_t* p, uint32_t want, uint32_
 // (a separate build); SF_TS(i) records the wall clock of thread 0 of each
 // workgroup in slot i (0..15) of that workgroup's row of the probe buffer.
 #ifdef SF_PROBE
-// one copy of the buffer pointer per translation unit (no relocatable device code)
-static __device__ long long* sf_probe_buf = nullptr;
+// one copy of the buffer pointer per translation unit (no relocatable device code),
+// in constant memory: a scalar load, which does not wait for the vector loads in flight
+static __constant__ long long* sf_probe_buf = nullptr;
 void sf_probe_register(void (*install)(long long*));
 namespace {
 struct SfProbeInstaller {
