@@ -726,6 +726,20 @@ __device__ __forceinline__ uint32_t gt_eq_count(const uint32_t* kp, uint32_t T) 
   return gt | (eq << 16);
 }
 
+// Sum of c (0 <= c < 256) over the lanes below this one, by ballots of its bits;
+// *total = the sum over the wave.
+__device__ __forceinline__ uint32_t wave_excl_sum8(uint32_t c, uint32_t* total) {
+  uint32_t ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t m = __ballot((c >> b) & 1u);
+    ex += (uint32_t)lanes_below(m) << b;
+    tot += (uint32_t)__popcll(m) << b;
+  }
+  *total = tot;
+  return ex;
+}
+
 // Sum of c (0 <= c < 16) over the lanes below this one, by ballots of its bits;
 // *total = the sum over the wave.
 __device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t* total) {
@@ -760,8 +774,9 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
   __shared__ uint32_t s_cnt[4 * (MAX_SEL_K / 2048)];
   __shared__ int lds[24];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < 4 * 256; i += 256) (&whist[0][0])[i] = 0u;
-  for (int i = tid; i < 4 * 128; i += 256) (&whist2[0][0])[i] = 0u;
+  // each wave clears the histograms it counts into (its own, before its atomics)
+  for (int i = lane; i < 256; i += 64) whist[wave][i] = 0u;
+  for (int i = lane; i < 128; i += 64) whist2[wave][i] = 0u;
   const int K = a.k_in, nchunks = K / C::CODES, xpairs = K / 2, ngr = K / 128, n8 = K / 8;
   const int ks = a.k_sel;
   const bool refine = ks > 0;
@@ -770,6 +785,9 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
   uint32_t* keys = (uint32_t*)(xsum + NB * ((nchunks + 3) & ~3));  // [K/2]: channel-order key pairs
   uint32_t* s_szw = keys + (refine ? xpairs : 0);              // [4][R][ngr]
   int32_t* l_sel = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [ks]
+  uint32_t* bm_sure = (uint32_t*)(l_sel + (refine ? ks : 0));      // [K/32]: keys above the boundary bin
+  uint32_t* bm_bnd = bm_sure + (refine ? K / 32 : 0);               // [K/32]: keys in the boundary bin
+  const bool computed = refine && !a.sel_in && ks < K;             // the selection is computed here
   const int tile_g = blockIdx.x;
   const int op = op_of_tile(a, tile_g);
   const GemvOpDev& o = a.ops[op];
@@ -828,6 +846,12 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
         if (m < n8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
       }
       if (refine && m < n8) *(u32x4*)(keys + 4 * m) = kv;
+      if (computed && m < n8)  // selection pass 1: top 8 key bits, one histogram per wave
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
+          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
+        }
     }
   };
   stage(xv0, 0);
@@ -850,69 +874,84 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
     } else if (ks >= K) {
       for (int j = tid; j < ks; j += 256) l_sel[j] = j;
     } else {
-      lds_barrier();  // keys, zeroed histograms
-      // pass 1: top 8 key bits, one histogram per wave
-      for (int m = tid; m < n8; m += 256) {
-        const u32x4 kv = *(const u32x4*)(keys + 4 * m);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
-          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
-        }
-      }
-      lds_barrier();
-      // every wave finds the bin itself (no further barrier)
+      lds_barrier();  // keys and the pass-1 histograms
+      // every wave finds the boundary bin itself (no further barrier)
       int b1, above1;
       wave_threshold4(whist, 256, ks, &b1, &above1);
       SF_TS(5);
-      int need = ks - above1;
-      // pass 2: low 7 bits of the keys in bin b1
-      for (int m = tid; m < n8; m += 256) {
-        const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+      // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
+      // (all taken) and in bin b1 (decided by the low bits)
+      {
+        uint8_t* bs = (uint8_t*)bm_sure;
+        uint8_t* bb = (uint8_t*)bm_bnd;
+        for (int m = tid; m < n8; m += 256) {
+          const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+          uint32_t sure = 0u, bnd = 0u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = kv[q] & 0xFFFFu, hi = kv[q] >> 16;
-          if ((int)(lo >> 7) == b1) atomicAdd(&whist2[wave][lo & 127u], 1u);
-          if ((int)(hi >> 7) == b1) atomicAdd(&whist2[wave][hi & 127u], 1u);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const int bin = (int)(key >> 7);
+            sure |= (uint32_t)(bin > b1) << e;
+            if (bin == b1) {
+              bnd |= 1u << e;
+              atomicAdd(&whist2[wave][key & 127u], 1u);
+            }
+          }
+          bs[m] = (uint8_t)sure;
+          bb[m] = (uint8_t)bnd;
         }
       }
       lds_barrier();
       int b2, above2;
-      wave_threshold4(whist2, 128, need, &b2, &above2);
+      wave_threshold4(whist2, 128, ks - above1, &b2, &above2);
       SF_TS(8);
-      const uint32_t T = ((uint32_t)b1 << 7) | (uint32_t)b2;
-      need -= above2;  // keys equal to T that are taken, lowest channels first
-      // compaction in channel order: per (round, wave) counts of keys above T and
-      // equal to T, one barrier, then every thread places its taken channels at
-      // (#above before) + min(#equal before, need)
-      const int rounds = (n8 + 255) / 256;
-      for (int it = 0; it < rounds; ++it) {
-        const int m = tid + 256 * it;
-        const uint32_t cnt = m < n8 ? gt_eq_count(keys + 4 * m, T) : 0u;
-        uint32_t tg, te;
-        (void)wave_excl_small(cnt & 0xFFFFu, &tg);
-        (void)wave_excl_small(cnt >> 16, &te);
-        if (lane == 0) s_cnt[it * 4 + wave] = tg | (te << 16);
-      }
-      lds_barrier();
-      uint32_t base = 0;  // packed (#above | #equal << 16) before this round
-      for (int it = 0; it < rounds; ++it) {
-        const int m = tid + 256 * it;
-        const uint32_t cnt = m < n8 ? gt_eq_count(keys + 4 * m, T) : 0u;
-        uint32_t tg, te;
-        uint32_t before = base + wave_excl_small(cnt & 0xFFFFu, &tg) + (wave_excl_small(cnt >> 16, &te) << 16);
-        for (int w = 0; w < wave; ++w) before += s_cnt[it * 4 + w];
-        base += (s_cnt[it * 4] + s_cnt[it * 4 + 1]) + (s_cnt[it * 4 + 2] + s_cnt[it * 4 + 3]);
-        if (cnt) {
-          const u32x4 kv = *(const u32x4*)(keys + 4 * m);
-          uint32_t gtb = before & 0xFFFFu, eqb = before >> 16;
+      const uint32_t need = (uint32_t)(ks - above1 - above2);  // keys equal to T taken, lowest channels first
+      // compaction in channel order: thread t owns words [t W, t W + W) of the
+      // bitmaps; taken = above-bin | (boundary with low bits > b2) | the first
+      // `need` boundary keys with low bits == b2
+      const int nw = K / 32, W = (nw + 255) / 256;
+      const uint16_t* key16 = (const uint16_t*)keys;
+      uint32_t sg[4], eqm[4], cs = 0u, ce = 0u;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const bool gt = key > T, eq = key == T;
-            if (gt || (eq && eqb < (uint32_t)need)) l_sel[gtb + min(eqb, (uint32_t)need)] = 8 * m + e;
-            gtb += gt;
-            eqb += eq;
+      for (int i = 0; i < 4; ++i) {
+        sg[i] = eqm[i] = 0u;
+        const int w = tid * W + i;
+        if (i < W && w < nw) {
+          uint32_t bnd = bm_bnd[w], gtw = 0u, eqw = 0u;
+          while (bnd) {
+            const int bit = __builtin_ctz(bnd);
+            bnd &= bnd - 1u;
+            const uint32_t lo = key16[32 * w + bit] & 127u;
+            gtw |= (uint32_t)(lo > (uint32_t)b2) << bit;
+            eqw |= (uint32_t)(lo == (uint32_t)b2) << bit;
+          }
+          sg[i] = bm_sure[w] | gtw;
+          eqm[i] = eqw;
+          cs += __popc(sg[i]);
+          ce += __popc(eqm[i]);
+        }
+      }
+      uint32_t ts, te;
+      uint32_t sbefore = wave_excl_sum8(cs, &ts), ebefore = wave_excl_sum8(ce, &te);
+      if (lane == 0) s_cnt[wave] = ts | (te << 16);
+      lds_barrier();
+      for (int w = 0; w < wave; ++w) {
+        sbefore += s_cnt[w] & 0xFFFFu;
+        ebefore += s_cnt[w] >> 16;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t all = sg[i] | eqm[i];
+        while (all) {
+          const int bit = __builtin_ctz(all);
+          all &= all - 1u;
+          const int c = 32 * (tid * W + i) + bit;
+          if ((sg[i] >> bit) & 1u) {
+            l_sel[sbefore + min(ebefore, need)] = c;
+            ++sbefore;
+          } else {
+            if (ebefore < need) l_sel[sbefore + ebefore] = c;
+            ++ebefore;
           }
         }
       }
@@ -1089,7 +1128,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
 
 size_t fused_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
   size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
-  if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel;
+  if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel + (size_t)(k_in / 16);
   return w * 4;
 }
 
