@@ -51,6 +51,7 @@ constexpr int TPT = CB / SEL_T;  // tokens per select thread
 constexpr int PW = HD + 4;       // partial record: N[HD], max, sum, pad
 constexpr int NBIN = 2048;       // histogram bins (levels: key bits 30..20, 19..10, 9..0)
 constexpr int MAX_CHUNKS = 256;
+constexpr int PV_NR = 8;         // value-sum records per KV head (pv split s adds into record s % PV_NR)
 
 __host__ __device__ constexpr int pv_tokens(int b) { return b <= 4 ? 512 : 256; }
 
@@ -74,7 +75,7 @@ struct AttnArgs {
   float* logits;    // [batch*n_q][LT] (rows padded to 4 floats)
   float* part_a;    // [bh][nsa][G][PW]: split max / sum (+ value sums without refinement)
   float* part_c;    // [bh][s2][G][PW]: chunk sums (without refinement)
-  float* part_p;    // [bh][nsp][G][PW]: pv sums (with refinement)
+  float* part_p;    // [bh][PV_NR][G][PW]: value sums of the splits (with refinement)
   float* cmax;      // [bh][s2][G]: chunk max of the replaced logits
   float* mref;      // [bh][G]: max logit after replacement
   int32_t* sel_ws;  // [bh][KS]: selection
@@ -138,6 +139,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   if (a.k_sel > 0) {
     uint32_t* h = a.hist + (size_t)bh * 3 * NBIN;
     for (int i = split * 256 + tid; i < 3 * NBIN; i += a.nsa * 256) h[i] = 0;
+    float* pp = a.part_p + (size_t)bh * PV_NR * G * PW;  // the value-sum records of the KV head
+    for (int i = split * 256 + tid; i < PV_NR * G * PW; i += a.nsa * 256) pp[i] = 0.f;
     if (split == 0 && tid == 0) {
       for (int i = 0; i < 8; ++i)
         if (i != 5) a.ctl[bh * 8 + i] = 0;
@@ -778,7 +781,12 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 // step), scale words, final logits, the KV head's max, and the selection words that
 // locate this split's hits.  V codes are staged column-major ([code word][token],
 // padded), so a lane's B operand -- one dim of 8 consecutive tokens -- is two
-// 16-byte LDS reads.  The last workgroup of the KV head sums every split's record.
+// 16-byte LDS reads.  The split's hits (token, slot) are gathered into LDS while
+// the weights are formed, and each wave requests the refinement words of all its
+// hits at once.  All splits of a KV head use the same max, so their sums are added
+// into one fp32 record per head (atomically); the last split divides.
+constexpr int PV_HB = 8;  // hits per wave whose refinement words are in flight together
+
 template <int B, int G>
 __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   constexpr int SP = pv_tokens(B);
@@ -792,6 +800,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __shared__ uint32_t s_vsz[SP];
   __shared__ float s_w[G][SP];
   __shared__ float s_acc[4][G][HD];
+  __shared__ int s_hit[SP][2];
   __shared__ float s_red[4][3 * G + 1];
   __shared__ float s_st[3 * G + 1];
   __shared__ int s_rng[4][2];
@@ -829,6 +838,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h) mh[h] = a.mref[bh * G + h];
   // selected positions of this split's tokens: [#sel < t_begin, #sel < t_end)
   const int* sel = a.sel_ws + (size_t)bh * a.k_sel;
+  const int* slots = a.slot_ws + (size_t)bh * a.k_sel;
   int below0 = 0, below1 = 0;
   for (int j = tid; j < a.k_sel; j += 256) {
     const int t = sel[j];
@@ -863,7 +873,16 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __syncthreads();
   smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
   const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
-  const int hit_hi = (s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]);
+  const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
+  // this split's selected tokens and their slots (the selection ascends): loads now,
+  // LDS writes after the weights
+  int ht[TPW], hsl[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int j = tid + 256 * i;
+    ht[i] = j < nh ? sel[hit_lo + j] - t_begin : -1;
+    hsl[i] = j < nh ? slots[hit_lo + j] : -1;
+  }
   const float smax = smx * (float)(1u << a.r);
   int e2 = 0;
   if (smax > 0.f) (void)frexpf(smax, &e2);
@@ -887,7 +906,13 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
       acc3[3 * h + 2] += (float)hi + (float)lo;
     }
-  __syncthreads();  // s_u, s_vc, s_vsz, s_w written; s_red free
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+    if (tid + 256 * i < nh) {
+      s_hit[tid + 256 * i][0] = ht[i];
+      s_hit[tid + 256 * i][1] = hsl[i];
+    }
+  __syncthreads();  // s_u, s_vc, s_vsz, s_w, s_hit written; s_red free
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1)
 #pragma unroll
@@ -896,6 +921,29 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
   SF_TS(13);
+
+  // ---- hits: request the refinement words of this wave's hits (w, w+4, ..) ----
+  // lane l covers dims 2l, 2l+1: value refinement bits [HD r + 2 l r, HD r + 2 l r + 2 r)
+  const int r = a.r;
+  const int vbit = HD * r + 2 * lane * r, vwi = vbit >> 5, voff = vbit & 31;
+  const int wpu = a.pool.unit_bytes >> 2;
+  uint32_t hw0[PV_HB], hw1[PV_HB];
+  int htk[PV_HB];
+#pragma unroll
+  for (int i = 0; i < PV_HB; ++i) {
+    const int j = wave + 4 * i;
+    htk[i] = -1;
+    hw0[i] = hw1[i] = 0u;
+    if (j < nh) {
+      const int t = s_hit[j][0], slot = s_hit[j][1];
+      if (slot >= 0 && t >= 0 && t < n_here) {
+        const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
+        htk[i] = t;
+        hw0[i] = unit[vwi];
+        if (vwi + 1 < wpu) hw1[i] = unit[vwi + 1];
+      }
+    }
+  }
 
   // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
   const int n = lane & 15, qg = lane >> 4;
@@ -926,27 +974,37 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     }
   }
 
-  // ---- hits in this split: + w * s_V * cV_lo; wave w takes hits w, w+4, ..; lane: dims 2l, 2l+1 ----
+  // ---- hits in this split: + w * s_V * cV_lo; lane: dims 2l, 2l+1 ----
   float hacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) hacc[h][0] = hacc[h][1] = 0.f;
-  {
-    // the selection ascends, so this split's hits are positions [hit_lo, hit_hi)
-    const int* slots = a.slot_ws + (size_t)bh * a.k_sel;
-    const int r = a.r;
-    for (int j = hit_lo + wave; j < hit_hi; j += 4) {
-      const int t = sel[j] - t_begin;
-      const int slot = slots[j];
-      if (slot < 0 || t < 0 || t >= n_here) continue;
-      const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
-      const float sv = sf_h2f(s_vsz[t]);
-      const float c0 = sv * (float)field(unit, HD * r + 2 * lane * r, r);
-      const float c1 = sv * (float)field(unit, HD * r + (2 * lane + 1) * r, r);
+  const uint32_t rmask = (1u << r) - 1u;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
-        hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
-      }
+  for (int i = 0; i < PV_HB; ++i) {
+    const int t = htk[i];
+    if (t < 0) continue;
+    const uint64_t w64 = ((uint64_t)hw1[i] << 32) | hw0[i];
+    const float sv = sf_h2f(s_vsz[t]);
+    const float c0 = sv * (float)((uint32_t)(w64 >> voff) & rmask);
+    const float c1 = sv * (float)((uint32_t)(w64 >> (voff + r)) & rmask);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
+      hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
+    }
+  }
+  // hits beyond PV_HB per wave (many hits in one split)
+  for (int j = wave + 4 * PV_HB; j < nh; j += 4) {
+    const int t = s_hit[j][0], slot = s_hit[j][1];
+    if (slot < 0 || t < 0 || t >= n_here) continue;
+    const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
+    const float sv = sf_h2f(s_vsz[t]);
+    const float c0 = sv * (float)field(unit, vbit, r);
+    const float c1 = sv * (float)field(unit, vbit + r, r);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
+      hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
     }
   }
 #pragma unroll
@@ -957,7 +1015,10 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __syncthreads();  // s_red, s_acc
   if (tid < 3 * G) s_st[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
   __syncthreads();
-  float* PP = a.part_p + ((size_t)bh * a.nsp + split) * G * PW;
+  // this split's sums, added into one of the KV head's records [PV_NR][G][PW] (zeroed
+  // by the split launch; several records keep the number of adds per address small)
+  float* PB = a.part_p + (size_t)bh * PV_NR * G * PW;
+  float* PP = PB + (size_t)(split % PV_NR) * G * PW;
   const float back = ldexpf(1.f, B - shift);
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
@@ -968,11 +1029,13 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       if (h < G) {
         const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
         const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
-        sf_put(PP + h * PW + d, s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr);
+        (void)__hip_atomic_fetch_add(PP + h * PW + d, s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  if (tid < G) sf_put(PP + tid * PW + HD + 1, s_st[3 * tid]);
+  if (tid < G)
+    (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, s_st[3 * tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   SF_TS(14);
   sf_drain();
   __syncthreads();
@@ -981,26 +1044,20 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
              (uint32_t)(a.nsp - 1);
   __syncthreads();
   if (!s_flag) return;
-  // last workgroup of this KV head: out = sum N / sum z (one common max); every
-  // thread issues a batch of coherent loads before adding any of them
-  const float* PB = a.part_p + (size_t)bh * a.nsp * G * PW;
+  // last split of this KV head: out = N / z over the records
   for (int i = tid; i < G * HD; i += 256) {
     const int h = i / HD, d = i - h * HD;
+    float vn[PV_NR], vz[PV_NR];
+#pragma unroll
+    for (int k = 0; k < PV_NR; ++k) {
+      vn[k] = sf_get(PB + ((size_t)k * G + h) * PW + d);
+      vz[k] = sf_get(PB + ((size_t)k * G + h) * PW + HD + 1);
+    }
     float num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < a.nsp; s0 += 32) {
-      float vn[32], vd[32];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int sp = min(s0 + k, a.nsp - 1);
-        vn[k] = sf_get(PB + (sp * G + h) * PW + d);
-        vd[k] = sf_get(PB + (sp * G + h) * PW + HD + 1);
-      }
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        if (s0 + k < a.nsp) {
-          num += vn[k];
-          den += vd[k];
-        }
+    for (int k = 0; k < PV_NR; ++k) {
+      num += vn[k];
+      den += vz[k];
     }
     a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
   }
@@ -1017,7 +1074,7 @@ size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12
       (size_t)batch * n_q * LT * 4,  // logits
       bh * nsa * G * PW * 4,         // split partials
       bh * s2 * G * PW * 4,          // chunk partials
-      bh * nsp * G * PW * 4,         // pv partials
+      bh * PV_NR * G * PW * 4,       // value-sum records
       bh * s2 * G * 4,               // chunk max
       bh * G * 4,                    // max after replacement
       bh * KS * 4,                   // selection
