@@ -112,3 +112,10 @@ def test_full_size_32k():
     batch, n_kv, G, T = 1, 8, 4, 32768
     K, V, q, kv, qk, qv = _case(3, batch, n_kv, G, T)
     _check(q, kv, qk, qv, (batch, n_kv, T, 128), selection.k_select(2, T))
+
+
+def test_ragged_long_context():
+    """T = 40000: ten selection chunks, the last one ragged."""
+    batch, n_kv, G, T = 1, 1, 4, 40000
+    K, V, q, kv, qk, qv = _case(53, batch, n_kv, G, T)
+    _check(q, kv, qk, qv, (batch, n_kv, T, 128), selection.k_select(2, T))
