@@ -99,6 +99,12 @@ _PROTOS = {
     "sf_refine_cache_resident": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64)]),
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
+    "sf_embed": (I32, [VP, I64, I32, VP, I32, VP, VP]),
+    "sf_add_rmsnorm": (I32, [VP, VP, VP, I32, I32, C.c_float, VP, VP]),
+    "sf_qk_rope": (I32, [VP, VP, I32, I32, I32, VP, VP, C.c_float, I32, C.c_float, VP, VP, VP]),
+    "sf_swiglu": (I32, [VP, VP, I64, VP, VP]),
+    "sf_to_f16": (I32, [VP, I64, VP, VP]),
+    "sf_argmax": (I32, [VP, I32, I64, VP, VP]),
 }
 EXPORTS = tuple(_PROTOS)
 
@@ -450,3 +456,57 @@ def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stre
         )
     )
     return o, sel[:, :, :k_sel], hit[:, :, :k_sel]
+
+
+# ---- decode-step glue ------------------------------------------------------------------
+def embed(table_f16, ids, out=None, stream=None):
+    """table_f16 int16/fp16 [vocab][hidden] (device), ids int32 [batch] -> fp32 [batch][hidden]."""
+    torch = _torch()
+    vocab, hidden = table_f16.shape
+    ids = _dev_tensor(ids, torch.int32, table_f16.device)
+    out = out if out is not None else torch.empty((ids.numel(), hidden), dtype=torch.float32, device=table_f16.device)
+    check(lib().sf_embed(_ptr(table_f16), vocab, hidden, _ptr(ids), ids.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def add_rmsnorm(h, y, w, eps, out=None, stream=None):
+    """h fp32 [batch][hidden] (h += y in place if y is given); returns fp16 bits int16 [batch][hidden]."""
+    torch = _torch()
+    batch, hidden = h.shape
+    out = out if out is not None else torch.empty((batch, hidden), dtype=torch.int16, device=h.device)
+    check(lib().sf_add_rmsnorm(_ptr(h), _ptr(y), _ptr(w), batch, hidden, float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
+def qk_rope(q, k, n_q, n_kv, q_norm_w, k_norm_w, eps, pos, theta, stream=None):
+    """q fp32 [batch][n_q*128], k fp32 [batch][n_kv*128]; returns (q fp16 bits int16
+    [batch][n_q][128], rotated k fp32 [batch][n_kv][128])."""
+    torch = _torch()
+    batch = q.shape[0]
+    qh = torch.empty((batch, n_q, 128), dtype=torch.int16, device=q.device)
+    ko = torch.empty((batch, n_kv, 128), dtype=torch.float32, device=q.device)
+    check(lib().sf_qk_rope(_ptr(q), _ptr(k), batch, n_q, n_kv, _ptr(q_norm_w), _ptr(k_norm_w), float(eps), int(pos),
+                           float(theta), _ptr(qh), _ptr(ko), _stream(stream)))
+    return qh, ko
+
+
+def swiglu(gate, up, out=None, stream=None):
+    torch = _torch()
+    out = out if out is not None else torch.empty(gate.shape, dtype=torch.int16, device=gate.device)
+    check(lib().sf_swiglu(_ptr(gate), _ptr(up), gate.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def to_f16(x, out=None, stream=None):
+    torch = _torch()
+    out = out if out is not None else torch.empty(x.shape, dtype=torch.int16, device=x.device)
+    check(lib().sf_to_f16(_ptr(x), x.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def argmax(logits, out=None, stream=None):
+    torch = _torch()
+    batch, vocab = logits.shape
+    out = out if out is not None else torch.empty(batch, dtype=torch.int32, device=logits.device)
+    check(lib().sf_argmax(_ptr(logits), batch, vocab, _ptr(out), _stream(stream)))
+    return out

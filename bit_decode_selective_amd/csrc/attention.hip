@@ -568,10 +568,14 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   }
 
   int off = 0, cnt = 0;  // this chunk's range of selection positions
+  float mx_uns[G];       // max logit of this thread's unselected tokens
+#pragma unroll
+  for (int h = 0; h < G; ++h) mx_uns[h] = -INFINITY;
   if (a.sel_in == nullptr) {
     // ---- scores of this chunk's tokens (TPT consecutive per thread) ----
     uint32_t key[TPT];
     const int tb = c0 + TPT * tid;
+    float lgk[G][TPT];  // this thread's logits (for the max over the unselected tokens)
     {
       float sc[TPT] = {};
 #pragma unroll
@@ -586,7 +590,10 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
             if (tb + i < T) l4[i] = lr[i];
         }
 #pragma unroll
-        for (int i = 0; i < TPT; ++i) sc[i] += __expf(l4[i] - s_m[h]) * s_iz[h];
+        for (int i = 0; i < TPT; ++i) {
+          sc[i] += __expf(l4[i] - s_m[h]) * s_iz[h];
+          lgk[h][i] = l4[i];
+        }
       }
 #pragma unroll
       for (int i = 0; i < TPT; ++i) key[i] = __float_as_uint(sc[i]);
@@ -693,11 +700,34 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i)
       if (take[i] && pos < CB) s_tok[pos++] = tb + i;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+        if (!take[i]) mx_uns[h] = fmaxf(mx_uns[h], lgk[h][i]);  // invalid tokens hold -inf
   } else {
     // external selection: chunk c takes positions [c*ks/s2, (c+1)*ks/s2)
     off = (int)(((long long)chunk * ks) / s2);
     cnt = (int)(((long long)(chunk + 1) * ks) / s2) - off;
     for (int j = tid; j < cnt; j += SEL_T) s_tok[j] = a.sel_in[(size_t)bh * ks + off + j];
+    // the max over the tokens of this chunk that no chunk selected
+    uint32_t* selbits = lh;  // [CB / 32] (the histograms are unused on this path)
+    for (int i = tid; i < CB / 32; i += SEL_T) selbits[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < ks; j += SEL_T) {
+      const int t = a.sel_in[(size_t)bh * ks + j] - c0;
+      if (t >= 0 && t < CB) atomicOr(&selbits[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    const int tb = c0 + TPT * tid;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int t = tb + i;
+      if (t < T && !((selbits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u))
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          mx_uns[h] = fmaxf(mx_uns[h], a.logits[((size_t)bi * a.n_q + kvh * G + h) * a.LT + t]);
+    }
   }
   // (off, cnt) are only out of range after a timed-out wait
   off = min(max(off, 0), ks);
@@ -709,9 +739,10 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   //      l' = l + scale * s_K * (q . cK_lo); item m = (selected j, head m % G) ----
   const size_t unit0 = (size_t)bh * a.t_cap;
   const int base = a.pool.log_count ? (int)sf_get(a.ctl + 5) : -1;
+  // max after replacement: unselected tokens, selected misses (old logit), hits (new)
   float mloc[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
+  for (int h = 0; h < G; ++h) mloc[h] = mx_uns[h];
 #pragma nounroll
   for (int m = tid; m < cnt * G; m += SEL_T) {
     const int j = m / G, hh = m - j * G;
@@ -732,7 +763,12 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
         a.pool.log_slots[base + p] = slot;
       }
     }
-    if (slot < 0) continue;
+    if (slot < 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (h == hh && ok) mloc[h] = fmaxf(mloc[h], l);
+      continue;
+    }
     const float dot = kref_dot(a.pool.slots + (size_t)slot * a.pool.unit_bytes, a.r, qf[hh]);
     const float l2 = l + a.scale * (s * dot);
     *lp = l2;
@@ -750,7 +786,7 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     for (int h = 0; h < G; ++h) s_wm[wave][h][0] = mloc[h];
   __syncthreads();
   if (tid < G) {
-    float mm = s_m[tid];
+    float mm = -INFINITY;
     for (int w = 0; w < SEL_T / 64; ++w) mm = fmaxf(mm, s_wm[w][tid][0]);
     sf_put(a.cmax + ((size_t)bh * s2 + chunk) * G + tid, mm);
   }
@@ -852,26 +888,42 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_vc[(c + e) * CST + tk] = vc[i][e];
   }
-  // largest value scale of the split, and the hit range
-  float smx = 0.f;
+  // largest value scale of the split, the split's max logit per head, the hit range
+  float smx = 0.f, lmx[G];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     s_vsz[tl0 + i] = vsz[i];
     smx = fmaxf(smx, sf_h2f(vsz[i]));
   }
 #pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lmx[h] = lg[h][0];
+#pragma unroll
+    for (int i = 1; i < TPW; ++i) lmx[h] = fmaxf(lmx[h], lg[h][i]);
+  }
+#pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     smx = fmaxf(smx, __shfl_xor(smx, o, 64));
+#pragma unroll
+    for (int h = 0; h < G; ++h) lmx[h] = fmaxf(lmx[h], __shfl_xor(lmx[h], o, 64));
     below0 += __shfl_xor(below0, o, 64);
     below1 += __shfl_xor(below1, o, 64);
   }
   if (lane == 0) {
     s_red[wave][0] = smx;
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_red[wave][1 + h] = lmx[h];
     s_rng[wave][0] = below0;
     s_rng[wave][1] = below1;
   }
   __syncthreads();
   smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
+  // weights relative to the split's own max (full fp16 precision in the value sums);
+  // the sums are rescaled to the KV head's common max before they are added
+  float msp[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
   const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
   const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
   // this split's selected tokens and their slots (the selection ascends): loads now,
@@ -895,7 +947,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const float w = __expf(lg[h][i] - mh[h]);
+      const float w = __expf(lg[h][i] - msp[h]);
       s_w[h][tl0 + i] = w;
       const float u = w * sf_h2f(vsz[i]) * uscale;
       const _Float16 hi = (_Float16)u;
@@ -1017,6 +1069,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __syncthreads();
   // this split's sums, added into one of the KV head's records [PV_NR][G][PW] (zeroed
   // by the split launch; several records keep the number of adds per address small)
+  float fsc[G];  // e^(split max - common max)
+#pragma unroll
+  for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
   float* PB = a.part_p + (size_t)bh * PV_NR * G * PW;
   float* PP = PB + (size_t)(split % PV_NR) * G * PW;
   const float back = ldexpf(1.f, B - shift);
@@ -1029,13 +1084,14 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       if (h < G) {
         const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
         const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
-        (void)__hip_atomic_fetch_add(PP + h * PW + d, s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr,
+        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr),
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (tid < G)
-    (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, s_st[3 * tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, fsc[tid] * s_st[3 * tid], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
   SF_TS(14);
   sf_drain();
   __syncthreads();

@@ -1,0 +1,206 @@
+// Decode-step glue around the refined GEMV and attention: embedding gather,
+// residual add + RMSNorm, per-head q/k RMSNorm + rotary embedding, SwiGLU, fp16
+// casts and greedy argmax.
+//
+// The pages describe only the refined GEMV and attention; a decoder step around
+// them follows the public Llama-3.1 / Qwen3 layer definitions (RMSNorm, rotate-half
+// rotary embedding, SwiGLU feed-forward, fp32 residual stream, fp16 GEMV inputs).
+// These kernels move a few KB per call; each is one launch of small workgroups,
+// with reductions inside a workgroup only.
+#include <algorithm>
+
+#include "sf_internal.h"
+
+namespace {
+
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// h[b] = table[ids[b]] (fp16 -> fp32); an id outside [0, vocab) gives a zero row
+__global__ __launch_bounds__(256) void embed_kernel(const uint16_t* table, int64_t vocab, int hidden, const int32_t* ids,
+                                                    float* h) {
+  const int b = blockIdx.x;
+  const int id = ids[b];
+  const bool ok = id >= 0 && id < vocab;
+  const uint16_t* row = table + (ok ? (size_t)id : 0) * hidden;
+  for (int i = threadIdx.x; i < hidden; i += 256) h[(size_t)b * hidden + i] = ok ? sf_h2f(row[i]) : 0.f;
+}
+
+// h[b] += y[b] (if y); x[b] = fp16(h[b] / sqrt(mean(h[b]^2) + eps) * w)
+constexpr int NORM_T = 256;
+__global__ __launch_bounds__(NORM_T) void add_rmsnorm_kernel(float* h, const float* y, const float* w, int hidden,
+                                                             float eps, uint16_t* x) {
+  __shared__ float red[NORM_T / 64];
+  const int b = blockIdx.x;
+  float* hr = h + (size_t)b * hidden;
+  const float* yr = y ? y + (size_t)b * hidden : nullptr;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < hidden; i += NORM_T) {
+    float v = hr[i];
+    if (yr) {
+      v += yr[i];
+      hr[i] = v;
+    }
+    ss = fmaf(v, v, ss);
+  }
+  const float tot = block_sum<NORM_T>(ss, red);
+  const float rstd = 1.f / sqrtf(tot / (float)hidden + eps);
+  for (int i = threadIdx.x; i < hidden; i += NORM_T) x[(size_t)b * hidden + i] = f2h(hr[i] * rstd * w[i]);
+}
+
+// One wave per (batch, head) of 128 dims; lane i owns the rotate-half pair (i, i + 64).
+// Heads [0, n_q) are queries (written as fp16 to qh), the rest keys (written as
+// fp32 to ko).  Optional per-head RMSNorm first.  Angles are formed and rotated in fp64
+// (positions reach 2^17 radians and beyond).
+__global__ __launch_bounds__(64) void qk_rope_kernel(const float* q, const float* k, int n_q, int n_kv, const float* qw,
+                                                     const float* kw, float eps, int pos, double theta, uint16_t* qh,
+                                                     float* ko) {
+  const int b = blockIdx.y, head = blockIdx.x, i = threadIdx.x;
+  const bool isq = head < n_q;
+  const float* v = isq ? q + ((size_t)b * n_q + head) * 128 : k + ((size_t)b * n_kv + (head - n_q)) * 128;
+  const float* nw = isq ? qw : kw;
+  float x0 = v[i], x1 = v[i + 64];
+  if (nw) {
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float rstd = 1.f / sqrtf(ss / 128.f + eps);
+    x0 = x0 * rstd * nw[i];
+    x1 = x1 * rstd * nw[i + 64];
+  }
+  const double ang = (double)pos * pow(theta, -2.0 * (double)i / 128.0);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const float r0 = (float)((double)x0 * cs - (double)x1 * sn);
+  const float r1 = (float)((double)x1 * cs + (double)x0 * sn);
+  if (isq) {
+    uint16_t* o = qh + ((size_t)b * n_q + head) * 128;
+    o[i] = f2h(r0);
+    o[i + 64] = f2h(r1);
+  } else {
+    float* o = ko + ((size_t)b * n_kv + (head - n_q)) * 128;
+    o[i] = r0;
+    o[i + 64] = r1;
+  }
+}
+
+// act = fp16(silu(gate) * up)
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* g, const float* u, int64_t n, uint16_t* act) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float gv = g[i];
+    act[i] = f2h(gv / (1.f + expf(-gv)) * u[i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void to_f16_kernel(const float* x, int64_t n, uint16_t* out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = f2h(x[i]);
+}
+
+// ids[b] = argmax over logits[b] (lowest index among equal maxima; NaN never wins)
+constexpr int AMAX_T = 1024;
+__global__ __launch_bounds__(AMAX_T) void argmax_kernel(const float* logits, int64_t vocab, int32_t* ids) {
+  __shared__ float sv[AMAX_T / 64];
+  __shared__ int64_t si[AMAX_T / 64];
+  const int b = blockIdx.x;
+  const float* row = logits + (size_t)b * vocab;
+  float best = -INFINITY;
+  int64_t bi = -1;
+  for (int64_t i = threadIdx.x; i < vocab; i += AMAX_T) {
+    const float v = row[i];
+    if (v > best || (bi < 0 && v == best)) {  // strided ascending: the first of equals stays
+      best = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int64_t oi = __shfl_xor(bi, o, 64);
+    if (oi >= 0 && (bi < 0 || ov > best || (ov == best && oi < bi))) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < AMAX_T / 64; ++w)
+      if (si[w] >= 0 && (bi < 0 || sv[w] > best || (sv[w] == best && si[w] < bi))) {
+        best = sv[w];
+        bi = si[w];
+      }
+    ids[b] = (int32_t)(bi < 0 ? 0 : bi);
+  }
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 4096); }
+
+}  // namespace
+
+extern "C" sf_status sf_embed(const uint16_t* table_f16, int64_t vocab, int32_t hidden, const int32_t* ids,
+                              int32_t batch, float* h_out, sf_stream stream) {
+  SF_REQUIRE(table_f16 && ids && h_out, SF_EINVAL, "null argument");
+  SF_REQUIRE(vocab > 0 && hidden > 0 && batch > 0, SF_EINVAL, "bad sizes");
+  hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, (hipStream_t)stream, table_f16, vocab, hidden, ids, h_out);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_add_rmsnorm(float* h, const float* y, const float* w, int32_t batch, int32_t hidden, float eps,
+                                    uint16_t* x_f16, sf_stream stream) {
+  SF_REQUIRE(h && w && x_f16, SF_EINVAL, "null argument");
+  SF_REQUIRE(batch > 0 && hidden > 0 && eps >= 0.f, SF_EINVAL, "bad sizes");
+  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(batch), dim3(NORM_T), 0, (hipStream_t)stream, h, y, w, hidden, eps, x_f16);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_qk_rope(const float* q, const float* k, int32_t batch, int32_t n_q, int32_t n_kv,
+                                const float* q_norm_w, const float* k_norm_w, float eps, int32_t pos, float theta,
+                                uint16_t* q_f16, float* k_out, sf_stream stream) {
+  SF_REQUIRE(q && k && q_f16 && k_out, SF_EINVAL, "null argument");
+  SF_REQUIRE(batch > 0 && n_q > 0 && n_kv > 0 && pos >= 0 && theta > 1.f, SF_EINVAL, "bad sizes");
+  SF_REQUIRE((q_norm_w == nullptr) == (k_norm_w == nullptr), SF_EINVAL, "give both head-norm weights or neither");
+  hipLaunchKernelGGL(qk_rope_kernel, dim3(n_q + n_kv, batch), dim3(64), 0, (hipStream_t)stream, q, k, n_q, n_kv,
+                     q_norm_w, k_norm_w, eps, pos, (double)theta, q_f16, k_out);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_swiglu(const float* gate, const float* up, int64_t n, uint16_t* act_f16, sf_stream stream) {
+  SF_REQUIRE(gate && up && act_f16 && n > 0, SF_EINVAL, "bad arguments");
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, gate, up, n, act_f16);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_to_f16(const float* x, int64_t n, uint16_t* out_f16, sf_stream stream) {
+  SF_REQUIRE(x && out_f16 && n > 0, SF_EINVAL, "bad arguments");
+  hipLaunchKernelGGL(to_f16_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, x, n, out_f16);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_argmax(const float* logits, int32_t batch, int64_t vocab, int32_t* ids, sf_stream stream) {
+  SF_REQUIRE(logits && ids && batch > 0 && vocab > 0, SF_EINVAL, "bad arguments");
+  hipLaunchKernelGGL(argmax_kernel, dim3(batch), dim3(AMAX_T), 0, (hipStream_t)stream, logits, vocab, ids);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}

@@ -1,0 +1,332 @@
+"""One greedy decode step of a Llama-3.1- or Qwen3-shaped model through the C ABI.
+
+Host orchestration only: every operation of the step is a library call (embedding,
+residual add + RMSNorm, refined GEMVs, q/k head norm + rotary embedding, KV append,
+refined attention, SwiGLU, lm_head GEMV, argmax).  The argument tuples of a step are
+built once per position, so a step is a fixed sequence of launches on one stream
+(capturable as a HIP graph).  Every intermediate has its own buffer per layer, so a
+finished step can be inspected operation by operation.
+
+Weights are random (no trained checkpoints are available); their shapes are the
+public model shapes.  The KV cache before the first step is filled with synthetic
+keys and values (not by running the model on a prompt).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import binding, inputs
+
+
+@dataclass(frozen=True)
+class Spec:
+    name: str
+    layers: int
+    hidden: int
+    n_q: int
+    n_kv: int
+    ffn: int
+    vocab: int
+    qk_norm: bool
+    theta: float
+    eps: float
+    head_dim: int = 128
+
+
+LLAMA31_8B = Spec("llama-3.1-8b", 32, 4096, 32, 8, 14336, 128256, False, 500000.0, 1e-5)
+QWEN3_8B = Spec("qwen3-8b", 36, 4096, 32, 8, 12288, 151936, True, 1000000.0, 1e-6)
+
+
+def k_select(percent, n):
+    return (percent * n + 99) // 100
+
+
+class HostWeights:
+    """Seeded numpy weights (small models for the step tests)."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+
+    def matrix(self, layer, tensor, n_out, k_in):
+        return inputs.weight(self.cfg, layer, tensor, n_out, k_in)
+
+    def gain(self, layer, which, dim):
+        return inputs.norm_gain(self.cfg, layer, which, dim)
+
+    def embedding(self, vocab, hidden):
+        return inputs.weight(self.cfg, 0, inputs.EMBED, vocab, hidden, std=1.0).astype(np.float16)
+
+    def kv(self, layer, batch, n_kv, T, d):
+        return inputs.kv(self.cfg, layer, batch, n_kv, T, d)
+
+
+class DeviceWeights:
+    """The same distributions drawn on the device (full-size models)."""
+
+    def __init__(self, seed, device):
+        import torch
+
+        self.g = torch.Generator(device=device)
+        self.g.manual_seed(seed)
+        self.device = device
+
+    def matrix(self, layer, tensor, n_out, k_in):
+        return inputs.torch_weight(self.g, n_out, k_in, device=self.device)
+
+    def gain(self, layer, which, dim):
+        return inputs.norm_gain(int(self.g.initial_seed()), layer, which, dim)
+
+    def embedding(self, vocab, hidden):
+        import torch
+
+        return torch.randn((vocab, hidden), generator=self.g, device=self.device, dtype=torch.float32).half()
+
+    def kv(self, layer, batch, n_kv, T, d):
+        return inputs.torch_kv(self.g, batch, n_kv, T, d, device=self.device)
+
+
+# gain ids of the norms (``inputs.norm_gain`` keys)
+ATTN_NORM, FFN_NORM, Q_NORM, K_NORM, FINAL_NORM = range(5)
+
+
+class DecodeModel:
+    """Quantised weights, KV caches, refinement cache and per-layer buffers.
+
+    b, r       weight format; kv_b, kv_r the KV format
+    ch_pct     percent of input channels selected per GEMV (also the lm_head)
+    tok_pct    percent of tokens selected per (batch, kv head)
+    pool_frac  None: every refinement unit resident on the device (pools never
+               miss); else the device slots per pool as a fraction of its units,
+               filled from pinned host stores by the cache (LRU)
+    """
+
+    def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
+                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda"):
+        import torch
+
+        self.torch, self.spec, self.batch, self.t_cap = torch, spec, batch, t_cap
+        self.b, self.r, self.kv_b, self.kv_r = b, r, kv_b, kv_r
+        self.ch_pct, self.tok_pct = ch_pct, tok_pct
+        dev = torch.device(device)
+        self.dev = dev
+        S, H, d = spec, spec.hidden, spec.head_dim
+        self.host = {}  # fp32 weights kept for the oracle checks (HostWeights only)
+        keep_host = isinstance(src, HostWeights)
+        pools = []
+        stores = []
+
+        def quant(layer, tensor, n, k):
+            W = src.matrix(layer, tensor, n, k)
+            if keep_host:
+                self.host[(layer, tensor)] = W
+            qw = binding.QuantWeight.from_host(W, b, r) if keep_host else binding.QuantWeight.from_device(W, b, r)
+            return qw
+
+        def add_pool(unit_bytes_obj):
+            if pool_frac is None:
+                pools.append(unit_bytes_obj.resident_pool_desc())
+            else:
+                st = unit_bytes_obj.host_store()
+                stores.append(st)
+                cap = max(0, int(pool_frac * st.shape[0]))
+                pools.append(binding.host_pool_desc(st, cap))
+            return len(pools) - 1
+
+        self.layers = []
+        for li in range(S.layers):
+            L = {}
+            L["q"] = quant(li, inputs.Q_PROJ, S.n_q * d, H)
+            L["k"] = quant(li, inputs.K_PROJ, S.n_kv * d, H)
+            L["v"] = quant(li, inputs.V_PROJ, S.n_kv * d, H)
+            L["o"] = quant(li, inputs.O_PROJ, H, S.n_q * d)
+            L["gate"] = quant(li, inputs.GATE, S.ffn, H)
+            L["up"] = quant(li, inputs.UP, S.ffn, H)
+            L["down"] = quant(li, inputs.DOWN, H, S.ffn)
+            if r > 0:
+                for name in ("q", "k", "v", "o", "gate", "up", "down"):
+                    L["pool_" + name] = add_pool(L[name])
+            L["attn_norm"] = torch.as_tensor(src.gain(li, ATTN_NORM, H), device=dev)
+            L["ffn_norm"] = torch.as_tensor(src.gain(li, FFN_NORM, H), device=dev)
+            if S.qk_norm:
+                L["q_norm"] = torch.as_tensor(src.gain(li, Q_NORM, d), device=dev)
+                L["k_norm"] = torch.as_tensor(src.gain(li, K_NORM, d), device=dev)
+            L["index"] = li
+            kv = binding.QuantKV(batch, S.n_kv, t_cap, kv_b, kv_r, device=dev)
+            L["kv"] = kv
+            if kv_r > 0:
+                L["pool_kv"] = add_pool(kv)  # store taken before any token: refilled from the device copy below
+            self.layers.append(L)
+            torch.cuda.synchronize()
+        self.final_norm = torch.as_tensor(src.gain(S.layers, FINAL_NORM, H), device=dev)
+        emb = src.embedding(S.vocab, H)
+        if keep_host:
+            self.host["embed"] = emb
+        self.embed = binding._f16_bits(emb, dev)
+        self.lm_head = quant(S.layers, inputs.LM_HEAD, S.vocab, H)
+        self.pool_lm = add_pool(self.lm_head) if r > 0 else -1
+        self._pool_frac = pool_frac
+        self._pools, self._stores = pools, stores
+        self.cache = binding.RefineCache(pools, mode=cache_mode, device=dev, keep=stores) if pools else None
+        self.side = torch.cuda.Stream(device=dev)
+        self._alloc_buffers()
+        self.pos = 0
+
+    # ---- KV prefix -------------------------------------------------------------------
+    def fill_kv(self, T0, src):
+        """Synthetic keys/values for positions [0, T0) of every layer (not a prefill)."""
+        for li, L in enumerate(self.layers):
+            K, V = src.kv(li, self.batch, self.spec.n_kv, T0, self.spec.head_dim)
+            if isinstance(src, HostWeights):
+                self.host[("kv", li)] = (K, V)
+            L["kv"].append(K, V)
+            if self._pool_frac is not None and self.kv_r > 0:
+                # the host store holds the prefix's refinement units too (one store per pool)
+                st = self._stores[L["pool_kv"]]
+                st.copy_(L["kv"].refine.reshape(st.shape).to("cpu"))
+        self.pos = T0
+        self.torch.cuda.synchronize()
+
+    # ---- buffers -----------------------------------------------------------------------
+    def _alloc_buffers(self):
+        torch, S, B, d = self.torch, self.spec, self.batch, self.spec.head_dim
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        i16 = dict(dtype=torch.int16, device=self.dev)
+        self.h = torch.zeros((B, S.hidden), **f32)
+        self.ids = torch.zeros(B, dtype=torch.int32, device=self.dev)
+        self.next_ids = torch.zeros(B, dtype=torch.int32, device=self.dev)
+        self.buf = []
+        for _ in range(S.layers):
+            self.buf.append({
+                "x_attn": torch.empty((B, S.hidden), **i16),
+                "q": torch.empty((B, S.n_q * d), **f32),
+                "k": torch.empty((B, S.n_kv * d), **f32),
+                "k_rot": torch.empty((B, S.n_kv, d), **f32),
+                "v": torch.empty((B, S.n_kv * d), **f32),
+                "q16": torch.empty((B, S.n_q, d), **i16),
+                "attn": torch.empty((B, S.n_q, d), **f32),
+                "a16": torch.empty((B, S.n_q * d), **i16),
+                "o": torch.empty((B, S.hidden), **f32),
+                "x_ffn": torch.empty((B, S.hidden), **i16),
+                "gate": torch.empty((B, S.ffn), **f32),
+                "up": torch.empty((B, S.ffn), **f32),
+                "act": torch.empty((B, S.ffn), **i16),
+                "down": torch.empty((B, S.hidden), **f32),
+                "sel_attn": torch.empty(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32, device=self.dev),
+                "sel_o": torch.empty(max(1, k_select(self.ch_pct, S.n_q * d)), dtype=torch.int32, device=self.dev),
+                "sel_ffn": torch.empty(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32, device=self.dev),
+                "sel_down": torch.empty(max(1, k_select(self.ch_pct, S.ffn)), dtype=torch.int32, device=self.dev),
+                # [batch][n_kv][k_sel] for the step's k_sel, packed (room for k_sel up to t_cap)
+                "sel_tok": torch.empty(B * S.n_kv * max(1, self.t_cap), dtype=torch.int32, device=self.dev),
+                "hit_tok": torch.empty(B * S.n_kv * max(1, self.t_cap), dtype=torch.int32, device=self.dev),
+            })
+        self.x_final = torch.empty((B, S.hidden), **i16)
+        self.logits = torch.empty((B, S.vocab), **f32)
+        self.sel_lm = torch.empty(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32, device=self.dev)
+        self.hits = {}  # (layer index or -1, op name) -> hit tensor [k_sel] of each GEMV op
+
+    def workspace_bytes(self, T):
+        L = binding.lib()
+        S = self.spec
+        best = L.sf_workspace_bytes_attn(self.batch, S.n_q, S.n_kv, T, k_select(self.tok_pct, T))
+        for li in (0,):
+            for names, k_in in ((("q", "k", "v"), S.hidden), (("o",), S.n_q * S.head_dim), (("gate", "up"), S.hidden),
+                                (("down",), S.ffn)):
+                arr = (binding.sf_gemv_op * len(names))()
+                for i, n in enumerate(names):
+                    arr[i] = binding.sf_gemv_op(self.layers[li][n].desc(), -1, None, None)
+                best = max(best, L.sf_workspace_bytes_gemv(arr, len(names), self.batch, k_select(self.ch_pct, k_in)))
+        arr = (binding.sf_gemv_op * 1)(binding.sf_gemv_op(self.lm_head.desc(), -1, None, None))
+        return max(best, L.sf_workspace_bytes_gemv(arr, 1, self.batch, k_select(self.ch_pct, S.hidden)))
+
+    # ---- one step ------------------------------------------------------------------------
+    def build_step(self, pos, refined=True):
+        """Prebuilt (function, args) list of the step that reads position ``pos`` (the
+        new token's K/V land at ``pos``; attention covers ``pos + 1`` tokens)."""
+        torch, S, B, d = self.torch, self.spec, self.batch, self.spec.head_dim
+        if pos + 1 > self.t_cap:
+            raise ValueError("the KV cache is full")
+        Lb = binding.lib()
+        P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+        cache = self.cache.handle if self.cache is not None else None
+        ws = binding.workspace(self.workspace_bytes(pos + 1), self.dev)
+        self._ws = ws
+        keep = []
+        calls = []
+
+        def gemv(names, layer, x, ys, k_in, sel):
+            ks = k_select(self.ch_pct, k_in) if refined and self.r > 0 else 0
+            arr = (binding.sf_gemv_op * len(names))()
+            for i, (n, y) in enumerate(zip(names, ys)):
+                W = layer[n] if isinstance(n, str) else n
+                pool = (layer.get("pool_" + n, -1) if isinstance(n, str) else self.pool_lm) if cache is not None else -1
+                hit = torch.empty(max(1, ks), dtype=torch.int32, device=self.dev)
+                self.hits[(layer.get("index", -1), n if isinstance(n, str) else "lm_head")] = hit
+                keep.append(hit)
+                arr[i] = binding.sf_gemv_op(W.desc(), pool, y.data_ptr(), hit.data_ptr())
+            keep.append(arr)
+            calls.append((Lb.sf_refined_gemv, [arr, len(names), P(x), B, ks, None, P(sel), cache, ws.handle, None]))
+
+        calls.append((Lb.sf_embed, [P(self.embed), S.vocab, S.hidden, P(self.ids), B, P(self.h), None]))
+        for li, L in enumerate(self.layers):
+            bf = self.buf[li]
+            prev = self.buf[li - 1]["down"] if li > 0 else None
+            calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(prev), P(L["attn_norm"]), B, S.hidden, S.eps, P(bf["x_attn"]), None]))
+            gemv(("q", "k", "v"), L, bf["x_attn"], (bf["q"], bf["k"], bf["v"]), S.hidden, bf["sel_attn"])
+            calls.append((Lb.sf_qk_rope, [P(bf["q"]), P(bf["k"]), B, S.n_q, S.n_kv, P(L.get("q_norm")), P(L.get("k_norm")),
+                                          S.eps, pos, S.theta, P(bf["q16"]), P(bf["k_rot"]), None]))
+            kv = L["kv"]
+            dsc_app = kv.desc(pos)
+            # the new token's refinement units: into the device copy, or straight into the
+            # pinned host store the cache fills from (device-visible memory)
+            if self._pool_frac is not None and self.kv_r > 0:
+                dst = self._stores[L["pool_kv"]].data_ptr() + pos * kv.unit_bytes
+            else:
+                dst = kv.refine.data_ptr() + pos * kv.unit_bytes
+            keep.append(dsc_app)
+            calls.append((Lb.sf_kv_append, [P(bf["k_rot"]), P(bf["v"]), 1, pos, C.byref(dsc_app), C.c_void_p(dst), kv.t_cap,
+                                            None]))
+            dsc = kv.desc(pos + 1)
+            keep.append(dsc)
+            kt = k_select(self.tok_pct, pos + 1) if refined and self.kv_r > 0 else 0
+            pool_kv = L.get("pool_kv", -1) if cache is not None else -1
+            calls.append((Lb.sf_refined_attn_decode, [P(bf["q16"]), S.n_q, C.byref(dsc), 1.0 / math.sqrt(d), kt, None,
+                                                      cache, pool_kv, P(bf["attn"]), P(bf["sel_tok"]), P(bf["hit_tok"]),
+                                                      ws.handle, None]))
+            calls.append((Lb.sf_to_f16, [P(bf["attn"]), B * S.n_q * d, P(bf["a16"]), None]))
+            gemv(("o",), L, bf["a16"], (bf["o"],), S.n_q * d, bf["sel_o"])
+            calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(bf["o"]), P(L["ffn_norm"]), B, S.hidden, S.eps, P(bf["x_ffn"]), None]))
+            gemv(("gate", "up"), L, bf["x_ffn"], (bf["gate"], bf["up"]), S.hidden, bf["sel_ffn"])
+            calls.append((Lb.sf_swiglu, [P(bf["gate"]), P(bf["up"]), B * S.ffn, P(bf["act"]), None]))
+            gemv(("down",), L, bf["act"], (bf["down"],), S.ffn, bf["sel_down"])
+        calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(self.buf[-1]["down"]), P(self.final_norm), B, S.hidden, S.eps,
+                                          P(self.x_final), None]))
+        gemv((self.lm_head,), {}, self.x_final, (self.logits,), S.hidden, self.sel_lm)
+        calls.append((Lb.sf_argmax, [P(self.logits), B, S.vocab, P(self.next_ids), None]))
+        return calls, keep
+
+    def enqueue(self, calls, stream):
+        s = C.c_void_p(stream.cuda_stream)
+        for fn, args in calls:
+            a = list(args)
+            a[-1] = s
+            st = fn(*a)
+            if st != 0:
+                binding.check(st)
+
+    def step(self, ids, stream=None, refined=True):
+        """One decode step at the current position: ids int [batch] -> next ids (device)."""
+        torch = self.torch
+        stream = stream or torch.cuda.current_stream()
+        self.ids.copy_(torch.as_tensor(np.asarray(ids), dtype=torch.int32))
+        calls, keep = self.build_step(self.pos, refined)
+        self.enqueue(calls, stream)
+        if self.cache is not None:
+            binding.check(binding.lib().sf_refine_cache_fill(self.cache.handle, C.c_void_p(stream.cuda_stream),
+                                                             C.c_void_p(self.side.cuda_stream), None))
+        self._keep = keep
+        self.pos += 1
+        return self.next_ids

@@ -250,6 +250,44 @@ sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const
                                  int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                  sf_stream stream);
 
+/* ---- a14: decode-step glue ------------------------------------------------- */
+/* A decoder step around the refined GEMV and attention, after the public
+ * Llama-3.1 / Qwen3 layer definitions (the pages describe only the refined ops):
+ * fp32 residual stream, fp16 GEMV inputs, RMSNorm, per-head q/k RMSNorm (Qwen3),
+ * rotate-half rotary embedding, SwiGLU, greedy argmax.  All pointers are device
+ * memory owned by the caller; every call is one stream-ordered launch. */
+
+/* h_out[b][:] = table_f16[ids[b]][:] as fp32 ([batch][hidden]).  table [vocab][hidden].
+ * An id outside [0, vocab) gives a row of zeros. */
+sf_status sf_embed(const uint16_t* table_f16, int64_t vocab, int32_t hidden, const int32_t* ids,
+                   int32_t batch, float* h_out, sf_stream stream);
+
+/* Residual add and RMSNorm, per batch row of `hidden` values: if y is non-NULL,
+ * h += y (h updated in place); then x_f16 = fp16(h / sqrt(mean(h^2) + eps) * w),
+ * rounded to nearest even.  h, y [batch][hidden] fp32; w [hidden] fp32. */
+sf_status sf_add_rmsnorm(float* h, const float* y, const float* w, int32_t batch, int32_t hidden,
+                         float eps, uint16_t* x_f16, sf_stream stream);
+
+/* Query / key heads (head_dim 128) at position `pos`: q [batch][n_q][128] and
+ * k [batch][n_kv][128] fp32 (the GEMV outputs).  If q_norm_w / k_norm_w ([128] each,
+ * both or neither) are given, each head is first RMS-normalised (eps) and scaled.
+ * Then the rotary embedding: dims i and i+64 rotate by pos * theta^(-2i/128)
+ * (angles in fp64).  Writes the queries as fp16 to q_f16 [batch][n_q][128] and the
+ * keys as fp32 to k_out [batch][n_kv][128] (the input of sf_kv_append; may be k). */
+sf_status sf_qk_rope(const float* q, const float* k, int32_t batch, int32_t n_q, int32_t n_kv,
+                     const float* q_norm_w, const float* k_norm_w, float eps, int32_t pos,
+                     float theta, uint16_t* q_f16, float* k_out, sf_stream stream);
+
+/* act_f16[i] = fp16(silu(gate[i]) * up[i]), silu(x) = x / (1 + e^-x); n elements. */
+sf_status sf_swiglu(const float* gate, const float* up, int64_t n, uint16_t* act_f16, sf_stream stream);
+
+/* out_f16[i] = fp16(x[i]) (nearest even), n elements. */
+sf_status sf_to_f16(const float* x, int64_t n, uint16_t* out_f16, sf_stream stream);
+
+/* ids[b] = index of the largest logits[b][:] ([batch][vocab] fp32), the lowest index
+ * among equal maxima; NaN values are never chosen. */
+sf_status sf_argmax(const float* logits, int32_t batch, int64_t vocab, int32_t* ids, sf_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
