@@ -30,6 +30,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -343,6 +345,120 @@ def traffic_bytes():
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
 
 
+def decode_workload(args):
+    """Full greedy decode steps (embedding .. argmax) of a Qwen3-8B-shaped model at
+    context 8192 with pools holding 25% of every tensor's refinement units (LRU,
+    deterministic fills), or a Llama-3.1-8B-shaped model at context 131072 with
+    3+1-bit weights, 2+2-bit KV and pools of 10% (asynchronous fills).  Each step is
+    one graph replay at a fixed position with new token ids, then the cache fill."""
+    import torch
+
+    from bit_decode_selective_amd import binding, decode
+
+    if args.workload == "qwen3-8b-decode":
+        spec, T, (wb, wr), frac, mode = decode.QWEN3_8B, args.context or 8192, (2, 2), 0.25, binding.SF_CACHE_DETERMINISTIC
+    else:
+        spec, T, (wb, wr), frac, mode = decode.LLAMA31_8B, args.context or 131072, (3, 1), 0.10, binding.SF_CACHE_ASYNC
+    kvb, kvr, ch_pct, tok_pct = 2, 2, 3, 2
+    layers = args.layers if args.layers else spec.layers
+    spec = decode.Spec(spec.name, layers, spec.hidden, spec.n_q, spec.n_kv, spec.ffn, spec.vocab, spec.qk_norm,
+                       spec.theta, spec.eps)
+    t0 = time.time()
+    src = decode.DeviceWeights(4321, "cuda")
+    model = decode.DecodeModel(spec, args.batch, T + 1, src, b=wb, r=wr, kv_b=kvb, kv_r=kvr, ch_pct=ch_pct,
+                               tok_pct=tok_pct, pool_frac=frac, cache_mode=mode)
+    model.fill_kv(T, src)
+    print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    calls, keep = model.build_step(T)
+    stream = torch.cuda.Stream(device=model.dev)
+    rng = np.random.default_rng(99)
+
+    def fill():
+        binding.check(binding.lib().sf_refine_cache_fill(model.cache.handle, C.c_void_p(stream.cuda_stream),
+                                                         C.c_void_p(model.side.cuda_stream), None))
+
+    def new_ids():
+        model.ids.copy_(torch.as_tensor(rng.integers(0, spec.vocab, size=args.batch), dtype=torch.int32))
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        new_ids()
+        model.enqueue(calls, stream)
+        fill()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        model.enqueue(calls, stream)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            new_ids()
+            g.replay()
+            fill()
+        torch.cuda.synchronize()
+        st0 = model.cache.stats()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            new_ids()
+            g.replay()
+            fill()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    st1 = model.cache.stats()
+    # the same replays without the end-of-step fills (the kernels alone)
+    with torch.cuda.stream(stream):
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        e3.record(stream)
+    torch.cuda.synchronize()
+    ms_kernels = e2.elapsed_time(e3) / args.steps
+    d = {k: st1[k] - st0[k] for k in st1}
+    H, d_ = spec.hidden, spec.head_dim
+    kg = lambda n: k_select(ch_pct, n)
+    gb = 0
+    for shapes, k_in in (([spec.n_q * d_, spec.n_kv * d_, spec.n_kv * d_], H), ([H], spec.n_q * d_),
+                         ([spec.ffn, spec.ffn], H), ([H], spec.ffn)):
+        gb += gemv_bytes(shapes, k_in, kg(k_in), wb, wr, args.batch)
+    step_bytes = layers * (gb + attn_bytes(T + 1, k_select(tok_pct, T + 1), kvb, kvr, args.batch)
+                           + append_bytes(kvb, kvr, args.batch)) + gemv_bytes([spec.vocab], H, kg(H), wb, wr, args.batch)
+    secs = ms * 1e-3
+    res = {
+        "metric": "refined decode tokens/s, full decode step (glue, lm_head, argmax, cache fills)",
+        "value": args.batch / secs,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"fp16 x int{wb} -> fp32",
+        "data": "synthetic (random-init weights of the model shape, synthetic KV prefix, random token ids)",
+        "config": {
+            "workload": (f"{spec.name}-shape greedy decode, batch {args.batch}, context {T}, {layers} layers, "
+                         f"weights {wb}+{wr}-bit, KV {kvb}+{kvr}-bit, top {ch_pct}% channels / {tok_pct}% tokens, "
+                         f"pools {int(frac * 100)}% of each tensor's refinement units, "
+                         f"{'deterministic' if mode == binding.SF_CACHE_DETERMINISTIC else 'async'} fills"),
+            "batch": args.batch,
+            "context": T,
+            "layers": layers,
+            "hip_graph": True,
+        },
+        "hbm_gbps": step_bytes / secs / 1e9,
+        "hbm_frac": step_bytes / secs / 1e9 / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": step_bytes,
+        "ms_per_step_kernels_only": ms_kernels,
+        "refinement_hit_rate": d["hits"] / max(1, d["lookups"]),
+        "fill_pcie_gbps": d["h2d_bytes"] / (args.steps * secs) / 1e9,
+        "units_installed_per_step": d["installed"] / args.steps,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +470,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unrefined", action="store_true")
+    ap.add_argument("--workload", default="llama8b-step",
+                    choices=["llama8b-step", "qwen3-8b-decode", "llama8b-128k-decode"],
+                    help="llama8b-step (default): the refined GEMVs + attention of a Llama-3.1-8B-shaped step; "
+                         "the others run full decode steps with glue, lm_head and LRU refinement pools")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy kernel (256 MiB read + 256 MiB written) "
                          "whose HBM counters scale those of the other kernels")
@@ -365,6 +485,13 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.workload != "llama8b-step":
+        if args.layers == 32:
+            args.layers = 0  # the model's own depth
+        if args.context == 32768:
+            args.context = 0  # the workload's own context
+        decode_workload(args)
+        return
     if args.copy_calibration:
         src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
