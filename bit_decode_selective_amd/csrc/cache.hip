@@ -1,6 +1,5 @@
 // Refinement slot cache: device slots + unit->slot table per pool, host-side
-// replacement policy, fills from a host refinement store by one hipMemcpyAsync per
-// pool on a side stream.
+// replacement policy, fills from the pools' host refinement stores.
 //
 // Method: rag-lover.com StrataFlux summary, explainer dialogue (解説) -- fetched
 // precision is cached on the GPU and reused across decode steps, and delivery is
@@ -8,13 +7,20 @@
 // precision.  Paper abstract (arXiv 2611.08363): generation need not wait for
 // every transfer.
 //
-// Consistency: the unit->slot table is only changed by small kernels on the
+// A decode step touches every pool of the model (a few hundred for an 8B decoder:
+// seven weight matrices and one KV cache per layer), so one fill handles all of
+// them at once: one kernel copies every pool's lookup log into a pinned host
+// mirror, the policy runs on the host, and the installs of every pool travel in
+// one staging buffer -- one entry copy, one unmap kernel, one data copy, one
+// scatter kernel and one map kernel per fill, whatever the number of pools.
+//
+// Consistency: the unit->slot tables are only changed by small kernels on the
 // compute stream (stream-ordered with every lookup), never while a reader can
 // use the entry.  A fill first unmaps its victims on the compute stream, then the
 // side stream (after that point of the compute stream) copies the new units into
-// the freed slots, and only after that copy has completed is a map kernel enqueued
-// on the compute stream.  Deterministic mode enqueues the map right away behind a
-// stream wait; async mode enqueues it at the next fill call.
+// the freed slots, and only after that copy has completed is the map kernel
+// enqueued on the compute stream.  Deterministic mode enqueues the map right away
+// behind a stream wait; async mode enqueues it at the next fill call.
 #include <algorithm>
 #include <cstring>
 #include <map>
@@ -24,37 +30,47 @@
 
 namespace {
 
-struct FillHeader {  // device staging header of one fill
-  int32_t n_unmap, n_map, pad0, pad1;
+struct LogTab {  // where a pool's lookup log sits in the log block
+  int64_t off;   // byte offset of units[cap]; slots[cap] follow
+  int32_t cap;   // 0: the pool keeps no log (resident)
+  int32_t pad;
 };
+
+struct PoolTab {  // what the fill kernels need of a pool
+  int32_t* unit2slot;
+  uint8_t* slots;
+  int64_t unit_bytes;
+};
+
+struct UnmapEnt {
+  int32_t pool, unit;
+};
+
+struct MapEnt {
+  int32_t pool, unit, slot, pad;
+  int64_t data_off;  // from the start of the staging's data region (16-byte aligned)
+  int64_t pad2;
+};
+
+constexpr int64_t DATA_ALIGN = 16;
 
 struct HostPool {
   sf_pool_desc d{};
   bool resident = false;
-  // device
   int32_t* d_unit2slot = nullptr;
   uint8_t* d_slots = nullptr;  // owned unless resident
-  int32_t* d_log_units = nullptr;
-  int32_t* d_log_slots = nullptr;
-  uint32_t* d_log_count = nullptr;
+  int64_t log_off = 0;         // in the cache's log block
   int32_t log_cap = 0;
-  uint8_t* d_stage = nullptr;  // [header | unmap ids | map (unit, slot) | unit bytes]
-  // host
-  uint8_t* h_stage = nullptr;  // pinned, same layout
-  size_t stage_bytes = 0;
-  int64_t stage_units = 0;
+  int64_t stage_units = 0;     // most units one fill installs
   std::vector<int64_t> slot_unit;  // -1 free
   std::vector<int64_t> slot_last;
   std::vector<int32_t> unit_slot;  // host view (includes units whose copy is in flight)
   std::vector<int32_t> free_slots; // kept sorted descending: back() is the lowest
-  std::map<int64_t, std::vector<int64_t>> buckets;  // last-use step -> units (lazy)
+  std::map<int64_t, std::vector<int64_t>> buckets;  // last-use step -> units (lazy, may hold stale ids)
   std::map<int64_t, size_t> bucket_pos;             // consumed prefix of a sorted bucket
+  int64_t bucket_entries = 0;                       // ids held by all buckets
   std::vector<int64_t> pending;
   std::vector<uint8_t> pending_flag;  // per unit
-  std::vector<int32_t> log_u, log_s;
-  hipEvent_t copy_done = nullptr;
-  bool in_flight = false;  // a copy whose map has not been enqueued
-  int32_t flight_maps = 0;
   // stats
   int64_t n_lookups = 0, n_hits = 0, n_installed = 0, h2d_bytes = 0;
 };
@@ -67,8 +83,24 @@ struct sf_refine_cache {
   int64_t max_fill = 0;
   int64_t step = 0;
   int device = 0;
+  bool any_cached = false;  // some pool is not resident
   hipEvent_t ev_compute = nullptr;
-  uint32_t* h_counts = nullptr;  // pinned [n_pools]
+  hipEvent_t copy_done = nullptr;
+  // lookup logs: [u32 count per pool, 256-aligned][per pool: units[cap] | slots[cap]],
+  // on the device and mirrored in pinned host memory at the same offsets
+  uint8_t* d_logs = nullptr;
+  uint8_t* h_logs = nullptr;
+  uint8_t* h_logs_dev = nullptr;  // the mirror's device address
+  size_t logs_bytes = 0;
+  LogTab* d_logtab = nullptr;
+  PoolTab* d_pooltab = nullptr;
+  // staging of one fill, device and pinned host: [unmaps | maps | unit bytes]
+  uint8_t* d_stage = nullptr;
+  uint8_t* h_stage = nullptr;
+  size_t stage_bytes = 0;
+  int64_t map_off = 0, data_off = 0;
+  bool in_flight = false;  // a copy whose map has not been enqueued
+  int32_t flight_maps = 0;
 };
 
 namespace {
@@ -84,37 +116,61 @@ __global__ void fill_kernel(int32_t* p, int64_t n, int32_t v) {
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
-__global__ void unmap_kernel(int32_t* unit2slot, const uint8_t* stage) {
-  const FillHeader* h = (const FillHeader*)stage;
-  const int32_t* ids = (const int32_t*)(stage + 16);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < h->n_unmap; i += gridDim.x * blockDim.x)
-    unit2slot[ids[i]] = -1;
+// One workgroup per pool: copies the step's count and the logged entries into the
+// pinned host mirror and clears the device count for the next step.
+__global__ __launch_bounds__(256) void logs_to_host_kernel(uint8_t* d_logs, uint8_t* h_logs, const LogTab* tab) {
+  __shared__ uint32_t s_cnt;
+  const int i = blockIdx.x;
+  uint32_t* dc = (uint32_t*)d_logs;
+  if (threadIdx.x == 0) {
+    const uint32_t c = dc[i];
+    s_cnt = c;
+    ((uint32_t*)h_logs)[i] = c;
+    dc[i] = 0;
+  }
+  __syncthreads();
+  const LogTab t = tab[i];
+  const uint32_t n = min(s_cnt, (uint32_t)t.cap);
+  const int32_t* src = (const int32_t*)(d_logs + t.off);
+  int32_t* dst = (int32_t*)(h_logs + t.off);
+  for (uint32_t j = threadIdx.x; j < n; j += 256) {
+    dst[j] = src[j];
+    dst[t.cap + j] = src[t.cap + j];
+  }
 }
 
-__global__ void map_kernel(int32_t* unit2slot, const uint8_t* stage, int64_t map_off) {
-  const FillHeader* h = (const FillHeader*)stage;
-  const int32_t* pairs = (const int32_t*)(stage + map_off);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < h->n_map; i += gridDim.x * blockDim.x)
-    unit2slot[pairs[2 * i]] = pairs[2 * i + 1];
+__global__ void unmap_kernel(const PoolTab* tab, const UnmapEnt* ents, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const UnmapEnt e = ents[i];
+    tab[e.pool].unit2slot[e.unit] = -1;
+  }
 }
 
-// Copies unit bytes from the device staging into their slots (4-byte words).
-__global__ void scatter_kernel(uint8_t* slots, const uint8_t* stage, int64_t map_off,
-                               int64_t data_off, int64_t unit_bytes) {
-  const FillHeader* h = (const FillHeader*)stage;
-  const int32_t* pairs = (const int32_t*)(stage + map_off);
-  const int64_t wpu = unit_bytes / 4;
-  const int64_t total = (int64_t)h->n_map * wpu;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / wpu, w = i - m * wpu;
-    const int32_t slot = pairs[2 * m + 1];
-    ((uint32_t*)(slots + (int64_t)slot * unit_bytes))[w] =
-        ((const uint32_t*)(stage + data_off + m * unit_bytes))[w];
+__global__ void map_kernel(const PoolTab* tab, const MapEnt* ents, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const MapEnt e = ents[i];
+    tab[e.pool].unit2slot[e.unit] = e.slot;
+  }
+}
+
+// One workgroup per staged unit (grid-stride): copies its bytes into its slot,
+// 16 bytes per thread where the unit size allows.
+__global__ __launch_bounds__(256) void scatter_kernel(const PoolTab* tab, const MapEnt* ents, int n,
+                                                      const uint8_t* data) {
+  for (int e = blockIdx.x; e < n; e += gridDim.x) {
+    const MapEnt m = ents[e];
+    const PoolTab p = tab[m.pool];
+    const uint8_t* src = data + m.data_off;
+    uint8_t* dst = p.slots + (int64_t)m.slot * p.unit_bytes;
+    if ((p.unit_bytes & 15) == 0) {
+      for (int64_t w = threadIdx.x; w < p.unit_bytes / 16; w += 256) ((uint4*)dst)[w] = ((const uint4*)src)[w];
+    } else {
+      for (int64_t w = threadIdx.x; w < p.unit_bytes / 4; w += 256)
+        ((uint32_t*)dst)[w] = ((const uint32_t*)src)[w];
+    }
   }
 }
 
@@ -142,22 +198,22 @@ __global__ __launch_bounds__(1024) void lookup_kernel(PoolDev p, int64_t n_units
   }
 }
 
-size_t stage_layout(int64_t units, int64_t unit_bytes, int64_t* map_off, int64_t* data_off) {
-  *map_off = sf_align256(16 + (size_t)units * 4);
-  *data_off = sf_align256((size_t)*map_off + (size_t)units * 8);
-  return sf_align256((size_t)*data_off + (size_t)units * unit_bytes);
-}
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-void destroy_pool(HostPool& p) {
-  if (p.d_unit2slot) hipFree(p.d_unit2slot);
-  if (p.d_slots && !p.resident) hipFree(p.d_slots);
-  if (p.d_log_units) hipFree(p.d_log_units);
-  if (p.d_log_slots) hipFree(p.d_log_slots);
-  if (p.d_log_count) hipFree(p.d_log_count);
-  if (p.d_stage) hipFree(p.d_stage);
-  if (p.h_stage) hipHostFree(p.h_stage);
-  if (p.copy_done) hipEventDestroy(p.copy_done);
-  p = HostPool();
+void destroy_cache(sf_refine_cache* c) {
+  for (auto& p : c->pools) {
+    if (p.d_unit2slot) hipFree(p.d_unit2slot);
+    if (p.d_slots && !p.resident) hipFree(p.d_slots);
+  }
+  if (c->d_logs) hipFree(c->d_logs);
+  if (c->h_logs) hipHostFree(c->h_logs);
+  if (c->d_logtab) hipFree(c->d_logtab);
+  if (c->d_pooltab) hipFree(c->d_pooltab);
+  if (c->d_stage) hipFree(c->d_stage);
+  if (c->h_stage) hipHostFree(c->h_stage);
+  if (c->ev_compute) hipEventDestroy(c->ev_compute);
+  if (c->copy_done) hipEventDestroy(c->copy_done);
+  delete c;
 }
 
 // Smallest (last use, unit id) resident unit with last use < step, or -1.
@@ -176,25 +232,39 @@ int64_t pick_victim(HostPool& p, int64_t step) {
       const int32_t s = p.unit_slot[u];
       if (s >= 0 && p.slot_last[s] == it->first) return u;
     }
+    p.bucket_entries -= (int64_t)v.size();
     p.bucket_pos.erase(it->first);
     p.buckets.erase(it);
   }
   return -1;
 }
 
-sf_status publish(sf_refine_cache* c, HostPool& p, hipStream_t compute) {
-  if (!p.in_flight) return SF_OK;
-  int64_t map_off, data_off;
-  stage_layout(p.stage_units, p.d.unit_bytes, &map_off, &data_off);
-  SF_HIP(hipStreamWaitEvent(compute, p.copy_done, 0));
-  if (p.flight_maps > 0) {
-    hipLaunchKernelGGL(map_kernel, dim3((p.flight_maps + 255) / 256), dim3(256), 0, compute,
-                       p.d_unit2slot, (const uint8_t*)p.d_stage, map_off);
+// Buckets keep one id per use, most of them stale once the unit is used again;
+// past a few times the slot count they are rebuilt from the slots (one id each).
+// The victim order (last use, unit id) does not change.
+void compact_buckets(HostPool& p) {
+  if (p.bucket_entries <= 4 * ((int64_t)p.slot_unit.size() + 1024)) return;
+  p.buckets.clear();
+  p.bucket_pos.clear();
+  int64_t n = 0;
+  for (size_t s = 0; s < p.slot_unit.size(); ++s)
+    if (p.slot_unit[s] >= 0) {
+      p.buckets[p.slot_last[s]].push_back(p.slot_unit[s]);
+      ++n;
+    }
+  p.bucket_entries = n;
+}
+
+sf_status publish(sf_refine_cache* c, hipStream_t compute) {
+  if (!c->in_flight) return SF_OK;
+  SF_HIP(hipStreamWaitEvent(compute, c->copy_done, 0));
+  if (c->flight_maps > 0) {
+    hipLaunchKernelGGL(map_kernel, dim3((c->flight_maps + 255) / 256), dim3(256), 0, compute, c->d_pooltab,
+                       (const MapEnt*)(c->d_stage + c->map_off), c->flight_maps);
     SF_LAUNCH_CHECK();
   }
-  p.in_flight = false;
-  p.flight_maps = 0;
-  (void)c;
+  c->in_flight = false;
+  c->flight_maps = 0;
   return SF_OK;
 }
 
@@ -208,11 +278,11 @@ sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out) {
   out->unit2slot = p.d_unit2slot;
   out->slots = p.d_slots;
   if (!p.resident) {  // a resident pool never misses: nothing to record
-    out->log_units = p.d_log_units;
-    out->log_slots = p.d_log_slots;
-    out->log_count = p.d_log_count;
+    out->log_units = (int32_t*)(c->d_logs + p.log_off);
+    out->log_slots = out->log_units + p.log_cap;
+    out->log_count = (uint32_t*)c->d_logs + pool;
+    out->log_cap = p.log_cap;
   }
-  out->log_cap = p.log_cap;
   out->resident = p.resident ? 1 : 0;
   out->unit_bytes = (int32_t)p.d.unit_bytes;
   out->n_units = p.d.n_units;
@@ -242,46 +312,57 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
   c->max_fill = max_fill;
   hipGetDevice(&c->device);
   c->pools.resize(n_pools);
-  auto fail = [&](sf_status st) {
-    for (auto& p : c->pools) destroy_pool(p);
-    if (c->ev_compute) hipEventDestroy(c->ev_compute);
-    if (c->h_counts) hipHostFree(c->h_counts);
-    delete c;
-    return st;
-  };
 #define CK(call)                                                                  \
   do {                                                                            \
     hipError_t e_ = (call);                                                       \
     if (e_ != hipSuccess) {                                                       \
       sf_set_error(std::string("sf_refine_cache_create: " #call ": ") + hipGetErrorString(e_)); \
-      return fail(e_ == hipErrorOutOfMemory ? SF_ENOMEM : SF_EHIP);               \
+      destroy_cache(c);                                                           \
+      return e_ == hipErrorOutOfMemory ? SF_ENOMEM : SF_EHIP;                     \
     }                                                                             \
   } while (0)
-  CK(hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming));
-  CK(hipHostMalloc((void**)&c->h_counts, sizeof(uint32_t) * n_pools, hipHostMallocDefault));
+  // layouts of the log block and of the staging
+  int64_t log_bytes = (int64_t)sf_align256(4 * (size_t)n_pools);
+  int64_t stage_ents = 0, stage_data = 0;
   for (int i = 0; i < n_pools; ++i) {
     HostPool& p = c->pools[i];
     p.d = pools[i];
     p.resident = pools[i].device_store != nullptr;
-    const int64_t nu = p.d.n_units, cap = p.d.capacity;
+    if (p.resident) continue;
+    c->any_cached = true;
     p.log_cap = p.d.max_lookup > 0 ? p.d.max_lookup : 65536;
+    p.log_off = log_bytes;
+    log_bytes += (int64_t)sf_align256(8 * (size_t)p.log_cap);
+    p.stage_units = std::min<int64_t>(p.d.capacity, max_fill > 0 ? max_fill : p.d.capacity);
+    stage_ents += p.stage_units;
+    stage_data += p.stage_units * align_up(p.d.unit_bytes, DATA_ALIGN);
+  }
+  c->logs_bytes = (size_t)log_bytes;
+  c->map_off = (int64_t)sf_align256((size_t)stage_ents * sizeof(UnmapEnt));
+  c->data_off = (int64_t)sf_align256((size_t)c->map_off + (size_t)stage_ents * sizeof(MapEnt));
+  c->stage_bytes = (size_t)c->data_off + (size_t)stage_data;
+  CK(hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming));
+  CK(hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming));
+  CK(hipMalloc((void**)&c->d_logs, c->logs_bytes));
+  CK(hipHostMalloc((void**)&c->h_logs, c->logs_bytes, hipHostMallocDefault));
+  CK(hipHostGetDevicePointer((void**)&c->h_logs_dev, c->h_logs, 0));
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, 0, (uint32_t*)c->d_logs, n_pools);
+  if (stage_ents > 0) {
+    CK(hipMalloc((void**)&c->d_stage, c->stage_bytes));
+    CK(hipHostMalloc((void**)&c->h_stage, c->stage_bytes, hipHostMallocDefault));
+  }
+  std::vector<LogTab> logtab(n_pools);
+  std::vector<PoolTab> pooltab(n_pools);
+  for (int i = 0; i < n_pools; ++i) {
+    HostPool& p = c->pools[i];
+    const int64_t nu = p.d.n_units, cap = p.d.capacity;
     CK(hipMalloc((void**)&p.d_unit2slot, sizeof(int32_t) * nu));
-    CK(hipMalloc((void**)&p.d_log_units, sizeof(int32_t) * p.log_cap));
-    CK(hipMalloc((void**)&p.d_log_slots, sizeof(int32_t) * p.log_cap));
-    CK(hipMalloc((void**)&p.d_log_count, 256));
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, 0, p.d_log_count, 64);
     p.unit_slot.assign(nu, -1);
     p.pending_flag.assign(nu, 0);
     if (p.resident) {
       p.d_slots = p.d.device_store;
       hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, 0, p.d_unit2slot, nu);
       for (int64_t u = 0; u < nu; ++u) p.unit_slot[u] = (int32_t)u;
-      p.slot_unit.resize(nu);
-      for (int64_t u = 0; u < nu; ++u) p.slot_unit[u] = u;
-      p.slot_last.assign(nu, -1);
-      std::vector<int64_t>& b = p.buckets[-1];
-      b.resize(nu);
-      for (int64_t u = 0; u < nu; ++u) b[u] = u;
     } else {
       hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, 0, p.d_unit2slot, nu, -1);
       if (cap > 0) CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
@@ -289,16 +370,14 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
       p.slot_last.assign(cap, -1);
       p.free_slots.resize(cap);
       for (int64_t s = 0; s < cap; ++s) p.free_slots[s] = (int32_t)(cap - 1 - s);
-      p.stage_units = std::min<int64_t>(cap, max_fill > 0 ? max_fill : cap);
-      if (p.stage_units > 0) {
-        int64_t mo, dof;
-        p.stage_bytes = stage_layout(p.stage_units, p.d.unit_bytes, &mo, &dof);
-        CK(hipMalloc((void**)&p.d_stage, p.stage_bytes));
-        CK(hipHostMalloc((void**)&p.h_stage, p.stage_bytes, hipHostMallocDefault));
-      }
-      CK(hipEventCreateWithFlags(&p.copy_done, hipEventDisableTiming));
     }
+    logtab[i] = LogTab{p.log_off, p.log_cap, 0};
+    pooltab[i] = PoolTab{p.d_unit2slot, p.d_slots, p.d.unit_bytes};
   }
+  CK(hipMalloc((void**)&c->d_logtab, sizeof(LogTab) * n_pools));
+  CK(hipMalloc((void**)&c->d_pooltab, sizeof(PoolTab) * n_pools));
+  CK(hipMemcpy(c->d_logtab, logtab.data(), sizeof(LogTab) * n_pools, hipMemcpyHostToDevice));
+  CK(hipMemcpy(c->d_pooltab, pooltab.data(), sizeof(PoolTab) * n_pools, hipMemcpyHostToDevice));
   CK(hipGetLastError());
   CK(hipDeviceSynchronize());
 #undef CK
@@ -309,10 +388,7 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
 extern "C" sf_status sf_refine_cache_destroy(sf_refine_cache* c) {
   if (!c) return SF_OK;
   hipDeviceSynchronize();
-  for (auto& p : c->pools) destroy_pool(p);
-  if (c->ev_compute) hipEventDestroy(c->ev_compute);
-  if (c->h_counts) hipHostFree(c->h_counts);
-  delete c;
+  destroy_cache(c);
   return SF_OK;
 }
 
@@ -336,79 +412,66 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
   SF_REQUIRE(c, SF_EINVAL, "null cache");
   hipStream_t compute = (hipStream_t)compute_, side = (hipStream_t)side_;
   const int64_t t = c->step;
-  bool any = false;
-  for (const auto& p : c->pools) any = any || !p.resident;
-  if (!any) {  // only resident pools: nothing is ever missing
+  if (!c->any_cached) {  // only resident pools: nothing is ever missing
     c->step = t + 1;
     if (n_filled) *n_filled = 0;
     return SF_OK;
   }
   const int np = (int)c->pools.size();
-  int64_t filled = 0;
-  bool overflow = false;
-  // 1. read the step's lookup logs
-  for (int i = 0; i < np; ++i)
-    SF_HIP(hipMemcpyAsync(c->h_counts + i, c->pools[i].d_log_count, 4, hipMemcpyDeviceToHost, compute));
+  // 1. every pool's lookup log into the pinned mirror (device counts cleared)
+  hipLaunchKernelGGL(logs_to_host_kernel, dim3(np), dim3(256), 0, compute, c->d_logs, c->h_logs_dev,
+                     (const LogTab*)c->d_logtab);
+  SF_LAUNCH_CHECK();
   SF_HIP(hipStreamSynchronize(compute));
+  // 2. async mode: publish the previous fill (its copy must be complete by now,
+  //    and the staging is free again after this wait)
+  if (c->in_flight) {
+    SF_HIP(hipEventSynchronize(c->copy_done));
+    sf_status st = publish(c, compute);
+    if (st != SF_OK) return st;
+  }
+  // 3. policy of every pool; installs gathered into the one staging
+  const uint32_t* counts = (const uint32_t*)c->h_logs;
+  UnmapEnt* unm = (UnmapEnt*)c->h_stage;
+  MapEnt* mp = (MapEnt*)(c->h_stage + c->map_off);
+  uint8_t* data = c->h_stage + c->data_off;
+  int32_t n_unmap = 0, n_map = 0;
+  int64_t dpos = 0;
+  bool overflow = false;
   for (int i = 0; i < np; ++i) {
     HostPool& p = c->pools[i];
-    uint32_t cnt = c->h_counts[i];
+    if (p.resident) continue;
+    uint32_t cnt = counts[i];
     if (cnt > (uint32_t)p.log_cap) {
       overflow = true;
       cnt = (uint32_t)p.log_cap;
     }
-    p.log_u.resize(cnt);
-    p.log_s.resize(cnt);
-    if (cnt) {
-      SF_HIP(hipMemcpyAsync(p.log_u.data(), p.d_log_units, 4 * (size_t)cnt, hipMemcpyDeviceToHost, compute));
-      SF_HIP(hipMemcpyAsync(p.log_s.data(), p.d_log_slots, 4 * (size_t)cnt, hipMemcpyDeviceToHost, compute));
-    }
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, compute, p.d_log_count, 1);
-    SF_LAUNCH_CHECK();
-  }
-  SF_HIP(hipStreamSynchronize(compute));
-  // 2. async mode: publish the previous fill (its copy must be complete by now)
-  for (int i = 0; i < np; ++i) {
-    HostPool& p = c->pools[i];
-    if (p.in_flight) {
-      SF_HIP(hipEventSynchronize(p.copy_done));
-      sf_status st = publish(c, p, compute);
-      if (st != SF_OK) return st;
-    }
-  }
-  // 3. policy, gather, copy, install
-  for (int i = 0; i < np; ++i) {
-    HostPool& p = c->pools[i];
-    for (size_t e = 0; e < p.log_u.size(); ++e) {
-      const int64_t u = p.log_u[e];
-      const int32_t s = p.log_s[e];
+    const int32_t* log_u = (const int32_t*)(c->h_logs + p.log_off);
+    const int32_t* log_s = log_u + p.log_cap;
+    const int64_t cap = p.d.capacity;
+    std::vector<int64_t>* now = nullptr;  // bucket of step t
+    for (uint32_t e = 0; e < cnt; ++e) {
+      const int64_t u = log_u[e];
+      const int32_t s = log_s[e];
       ++p.n_lookups;
       if (u < 0 || u >= p.d.n_units) continue;
-      if (s >= 0) {
+      if (s >= 0 && s < cap) {
         ++p.n_hits;
         p.slot_last[s] = t;
-        p.buckets[t].push_back(u);
+        if (!now) now = &p.buckets[t];
+        now->push_back(u);
+        ++p.bucket_entries;
       } else if (p.unit_slot[u] < 0 && !p.pending_flag[u]) {
         p.pending_flag[u] = 1;
         p.pending.push_back(u);
       }
     }
-    if (p.resident || p.d.capacity == 0) {
-      for (int64_t u : p.pending) p.pending_flag[u] = 0;
-      p.pending.clear();
-      continue;
-    }
-    int64_t map_off, data_off;
-    stage_layout(p.stage_units, p.d.unit_bytes, &map_off, &data_off);
-    FillHeader* hdr = (FillHeader*)p.h_stage;
-    int32_t* unmap_ids = (int32_t*)(p.h_stage + 16);
-    int32_t* pairs = (int32_t*)(p.h_stage + map_off);
-    int32_t n_unmap = 0, n_map = 0;
     const int64_t cap_fill = c->max_fill > 0 ? c->max_fill : (int64_t)p.pending.size();
+    int64_t n_pool = 0;
     for (size_t q = 0; q < p.pending.size(); ++q) {
       const int64_t u = p.pending[q];
       p.pending_flag[u] = 0;
-      if ((int64_t)q >= cap_fill || n_map >= p.stage_units) continue;
+      if (cap == 0 || (int64_t)q >= cap_fill || n_pool >= p.stage_units) continue;
       int32_t slot;
       if (!p.free_slots.empty()) {
         slot = p.free_slots.back();
@@ -418,53 +481,54 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
         if (victim < 0) continue;
         slot = p.unit_slot[victim];
         p.unit_slot[victim] = -1;
-        unmap_ids[n_unmap++] = (int32_t)victim;
+        unm[n_unmap++] = UnmapEnt{i, (int32_t)victim};
       }
       p.slot_unit[slot] = u;
       p.unit_slot[u] = slot;
       p.slot_last[slot] = t;
-      p.buckets[t].push_back(u);
-      pairs[2 * n_map] = (int32_t)u;
-      pairs[2 * n_map + 1] = slot;
-      std::memcpy(p.h_stage + data_off + (int64_t)n_map * p.d.unit_bytes,
-                  p.d.host_store + u * p.d.unit_bytes, (size_t)p.d.unit_bytes);
+      if (!now) now = &p.buckets[t];
+      now->push_back(u);
+      ++p.bucket_entries;
+      mp[n_map] = MapEnt{i, (int32_t)u, slot, 0, dpos, 0};
+      std::memcpy(data + dpos, p.d.host_store + u * p.d.unit_bytes, (size_t)p.d.unit_bytes);
+      dpos += align_up(p.d.unit_bytes, DATA_ALIGN);
       ++n_map;
+      ++n_pool;
+      ++p.n_installed;
+      p.h2d_bytes += p.d.unit_bytes;
     }
     p.pending.clear();
-    if (n_map == 0) continue;
-    hdr->n_unmap = n_unmap;
-    hdr->n_map = n_map;
-    // header + lists first, on the compute stream, then unmap there
-    SF_HIP(hipMemcpyAsync(p.d_stage, p.h_stage, (size_t)map_off + (size_t)n_map * 8,
+    compact_buckets(p);
+  }
+  if (n_map > 0) {
+    // 4. entries and unmaps on the compute stream; data and scatter on the side
+    //    stream once the unmaps are done there
+    if (n_unmap > 0)
+      SF_HIP(hipMemcpyAsync(c->d_stage, c->h_stage, sizeof(UnmapEnt) * (size_t)n_unmap, hipMemcpyHostToDevice,
+                            compute));
+    SF_HIP(hipMemcpyAsync(c->d_stage + c->map_off, c->h_stage + c->map_off, sizeof(MapEnt) * (size_t)n_map,
                           hipMemcpyHostToDevice, compute));
     if (n_unmap > 0) {
-      hipLaunchKernelGGL(unmap_kernel, dim3((n_unmap + 255) / 256), dim3(256), 0, compute,
-                         p.d_unit2slot, (const uint8_t*)p.d_stage);
+      hipLaunchKernelGGL(unmap_kernel, dim3((n_unmap + 255) / 256), dim3(256), 0, compute, c->d_pooltab,
+                         (const UnmapEnt*)c->d_stage, n_unmap);
       SF_LAUNCH_CHECK();
     }
     SF_HIP(hipEventRecord(c->ev_compute, compute));
     SF_HIP(hipStreamWaitEvent(side, c->ev_compute, 0));
-    const size_t bytes = (size_t)n_map * p.d.unit_bytes;
-    SF_HIP(hipMemcpyAsync(p.d_stage + data_off, p.h_stage + data_off, bytes, hipMemcpyHostToDevice, side));
-    const int64_t words = bytes / 4;
-    const unsigned blocks = (unsigned)std::min<int64_t>((words + 255) / 256, 4096);
-    hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, side, p.d_slots,
-                       (const uint8_t*)p.d_stage, map_off, data_off, p.d.unit_bytes);
+    SF_HIP(hipMemcpyAsync(c->d_stage + c->data_off, data, (size_t)dpos, hipMemcpyHostToDevice, side));
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)std::min(n_map, 4096)), dim3(256), 0, side, c->d_pooltab,
+                       (const MapEnt*)(c->d_stage + c->map_off), n_map, (const uint8_t*)(c->d_stage + c->data_off));
     SF_LAUNCH_CHECK();
-    SF_HIP(hipEventRecord(p.copy_done, side));
-    p.in_flight = true;
-    p.flight_maps = n_map;
-    p.n_installed += n_map;
-    p.h2d_bytes += (int64_t)bytes;
-    filled += n_map;
+    SF_HIP(hipEventRecord(c->copy_done, side));
+    c->in_flight = true;
+    c->flight_maps = n_map;
     if (c->mode == SF_CACHE_DETERMINISTIC) {
-      sf_status st = publish(c, p, compute);
+      sf_status st = publish(c, compute);
       if (st != SF_OK) return st;
     }
   }
-  if (c->mode == SF_CACHE_DETERMINISTIC) SF_HIP(hipStreamSynchronize(compute));
   c->step = t + 1;
-  if (n_filled) *n_filled = filled;
+  if (n_filled) *n_filled = n_map;
   if (overflow) {
     sf_set_error("sf_refine_cache_fill: lookup log overflow (raise max_lookup); some lookups were not recorded");
     return SF_ESTATE;

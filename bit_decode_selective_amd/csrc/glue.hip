@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const uint16_t* table, int64
 }
 
 // h[b] += y[b] (if y); x[b] = fp16(h[b] / sqrt(mean(h[b]^2) + eps) * w)
+// General form: any hidden size, one strided pass to add and square, one to scale.
 constexpr int NORM_T = 256;
 __global__ __launch_bounds__(NORM_T) void add_rmsnorm_kernel(float* h, const float* y, const float* w, int hidden,
                                                              float eps, uint16_t* x) {
@@ -59,6 +60,56 @@ __global__ __launch_bounds__(NORM_T) void add_rmsnorm_kernel(float* h, const flo
   const float tot = block_sum<NORM_T>(ss, red);
   const float rstd = 1.f / sqrtf(tot / (float)hidden + eps);
   for (int i = threadIdx.x; i < hidden; i += NORM_T) x[(size_t)b * hidden + i] = f2h(hr[i] * rstd * w[i]);
+}
+
+// Row kept in registers: hidden % 4 == 0 and hidden <= 4 * NORMV_T * NORMV_N.  Every
+// load of the row is issued before the first reduction, so a row costs about one
+// memory latency instead of one per strided step.
+constexpr int NORMV_T = 1024, NORMV_N = 4;
+__global__ __launch_bounds__(NORMV_T) void add_rmsnorm_vec_kernel(float* __restrict__ h, const float* __restrict__ y,
+                                                                  const float* __restrict__ w, int hidden, float eps,
+                                                                  uint16_t* __restrict__ x) {
+  __shared__ float red[NORMV_T / 64];
+  const int b = blockIdx.x, n4 = hidden >> 2;
+  float4* hr = (float4*)(h + (size_t)b * hidden);
+  const float4* yr = y ? (const float4*)(y + (size_t)b * hidden) : nullptr;
+  float4 v[NORMV_N];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NORMV_N; ++k) {
+    const int i = threadIdx.x + k * NORMV_T;
+    v[k] = i < n4 ? hr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (yr && i < n4) {
+      const float4 t = yr[i];
+      v[k].x += t.x;
+      v[k].y += t.y;
+      v[k].z += t.z;
+      v[k].w += t.w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NORMV_N; ++k) {
+    const int i = threadIdx.x + k * NORMV_T;
+    if (yr && i < n4) hr[i] = v[k];
+    ss = fmaf(v[k].x, v[k].x, ss);
+    ss = fmaf(v[k].y, v[k].y, ss);
+    ss = fmaf(v[k].z, v[k].z, ss);
+    ss = fmaf(v[k].w, v[k].w, ss);
+  }
+  const float tot = block_sum<NORMV_T>(ss, red);
+  const float rstd = 1.f / sqrtf(tot / (float)hidden + eps);
+  const float4* wr = (const float4*)w;
+  uint2* xr = (uint2*)(x + (size_t)b * hidden);
+#pragma unroll
+  for (int k = 0; k < NORMV_N; ++k) {
+    const int i = threadIdx.x + k * NORMV_T;
+    if (i < n4) {
+      const float4 g = wr[i];
+      const uint32_t lo = (uint32_t)f2h(v[k].x * rstd * g.x) | ((uint32_t)f2h(v[k].y * rstd * g.y) << 16);
+      const uint32_t hi = (uint32_t)f2h(v[k].z * rstd * g.z) | ((uint32_t)f2h(v[k].w * rstd * g.w) << 16);
+      xr[i] = make_uint2(lo, hi);
+    }
+  }
 }
 
 // One wave per (batch, head) of 128 dims; lane i owns the rotate-half pair (i, i + 64).
@@ -167,7 +218,14 @@ extern "C" sf_status sf_add_rmsnorm(float* h, const float* y, const float* w, in
                                     uint16_t* x_f16, sf_stream stream) {
   SF_REQUIRE(h && w && x_f16, SF_EINVAL, "null argument");
   SF_REQUIRE(batch > 0 && hidden > 0 && eps >= 0.f, SF_EINVAL, "bad sizes");
-  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(batch), dim3(NORM_T), 0, (hipStream_t)stream, h, y, w, hidden, eps, x_f16);
+  const auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+  if (hidden % 4 == 0 && hidden <= 4 * NORMV_T * NORMV_N && al(h, 16) && (!y || al(y, 16)) && al(w, 16) &&
+      al(x_f16, 8))
+    hipLaunchKernelGGL(add_rmsnorm_vec_kernel, dim3(batch), dim3(NORMV_T), 0, (hipStream_t)stream, h, y, w, hidden,
+                       eps, x_f16);
+  else
+    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(batch), dim3(NORM_T), 0, (hipStream_t)stream, h, y, w, hidden, eps,
+                       x_f16);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }

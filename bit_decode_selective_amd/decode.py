@@ -126,14 +126,15 @@ class DecodeModel:
             qw = binding.QuantWeight.from_host(W, b, r) if keep_host else binding.QuantWeight.from_device(W, b, r)
             return qw
 
-        def add_pool(unit_bytes_obj):
+        def add_pool(unit_bytes_obj, n_lookup):
+            """n_lookup: unit ids one step looks up in the pool (sizes its lookup log)."""
             if pool_frac is None:
                 pools.append(unit_bytes_obj.resident_pool_desc())
             else:
                 st = unit_bytes_obj.host_store()
                 stores.append(st)
                 cap = max(0, int(pool_frac * st.shape[0]))
-                pools.append(binding.host_pool_desc(st, cap))
+                pools.append(binding.host_pool_desc(st, cap, max_lookup=n_lookup))
             return len(pools) - 1
 
         self.layers = []
@@ -148,7 +149,7 @@ class DecodeModel:
             L["down"] = quant(li, inputs.DOWN, H, S.ffn)
             if r > 0:
                 for name in ("q", "k", "v", "o", "gate", "up", "down"):
-                    L["pool_" + name] = add_pool(L[name])
+                    L["pool_" + name] = add_pool(L[name], k_select(ch_pct, L[name].k_in))
             L["attn_norm"] = torch.as_tensor(src.gain(li, ATTN_NORM, H), device=dev)
             L["ffn_norm"] = torch.as_tensor(src.gain(li, FFN_NORM, H), device=dev)
             if S.qk_norm:
@@ -158,7 +159,8 @@ class DecodeModel:
             kv = binding.QuantKV(batch, S.n_kv, t_cap, kv_b, kv_r, device=dev)
             L["kv"] = kv
             if kv_r > 0:
-                L["pool_kv"] = add_pool(kv)  # store taken before any token: refilled from the device copy below
+                # store taken before any token: refilled from the device copy in fill_kv
+                L["pool_kv"] = add_pool(kv, batch * S.n_kv * k_select(tok_pct, t_cap))
             self.layers.append(L)
             torch.cuda.synchronize()
         self.final_norm = torch.as_tensor(src.gain(S.layers, FINAL_NORM, H), device=dev)
@@ -167,7 +169,7 @@ class DecodeModel:
             self.host["embed"] = emb
         self.embed = binding._f16_bits(emb, dev)
         self.lm_head = quant(S.layers, inputs.LM_HEAD, S.vocab, H)
-        self.pool_lm = add_pool(self.lm_head) if r > 0 else -1
+        self.pool_lm = add_pool(self.lm_head, k_select(ch_pct, H)) if r > 0 else -1
         self._pool_frac = pool_frac
         self._pools, self._stores = pools, stores
         self.cache = binding.RefineCache(pools, mode=cache_mode, device=dev, keep=stores) if pools else None

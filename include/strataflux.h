@@ -181,13 +181,15 @@ sf_status sf_refine_cache_destroy(sf_refine_cache* c);
 sf_status sf_refine_cache_lookup(sf_refine_cache* c, int32_t pool, const int32_t* unit_ids,
                                  int32_t n, int32_t* slot_out, sf_stream compute);
 
-/* End of a decode step: reads the step's lookups, runs the replacement policy,
- * gathers the missed units from the host stores into pinned staging and copies
- * them with one hipMemcpyAsync per pool on `side`, then installs them.
+/* End of a decode step: reads the step's lookups of every pool (one kernel into a
+ * pinned mirror, then one wait on `compute`), runs the replacement policy, gathers
+ * the missed units of every pool from the host stores into one pinned staging
+ * buffer and copies it with one hipMemcpyAsync on `side`, then installs them.
  * Deterministic mode: returns after the new units are visible to work enqueued
  * later on `compute`.  Async mode: returns after enqueueing; units whose copy
  * finished are published at a later fill call.  n_filled (host, may be NULL):
- * units installed or queued for install by this call. */
+ * units installed or queued for install by this call.  SF_ESTATE if a pool's
+ * lookups of the step exceeded its max_lookup (the excess was not recorded). */
 sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream side,
                                int64_t* n_filled);
 

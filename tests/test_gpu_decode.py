@@ -50,7 +50,7 @@ def test_embed_and_argmax():
         assert got.tolist() == o_dec.argmax(lg).tolist() and got[1] == 7 and got[2] == 0
 
 
-@pytest.mark.parametrize("hidden", [256, 4096, 5000])
+@pytest.mark.parametrize("hidden", [256, 4096, 5000, 4098, 20480])
 def test_add_rmsnorm(hidden):
     rng = np.random.default_rng(hidden)
     h = rng.standard_normal((3, hidden)).astype(np.float32)
