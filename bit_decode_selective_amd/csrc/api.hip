@@ -56,7 +56,7 @@ extern "C" sf_status sf_workspace_create(size_t bytes, sf_workspace** out) {
   }
   w->bytes = bytes;
   const int words = (int)(sizeof(WsControl) / 4);
-  hipLaunchKernelGGL(ws_zero_kernel, dim3(8), dim3(256), 0, 0, (uint32_t*)w->base, words);
+  hipLaunchKernelGGL(ws_zero_kernel, dim3(64), dim3(256), 0, 0, (uint32_t*)w->base, words);
   e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     hipFree(w->base);

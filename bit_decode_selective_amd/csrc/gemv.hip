@@ -66,6 +66,10 @@ struct GemvArgs {
   int32_t report;  // fused kernel: report the selection, hits and lookup log
   float* part;
   uint32_t* ctr;
+  // overlapped kernel: workgroup 0 selects (sel_wg = 1) and publishes through the
+  // workspace control words ctl (WsControl: sel_state, done, timeout)
+  int32_t sel_wg;
+  uint32_t* ctl;
 };
 
 // ---- code layouts ----------------------------------------------------------------
@@ -75,6 +79,18 @@ struct GemvArgs {
 // b in {1, 2, 4, 8}: a 16-byte chunk of 4 words, P = 32/b codes per word.  Codes i
 // and i + P/2 of a word are 16 bits apart, so one shift and one and-or put both in
 // the top mantissa bits of the two fp16 halves.
+// Constants of the code expansion held in VGPRs: with both in VGPRs the mask-and-or
+// is one v_and_or_b32 (a 32-bit literal cannot be a VOP3 operand here, which would
+// split it into v_and_b32 + v_or_b32).
+struct PairK {
+  uint32_t m, e;
+};
+__device__ __forceinline__ PairK pair_k(uint32_t m) {
+  PairK k{m, 0x3C003C00u};
+  asm volatile("" : "+v"(k.m), "+v"(k.e));
+  return k;
+}
+
 template <int B>
 struct CodecPow2 {
   static constexpr int WORDS = 4;
@@ -87,12 +103,25 @@ struct CodecPow2 {
     *hi = q >= HP;
     *j = w * HP + (q - (*hi) * HP);
   }
+  // channels (within the chunk) of the low and high half of pair j
+  __host__ __device__ static constexpr int lo(int j) { return (j / HP) * P + j % HP; }
+  __host__ __device__ static constexpr int hi(int j) { return (j / HP) * P + HP + j % HP; }
   __device__ static __forceinline__ uint32_t pair(const uint32_t* w, int j) {
     const int wi = j / HP, i = j % HP;
     const int sh = (10 - B) - i * B;
     const uint32_t t = sh >= 0 ? (w[wi] << sh) : (w[wi] >> (-sh));
     constexpr uint32_t m = ((1u << B) - 1u) << (10 - B);
     return (t & (m | (m << 16))) | 0x3C003C00u;
+  }
+  __device__ static __forceinline__ PairK consts() {
+    constexpr uint32_t m = ((1u << B) - 1u) << (10 - B);
+    return pair_k(m | (m << 16));
+  }
+  __device__ static __forceinline__ uint32_t pair(const uint32_t* w, int j, const PairK& k) {
+    const int wi = j / HP, i = j % HP;
+    const int sh = (10 - B) - i * B;
+    const uint32_t t = sh >= 0 ? (w[wi] << sh) : (w[wi] >> (-sh));
+    return (t & k.m) | k.e;
   }
 };
 
@@ -107,6 +136,8 @@ struct CodecStream {
     *j = kk >> 1;
     *hi = kk & 1;
   }
+  __host__ __device__ static constexpr int lo(int j) { return 2 * j; }
+  __host__ __device__ static constexpr int hi(int j) { return 2 * j + 1; }
   __device__ static __forceinline__ uint32_t code(const uint32_t* w, int k) {
     const int bit = k * B, wi = bit >> 5, off = bit & 31;
     uint32_t v = w[wi] >> off;
@@ -116,6 +147,11 @@ struct CodecStream {
   __device__ static __forceinline__ uint32_t pair(const uint32_t* w, int j) {
     const uint32_t c0 = code(w, 2 * j), c1 = code(w, 2 * j + 1);
     return ((c0 | (c1 << 16)) << (10 - B)) | 0x3C003C00u;
+  }
+  __device__ static __forceinline__ PairK consts() { return pair_k(0u); }
+  __device__ static __forceinline__ uint32_t pair(const uint32_t* w, int j, const PairK& k) {
+    const uint32_t c0 = code(w, 2 * j), c1 = code(w, 2 * j + 1);
+    return ((c0 | (c1 << 16)) << (10 - B)) | k.e;
   }
 };
 
@@ -522,6 +558,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         }
       }
     }
+    const PairK pk = C::consts();
     float acc[NB][R];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
@@ -546,7 +583,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
           for (int rr = 0; rr < R; ++rr)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[rr], 4 * jb + q)), as_h2(xv[q]), d[rr], false);
+              d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[rr], 4 * jb + q, pk)), as_h2(xv[q]), d[rr], false);
         }
         const float X = xsum[bb * nchunks + c];
 #pragma unroll
@@ -645,6 +682,48 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
 
 
+// ---- cross-lane sums by DPP -------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                               false));
+}
+// Sum over groups of N = 2, 4, 8 or 16 consecutive lanes; every lane of a group
+// gets its group's sum (quad swaps, then half-row and row mirrors).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v); // row_mirror
+  return v;
+}
+// Sum over the wave, complete in lane 63 (rows 1 and 3 take row 0 / row 2 by
+// row_bcast15, then row 3 takes rows 0-1 by row_bcast31).
+__device__ __forceinline__ float wave_sum63(float v) {
+  v = group_sum<16>(v);
+  v += dpp_mov<0x142, 0xA>(v);
+  v += dpp_mov<0x143, 0xC>(v);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes: row-local Hillis-Steele steps (row_shr
+// 1, 2, 4, 8 with zeros shifted in), then rows 1 and 3 add the totals of rows 0
+// and 2 (row_bcast15) and rows 2 and 3 the total of rows 0-1 (row_bcast31).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_mov_z(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_mov_z<0x111>(v);  // row_shr:1
+  v += dpp_mov_z<0x112>(v);  // row_shr:2
+  v += dpp_mov_z<0x114>(v);  // row_shr:4
+  v += dpp_mov_z<0x118>(v);  // row_shr:8
+  v += dpp_mov_z<0x142, 0xA>(v);
+  v += dpp_mov_z<0x143, 0xC>(v);
+  return v;
+}
+
 // Largest bin b of the sum of four per-wave histograms h[w][0..nbin) whose suffix
 // count (bins >= b) reaches `need`; *above = count in bins above b.  Every wave
 // computes it from the histograms itself.  nbin = 256 or 128.
@@ -660,12 +739,7 @@ __device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[256], int nb
       c[i] = (int)((h[0][b] + h[1][b]) + (h[2][b] + h[3][b]));
       s += c[i];
     }
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_scan(s);
   int run = incl - s, hit = -1, hab = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -678,8 +752,8 @@ __device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[256], int nb
     }
   const uint64_t m = __ballot(hit >= 0);
   const int src = m ? __builtin_ctzll(m) : 0;
-  *bin = __shfl(hit, src, 64);
-  *above = __shfl(hab, src, 64);
+  *bin = __builtin_amdgcn_readlane(hit, src);
+  *above = __builtin_amdgcn_readlane(hab, src);
 }
 __device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[128], int nbin, int need, int* bin,
                                                 int* above) {
@@ -692,12 +766,7 @@ __device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[128], int nb
     s += c[i];
   }
   (void)nbin;
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_scan(s);
   int run = incl - s, hit = -1, hab = 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -709,8 +778,8 @@ __device__ __forceinline__ void wave_threshold4(const uint32_t (*h)[128], int nb
   }
   const uint64_t m = __ballot(hit >= 0);
   const int src = m ? __builtin_ctzll(m) : 0;
-  *bin = __shfl(hit, src, 64);
-  *above = __shfl(hab, src, 64);
+  *bin = __builtin_amdgcn_readlane(hit, src);
+  *above = __builtin_amdgcn_readlane(hab, src);
 }
 
 // Keys of 8 channels (4 words of two 15-bit keys): (#keys > T) | (#keys == T) << 16.
@@ -988,6 +1057,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
     }
   }
 
+  const PairK pk = C::consts();
   float acc[NB][R];
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb)
@@ -1014,7 +1084,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
             for (int rr = 0; rr < R; ++rr)
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q)), as_h2(xv[q]), d[rr], false);
+                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q, pk)), as_h2(xv[q]), d[rr], false);
           }
           const float X = xsum[bb * nchunks + c];
 #pragma unroll
@@ -1130,6 +1200,456 @@ size_t fused_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
   size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
   if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel + (size_t)(k_in / 16);
   return w * 4;
+}
+
+// ---- batch-1/2 GEMV with one selecting workgroup ---------------------------------
+// Workgroup 0 selects the channels (the same two-pass radix select as the other
+// kernels, on its 4 waves), looks up their slots per matrix and publishes both
+// through the workspace with agent-scope stores before raising sel_state.  Every
+// other workgroup is one row tile (4 waves x R rows) and needs the selection only
+// at its end: it requests x and the tile's codes, stages x in LDS (pair order,
+// chunk stride padded by 4 words so that the lanes' 16-byte reads of consecutive
+// chunks fall in different banks), runs the resident dot products, then waits for
+// the selection, fetches the refinement words of its rows at the hit channels and
+// adds them before the row sums (DPP) are written.  The last tile to read the
+// selection resets sel_state for the next launch.
+// Dynamic LDS, tiles: x pairs [NB][nchunks][PAIRS + 4] | chunk sums [NB][nchunks]
+// | scale words [4][R][K/128]; selector: keys [K/2] | bitmaps [2][K/32] |
+// selection [k_sel] | histograms [4][256] + [4][128] | 16 words.
+template <class C>
+__host__ __device__ constexpr int chunk_stride() { return C::PAIRS + 4; }
+
+size_t split_lds_bytes(int k_in, int pairs, int codes, int nb, int k_sel, int rpw) {
+  (void)pairs;
+  (void)codes;
+  size_t tile = 0;
+  if (k_sel > 0) tile += (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel * (1 + nb + (31 + 4 * rpw * 7 + 31) / 32);
+  size_t sel = 0;
+  if (k_sel > 0) sel = (size_t)(k_in / 2) + 2 * (size_t)(k_in / 32) + (((size_t)k_sel + 3) & ~(size_t)3) + 4 * 256 + 4 * 128 + 16;
+  return std::max(tile, sel) * 4;
+}
+
+// Copies of the published words (tile t reads copy t mod SPLIT_COPIES), and the
+// stride of one copy in words.
+constexpr int SPLIT_COPIES = 8;
+__host__ __device__ inline int split_copy_words(int k_sel, int n_ops) { return ((k_sel * (1 + n_ops)) + 31) & ~31; }
+
+// A tile that has seen the flag counts itself (no return value).
+__device__ __forceinline__ void count_reader(const GemvArgs& a, int grp) {
+  uint32_t* c = a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * grp;
+  (void)__hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane 0 of a wave polls its group's flag (bounded); the result is wave-uniform.
+__device__ __forceinline__ bool wait_published(const GemvArgs& a, int grp) {
+  const uint32_t* f = a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * grp;
+  for (uint32_t it = 0;; ++it) {
+    uint32_t v = 0u;
+    if ((threadIdx.x & 63) == 0) v = sf_get(f);
+    if (__builtin_amdgcn_readfirstlane(v) != 0u) return true;
+    if (it >= (1u << 22)) {
+      if ((threadIdx.x & 63) == 0) sf_put(a.ctl + 2, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Workgroup 0, after publishing: waits until every tile has seen the flag, then
+// lowers the flags and clears the counts for the next launch.
+__device__ __forceinline__ void split_retire(const GemvArgs& a) {
+  const int tid = threadIdx.x;
+  if (tid >= 64) return;
+  uint32_t* ctr = a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * tid;
+  uint32_t* flag = a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid;
+  const uint32_t tiles = (uint32_t)a.total_tiles;
+  const uint32_t want = (uint32_t)tid < tiles ? (tiles - (uint32_t)tid + 63u) / 64u : 0u;
+  for (uint32_t it = 0;; ++it) {
+    if (__all(sf_get(ctr) >= want)) break;
+    if (it >= (1u << 22)) {
+      sf_put(a.ctl + 2, 1u);
+      return;  // the timeout flag reports it
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+  sf_put(flag, 0u);
+  sf_put(ctr, 0u);
+}
+
+// Workgroup 0: selection into l_sel (LDS), then the lookups, the published copy in
+// the workspace and the reports.
+__device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint32_t* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.k_in, ks = a.k_sel, n8 = K / 8;
+  uint32_t* keys = smem;                       // [K/2]
+  uint32_t* bm_sure = keys + K / 2;            // [K/32]
+  uint32_t* bm_bnd = bm_sure + K / 32;         // [K/32]
+  int32_t* l_sel = (int32_t*)(bm_bnd + K / 32);  // [ks]
+  uint32_t (*whist)[256] = (uint32_t (*)[256])(l_sel + ((ks + 3) & ~3));
+  uint32_t (*whist2)[128] = (uint32_t (*)[128])(whist[4]);
+  int* sc = (int*)(whist2[4]);  // [16]
+  SF_TS(6);
+  if (a.sel_in) {
+    for (int j = tid; j < ks; j += 256) l_sel[j] = a.sel_in[j];
+  } else if (ks >= K) {
+    for (int j = tid; j < ks; j += 256) l_sel[j] = j;
+  } else {
+    for (int i = lane; i < 256; i += 64) whist[wave][i] = 0u;
+    for (int i = lane; i < 128; i += 64) whist2[wave][i] = 0u;
+    // keys (max over the batch of |x| as 15-bit patterns) and pass 1: top 8 key bits;
+    // 8 loads a thread in flight (K <= 16384 in one round)
+    for (int m0 = 0; m0 < n8; m0 += 256 * 8) {
+      u32x4 kv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kv[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int bb = 0; bb < a.batch; ++bb) {
+        const u32x4* xr = (const u32x4*)(a.x + (size_t)bb * K);
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x2 = v[i][q] & 0x7FFF7FFFu;
+            kv[i][q] = max(kv[i][q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[i][q] >> 16, x2 >> 16) << 16);
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 256 * i + tid;
+        if (m < n8) {
+          *(u32x4*)(keys + 4 * m) = kv[i];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            atomicAdd(&whist[wave][(kv[i][q] & 0xFFFFu) >> 7], 1u);
+            atomicAdd(&whist[wave][kv[i][q] >> 23], 1u);
+          }
+        }
+      }
+    }
+    lds_barrier();
+    SF_TS(7);
+    int b1, above1;
+    wave_threshold4(whist, 256, ks, &b1, &above1);
+    // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
+    // (all taken) and in bin b1
+    {
+      uint8_t* bs = (uint8_t*)bm_sure;
+      uint8_t* bb = (uint8_t*)bm_bnd;
+      for (int m = tid; m < n8; m += 256) {
+        const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+        uint32_t sure = 0u, bnd = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const int bin = (int)(key >> 7);
+          sure |= (uint32_t)(bin > b1) << e;
+          if (bin == b1) {
+            bnd |= 1u << e;
+            atomicAdd(&whist2[wave][key & 127u], 1u);
+          }
+        }
+        bs[m] = (uint8_t)sure;
+        bb[m] = (uint8_t)bnd;
+      }
+    }
+    lds_barrier();
+    SF_TS(11);
+    int b2, above2;
+    wave_threshold4(whist2, 128, ks - above1, &b2, &above2);
+    const uint32_t need = (uint32_t)(ks - above1 - above2);  // keys equal to T taken, lowest channels first
+    // compaction in channel order (thread t owns bitmap words [t W, t W + W))
+    const int nw = K / 32, W = (nw + 255) / 256;
+    const uint16_t* key16 = (const uint16_t*)keys;
+    uint32_t sg[4], eqm[4], cs = 0u, ce = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sg[i] = eqm[i] = 0u;
+      const int w = tid * W + i;
+      if (i < W && w < nw) {
+        uint32_t bnd = bm_bnd[w], gtw = 0u, eqw = 0u;
+        while (bnd) {
+          const int bit = __builtin_ctz(bnd);
+          bnd &= bnd - 1u;
+          const uint32_t lo = key16[32 * w + bit] & 127u;
+          gtw |= (uint32_t)(lo > (uint32_t)b2) << bit;
+          eqw |= (uint32_t)(lo == (uint32_t)b2) << bit;
+        }
+        sg[i] = bm_sure[w] | gtw;
+        eqm[i] = eqw;
+        cs += __popc(sg[i]);
+        ce += __popc(eqm[i]);
+      }
+    }
+    uint32_t ts, te;
+    uint32_t sbefore = wave_excl_sum8(cs, &ts), ebefore = wave_excl_sum8(ce, &te);
+    if (lane == 0) sc[wave] = (int)(ts | (te << 16));
+    lds_barrier();
+    for (int w = 0; w < wave; ++w) {
+      sbefore += (uint32_t)sc[w] & 0xFFFFu;
+      ebefore += (uint32_t)sc[w] >> 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t all = sg[i] | eqm[i];
+      while (all) {
+        const int bit = __builtin_ctz(all);
+        all &= all - 1u;
+        const int c = 32 * (tid * W + i) + bit;
+        if ((sg[i] >> bit) & 1u) {
+          l_sel[sbefore + min(ebefore, need)] = c;
+          ++sbefore;
+        } else {
+          if (ebefore < need) l_sel[sbefore + ebefore] = c;
+          ++ebefore;
+        }
+      }
+    }
+  }
+  // the lookup-log bases (one reservation per matrix)
+  if (a.report && tid < a.n_ops) {
+    const PoolDev& pool = a.ops[tid].pool;
+    int base = -1;
+    if (pool.log_count) {
+      const uint32_t bse = atomicAdd(pool.log_count, (uint32_t)ks);
+      base = (bse + (uint32_t)ks <= (uint32_t)pool.log_cap) ? (int)bse : -1;
+    }
+    sc[8 + tid] = base;
+  }
+  lds_barrier();
+  SF_TS(12);
+  uint32_t* hw = a.ctl + offsetof(WsControl, hit) / 4;
+  const int cst = split_copy_words(ks, a.n_ops);
+  for (int j = tid; j < ks; j += 256) {
+    const int k = l_sel[j];
+#pragma unroll
+    for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + j, (uint32_t)k);
+    if (a.report && a.sel_out) a.sel_out[j] = k;
+#pragma unroll
+    for (int op = 0; op < SF_MAX_OPS; ++op) {
+      if (op >= a.n_ops) break;
+      const PoolDev& pool = a.ops[op].pool;
+      const int slot = pool.resident ? k : (pool.unit2slot ? pool.unit2slot[k] : -1);
+      if (!pool.resident)
+#pragma unroll
+        for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + ks * (1 + op) + j, (uint32_t)slot);
+      if (a.report) {
+        if (a.ops[op].hit_out) a.ops[op].hit_out[j] = slot;
+        const int base = sc[8 + op];
+        if (base >= 0) {
+          pool.log_units[base + j] = k;
+          pool.log_slots[base + j] = slot;
+        }
+      }
+    }
+  }
+  // the words are complete at the coherence point before any flag goes up
+  sf_drain();
+  __syncthreads();
+  if (tid < 64) sf_put(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 1u);
+  SF_TS(13);
+}
+
+// x pair j of a chunk from the chunk's x in natural order (word t = channels 2t, 2t+1)
+template <class C>
+__device__ __forceinline__ uint32_t xpair(const uint32_t* X, int j) {
+  const int l = C::lo(j), h = C::hi(j);
+  if (l / 2 == h / 2 && l % 2 == 0 && h % 2 == 1) return X[l / 2];
+  return __builtin_amdgcn_perm(X[h / 2], X[l / 2], ((h % 2 ? 0x0706u : 0x0504u) << 16) | (l % 2 ? 0x0302u : 0x0100u));
+}
+
+template <class C, int R, int NB>
+__device__ __forceinline__ void load_x_chunk(const GemvArgs& a, int c, uint32_t (&xw)[NB][C::CODES / 2]) {
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * a.k_in + (size_t)c * C::CODES);
+#pragma unroll
+    for (int i = 0; i < C::CODES / 8; ++i) {
+      const u32x4 v = xr[i];
+      xw[bb][4 * i] = v.x;
+      xw[bb][4 * i + 1] = v.y;
+      xw[bb][4 * i + 2] = v.z;
+      xw[bb][4 * i + 3] = v.w;
+    }
+  }
+}
+
+constexpr int SPLIT_HPF = 8;  // hits per lane whose words are requested together
+
+template <class C, int B, int R, int NB, int D>
+__global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
+  constexpr int WTM = (31 + 4 * R * 7 + 31) / 32;  // words of a tile's refinement window (r <= 7)
+  extern __shared__ uint32_t smem[];
+  __shared__ int s_flag;
+  const int ks = a.k_sel;
+  const bool refine = ks > 0;
+  if (a.sel_wg && blockIdx.x == 0) {
+    __builtin_amdgcn_s_setprio(3);  // issue ahead of the streaming waves sharing the CU
+    split_select_and_publish(a, smem);
+    __builtin_amdgcn_s_setprio(0);
+    split_retire(a);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.k_in, nchunks = K / C::CODES, ngr = K / 128;
+  uint32_t* s_szw = smem;                                          // [4][R][ngr]
+  int32_t* l_hk = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [k_sel] hit channel or -1
+  float* l_hx = (float*)(l_hk + (refine ? ks : 0));                 // [k_sel][NB] x at the hit
+  uint32_t* l_hw = (uint32_t*)(l_hx + (refine ? ks * NB : 0));      // [k_sel][WTM] the tile's words
+  const int tile_g = blockIdx.x - a.sel_wg;
+  const int op = op_of_tile(a, tile_g);
+  const GemvOpDev& o = a.ops[op];
+  const int row0 = (tile_g - o.tile_begin) * 4 * R + wave * R;
+  const size_t rowbytes = (size_t)K * B / 8;
+  SF_TS(0);
+
+  // the first D chunks of this lane: codes of the wave's rows, their scale words
+  // and x (natural order; L1/L2-resident after the first wave), clamped so that
+  // every load is unconditional
+  uint32_t cw[D][R][C::WORDS];
+  uint32_t szw[D][R];
+  uint32_t xw[D][NB][C::CODES / 2];
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int c = min(lane + 64 * u, nchunks - 1);
+    load_chunk_clamped<C, R>(o, row0, c, rowbytes, ngr, cw[u], szw[u]);
+    load_x_chunk<C, R, NB>(a, c, xw[u]);
+  }
+
+  const float scl = (float)(1u << (a.r + B));
+  const int r = a.r;
+  uint32_t* szrow = s_szw + wave * R * ngr;  // this wave's rows' scale words, [R][ngr]
+  const PairK pk = C::consts();
+  float acc[NB][R];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = 0.f;
+  for (int c0 = 0; c0 < nchunks; c0 += 64 * D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int c = c0 + 64 * u + lane;
+      if (c < nchunks) {
+        if (refine && (c * C::CODES) % 128 == 0)
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[u][rr];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          float X = 0.f;
+#pragma unroll
+          for (int t = 0; t < C::CODES / 2; ++t) X = __builtin_amdgcn_fdot2(as_h2(xw[u][bb][t]), as_h2(0x3C003C00u), X, false);
+          float d[R];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
+#pragma unroll
+          for (int jb = 0; jb < C::PAIRS; jb += 4) {
+            // four pairs at a time keeps the live x pairs and expanded codes few
+            uint32_t xp[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xp[q] = xpair<C>(xw[u][bb], jb + q);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], jb + q, pk)), as_h2(xp[q]), d[rr], false);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+            const float sv = sf_h2f(szw[u][rr]), zv = sf_h2f(szw[u][rr] >> 16);
+            acc[bb][rr] += (sv * scl) * (d[rr] - X) + zv * X;
+          }
+        }
+        const int cn = c + 64 * D;
+        if (cn < nchunks) {
+          load_chunk_clamped<C, R>(o, row0, cn, rowbytes, ngr, cw[u], szw[u]);
+          load_x_chunk<C, R, NB>(a, cn, xw[u]);
+        }
+      }
+    }
+  }
+  SF_TS(2);
+  // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
+  if (refine) {
+    // wave 0 waits for the selection and counts the tile
+    if (wave == 0) {
+      const bool ok0 = wait_published(a, tile_g & 63);
+      if (lane == 0) {
+        count_reader(a, tile_g & 63);
+        s_flag = ok0 ? 1 : 0;
+      }
+    }
+    lds_barrier();
+    // the tile gathers, per hit, the refinement words of its 4R rows (one request
+    // per hit and tile) and x at the hit channel into LDS
+    const int tb = (tile_g - o.tile_begin) * 4 * R * r, tw0 = tb >> 5, toff = tb & 31;
+    const int wt = (toff + 4 * R * r + 31) >> 5;  // words of the tile's window (<= WTM)
+    const int wpu = o.pool.unit_bytes >> 2;
+    const uint32_t* units = (const uint32_t*)o.pool.slots;
+    const bool resident = o.pool.resident != 0;
+    const bool any = s_flag != 0 && (resident || o.pool.unit2slot != nullptr);
+    if (any) {
+      const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (tile_g % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
+      for (int j = tid; j < ks; j += 256) {
+        const int k = (int)sf_get(hc + j);
+        const int slot = resident ? k : (int)sf_get(hc + ks * (1 + op) + j);
+        l_hk[j] = slot >= 0 ? k : -1;
+        if (slot >= 0) {
+          const uint32_t* u = units + (size_t)slot * wpu + tw0;
+#pragma unroll
+          for (int w = 0; w < WTM; ++w)
+            if (w < wt) l_hw[j * WTM + w] = tw0 + w < wpu ? u[w] : 0u;
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) l_hx[j * NB + bb] = sf_h2f(a.x[(size_t)(a.batch_off + bb) * K + k]);
+        }
+      }
+    }
+    lds_barrier();  // the hits, and the rows' scale words recorded by other lanes
+    SF_TS(3);
+    if (any) {
+      const int pw = toff + wave * R * r;  // this wave's first row in the window
+      for (int j = lane; j < ks; j += 64) {
+        const int k = l_hk[j];
+        if (k < 0) continue;
+        uint32_t wv[WTM];
+#pragma unroll
+        for (int w = 0; w < WTM; ++w) wv[w] = w < wt ? l_hw[j * WTM + w] : 0u;
+        float xq[NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) xq[bb] = l_hx[j * NB + bb];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const int p = pw + rr * r, wi = p >> 5;
+          uint32_t lo = wv[0], hi = wv[1 < WTM ? 1 : 0];
+#pragma unroll
+          for (int w = 1; w < WTM; ++w)
+            if (w == wi) {
+              lo = wv[w];
+              hi = w + 1 < WTM ? wv[w + 1 < WTM ? w + 1 : w] : 0u;
+            }
+          const uint32_t clo = bits64(lo, hi, p & 31, r);
+          const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) acc[bb][rr] = fmaf(xq[bb], sv, acc[bb][rr]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = wave_sum63(acc[bb][rr]);
+  if (lane == 63) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int row = row0 + rr;
+      if (row < o.n_out)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][rr];
+    }
+  }
+  SF_TS(4);
 }
 
 // ---- batched GEMV on MFMA (batch 3..16 per launch) --------------------------------
@@ -1321,6 +1841,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   }
 
   // resident GEMV
+  const PairK pk = C::consts();
   f4_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -1346,8 +1867,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
           f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const u32x4 bv = {C::pair(cw[u][t], 4 * m), C::pair(cw[u][t], 4 * m + 1), C::pair(cw[u][t], 4 * m + 2),
-                              C::pair(cw[u][t], 4 * m + 3)};
+            const u32x4 bv = {C::pair(cw[u][t], 4 * m, pk), C::pair(cw[u][t], 4 * m + 1, pk),
+                              C::pair(cw[u][t], 4 * m + 2, pk), C::pair(cw[u][t], 4 * m + 3, pk)};
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[m], __builtin_bit_cast(h8_t, bv), d, 0, 0, 0);
           }
           const float2 sc = sp[(wrow0 + 16 * t + n) * SSTR + gl];
@@ -1517,30 +2038,59 @@ sf_status launch_fused(GemvArgs& a, hipStream_t s) {
   return SF_OK;
 }
 
+int device_cus();
+
+template <class C, int B, int R, int NB>
+sf_status launch_split(GemvArgs& a, hipStream_t s) {
+  constexpr int D = R >= 8 ? 1 : 2;
+  const size_t lds = split_lds_bytes(a.k_in, C::PAIRS, C::CODES, NB, a.k_sel, R);
+  SF_REQUIRE(lds <= MAX_DYN_LDS, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  // the tiles wait for workgroup 0 only at their end, but a tile that has to wait
+  // for a free slot adds a whole tile time: when the grid does not fit the device
+  // at once, the fused kernel (selection in every workgroup) is used instead
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)gemv_split_kernel<C, B, R, NB, D>, 256, lds) !=
+          hipSuccess ||
+      occ < 1)
+    occ = 1;
+  if ((long)occ * device_cus() < (long)a.total_tiles + a.sel_wg &&
+      fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R) <= MAX_DYN_LDS) {
+    a.sel_wg = 0;
+    return launch_fused<C, B, R, NB>(a, s);
+  }
+  const dim3 grid((unsigned)(a.total_tiles + a.sel_wg));
+  hipLaunchKernelGGL((gemv_split_kernel<C, B, R, NB, D>), grid, dim3(256), lds, s, a);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+enum GemvKind { KIND_PERSISTENT = 0, KIND_FUSED = 1, KIND_SPLIT = 2 };
+
 template <class C, int B, int R>
-sf_status dispatch_nb(GemvArgs& a, int nb, bool fused, hipStream_t s) {
-  if (fused) return nb == 2 ? launch_fused<C, B, R, 2>(a, s) : launch_fused<C, B, R, 1>(a, s);
+sf_status dispatch_nb(GemvArgs& a, int nb, int kind, hipStream_t s) {
+  if (kind == KIND_SPLIT) return nb == 2 ? launch_split<C, B, R, 2>(a, s) : launch_split<C, B, R, 1>(a, s);
+  if (kind == KIND_FUSED) return nb == 2 ? launch_fused<C, B, R, 2>(a, s) : launch_fused<C, B, R, 1>(a, s);
   if (nb == 2) return launch_gemv<C, B, R, 2>(a, s);
   return launch_gemv<C, B, R, 1>(a, s);
 }
 
 template <class C, int B>
-sf_status dispatch_r(GemvArgs& a, int R, int nb, bool fused, hipStream_t s) {
+sf_status dispatch_r(GemvArgs& a, int R, int nb, int kind, hipStream_t s) {
   switch (R) {
-    case 1: return dispatch_nb<C, B, 1>(a, nb, fused, s);
-    case 2: return dispatch_nb<C, B, 2>(a, nb, fused, s);
-    case 4: return dispatch_nb<C, B, 4>(a, nb, fused, s);
-    default: return dispatch_nb<C, B, 8>(a, nb, fused, s);
+    case 1: return dispatch_nb<C, B, 1>(a, nb, kind, s);
+    case 2: return dispatch_nb<C, B, 2>(a, nb, kind, s);
+    case 4: return dispatch_nb<C, B, 4>(a, nb, kind, s);
+    default: return dispatch_nb<C, B, 8>(a, nb, kind, s);
   }
 }
 
-sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, bool fused, hipStream_t s) {
+sf_status dispatch_b(GemvArgs& a, int b, int R, int nb, int kind, hipStream_t s) {
   switch (b) {
-    case 1: return dispatch_r<CodecPow2<1>, 1>(a, R, nb, fused, s);
-    case 2: return dispatch_r<CodecPow2<2>, 2>(a, R, nb, fused, s);
-    case 3: return dispatch_r<CodecStream<3>, 3>(a, R, nb, fused, s);
-    case 4: return dispatch_r<CodecPow2<4>, 4>(a, R, nb, fused, s);
-    case 8: return dispatch_r<CodecPow2<8>, 8>(a, R, nb, fused, s);
+    case 1: return dispatch_r<CodecPow2<1>, 1>(a, R, nb, kind, s);
+    case 2: return dispatch_r<CodecPow2<2>, 2>(a, R, nb, kind, s);
+    case 3: return dispatch_r<CodecStream<3>, 3>(a, R, nb, kind, s);
+    case 4: return dispatch_r<CodecPow2<4>, 4>(a, R, nb, kind, s);
+    case 8: return dispatch_r<CodecPow2<8>, 8>(a, R, nb, kind, s);
     default:
       sf_set_error("sf_refined_gemv: resident width b must be 1, 2, 3, 4 or 8");
       return SF_EUNSUPPORTED;
@@ -1687,7 +2237,7 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   int64_t rows_total = 0;
   for (int i = 0; i < n_ops; ++i) rows_total += ops[i].w.n_out;
   if (rpw != 1 && rpw != 2 && rpw != 4 && rpw != 8) {
-    if (env_int("SF_GEMV_FUSED", 1) != 0)  // one row tile per workgroup: about one per CU, 8 rows a wave at most
+    if (env_int("SF_GEMV_SPLIT", 1) != 0 || env_int("SF_GEMV_FUSED", 1) != 0)  // one row tile per workgroup, 8 rows a wave at most
       rpw = rows_total <= 8192 ? 4 : 8;
     else
       rpw = rows_total <= 8192 ? 2 : (rows_total <= 16384 ? 4 : 8);
@@ -1735,15 +2285,24 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.total_tiles = tiles;
   hipStream_t s = (hipStream_t)stream;
   const int cpc = codes_per_chunk(f.b);
-  // Batch 1-2 without the batched kernel: the fused kernel selects the channels in
-  // every workgroup (SF_GEMV_FUSED=0 selects the separate selection launch and the
-  // persistent kernel).  With more rows than one launch takes, the selection over
-  // all rows comes from the selection launch.
-  const bool fused = !mfma && env_int("SF_GEMV_FUSED", 1) != 0 &&
-                     fused_lds_bytes((int)K, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS;
-  const int max_nb = fused ? (fused_lds_bytes((int)K, cpc, 2, k_sel, rpw) <= 64 * 1024 ? 2 : 1)
-                           : (gemv_lds_bytes((int)K, cpc, 2, n_ops, k_sel, rpw, false) <= 64 * 1024 ? 2 : 1);
-  const bool one_launch = fused && batch <= max_nb;
+  // Batch 1-2 without the batched kernel: by default the split kernel (workgroup 0
+  // selects while the others stream; SF_GEMV_SPLIT=0 falls back to the fused
+  // kernel, which selects in every workgroup, and SF_GEMV_FUSED=0 then to the
+  // separate selection launch and the persistent kernel).  With more rows than one
+  // launch takes, the selection over all rows comes from the selection launch.
+  int kind = KIND_PERSISTENT;
+  if (!mfma) {
+    if (env_int("SF_GEMV_SPLIT", 1) != 0 && split_lds_bytes((int)K, cpc / 2, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS &&
+        (size_t)SPLIT_COPIES * split_copy_words(k_sel, n_ops) <= sizeof(((WsControl*)nullptr)->hit) / 4)
+      kind = KIND_SPLIT;
+    else if (env_int("SF_GEMV_FUSED", 1) != 0 && fused_lds_bytes((int)K, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS)
+      kind = KIND_FUSED;
+  }
+  const size_t lds2 = kind == KIND_SPLIT   ? split_lds_bytes((int)K, cpc / 2, cpc, 2, k_sel, rpw)
+                      : kind == KIND_FUSED ? fused_lds_bytes((int)K, cpc, 2, k_sel, rpw)
+                                           : gemv_lds_bytes((int)K, cpc, 2, n_ops, k_sel, rpw, false);
+  const int max_nb = lds2 <= 64 * 1024 ? 2 : 1;
+  const bool one_launch = kind != KIND_PERSISTENT && batch <= max_nb;
   if (k_sel > 0 && !one_launch) {
     hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(SEL_NT), 0, s, a);
     SF_LAUNCH_CHECK();
@@ -1764,14 +2323,16 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     return SF_OK;
   }
   // two batch rows per launch when both fit the LDS staging of x, else one
-  if (fused) {
+  if (kind != KIND_PERSISTENT) {
     a.report = one_launch ? 1 : 0;
     if (!one_launch && k_sel > 0) a.sel_in = a.ws_sel;
   }
+  a.sel_wg = (kind == KIND_SPLIT && k_sel > 0) ? 1 : 0;
+  a.ctl = (uint32_t*)ws->base;
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;
-    sf_status st = dispatch_b(a, f.b, rpw, nb, fused, s);
+    sf_status st = dispatch_b(a, f.b, rpw, nb, kind, s);
     if (st != SF_OK) return st;
   }
   return SF_OK;

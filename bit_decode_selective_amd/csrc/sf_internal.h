@@ -39,6 +39,13 @@ struct WsControl {
   uint32_t timeout;    // set when a bounded device wait gave up
   uint32_t pad[61];    // keeps the data area 256-byte aligned
   uint32_t row_ctr[1024];  // batched GEMV: slices finished per row block (last one resets)
+  // split GEMV: the published selection in SPLIT_COPIES copies (word j = channel,
+  // then per matrix word k_sel * (1 + op) + j = slot), valid while sel_flag is
+  // raised; per group g = tile mod 64, flag word 32 g and reader count word 32 g
+  // (one 128-byte line each, so that no single line takes every tile's requests)
+  uint32_t hit[32768];
+  uint32_t sel_flag[64 * 32];
+  uint32_t rd_ctr[64 * 32];
 };
 
 struct sf_workspace {

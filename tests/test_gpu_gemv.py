@@ -30,16 +30,21 @@ def _run(qws, x, k_sel, sel_in=None, cache="resident"):
     return [y.cpu().numpy() for y in ys], sel.cpu().numpy().tolist(), [h.cpu().numpy() for h in hits]
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
+KINDS = {"split": ("1", "1"), "fused": ("0", "1"), "persistent": ("0", "0")}
+
+
+@pytest.mark.parametrize("kind", list(KINDS))
 @pytest.mark.parametrize("rpw", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("b,r", [(2, 2), (3, 1), (4, 4), (1, 3), (8, 0), (2, 0)])
 @pytest.mark.parametrize("batch", [1, 2, 3])
-def test_small_shapes(b, r, batch, rpw, fused, monkeypatch):
-    """Selection in every workgroup (fused) or in its own launch; 1-8 rows per wave;
-    one launch for batch 1-2; b = 3 at batch 3 takes the selection launch and two
+def test_small_shapes(b, r, batch, rpw, kind, monkeypatch):
+    """Selection by one workgroup while the others stream (split), in every
+    workgroup (fused) or in its own launch (persistent); 1-8 rows per wave; one
+    launch for batch 1-2; b = 3 at batch 3 takes the selection launch and two
     launches, the others the batched kernel."""
     monkeypatch.setenv("SF_GEMV_ROWS_PER_WAVE", rpw)
-    monkeypatch.setenv("SF_GEMV_FUSED", fused)
+    monkeypatch.setenv("SF_GEMV_SPLIT", KINDS[kind][0])
+    monkeypatch.setenv("SF_GEMV_FUSED", KINDS[kind][1])
     # 200 rows is ragged against every row tile; channel-major refinement units need
     # n_out * r to be a multiple of 32, so the odd-r formats use 224 rows
     n_out = 200 if r in (0, 4) else 224
