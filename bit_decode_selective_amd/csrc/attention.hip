@@ -494,6 +494,25 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
       qf[h][d] = h2f16(a.q[((size_t)bi * a.n_q + kvh * G + h) * HD + d]);
     }
 
+  // this thread's logits (TPT consecutive tokens per head), requested before the
+  // split statistics are merged so that the two round trips overlap
+  const int tb = c0 + TPT * tid;
+  f4_t l4p[G];
+  if (ks > 0 && a.sel_in == nullptr) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + tb;
+      l4p[h] = f4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (tb + 3 < T) {
+        l4p[h] = *(const f4_t*)lr;
+      } else {
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+          if (tb + i < T) l4p[h][i] = lr[i];
+      }
+    }
+  }
+
   // ---- softmax max / sum per head from the split statistics ----
   {
     constexpr int NJ = SEL_T / G;
@@ -574,21 +593,12 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   if (a.sel_in == nullptr) {
     // ---- scores of this chunk's tokens (TPT consecutive per thread) ----
     uint32_t key[TPT];
-    const int tb = c0 + TPT * tid;
     float lgk[G][TPT];  // this thread's logits (for the max over the unselected tokens)
     {
       float sc[TPT] = {};
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + tb;
-        f4_t l4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (tb + 3 < T) {
-          l4 = *(const f4_t*)lr;
-        } else {
-#pragma unroll
-          for (int i = 0; i < TPT; ++i)
-            if (tb + i < T) l4[i] = lr[i];
-        }
+        const f4_t l4 = l4p[h];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
           sc[i] += __expf(l4[i] - s_m[h]) * s_iz[h];
@@ -719,7 +729,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
       if (t >= 0 && t < CB) atomicOr(&selbits[t >> 5], 1u << (t & 31));
     }
     __syncthreads();
-    const int tb = c0 + TPT * tid;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int t = tb + i;
