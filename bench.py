@@ -45,13 +45,13 @@ HBM_PEAK_GBPS = 8000.0
 # only while the kernel source still has the hash it was measured on.
 DOMINANT = {
     "tag": "gateup",
-    "kernel": "gemv_kernel (fused gate/up, 2 x 14336 x 4096)",
+    "kernel": "gemv_fused_kernel<CodecPow2<2>, 2, 8, 1, 1, 2> (gate/up, 2 x 14336 x 4096, 896 x 256)",
     "source": "bit_decode_selective_amd/csrc/gemv.hip",
 }
 TRAFFIC = {
-    "source_sha256": "b79993cf88aee4cc1a4ab517df91f368adfc06cb0d5058f8aac2c8274668fd3b",
-    "fetch_bytes": 40645820,
-    "write_bytes": 143565,
+    "source_sha256": "2d8a6cb99fdfa0419968e2acadd2487a195f803f28ada8c083759d2038974bc1",
+    "fetch_bytes": 40469682,
+    "write_bytes": 114688,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
 HIDDEN, FFN, NQ, NKV, HD = 4096, 14336, 32, 8, 128
@@ -515,15 +515,21 @@ def main():
         calls0 = model.build_calls(refined=False)
         unref_ms = time_steps(model, calls0, args.steps, args.warmup, use_graph)
         print(f"# unrefined step {unref_ms:.3f} ms", file=sys.stderr, flush=True)
-    # dominant kernel: fused gate/up GEMV, HIP events around each launch (eager pass)
+    # dominant kernel: the refined gate/up GEMV of layer 0, launched DOM_REPS times back
+    # to back between two HIP events on its stream (the call is idempotent)
     stream = torch.cuda.Stream(device=model.dev)
-    evs = []
+    dom = [c for c in calls if c[2] == DOMINANT["tag"]][0]
+    DOM_REPS = 50
     with torch.cuda.stream(stream):
-        for _ in range(max(1, args.steps // 4)):
-            model.enqueue(calls, stream, events=evs, tag=DOMINANT["tag"])
-            model.fill(stream)
+        for _ in range(5):
+            model.enqueue([dom], stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(DOM_REPS):
+            model.enqueue([dom], stream)
+        e1.record(stream)
     torch.cuda.synchronize()
-    dom_us = 1000.0 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    dom_us = 1000.0 * e0.elapsed_time(e1) / DOM_REPS
     dom_bytes = model.dominant_bytes(DOMINANT["tag"])
     step_bytes = model.step_bytes(True)
     gbps = step_bytes / (ms * 1e-3) / 1e9
