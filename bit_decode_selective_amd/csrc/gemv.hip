@@ -389,6 +389,8 @@ __global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
 // Dynamic LDS: x pairs [NB][K/2] | x chunk sums [NB][nchunks] | scale words
 // [4][R][K/128] | (selection [k_sel] | slots [n_ops][k_sel] when they fit).
 constexpr int HPF = 8;  // hits per lane whose refinement words are requested at tile start
+// Words of a tile's refinement window: 4R rows of up to 7 bits, plus misalignment.
+__host__ __device__ constexpr int wtm_of(int R) { return (31 + 4 * R * 7 + 31) / 32; }
 
 template <class C, int R>
 __device__ __forceinline__ void load_chunk(const GemvOpDev& o, int row0, int c, size_t rowbytes, int ngr,
@@ -823,383 +825,25 @@ __device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t* total)
   return ex;
 }
 
-// ---- batch-1/2 GEMV with the selection in every workgroup ----------------------
-// One row tile per workgroup (4 waves x R rows).  All code loads of the tile are
-// issued first (a window of D chunks per lane when a row has more than 64 chunks).
-// While they are in flight the workgroup stages x in LDS and selects the channels
-// itself, exactly as the selection workgroup does: keys max-over-batch |x| as
-// 15-bit fp16 patterns (kept in LDS in channel order), the k-th largest by two
-// histogram passes (one histogram per wave), the selected channels in channel
-// order by ballot prefixes.  Each lane then looks up the slots of its hits and
-// requests their refinement words for its wave's rows; the resident dot products
-// run meanwhile and the deltas are added before the row sums are written.  The
-// first workgroup of each matrix reports its hits and lookup log, workgroup 0 the
-// selection.
-template <class C, int B, int R, int NB, int D, int XB>
-__global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
-  extern __shared__ uint32_t smem[];
-  __shared__ uint32_t whist[4][256];
-  __shared__ uint32_t whist2[4][128];
-  __shared__ uint32_t s_cnt[4 * (MAX_SEL_K / 2048)];
-  __shared__ int lds[24];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // each wave clears the histograms it counts into (its own, before its atomics)
-  for (int i = lane; i < 256; i += 64) whist[wave][i] = 0u;
-  for (int i = lane; i < 128; i += 64) whist2[wave][i] = 0u;
-  const int K = a.k_in, nchunks = K / C::CODES, xpairs = K / 2, ngr = K / 128, n8 = K / 8;
-  const int ks = a.k_sel;
-  const bool refine = ks > 0;
-  uint32_t* xs = smem;                                         // [NB][K/2] fp16 pairs
-  float* xsum = (float*)(smem + NB * xpairs);                  // [NB][nchunks]
-  uint32_t* keys = (uint32_t*)(xsum + NB * ((nchunks + 3) & ~3));  // [K/2]: channel-order key pairs
-  uint32_t* s_szw = keys + (refine ? xpairs : 0);              // [4][R][ngr]
-  int32_t* l_sel = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [ks]
-  uint32_t* bm_sure = (uint32_t*)(l_sel + (refine ? ks : 0));      // [K/32]: keys above the boundary bin
-  uint32_t* bm_bnd = bm_sure + (refine ? K / 32 : 0);               // [K/32]: keys in the boundary bin
-  const bool computed = refine && !a.sel_in && ks < K;             // the selection is computed here
-  const int tile_g = blockIdx.x;
-  const int op = op_of_tile(a, tile_g);
-  const GemvOpDev& o = a.ops[op];
-  const int row0 = (tile_g - o.tile_begin) * 4 * R + wave * R;
-  const size_t rowbytes = (size_t)K * B / 8;
-  SF_TS(0);
-
-  // x first (the selection needs it early; loads complete in order), then the
-  // tile's codes; both unconditional (clamped addresses, unused values), so that
-  // staging x waits for the x loads only
-  u32x4 xv0[NB][XB];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
-#pragma unroll
-    for (int i = 0; i < XB; ++i) xv0[bb][i] = xr[min(256 * i + tid, n8 - 1)];
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code loads
-  // the first D chunks of every row of this lane
-  uint32_t cw[D][R][C::WORDS];
-  uint32_t szw[D][R];
-#pragma unroll
-  for (int u = 0; u < D; ++u) load_chunk_clamped<C, R>(o, row0, min(lane + 64 * u, nchunks - 1), rowbytes, ngr, cw[u], szw[u]);
-
-  // x in pair order; chunk sums; selection keys in channel order
-  uint16_t* xh = (uint16_t*)xs;
-  auto stage = [&](const u32x4 (&xv)[NB][XB], int m0) {
-    constexpr int TPC = C::CODES / 8;  // threads per chunk
-#pragma unroll
-    for (int i = 0; i < XB; ++i) {
-      const int m = m0 + 256 * i + tid;
-      u32x4 kv = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        float part = 0.f;
-        if (m < n8) {
-          const uint32_t wds[4] = {xv[bb][i].x, xv[bb][i].y, xv[bb][i].z, xv[bb][i].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x2 = wds[q] & 0x7FFF7FFFu;
-            kv[q] = max(kv[q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[q] >> 16, x2 >> 16) << 16);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int k = 8 * m + e;
-            const int c = k / C::CODES, kk = k - c * C::CODES;
-            int j, hi;
-            C::locate(kk, &j, &hi);
-            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
-            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
-            part += (float)__builtin_bit_cast(_Float16, hb);
-          }
-        }
-#pragma unroll
-        for (int o2 = TPC / 2; o2 >= 1; o2 >>= 1) part += __shfl_xor(part, o2, TPC);
-        if (m < n8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
-      }
-      if (refine && m < n8) *(u32x4*)(keys + 4 * m) = kv;
-      if (computed && m < n8)  // selection pass 1: top 8 key bits, one histogram per wave
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
-          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
-        }
-    }
-  };
-  stage(xv0, 0);
-  for (int m0 = 256 * XB; m0 < n8; m0 += 256 * XB) {  // x longer than XB loads a thread
-    u32x4 xv[NB][XB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
-#pragma unroll
-      for (int i = 0; i < XB; ++i) xv[bb][i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
-    }
-    stage(xv, m0);
-  }
-  SF_TS(1);
-
-  // the selection, ascending, into l_sel
-  if (refine) {
-    if (a.sel_in) {
-      for (int j = tid; j < ks; j += 256) l_sel[j] = a.sel_in[j];
-    } else if (ks >= K) {
-      for (int j = tid; j < ks; j += 256) l_sel[j] = j;
-    } else {
-      lds_barrier();  // keys and the pass-1 histograms
-      // every wave finds the boundary bin itself (no further barrier)
-      int b1, above1;
-      wave_threshold4(whist, 256, ks, &b1, &above1);
-      SF_TS(5);
-      // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
-      // (all taken) and in bin b1 (decided by the low bits)
-      {
-        uint8_t* bs = (uint8_t*)bm_sure;
-        uint8_t* bb = (uint8_t*)bm_bnd;
-        for (int m = tid; m < n8; m += 256) {
-          const u32x4 kv = *(const u32x4*)(keys + 4 * m);
-          uint32_t sure = 0u, bnd = 0u;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const int bin = (int)(key >> 7);
-            sure |= (uint32_t)(bin > b1) << e;
-            if (bin == b1) {
-              bnd |= 1u << e;
-              atomicAdd(&whist2[wave][key & 127u], 1u);
-            }
-          }
-          bs[m] = (uint8_t)sure;
-          bb[m] = (uint8_t)bnd;
-        }
-      }
-      lds_barrier();
-      int b2, above2;
-      wave_threshold4(whist2, 128, ks - above1, &b2, &above2);
-      SF_TS(8);
-      const uint32_t need = (uint32_t)(ks - above1 - above2);  // keys equal to T taken, lowest channels first
-      // compaction in channel order: thread t owns words [t W, t W + W) of the
-      // bitmaps; taken = above-bin | (boundary with low bits > b2) | the first
-      // `need` boundary keys with low bits == b2
-      const int nw = K / 32, W = (nw + 255) / 256;
-      const uint16_t* key16 = (const uint16_t*)keys;
-      uint32_t sg[4], eqm[4], cs = 0u, ce = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sg[i] = eqm[i] = 0u;
-        const int w = tid * W + i;
-        if (i < W && w < nw) {
-          uint32_t bnd = bm_bnd[w], gtw = 0u, eqw = 0u;
-          while (bnd) {
-            const int bit = __builtin_ctz(bnd);
-            bnd &= bnd - 1u;
-            const uint32_t lo = key16[32 * w + bit] & 127u;
-            gtw |= (uint32_t)(lo > (uint32_t)b2) << bit;
-            eqw |= (uint32_t)(lo == (uint32_t)b2) << bit;
-          }
-          sg[i] = bm_sure[w] | gtw;
-          eqm[i] = eqw;
-          cs += __popc(sg[i]);
-          ce += __popc(eqm[i]);
-        }
-      }
-      uint32_t ts, te;
-      uint32_t sbefore = wave_excl_sum8(cs, &ts), ebefore = wave_excl_sum8(ce, &te);
-      if (lane == 0) s_cnt[wave] = ts | (te << 16);
-      lds_barrier();
-      for (int w = 0; w < wave; ++w) {
-        sbefore += s_cnt[w] & 0xFFFFu;
-        ebefore += s_cnt[w] >> 16;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t all = sg[i] | eqm[i];
-        while (all) {
-          const int bit = __builtin_ctz(all);
-          all &= all - 1u;
-          const int c = 32 * (tid * W + i) + bit;
-          if ((sg[i] >> bit) & 1u) {
-            l_sel[sbefore + min(ebefore, need)] = c;
-            ++sbefore;
-          } else {
-            if (ebefore < need) l_sel[sbefore + ebefore] = c;
-            ++ebefore;
-          }
-        }
-      }
-    }
-  }
-  lds_barrier();  // x, chunk sums and the selection
-  SF_TS(2);
-
-  const float scl = (float)(1u << (a.r + B));
-  const int r = a.r;
-  uint32_t* szrow = s_szw + wave * R * ngr;  // this wave's rows' scale words, [R][ngr]
-  // the wave's R rows occupy bits [row0 * r, (row0 + R) * r) of every unit
-  const int ubit = row0 * r, uwi = ubit >> 5, uoff = ubit & 31;
-  const int wpu = o.pool.unit_bytes >> 2;
-  const uint32_t* units = (const uint32_t*)o.pool.slots;
-  const int32_t* u2s = o.pool.unit2slot;
-  // slots of this lane's first HPF hits and their refinement words for the wave's rows
-  int pslot[HPF];
-  uint32_t pw0[HPF], pw1[HPF];
-  if (refine) {
-#pragma unroll
-    for (int i = 0; i < HPF; ++i) {
-      const int j = lane + 64 * i;
-      pslot[i] = j < ks ? (o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1)) : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < HPF; ++i) {
-      pw0[i] = pw1[i] = 0u;
-      if (pslot[i] >= 0) {
-        const uint32_t* u = units + (size_t)pslot[i] * wpu;
-        if (uwi < wpu) pw0[i] = u[uwi];
-        if (uwi + 1 < wpu) pw1[i] = u[uwi + 1];
-      }
-    }
-  }
-
-  const PairK pk = C::consts();
-  float acc[NB][R];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = 0.f;
-  for (int c0 = 0; c0 < nchunks; c0 += 64 * D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int c = c0 + 64 * u + lane;
-      if (c < nchunks) {
-        if (refine && (c * C::CODES) % 128 == 0)
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[u][rr];
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
-          float d[R];
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
-#pragma unroll 2
-          for (int jb = 0; jb < C::PAIRS / 4; ++jb) {
-            const u32x4 xv = xp[jb];
-#pragma unroll
-            for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q, pk)), as_h2(xv[q]), d[rr], false);
-          }
-          const float X = xsum[bb * nchunks + c];
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) {
-            const float sv = sf_h2f(szw[u][rr]), zv = sf_h2f(szw[u][rr] >> 16);
-            acc[bb][rr] += (sv * scl) * (d[rr] - X) + zv * X;
-          }
-        }
-        const int cn = c + 64 * D;
-        if (cn < nchunks) load_chunk_clamped<C, R>(o, row0, cn, rowbytes, ngr, cw[u], szw[u]);
-      }
-    }
-  }
-  SF_TS(3);
-  // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
-  if (refine) {
-    // the rows' scale words were recorded by other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int j = lane; j < ks; j += 64) {
-      const int i = (j - lane) >> 6;
-      int slot;
-      uint32_t w0, w1, w2 = 0u;
-      if (i < HPF) {
-        slot = pslot[0];
-        w0 = pw0[0];
-        w1 = pw1[0];
-#pragma unroll
-        for (int q = 1; q < HPF; ++q)
-          if (q == i) {
-            slot = pslot[q];
-            w0 = pw0[q];
-            w1 = pw1[q];
-          }
-        if (slot >= 0 && uoff + R * r > 64 && uwi + 2 < wpu) w2 = units[(size_t)slot * wpu + uwi + 2];
-      } else {
-        slot = o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1);
-        w0 = w1 = 0u;
-        if (slot >= 0) {
-          const uint32_t* u = units + (size_t)slot * wpu;
-          if (uwi < wpu) w0 = u[uwi];
-          if (uwi + 1 < wpu) w1 = u[uwi + 1];
-          if (uwi + 2 < wpu) w2 = u[uwi + 2];
-        }
-      }
-      if (slot < 0) continue;
-      const int k = l_sel[j];
-      const int c = k / C::CODES, kk = k - c * C::CODES;
-      int jj, hi;
-      C::locate(kk, &jj, &hi);
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
-        const int p = uoff + rr * r;
-        const uint32_t clo = p + r <= 64 ? bits64(w0, w1, p, r) : bits64(w1, w2, p - 32, r);
-        const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
-          acc[bb][rr] = fmaf(hi ? (float)xh.y : (float)xh.x, sv, acc[bb][rr]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      float v = acc[bb][rr];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      acc[bb][rr] = v;
-    }
-  if (lane == 0) {
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      const int row = row0 + rr;
-      if (row < o.n_out)
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][rr];
-    }
-  }
-  // reports (once per call): the selection, each matrix's hits and lookup log
-  if (refine && a.report) {
-    if (tile_g == 0 && a.sel_out)
-      for (int j = tid; j < ks; j += 256) a.sel_out[j] = l_sel[j];
-    if (tile_g == o.tile_begin && (o.hit_out || o.pool.log_count)) {
-      if (tid == 0) {
-        int base = -1;
-        if (o.pool.log_count) {
-          const uint32_t bse = atomicAdd(o.pool.log_count, (uint32_t)ks);
-          base = (bse + (uint32_t)ks <= (uint32_t)o.pool.log_cap) ? (int)bse : -1;
-        }
-        lds[22] = base;
-      }
-      lds_barrier();
-      const int base = lds[22];
-      for (int j = tid; j < ks; j += 256) {
-        const int k = l_sel[j];
-        const int slot = o.pool.resident ? k : (u2s ? u2s[k] : -1);
-        if (o.hit_out) o.hit_out[j] = slot;
-        if (base >= 0) {
-          o.pool.log_units[base + j] = k;
-          o.pool.log_slots[base + j] = slot;
-        }
-      }
-    }
-  }
-  SF_TS(4);
-}
 
 size_t fused_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
   size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
   if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel + (size_t)(k_in / 16);
   return w * 4;
+}
+
+size_t split_sel_lds_words(int k_in, int k_sel) {
+  return (size_t)(k_in / 2) + 2 * (size_t)(k_in / 32) + (((size_t)k_sel + 3) & ~(size_t)3) + 4 * 256 + 4 * 128 + 16;
+}
+
+// The fused kernel with workgroup 0 selecting: x staged as in the fused kernel, the
+// hits (channel, x, the tile's window words) after the scale words; the selecting
+// workgroup's own layout may be larger.
+size_t fused_sw_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
+  size_t tile = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
+  if (k_sel > 0) tile += (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel * (1 + nb + wtm_of(rpw));
+  const size_t sel = k_sel > 0 ? split_sel_lds_words(k_in, k_sel) : 0;
+  return std::max(tile, sel) * 4;
 }
 
 // ---- batch-1/2 GEMV with one selecting workgroup ---------------------------------
@@ -1451,6 +1095,465 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
   SF_TS(13);
 }
 
+
+// Refinement of one row tile from workgroup 0's published selection: wave 0 waits
+// for its flag group and counts the tile; the tile gathers per hit the words that
+// hold its 4R rows' refinement bits (one request per hit and tile) and x at the hit
+// into LDS; each wave adds x_k * s[row][k/128] * c_lo[row][k] for its R rows.
+// szrow: this wave's rows' scale words [R][K/128] (LDS, complete for all lanes
+// before the first barrier here); sflag: one LDS word.
+template <class C, int R, int NB, int WTM>
+__device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvOpDev& o, int op, int tile_g, int row0,
+                                                  const uint32_t* szrow, int32_t* l_hk, float* l_hx, uint32_t* l_hw,
+                                                  float (&acc)[NB][R], int* sflag) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = a.k_sel, K = a.k_in, ngr = K / 128, r = a.r;
+  if (wave == 0) {
+    const bool ok0 = wait_published(a, tile_g & 63);
+    if (lane == 0) {
+      count_reader(a, tile_g & 63);
+      *sflag = ok0 ? 1 : 0;
+    }
+  }
+  lds_barrier();
+  const int tb = (tile_g - o.tile_begin) * 4 * R * r, tw0 = tb >> 5, toff = tb & 31;
+  const int wt = (toff + 4 * R * r + 31) >> 5;  // words of the tile's window (<= WTM)
+  const int wpu = o.pool.unit_bytes >> 2;
+  const uint32_t* units = (const uint32_t*)o.pool.slots;
+  const bool resident = o.pool.resident != 0;
+  const bool any = *sflag != 0 && (resident || o.pool.unit2slot != nullptr);
+  if (any) {
+    const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (tile_g % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
+    for (int j = tid; j < ks; j += 256) {
+      const int k = (int)sf_get(hc + j);
+      const int slot = resident ? k : (int)sf_get(hc + ks * (1 + op) + j);
+      l_hk[j] = slot >= 0 ? k : -1;
+      if (slot >= 0) {
+        const uint32_t* u = units + (size_t)slot * wpu + tw0;
+#pragma unroll
+        for (int w = 0; w < WTM; ++w)
+          if (w < wt) l_hw[j * WTM + w] = tw0 + w < wpu ? u[w] : 0u;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) l_hx[j * NB + bb] = sf_h2f(a.x[(size_t)(a.batch_off + bb) * K + k]);
+      }
+    }
+  }
+  lds_barrier();  // the hits
+  SF_TS(5);
+  if (!any) return;
+  const int pw = toff + wave * R * r;  // this wave's first row in the window
+  for (int j = lane; j < ks; j += 64) {
+    const int k = l_hk[j];
+    if (k < 0) continue;
+    uint32_t wv[WTM];
+#pragma unroll
+    for (int w = 0; w < WTM; ++w) wv[w] = w < wt ? l_hw[j * WTM + w] : 0u;
+    float xq[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) xq[bb] = l_hx[j * NB + bb];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int p = pw + rr * r, wi = p >> 5;
+      uint32_t lo = wv[0], hi = wv[1 < WTM ? 1 : 0];
+#pragma unroll
+      for (int w = 1; w < WTM; ++w)
+        if (w == wi) {
+          lo = wv[w];
+          hi = w + 1 < WTM ? wv[w + 1 < WTM ? w + 1 : w] : 0u;
+        }
+      const uint32_t clo = bits64(lo, hi, p & 31, r);
+      const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) acc[bb][rr] = fmaf(xq[bb], sv, acc[bb][rr]);
+    }
+  }
+}
+
+// ---- batch-1/2 GEMV with the selection in every workgroup ----------------------
+// One row tile per workgroup (4 waves x R rows).  All code loads of the tile are
+// issued first (a window of D chunks per lane when a row has more than 64 chunks).
+// While they are in flight the workgroup stages x in LDS and selects the channels
+// itself, exactly as the selection workgroup does: keys max-over-batch |x| as
+// 15-bit fp16 patterns (kept in LDS in channel order), the k-th largest by two
+// histogram passes (one histogram per wave), the selected channels in channel
+// order by ballot prefixes.  Each lane then looks up the slots of its hits and
+// requests their refinement words for its wave's rows; the resident dot products
+// run meanwhile and the deltas are added before the row sums are written.  The
+// first workgroup of each matrix reports its hits and lookup log, workgroup 0 the
+// selection.
+// SW = true: workgroup 0 selects for all (as in the split kernel) and the tiles
+// take the selection from its published words after their resident dot products.
+template <class C, int B, int R, int NB, int D, int XB, bool SW>
+__global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t whist[4][256];
+  __shared__ uint32_t whist2[4][128];
+  __shared__ uint32_t s_cnt[4 * (MAX_SEL_K / 2048)];
+  __shared__ int lds[24];
+  if constexpr (SW) {
+    if (blockIdx.x == 0) {
+      __builtin_amdgcn_s_setprio(3);
+      split_select_and_publish(a, smem);
+      __builtin_amdgcn_s_setprio(0);
+      split_retire(a);
+      return;
+    }
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // each wave clears the histograms it counts into (its own, before its atomics)
+  for (int i = lane; i < 256; i += 64) whist[wave][i] = 0u;
+  for (int i = lane; i < 128; i += 64) whist2[wave][i] = 0u;
+  const int K = a.k_in, nchunks = K / C::CODES, xpairs = K / 2, ngr = K / 128, n8 = K / 8;
+  const int ks = a.k_sel;
+  const bool refine = ks > 0;
+  uint32_t* xs = smem;                                         // [NB][K/2] fp16 pairs
+  float* xsum = (float*)(smem + NB * xpairs);                  // [NB][nchunks]
+  uint32_t* keys = (uint32_t*)(xsum + NB * ((nchunks + 3) & ~3));  // [K/2]: channel-order key pairs
+  uint32_t* s_szw = keys + ((refine && !SW) ? xpairs : 0);     // [4][R][ngr]
+  int32_t* l_sel = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [ks]
+  uint32_t* bm_sure = (uint32_t*)(l_sel + (refine ? ks : 0));      // [K/32]: keys above the boundary bin
+  uint32_t* bm_bnd = bm_sure + (refine ? K / 32 : 0);               // [K/32]: keys in the boundary bin
+  const bool computed = !SW && refine && !a.sel_in && ks < K;      // the selection is computed here
+  const int tile_g = blockIdx.x - (SW ? 1 : 0);
+  const int op = op_of_tile(a, tile_g);
+  const GemvOpDev& o = a.ops[op];
+  const int row0 = (tile_g - o.tile_begin) * 4 * R + wave * R;
+  const size_t rowbytes = (size_t)K * B / 8;
+  SF_TS(0);
+
+  // x first (the selection needs it early; loads complete in order), then the
+  // tile's codes; both unconditional (clamped addresses, unused values), so that
+  // staging x waits for the x loads only
+  u32x4 xv0[NB][XB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+#pragma unroll
+    for (int i = 0; i < XB; ++i) xv0[bb][i] = xr[min(256 * i + tid, n8 - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code loads
+  // the first D chunks of every row of this lane
+  uint32_t cw[D][R][C::WORDS];
+  uint32_t szw[D][R];
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_chunk_clamped<C, R>(o, row0, min(lane + 64 * u, nchunks - 1), rowbytes, ngr, cw[u], szw[u]);
+
+  // x in pair order; chunk sums; selection keys in channel order
+  uint16_t* xh = (uint16_t*)xs;
+  auto stage = [&](const u32x4 (&xv)[NB][XB], int m0) {
+    constexpr int TPC = C::CODES / 8;  // threads per chunk
+#pragma unroll
+    for (int i = 0; i < XB; ++i) {
+      const int m = m0 + 256 * i + tid;
+      u32x4 kv = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        float part = 0.f;
+        if (m < n8) {
+          const uint32_t wds[4] = {xv[bb][i].x, xv[bb][i].y, xv[bb][i].z, xv[bb][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x2 = wds[q] & 0x7FFF7FFFu;
+            kv[q] = max(kv[q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[q] >> 16, x2 >> 16) << 16);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = 8 * m + e;
+            const int c = k / C::CODES, kk = k - c * C::CODES;
+            int j, hi;
+            C::locate(kk, &j, &hi);
+            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
+            part += (float)__builtin_bit_cast(_Float16, hb);
+          }
+        }
+        part = group_sum<TPC>(part);
+        if (m < n8 && (m % TPC) == 0) xsum[bb * nchunks + m / TPC] = part;
+      }
+      if (!SW && refine && m < n8) *(u32x4*)(keys + 4 * m) = kv;
+      if (computed && m < n8)  // selection pass 1: top 8 key bits, one histogram per wave
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
+          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
+        }
+    }
+  };
+  stage(xv0, 0);
+  for (int m0 = 256 * XB; m0 < n8; m0 += 256 * XB) {  // x longer than XB loads a thread
+    u32x4 xv[NB][XB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)(a.batch_off + bb) * K);
+#pragma unroll
+      for (int i = 0; i < XB; ++i) xv[bb][i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
+    }
+    stage(xv, m0);
+  }
+  SF_TS(1);
+
+  // the selection, ascending, into l_sel
+  if (!SW && refine) {
+    if (a.sel_in) {
+      for (int j = tid; j < ks; j += 256) l_sel[j] = a.sel_in[j];
+    } else if (ks >= K) {
+      for (int j = tid; j < ks; j += 256) l_sel[j] = j;
+    } else {
+      lds_barrier();  // keys and the pass-1 histograms
+      // every wave finds the boundary bin itself (no further barrier)
+      int b1, above1;
+      wave_threshold4(whist, 256, ks, &b1, &above1);
+      SF_TS(5);
+      // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
+      // (all taken) and in bin b1 (decided by the low bits)
+      {
+        uint8_t* bs = (uint8_t*)bm_sure;
+        uint8_t* bb = (uint8_t*)bm_bnd;
+        for (int m = tid; m < n8; m += 256) {
+          const u32x4 kv = *(const u32x4*)(keys + 4 * m);
+          uint32_t sure = 0u, bnd = 0u;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const int bin = (int)(key >> 7);
+            sure |= (uint32_t)(bin > b1) << e;
+            if (bin == b1) {
+              bnd |= 1u << e;
+              atomicAdd(&whist2[wave][key & 127u], 1u);
+            }
+          }
+          bs[m] = (uint8_t)sure;
+          bb[m] = (uint8_t)bnd;
+        }
+      }
+      lds_barrier();
+      int b2, above2;
+      wave_threshold4(whist2, 128, ks - above1, &b2, &above2);
+      SF_TS(8);
+      const uint32_t need = (uint32_t)(ks - above1 - above2);  // keys equal to T taken, lowest channels first
+      // compaction in channel order: thread t owns words [t W, t W + W) of the
+      // bitmaps; taken = above-bin | (boundary with low bits > b2) | the first
+      // `need` boundary keys with low bits == b2
+      const int nw = K / 32, W = (nw + 255) / 256;
+      const uint16_t* key16 = (const uint16_t*)keys;
+      uint32_t sg[4], eqm[4], cs = 0u, ce = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sg[i] = eqm[i] = 0u;
+        const int w = tid * W + i;
+        if (i < W && w < nw) {
+          uint32_t bnd = bm_bnd[w], gtw = 0u, eqw = 0u;
+          while (bnd) {
+            const int bit = __builtin_ctz(bnd);
+            bnd &= bnd - 1u;
+            const uint32_t lo = key16[32 * w + bit] & 127u;
+            gtw |= (uint32_t)(lo > (uint32_t)b2) << bit;
+            eqw |= (uint32_t)(lo == (uint32_t)b2) << bit;
+          }
+          sg[i] = bm_sure[w] | gtw;
+          eqm[i] = eqw;
+          cs += __popc(sg[i]);
+          ce += __popc(eqm[i]);
+        }
+      }
+      uint32_t ts, te;
+      uint32_t sbefore = wave_excl_sum8(cs, &ts), ebefore = wave_excl_sum8(ce, &te);
+      if (lane == 0) s_cnt[wave] = ts | (te << 16);
+      lds_barrier();
+      for (int w = 0; w < wave; ++w) {
+        sbefore += s_cnt[w] & 0xFFFFu;
+        ebefore += s_cnt[w] >> 16;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t all = sg[i] | eqm[i];
+        while (all) {
+          const int bit = __builtin_ctz(all);
+          all &= all - 1u;
+          const int c = 32 * (tid * W + i) + bit;
+          if ((sg[i] >> bit) & 1u) {
+            l_sel[sbefore + min(ebefore, need)] = c;
+            ++sbefore;
+          } else {
+            if (ebefore < need) l_sel[sbefore + ebefore] = c;
+            ++ebefore;
+          }
+        }
+      }
+    }
+  }
+  lds_barrier();  // x, chunk sums and the selection
+  SF_TS(2);
+
+  const float scl = (float)(1u << (a.r + B));
+  const int r = a.r;
+  uint32_t* szrow = s_szw + wave * R * ngr;  // this wave's rows' scale words, [R][ngr]
+  // the wave's R rows occupy bits [row0 * r, (row0 + R) * r) of every unit
+  const int ubit = row0 * r, uwi = ubit >> 5, uoff = ubit & 31;
+  const int wpu = o.pool.unit_bytes >> 2;
+  const uint32_t* units = (const uint32_t*)o.pool.slots;
+  const int32_t* u2s = o.pool.unit2slot;
+  // slots of this lane's first HPF hits and their refinement words for the wave's rows
+  int pslot[HPF];
+  uint32_t pw0[HPF], pw1[HPF];
+  if (!SW && refine) {
+#pragma unroll
+    for (int i = 0; i < HPF; ++i) {
+      const int j = lane + 64 * i;
+      pslot[i] = j < ks ? (o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1)) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < HPF; ++i) {
+      pw0[i] = pw1[i] = 0u;
+      if (pslot[i] >= 0) {
+        const uint32_t* u = units + (size_t)pslot[i] * wpu;
+        if (uwi < wpu) pw0[i] = u[uwi];
+        if (uwi + 1 < wpu) pw1[i] = u[uwi + 1];
+      }
+    }
+  }
+
+  const PairK pk = C::consts();
+  float acc[NB][R];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = 0.f;
+  for (int c0 = 0; c0 < nchunks; c0 += 64 * D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int c = c0 + 64 * u + lane;
+      if (c < nchunks) {
+        if (refine && (c * C::CODES) % 128 == 0)
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[u][rr];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
+          float d[R];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
+#pragma unroll 2
+          for (int jb = 0; jb < C::PAIRS / 4; ++jb) {
+            const u32x4 xv = xp[jb];
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q, pk)), as_h2(xv[q]), d[rr], false);
+          }
+          const float X = xsum[bb * nchunks + c];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+            const float sv = sf_h2f(szw[u][rr]), zv = sf_h2f(szw[u][rr] >> 16);
+            acc[bb][rr] += (sv * scl) * (d[rr] - X) + zv * X;
+          }
+        }
+        const int cn = c + 64 * D;
+        if (cn < nchunks) load_chunk_clamped<C, R>(o, row0, cn, rowbytes, ngr, cw[u], szw[u]);
+      }
+    }
+  }
+  SF_TS(3);
+  if constexpr (SW) {
+    if (refine) {
+      int32_t* l_hk = (int32_t*)(s_szw + 4 * R * ngr);
+      split_refine_tile<C, R, NB, wtm_of(R)>(a, o, op, tile_g, row0, szrow, l_hk, (float*)(l_hk + ks),
+                                            (uint32_t*)(l_hk + ks + ks * NB), acc, &lds[23]);
+    }
+  }
+  // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
+  if (!SW && refine) {
+    // the rows' scale words were recorded by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = lane; j < ks; j += 64) {
+      const int i = (j - lane) >> 6;
+      int slot;
+      uint32_t w0, w1, w2 = 0u;
+      if (i < HPF) {
+        slot = pslot[0];
+        w0 = pw0[0];
+        w1 = pw1[0];
+#pragma unroll
+        for (int q = 1; q < HPF; ++q)
+          if (q == i) {
+            slot = pslot[q];
+            w0 = pw0[q];
+            w1 = pw1[q];
+          }
+        if (slot >= 0 && uoff + R * r > 64 && uwi + 2 < wpu) w2 = units[(size_t)slot * wpu + uwi + 2];
+      } else {
+        slot = o.pool.resident ? l_sel[j] : (u2s ? u2s[l_sel[j]] : -1);
+        w0 = w1 = 0u;
+        if (slot >= 0) {
+          const uint32_t* u = units + (size_t)slot * wpu;
+          if (uwi < wpu) w0 = u[uwi];
+          if (uwi + 1 < wpu) w1 = u[uwi + 1];
+          if (uwi + 2 < wpu) w2 = u[uwi + 2];
+        }
+      }
+      if (slot < 0) continue;
+      const int k = l_sel[j];
+      const int c = k / C::CODES, kk = k - c * C::CODES;
+      int jj, hi;
+      C::locate(kk, &jj, &hi);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int p = uoff + rr * r;
+        const uint32_t clo = p + r <= 64 ? bits64(w0, w1, p, r) : bits64(w1, w2, p - 32, r);
+        const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
+          acc[bb][rr] = fmaf(hi ? (float)xh.y : (float)xh.x, sv, acc[bb][rr]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) acc[bb][rr] = wave_sum63(acc[bb][rr]);
+  if (lane == 63) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int row = row0 + rr;
+      if (row < o.n_out)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) o.y[(size_t)(a.batch_off + bb) * o.n_out + row] = acc[bb][rr];
+    }
+  }
+  // reports (once per call): the selection, each matrix's hits and lookup log
+  if (!SW && refine && a.report) {
+    if (tile_g == 0 && a.sel_out)
+      for (int j = tid; j < ks; j += 256) a.sel_out[j] = l_sel[j];
+    if (tile_g == o.tile_begin && (o.hit_out || o.pool.log_count)) {
+      if (tid == 0) {
+        int base = -1;
+        if (o.pool.log_count) {
+          const uint32_t bse = atomicAdd(o.pool.log_count, (uint32_t)ks);
+          base = (bse + (uint32_t)ks <= (uint32_t)o.pool.log_cap) ? (int)bse : -1;
+        }
+        lds[22] = base;
+      }
+      lds_barrier();
+      const int base = lds[22];
+      for (int j = tid; j < ks; j += 256) {
+        const int k = l_sel[j];
+        const int slot = o.pool.resident ? k : (u2s ? u2s[k] : -1);
+        if (o.hit_out) o.hit_out[j] = slot;
+        if (base >= 0) {
+          o.pool.log_units[base + j] = k;
+          o.pool.log_slots[base + j] = slot;
+        }
+      }
+    }
+  }
+  SF_TS(4);
+}
+
 // x pair j of a chunk from the chunk's x in natural order (word t = channels 2t, 2t+1)
 template <class C>
 __device__ __forceinline__ uint32_t xpair(const uint32_t* X, int j) {
@@ -1479,7 +1582,6 @@ constexpr int SPLIT_HPF = 8;  // hits per lane whose words are requested togethe
 
 template <class C, int B, int R, int NB, int D>
 __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
-  constexpr int WTM = (31 + 4 * R * 7 + 31) / 32;  // words of a tile's refinement window (r <= 7)
   extern __shared__ uint32_t smem[];
   __shared__ int s_flag;
   const int ks = a.k_sel;
@@ -1496,7 +1598,7 @@ __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
   uint32_t* s_szw = smem;                                          // [4][R][ngr]
   int32_t* l_hk = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [k_sel] hit channel or -1
   float* l_hx = (float*)(l_hk + (refine ? ks : 0));                 // [k_sel][NB] x at the hit
-  uint32_t* l_hw = (uint32_t*)(l_hx + (refine ? ks * NB : 0));      // [k_sel][WTM] the tile's words
+  uint32_t* l_hw = (uint32_t*)(l_hx + (refine ? ks * NB : 0));      // [k_sel][wtm_of(R)] the tile's words
   const int tile_g = blockIdx.x - a.sel_wg;
   const int op = op_of_tile(a, tile_g);
   const GemvOpDev& o = a.ops[op];
@@ -1571,71 +1673,7 @@ __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
   }
   SF_TS(2);
   // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
-  if (refine) {
-    // wave 0 waits for the selection and counts the tile
-    if (wave == 0) {
-      const bool ok0 = wait_published(a, tile_g & 63);
-      if (lane == 0) {
-        count_reader(a, tile_g & 63);
-        s_flag = ok0 ? 1 : 0;
-      }
-    }
-    lds_barrier();
-    // the tile gathers, per hit, the refinement words of its 4R rows (one request
-    // per hit and tile) and x at the hit channel into LDS
-    const int tb = (tile_g - o.tile_begin) * 4 * R * r, tw0 = tb >> 5, toff = tb & 31;
-    const int wt = (toff + 4 * R * r + 31) >> 5;  // words of the tile's window (<= WTM)
-    const int wpu = o.pool.unit_bytes >> 2;
-    const uint32_t* units = (const uint32_t*)o.pool.slots;
-    const bool resident = o.pool.resident != 0;
-    const bool any = s_flag != 0 && (resident || o.pool.unit2slot != nullptr);
-    if (any) {
-      const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (tile_g % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
-      for (int j = tid; j < ks; j += 256) {
-        const int k = (int)sf_get(hc + j);
-        const int slot = resident ? k : (int)sf_get(hc + ks * (1 + op) + j);
-        l_hk[j] = slot >= 0 ? k : -1;
-        if (slot >= 0) {
-          const uint32_t* u = units + (size_t)slot * wpu + tw0;
-#pragma unroll
-          for (int w = 0; w < WTM; ++w)
-            if (w < wt) l_hw[j * WTM + w] = tw0 + w < wpu ? u[w] : 0u;
-#pragma unroll
-          for (int bb = 0; bb < NB; ++bb) l_hx[j * NB + bb] = sf_h2f(a.x[(size_t)(a.batch_off + bb) * K + k]);
-        }
-      }
-    }
-    lds_barrier();  // the hits, and the rows' scale words recorded by other lanes
-    SF_TS(3);
-    if (any) {
-      const int pw = toff + wave * R * r;  // this wave's first row in the window
-      for (int j = lane; j < ks; j += 64) {
-        const int k = l_hk[j];
-        if (k < 0) continue;
-        uint32_t wv[WTM];
-#pragma unroll
-        for (int w = 0; w < WTM; ++w) wv[w] = w < wt ? l_hw[j * WTM + w] : 0u;
-        float xq[NB];
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) xq[bb] = l_hx[j * NB + bb];
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-          const int p = pw + rr * r, wi = p >> 5;
-          uint32_t lo = wv[0], hi = wv[1 < WTM ? 1 : 0];
-#pragma unroll
-          for (int w = 1; w < WTM; ++w)
-            if (w == wi) {
-              lo = wv[w];
-              hi = w + 1 < WTM ? wv[w + 1 < WTM ? w + 1 : w] : 0u;
-            }
-          const uint32_t clo = bits64(lo, hi, p & 31, r);
-          const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
-#pragma unroll
-          for (int bb = 0; bb < NB; ++bb) acc[bb][rr] = fmaf(xq[bb], sv, acc[bb][rr]);
-        }
-      }
-    }
-  }
+  if (refine) split_refine_tile<C, R, NB, wtm_of(R)>(a, o, op, tile_g, row0, szrow, l_hk, l_hx, l_hw, acc, &s_flag);
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
@@ -2025,18 +2063,21 @@ sf_status launch_gemv(GemvArgs& a, hipStream_t s) {
   return SF_OK;
 }
 
-template <class C, int B, int R, int NB>
+template <class C, int B, int R, int NB, bool SW = false>
 sf_status launch_fused(GemvArgs& a, hipStream_t s) {
   constexpr int D = R >= 8 ? 1 : (R >= 4 ? 2 : 4);
-  const size_t lds = fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);
+  const size_t lds =
+      SW ? fused_sw_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R) : fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);
   SF_REQUIRE(lds <= MAX_DYN_LDS, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  const dim3 grid((unsigned)(a.total_tiles + (SW ? 1 : 0)));
   if (a.k_in <= 256 * 8 * 2)
-    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 2>), dim3((unsigned)a.total_tiles), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 2, SW>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 8>), dim3((unsigned)a.total_tiles), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((gemv_fused_kernel<C, B, R, NB, D, 8, SW>), grid, dim3(256), lds, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }
+
 
 int device_cus();
 
@@ -2053,10 +2094,22 @@ sf_status launch_split(GemvArgs& a, hipStream_t s) {
           hipSuccess ||
       occ < 1)
     occ = 1;
-  if ((long)occ * device_cus() < (long)a.total_tiles + a.sel_wg &&
-      fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R) <= MAX_DYN_LDS) {
-    a.sel_wg = 0;
-    return launch_fused<C, B, R, NB>(a, s);
+  // SF_GEMV_SPLIT=2 always takes the staged variant (x in LDS, workgroup 0 selecting)
+  const bool staged = env_int("SF_GEMV_SPLIT", 1) == 2;
+  if (staged || (long)occ * device_cus() < (long)a.total_tiles + a.sel_wg) {
+    // the staged variant needs fewer registers; else the fused kernel
+    constexpr int D2 = R >= 8 ? 1 : (R >= 4 ? 2 : 4);
+    const size_t lds2 = fused_sw_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);
+    int occ2 = 0;
+    const void* k2 = a.k_in <= 256 * 8 * 2 ? (const void*)gemv_fused_kernel<C, B, R, NB, D2, 2, true>
+                                           : (const void*)gemv_fused_kernel<C, B, R, NB, D2, 8, true>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ2, k2, 256, lds2) != hipSuccess || occ2 < 1) occ2 = 1;
+    if (a.sel_wg && lds2 <= MAX_DYN_LDS && (staged || (long)occ2 * device_cus() >= (long)a.total_tiles + 1))
+      return launch_fused<C, B, R, NB, true>(a, s);
+    if (fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R) <= MAX_DYN_LDS) {
+      a.sel_wg = 0;
+      return launch_fused<C, B, R, NB>(a, s);
+    }
   }
   const dim3 grid((unsigned)(a.total_tiles + a.sel_wg));
   hipLaunchKernelGGL((gemv_split_kernel<C, B, R, NB, D>), grid, dim3(256), lds, s, a);

@@ -30,7 +30,7 @@ def _run(qws, x, k_sel, sel_in=None, cache="resident"):
     return [y.cpu().numpy() for y in ys], sel.cpu().numpy().tolist(), [h.cpu().numpy() for h in hits]
 
 
-KINDS = {"split": ("1", "1"), "fused": ("0", "1"), "persistent": ("0", "0")}
+KINDS = {"split": ("1", "1"), "staged": ("2", "1"), "fused": ("0", "1"), "persistent": ("0", "0")}
 
 
 @pytest.mark.parametrize("kind", list(KINDS))
@@ -38,8 +38,9 @@ KINDS = {"split": ("1", "1"), "fused": ("0", "1"), "persistent": ("0", "0")}
 @pytest.mark.parametrize("b,r", [(2, 2), (3, 1), (4, 4), (1, 3), (8, 0), (2, 0)])
 @pytest.mark.parametrize("batch", [1, 2, 3])
 def test_small_shapes(b, r, batch, rpw, kind, monkeypatch):
-    """Selection by one workgroup while the others stream (split), in every
-    workgroup (fused) or in its own launch (persistent); 1-8 rows per wave; one
+    """Selection by one workgroup while the others stream (split: x in registers;
+    staged: x in LDS), in every workgroup (fused) or in its own launch
+    (persistent); 1-8 rows per wave; one
     launch for batch 1-2; b = 3 at batch 3 takes the selection launch and two
     launches, the others the batched kernel."""
     monkeypatch.setenv("SF_GEMV_ROWS_PER_WAVE", rpw)
