@@ -380,12 +380,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 __device__ __forceinline__ int blk_exclusive_scan(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int NW = SEL_T / 64;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const int incl = sf_wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) lds[wave] = incl;
   __syncthreads();
@@ -663,27 +658,17 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
           g_ = (int)sf_get(a.cnts + ((size_t)bh * s2 + c) * 2);
           e_ = (int)sf_get(a.cnts + ((size_t)bh * s2 + c) * 2 + 1);
         }
-        int ie = e_;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_up(ie, o, 64);
-          if (lane >= o) ie += v;
-        }
+        const int ie = sf_wave_incl_scan(e_);
         const int eb = run_eq + ie - e_;  // equal keys before chunk c
         const int tk = max(0, min(e_, need - eb));
-        int is = g_ + tk;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_up(is, o, 64);
-          if (lane >= o) is += v;
-        }
+        const int is = sf_wave_incl_scan(g_ + tk);
         if (c == chunk) {
           lds[37] = run_sel + is - (g_ + tk);
           lds[38] = g_ + tk;
           lds[39] = eb;
         }
-        run_sel += __shfl(is, 63, 64);
-        run_eq += __shfl(ie, 63, 64);
+        run_sel += __builtin_amdgcn_readlane(is, 63);
+        run_eq += __builtin_amdgcn_readlane(ie, 63);
       }
     }
     __syncthreads();

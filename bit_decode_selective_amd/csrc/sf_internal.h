@@ -154,4 +154,22 @@ static SfProbeInstaller sf_probe_installer;
 #define SF_TS_T(i, t) ((void)0)
 #endif
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: row-local Hillis-Steele
+// steps (row_shr 1, 2, 4, 8 with zeros shifted in), then rows 1 and 3 add the totals
+// of rows 0 and 2 (row_bcast15) and rows 2 and 3 the total of rows 0-1 (row_bcast31).
+// Every lane must be active.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int sf_dpp_z(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int sf_wave_incl_scan(int v) {
+  v += sf_dpp_z<0x111>(v);
+  v += sf_dpp_z<0x112>(v);
+  v += sf_dpp_z<0x114>(v);
+  v += sf_dpp_z<0x118>(v);
+  v += sf_dpp_z<0x142, 0xA>(v);
+  v += sf_dpp_z<0x143, 0xC>(v);
+  return v;
+}
+
 static inline size_t sf_align256(size_t v) { return (v + 255) & ~size_t(255); }
