@@ -10,9 +10,11 @@
 // A decode step touches every pool of the model (a few hundred for an 8B decoder:
 // seven weight matrices and one KV cache per layer), so one fill handles all of
 // them at once: one kernel copies every pool's lookup log into a pinned host
-// mirror, the policy runs on the host, and the installs of every pool travel in
-// one staging buffer -- one entry copy, one unmap kernel, one data copy, one
-// scatter kernel and one map kernel per fill, whatever the number of pools.
+// mirror, the policy runs on the host and lists the installs of every pool (two
+// small entry copies per fill); an unmap kernel (compute stream), a scatter kernel
+// (side stream; it reads the units straight from the pinned host stores over PCIe
+// into their slots) and a map kernel (compute stream, behind the scatter) apply
+// them.  No host-side gather of unit bytes and no bulk staging copy.
 //
 // Consistency: the unit->slot tables are only changed by small kernels on the
 // compute stream (stream-ordered with every lookup), never while a reader can
@@ -39,6 +41,7 @@ struct LogTab {  // where a pool's lookup log sits in the log block
 struct PoolTab {  // what the fill kernels need of a pool
   int32_t* unit2slot;
   uint8_t* slots;
+  const uint8_t* store;  // the pinned host store, device view
   int64_t unit_bytes;
 };
 
@@ -48,11 +51,7 @@ struct UnmapEnt {
 
 struct MapEnt {
   int32_t pool, unit, slot, pad;
-  int64_t data_off;  // from the start of the staging's data region (16-byte aligned)
-  int64_t pad2;
 };
-
-constexpr int64_t DATA_ALIGN = 16;
 
 struct HostPool {
   sf_pool_desc d{};
@@ -62,6 +61,7 @@ struct HostPool {
   int64_t log_off = 0;         // in the cache's log block
   int32_t log_cap = 0;
   int64_t stage_units = 0;     // most units one fill installs
+  const uint8_t* store_dev = nullptr;  // device view of d.host_store
   std::vector<int64_t> slot_unit;  // -1 free
   std::vector<int64_t> slot_last;
   std::vector<int32_t> unit_slot;  // host view (includes units whose copy is in flight)
@@ -94,11 +94,11 @@ struct sf_refine_cache {
   size_t logs_bytes = 0;
   LogTab* d_logtab = nullptr;
   PoolTab* d_pooltab = nullptr;
-  // staging of one fill, device and pinned host: [unmaps | maps | unit bytes]
+  // fill entries, device and pinned host: [unmaps | maps]
   uint8_t* d_stage = nullptr;
   uint8_t* h_stage = nullptr;
   size_t stage_bytes = 0;
-  int64_t map_off = 0, data_off = 0;
+  int64_t map_off = 0;
   bool in_flight = false;  // a copy whose map has not been enqueued
   int32_t flight_maps = 0;
 };
@@ -156,16 +156,16 @@ __global__ void map_kernel(const PoolTab* tab, const MapEnt* ents, int n) {
   }
 }
 
-// One workgroup per staged unit (grid-stride): copies its bytes into its slot,
-// 16 bytes per thread where the unit size allows.
-__global__ __launch_bounds__(256) void scatter_kernel(const PoolTab* tab, const MapEnt* ents, int n,
-                                                      const uint8_t* data) {
+// One workgroup per installed unit (grid-stride): copies its bytes from the pinned
+// host store (over PCIe) into its slot, 16 bytes per thread where the unit size
+// allows (a pinned store is at least 16-byte aligned).
+__global__ __launch_bounds__(256) void scatter_kernel(const PoolTab* tab, const MapEnt* ents, int n) {
   for (int e = blockIdx.x; e < n; e += gridDim.x) {
     const MapEnt m = ents[e];
     const PoolTab p = tab[m.pool];
-    const uint8_t* src = data + m.data_off;
+    const uint8_t* src = p.store + (int64_t)m.unit * p.unit_bytes;
     uint8_t* dst = p.slots + (int64_t)m.slot * p.unit_bytes;
-    if ((p.unit_bytes & 15) == 0) {
+    if ((p.unit_bytes & 15) == 0 && (((uintptr_t)p.store | (uintptr_t)p.slots) & 15) == 0) {
       for (int64_t w = threadIdx.x; w < p.unit_bytes / 16; w += 256) ((uint4*)dst)[w] = ((const uint4*)src)[w];
     } else {
       for (int64_t w = threadIdx.x; w < p.unit_bytes / 4; w += 256)
@@ -197,8 +197,6 @@ __global__ __launch_bounds__(1024) void lookup_kernel(PoolDev p, int64_t n_units
     }
   }
 }
-
-int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 void destroy_cache(sf_refine_cache* c) {
   for (auto& p : c->pools) {
@@ -323,7 +321,7 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
   } while (0)
   // layouts of the log block and of the staging
   int64_t log_bytes = (int64_t)sf_align256(4 * (size_t)n_pools);
-  int64_t stage_ents = 0, stage_data = 0;
+  int64_t stage_ents = 0;
   for (int i = 0; i < n_pools; ++i) {
     HostPool& p = c->pools[i];
     p.d = pools[i];
@@ -335,12 +333,10 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
     log_bytes += (int64_t)sf_align256(8 * (size_t)p.log_cap);
     p.stage_units = std::min<int64_t>(p.d.capacity, max_fill > 0 ? max_fill : p.d.capacity);
     stage_ents += p.stage_units;
-    stage_data += p.stage_units * align_up(p.d.unit_bytes, DATA_ALIGN);
   }
   c->logs_bytes = (size_t)log_bytes;
   c->map_off = (int64_t)sf_align256((size_t)stage_ents * sizeof(UnmapEnt));
-  c->data_off = (int64_t)sf_align256((size_t)c->map_off + (size_t)stage_ents * sizeof(MapEnt));
-  c->stage_bytes = (size_t)c->data_off + (size_t)stage_data;
+  c->stage_bytes = sf_align256((size_t)c->map_off + (size_t)stage_ents * sizeof(MapEnt));
   CK(hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming));
   CK(hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming));
   CK(hipMalloc((void**)&c->d_logs, c->logs_bytes));
@@ -365,14 +361,27 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
       for (int64_t u = 0; u < nu; ++u) p.unit_slot[u] = (int32_t)u;
     } else {
       hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, 0, p.d_unit2slot, nu, -1);
-      if (cap > 0) CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
+      if (cap > 0) {
+        CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
+        // the fill kernels read the store directly: it must be pinned host memory
+        hipPointerAttribute_t attr{};
+        if (hipPointerGetAttributes(&attr, p.d.host_store) != hipSuccess || attr.type != hipMemoryTypeHost ||
+            attr.devicePointer == nullptr) {
+          (void)hipGetLastError();
+          sf_set_error("sf_refine_cache_create: host_store of pool " + std::to_string(i) +
+                       " is not pinned host memory (hipHostMalloc / pin_memory)");
+          destroy_cache(c);
+          return SF_EINVAL;
+        }
+        p.store_dev = (const uint8_t*)attr.devicePointer;
+      }
       p.slot_unit.assign(cap, -1);
       p.slot_last.assign(cap, -1);
       p.free_slots.resize(cap);
       for (int64_t s = 0; s < cap; ++s) p.free_slots[s] = (int32_t)(cap - 1 - s);
     }
     logtab[i] = LogTab{p.log_off, p.log_cap, 0};
-    pooltab[i] = PoolTab{p.d_unit2slot, p.d_slots, p.d.unit_bytes};
+    pooltab[i] = PoolTab{p.d_unit2slot, p.d_slots, p.store_dev, p.d.unit_bytes};
   }
   CK(hipMalloc((void**)&c->d_logtab, sizeof(LogTab) * n_pools));
   CK(hipMalloc((void**)&c->d_pooltab, sizeof(PoolTab) * n_pools));
@@ -430,13 +439,11 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     sf_status st = publish(c, compute);
     if (st != SF_OK) return st;
   }
-  // 3. policy of every pool; installs gathered into the one staging
+  // 3. policy of every pool; installs listed in the pinned entry buffer
   const uint32_t* counts = (const uint32_t*)c->h_logs;
   UnmapEnt* unm = (UnmapEnt*)c->h_stage;
   MapEnt* mp = (MapEnt*)(c->h_stage + c->map_off);
-  uint8_t* data = c->h_stage + c->data_off;
   int32_t n_unmap = 0, n_map = 0;
-  int64_t dpos = 0;
   bool overflow = false;
   for (int i = 0; i < np; ++i) {
     HostPool& p = c->pools[i];
@@ -489,9 +496,7 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
       if (!now) now = &p.buckets[t];
       now->push_back(u);
       ++p.bucket_entries;
-      mp[n_map] = MapEnt{i, (int32_t)u, slot, 0, dpos, 0};
-      std::memcpy(data + dpos, p.d.host_store + u * p.d.unit_bytes, (size_t)p.d.unit_bytes);
-      dpos += align_up(p.d.unit_bytes, DATA_ALIGN);
+      mp[n_map] = MapEnt{i, (int32_t)u, slot, 0};
       ++n_map;
       ++n_pool;
       ++p.n_installed;
@@ -501,8 +506,8 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     compact_buckets(p);
   }
   if (n_map > 0) {
-    // 4. entries and unmaps on the compute stream; data and scatter on the side
-    //    stream once the unmaps are done there
+    // 4. entries and unmaps on the compute stream; the scatter (units read from the
+    //    pinned stores) on the side stream once the unmaps are done there
     if (n_unmap > 0)
       SF_HIP(hipMemcpyAsync(c->d_stage, c->h_stage, sizeof(UnmapEnt) * (size_t)n_unmap, hipMemcpyHostToDevice,
                             compute));
@@ -515,9 +520,8 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     }
     SF_HIP(hipEventRecord(c->ev_compute, compute));
     SF_HIP(hipStreamWaitEvent(side, c->ev_compute, 0));
-    SF_HIP(hipMemcpyAsync(c->d_stage + c->data_off, data, (size_t)dpos, hipMemcpyHostToDevice, side));
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)std::min(n_map, 4096)), dim3(256), 0, side, c->d_pooltab,
-                       (const MapEnt*)(c->d_stage + c->map_off), n_map, (const uint8_t*)(c->d_stage + c->data_off));
+                       (const MapEnt*)(c->d_stage + c->map_off), n_map);
     SF_LAUNCH_CHECK();
     SF_HIP(hipEventRecord(c->copy_done, side));
     c->in_flight = true;

@@ -151,6 +151,8 @@ sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok, in
 /* One pool per refined tensor.  Units are fixed-size byte strings, unit ids
  * 0..n_units-1; host_store (pinned host memory, from hipHostMalloc or torch
  * pin_memory, kept alive by the caller) holds every unit, [n_units][unit_bytes].
+ * Fills read it directly from the device over PCIe; create fails with SF_EINVAL
+ * if a pool with slots has a store that is not pinned.
  * If device_store is non-NULL, the pool is a resident pool: capacity must equal
  * n_units, device_store [n_units][unit_bytes] (caller device memory) already
  * holds every unit, unit u lives in slot u, and the pool never misses. */
@@ -182,9 +184,10 @@ sf_status sf_refine_cache_lookup(sf_refine_cache* c, int32_t pool, const int32_t
                                  int32_t n, int32_t* slot_out, sf_stream compute);
 
 /* End of a decode step: reads the step's lookups of every pool (one kernel into a
- * pinned mirror, then one wait on `compute`), runs the replacement policy, gathers
- * the missed units of every pool from the host stores into one pinned staging
- * buffer and copies it with one hipMemcpyAsync on `side`, then installs them.
+ * pinned mirror, then one wait on `compute`), runs the replacement policy, and
+ * installs the missed units of every pool: the victims are unmapped on `compute`,
+ * one kernel on `side` copies the new units from the pinned host stores into
+ * their slots, and they are mapped on `compute` behind that copy.
  * Deterministic mode: returns after the new units are visible to work enqueued
  * later on `compute`.  Async mode: returns after enqueueing; units whose copy
  * finished are published at a later fill call.  n_filled (host, may be NULL):

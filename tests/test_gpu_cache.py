@@ -127,3 +127,16 @@ def test_async_fills_are_consistent_and_land():
         cache.fill()
     torch.cuda.synchronize()
     assert seen_all, "a repeated selection is served once its fill has landed"
+
+
+def test_pageable_store_is_refused():
+    """Fills read the store from the device: a pool over pageable memory is an error
+    at create time (SF_EINVAL), before any kernel could touch it."""
+    qw, _ = _weight(61, 256, 512, 2, 2)
+    pinned = qw.host_store()
+    pageable = torch.empty_like(pinned, device="cpu", pin_memory=False)
+    pageable.copy_(pinned)
+    with pytest.raises(binding.SFError):
+        binding.RefineCache([binding.host_pool_desc(pageable, 8)], keep=[pageable])
+    # a pool without slots never reads its store
+    binding.RefineCache([binding.host_pool_desc(pageable, 0)], keep=[pageable])
