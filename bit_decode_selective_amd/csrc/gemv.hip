@@ -155,6 +155,11 @@ struct CodecStream {
   }
 };
 
+// Words per chunk of x pairs in LDS: the pairs plus 4 words of padding, so that the
+// lanes' 16-byte reads of consecutive chunks start in different banks.
+template <class C>
+__host__ __device__ constexpr int x_chunk_words() { return C::PAIRS + 4; }
+
 // ---- selection + lookup (one 1024-thread workgroup) ----------------------------------
 // Wave 0 scans NBIN = 64 * PER histogram bins from the top: the largest bin whose
 // suffix count reaches `need`; lds[20] = bin, lds[21] = count above it.
@@ -827,7 +832,7 @@ __device__ __forceinline__ uint32_t wave_excl_small(uint32_t c, uint32_t* total)
 
 
 size_t fused_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
-  size_t w = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
+  size_t w = (size_t)nb * (k_in / codes) * (codes / 2 + 4) + (size_t)nb * (((k_in / codes) + 3) & ~3);
   if (k_sel > 0) w += (size_t)(k_in / 2) + (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel + (size_t)(k_in / 16);
   return w * 4;
 }
@@ -840,7 +845,7 @@ size_t split_sel_lds_words(int k_in, int k_sel) {
 // hits (channel, x, the tile's window words) after the scale words; the selecting
 // workgroup's own layout may be larger.
 size_t fused_sw_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
-  size_t tile = (size_t)nb * (k_in / 2) + (size_t)nb * (((k_in / codes) + 3) & ~3);
+  size_t tile = (size_t)nb * (k_in / codes) * (codes / 2 + 4) + (size_t)nb * (((k_in / codes) + 3) & ~3);
   if (k_sel > 0) tile += (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel * (1 + nb + wtm_of(rpw));
   const size_t sel = k_sel > 0 ? split_sel_lds_words(k_in, k_sel) : 0;
   return std::max(tile, sel) * 4;
@@ -860,9 +865,6 @@ size_t fused_sw_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw) {
 // Dynamic LDS, tiles: x pairs [NB][nchunks][PAIRS + 4] | chunk sums [NB][nchunks]
 // | scale words [4][R][K/128]; selector: keys [K/2] | bitmaps [2][K/32] |
 // selection [k_sel] | histograms [4][256] + [4][128] | 16 words.
-template <class C>
-__host__ __device__ constexpr int chunk_stride() { return C::PAIRS + 4; }
-
 size_t split_lds_bytes(int k_in, int pairs, int codes, int nb, int k_sel, int rpw) {
   (void)pairs;
   (void)codes;
@@ -1130,9 +1132,15 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
       l_hk[j] = slot >= 0 ? k : -1;
       if (slot >= 0) {
         const uint32_t* u = units + (size_t)slot * wpu + tw0;
+        if (wt <= 2 && tw0 + 1 < wpu && ((uintptr_t)u & 7u) == 0) {  // one 8-byte request
+          const u32x2 v = *(const u32x2*)u;
+          l_hw[j * WTM] = v.x;
+          if (WTM > 1) l_hw[j * WTM + 1] = v.y;
+        } else {
 #pragma unroll
-        for (int w = 0; w < WTM; ++w)
-          if (w < wt) l_hw[j * WTM + w] = tw0 + w < wpu ? u[w] : 0u;
+          for (int w = 0; w < WTM; ++w)
+            if (w < wt) l_hw[j * WTM + w] = tw0 + w < wpu ? u[w] : 0u;
+        }
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) l_hx[j * NB + bb] = sf_h2f(a.x[(size_t)(a.batch_off + bb) * K + k]);
       }
@@ -1206,8 +1214,9 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
   const int K = a.k_in, nchunks = K / C::CODES, xpairs = K / 2, ngr = K / 128, n8 = K / 8;
   const int ks = a.k_sel;
   const bool refine = ks > 0;
-  uint32_t* xs = smem;                                         // [NB][K/2] fp16 pairs
-  float* xsum = (float*)(smem + NB * xpairs);                  // [NB][nchunks]
+  constexpr int XCS = x_chunk_words<C>();                      // words per chunk of x pairs
+  uint32_t* xs = smem;                                         // [NB][nchunks][XCS] fp16 pairs
+  float* xsum = (float*)(smem + NB * nchunks * XCS);           // [NB][nchunks]
   uint32_t* keys = (uint32_t*)(xsum + NB * ((nchunks + 3) & ~3));  // [K/2]: channel-order key pairs
   uint32_t* s_szw = keys + ((refine && !SW) ? xpairs : 0);     // [4][R][ngr]
   int32_t* l_sel = (int32_t*)(s_szw + (refine ? 4 * R * ngr : 0));  // [ks]
@@ -1263,7 +1272,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
             int j, hi;
             C::locate(kk, &j, &hi);
             const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
-            xh[2 * (bb * xpairs + c * C::PAIRS + j) + hi] = hb;
+            xh[2 * ((bb * nchunks + c) * XCS + j) + hi] = hb;
             part += (float)__builtin_bit_cast(_Float16, hb);
           }
         }
@@ -1429,18 +1438,26 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
           for (int rr = 0; rr < R; ++rr) szrow[rr * ngr + (c * C::CODES) / 128] = szw[u][rr];
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
-          const u32x4* xp = (const u32x4*)(xs + bb * xpairs + c * C::PAIRS);
+          const u32x4* xp = (const u32x4*)(xs + (bb * nchunks + c) * XCS);
           float d[R];
 #pragma unroll
           for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
-#pragma unroll 2
+          // batch 1: fully unrolled (constant word indices, no indexed register
+          // reads); the x pairs are read one step ahead and no further (the empty
+          // asm keeps later LDS reads after it).  Batch 2 keeps a short loop, for
+          // its register count.
+          constexpr int JU = NB == 1 ? C::PAIRS / 4 : 2;
+          u32x4 xn = xp[0];
+#pragma unroll JU
           for (int jb = 0; jb < C::PAIRS / 4; ++jb) {
-            const u32x4 xv = xp[jb];
+            const u32x4 xv = xn;
+            if (jb + 1 < C::PAIRS / 4) xn = xp[jb + 1];
 #pragma unroll
             for (int rr = 0; rr < R; ++rr)
 #pragma unroll
               for (int q = 0; q < 4; ++q)
                 d[rr] = __builtin_amdgcn_fdot2(as_h2(C::pair(cw[u][rr], 4 * jb + q, pk)), as_h2(xv[q]), d[rr], false);
+            asm volatile("" ::: "memory");
           }
           const float X = xsum[bb * nchunks + c];
 #pragma unroll
@@ -1449,10 +1466,15 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
             acc[bb][rr] += (sv * scl) * (d[rr] - X) + zv * X;
           }
         }
-        const int cn = c + 64 * D;
-        if (cn < nchunks) load_chunk_clamped<C, R>(o, row0, cn, rowbytes, ngr, cw[u], szw[u]);
       }
     }
+    // the next chunks: a wave-uniform exit first, then unconditional loads (clamped
+    // addresses; a lane past the end loads a chunk it never uses), so the loaded
+    // words replace the current ones in place
+    if (c0 + 64 * D >= nchunks) break;
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+      load_chunk_clamped<C, R>(o, row0, min(c0 + 64 * D + 64 * u + lane, nchunks - 1), rowbytes, ngr, cw[u], szw[u]);
   }
   SF_TS(3);
   if constexpr (SW) {
@@ -1506,7 +1528,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
         const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
-          const h2_t xh = as_h2(xs[bb * xpairs + c * C::PAIRS + jj]);
+          const h2_t xh = as_h2(xs[(bb * nchunks + c) * XCS + jj]);
           acc[bb][rr] = fmaf(hi ? (float)xh.y : (float)xh.x, sv, acc[bb][rr]);
         }
       }
