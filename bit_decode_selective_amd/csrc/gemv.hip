@@ -1150,6 +1150,31 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
   SF_TS(5);
   if (!any) return;
   const int pw = toff + wave * R * r;  // this wave's first row in the window
+  const int wi0 = pw >> 5, sh0 = pw & 31;
+  if (sh0 + R * r <= 64) {
+    // the wave's R * r bits lie in two consecutive window words (wave-uniform
+    // position): one 64-bit shift per hit, then a field per row
+    const uint32_t fmask = (1u << r) - 1u;
+    for (int j = lane; j < ks; j += 64) {
+      const int k = l_hk[j];
+      if (k < 0) continue;
+      const uint32_t lo = l_hw[j * WTM + wi0];
+      const uint32_t hi = wi0 + 1 < WTM ? l_hw[j * WTM + min(wi0 + 1, WTM - 1)] : 0u;
+      const uint64_t bits = ((((uint64_t)hi) << 32) | lo) >> sh0;  // a word past the window only feeds unused bits
+      float xq[NB];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) xq[bb] = l_hx[j * NB + bb];
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const uint32_t clo = (uint32_t)(bits >> (rr * r)) & fmask;
+        const float sv = sf_h2f(szrow[rr * ngr + (k >> 7)]) * (float)clo;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) acc[bb][rr] = fmaf(xq[bb], sv, acc[bb][rr]);
+      }
+    }
+    SF_TS(9);
+    return;
+  }
   for (int j = lane; j < ks; j += 64) {
     const int k = l_hk[j];
     if (k < 0) continue;
@@ -1175,6 +1200,7 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
       for (int bb = 0; bb < NB; ++bb) acc[bb][rr] = fmaf(xq[bb], sv, acc[bb][rr]);
     }
   }
+  SF_TS(9);
 }
 
 // ---- batch-1/2 GEMV with the selection in every workgroup ----------------------
@@ -1538,6 +1564,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
   for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) acc[bb][rr] = wave_sum63(acc[bb][rr]);
+  SF_TS(10);
   if (lane == 63) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
