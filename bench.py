@@ -49,8 +49,8 @@ DOMINANT = {
     "source": "bit_decode_selective_amd/csrc/gemv.hip",
 }
 TRAFFIC = {
-    "source_sha256": "358ba92dc19d5a8399cede4c0b70f5c9e822fdd42fd578bb71e9ab4948573925",
-    "fetch_bytes": 40437169,
+    "source_sha256": "971dd4955d9906e3d72875c7811e471a0ef337cf8e6409c9ec4a75bd5caef2a2",
+    "fetch_bytes": 40477568,
     "write_bytes": 153600,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
