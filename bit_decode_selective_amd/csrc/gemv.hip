@@ -1053,8 +1053,35 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
       }
     }
   }
-  // the lookup-log bases (one reservation per matrix)
-  if (a.report && tid < a.n_ops) {
+  lds_barrier();
+  SF_TS(12);
+  // the published words first: the channels and, per matrix without resident
+  // units, the slots, in SPLIT_COPIES copies
+  uint32_t* hw = a.ctl + offsetof(WsControl, hit) / 4;
+  const int cst = split_copy_words(ks, a.n_ops);
+  for (int j = tid; j < ks; j += 256) {
+    const int k = l_sel[j];
+#pragma unroll
+    for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + j, (uint32_t)k);
+#pragma unroll
+    for (int op = 0; op < SF_MAX_OPS; ++op) {
+      if (op >= a.n_ops) break;
+      const PoolDev& pool = a.ops[op].pool;
+      if (pool.resident) continue;
+      const int slot = pool.unit2slot ? pool.unit2slot[k] : -1;
+#pragma unroll
+      for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + ks * (1 + op) + j, (uint32_t)slot);
+    }
+  }
+  // the words are complete at the coherence point before any flag goes up
+  sf_drain();
+  __syncthreads();
+  if (tid < 64) sf_put(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 1u);
+  SF_TS(13);
+  // the reports (selection, hits, lookup log: one reservation per matrix) after
+  // the flags, off the tiles' path
+  if (!a.report) return;
+  if (tid < a.n_ops) {
     const PoolDev& pool = a.ops[tid].pool;
     int base = -1;
     if (pool.log_count) {
@@ -1064,37 +1091,22 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
     sc[8 + tid] = base;
   }
   lds_barrier();
-  SF_TS(12);
-  uint32_t* hw = a.ctl + offsetof(WsControl, hit) / 4;
-  const int cst = split_copy_words(ks, a.n_ops);
   for (int j = tid; j < ks; j += 256) {
     const int k = l_sel[j];
-#pragma unroll
-    for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + j, (uint32_t)k);
-    if (a.report && a.sel_out) a.sel_out[j] = k;
+    if (a.sel_out) a.sel_out[j] = k;
 #pragma unroll
     for (int op = 0; op < SF_MAX_OPS; ++op) {
       if (op >= a.n_ops) break;
       const PoolDev& pool = a.ops[op].pool;
       const int slot = pool.resident ? k : (pool.unit2slot ? pool.unit2slot[k] : -1);
-      if (!pool.resident)
-#pragma unroll
-        for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + ks * (1 + op) + j, (uint32_t)slot);
-      if (a.report) {
-        if (a.ops[op].hit_out) a.ops[op].hit_out[j] = slot;
-        const int base = sc[8 + op];
-        if (base >= 0) {
-          pool.log_units[base + j] = k;
-          pool.log_slots[base + j] = slot;
-        }
+      if (a.ops[op].hit_out) a.ops[op].hit_out[j] = slot;
+      const int base = sc[8 + op];
+      if (base >= 0) {
+        pool.log_units[base + j] = k;
+        pool.log_slots[base + j] = slot;
       }
     }
   }
-  // the words are complete at the coherence point before any flag goes up
-  sf_drain();
-  __syncthreads();
-  if (tid < 64) sf_put(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 1u);
-  SF_TS(13);
 }
 
 
