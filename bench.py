@@ -49,8 +49,8 @@ DOMINANT = {
     "source": "bit_decode_selective_amd/csrc/gemv.hip",
 }
 TRAFFIC = {
-    "source_sha256": "971dd4955d9906e3d72875c7811e471a0ef337cf8e6409c9ec4a75bd5caef2a2",
-    "fetch_bytes": 40477568,
+    "source_sha256": "8a736a1b0b5cdc9e3f878eb8104e28b4597c23b765dd5a20ecb5d4c6f725e3ed",
+    "fetch_bytes": 40468670,
     "write_bytes": 153600,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
