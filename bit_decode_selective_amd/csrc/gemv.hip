@@ -1661,6 +1661,9 @@ __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
   float* l_hx = (float*)(l_hk + (refine ? ks : 0));                 // [k_sel][NB] x at the hit
   uint32_t* l_hw = (uint32_t*)(l_hx + (refine ? ks * NB : 0));      // [k_sel][wtm_of(R)] the tile's words
   const int tile_g = blockIdx.x - a.sel_wg;
+  // the selecting workgroup's x requests reach the memory queues ahead of the tiles'
+  // code streams (the tiles finish before the selection at these sizes)
+  if (refine && a.sel_wg) __builtin_amdgcn_s_sleep(40);
   const int op = op_of_tile(a, tile_g);
   const GemvOpDev& o = a.ops[op];
   const int row0 = (tile_g - o.tile_begin) * 4 * R + wave * R;
