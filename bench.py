@@ -49,8 +49,8 @@ DOMINANT = {
     "source": "bit_decode_selective_amd/csrc/gemv.hip",
 }
 TRAFFIC = {
-    "source_sha256": "8a736a1b0b5cdc9e3f878eb8104e28b4597c23b765dd5a20ecb5d4c6f725e3ed",
-    "fetch_bytes": 40468670,
+    "source_sha256": "ffb5c6f84dae954a5b1ef03c92df002c2df485a125c67529df614d0f9bcc2526",
+    "fetch_bytes": 40457928,
     "write_bytes": 153600,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
