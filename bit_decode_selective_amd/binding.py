@@ -88,6 +88,7 @@ _PROTOS = {
     "sf_workspace_bytes_gemv": (SZ, [C.POINTER(sf_gemv_op), I32, I32, I32]),
     "sf_workspace_bytes_attn": (SZ, [I32, I32, I32, I32, I32]),
     "sf_workspace_check": (I32, [VP]),
+    "sf_workspace_set_spin_limit": (I32, [VP, C.c_uint32]),
     "sf_quantize_nested": (I32, [VP, I64, I64, sf_qfmt, I32, VP, VP, VP, VP]),
     "sf_debug_dequantize": (I32, [VP, VP, VP, I64, I64, sf_qfmt, I32, I32, VP, VP]),
     "sf_kv_append": (I32, [VP, VP, I32, I32, C.POINTER(sf_qkv), VP, I64, VP]),
@@ -187,8 +188,18 @@ class Workspace:
     def check(self):
         check(lib().sf_workspace_check(self.handle))
 
+    def set_spin_limit(self, polls):
+        check(lib().sf_workspace_set_spin_limit(self.handle, int(polls)))
+
 
 _ws = {}
+
+
+def check_workspaces():
+    """sf_workspace_check on every workspace this module created (raises SFError with
+    SF_ESTATE if a device-side wait timed out since the last check)."""
+    for w in list(_ws.values()):
+        w.check()
 
 
 def workspace(nbytes, device=None):

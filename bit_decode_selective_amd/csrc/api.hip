@@ -13,18 +13,6 @@ __global__ void ws_zero_kernel(uint32_t* p, int n) {
 
 void sf_set_error(const std::string& msg) { g_last_error = msg; }
 
-#ifdef SF_PROBE
-static std::vector<void (*)(long long*)>& sf_probe_installers() {
-  static std::vector<void (*)(long long*)> v;
-  return v;
-}
-void sf_probe_register(void (*install)(long long*)) { sf_probe_installers().push_back(install); }
-extern "C" int sf_probe_set_buffer(long long* p) {
-  for (auto f : sf_probe_installers()) f(p);
-  return 0;
-}
-#endif
-
 extern "C" int32_t sf_abi_version(void) { return SF_ABI_VERSION; }
 
 extern "C" const char* sf_last_error(void) { return g_last_error.c_str(); }
@@ -82,10 +70,20 @@ extern "C" sf_status sf_workspace_check(sf_workspace* ws) {
   WsControl ctl;
   SF_HIP(hipMemcpy(&ctl, ws->base, sizeof(ctl), hipMemcpyDeviceToHost));
   if (ctl.timeout) {
-    const uint32_t zero = 0;
-    SF_HIP(hipMemcpy(ws->base + offsetof(WsControl, timeout), &zero, 4, hipMemcpyHostToDevice));
+    // a wait gave up: clear every flag and counter the kernels hand over with (the
+    // control block and the per-call words in the data area), keeping the spin limit
+    SF_HIP(hipMemset(ws->base, 0, ws->bytes));
+    SF_HIP(hipMemcpy(ws->base + offsetof(WsControl, spin_limit), &ctl.spin_limit, 4, hipMemcpyHostToDevice));
+    SF_HIP(hipDeviceSynchronize());
     sf_set_error("a device-side wait timed out; the affected rows carry no refinement");
     return SF_ESTATE;
   }
+  return SF_OK;
+}
+
+extern "C" sf_status sf_workspace_set_spin_limit(sf_workspace* ws, uint32_t polls) {
+  SF_REQUIRE(ws, SF_EINVAL, "null workspace");
+  SF_HIP(hipDeviceSynchronize());
+  SF_HIP(hipMemcpy(ws->base + offsetof(WsControl, spin_limit), &polls, 4, hipMemcpyHostToDevice));
   return SF_OK;
 }

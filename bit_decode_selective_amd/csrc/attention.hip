@@ -51,7 +51,8 @@ constexpr int TPT = CB / SEL_T;  // tokens per select thread
 constexpr int PW = HD + 4;       // partial record: N[HD], max, sum, pad
 constexpr int NBIN = 2048;       // histogram bins (levels: key bits 30..20, 19..10, 9..0)
 constexpr int MAX_CHUNKS = 256;
-constexpr int PV_NR = 8;         // value-sum records per KV head (pv split s adds into record s % PV_NR)
+constexpr int PV_NR = 8;
+constexpr float SCORE_CUTOFF = -64.f;  // logit below the head's max past which a weight scores 0         // value-sum records per KV head (pv split s adds into record s % PV_NR)
 
 __host__ __device__ constexpr int pv_tokens(int b) { return b <= 4 ? 512 : 256; }
 
@@ -133,7 +134,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   const int T = a.T;
   const int t_begin = split * SA, n_here = min(SA, T - t_begin);
   const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
-  SF_TS(0);
 
   // this call's selection histograms, counters and lookup-log base
   if (a.k_sel > 0) {
@@ -148,8 +148,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
         int base = -1;
         if (a.pool.log_count) {
           const uint32_t n = (uint32_t)(a.batch * a.n_kv) * (uint32_t)a.k_sel;
-          const uint32_t bse = atomicAdd(a.pool.log_count, n);
-          base = (bse + n <= (uint32_t)a.pool.log_cap) ? (int)bse : -1;
+          base = sf_log_reserve(a.pool.log_count, n, (uint32_t)a.pool.log_cap);
         }
         a.ctl[5] = (uint32_t)base;
       }
@@ -269,7 +268,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     }
   }
   __syncthreads();  // s_l
-  SF_TS(1);
 
   // ---- split max per head (and the largest value scale) ----
   const int t = tid;  // this thread's token within the split
@@ -373,7 +371,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     PS[tid * PW + HD] = ms[tid];
     PS[tid * PW + HD + 1] = s_st[3 * tid];
   }
-  SF_TS(2);
 }
 
 // ---- select / merge ----------------------------------------------------------------
@@ -435,7 +432,7 @@ __device__ __forceinline__ void chunk_barrier(uint32_t* ctr, uint32_t n, uint32_
   sf_drain();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    (void)sf_add_release(ctr, 1u);
     (void)sf_wait_word(ctr, n, timeout);
   }
   __syncthreads();
@@ -482,7 +479,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   const int KS = ks > 0 ? ks : 1;
   const int c0 = chunk * CB;
   uint32_t* ctl = a.ctl + bh * 8;
-  SF_TS(4);
   if (ks > 0)
     for (int i = tid; i < G * HD; i += SEL_T) {
       const int h = i / HD, d = i - h * HD;
@@ -530,7 +526,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  SF_TS(5);
 
   if (ks == 0) {
     // ---- no refinement: this chunk's value sums relative to the global max ----
@@ -596,7 +591,10 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
         const f4_t l4 = l4p[h];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
-          sc[i] += __expf(l4[i] - s_m[h]) * s_iz[h];
+          // a weight below e^-64 of the head's largest adds nothing (ties at zero
+          // then go to the lower token)
+          const float dl = l4[i] - s_m[h];
+          sc[i] += dl >= SCORE_CUTOFF ? __expf(dl) * s_iz[h] : 0.f;
           lgk[h][i] = l4[i];
         }
       }
@@ -631,7 +629,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
       sh = lsh;
       if (need == inbin) break;  // the whole bin is taken: no finer level needed
     }
-    SF_TS(6);
     // ---- counts above / at the threshold, exchanged between the chunks ----
     int gt = 0, eq = 0;
 #pragma unroll
@@ -727,7 +724,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   off = min(max(off, 0), ks);
   cnt = min(max(cnt, 0), min(CB, ks - off));
   __syncthreads();
-  SF_TS(7);
 
   // ---- lookups (in selection order) and, for the hits, the logits become
   //      l' = l + scale * s_K * (q . cK_lo); item m = (selected j, head m % G) ----
@@ -784,7 +780,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     for (int w = 0; w < SEL_T / 64; ++w) mm = fmaxf(mm, s_wm[w][tid][0]);
     sf_put(a.cmax + ((size_t)bh * s2 + chunk) * G + tid, mm);
   }
-  SF_TS(8);
   sf_drain();
   __syncthreads();
   if (tid == 0)
@@ -803,7 +798,6 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     }
     a.mref[bh * G + tid] = mm;
   }
-  SF_TS(9);
 }
 
 // ---- pv: final weights, value sums, hit refinements, merge ---------------------------
@@ -841,7 +835,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   const int T = a.T;
   const int t_begin = split * SP, n_here = min(SP, T - t_begin);
   const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
-  SF_TS(12);
   // ---- loads ----
   u32x4 vc[NV];
   {
@@ -966,7 +959,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   if (lane == 0)
 #pragma unroll
     for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
-  SF_TS(13);
 
   // ---- hits: request the refinement words of this wave's hits (w, w+4, ..) ----
   // lane l covers dims 2l, 2l+1: value refinement bits [HD r + 2 l r, HD r + 2 l r + 2 r)
@@ -1086,7 +1078,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   if (tid < G)
     (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, fsc[tid] * s_st[3 * tid], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
-  SF_TS(14);
   sf_drain();
   __syncthreads();
   if (tid == 0)
@@ -1111,7 +1102,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     }
     a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
   }
-  SF_TS(15);
 }
 
 size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12]) {
@@ -1141,9 +1131,29 @@ size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12
   return o;
 }
 
+int attn_device_cus() {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, cus = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    n_cu = cus;
+  }
+  return n_cu;
+}
+
 template <int B, int G>
 sf_status launch_attn(AttnArgs& a, hipStream_t s) {
   const int bh = a.batch * a.n_kv;
+  // the chunks of one KV head wait for each other: all of them must be resident at
+  // once (workgroups are dispatched in order, so the chunks of earlier KV heads
+  // finish and make room for later ones)
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)attn_select_kernel<G>, SEL_T, 0) != hipSuccess ||
+      occ < 1)
+    occ = 1;
+  SF_REQUIRE((long)a.s2 <= (long)occ * attn_device_cus(), SF_EUNSUPPORTED,
+             "t_len too long: the selection chunks of one KV head do not fit the device at once");
   if (a.k_sel == 0) {
     hipLaunchKernelGGL((attn_split_kernel<B, G, true>), dim3(a.nsa, bh), dim3(256), 0, s, a);
     SF_LAUNCH_CHECK();

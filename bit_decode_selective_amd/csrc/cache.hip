@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void logs_to_host_kernel(uint8_t* d_logs, uint
   }
   __syncthreads();
   const LogTab t = tab[i];
-  const uint32_t n = min(s_cnt, (uint32_t)t.cap);
+  const uint32_t n = min(s_cnt & 0x7FFFFFFFu, (uint32_t)t.cap);
   const int32_t* src = (const int32_t*)(d_logs + t.off);
   int32_t* dst = (int32_t*)(h_logs + t.off);
   for (uint32_t j = threadIdx.x; j < n; j += 256) {
@@ -182,8 +182,7 @@ __global__ __launch_bounds__(1024) void lookup_kernel(PoolDev p, int64_t n_units
   if (threadIdx.x == 0) {
     base = -1;
     if (p.log_count) {
-      const uint32_t b = atomicAdd(p.log_count, (uint32_t)n);
-      base = (b + (uint32_t)n <= (uint32_t)p.log_cap) ? (int)b : -1;
+      base = sf_log_reserve(p.log_count, (uint32_t)n, (uint32_t)p.log_cap);
     }
   }
   __syncthreads();
@@ -448,11 +447,10 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
   for (int i = 0; i < np; ++i) {
     HostPool& p = c->pools[i];
     if (p.resident) continue;
-    uint32_t cnt = counts[i];
-    if (cnt > (uint32_t)p.log_cap) {
-      overflow = true;
-      cnt = (uint32_t)p.log_cap;
-    }
+    // entries below the count are complete; bit 31 marks a lookup that did not fit
+    uint32_t cnt = counts[i] & 0x7FFFFFFFu;
+    if (counts[i] & 0x80000000u) overflow = true;
+    if (cnt > (uint32_t)p.log_cap) cnt = (uint32_t)p.log_cap;
     const int32_t* log_u = (const int32_t*)(c->h_logs + p.log_off);
     const int32_t* log_s = log_u + p.log_cap;
     const int64_t cap = p.d.capacity;

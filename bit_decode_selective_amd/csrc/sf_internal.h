@@ -32,12 +32,16 @@ void sf_set_error(const std::string& msg);
 #define SF_LAUNCH_CHECK() SF_HIP(hipGetLastError())
 
 // ---- workspace -------------------------------------------------------------------
-// Control words at the start of every workspace (device memory).
+// Control words at the start of every workspace (device memory).  Kernels that hand
+// data from one workgroup to another inside a launch keep their flags and counters
+// here; every launch leaves them as it found them (zero), and sf_workspace_check
+// clears them all after a bounded wait has given up.
 struct WsControl {
-  uint32_t sel_state;  // 0 idle, 1 selection in progress, 2 published
-  uint32_t done;       // workgroups finished (last one resets the words)
-  uint32_t timeout;    // set when a bounded device wait gave up
-  uint32_t pad[61];    // keeps the data area 256-byte aligned
+  uint32_t sel_state;   // 0 idle, 1 selection in progress, 2 published
+  uint32_t done;        // workgroups finished (last one resets the words)
+  uint32_t timeout;     // set when a bounded device wait gave up
+  uint32_t spin_limit;  // polls a bounded wait makes before it gives up (0: 1 << 22)
+  uint32_t pad[60];     // keeps the data area 256-byte aligned
   uint32_t row_ctr[1024];  // batched GEMV: slices finished per row block (last one resets)
   // split GEMV: the published selection in SPLIT_COPIES copies (word j = channel,
   // then per matrix word k_sel * (1 + op) + j = slot), valid while sel_flag is
@@ -71,17 +75,36 @@ struct PoolDev {
 // NULL or pool < 0.  Fails with SF_EINVAL for a bad pool index.
 sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out);
 
+// Reserves n entries of a pool's lookup log (count word: entries reserved in bits
+// 0..30, never more than cap; bit 31 set once a reservation did not fit).  Returns
+// the first entry, or -1 if the n entries do not fit (nothing is reserved then, so
+// every entry below the count has been written by its reserver).
+__device__ __forceinline__ int sf_log_reserve(uint32_t* count, uint32_t n, uint32_t cap) {
+  uint32_t old = __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint32_t used = old & 0x7FFFFFFFu;
+    if (used + n > cap) {
+      (void)__hip_atomic_fetch_or(count, 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return -1;
+    }
+    if (__hip_atomic_compare_exchange_weak(count, &old, old + n, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+      return (int)used;
+  }
+}
+
 // ---- fp16 helpers ------------------------------------------------------------------
 __device__ __forceinline__ float sf_h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
 }
 
 // Cross-workgroup hand-off inside one launch.  Data published by one workgroup for
-// others is written with agent-scope atomic stores and read with agent-scope
-// atomic loads, which are performed at the device coherence point (no L2 writeback
-// or invalidation, which on a multi-XCD device would be needed for plain accesses
-// and are costly).  The writer waits for its stores to complete (s_waitcnt) and
-// passes a workgroup barrier before one thread raises the flag.
+// others is written with agent-scope atomic stores and read with agent-scope atomic
+// loads, which are performed at the device coherence point (no L2 writeback or
+// invalidation of the data itself).  The flag that announces the data is a release
+// store after the data stores, and the reader's poll of the flag is an acquire
+// load: the memory model then orders the data before the flag for any reader that
+// sees the flag.
 __device__ __forceinline__ void sf_put(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -100,6 +123,22 @@ __device__ __forceinline__ int32_t sf_get(const int32_t* p) {
 __device__ __forceinline__ float sf_get(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// flag store that releases this thread's earlier stores, and the matching acquire poll
+__device__ __forceinline__ void sf_put_release(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sf_get_acquire(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+// counter increment that releases this thread's earlier stores (a workgroup's
+// contribution is complete once its thread 0 counts it after a barrier)
+__device__ __forceinline__ uint32_t sf_add_release(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sf_add_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup barrier that orders LDS accesses only: this thread's global loads stay
 // in flight (a plain __syncthreads() waits for them).
 __device__ __forceinline__ void lds_barrier() {
@@ -111,48 +150,29 @@ __device__ __forceinline__ void lds_barrier() {
 // All of this thread's memory operations have completed.
 __device__ __forceinline__ void sf_drain() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Bounded spin on a flag raised by another workgroup of the same launch.  Returns
-// false if it gave up (after about a second); the caller then skips the work that
-// needed the flag.
+// Polls a bounded wait makes before it gives up: the workspace's spin-limit word,
+// which follows its timeout word (0 means 1 << 22, about a second).
+__device__ __forceinline__ uint32_t sf_spin_limit(const uint32_t* timeout_flag) {
+  const uint32_t v = __hip_atomic_load(timeout_flag + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v ? v : (1u << 22);
+}
+
+// Bounded spin on a word raised by another workgroup of the same launch (acquire:
+// what the other workgroup stored before it raised the word is visible after a
+// true return).  Returns false if it gave up; the caller then skips the work that
+// needed the word and the timeout flag reports it.
 __device__ __forceinline__ bool sf_wait_word(uint32_t* p, uint32_t want, uint32_t* timeout_flag) {
-  for (uint32_t it = 0; it < (1u << 22); ++it) {
-    if (sf_get(p) == want) return true;
+  const uint32_t lim = sf_spin_limit(timeout_flag);
+  for (uint32_t it = 0; it < lim; ++it) {
+    if (sf_get(p) == want) {
+      (void)sf_get_acquire(p);
+      return true;
+    }
     __builtin_amdgcn_s_sleep(4);
   }
   sf_put(timeout_flag, 1u);
   return false;
 }
-
-// Phase timestamps for performance analysis.  Compiled in only with -DSF_PROBE
-// (a separate build); SF_TS(i) records the wall clock of thread 0 of each
-// workgroup in slot i (0..15) of that workgroup's row of the probe buffer.
-#ifdef SF_PROBE
-// one copy of the buffer pointer per translation unit (no relocatable device code),
-// in constant memory: a scalar load, which does not wait for the vector loads in flight
-static __constant__ long long* sf_probe_buf = nullptr;
-void sf_probe_register(void (*install)(long long*));
-namespace {
-struct SfProbeInstaller {
-  static void install(long long* p) { (void)hipMemcpyToSymbol(HIP_SYMBOL(sf_probe_buf), &p, sizeof(p)); }
-  SfProbeInstaller() { sf_probe_register(&install); }
-};
-static SfProbeInstaller sf_probe_installer;
-}  // namespace
-#define SF_TS(i)                                                                          \
-  do {                                                                                    \
-    if (threadIdx.x == 0 && sf_probe_buf)                                                 \
-      sf_probe_buf[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + (i)] = wall_clock64(); \
-  } while (0)
-// the same, recorded by thread t of the workgroup
-#define SF_TS_T(i, t)                                                                     \
-  do {                                                                                    \
-    if (threadIdx.x == (t) && sf_probe_buf)                                               \
-      sf_probe_buf[((size_t)blockIdx.y * gridDim.x + blockIdx.x) * 16 + (i)] = wall_clock64(); \
-  } while (0)
-#else
-#define SF_TS(i) ((void)0)
-#define SF_TS_T(i, t) ((void)0)
-#endif
 
 // Inclusive prefix sum over the 64 lanes of a wave by DPP: row-local Hillis-Steele
 // steps (row_shr 1, 2, 4, 8 with zeros shifted in), then rows 1 and 3 add the totals

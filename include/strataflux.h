@@ -112,10 +112,17 @@ sf_status sf_workspace_create(size_t bytes, sf_workspace** out);
 sf_status sf_workspace_destroy(sf_workspace* ws);
 size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t t_len, int32_t k_sel);
-/* Returns SF_ESTATE (and clears the flag) if a device-side wait timed out in a
- * call that used this workspace since the last check; the affected rows then
- * carry no refinement.  Synchronises the device. */
+/* Returns SF_ESTATE if a device-side wait timed out in a call that used this
+ * workspace since the last check; the affected rows then carry no refinement.
+ * After a timeout it also clears every flag and counter in the workspace, so the
+ * next call starts from a clean state.  Synchronises the device. */
 sf_status sf_workspace_check(sf_workspace* ws);
+/* Test hook: the number of polls a bounded device wait of calls on this workspace
+ * makes before it gives up (0 = the default, about a second).  A small value makes
+ * the waits give up early, from the host, without any kernel hanging; the calls then
+ * fall back to resident precision where they gave up and sf_workspace_check reports
+ * it.  Synchronises the device. */
+sf_status sf_workspace_set_spin_limit(sf_workspace* ws, uint32_t polls);
 
 /* ---- a1: nested quantisation ----------------------------------------------- */
 /* Quantise x fp32 [rows][cols] (cols % 128 == 0) to the nested format above.

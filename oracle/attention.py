@@ -10,7 +10,8 @@ token whose refinement is missing stays at resident precision.
 Readings (the pages give no formula):
 * query head h reads KV head floor(h / G), G = n_q_heads / n_kv_heads;
 * one selection per (batch, kv head): a token's score is the softmax weight of the
-  low-bit logits summed over the G query heads that read that KV head;
+  low-bit logits summed over the G query heads that read that KV head, where a
+  weight below e^-64 of its head's largest counts as zero;
 * for the selected tokens that hit, both the key (for the logit) and the value use
   the (b+r)-bit dequantised vectors; every other token uses the resident b-bit
   ones; the softmax is taken over all T tokens after that replacement.
@@ -35,15 +36,25 @@ def _softmax_rows(logits):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+# A head's softmax weight below e^-64 of its largest weight counts as zero in the
+# selection score (reading: such weights carry no usable signal, and kernels that
+# form the weights in fp32 cannot rank them; tokens whose score is zero tie, and
+# ties go to the lower token).
+SCORE_CUTOFF = -64.0
+
+
 def token_scores(q_f16, k_res, scale):
     """Selection scores of one (batch, kv head).
 
     q_f16 [G][d], k_res [T][d] (resident keys, fp64) -> per token
-    sum over the G heads of softmax_t(scale * q_h . k_t).
+    sum over the G heads of softmax_t(scale * q_h . k_t), where a head contributes
+    nothing for a token whose logit lies more than 64 below that head's maximum.
     """
     q = np.asarray(q_f16, dtype=np.float16).astype(np.float64)
     logits = scale * (q @ k_res.T)  # [G][T]
-    return _softmax_rows(logits).sum(axis=0)
+    w = _softmax_rows(logits)
+    rel = logits - logits.max(axis=-1, keepdims=True)
+    return np.where(rel >= SCORE_CUTOFF, w, 0.0).sum(axis=0)
 
 
 def refined_attention(q_f16, qk, qv, shape, scale, k_sel, sel_in=None, hits=None):

@@ -28,3 +28,16 @@ def golden():
 
     with open(os.path.join(ROOT, "tests", "golden", "worked_examples.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture(autouse=True)
+def _device_waits_completed(request):
+    """After every GPU test: no bounded device-side wait of the library gave up
+    (sf_workspace_check on every workspace the binding created)."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    from bit_decode_selective_amd import binding
+
+    if binding._lib is not None:
+        binding.check_workspaces()

@@ -36,5 +36,47 @@ def topk_is_valid(scores, sel, k, rel=1e-4):
     mask = np.zeros(len(scores), dtype=bool)
     mask[sel] = True
     ok = np.all(scores[mask] >= kth * (1 - rel)) and np.all(scores[~mask] <= kth * (1 + rel))
-    separated = (kth - nxt) > rel * kth
+    # scores of exactly zero (every head's weight below the cutoff) tie exactly on
+    # both sides and go to the lower index: that choice is unique too
+    separated = (kth - nxt) > rel * kth or kth == 0.0
     return bool(ok), bool(separated)
+
+
+def separated_query(cfg, layer, batch, n_kv, G, d, k_res, scale, k_sel, rel=1e-4, max_redraws=400):
+    """A query fp16 [batch][n_kv*G][d] whose oracle token scores separate the k-th and
+    the (k+1)-th token of every (batch, kv head) by at least `rel` (relative), so that
+    the top-k index set is unique in any precision the kernels use.
+
+    k_res(bi, g) -> resident keys fp64 [T][d] of KV head g of batch row bi.  Every
+    (batch, kv head) group starts with its heads of inputs.query(cfg, layer, 0, ...);
+    while its scores have a near-tie at the boundary it takes its heads from the draw
+    of the next step.  Returns (q, steps): steps[(bi, g)] = the step used."""
+    from bit_decode_selective_amd import inputs
+    from oracle import attention as o_attn
+
+    n_q = n_kv * G
+    draws = {0: inputs.query(cfg, layer, 0, batch, n_q, d)}
+    q = draws[0].copy()
+    steps = {}
+    for bi in range(batch):
+        for g in range(n_kv):
+            kr = k_res(bi, g)
+            for step in range(max_redraws):
+                if step not in draws:
+                    draws[step] = inputs.query(cfg, layer, step, batch, n_q, d)
+                qg = draws[step][bi, g * G:(g + 1) * G]
+                if k_sel == 0 or token_gap(o_attn.token_scores(qg, kr, scale), k_sel) >= rel:
+                    q[bi, g * G:(g + 1) * G] = qg
+                    steps[(bi, g)] = step
+                    break
+            else:
+                raise RuntimeError(f"no separated query for group {(bi, g)} in {max_redraws} draws")
+    return q, steps
+
+
+def token_gap(scores, k):
+    """Relative gap (s_k - s_{k+1}) / s_k of the k-th and (k+1)-th largest scores."""
+    order = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
+    if k == 0 or k >= len(order):
+        return np.inf
+    return (order[k - 1] - order[k]) / order[k - 1]

@@ -1,7 +1,11 @@
-"""GPU parity: refined GQA decode attention.  Token selection must be the oracle's
-top-k (exactly, when the k-th and (k+1)-th oracle scores are separated by more than
-1e-4 relative; otherwise a valid top-k within that margin), and the output must match
-the oracle evaluated on the kernel's selection within 1e-3 rel / 1e-4 abs."""
+"""GPU parity: refined GQA decode attention, through the C ABI.
+
+Queries are drawn without near-ties: for every (batch, kv head) the k-th and
+(k+1)-th oracle token scores differ by at least 1e-4 relative (the group's heads
+are redrawn from the next step's query until they do), so the selected index set
+is unique and must equal the oracle's exactly.  Outputs must match the oracle
+within 1e-3 rel / 1e-4 abs; with every selected unit resident in the cache the
+oracle runs on its own selection, so a wrong choice shows in the output too."""
 import math
 
 import numpy as np
@@ -12,110 +16,154 @@ from bit_decode_selective_amd import binding, inputs
 from oracle import attention as o_attn
 from oracle import nested, selection
 
-from gpu_util import assert_close, topk_is_valid
+from gpu_util import assert_close, separated_query
 
 pytestmark = pytest.mark.gpu
 
-
-def _case(cfg, batch, n_kv, G, T, b=2, r=2, q_scale=1.0):
-    K, V = inputs.kv(cfg, 0, batch, n_kv, T, 128)
-    q = (inputs.query(cfg, 0, 0, batch, n_kv * G, 128).astype(np.float32) * q_scale).astype(np.float16)
-    kv = binding.QuantKV.from_host(K, V, b, r)
-    qk = o_attn.quantize_kv(K, b, r)
-    qv = o_attn.quantize_kv(V, b, r)
-    return K, V, q, kv, qk, qv
+D = 128
+SCALE = 1.0 / math.sqrt(D)
 
 
-def _check(q, kv, qk, qv, shape, k_sel, cache="resident", exact_required=False):
-    batch, n_kv, T, d = shape
-    scale = 1.0 / math.sqrt(d)
+class Case:
+    """Seeded K/V of one layer, quantised on the GPU and in the oracle."""
+
+    def __init__(self, cfg, batch, n_kv, G, T, b=2, r=2, t_cap=None):
+        self.cfg, self.batch, self.n_kv, self.G, self.T, self.b, self.r = cfg, batch, n_kv, G, T, b, r
+        K, V = inputs.kv(cfg, 0, batch, n_kv, T, D)
+        self.kv = binding.QuantKV.from_host(K, V, b, r, t_cap=t_cap)
+        self.qk = o_attn.quantize_kv(K, b, r)
+        self.qv = o_attn.quantize_kv(V, b, r)
+        self.k_res = nested.dequant_resident(self.qk).reshape(batch, n_kv, T, D)
+
+    @property
+    def shape(self):
+        return (self.batch, self.n_kv, self.T, D)
+
+    def query(self, k_sel):
+        q, _ = separated_query(self.cfg, 0, self.batch, self.n_kv, self.G, D, lambda bi, g: self.k_res[bi, g],
+                               SCALE, k_sel)
+        return q
+
+
+def _run(case, q, k_sel, cache="resident", sel_in=None):
     if cache == "resident":
-        cache = binding.RefineCache([kv.resident_pool_desc()])
-    out, sel, hit = binding.refined_attention(q, kv, scale, k_sel, cache=cache)
+        cache = binding.RefineCache([case.kv.resident_pool_desc()])
+    out, sel, hit = binding.refined_attention(q, case.kv, SCALE, k_sel, cache=cache, sel_in=sel_in)
     torch.cuda.synchronize()
-    out, sel, hit = out.cpu().numpy(), sel.cpu().numpy(), hit.cpu().numpy()
-    k_res = nested.dequant_resident(qk).reshape(batch, n_kv, T, d)
-    G = q.shape[1] // n_kv
-    n_exact = 0
-    for bi in range(batch):
-        for g in range(n_kv):
-            sc = o_attn.token_scores(q[bi, g * G:(g + 1) * G], k_res[bi, g], scale)
-            s = sel[bi, g].tolist()
-            assert s == sorted(s)
-            ok, separated = topk_is_valid(sc, s, k_sel)
-            assert ok, (bi, g)
-            if separated:
-                assert s == selection.top_k(sc, k_sel), (bi, g)
-                n_exact += 1
-    if exact_required:
-        assert n_exact == batch * n_kv
-    hits = None
-    if cache is None:
-        hits = {}
-    sel_map = {(bi, g): sel[bi, g].tolist() for bi in range(batch) for g in range(n_kv)}
-    if cache is not None and cache != "resident":
-        hits = {(bi, g): {t for t, h in zip(sel[bi, g], hit[bi, g]) if h >= 0}
-                for bi in range(batch) for g in range(n_kv)}
-    ref, _ = o_attn.refined_attention(q, qk, qv, shape, scale, k_sel, sel_in=sel_map, hits=hits)
-    assert_close(out, ref, what=f"attention T={T} k={k_sel}")
+    return out.cpu().numpy(), sel.cpu().numpy(), hit.cpu().numpy()
+
+
+def _check(case, q, k_sel, cache="resident"):
+    """Exact selection per (batch, kv head) and the output against the oracle's own
+    refined attention (every hit when the pool is resident, else the reported hits)."""
+    out, sel, hit = _run(case, q, k_sel, cache)
+    G = case.G
+    for bi in range(case.batch):
+        for g in range(case.n_kv):
+            sc = o_attn.token_scores(q[bi, g * G:(g + 1) * G], case.k_res[bi, g], SCALE)
+            assert sel[bi, g].tolist() == selection.top_k(sc, k_sel), (bi, g)
+    if cache == "resident":
+        ref, chosen = o_attn.refined_attention(q, case.qk, case.qv, case.shape, SCALE, k_sel)
+        assert all(chosen[(bi, g)] == sel[bi, g].tolist() for bi in range(case.batch) for g in range(case.n_kv))
+    else:
+        hits = {(bi, g): {int(t) for t, h in zip(sel[bi, g], hit[bi, g]) if h >= 0}
+                for bi in range(case.batch) for g in range(case.n_kv)}
+        sel_map = {(bi, g): sel[bi, g].tolist() for bi in range(case.batch) for g in range(case.n_kv)}
+        ref, _ = o_attn.refined_attention(q, case.qk, case.qv, case.shape, SCALE, k_sel, sel_in=sel_map, hits=hits)
+    assert_close(out, ref, what=f"attention T={case.T} k={k_sel}")
     return out, sel, hit
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_small(G):
-    batch, n_kv, T = 2, 2, 300
-    K, V, q, kv, qk, qv = _case(20 + G, batch, n_kv, G, T)
-    for k_sel in (0, 1, 7, T):
-        _check(q, kv, qk, qv, (batch, n_kv, T, 128), k_sel)
+    case = Case(20 + G, 2, 2, G, 300)
+    for k_sel in (0, 1, 7, 300):
+        _check(case, case.query(k_sel), k_sel)
 
 
 @pytest.mark.parametrize("b,r", [(1, 1), (4, 4), (2, 1)])
 def test_formats(b, r):
-    K, V, q, kv, qk, qv = _case(30 + b, 1, 2, 4, 777, b, r)
-    _check(q, kv, qk, qv, (1, 2, 777, 128), 16)
+    case = Case(30 + b, 1, 2, 4, 777, b, r)
+    _check(case, case.query(16), 16)
 
 
 def test_single_token_and_tiny():
     for T in (1, 2, 65):
-        K, V, q, kv, qk, qv = _case(40 + T, 1, 1, 4, T)
-        _check(q, kv, qk, qv, (1, 1, T, 128), min(T, 3))
+        case = Case(40 + T, 1, 1, 4, T)
+        k = min(T, 3)
+        _check(case, case.query(k), k)
 
 
 def test_uniform_query_selects_first_tokens():
-    K, V, q, kv, qk, qv = _case(50, 1, 2, 4, 200)
-    q = np.zeros_like(q)
-    out, sel, _ = _check(q, kv, qk, qv, (1, 2, 200, 128), 5)
-    assert sel[0, 0].tolist() == [0, 1, 2, 3, 4]
+    """q = 0: every logit is 0 and every score equal, so the lowest tokens win."""
+    case = Case(50, 1, 2, 4, 200)
+    q = np.zeros((1, 8, D), dtype=np.float16)
+    out, sel, _ = _check(case, q, 5)
+    assert sel[0, 0].tolist() == sel[0, 1].tolist() == [0, 1, 2, 3, 4]
 
 
 def test_misses_fall_back_to_resident():
-    K, V, q, kv, qk, qv = _case(51, 1, 2, 4, 500)
-    _, sel, hit = _check(q, kv, qk, qv, (1, 2, 500, 128), 10, cache=None)
+    case = Case(51, 1, 2, 4, 500)
+    _, sel, hit = _check(case, case.query(10), 10, cache=None)
     assert np.all(hit == -1)
 
 
 def test_external_selection():
-    batch, n_kv, G, T = 1, 2, 4, 400
-    K, V, q, kv, qk, qv = _case(52, batch, n_kv, G, T)
+    case = Case(52, 1, 2, 4, 400)
     rng = np.random.default_rng(1)
-    ext = np.stack([np.sort(rng.choice(T, 9, replace=False)) for _ in range(n_kv)])[None].astype(np.int32)
-    cache = binding.RefineCache([kv.resident_pool_desc()])
-    out, sel, hit = binding.refined_attention(q, kv, 1 / math.sqrt(128), 9, cache=cache, sel_in=ext)
-    assert np.array_equal(sel.cpu().numpy(), ext)
-    ref, _ = o_attn.refined_attention(q, qk, qv, (batch, n_kv, T, 128), 1 / math.sqrt(128), 9,
-                                      sel_in={(0, g): ext[0, g].tolist() for g in range(n_kv)})
-    assert_close(out.cpu().numpy(), ref)
+    ext = np.stack([np.sort(rng.choice(400, 9, replace=False)) for _ in range(2)])[None].astype(np.int32)
+    q = inputs.query(52, 0, 0, 1, 8, D)
+    out, sel, _ = _run(case, q, 9, sel_in=ext)
+    assert np.array_equal(sel, ext)
+    ref, _ = o_attn.refined_attention(q, case.qk, case.qv, case.shape, SCALE, 9,
+                                      sel_in={(0, g): ext[0, g].tolist() for g in range(2)})
+    assert_close(out, ref)
 
 
 def test_full_size_32k():
     """32 query heads, 8 KV heads, head dim 128, T = 32768, 2 + 2 bit KV, top 2% tokens."""
-    batch, n_kv, G, T = 1, 8, 4, 32768
-    K, V, q, kv, qk, qv = _case(3, batch, n_kv, G, T)
-    _check(q, kv, qk, qv, (batch, n_kv, T, 128), selection.k_select(2, T))
+    case = Case(3, 1, 8, 4, 32768)
+    ks = selection.k_select(2, 32768)
+    _check(case, case.query(ks), ks)
 
 
 def test_ragged_long_context():
     """T = 40000: ten selection chunks, the last one ragged."""
-    batch, n_kv, G, T = 1, 1, 4, 40000
-    K, V, q, kv, qk, qv = _case(53, batch, n_kv, G, T)
-    _check(q, kv, qk, qv, (batch, n_kv, T, 128), selection.k_select(2, T))
+    case = Case(53, 1, 1, 4, 40000)
+    ks = selection.k_select(2, 40000)
+    _check(case, case.query(ks), ks)
+
+
+def test_batch8_context_8k():
+    """Batch 8 at context 8192 (the batch-8 full-step shape): 64 (batch, kv head)
+    selections of 164 tokens each."""
+    case = Case(4, 8, 8, 4, 8192)
+    ks = selection.k_select(2, 8192)
+    _check(case, case.query(ks), ks)
+
+
+def test_full_size_128k():
+    """T = 131072, 8 KV heads, 2 + 2 bit KV, top 2% (2622 tokens per KV head): every
+    selection exact; the output of every KV head against the oracle, one KV head at a
+    time (the oracle's dequantised cache of all heads would not fit a test's memory)."""
+    T, n_kv, G = 131072, 8, 4
+    K, V = inputs.kv(5, 0, 1, n_kv, T, D)
+    kv = binding.QuantKV.from_host(K, V, 2, 2)
+    ks = selection.k_select(2, T)
+    per_head = []
+    for g in range(n_kv):
+        qk = o_attn.quantize_kv(K[:, g:g + 1], 2, 2)
+        qv = o_attn.quantize_kv(V[:, g:g + 1], 2, 2)
+        per_head.append((qk, qv, nested.dequant_resident(qk)))
+    del K, V
+    q, _ = separated_query(5, 0, 1, n_kv, G, D, lambda bi, g: per_head[g][2], SCALE, ks)
+    cache = binding.RefineCache([kv.resident_pool_desc()])
+    out, sel, hit = binding.refined_attention(q, kv, SCALE, ks, cache=cache)
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    for g in range(n_kv):
+        qk, qv, k_res = per_head[g]
+        qg = q[:, g * G:(g + 1) * G]
+        assert sel[0, g].tolist() == selection.top_k(o_attn.token_scores(qg[0], k_res, SCALE), ks), g
+        ref, _ = o_attn.refined_attention(qg, qk, qv, (1, 1, T, D), SCALE, ks)
+        assert_close(out[:, g * G:(g + 1) * G], ref, what=f"128K kv head {g}")

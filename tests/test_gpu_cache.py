@@ -140,3 +140,36 @@ def test_pageable_store_is_refused():
         binding.RefineCache([binding.host_pool_desc(pageable, 8)], keep=[pageable])
     # a pool without slots never reads its store
     binding.RefineCache([binding.host_pool_desc(pageable, 0)], keep=[pageable])
+
+
+def test_lookup_call_matches_oracle_lru():
+    """sf_refine_cache_lookup on its own: the slot of every resident unit and -1 for
+    the rest, in the order asked; its lookups are logged like the kernels' own, so
+    the fills that follow install the same units as the oracle LRU (two lookup calls
+    per step, repeated and duplicate ids, a pool smaller than one step's lookups)."""
+    qw, _ = _weight(64, 256, 512, 2, 2)
+    store = qw.host_store()
+    cap = 24
+    cache = binding.RefineCache([binding.host_pool_desc(store, cap, max_lookup=64)], keep=[store])
+    pool = o_cache.LRUPool(cap)
+    rng = np.random.default_rng(5)
+    for t in range(10):
+        for call in range(2):
+            ids = rng.choice(48, 20, replace=False).astype(np.int32)
+            if call == 1:
+                ids[:3] = ids[3]  # the same unit three times in one call
+            slots = cache.lookup(0, torch.as_tensor(ids, device="cuda")).cpu().numpy()
+            want = pool.lookup(ids.tolist(), t)
+            assert (slots >= 0).tolist() == want, (t, call)
+            hit_slots = slots[slots >= 0]
+            assert np.all(hit_slots < cap)
+            # a unit has one slot, and different units have different slots
+            by_unit = {}
+            for u, s in zip(ids.tolist(), slots.tolist()):
+                if s >= 0:
+                    assert by_unit.setdefault(u, s) == s
+            assert len(set(by_unit.values())) == len(by_unit)
+        cache.fill()
+        pool.fill(t)
+        assert cache.resident(0, cap) == pool.resident(), t
+    assert cache.stats(0)["lookups"] == 10 * 2 * 20

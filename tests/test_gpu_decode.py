@@ -19,6 +19,7 @@ import torch
 
 from bit_decode_selective_amd import binding, decode, inputs
 from oracle import attention as o_attn
+from oracle import cache as o_cache
 from oracle import decode as o_dec
 from oracle import gemv as o_gemv
 from oracle import nested, selection
@@ -96,44 +97,80 @@ TINY_LLAMA = decode.Spec("tiny-llama", 2, 256, 4, 2, 512, 1024, False, 500000.0,
 TINY_QWEN = decode.Spec("tiny-qwen", 2, 256, 4, 2, 384, 1280, True, 1000000.0, 1e-6)
 
 
-def _gemv_check(model, li, names, x16, ys, sel_t, k_in, what):
-    """Selection = oracle top-k of the GPU's fp16 input; outputs = oracle GEMV on it."""
+class Quants:
+    """Oracle quantisation of each host weight, computed once per test."""
+
+    def __init__(self, model):
+        self.model, self.q = model, {}
+
+    def __call__(self, key):
+        if key not in self.q:
+            m = self.model
+            self.q[key] = nested.quantize(m.host[key], m.b, m.r, 128)
+        return self.q[key]
+
+
+def _pool_of(model, li, name):
+    if li >= model.spec.layers:
+        return model.pool_lm
+    return model.layers[li].get("pool_" + name, -1)
+
+
+def _gemv_check(model, li, names, x16, ys, sel_t, k_in, what, quants, lru=None, step=0, outputs=True):
+    """Selection = oracle top-k of the GPU's fp16 input; the hit set of each matrix =
+    the oracle LRU's (or every channel for resident pools); outputs = oracle GEMV on
+    the hit channels."""
     ks = decode.k_select(model.ch_pct, k_in)
     x = x16.astype(np.float16)
     sel = sel_t.cpu().numpy()[:ks].tolist()
     assert sel == selection.select_channels(x, ks), what
     for name, y in zip(names, ys):
-        W = model.host[(li, name)]
+        key = (li, name)
         hit = model.hits[(li if li < model.spec.layers else -1, name if li < model.spec.layers else "lm_head")]
-        assert np.all(hit.cpu().numpy()[:ks] >= 0)  # resident pools
-        q = nested.quantize(W, model.b, model.r, 128)
-        assert_close(y, o_gemv.refined_gemv(q, x, sel), what=f"{what} {name}")
+        got_hits = (hit.cpu().numpy()[:ks] >= 0).tolist()
+        if lru is None:
+            want_hits = [True] * ks  # resident pools
+        else:
+            want_hits = lru[_pool_of(model, li, name)].lookup(sel, step)
+        assert got_hits == want_hits, f"{what} {name} hits"
+        if outputs:
+            chans = [k for k, h in zip(sel, want_hits) if h]
+            assert_close(y, o_gemv.refined_gemv(quants(key), x, chans), what=f"{what} {name}")
 
 
 TENSOR = {"q": inputs.Q_PROJ, "k": inputs.K_PROJ, "v": inputs.V_PROJ, "o": inputs.O_PROJ, "gate": inputs.GATE,
           "up": inputs.UP, "down": inputs.DOWN}
 
 
-@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
-@pytest.mark.parametrize("batch", [1, 2])
-def test_decode_steps(spec, batch):
-    src = decode.HostWeights(70 + batch)
-    T0, steps = 40, 2
-    model = decode.DecodeModel(spec, batch, T0 + steps, src)
-    # host weight keys by name
+def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None):
+    """Teacher-forced decode steps; every operation of every step checked against the
+    oracle on the GPU's own inputs.  With pool_frac, the LRU pools of every weight,
+    KV cache and lm_head are replayed by the oracle (``cache.LRUPool``): each GEMV's
+    and each attention's hit set must be the oracle's, and every pool's resident set
+    must agree after each step's fill.  output_steps: the steps whose operation
+    outputs are compared (all by default); selections and hit sets are checked at
+    every step."""
+    src = decode.HostWeights(cfg)
+    model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac)
     for li in range(spec.layers):
         for name, t in TENSOR.items():
             model.host[(li, name)] = model.host[(li, t)]
     model.host[(spec.layers, "lm_head")] = model.host[(spec.layers, inputs.LM_HEAD)]
     model.fill_kv(T0, src)
+    quants = Quants(model)
+    lru = None
+    if pool_frac is not None:
+        lru = {i: o_cache.LRUPool(int(p.capacity)) for i, p in enumerate(model._pools)}
     S, d = spec, spec.head_dim
     kv_host = {li: model.host[("kv", li)] for li in range(S.layers)}
     appended = {li: ([], []) for li in range(S.layers)}
-    ids = inputs.tokens(70, steps, batch, S.vocab)
+    ids = inputs.tokens(cfg, steps, batch, S.vocab)
     for step in range(steps):
+        outs = output_steps is None or step in output_steps
         pos = model.pos
         nxt = model.step(ids[step])
         torch.cuda.synchronize()
+        binding.check_workspaces()
         # rebuild the residual stream in fp64 from the GPU's op outputs
         h = o_dec.embed(model.host["embed"], ids[step])
         for li, L in enumerate(model.layers):
@@ -142,7 +179,8 @@ def test_decode_steps(spec, batch):
             assert_close(x, o_dec.to_f16(o_dec.rmsnorm(h, L["attn_norm"].cpu().numpy(), S.eps)).astype(np.float64),
                          what=f"layer {li} attn norm", **F16)
             ys = [bf[n].cpu().numpy() for n in ("q", "k", "v")]
-            _gemv_check(model, li, ("q", "k", "v"), x, ys, bf["sel_attn"], S.hidden, f"step {step} layer {li} qkv")
+            _gemv_check(model, li, ("q", "k", "v"), x, ys, bf["sel_attn"], S.hidden, f"step {step} layer {li} qkv",
+                        quants, lru, step, outs)
             qn = L["q_norm"].cpu().numpy() if S.qk_norm else None
             kn = L["k_norm"].cpu().numpy() if S.qk_norm else None
             qh, kh = o_dec.qk_heads(ys[0], ys[1], S.n_q, S.n_kv, d, qn, kn, S.eps, pos, S.theta)
@@ -159,38 +197,94 @@ def test_decode_steps(spec, batch):
             qk = o_attn.quantize_kv(K, model.kv_b, model.kv_r)
             qv = o_attn.quantize_kv(V, model.kv_b, model.kv_r)
             kt = decode.k_select(model.tok_pct, T)
-            sel = bf["sel_tok"].reshape(-1)[: batch * S.n_kv * kt].reshape(batch, S.n_kv, kt).cpu().numpy()
+            n_sel = batch * S.n_kv * kt
+            sel = bf["sel_tok"].reshape(-1)[:n_sel].reshape(batch, S.n_kv, kt).cpu().numpy()
+            hit = bf["hit_tok"].reshape(-1)[:n_sel].reshape(batch, S.n_kv, kt).cpu().numpy()
             scale = 1.0 / math.sqrt(d)
             k_res = nested.dequant_resident(qk).reshape(batch, S.n_kv, T, d)
             G = S.n_q // S.n_kv
             for bi in range(batch):
                 for g in range(S.n_kv):
                     sc = o_attn.token_scores(q16.astype(np.float16)[bi, g * G:(g + 1) * G], k_res[bi, g], scale)
-                    ok, _ = topk_is_valid(sc, sel[bi, g].tolist(), kt)
+                    ok, separated = topk_is_valid(sc, sel[bi, g].tolist(), kt)
                     assert ok, (step, li, bi, g)
+                    if separated:
+                        assert sel[bi, g].tolist() == selection.top_k(sc, kt), (step, li, bi, g)
             sel_map = {(bi, g): sel[bi, g].tolist() for bi in range(batch) for g in range(S.n_kv)}
-            ref, _ = o_attn.refined_attention(q16.astype(np.float16), qk, qv, (batch, S.n_kv, T, d), scale, kt,
-                                              sel_in=sel_map)
+            hits = None
+            if lru is not None:
+                units = [(bi * S.n_kv + g) * model.t_cap + int(t) for bi in range(batch) for g in range(S.n_kv)
+                         for t in sel[bi, g]]
+                want = lru[L["pool_kv"]].lookup(units, step)
+                assert (hit.reshape(-1) >= 0).tolist() == want, f"step {step} layer {li} KV hits"
+                hits = {(bi, g): {int(t) for t, hh in zip(sel[bi, g], hit[bi, g]) if hh >= 0}
+                        for bi in range(batch) for g in range(S.n_kv)}
             attn = bf["attn"].cpu().numpy()
-            assert_close(attn, ref, what=f"step {step} layer {li} attention")
+            if outs:
+                ref, _ = o_attn.refined_attention(q16.astype(np.float16), qk, qv, (batch, S.n_kv, T, d), scale, kt,
+                                                  sel_in=sel_map, hits=hits)
+                assert_close(attn, ref, what=f"step {step} layer {li} attention")
             a16 = _f16(bf["a16"])
             assert np.array_equal(a16, attn.reshape(batch, -1).astype(np.float16).astype(np.float64))
             o = bf["o"].cpu().numpy()
-            _gemv_check(model, li, ("o",), a16, [o], bf["sel_o"], S.n_q * d, f"layer {li} o")
+            _gemv_check(model, li, ("o",), a16, [o], bf["sel_o"], S.n_q * d, f"step {step} layer {li} o", quants, lru,
+                        step, outs)
             h = h + o.astype(np.float64)
             x2 = _f16(bf["x_ffn"])
             assert_close(x2, o_dec.to_f16(o_dec.rmsnorm(h, L["ffn_norm"].cpu().numpy(), S.eps)).astype(np.float64),
                          what=f"layer {li} ffn norm", **F16)
             gu = [bf[n].cpu().numpy() for n in ("gate", "up")]
-            _gemv_check(model, li, ("gate", "up"), x2, gu, bf["sel_ffn"], S.hidden, f"layer {li} gate/up")
+            _gemv_check(model, li, ("gate", "up"), x2, gu, bf["sel_ffn"], S.hidden, f"step {step} layer {li} gate/up",
+                        quants, lru, step, outs)
             act = _f16(bf["act"])
             assert_close(act, o_dec.swiglu(gu[0], gu[1]), what="swiglu", **F16)
             dn = bf["down"].cpu().numpy()
-            _gemv_check(model, li, ("down",), act, [dn], bf["sel_down"], S.ffn, f"layer {li} down")
+            _gemv_check(model, li, ("down",), act, [dn], bf["sel_down"], S.ffn, f"step {step} layer {li} down", quants,
+                        lru, step, outs)
             h = h + dn.astype(np.float64)
         xf = _f16(model.x_final)
         assert_close(xf, o_dec.to_f16(o_dec.rmsnorm(h, model.final_norm.cpu().numpy(), S.eps)).astype(np.float64),
                      what="final norm", **F16)
         logits = model.logits.cpu().numpy()
-        _gemv_check(model, S.layers, ("lm_head",), xf, [logits], model.sel_lm, S.hidden, "lm_head")
+        _gemv_check(model, S.layers, ("lm_head",), xf, [logits], model.sel_lm, S.hidden, f"step {step} lm_head",
+                    quants, lru, step, outs)
         assert nxt.cpu().numpy().tolist() == o_dec.argmax(logits).tolist()
+        if lru is not None:
+            for i, p in lru.items():
+                p.fill(step)
+                assert model.cache.resident(i, max(1, p.capacity)) == p.resident(), (step, i)
+
+
+TINY_LLAMA = decode.Spec("tiny-llama", 2, 256, 4, 2, 512, 1024, False, 500000.0, 1e-5)
+TINY_QWEN = decode.Spec("tiny-qwen", 2, 256, 4, 2, 384, 1280, True, 1000000.0, 1e-6)
+
+
+@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
+@pytest.mark.parametrize("batch", [1, 2])
+def test_decode_steps(spec, batch):
+    _run_steps(spec, batch, 40, 2, 70 + batch)
+
+
+@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
+def test_decode_steps_lru_pools(spec):
+    """Small decoders with LRU pools holding 25% of every tensor's units over 8 steps."""
+    _run_steps(spec, 2, 60, 8, 80, pool_frac=0.25)
+
+
+# full hidden width, two layers, a 4096-token vocabulary (the lm_head's shape aside,
+# every matrix has the model's own size)
+WIDE_LLAMA = decode.Spec("llama-3.1-8b-width-2-layers", 2, 4096, 32, 8, 14336, 4096, False, 500000.0, 1e-5)
+WIDE_QWEN = decode.Spec("qwen3-8b-width-2-layers", 2, 4096, 32, 8, 12288, 4096, True, 1000000.0, 1e-6)
+
+
+def test_decode_full_width_qwen3_pools25():
+    """The Qwen3-8B workload's step at full width: 2+2-bit weights and KV, pools of 25%
+    with LRU replacement and deterministic fills, 8 steps; every operation's output
+    checked on the first and last step, selections and hit sets on all."""
+    _run_steps(WIDE_QWEN, 1, 192, 8, 90, pool_frac=0.25, output_steps={0, 7})
+
+
+def test_decode_full_width_llama_w3r1_pools10():
+    """The 128K workload's formats at full width: 3-bit weights + 1 refinement bit,
+    2+2-bit KV, pools of 10%, 8 steps (short context)."""
+    _run_steps(WIDE_LLAMA, 1, 192, 8, 91, b=3, r=1, pool_frac=0.10, output_steps={0, 7})

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, nested
+from oracle import attention, selection, nested
 
 
 def _cache(K, V, b=2, r=2):
@@ -85,6 +85,28 @@ def test_summed_softmax_scores_by_hand():
     q2 = np.array([[1.0, 1.2, 0, 0], [1.0, 0, 1.2, 0]], dtype=np.float16)
     s2 = attention.token_scores(q2, k2, 1.0)
     assert s2[0] > s2[1] and s2[0] > s2[2]
+
+
+def test_negligible_weights_score_zero_and_tie_to_lower_tokens():
+    """A head's weight counts in the score only while the token's logit is within 64
+    of the head's maximum: logits 0, -10, -63.5, -70, -80 (one head) score their
+    softmax weights for the first three and exactly 0 for the last two, which then
+    tie and go to the lower token."""
+    k_res = np.zeros((5, 4))
+    k_res[:, 0] = [0.0, -10.0, -63.5, -70.0, -80.0]
+    q = np.array([[1.0, 0.0, 0.0, 0.0]], dtype=np.float16)
+    sc = attention.token_scores(q, k_res, 1.0)
+    e = [math.exp(v) for v in (0.0, -10.0, -63.5, -70.0, -80.0)]
+    z = sum(e)
+    np.testing.assert_allclose(sc[:3], [v / z for v in e[:3]], rtol=1e-14)
+    assert sc[3] == 0.0 and sc[4] == 0.0
+    assert selection.top_k(sc, 4) == [0, 1, 2, 3]
+    # with two heads a token keeps the weight of the head that still sees it
+    q2 = np.array([[1.0, 0.0, 0.0, 0.0], [-1.0, 0.0, 0.0, 0.0]], dtype=np.float16)
+    s2 = attention.token_scores(q2, k_res, 1.0)
+    e2 = [math.exp(-v - 80.0) for v in (0.0, -10.0, -63.5, -70.0, -80.0)]  # head 2: logits 0..80, max 80
+    np.testing.assert_allclose(s2[4], 1.0 / sum(e2) + 0.0, rtol=1e-14)
+    assert s2[0] == e[0] / z  # head 2 sees token 0 at 80 below its max: nothing added
 
 
 def _sdpa(q_f16, Kd, Vd, scale):
