@@ -99,6 +99,7 @@ _PROTOS = {
     "sf_refine_cache_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(I64), C.POINTER(I64)]),
     "sf_refine_cache_resident": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64)]),
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
+    "sf_refined_gemv_noalloc": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
     "sf_embed": (I32, [VP, I64, I32, VP, I32, VP, VP]),
     "sf_add_rmsnorm": (I32, [VP, VP, VP, I32, I32, C.c_float, VP, VP]),

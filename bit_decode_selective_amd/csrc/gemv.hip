@@ -22,6 +22,9 @@
 //     written: the refinement words of the tile's rows in every hit slot are
 //     requested when the tile starts and consumed after its chunks.
 
+#include <mutex>
+#include <string>
+
 #include "gemv_rows.h"
 
 namespace sfg {
@@ -634,13 +637,13 @@ extern "C" size_t sf_workspace_bytes_gemv(const sf_gemv_op* ops, int32_t n_ops, 
   return gemv_ws_layout(n_ops, k_sel, part, &a, &b, &c);
 }
 
-extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
-                                     int32_t batch, int32_t k_sel, const int32_t* sel_in,
-                                     int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
-                                     sf_stream stream) {
+// The refined GEMV on a workspace at ws_base (ws_bytes long, control block zeroed
+// and left zeroed by every call).
+static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16, int32_t batch,
+                                 int32_t k_sel, const int32_t* sel_in, int32_t* sel_out, sf_refine_cache* cache,
+                                 uint8_t* ws_base, size_t ws_bytes, sf_stream stream) {
   SF_REQUIRE(ops && n_ops >= 1 && n_ops <= SF_MAX_OPS, SF_EINVAL, "need 1..4 ops");
   SF_REQUIRE(x_f16 && batch >= 1, SF_EINVAL, "bad x / batch");
-  SF_REQUIRE(ws, SF_EINVAL, "workspace required");
   const sf_qfmt f = ops[0].w.fmt;
   const int64_t K = ops[0].w.k_in;
   SF_REQUIRE(f.group == 128 && f.b >= 1 && f.r >= 0 && f.b + f.r <= 8, SF_EUNSUPPORTED, "bad format");
@@ -684,13 +687,13 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     tiles += (int)((o.w.n_out + rows_wg - 1) / rows_wg);
   }
   size_t o_sel, o_slot, o_part;
-  SF_REQUIRE(ws->bytes >= gemv_ws_layout(n_ops, k_sel, mp.part_bytes, &o_sel, &o_slot, &o_part), SF_ENOMEM,
+  SF_REQUIRE(ws_bytes >= gemv_ws_layout(n_ops, k_sel, mp.part_bytes, &o_sel, &o_slot, &o_part), SF_ENOMEM,
              "workspace too small");
   a.x = x_f16;
   a.sel_in = sel_in;
   a.sel_out = sel_out;
-  a.ws_sel = (int32_t*)(ws->base + o_sel);
-  a.ws_slot = (int32_t*)(ws->base + o_slot);
+  a.ws_sel = (int32_t*)(ws_base + o_sel);
+  a.ws_slot = (int32_t*)(ws_base + o_slot);
   a.n_ops = n_ops;
   a.k_in = (int32_t)K;
   a.batch = batch;
@@ -727,8 +730,8 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     a.gs = mp.gs;
     a.nhp = mp.nhp;
     a.rows_pad = tiles * rows_wg;
-    a.part = (float*)(ws->base + o_part);
-    a.ctr = (uint32_t*)(ws->base + offsetof(WsControl, row_ctr));
+    a.part = (float*)(ws_base + o_part);
+    a.ctr = (uint32_t*)(ws_base + offsetof(WsControl, row_ctr));
     for (int b0 = 0; b0 < batch; b0 += 16) {
       const int nb = batch - b0 < 16 ? batch - b0 : 16;
       a.batch_off = b0;
@@ -741,7 +744,7 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
   a.report = one_launch ? 1 : 0;
   if (!one_launch && k_sel > 0) a.sel_in = a.ws_sel;
   a.sel_wg = (kind == KIND_SPLIT && k_sel > 0) ? 1 : 0;
-  a.ctl = (uint32_t*)ws->base;
+  a.ctl = (uint32_t*)ws_base;
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;
@@ -749,4 +752,73 @@ extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const
     if (st != SF_OK) return st;
   }
   return SF_OK;
+}
+
+extern "C" sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
+                                     int32_t batch, int32_t k_sel, const int32_t* sel_in,
+                                     int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
+                                     sf_stream stream) {
+  SF_REQUIRE(ws, SF_EINVAL, "workspace required");
+  return refined_gemv_on(ops, n_ops, x_f16, batch, k_sel, sel_in, sel_out, cache, ws->base, ws->bytes, stream);
+}
+
+// ---- the same call without a workspace: a library-owned scratch array ------------
+// For callers that cannot allocate (graph capture, serving loops).  The array is a
+// file-scope device variable: each device the library runs on holds its own copy
+// from module load until the process ends.  Host code never uses the array's name as
+// an address: its device address comes from hipGetSymbolAddress, once per device.
+namespace {
+constexpr size_t SF_SCRATCH_BYTES = size_t(8) << 20;
+__device__ __align__(256) uint8_t scratch[SF_SCRATCH_BYTES];
+constexpr int SF_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[SF_MAX_DEVICES] = {};
+
+// Clears the control block's flags and counters (the split kernel's hand-off words,
+// the batched kernel's row-block counters and the timeout word) on the stream.
+__global__ void scratch_clear_kernel(uint32_t* ctl) {
+  WsControl* c = (WsControl*)ctl;
+  for (int i = threadIdx.x; i < 64 * 32; i += blockDim.x) {
+    c->sel_flag[i] = 0u;
+    c->rd_ctr[i] = 0u;
+  }
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) c->row_ctr[i] = 0u;
+  if (threadIdx.x == 0) {
+    c->sel_state = 0u;
+    c->done = 0u;
+    c->timeout = 0u;
+    c->spin_limit = 0u;
+  }
+}
+
+sf_status scratch_of_device(uint8_t** out) {
+  int dev = 0;
+  SF_HIP(hipGetDevice(&dev));
+  SF_REQUIRE(dev >= 0 && dev < SF_MAX_DEVICES, SF_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    SF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    SF_REQUIRE(p != nullptr, SF_EHIP, "no device address for the scratch array");
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SF_OK;
+}
+}  // namespace
+
+extern "C" sf_status sf_refined_gemv_noalloc(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
+                                             int32_t batch, int32_t k_sel, const int32_t* sel_in,
+                                             int32_t* sel_out, sf_refine_cache* cache, sf_stream stream) {
+  SF_REQUIRE(ops && n_ops >= 1 && n_ops <= SF_MAX_OPS && batch >= 1, SF_EINVAL, "need 1..4 ops and batch >= 1");
+  const size_t need = sf_workspace_bytes_gemv(ops, n_ops, batch, k_sel);
+  SF_REQUIRE(need <= SF_SCRATCH_BYTES, SF_ENOMEM,
+             "this call needs " + std::to_string(need) + " bytes of scratch; the scratch array holds " +
+                 std::to_string(SF_SCRATCH_BYTES) + " (use sf_refined_gemv with a workspace)");
+  uint8_t* base = nullptr;
+  sf_status st = scratch_of_device(&base);
+  if (st != SF_OK) return st;
+  hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, (uint32_t*)base);
+  SF_LAUNCH_CHECK();
+  return refined_gemv_on(ops, n_ops, x_f16, batch, k_sel, sel_in, sel_out, cache, base, SF_SCRATCH_BYTES, stream);
 }

@@ -243,6 +243,21 @@ sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* 
                           int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
                           sf_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): sf_refined_gemv without a
+ * workspace.  Same arguments, semantics and kernels; the selection, slot lists,
+ * hand-off words and batched partials live in a library-owned scratch array of
+ * 8 MiB per device (a static device variable, held by each device the library runs
+ * on until the process ends).  Allocates nothing and calls no allocating routine.
+ * Returns SF_ENOMEM, before any launch, if the call would need more scratch than
+ * that (sf_workspace_bytes_gemv for the same arguments above 8 MiB).  Every call on
+ * a device shares that device's array and first clears its flags and counters
+ * (one small kernel on `stream`): calls that can run at the same time on one device
+ * (other streams, other host threads) race and must not be issued. */
+sf_status sf_refined_gemv_noalloc(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
+                                  int32_t batch, int32_t k_sel, const int32_t* sel_in,
+                                  int32_t* sel_out, sf_refine_cache* cache, sf_stream stream);
+
 /* ---- a8-a12: refined GQA decode attention ------------------------------------ */
 /* out fp32 [batch][n_q_heads][head_dim] for q fp16 [batch][n_q_heads][head_dim]
  * over tokens [0, kv->t_len).  Query head h reads KV head h / (n_q/n_kv).
