@@ -99,9 +99,20 @@ __device__ __forceinline__ void merge_ms(float& m, float& z, float om, float oz)
   m = nm;
 }
 
+typedef _Float16 h2v_t __attribute__((ext_vector_type(2)));
+
+// Two codes (low, high half) as the exact fp16 values c/2^B: built as 1 + c/2^B in
+// the mantissa, then one exact packed fp16 subtraction of 1.  A value sum on MFMA is
+// then the sum itself, not the difference of two larger sums.
+template <int B>
+__device__ __forceinline__ uint32_t code_pair(uint32_t c_lo, uint32_t c_hi) {
+  const h2v_t one = {(_Float16)1.f, (_Float16)1.f};
+  const uint32_t x = (((c_hi << 16) | c_lo) << (10 - B)) | 0x3C003C00u;
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v_t, x) - one);
+}
+
 // B operand of a value-sum MFMA: the codes of dim d for this lane's 8 tokens
-// tk0..tk0+7 (rows of the LDS-staged codes, stride WPTP words), each as the fp16
-// value 1 + c/2^B, two per word.
+// tk0..tk0+7 (rows of the LDS-staged codes, stride WPTP words), as c/2^B.
 template <int B, int WPTP>
 __device__ __forceinline__ u32x4 code_operand(const uint32_t* s_vc, int tk0, int d) {
   constexpr uint32_t cmask = (1u << B) - 1u;
@@ -111,7 +122,7 @@ __device__ __forceinline__ u32x4 code_operand(const uint32_t* s_vc, int tk0, int
   for (int e = 0; e < 8; ++e) c[e] = (s_vc[(tk0 + e) * WPTP + wi] >> sh) & cmask;
   u32x4 bv;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) bv[e] = (((c[2 * e + 1] << 16) | c[2 * e]) << (10 - B)) | 0x3C003C00u;
+  for (int e = 0; e < 4; ++e) bv[e] = code_pair<B>(c[2 * e], c[2 * e + 1]);
   return bv;
 }
 
@@ -309,12 +320,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     acc3[3 * h + 1] = acc3[3 * h + 2] = 0.f;
     if constexpr (PV) {
       const float u = w * sv * uscale;
+      // weight * scale as an fp16 high part plus a low part scaled by 2^11, which
+      // stays a normal fp16 (about 22 bits for weights down to 2^-28 of the largest)
       const _Float16 hi = (_Float16)u;
-      const _Float16 lo = (_Float16)(u - (float)hi);
+      const _Float16 lo = (_Float16)((u - (float)hi) * 2048.f);
       s_u[2 * h][t] = hi;
       s_u[2 * h + 1][t] = lo;
       acc3[3 * h + 1] = w * zv;
-      acc3[3 * h + 2] = (float)hi + (float)lo;
     }
   }
   __syncthreads();  // s_u written; s_red free
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   float* PS = a.part_a + ((size_t)bh * a.nsa + split) * G * PW;
   if constexpr (PV) {
     // lane group qg holds rows 4qg..4qg+3 = head 2qg (rows 0, 1) and head 2qg+1 (rows 2, 3)
-    const float back = ldexpf(1.f, B - shift);  // 2^B undoes the 1 + c/2^B form, 2^-shift the scaling
+    const float back = ldexpf(1.f, B - shift);  // 2^B undoes the c/2^B form, 2^-shift the scaling
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int d = 32 * wave + 16 * db + n;
@@ -361,8 +373,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
       for (int hh = 0; hh < 2; ++hh) {
         const int h = 2 * qg + hh;
         if (h < G) {
-          const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
-          PS[h * PW + d] = s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]);
+          const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1] * (1.f / 2048.f);
+          PS[h * PW + d] = s_st[3 * h + 1] + back * D;
         }
       }
     }
@@ -548,7 +560,7 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     sf_drain();
     __syncthreads();
     if (tid == 0)
-      lds[36] = __hip_atomic_fetch_add(ctl + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(s2 - 1);
+      lds[36] = sf_add_acq_rel(ctl + 4, 1u) == (uint32_t)(s2 - 1);
     __syncthreads();
     if (!lds[36]) return;
     // last chunk: out = sum_c N_c / sum_c z_c (all relative to the same max)
@@ -783,7 +795,7 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   sf_drain();
   __syncthreads();
   if (tid == 0)
-    lds[36] = __hip_atomic_fetch_add(ctl + 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(s2 - 1);
+    lds[36] = sf_add_acq_rel(ctl + 4, 1u) == (uint32_t)(s2 - 1);
   __syncthreads();
   if (!lds[36]) return;
   // last chunk: the max logit after replacement
@@ -938,12 +950,11 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       s_w[h][tl0 + i] = w;
       const float u = w * sf_h2f(vsz[i]) * uscale;
       const _Float16 hi = (_Float16)u;
-      const _Float16 lo = (_Float16)(u - (float)hi);
+      const _Float16 lo = (_Float16)((u - (float)hi) * 2048.f);
       s_u[2 * h][tl0 + i] = hi;
       s_u[2 * h + 1][tl0 + i] = lo;
       acc3[3 * h] += w;
       acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
-      acc3[3 * h + 2] += (float)hi + (float)lo;
     }
 #pragma unroll
   for (int i = 0; i < TPW; ++i)
@@ -1007,7 +1018,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
                              (w1.x >> sh) & cmask, (w1.y >> sh) & cmask, (w1.z >> sh) & cmask, (w1.w >> sh) & cmask};
       u32x4 bv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = (((c[2 * e + 1] << 16) | c[2 * e]) << (10 - B)) | 0x3C003C00u;
+      for (int e = 0; e < 4; ++e) bv[e] = code_pair<B>(c[2 * e], c[2 * e + 1]);
       pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
     }
   }
@@ -1068,9 +1079,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int h = 2 * qg + hh;
       if (h < G) {
-        const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1];
+        const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1] * (1.f / 2048.f);
         const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
-        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * (D - s_st[3 * h + 2]) + corr),
+        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * D + corr),
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -1081,7 +1092,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   sf_drain();
   __syncthreads();
   if (tid == 0)
-    s_flag = __hip_atomic_fetch_add(a.ctl + bh * 8 + 6, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_flag = sf_add_acq_rel(a.ctl + bh * 8 + 6, 1u) ==
              (uint32_t)(a.nsp - 1);
   __syncthreads();
   if (!s_flag) return;

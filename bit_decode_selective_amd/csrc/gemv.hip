@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   sf_drain();
   __syncthreads();
   if (tid == 0)
-    s_last = __builtin_amdgcn_atomic_inc32(a.ctr + tile_g, (uint32_t)(ns - 1), __ATOMIC_RELAXED, "agent") ==
+    s_last = __builtin_amdgcn_atomic_inc32(a.ctr + tile_g, (uint32_t)(ns - 1), __ATOMIC_ACQ_REL, "agent") ==
              (uint32_t)(ns - 1);
   __syncthreads();
   if (!s_last) return;

@@ -468,14 +468,35 @@ __device__ __forceinline__ void count_reader(const GemvArgs& a, int grp) {
   (void)__hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Lane 0 of a wave polls its group's flag (bounded, acquire); the result is
-// wave-uniform.
+// Published words carry their own validity: bit 31 set on a word the selecting
+// workgroup has written in this launch, 0 on a cleared one.  A reader that sees bit
+// 31 reads that writer's value (one location, one atomic store): the hand-off needs
+// no ordering between different locations, so the flags are only a hint of when to
+// start reading and no cache writeback or invalidation is needed.
+__device__ __forceinline__ uint32_t pub_word(int v) { return 0x80000000u | ((uint32_t)v & 0x7FFFFFFFu); }
+__device__ __forceinline__ int pub_value(uint32_t w) { return (int)(w << 1) >> 1; }  // sign from bit 30
+
+// A published word, waited for (bounded); -1 if it never became valid.
+__device__ __forceinline__ int read_published(const uint32_t* p, const GemvArgs& a) {
+  uint32_t w = sf_get(p);
+  if (w >> 31) return pub_value(w);
+  const uint32_t lim = sf_spin_limit(a.ctl + 2);
+  for (uint32_t it = 0; it < lim; ++it) {
+    __builtin_amdgcn_s_sleep(2);
+    w = sf_get(p);
+    if (w >> 31) return pub_value(w);
+  }
+  sf_put(a.ctl + 2, 1u);
+  return -1;
+}
+
+// Lane 0 of a wave polls its group's flag (bounded); the result is wave-uniform.
 __device__ __forceinline__ bool wait_published(const GemvArgs& a, int grp) {
   const uint32_t* f = a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * grp;
   const uint32_t lim = sf_spin_limit(a.ctl + 2);
   for (uint32_t it = 0;; ++it) {
     uint32_t v = 0u;
-    if ((threadIdx.x & 63) == 0) v = sf_get_acquire(f);
+    if ((threadIdx.x & 63) == 0) v = sf_get(f);
     if (__builtin_amdgcn_readfirstlane(v) != 0u) return true;
     if (it >= lim) {
       if ((threadIdx.x & 63) == 0) sf_put(a.ctl + 2, 1u);
@@ -485,29 +506,35 @@ __device__ __forceinline__ bool wait_published(const GemvArgs& a, int grp) {
   }
 }
 
-// Workgroup 0, after publishing: waits until every tile has seen the flag, then
-// lowers the flags and clears the counts for the next launch.  If the wait gives
-// up, the flags are lowered all the same (a tile still to come then finds no
-// selection and keeps its rows unrefined) and the timeout word reports it; the
-// workspace check clears any count such a late tile leaves behind.
+// Workgroup 0, after publishing: waits until every tile has read the words, then
+// clears them and lowers the flags and counts for the next launch.  If the wait
+// gives up, it clears them all the same (a tile still to come then finds no valid
+// word and keeps its rows unrefined) and the timeout word reports it; the workspace
+// check clears any count such a late tile leaves behind.
 __device__ __forceinline__ void split_retire(const GemvArgs& a) {
   const int tid = threadIdx.x;
-  if (tid >= 64) return;
-  uint32_t* ctr = a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * tid;
-  uint32_t* flag = a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid;
-  const uint32_t tiles = (uint32_t)a.total_tiles;
-  const uint32_t want = (uint32_t)tid < tiles ? (tiles - (uint32_t)tid + 63u) / 64u : 0u;
-  const uint32_t lim = sf_spin_limit(a.ctl + 2);
-  for (uint32_t it = 0;; ++it) {
-    if (__all(sf_get(ctr) >= want)) break;
-    if (it >= lim) {
-      sf_put(a.ctl + 2, 1u);
-      break;
+  if (tid < 64) {
+    uint32_t* ctr = a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * tid;
+    const uint32_t tiles = (uint32_t)a.total_tiles;
+    const uint32_t want = (uint32_t)tid < tiles ? (tiles - (uint32_t)tid + 63u) / 64u : 0u;
+    const uint32_t lim = sf_spin_limit(a.ctl + 2);
+    for (uint32_t it = 0;; ++it) {
+      if (__all(sf_get(ctr) >= want)) break;
+      if (it >= lim) {
+        sf_put(a.ctl + 2, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
     }
-    __builtin_amdgcn_s_sleep(8);
   }
-  sf_put(flag, 0u);
-  sf_put(ctr, 0u);
+  __syncthreads();
+  uint32_t* hw = a.ctl + offsetof(WsControl, hit) / 4;
+  const int n = SPLIT_COPIES * split_copy_words(a.k_sel, a.n_ops);
+  for (int i = tid; i < n; i += 256) sf_put(hw + i, 0u);
+  if (tid < 64) {
+    sf_put(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 0u);
+    sf_put(a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * tid, 0u);
+  }
 }
 
 // Workgroup 0: selection into l_sel (LDS), then the lookups, the published copy in
@@ -646,7 +673,7 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
   for (int j = tid; j < ks; j += 256) {
     const int k = l_sel[j];
 #pragma unroll
-    for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + j, (uint32_t)k);
+    for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + j, pub_word(k));
 #pragma unroll
     for (int op = 0; op < SF_MAX_OPS; ++op) {
       if (op >= a.n_ops) break;
@@ -654,13 +681,13 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
       if (pool.resident) continue;
       const int slot = pool.unit2slot ? pool.unit2slot[k] : -1;
 #pragma unroll
-      for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + ks * (1 + op) + j, (uint32_t)slot);
+      for (int c = 0; c < SPLIT_COPIES; ++c) sf_put(hw + c * cst + ks * (1 + op) + j, pub_word(slot));
     }
   }
   // the words are complete at the coherence point before any flag goes up
   sf_drain();
   __syncthreads();
-  if (tid < 64) sf_put_release(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 1u);
+  if (tid < 64) sf_put(a.ctl + offsetof(WsControl, sel_flag) / 4 + 32 * tid, 1u);
   // the reports (selection, hits, lookup log: one reservation per matrix) after
   // the flags, off the tiles' path
   if (!a.report) return;
@@ -706,10 +733,7 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
   const int ks = a.k_sel, K = a.k_in, ngr = K / 128, r = a.r;
   if (wave == 0) {
     const bool ok0 = wait_published(a, tile_g & 63);
-    if (lane == 0) {
-      count_reader(a, tile_g & 63);
-      *sflag = ok0 ? 1 : 0;
-    }
+    if (lane == 0) *sflag = ok0 ? 1 : 0;
   }
   lds_barrier();
   const int tb = (tile_g - o.tile_begin) * 4 * R * r, tw0 = tb >> 5, toff = tb & 31;
@@ -721,8 +745,8 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
   if (any) {
     const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (tile_g % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
     for (int j = tid; j < ks; j += 256) {
-      const int k = (int)sf_get(hc + j);
-      int slot = resident ? k : (int)sf_get(hc + ks * (1 + op) + j);
+      const int k = read_published(hc + j, a);
+      int slot = resident ? k : read_published(hc + ks * (1 + op) + j, a);
       if ((unsigned)k >= (unsigned)K) slot = -1;  // never read outside x or the units
       l_hk[j] = slot >= 0 ? k : -1;
       if (slot >= 0) {
@@ -742,6 +766,9 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
     }
   }
   lds_barrier();  // the hits
+  // counted only once every read of the published words has completed (their values
+  // are in LDS): the selecting workgroup clears the words when all tiles are counted
+  if (tid == 0) count_reader(a, tile_g & 63);
   if (!any) return;
   const int pw = toff + wave * R * r;  // this wave's first row in the window
   const int wi0 = pw >> 5, sh0 = pw & 31;

@@ -167,3 +167,39 @@ def test_full_size_128k():
         assert sel[0, g].tolist() == selection.top_k(o_attn.token_scores(qg[0], k_res, SCALE), ks), g
         ref, _ = o_attn.refined_attention(qg, qk, qv, (1, 1, T, D), SCALE, ks)
         assert_close(out[:, g * G:(g + 1) * G], ref, what=f"128K kv head {g}")
+
+
+def test_refinement_that_removes_the_dominant_token():
+    """KV head 0's token 0 holds nearly all of the softmax mass at resident precision
+    and loses it once refined (its refinement bits sit where the query is negative),
+    so the refined output is set by the other tokens; KV head 1 is ordinary.  Both
+    heads must match the oracle."""
+    T, n_kv, G = 96, 2, 2
+    K, V = inputs.kv(54, 0, 1, n_kv, T, D)
+    K[0, 0, 1:] *= np.float32(0.05)  # the other tokens of KV head 0: small keys, small logits
+    # token 0 of KV head 0: codes 15, 0, then 3 everywhere (z = 0, s = 1 exactly):
+    # resident values 12, 0, 0, ..; refined 15, 0, 3, ..
+    K[0, 0, 0, :] = 3.0
+    K[0, 0, 0, 0] = 15.0
+    K[0, 0, 0, 1] = 0.0
+    q = inputs.query(54, 0, 0, 1, n_kv * G, D).astype(np.float32)
+    q[0, :G, :] = -1.0
+    q[0, :G, 0] = 16.0
+    q = q.astype(np.float16)
+    kv = binding.QuantKV.from_host(K, V, 2, 2)
+    qk, qv = o_attn.quantize_kv(K, 2, 2), o_attn.quantize_kv(V, 2, 2)
+    k_res = nested.dequant_resident(qk).reshape(1, n_kv, T, D)
+    k_full = nested.dequant_full(qk).reshape(1, n_kv, T, D)
+    l_res = SCALE * (q[0, 0].astype(np.float64) @ k_res[0, 0].T)
+    l_full = SCALE * (q[0, 0].astype(np.float64) @ k_full[0, 0].T)
+    assert l_res[0] - np.max(l_res[1:]) > 8 and l_full[0] < np.max(l_full[1:]) - 8  # the construction holds
+    ks = 3
+    from gpu_util import token_gap
+    for g in range(n_kv):
+        assert token_gap(o_attn.token_scores(q[0, g * G:(g + 1) * G], k_res[0, g], SCALE), ks) >= 1e-4
+    cache = binding.RefineCache([kv.resident_pool_desc()])
+    out, sel, hit = binding.refined_attention(q, kv, SCALE, ks, cache=cache)
+    torch.cuda.synchronize()
+    ref, chosen = o_attn.refined_attention(q, qk, qv, (1, n_kv, T, D), SCALE, ks)
+    assert sel.cpu().numpy()[0, 0].tolist() == chosen[(0, 0)] and 0 in chosen[(0, 0)]
+    assert_close(out.cpu().numpy(), ref, what="dominant token refined away")
