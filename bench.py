@@ -1,29 +1,38 @@
 #!/usr/bin/env python3
 """Refined low-bit decode-step benchmark on one MI355X.
 
-One step = one decode step of a Llama-3.1-8B-shaped model at batch 1 through the
-whole refined path, for each of the 32 layers:
-  KV append (the new token's K and V quantised into the 2+2-bit cache),
+Default workload: one decode step of a Llama-3.1-8B-shaped model at batch 1 through
+the whole refined path, 32 layers, each:
+  residual add + RMSNorm (which also selects the q/k/v channels),
   q/k/v refined GEMV (one fused launch, top 3% input channels refined),
-  refined GQA attention over the 32768-token context (32 query / 8 KV heads,
-  head dim 128, top 2% tokens refined),
-  o refined GEMV, gate/up refined GEMV (fused), down refined GEMV,
-plus the refinement-cache fill at the end of the step.  Weights and KV are 2-bit
-resident + 2-bit refinement, group 128.  Every refinement pool holds all of its
-units on the device (no capacity limit is set for this workload), so every
-selected unit hits.  Inputs are seeded synthetic data with the pages' shapes and
-distributions (no trained weights or datasets): W ~ N(0, 0.02), activations
-N(0, 1) with 1% of channels x20, K and V ~ N(0, 1) with 4 dims of K x8, q ~ N(0,1).
+  rotary embedding, KV append (the new token quantised into the 2+2-bit cache),
+  refined GQA attention over the 32768-token context (32 query / 8 KV heads, head
+  dim 128, top 2% tokens refined),
+  fp16 cast of the attention output (selecting the o channels), o refined GEMV,
+  residual add + RMSNorm (selecting the gate/up channels), gate/up refined GEMV,
+  SwiGLU (selecting the down channels), down refined GEMV.
+The step starts from a synthetic residual state (in place of the embedding; no
+lm_head, as the GEMV configuration has none).  Weights and KV are 2-bit resident +
+2-bit refinement, group 128.  Every refinement pool holds all of its units on the
+device, so every selected unit hits.  Inputs are seeded synthetic data with the
+pages' shapes and distributions (no trained weights or datasets): W ~ N(0, 0.02),
+K and V ~ N(0, 1) with 4 dims of K x8, RMSNorm gains 1 with 1% of channels x20.
 
 Timing: the step is captured once as a HIP graph and replayed; inputs are resident
-in HBM before the timed region.  The dominant kernel (the fused gate/up GEMV) is
-timed with HIP events around each of its launches in an eager pass over the same
-step.  The CPU baseline is the fp64 oracle on a bounded sample of the workload.
+in HBM before the timed region.  Every call of the step is also timed on its own
+with HIP events in eager passes over the same step (every layer's own matrices and
+cache, so nothing is timed hot); the call with the largest share of the step gives
+the roofline line.  The CPU baseline is the fp64 oracle on a bounded sample.
+
+Other workloads (--workload): full greedy decode steps with embedding and lm_head of
+a Qwen3-8B-shaped model at context 8192 with 25% LRU pools, or a Llama-3.1-8B-shaped
+model at context 131072 with 3+1-bit weights and 10% pools with asynchronous fills.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes as C
+import hashlib
 import json
 import math
 import os
@@ -37,249 +46,170 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-
-# The kernel whose launches are timed for the roofline line: the step's largest share
-# of time.  `traffic` is its HBM bytes per launch from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE), each divided by what the same counter reads per byte
-# for a plain copy kernel of known size (bench.py --copy-calibration); it is reported
-# only while the kernel source still has the hash it was measured on.
-DOMINANT = {
-    "tag": "gateup",
-    "kernel": "gemv_fused_kernel<CodecPow2<2>, 2, 8, 1, 1, 2, true> (gate/up, 2 x 14336 x 4096, 1 selecting + 896 tile workgroups x 256)",
-    "source": "bit_decode_selective_amd/csrc/gemv.hip",
-}
-TRAFFIC = {
-    "source_sha256": "ffb5c6f84dae954a5b1ef03c92df002c2df485a125c67529df614d0f9bcc2526",
-    "fetch_bytes": 40457928,
-    "write_bytes": 153600,
-}
+HD = 128
+SOURCES = ("bit_decode_selective_amd/csrc/gemv_rows.h", "bit_decode_selective_amd/csrc/gemv.hip",
+           "bit_decode_selective_amd/csrc/attention.hip", "bit_decode_selective_amd/csrc/glue.hip",
+           "bit_decode_selective_amd/csrc/sf_internal.h", "bit_decode_selective_amd/csrc/select_core.h")
+# HBM bytes per call of the dominant call of the default workload, from two rocprofv3
+# --pmc runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain copy
+# of known size (--copy-calibration); reported only while the kernel sources have
+# the hash they were measured on, and only for the call they were measured for.
+TRAFFIC = None
 COPY_CALIBRATION_BYTES = 256 << 20
-HIDDEN, FFN, NQ, NKV, HD = 4096, 14336, 32, 8, 128
 
 
 def k_select(percent, n):
     return (percent * n + 99) // 100
 
 
+def sources_hash():
+    h = hashlib.sha256()
+    for s in SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# ---- algorithmic bytes ----------------------------------------------------------------
 def gemv_bytes(shapes, k_in, k_sel, b, r, batch):
-    """Algorithmic bytes of one fused refined GEMV call: resident codes, scale/zero
-    words, refinement bits of the applied (hit) channels, x, y, selected indices."""
+    """One fused refined GEMV call: resident codes, scale/zero words, refinement bits
+    of the applied (hit) channels, x, y, the selected indices."""
     tot = 0
     for n_out in shapes:
         tot += n_out * k_in * b // 8 + n_out * (k_in // 128) * 4 + k_sel * n_out * r // 8 + n_out * 4 * batch
     return tot + k_in * 2 * batch + k_sel * 4
 
 
-def attn_bytes(T, k_sel, b, r, batch):
-    """Algorithmic bytes of one refined attention call: resident K and V codes and
-    their scale/zero words, refinement units of the applied tokens, q, out, indices."""
+def attn_bytes(T, k_sel, b, r, batch, n_q, n_kv):
+    """One refined attention call: resident K and V codes with their scale/zero words,
+    refinement units of the applied tokens, q, out, the selected indices."""
     per_th = 2 * (HD * b // 8 + 4)
-    return batch * (NKV * T * per_th + NKV * k_sel * (2 * HD * r // 8) + NQ * HD * 2 + NQ * HD * 4 + NKV * k_sel * 4)
+    return batch * (n_kv * T * per_th + n_kv * k_sel * (2 * HD * r // 8) + n_q * HD * 2 + n_q * HD * 4
+                    + n_kv * k_sel * 4)
 
 
-def append_bytes(b, r, batch):
-    return batch * NKV * (2 * HD * 4 + 2 * (HD * b // 8 + 4) + 2 * HD * r // 8)
+def append_bytes(b, r, batch, n_kv):
+    return batch * n_kv * (2 * HD * 4 + 2 * (HD * b // 8 + 4) + 2 * HD * r // 8)
 
 
-class Model:
-    def __init__(self, layers, T, batch, b, r, ch_pct, tok_pct, seed=1234):
-        import torch
-
-        from bit_decode_selective_amd import binding, inputs
-
-        self.torch, self.binding, self.inputs = torch, binding, inputs
-        self.layers, self.T, self.batch, self.b, self.r = layers, T, batch, b, r
-        dev = torch.device("cuda", 0)
-        self.dev = dev
-        g = torch.Generator(device=dev)
-        self.groups = []  # per layer: list of (name, [QuantWeight], k_in)
-        pools = []
-        self.kvs = []
-        for li in range(layers):
-            g.manual_seed(seed + li)
-            mats = {}
-            for name, (n, k) in (("q", (HIDDEN, HIDDEN)), ("k", (NKV * HD, HIDDEN)), ("v", (NKV * HD, HIDDEN)),
-                                 ("o", (HIDDEN, NQ * HD)), ("gate", (FFN, HIDDEN)), ("up", (FFN, HIDDEN)),
-                                 ("down", (HIDDEN, FFN))):
-                W = inputs.torch_weight(g, n, k, device=dev)
-                mats[name] = binding.QuantWeight.from_device(W, b, r)
-                del W
-            grp = []
-            for gname, names in (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",))):
-                ws = [mats[n] for n in names]
-                ops = []
-                for w in ws:
-                    ops.append((w, len(pools)))
-                    pools.append(w.resident_pool_desc())
-                grp.append((gname, ops, ws[0].k_in))
-            self.groups.append(grp)
-            kv = binding.QuantKV(batch, NKV, T, b, r, device=dev)
-            for t0 in range(0, T - 1, 8192):
-                n = min(8192, T - 1 - t0)
-                K, V = inputs.torch_kv(g, batch, NKV, n, HD, device=dev)
-                kv.append(K, V)
-                del K, V
-            self.kvs.append((kv, len(pools)))
-            pools.append(kv.resident_pool_desc())
-            torch.cuda.synchronize()
-        self.cache = binding.RefineCache(pools, device=dev)
-        self.side = torch.cuda.Stream(device=dev)
-        # per-layer synthetic inputs and outputs
-        self.x = []
-        self.y = []
-        self.q = []
-        self.knew = []
-        self.out = []
-        for li in range(layers):
-            g.manual_seed(seed + 1000 + li)
-            xs, ys = [], []
-            for gname, ops, k_in in self.groups[li]:
-                outl = torch.randperm(k_in, generator=g, device=dev)[: (k_in + 99) // 100].cpu().numpy()
-                xs.append(binding._f16_bits(inputs.torch_activation(g, batch, k_in, outl, device=dev), dev))
-                ys.append([torch.empty((batch, w.n_out), dtype=torch.float32, device=dev) for w, _ in ops])
-            self.x.append(xs)
-            self.y.append(ys)
-            self.q.append(binding._f16_bits(torch.randn((batch, NQ, HD), generator=g, device=dev).half(), dev))
-            K, V = inputs.torch_kv(g, batch, NKV, 1, HD, device=dev)
-            self.knew.append((K.contiguous(), V.contiguous()))
-            self.out.append(torch.empty((batch, NQ, HD), dtype=torch.float32, device=dev))
-        self.ch_pct, self.tok_pct = ch_pct, tok_pct
-        ws_bytes = max(
-            [self._gemv_ws_bytes(ops, batch, k_select(ch_pct, k_in))
-             for grp in self.groups for _, ops, k_in in grp]
-            + [binding.lib().sf_workspace_bytes_attn(batch, NQ, NKV, T, k_select(tok_pct, T))]
-        )
-        self.ws = binding.workspace(ws_bytes, dev)
-        torch.cuda.synchronize()
-
-    def _gemv_ws_bytes(self, ops, batch, ks):
-        b = self.binding
-        arr = (b.sf_gemv_op * len(ops))()
-        for i, (w, pool) in enumerate(ops):
-            arr[i] = b.sf_gemv_op(w.desc(), pool, None, None)
-        return b.lib().sf_workspace_bytes_gemv(arr, len(ops), batch, ks)
-
-    def build_calls(self, refined=True):
-        """Prebuilt ctypes argument tuples for every launch of one step."""
-        b = self.binding
-        L = b.lib()
-        calls = []  # (fn, args, tag)
-        for li in range(self.layers):
-            kv, kv_pool = self.kvs[li]
-            T = self.T
-            Kn, Vn = self.knew[li]
-            dsc_app = kv.desc(T - 1)
-            dst = kv.refine.data_ptr() + (T - 1) * kv.unit_bytes
-            calls.append((L.sf_kv_append, (C.c_void_p(Kn.data_ptr()), C.c_void_p(Vn.data_ptr()), 1, T - 1,
-                                           C.byref(dsc_app), C.c_void_p(dst), kv.t_cap, None), "append", dsc_app))
-            for gi, (gname, ops, k_in) in enumerate(self.groups[li]):
-                ks = k_select(self.ch_pct, k_in) if refined else 0
-                arr = (b.sf_gemv_op * len(ops))()
-                for i, (w, pool) in enumerate(ops):
-                    arr[i] = b.sf_gemv_op(w.desc(), pool, self.y[li][gi][i].data_ptr(), None)
-                args = (arr, len(ops), C.c_void_p(self.x[li][gi].data_ptr()), self.batch, ks, None, None,
-                        self.cache.handle, self.ws.handle, None)
-                calls.append((L.sf_refined_gemv, args, gname, arr))
-                if gname == "qkv":
-                    dsc = kv.desc(T)
-                    kt = k_select(self.tok_pct, T) if refined else 0
-                    aargs = (C.c_void_p(self.q[li].data_ptr()), NQ, C.byref(dsc), 1.0 / math.sqrt(HD), kt, None,
-                             self.cache.handle, kv_pool, C.c_void_p(self.out[li].data_ptr()), None, None,
-                             self.ws.handle, None)
-                    calls.append((L.sf_refined_attn_decode, aargs, "attn", dsc))
-        return calls
-
-    def enqueue(self, calls, stream, events=None, tag=None):
-        """Launch every kernel of one step on `stream` (no host synchronisation)."""
-        s = C.c_void_p(stream.cuda_stream)
-        for fn, args, t, _keep in calls:
-            a = list(args)
-            a[-1] = s
-            if events is not None and t == tag:
-                e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                st = fn(*a)
-                e1.record(stream)
-                events.append((e0, e1))
-            else:
-                st = fn(*a)
-            if st != 0:
-                self.binding.check(st)
-
-    def fill(self, stream):
-        """End-of-step refinement-cache fill (host side; enqueues copies if needed)."""
-        st = self.binding.lib().sf_refine_cache_fill(self.cache.handle, C.c_void_p(stream.cuda_stream),
-                                                     C.c_void_p(self.side.cuda_stream), None)
-        self.binding.check(st)
-
-    def step_bytes(self, refined=True):
-        tot = 0
-        for li in range(self.layers):
-            for gname, ops, k_in in self.groups[li]:
-                ks = k_select(self.ch_pct, k_in) if refined else 0
-                tot += gemv_bytes([w.n_out for w, _ in ops], k_in, ks, self.b, self.r, self.batch)
-            tot += attn_bytes(self.T, k_select(self.tok_pct, self.T) if refined else 0, self.b, self.r, self.batch)
-            tot += append_bytes(self.b, self.r, self.batch)
-        return tot
-
-    def dominant_bytes(self, tag):
-        """Algorithmic bytes of one launch of the call tagged `tag` (refined)."""
-        if tag == "attn":
-            return attn_bytes(self.T, k_select(self.tok_pct, self.T), self.b, self.r, self.batch)
-        for gname, ops, k_in in self.groups[0]:
-            if gname == tag:
-                return gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(self.ch_pct, k_in), self.b, self.r,
-                                  self.batch)
-        raise KeyError(tag)
+def call_bytes(model, tag, T, refined):
+    """Algorithmic bytes of one call with this tag in a step of `model` at context T."""
+    S, B = model.spec, model.batch
+    ks = (lambda n: k_select(model.ch_pct, n)) if refined and model.r > 0 else (lambda n: 0)
+    kt = k_select(model.tok_pct, T) if refined and model.kv_r > 0 else 0
+    H, QD = S.hidden, S.n_q * HD
+    if tag == "qkv":
+        return gemv_bytes([QD, S.n_kv * HD, S.n_kv * HD], H, ks(H), model.b, model.r, B)
+    if tag == "o":
+        return gemv_bytes([H], QD, ks(QD), model.b, model.r, B)
+    if tag == "gateup":
+        return gemv_bytes([S.ffn, S.ffn], H, ks(H), model.b, model.r, B)
+    if tag == "down":
+        return gemv_bytes([H], S.ffn, ks(S.ffn), model.b, model.r, B)
+    if tag == "lm_head":
+        return gemv_bytes([S.vocab], H, ks(H), model.b, model.r, B)
+    if tag == "attn":
+        return attn_bytes(T, kt, model.kv_b, model.kv_r, B, S.n_q, S.n_kv)
+    if tag == "append":
+        return append_bytes(model.kv_b, model.kv_r, B, S.n_kv)
+    if tag == "norm":  # h (+ y) read, h written, gains, x written, selection
+        return B * H * (4 + 4 + 4 + 2) + H * 4 + ks(H) * 4
+    if tag == "cast":
+        return B * QD * (4 + 2) + ks(QD) * 4
+    if tag == "swiglu":
+        return B * S.ffn * (4 + 4 + 2) + ks(S.ffn) * 4
+    if tag == "rope":
+        return B * (S.n_q + S.n_kv) * HD * 4 + B * S.n_q * HD * 2 + B * S.n_kv * HD * 4
+    if tag == "embed":
+        return B * H * (2 + 4)
+    if tag == "argmax":
+        return B * S.vocab * 4 + B * 4
+    return 0
 
 
-def time_steps(model, calls, steps, warmup, use_graph):
-    """Average ms per step over `steps` timed steps after `warmup` untimed ones."""
-    torch = model.torch
-    stream = torch.cuda.Stream(device=model.dev)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            model.enqueue(calls, stream)
-            model.fill(stream)
-    torch.cuda.synchronize()
-    if use_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            model.enqueue(calls, stream)
+def step_bytes(model, calls, T, refined):
+    return sum(call_bytes(model, tag, T, refined) for _, _, tag in calls)
 
-        def step():
-            g.replay()
-            model.fill(stream)
-    else:
-        def step():
-            model.enqueue(calls, stream)
-            model.fill(stream)
+
+# ---- timing ----------------------------------------------------------------------------
+class CallTimer:
+    """HIP events around every call of a step, by tag."""
+
+    def __init__(self, torch):
+        self.torch, self.ev = torch, {}
+
+    def __call__(self, tag):
+        e = (self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True))
+        self.ev.setdefault(tag, []).append(e)
+        return e
+
+    def us(self):
+        return {t: [1000.0 * a.elapsed_time(b) for a, b in v] for t, v in self.ev.items()}
+
+
+def capture(torch, model, calls, stream, before=None):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        if before is not None:
+            before()
+        model.enqueue(calls, stream)
+    return g
+
+
+def time_replays(torch, g, stream, steps, warmup, after=None):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
-            step()
+            g.replay()
+            if after is not None:
+                after()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record(stream)
         for _ in range(steps):
-            step()
+            g.replay()
+            if after is not None:
+                after()
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
 
 
-def _timed_reps(fn, budget_s):
-    """One untimed warm-up call, then timed calls until `budget_s` seconds have
-    been spent (at least three); returns (median seconds per call, reps)."""
-    fn()
-    times = []
-    while len(times) < 3 or sum(times) < budget_s:
-        t0 = time.perf_counter()
-        fn()
-        times.append(time.perf_counter() - t0)
-    times.sort()
-    return times[len(times) // 2], len(times)
+def per_call(torch, model, calls, stream, passes, before=None):
+    """Per-tag call durations (us) over `passes` eager passes of the step."""
+    timer = CallTimer(torch)
+    with torch.cuda.stream(stream):
+        for _ in range(passes):
+            if before is not None:
+                before()
+            model.enqueue(calls, stream, timer)
+    torch.cuda.synchronize()
+    return timer.us()
+
+
+def call_table(model, calls, T, refined, us):
+    """Per tag: launches per step, average us, bytes per call, GB/s, fraction of the
+    HBM peak, and the tag's share of the step's summed call time."""
+    count = {}
+    for _, _, tag in calls:
+        count[tag] = count.get(tag, 0) + 1
+    total = sum(np.mean(us[t]) * count[t] for t in count)
+    out = {}
+    for t in count:
+        a = float(np.mean(us[t]))
+        by = call_bytes(model, t, T, refined)
+        out[t] = {"per_step": count[t], "avg_us": a, "bytes": by, "gbps": by / (a * 1e3),
+                  "frac": by / (a * 1e3) / HBM_PEAK_GBPS, "share": a * count[t] / total}
+    return out
+
+
+KERNELS = {  # the kernels one call of a tag launches (batch 1-2)
+    "qkv": "gemv_split_kernel", "o": "gemv_split_kernel", "down": "gemv_split_kernel",
+    "gateup": "gemv_split_kernel", "lm_head": "gemv_split_kernel",
+    "attn": "attn_split_kernel + attn_select_kernel + attn_pv_kernel",
+    "norm": "produce_select_kernel<PROD_NORM>", "cast": "produce_select_kernel<PROD_CAST>",
+    "swiglu": "produce_select_kernel<PROD_SWIGLU>", "rope": "qk_rope_kernel", "append": "kv_append_kernel",
+}
 
 
 def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, batch, budget_s=8.0):
@@ -298,51 +228,156 @@ def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, bat
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    W = inputs.weight(2, 0, inputs.Q_PROJ, HIDDEN, HIDDEN)
+
+    def timed(fn):
+        fn()
+        times = []
+        while len(times) < 3 or sum(times) < budget_s:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        times.sort()
+        return times[len(times) // 2], len(times)
+
+    H = 4096
+    W = inputs.weight(2, 0, inputs.Q_PROJ, H, H)
     q = nested.quantize(W, b, r, 128)
-    x = inputs.activation(2, 0, inputs.Q_PROJ, 0, batch, HIDDEN)
-    ks = selection.k_select(ch_pct, HIDDEN)
-
-    def gemv():
-        sel = selection.select_channels(x, ks)
-        o_gemv.refined_gemv(q, x, sel)
-
-    tg, ng = _timed_reps(gemv, budget_s)
-    gb = gemv_bytes([HIDDEN], HIDDEN, ks, b, r, batch)
-    nkv = NKV
-    K, V = inputs.kv(3, 0, 1, nkv, T, HD)
-    qh = inputs.query(3, 0, 0, 1, nkv * NQ // NKV, HD)
+    x = inputs.activation(2, 0, inputs.Q_PROJ, 0, batch, H)
+    ks = selection.k_select(ch_pct, H)
+    tg, ng = timed(lambda: o_gemv.refined_gemv(q, x, selection.select_channels(x, ks)))
+    gb = gemv_bytes([H], H, ks, b, r, batch)
+    K, V = inputs.kv(3, 0, 1, 8, T, HD)
+    qh = inputs.query(3, 0, 0, 1, 32, HD)
     qk, qv = o_attn.quantize_kv(K, b, r), o_attn.quantize_kv(V, b, r)
     del K, V
     kt = selection.k_select(tok_pct, T)
-    ta, na = _timed_reps(lambda: o_attn.refined_attention(qh, qk, qv, (1, nkv, T, HD), 1 / math.sqrt(HD), kt),
-                         budget_s)
-    ab = attn_bytes(T, kt, b, r, 1) * nkv / NKV
+    ta, na = timed(lambda: o_attn.refined_attention(qh, qk, qv, (1, 8, T, HD), 1 / math.sqrt(HD), kt))
+    ab = attn_bytes(T, kt, b, r, 1, 32, 8)
     step_s = gemv_step_bytes / (gb / tg) + attn_step_bytes / (ab / ta)
     return {
         "value": batch / step_s,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, median of {ng} calls of one {HIDDEN}x{HIDDEN} {b}+{r}-bit refined GEMV "
-                   f"with top-{ks} channel selection ({tg:.3f} s each) and of {na} calls of refined attention, "
-                   f"batch 1, {NQ} query / {nkv} KV heads x {T} tokens, top-{kt} tokens ({ta:.3f} s each); "
-                   f"scaled to the full step by algorithmic bytes (GEMV {gb / tg / 1e6:.1f} MB/s, attention "
-                   f"{ab / ta / 1e6:.1f} MB/s); host cpu_count={os.cpu_count()}"),
+        "sample": (f"fp64 numpy oracle, median of {ng} calls of one {H}x{H} {b}+{r}-bit refined GEMV with top-{ks} "
+                   f"channel selection ({tg:.3f} s each) and of {na} calls of refined attention, batch 1, 32 query / "
+                   f"8 KV heads x {T} tokens, top-{kt} tokens ({ta:.3f} s each); scaled to the step's GEMV and "
+                   f"attention bytes (GEMV {gb / tg / 1e6:.1f} MB/s, attention {ab / ta / 1e6:.1f} MB/s); host "
+                   f"cpu_count={os.cpu_count()}"),
     }
 
 
-def traffic_bytes():
-    """Measured HBM bytes per launch of the dominant kernel, or None when unmeasured or
-    when its source changed since the counters were taken."""
-    if TRAFFIC is None:
-        return None
-    import hashlib
+# ---- workloads -------------------------------------------------------------------------
+def layer_step(args):
+    """The default workload: the decoder layers of a Llama-3.1-8B-shaped step."""
+    import torch
 
-    with open(os.path.join(ROOT, DOMINANT["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["source_sha256"]:
-            return None
-    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    from bit_decode_selective_amd import binding, decode
+
+    if args.copy_calibration:
+        src_t = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: 3 x torch.neg over {COPY_CALIBRATION_BYTES} bytes", file=sys.stderr, flush=True)
+        del src_t, dst_t
+    T, B = args.context, args.batch
+    base = decode.LLAMA31_8B
+    spec = decode.Spec(base.name, args.layers, base.hidden, base.n_q, base.n_kv, base.ffn, base.vocab, base.qk_norm,
+                       base.theta, base.eps)
+    t0 = time.time()
+    src = decode.DeviceWeights(1234, "cuda")
+    model = decode.DecodeModel(spec, B, T, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
+                               head=False, producer_select=args.producer_select)
+    model.fill_kv(T - 1, src)
+    pos = T - 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    h0 = torch.randn((B, spec.hidden), generator=g, device="cuda", dtype=torch.float32)
+    print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    reset = lambda: model.h.copy_(h0)  # the step's input state (in place of the embedding)
+    calls, keep = model.build_step(pos, refined=True)
+    calls0, keep0 = model.build_step(pos, refined=False)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):  # first launches outside capture
+        reset()
+        model.enqueue(calls, stream)
+        reset()
+        model.enqueue(calls0, stream)
+    torch.cuda.synchronize()
+    graph = capture(torch, model, calls, stream, reset)
+    ms = time_replays(torch, graph, stream, args.steps, args.warmup)
+    print(f"# refined step {ms:.3f} ms", file=sys.stderr, flush=True)
+    ws = binding.workspace(0, model.dev)
+    ws.check()  # raises if a bounded device wait gave up during the timed steps
+    unref_ms = None
+    if not args.no_unrefined:
+        graph0 = capture(torch, model, calls0, stream, reset)
+        unref_ms = time_replays(torch, graph0, stream, args.steps, args.warmup)
+        print(f"# unrefined step {unref_ms:.3f} ms", file=sys.stderr, flush=True)
+    us = per_call(torch, model, calls, stream, 3, reset)
+    ws.check()
+    table = call_table(model, calls, T, True, us)
+    dom = max(table, key=lambda t: table[t]["avg_us"] * table[t]["per_step"])
+    sb = step_bytes(model, calls, T, True)
+    gbps = sb / (ms * 1e-3) / 1e9
+    traffic = None
+    if TRAFFIC is not None and TRAFFIC.get("call") == dom and TRAFFIC.get("sources_sha256") == sources_hash():
+        traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    res = {
+        "metric": "refined decode tokens/s + achieved HBM GB/s (% peak), Llama-8B-shape 2-bit",
+        "value": B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 x int2 -> fp32",
+        "data": "synthetic (seeded random weights/KV/residual state of the model shapes; no trained weights)",
+        "config": {
+            "workload": (f"Llama-3.1-8B-shape refined decode step, batch {B}: {args.layers} decoder layers x (RMSNorm "
+                         f"selecting channels, q/k/v GEMV, RoPE, KV append, GQA attention 32q/8kv d128 T={T}, o GEMV, "
+                         f"RMSNorm, gate/up GEMV, SwiGLU, down GEMV); weights and KV 2+2-bit, top 3% channels / 2% "
+                         f"tokens refined"),
+            "layers": args.layers,
+            "batch": B,
+            "context": T,
+            "weight_bits": "2+2",
+            "kv_bits": "2+2",
+            "refine_channels_pct": 3,
+            "refine_tokens_pct": 2,
+            "refinement_pools": "all units resident on the device",
+            "hip_graph": True,
+        },
+        "hbm_gbps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": sb,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{dom} call: {KERNELS.get(dom, dom)}",
+            "achieved": table[dom]["gbps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": table[dom]["frac"],
+            "traffic": traffic,
+            "launch_us": table[dom]["avg_us"],
+            "bytes_per_launch": table[dom]["bytes"],
+        },
+        "calls": {t: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()} for t, d in table.items()},
+    }
+    if unref_ms is not None:
+        res["unrefined_tokens_per_s"] = B / (unref_ms * 1e-3)
+        res["refined_over_unrefined"] = unref_ms / ms
+    if not args.no_cpu_baseline:
+        gsb = sum(call_bytes(model, t, T, True) for _, _, t in calls if t in ("qkv", "o", "gateup", "down"))
+        asb = sum(call_bytes(model, t, T, True) for _, _, t in calls if t == "attn")
+        res["cpu_baseline"] = cpu_baseline(T, 3, 2, 2, 2, gsb, asb, B)
+    print(json.dumps(res), flush=True)
 
 
 def decode_workload(args):
@@ -386,44 +421,20 @@ def decode_workload(args):
         model.enqueue(calls, stream)
         fill()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        model.enqueue(calls, stream)
+    g = capture(torch, model, calls, stream)
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             new_ids()
             g.replay()
             fill()
-        torch.cuda.synchronize()
-        st0 = model.cache.stats()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            new_ids()
-            g.replay()
-            fill()
-        e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    st0 = model.cache.stats()
+    ms = time_replays(torch, g, stream, args.steps, 0, after=lambda: (new_ids(), fill()))
     st1 = model.cache.stats()
-    # the same replays without the end-of-step fills (the kernels alone)
-    with torch.cuda.stream(stream):
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e2.record(stream)
-        for _ in range(args.steps):
-            g.replay()
-        e3.record(stream)
-    torch.cuda.synchronize()
-    ms_kernels = e2.elapsed_time(e3) / args.steps
+    ms_kernels = time_replays(torch, g, stream, args.steps, 0)
+    binding.workspace(0, model.dev).check()
     d = {k: st1[k] - st0[k] for k in st1}
-    H, d_ = spec.hidden, spec.head_dim
-    kg = lambda n: k_select(ch_pct, n)
-    gb = 0
-    for shapes, k_in in (([spec.n_q * d_, spec.n_kv * d_, spec.n_kv * d_], H), ([H], spec.n_q * d_),
-                         ([spec.ffn, spec.ffn], H), ([H], spec.ffn)):
-        gb += gemv_bytes(shapes, k_in, kg(k_in), wb, wr, args.batch)
-    step_bytes = layers * (gb + attn_bytes(T + 1, k_select(tok_pct, T + 1), kvb, kvr, args.batch)
-                           + append_bytes(kvb, kvr, args.batch)) + gemv_bytes([spec.vocab], H, kg(H), wb, wr, args.batch)
+    sb = step_bytes(model, calls, T + 1, True)
     secs = ms * 1e-3
     res = {
         "metric": "refined decode tokens/s, full decode step (glue, lm_head, argmax, cache fills)",
@@ -448,12 +459,12 @@ def decode_workload(args):
             "layers": layers,
             "hip_graph": True,
         },
-        "hbm_gbps": step_bytes / secs / 1e9,
-        "hbm_frac": step_bytes / secs / 1e9 / HBM_PEAK_GBPS,
-        "step_algorithmic_bytes": step_bytes,
+        "hbm_gbps": sb / secs / 1e9,
+        "hbm_frac": sb / secs / 1e9 / HBM_PEAK_GBPS,
+        "step_algorithmic_bytes": sb,
         "ms_per_step_kernels_only": ms_kernels,
         "refinement_hit_rate": d["hits"] / max(1, d["lookups"]),
-        "fill_pcie_gbps": d["h2d_bytes"] / (args.steps * secs) / 1e9,
+        "fill_bytes_per_step": d["h2d_bytes"] / args.steps,
         "units_installed_per_step": d["installed"] / args.steps,
     }
     print(json.dumps(res), flush=True)
@@ -467,24 +478,22 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--batch", type=int, default=1)
-    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unrefined", action="store_true")
     ap.add_argument("--workload", default="llama8b-step",
                     choices=["llama8b-step", "qwen3-8b-decode", "llama8b-128k-decode"],
-                    help="llama8b-step (default): the refined GEMVs + attention of a Llama-3.1-8B-shaped step; "
-                         "the others run full decode steps with glue, lm_head and LRU refinement pools")
+                    help="llama8b-step (default): the decoder layers of a Llama-3.1-8B-shaped step; the others run "
+                         "full decode steps with embedding, lm_head and LRU refinement pools")
+    ap.add_argument("--producer-select", action="store_true",
+                    help="the kernels that form each GEMV input also select its channels (else each GEMV selects)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain device copy kernel (256 MiB read + 256 MiB written) "
-                         "whose HBM counters scale those of the other kernels")
+                    help="first run a plain device copy (256 MiB read + 256 MiB written) whose HBM counters scale "
+                         "those of the other kernels")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the refined decode path runs on a single device; see DESIGN.md for how it would shard)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the refined decode path runs on "
+              "a single device; DESIGN.md describes how it would shard)", file=sys.stderr)
         sys.exit(2)
-    import torch
-
     if args.workload != "llama8b-step":
         if args.layers == 32:
             args.layers = 0  # the model's own depth
@@ -492,99 +501,7 @@ def main():
             args.context = 0  # the workload's own context
         decode_workload(args)
         return
-    if args.copy_calibration:
-        src = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        print(f"# copy calibration: 3 x torch.neg over {COPY_CALIBRATION_BYTES} bytes", file=sys.stderr, flush=True)
-        del src, dst
-    b = r = 2
-    ch_pct, tok_pct = 3, 2
-    t_setup = time.time()
-    model = Model(args.layers, args.context, args.batch, b, r, ch_pct, tok_pct)
-    print(f"# setup {time.time() - t_setup:.1f} s", file=sys.stderr, flush=True)
-    calls = model.build_calls(refined=True)
-
-    use_graph = not args.no_graph
-    ms = time_steps(model, calls, args.steps, args.warmup, use_graph)
-    print(f"# refined step {ms:.3f} ms", file=sys.stderr, flush=True)
-    unref_ms = None
-    if not args.no_unrefined:
-        calls0 = model.build_calls(refined=False)
-        unref_ms = time_steps(model, calls0, args.steps, args.warmup, use_graph)
-        print(f"# unrefined step {unref_ms:.3f} ms", file=sys.stderr, flush=True)
-    # dominant kernel: the refined gate/up GEMV of layer 0, launched DOM_REPS times back
-    # to back between two HIP events on its stream (the call is idempotent)
-    stream = torch.cuda.Stream(device=model.dev)
-    dom = [c for c in calls if c[2] == DOMINANT["tag"]][0]
-    DOM_REPS = 50
-    with torch.cuda.stream(stream):
-        for _ in range(5):
-            model.enqueue([dom], stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(DOM_REPS):
-            model.enqueue([dom], stream)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    dom_us = 1000.0 * e0.elapsed_time(e1) / DOM_REPS
-    dom_bytes = model.dominant_bytes(DOMINANT["tag"])
-    step_bytes = model.step_bytes(True)
-    gbps = step_bytes / (ms * 1e-3) / 1e9
-    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
-    res = {
-        "metric": "refined decode tokens/s + achieved HBM GB/s (% peak), Llama-8B-shape 2-bit",
-        "value": args.batch / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16 x int2 -> fp32",
-        "data": "synthetic (seeded random weights/KV/activations of the model shapes; no trained weights)",
-        "config": {
-            "workload": (f"Llama-3.1-8B-shape refined decode step, batch {args.batch}: {args.layers} layers x "
-                         f"(KV append, q/k/v + o + gate/up + down GEMVs {b}+{r}-bit top {ch_pct}% channels, "
-                         f"GQA attention 32q/8kv d128 T={args.context} KV {b}+{r}-bit top {tok_pct}% tokens)"),
-            "layers": args.layers,
-            "batch": args.batch,
-            "context": args.context,
-            "weight_bits": f"{b}+{r}",
-            "kv_bits": f"{b}+{r}",
-            "refine_channels_pct": ch_pct,
-            "refine_tokens_pct": tok_pct,
-            "refinement_pools": "all units resident on the device",
-            "hip_graph": use_graph,
-        },
-        "hbm_gbps": gbps,
-        "hbm_frac": gbps / HBM_PEAK_GBPS,
-        "step_algorithmic_bytes": step_bytes,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": DOMINANT["kernel"],
-            "achieved": dom_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": dom_gbps / HBM_PEAK_GBPS,
-            "traffic": traffic_bytes(),
-            "launch_us": dom_us,
-            "bytes_per_launch": dom_bytes,
-        },
-    }
-    if unref_ms is not None:
-        res["unrefined_tokens_per_s"] = args.batch / (unref_ms * 1e-3)
-        res["refined_over_unrefined"] = unref_ms / ms
-    if not args.no_cpu_baseline:
-        gsb = sum(gemv_bytes([w.n_out for w, _ in ops], k_in, k_select(ch_pct, k_in), b, r, args.batch)
-                  for grp in model.groups for _, ops, k_in in grp)
-        asb = args.layers * attn_bytes(args.context, k_select(tok_pct, args.context), b, r, args.batch)
-        res["cpu_baseline"] = cpu_baseline(args.context, ch_pct, tok_pct, b, r, gsb, asb, args.batch)
-    print(json.dumps(res), flush=True)
+    layer_step(args)
 
 
 if __name__ == "__main__":

@@ -105,6 +105,9 @@ _PROTOS = {
     "sf_add_rmsnorm": (I32, [VP, VP, VP, I32, I32, C.c_float, VP, VP]),
     "sf_qk_rope": (I32, [VP, VP, I32, I32, I32, VP, VP, C.c_float, I32, C.c_float, VP, VP, VP]),
     "sf_swiglu": (I32, [VP, VP, I64, VP, VP]),
+    "sf_add_rmsnorm_select": (I32, [VP, VP, VP, I32, I32, C.c_float, VP, I32, VP, VP]),
+    "sf_swiglu_select": (I32, [VP, VP, I32, I32, VP, I32, VP, VP]),
+    "sf_to_f16_select": (I32, [VP, I32, I32, VP, I32, VP, VP]),
     "sf_to_f16": (I32, [VP, I64, VP, VP]),
     "sf_argmax": (I32, [VP, I32, I64, VP, VP]),
 }
@@ -522,3 +525,33 @@ def argmax(logits, out=None, stream=None):
     out = out if out is not None else torch.empty(batch, dtype=torch.int32, device=logits.device)
     check(lib().sf_argmax(_ptr(logits), batch, vocab, _ptr(out), _stream(stream)))
     return out
+
+
+def add_rmsnorm_select(h, y, w, eps, k_sel, out=None, sel=None, stream=None):
+    """h fp32 [batch][hidden] (h += y in place if y is given) -> (x fp16 bits int16
+    [batch][hidden], the k_sel channels of largest max-over-rows |x|, ascending)."""
+    torch = _torch()
+    batch, hidden = h.shape
+    out = out if out is not None else torch.empty((batch, hidden), dtype=torch.int16, device=h.device)
+    sel = sel if sel is not None else torch.empty(max(1, k_sel), dtype=torch.int32, device=h.device)
+    check(lib().sf_add_rmsnorm_select(_ptr(h), _ptr(y), _ptr(w), batch, hidden, float(eps), _ptr(out), k_sel, _ptr(sel),
+                                      _stream(stream)))
+    return out, sel[:k_sel]
+
+
+def swiglu_select(gate, up, k_sel, out=None, sel=None, stream=None):
+    torch = _torch()
+    batch, n = gate.shape
+    out = out if out is not None else torch.empty((batch, n), dtype=torch.int16, device=gate.device)
+    sel = sel if sel is not None else torch.empty(max(1, k_sel), dtype=torch.int32, device=gate.device)
+    check(lib().sf_swiglu_select(_ptr(gate), _ptr(up), batch, n, _ptr(out), k_sel, _ptr(sel), _stream(stream)))
+    return out, sel[:k_sel]
+
+
+def to_f16_select(x, k_sel, out=None, sel=None, stream=None):
+    torch = _torch()
+    batch, n = x.shape
+    out = out if out is not None else torch.empty((batch, n), dtype=torch.int16, device=x.device)
+    sel = sel if sel is not None else torch.empty(max(1, k_sel), dtype=torch.int32, device=x.device)
+    check(lib().sf_to_f16_select(_ptr(x), batch, n, _ptr(out), k_sel, _ptr(sel), _stream(stream)))
+    return out, sel[:k_sel]

@@ -624,9 +624,18 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
       for (int i = tid; i < nb; i += SEL_T) lh[i] = 0;
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < TPT; ++i)
-        if (tb + i < T && (level == 0 || (key[i] >> sh) == tv))
+      for (int i = 0; i < TPT; ++i) {
+        const bool valid = tb + i < T;
+        if (level == 0) {
+          // scores of exactly 0 (every head past the cutoff) are common in peaked
+          // attention: counted by ballot, one LDS add per wave, not one per token
+          const uint64_t zm = __ballot(valid && key[i] == 0u);
+          if (lane == 0 && zm) atomicAdd(&lh[0], (uint32_t)__popcll(zm));
+          if (valid && key[i] != 0u) atomicAdd(&lh[(key[i] >> lsh) & (uint32_t)(nb - 1)], 1u);
+        } else if (valid && (key[i] >> sh) == tv) {
           atomicAdd(&lh[(key[i] >> lsh) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
       __syncthreads();
       uint32_t* g = gh + level * NBIN;
       for (int i = tid; i < nb; i += SEL_T)
@@ -640,6 +649,9 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
       tv = level == 0 ? bin : ((tv << 10) | bin);
       sh = lsh;
       if (need == inbin) break;  // the whole bin is taken: no finer level needed
+      // level-0 bin 0 holds exactly the zero scores (a nonzero score is at least
+      // e^-64 / sum, far above the bin's bound): the k-th score is 0
+      if (level == 0 && bin == 0u) break;
     }
     // ---- counts above / at the threshold, exchanged between the chunks ----
     int gt = 0, eq = 0;
@@ -821,7 +833,8 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 // the weights are formed, and each wave requests the refinement words of all its
 // hits at once.  All splits of a KV head use the same max, so their sums are added
 // into one fp32 record per head (atomically); the last split divides.
-constexpr int PV_HB = 8;  // hits per wave whose refinement words are in flight together
+constexpr int PV_HB = 128;  // hits whose value refinement words are staged in LDS together
+constexpr int PV_RWM = 28;  // value refinement words of a unit at most (HD * r / 32, r <= 7)
 
 template <int B, int G>
 __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
@@ -837,6 +850,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __shared__ float s_w[G][SP];
   __shared__ float s_acc[4][G][HD];
   __shared__ int s_hit[SP][2];
+  __shared__ uint32_t s_hr[PV_HB * PV_RWM];
   __shared__ float s_red[4][3 * G + 1];
   __shared__ float s_st[3 * G + 1];
   __shared__ int s_rng[4][2];
@@ -971,29 +985,20 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
 
-  // ---- hits: request the refinement words of this wave's hits (w, w+4, ..) ----
-  // lane l covers dims 2l, 2l+1: value refinement bits [HD r + 2 l r, HD r + 2 l r + 2 r)
-  const int r = a.r;
-  const int vbit = HD * r + 2 * lane * r, vwi = vbit >> 5, voff = vbit & 31;
-  const int wpu = a.pool.unit_bytes >> 2;
-  uint32_t hw0[PV_HB], hw1[PV_HB];
-  int htk[PV_HB];
+  // e^(split max - common max) per head; a hit whose weight times this is 0 in fp32
+  // for every head adds nothing above fp32's smallest value, and its refinement is not
+  // fetched (in very peaked attention the selection ends in tokens of no weight)
+  float fsc[G];
 #pragma unroll
-  for (int i = 0; i < PV_HB; ++i) {
-    const int j = wave + 4 * i;
-    htk[i] = -1;
-    hw0[i] = hw1[i] = 0u;
-    if (j < nh) {
-      const int t = s_hit[j][0], slot = s_hit[j][1];
-      if (slot >= 0 && t >= 0 && t < n_here) {
-        const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
-        htk[i] = t;
-        hw0[i] = unit[vwi];
-        if (vwi + 1 < wpu) hw1[i] = unit[vwi + 1];
-      }
-    }
-  }
+  for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
+  const auto live = [&](int t) {
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) any = any || s_w[h][t] * fsc[h] != 0.f;
+    return any;
+  };
 
+  const int r = a.r;
   // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
   const int n = lane & 15, qg = lane >> 4;
   constexpr uint32_t cmask = (1u << B) - 1u;
@@ -1024,37 +1029,51 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   }
 
   // ---- hits in this split: + w * s_V * cV_lo; lane: dims 2l, 2l+1 ----
+  // In batches of PV_HB hits: every thread requests its share of the batch's value
+  // refinement words into LDS at once (one memory latency per batch, however the
+  // hits crowd into this split), then each wave adds the hits w, w + 4, ..
   float hacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) hacc[h][0] = hacc[h][1] = 0.f;
-  const uint32_t rmask = (1u << r) - 1u;
+  const int RW = HD * r / 32;  // value refinement words of a unit (after the key's)
+  for (int j0 = 0; j0 < nh; j0 += PV_HB) {
+    const int nb = min(PV_HB, nh - j0);
+    constexpr int NPT = (PV_HB * PV_RWM + 255) / 256;  // words a thread stages at most
+    uint32_t v[NPT];
 #pragma unroll
-  for (int i = 0; i < PV_HB; ++i) {
-    const int t = htk[i];
-    if (t < 0) continue;
-    const uint64_t w64 = ((uint64_t)hw1[i] << 32) | hw0[i];
-    const float sv = sf_h2f(s_vsz[t]);
-    const float c0 = sv * (float)((uint32_t)(w64 >> voff) & rmask);
-    const float c1 = sv * (float)((uint32_t)(w64 >> (voff + r)) & rmask);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
-      hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
+    for (int q = 0; q < NPT; ++q) {  // every load first, then the LDS writes
+      const int i = tid + 256 * q;
+      v[q] = 0u;
+      if (i < nb * RW) {
+        const int jj = i / RW, w = i - jj * RW;
+        const int t = s_hit[j0 + jj][0], slot = s_hit[j0 + jj][1];
+        if (slot >= 0 && t >= 0 && t < n_here && live(t))
+          v[q] = ((const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes))[RW + w];
+      }
     }
-  }
-  // hits beyond PV_HB per wave (many hits in one split)
-  for (int j = wave + 4 * PV_HB; j < nh; j += 4) {
-    const int t = s_hit[j][0], slot = s_hit[j][1];
-    if (slot < 0 || t < 0 || t >= n_here) continue;
-    const uint32_t* unit = (const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes);
-    const float sv = sf_h2f(s_vsz[t]);
-    const float c0 = sv * (float)field(unit, vbit, r);
-    const float c1 = sv * (float)field(unit, vbit + r, r);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
-      hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
+    for (int q = 0; q < NPT; ++q) {
+      const int i = tid + 256 * q;
+      if (i < nb * RW) {
+        const int jj = i / RW;
+        s_hr[jj * PV_RWM + (i - jj * RW)] = v[q];
+      }
     }
+    __syncthreads();
+    for (int jj = wave; jj < nb; jj += 4) {
+      const int t = s_hit[j0 + jj][0], slot = s_hit[j0 + jj][1];
+      if (slot < 0 || t < 0 || t >= n_here) continue;
+      const uint32_t* vr = s_hr + jj * PV_RWM;
+      const float sv = sf_h2f(s_vsz[t]);
+      const float c0 = sv * (float)field(vr, 2 * lane * r, r);
+      const float c1 = sv * (float)field(vr, (2 * lane + 1) * r, r);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
+        hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
+      }
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1066,9 +1085,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __syncthreads();
   // this split's sums, added into one of the KV head's records [PV_NR][G][PW] (zeroed
   // by the split launch; several records keep the number of adds per address small)
-  float fsc[G];  // e^(split max - common max)
-#pragma unroll
-  for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
   float* PB = a.part_p + (size_t)bh * PV_NR * G * PW;
   float* PP = PB + (size_t)(split % PV_NR) * G * PW;
   const float back = ldexpf(1.f, B - shift);

@@ -26,22 +26,14 @@
 #include <string>
 
 #include "gemv_rows.h"
+#include "select_core.h"
 
 namespace sfg {
-// Keys are max over the batch of |x| as 15-bit fp16 patterns, which order like the
-// values.  Thread t holds channels 8m..8m+7 for m = t + 1024 i, two per register
-// (word 4i + q: channel 8m + 2q low half, 8m + 2q + 1 high half).  The k-th largest
-// key T comes from two histogram passes (top 8 bits, then the low 7), each wave
-// counting into its own LDS histogram (the keys concentrate in a few bins, so one
-// shared histogram would serialise the atomics) before the 16 are summed; then,
-// per i, ballots place the keys above T and the first `need` keys equal to T
-// (lowest channels first) in channel order.
+// The channel selection (select_core.h) over x read from memory, then the lookups
+// and reports of every matrix of the call.
 __global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
-  constexpr int NW = SEL_NT / 64;
-  __shared__ uint32_t whist[NW][256];
-  __shared__ uint32_t hist[384];
   __shared__ int lds[24];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int K = a.k_in, ks = a.k_sel;
   int32_t* sel = a.ws_sel;
   if (a.sel_in) {
@@ -61,93 +53,11 @@ __global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
         if (m < K / 8) {
           const u32x4 v = xr[m];
           const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x2 = wv[q] & 0x7FFF7FFFu;
-            kw[4 * i + q] = max(kw[4 * i + q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kw[4 * i + q] >> 16, x2 >> 16) << 16);
-          }
+          sfsel::key_max8(kw + 4 * i, wv);
         }
       }
     }
-    uint32_t* wh = whist[wave];
-    for (int i = lane; i < 256; i += 64) wh[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      if (tid + SEL_NT * i < K / 8)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          atomicAdd(&wh[(kw[4 * i + q] & 0xFFFFu) >> 7], 1u);
-          atomicAdd(&wh[kw[4 * i + q] >> 23], 1u);
-        }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c += whist[w][tid];
-      hist[tid] = c;
-    }
-    __syncthreads();
-    for (int i = lane; i < 128; i += 64) wh[i] = 0;  // every wave has been summed
-    if (tid < 64) wave_threshold<4>(hist, ks, lds);
-    __syncthreads();
-    const uint32_t b1 = (uint32_t)lds[20];
-    int need = ks - lds[21];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-      if (tid + SEL_NT * i < K / 8)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = kw[4 * i + q] & 0xFFFFu, hi = kw[4 * i + q] >> 16;
-          if ((lo >> 7) == b1) atomicAdd(&wh[lo & 127u], 1u);
-          if ((hi >> 7) == b1) atomicAdd(&wh[hi & 127u], 1u);
-        }
-    __syncthreads();
-    if (tid < 128) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c += whist[w][tid];
-      hist[256 + tid] = c;
-    }
-    __syncthreads();
-    if (tid < 64) wave_threshold<2>(hist + 256, need, lds);
-    __syncthreads();
-    const uint32_t T = (b1 << 7) | (uint32_t)lds[20];
-    need -= lds[21];  // keys equal to T that are taken, lowest channels first
-    int written = 0, eq_seen = 0;
-    for (int i = 0; i < MI; ++i) {
-      if (SEL_NT * 8 * i >= K) break;
-      const bool ok = tid + SEL_NT * i < K / 8;
-      bool gt[8], eq[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = kw[4 * i + q] & 0xFFFFu, hi = kw[4 * i + q] >> 16;
-        gt[2 * q] = ok && lo > T;
-        gt[2 * q + 1] = ok && hi > T;
-        eq[2 * q] = ok && lo == T;
-        eq[2 * q + 1] = ok && hi == T;
-      }
-      // equal keys before each of this thread's channels, then the taken ones
-      int tot_eq;
-      int eb = eq_seen + blk_flag_prefix(eq, lds, &tot_eq);
-      bool take[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        take[q] = gt[q] || (eq[q] && eb < need);
-        eb += eq[q];
-      }
-      int tot;
-      int pos = written + blk_flag_prefix(take, lds, &tot);
-      const int k0 = 8 * (tid + SEL_NT * i);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (take[q]) {
-          if (pos < ks) sel[pos] = k0 + q;
-          ++pos;
-        }
-      written += tot;
-      eq_seen += tot_eq;
-    }
+    sfsel::topk_keys<SEL_NT, MI>(kw, K, ks, sel);
   }
   // sel[] is read back below by other threads of this workgroup
   __syncthreads();
@@ -708,16 +618,21 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
   // forces the fused kernel and SF_GEMV_SPLIT=2 the staged split variant (test
   // hooks).  With more batch rows than one launch takes, the selection over all rows
   // comes from the selection launch.
+  // A selection that is given (sel_in, or every channel) needs no selecting
+  // workgroup: each tile looks its hits up itself ("direct").
+  const bool given = k_sel == 0 || sel_in != nullptr || k_sel >= K;
   int kind = KIND_NONE;
   if (!mfma) {
-    if (env_int("SF_GEMV_SPLIT", 1) != 0 && split_lds_bytes((int)K, cpc / 2, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS &&
+    if (env_int("SF_GEMV_SPLIT", 1) != 0 && given && split_lds_bytes((int)K, cpc / 2, cpc, 1, k_sel, rpw, false) <= MAX_DYN_LDS)
+      kind = KIND_SPLIT;
+    else if (env_int("SF_GEMV_SPLIT", 1) != 0 && split_lds_bytes((int)K, cpc / 2, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS &&
         (size_t)SPLIT_COPIES * split_copy_words(k_sel, n_ops) <= sizeof(((WsControl*)nullptr)->hit) / 4)
       kind = KIND_SPLIT;
     else if (fused_lds_bytes((int)K, cpc, 1, k_sel, rpw) <= MAX_DYN_LDS)
       kind = KIND_FUSED;
     SF_REQUIRE(kind != KIND_NONE, SF_EUNSUPPORTED, "k_in too large for the batch-1/2 kernels' LDS");
   }
-  const size_t lds2 = kind == KIND_SPLIT ? split_lds_bytes((int)K, cpc / 2, cpc, 2, k_sel, rpw)
+  const size_t lds2 = kind == KIND_SPLIT ? split_lds_bytes((int)K, cpc / 2, cpc, 2, k_sel, rpw, !given)
                                          : fused_lds_bytes((int)K, cpc, 2, k_sel, rpw);
   const int max_nb = lds2 <= 64 * 1024 ? 2 : 1;
   const bool one_launch = !mfma && batch <= max_nb;
@@ -743,7 +658,8 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
   // two batch rows per launch when both fit the LDS staging of x, else one
   a.report = one_launch ? 1 : 0;
   if (!one_launch && k_sel > 0) a.sel_in = a.ws_sel;
-  a.sel_wg = (kind == KIND_SPLIT && k_sel > 0) ? 1 : 0;
+  // the selecting workgroup only where the selection is computed in this launch
+  a.sel_wg = (kind == KIND_SPLIT && k_sel > 0 && a.sel_in == nullptr && k_sel < K) ? 1 : 0;
   a.ctl = (uint32_t*)ws_base;
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;

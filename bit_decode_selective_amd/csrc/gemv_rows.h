@@ -145,68 +145,10 @@ struct CodecStream {
 template <class C>
 __host__ __device__ constexpr int x_chunk_words() { return C::PAIRS + 4; }
 
-// ---- selection + lookup (one 1024-thread workgroup) ----------------------------------
-// Wave 0 scans NBIN = 64 * PER histogram bins from the top: the largest bin whose
-// suffix count reaches `need`; lds[20] = bin, lds[21] = count above it.
-template <int PER>
-__device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int* lds) {
-  constexpr int NBIN = 64 * PER;
-  const int lane = threadIdx.x & 63;
-  int c[PER], s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = (int)h[NBIN - 1 - PER * lane - i];
-    s += c[i];
-  }
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  int run = incl - s;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (run < need && run + c[i] >= need) {
-      lds[20] = NBIN - 1 - PER * lane - i;
-      lds[21] = run;
-    }
-    run += c[i];
-  }
-}
-
 // number of set bits of m in the lanes below this one
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
-
-// Channel-order prefix of per-channel flags f[q] (q = 0..7: this thread's 8
-// consecutive channels) over the whole workgroup: returns the number of flags in
-// earlier channels; *total = all flags.  One LDS round (lds[0..15]).
-template <int NW = SEL_NT / 64>
-__device__ __forceinline__ int blk_flag_prefix(const bool (&f)[8], int* lds, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int below = 0, wtot = 0;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint64_t m = __ballot(f[q]);
-    below += lanes_below(m);
-    wtot += __popcll(m);
-  }
-  __syncthreads();
-  if (lane == 0) lds[wave] = wtot;
-  __syncthreads();
-  int base = 0, sum = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = lds[w];
-    if (w < wave) base += t;
-    sum += t;
-  }
-  *total = sum;
-  return base + below;
-}
-
 
 // ---- the GEMV kernel -------------------------------------------------------------
 // Shared pieces of the row-tile kernels: chunk loads of R rows, the op of a tile
@@ -447,13 +389,14 @@ inline size_t fused_sw_lds_bytes(int k_in, int codes, int nb, int k_sel, int rpw
 // Dynamic LDS, tiles: x pairs [NB][nchunks][PAIRS + 4] | chunk sums [NB][nchunks]
 // | scale words [4][R][K/128]; selector: keys [K/2] | bitmaps [2][K/32] |
 // selection [k_sel] | histograms [4][256] + [4][128] | 16 words.
-inline size_t split_lds_bytes(int k_in, int pairs, int codes, int nb, int k_sel, int rpw) {
+inline size_t split_lds_bytes(int k_in, int pairs, int codes, int nb, int k_sel, int rpw, bool selector = true) {
   (void)pairs;
   (void)codes;
   size_t tile = 0;
   if (k_sel > 0) tile += (size_t)4 * rpw * (k_in / 128) + (size_t)k_sel * (1 + nb + (31 + 4 * rpw * 7 + 31) / 32);
   size_t sel = 0;
-  if (k_sel > 0) sel = (size_t)(k_in / 2) + 2 * (size_t)(k_in / 32) + (((size_t)k_sel + 3) & ~(size_t)3) + 4 * 256 + 4 * 128 + 16;
+  if (k_sel > 0 && selector)
+    sel = (size_t)(k_in / 2) + 2 * (size_t)(k_in / 32) + (((size_t)k_sel + 3) & ~(size_t)3) + 4 * 256 + 4 * 128 + 16;
   return std::max(tile, sel) * 4;
 }
 
@@ -731,8 +674,9 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
                                                   float (&acc)[NB][R], int* sflag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = a.k_sel, K = a.k_in, ngr = K / 128, r = a.r;
+  const bool direct = a.sel_wg == 0;  // the selection is in sel_in, complete before the launch
   if (wave == 0) {
-    const bool ok0 = wait_published(a, tile_g & 63);
+    const bool ok0 = direct || wait_published(a, tile_g & 63);
     if (lane == 0) *sflag = ok0 ? 1 : 0;
   }
   lds_barrier();
@@ -742,11 +686,35 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
   const uint32_t* units = (const uint32_t*)o.pool.slots;
   const bool resident = o.pool.resident != 0;
   const bool any = *sflag != 0 && (resident || o.pool.unit2slot != nullptr);
-  if (any) {
+  // direct: the first tile of each matrix reports its hits and logs its lookups
+  // (one reservation per matrix); the first tile of matrix 0 reports the selection
+  const bool reporter = direct && a.report && tile_g == o.tile_begin;
+  int log_base = -1;
+  if (reporter && o.pool.log_count) {
+    if (tid == 0) sflag[1] = sf_log_reserve(o.pool.log_count, (uint32_t)ks, (uint32_t)o.pool.log_cap);
+    lds_barrier();
+    log_base = sflag[1];
+  }
+  if (any || reporter) {
     const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (tile_g % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
     for (int j = tid; j < ks; j += 256) {
-      const int k = read_published(hc + j, a);
-      int slot = resident ? k : read_published(hc + ks * (1 + op) + j, a);
+      int k, slot;
+      if (direct) {
+        k = a.sel_in ? a.sel_in[j] : j;  // no sel_in: every channel (k_sel = k_in)
+        slot = (unsigned)k >= (unsigned)K ? -1 : (resident ? k : (o.pool.unit2slot ? o.pool.unit2slot[k] : -1));
+        if (reporter) {
+          if (op == 0 && a.sel_out) a.sel_out[j] = k;
+          if (o.hit_out) o.hit_out[j] = slot;
+          if (log_base >= 0) {
+            o.pool.log_units[log_base + j] = k;
+            o.pool.log_slots[log_base + j] = slot;
+          }
+        }
+        if (!any) continue;
+      } else {
+        k = read_published(hc + j, a);
+        slot = resident ? k : read_published(hc + ks * (1 + op) + j, a);
+      }
       if ((unsigned)k >= (unsigned)K) slot = -1;  // never read outside x or the units
       l_hk[j] = slot >= 0 ? k : -1;
       if (slot >= 0) {
@@ -768,7 +736,7 @@ __device__ __forceinline__ void split_refine_tile(const GemvArgs& a, const GemvO
   lds_barrier();  // the hits
   // counted only once every read of the published words has completed (their values
   // are in LDS): the selecting workgroup clears the words when all tiles are counted
-  if (tid == 0) count_reader(a, tile_g & 63);
+  if (tid == 0 && !direct) count_reader(a, tile_g & 63);
   if (!any) return;
   const int pw = toff + wave * R * r;  // this wave's first row in the window
   const int wi0 = pw >> 5, sh0 = pw & 31;
@@ -842,7 +810,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
   __shared__ uint32_t whist[4][256];
   __shared__ uint32_t whist2[4][128];
   __shared__ uint32_t s_cnt[4 * (MAX_SEL_K / 2048)];
-  __shared__ int lds[24];
+  __shared__ int lds[25];
   if constexpr (SW) {
     if (blockIdx.x == 0) {
       __builtin_amdgcn_s_setprio(3);
@@ -1242,7 +1210,7 @@ constexpr int SPLIT_HPF = 8;  // hits per lane whose words are requested togethe
 template <class C, int B, int R, int NB, int D>
 __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
-  __shared__ int s_flag;
+  __shared__ int s_flag[2];
   const int ks = a.k_sel;
   const bool refine = ks > 0;
   if (a.sel_wg && blockIdx.x == 0) {
@@ -1333,7 +1301,7 @@ __global__ __launch_bounds__(256) void gemv_split_kernel(GemvArgs a) {
     }
   }
   // refinement of the hit channels: + x_k * s[row][k/128] * c_lo[row][k]
-  if (refine) split_refine_tile<C, R, NB, wtm_of(R)>(a, o, op, tile_g, row0, szrow, l_hk, l_hx, l_hw, acc, &s_flag);
+  if (refine) split_refine_tile<C, R, NB, wtm_of(R)>(a, o, op, tile_g, row0, szrow, l_hk, l_hx, l_hw, acc, s_flag);
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
@@ -1388,8 +1356,9 @@ inline int device_cus() {
 template <class C, int B, int R, int NB>
 sf_status launch_split(GemvArgs a, hipStream_t s) {
   constexpr int D = R >= 8 ? 1 : 2;
-  const size_t lds = split_lds_bytes(a.k_in, C::PAIRS, C::CODES, NB, a.k_sel, R);
+  const size_t lds = split_lds_bytes(a.k_in, C::PAIRS, C::CODES, NB, a.k_sel, R, a.sel_wg != 0);
   SF_REQUIRE(lds <= MAX_DYN_LDS, SF_EUNSUPPORTED, "k_in too large for the LDS staging of x");
+  // without a selecting workgroup no workgroup waits for another: any grid size
   // the tiles wait for workgroup 0 only at their end, but a tile that has to wait
   // for a free slot adds a whole tile time: when the grid does not fit the device
   // at once, the fused kernel (selection in every workgroup) is used instead
@@ -1400,7 +1369,7 @@ sf_status launch_split(GemvArgs a, hipStream_t s) {
     occ = 1;
   // SF_GEMV_SPLIT=2 always takes the staged variant (x in LDS, workgroup 0 selecting)
   const bool staged = env_int("SF_GEMV_SPLIT", 1) == 2;
-  if (staged || (long)occ * device_cus() < (long)a.total_tiles + a.sel_wg) {
+  if (a.sel_wg && (staged || (long)occ * device_cus() < (long)a.total_tiles + a.sel_wg)) {
     // the staged variant needs fewer registers; else the fused kernel
     constexpr int D2 = R >= 8 ? 1 : (R >= 4 ? 2 : 4);
     const size_t lds2 = fused_sw_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);

@@ -9,6 +9,7 @@
 // with reductions inside a workgroup only.
 #include <algorithm>
 
+#include "select_core.h"
 #include "sf_internal.h"
 
 namespace {
@@ -203,6 +204,157 @@ __global__ __launch_bounds__(AMAX_T) void argmax_kernel(const float* logits, int
 
 unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 4096); }
 
+// ---- producers of a GEMV input that also select its channels ----------------------
+// One 1024-thread workgroup forms the fp16 input x of `batch` rows of n channels and
+// selects the k_sel channels of largest max-over-rows |x| (select_core.h), so that
+// the GEMV that reads x starts with its selection ready.  Thread t owns channels
+// 8m .. 8m+7 of every row, m = t + 1024 i (i < MI).  The element arithmetic is that
+// of sf_add_rmsnorm, sf_swiglu and sf_to_f16.
+constexpr int PS_T = 1024, PS_MAXB = 16;
+enum ProdOp { PROD_NORM = 0, PROD_SWIGLU = 1, PROD_CAST = 2 };
+
+struct ProdArgs {
+  float* h;         // NORM: residual rows [batch][n] (h += y in place when y is given)
+  const float* y;
+  const float* w;   // NORM: gain [n]
+  const float* a;   // SWIGLU: gate; CAST: x
+  const float* b;   // SWIGLU: up
+  int batch, n;
+  float eps;
+  uint16_t* out;    // [batch][n] fp16 bits
+  int k_sel;
+  int32_t* sel_out; // [k_sel]
+};
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <int OP, int MI>
+__global__ __launch_bounds__(PS_T) void produce_select_kernel(ProdArgs p) {
+  __shared__ float red[PS_T / 64][PS_MAXB];
+  __shared__ float rstd[PS_MAXB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = p.n, n8 = n / 8;
+  // rows 0 and 1 of this thread's channels stay in registers between the passes
+  float keep[2][MI][8];
+  if constexpr (OP == PROD_NORM) {
+    // h += y, and per row the sum of squares (all rows reduced together)
+    float ss[PS_MAXB];
+#pragma unroll
+    for (int bb = 0; bb < PS_MAXB; ++bb) ss[bb] = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < PS_MAXB; ++bb) {
+      if (bb >= p.batch) break;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = tid + PS_T * i;
+        if (m >= n8) continue;
+        float v[8], t[8];
+        load8(p.h + (size_t)bb * n + 8 * m, v);
+        if (p.y) load8(p.y + (size_t)bb * n + 8 * m, t);
+        if (p.y) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += t[e];
+          float4* hp = (float4*)(p.h + (size_t)bb * n + 8 * m);
+          hp[0] = make_float4(v[0], v[1], v[2], v[3]);
+          hp[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[bb] = fmaf(v[e], v[e], ss[bb]);
+        if (bb < 2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) keep[bb][i][e] = v[e];
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < PS_MAXB; ++bb) {
+      if (bb >= p.batch) break;
+      float v = ss[bb];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) red[wave][bb] = v;
+    }
+    __syncthreads();
+    if (tid < p.batch) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < PS_T / 64; ++w) t += red[w][tid];
+      rstd[tid] = 1.f / sqrtf(t / (float)n + p.eps);
+    }
+    __syncthreads();
+  }
+  uint32_t kw[4 * MI];
+#pragma unroll
+  for (int i = 0; i < 4 * MI; ++i) kw[i] = 0u;
+  for (int bb = 0; bb < p.batch; ++bb) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int m = tid + PS_T * i;
+      if (m >= n8) continue;
+      const size_t off = (size_t)bb * n + 8 * m;
+      float v[8];
+      if constexpr (OP == PROD_NORM) {
+        float g[8];
+        if (bb < 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = keep[bb < 1 ? 0 : 1][i][e];
+        } else {
+          load8(p.h + off, v);
+        }
+        load8(p.w + 8 * m, g);
+        const float rs = rstd[bb];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * rs * g[e];
+      } else if constexpr (OP == PROD_SWIGLU) {
+        float u[8];
+        load8(p.a + off, v);
+        load8(p.b + off, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] / (1.f + expf(-v[e])) * u[e];
+      } else {
+        load8(p.a + off, v);
+      }
+      uint32_t x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = (uint32_t)f2h(v[2 * q]) | ((uint32_t)f2h(v[2 * q + 1]) << 16);
+      ((uint4*)(p.out + off))[0] = make_uint4(x[0], x[1], x[2], x[3]);
+      sfsel::key_max8(kw + 4 * i, x);
+    }
+  }
+  const int ks = p.k_sel;
+  if (ks <= 0 || !p.sel_out) return;
+  if (ks >= n) {
+    for (int j = tid; j < ks; j += PS_T) p.sel_out[j] = j;
+    return;
+  }
+  sfsel::topk_keys<PS_T, MI>(kw, n, ks, p.sel_out);
+}
+
+template <int OP>
+sf_status launch_produce(const ProdArgs& p, hipStream_t s) {
+  const int mi = (p.n / 8 + PS_T - 1) / PS_T;
+  if (mi <= 1)
+    hipLaunchKernelGGL((produce_select_kernel<OP, 1>), dim3(1), dim3(PS_T), 0, s, p);
+  else if (mi <= 2)
+    hipLaunchKernelGGL((produce_select_kernel<OP, 2>), dim3(1), dim3(PS_T), 0, s, p);
+  else
+    hipLaunchKernelGGL((produce_select_kernel<OP, 4>), dim3(1), dim3(PS_T), 0, s, p);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+sf_status check_produce(const ProdArgs& p) {
+  const auto al = [](const void* q, uintptr_t a) { return q == nullptr || ((uintptr_t)q & (a - 1)) == 0; };
+  SF_REQUIRE(p.out && p.batch >= 1 && p.batch <= PS_MAXB, SF_EINVAL, "need an output and 1 <= batch <= 16");
+  SF_REQUIRE(p.n > 0 && p.n % 8 == 0 && p.n <= 8 * PS_T * 4, SF_EINVAL, "n must be a multiple of 8, at most 32768");
+  SF_REQUIRE(p.k_sel >= 0 && p.k_sel <= p.n && (p.k_sel == 0 || p.sel_out), SF_EINVAL, "bad k_sel / sel_out");
+  SF_REQUIRE(al(p.h, 16) && al(p.y, 16) && al(p.w, 16) && al(p.a, 16) && al(p.b, 16) && al(p.out, 16), SF_EINVAL,
+             "tensors must be 16-byte aligned");
+  return SF_OK;
+}
+
 }  // namespace
 
 extern "C" sf_status sf_embed(const uint16_t* table_f16, int64_t vocab, int32_t hidden, const int32_t* ids,
@@ -261,4 +413,32 @@ extern "C" sf_status sf_argmax(const float* logits, int32_t batch, int64_t vocab
   hipLaunchKernelGGL(argmax_kernel, dim3(batch), dim3(AMAX_T), 0, (hipStream_t)stream, logits, vocab, ids);
   SF_LAUNCH_CHECK();
   return SF_OK;
+}
+
+extern "C" sf_status sf_add_rmsnorm_select(float* h, const float* y, const float* w, int32_t batch, int32_t hidden,
+                                           float eps, uint16_t* x_f16, int32_t k_sel, int32_t* sel_out,
+                                           sf_stream stream) {
+  SF_REQUIRE(h && w && eps >= 0.f, SF_EINVAL, "null argument");
+  ProdArgs p{h, y, w, nullptr, nullptr, batch, hidden, eps, x_f16, k_sel, sel_out};
+  sf_status st = check_produce(p);
+  if (st != SF_OK) return st;
+  return launch_produce<PROD_NORM>(p, (hipStream_t)stream);
+}
+
+extern "C" sf_status sf_swiglu_select(const float* gate, const float* up, int32_t batch, int32_t n, uint16_t* act_f16,
+                                      int32_t k_sel, int32_t* sel_out, sf_stream stream) {
+  SF_REQUIRE(gate && up, SF_EINVAL, "null argument");
+  ProdArgs p{nullptr, nullptr, nullptr, gate, up, batch, n, 0.f, act_f16, k_sel, sel_out};
+  sf_status st = check_produce(p);
+  if (st != SF_OK) return st;
+  return launch_produce<PROD_SWIGLU>(p, (hipStream_t)stream);
+}
+
+extern "C" sf_status sf_to_f16_select(const float* x, int32_t batch, int32_t n, uint16_t* out_f16, int32_t k_sel,
+                                      int32_t* sel_out, sf_stream stream) {
+  SF_REQUIRE(x, SF_EINVAL, "null argument");
+  ProdArgs p{nullptr, nullptr, nullptr, x, nullptr, batch, n, 0.f, out_f16, k_sel, sel_out};
+  sf_status st = check_produce(p);
+  if (st != SF_OK) return st;
+  return launch_produce<PROD_CAST>(p, (hipStream_t)stream);
 }

@@ -102,13 +102,22 @@ class DecodeModel:
     pool_frac  None: every refinement unit resident on the device (pools never
                miss); else the device slots per pool as a fraction of its units,
                filled from pinned host stores by the cache (LRU)
+    head       False: the layers only (no embedding, final norm, lm_head or argmax);
+               the step then starts from the residual state in ``h``
+    producer_select
+               the kernel that forms each GEMV input also selects its channels
+               (sf_add_rmsnorm_select, sf_to_f16_select, sf_swiglu_select) and the
+               GEMV takes that selection as sel_in (batch <= 16); otherwise each GEMV
+               selects its channels itself
     """
 
     def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
-                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda"):
+                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True):
         import torch
 
         self.torch, self.spec, self.batch, self.t_cap = torch, spec, batch, t_cap
+        self.head = head
+        self.producer_select = producer_select and batch <= 16
         self.b, self.r, self.kv_b, self.kv_r = b, r, kv_b, kv_r
         self.ch_pct, self.tok_pct = ch_pct, tok_pct
         dev = torch.device(device)
@@ -164,12 +173,14 @@ class DecodeModel:
             self.layers.append(L)
             torch.cuda.synchronize()
         self.final_norm = torch.as_tensor(src.gain(S.layers, FINAL_NORM, H), device=dev)
-        emb = src.embedding(S.vocab, H)
-        if keep_host:
-            self.host["embed"] = emb
-        self.embed = binding._f16_bits(emb, dev)
-        self.lm_head = quant(S.layers, inputs.LM_HEAD, S.vocab, H)
-        self.pool_lm = add_pool(self.lm_head, k_select(ch_pct, H)) if r > 0 else -1
+        self.pool_lm = -1
+        if head:
+            emb = src.embedding(S.vocab, H)
+            if keep_host:
+                self.host["embed"] = emb
+            self.embed = binding._f16_bits(emb, dev)
+            self.lm_head = quant(S.layers, inputs.LM_HEAD, S.vocab, H)
+            self.pool_lm = add_pool(self.lm_head, k_select(ch_pct, H)) if r > 0 else -1
         self._pool_frac = pool_frac
         self._pools, self._stores = pools, stores
         self.cache = binding.RefineCache(pools, mode=cache_mode, device=dev, keep=stores) if pools else None
@@ -226,7 +237,7 @@ class DecodeModel:
                 "hit_tok": torch.empty(B * S.n_kv * max(1, self.t_cap), dtype=torch.int32, device=self.dev),
             })
         self.x_final = torch.empty((B, S.hidden), **i16)
-        self.logits = torch.empty((B, S.vocab), **f32)
+        self.logits = torch.empty((B, S.vocab if self.head else 1), **f32)
         self.sel_lm = torch.empty(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32, device=self.dev)
         self.hits = {}  # (layer index or -1, op name) -> hit tensor [k_sel] of each GEMV op
 
@@ -241,6 +252,8 @@ class DecodeModel:
                 for i, n in enumerate(names):
                     arr[i] = binding.sf_gemv_op(self.layers[li][n].desc(), -1, None, None)
                 best = max(best, L.sf_workspace_bytes_gemv(arr, len(names), self.batch, k_select(self.ch_pct, k_in)))
+        if not self.head:
+            return best
         arr = (binding.sf_gemv_op * 1)(binding.sf_gemv_op(self.lm_head.desc(), -1, None, None))
         return max(best, L.sf_workspace_bytes_gemv(arr, 1, self.batch, k_select(self.ch_pct, S.hidden)))
 
@@ -259,8 +272,15 @@ class DecodeModel:
         keep = []
         calls = []
 
-        def gemv(names, layer, x, ys, k_in, sel):
-            ks = k_select(self.ch_pct, k_in) if refined and self.r > 0 else 0
+        ps = self.producer_select
+
+        def ksel(k_in):
+            return k_select(self.ch_pct, k_in) if refined and self.r > 0 else 0
+
+        def gemv(names, layer, x, ys, k_in, sel, tag):
+            """The selection is in `sel` already when its producer made it (sel_in);
+            otherwise the GEMV computes it and writes it there (sel_out)."""
+            ks = ksel(k_in)
             arr = (binding.sf_gemv_op * len(names))()
             for i, (n, y) in enumerate(zip(names, ys)):
                 W = layer[n] if isinstance(n, str) else n
@@ -270,16 +290,25 @@ class DecodeModel:
                 keep.append(hit)
                 arr[i] = binding.sf_gemv_op(W.desc(), pool, y.data_ptr(), hit.data_ptr())
             keep.append(arr)
-            calls.append((Lb.sf_refined_gemv, [arr, len(names), P(x), B, ks, None, P(sel), cache, ws.handle, None]))
+            sel_in, sel_out = (P(sel), None) if (ps and ks > 0) else (None, P(sel))
+            calls.append((Lb.sf_refined_gemv, [arr, len(names), P(x), B, ks, sel_in, sel_out, cache, ws.handle, None], tag))
 
-        calls.append((Lb.sf_embed, [P(self.embed), S.vocab, S.hidden, P(self.ids), B, P(self.h), None]))
+        def norm(y, w, x, sel, k_in, tag):
+            if ps:
+                calls.append((Lb.sf_add_rmsnorm_select, [P(self.h), P(y), P(w), B, S.hidden, S.eps, P(x), ksel(k_in),
+                                                         P(sel), None], tag))
+            else:
+                calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(y), P(w), B, S.hidden, S.eps, P(x), None], tag))
+
+        if self.head:
+            calls.append((Lb.sf_embed, [P(self.embed), S.vocab, S.hidden, P(self.ids), B, P(self.h), None], "embed"))
         for li, L in enumerate(self.layers):
             bf = self.buf[li]
             prev = self.buf[li - 1]["down"] if li > 0 else None
-            calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(prev), P(L["attn_norm"]), B, S.hidden, S.eps, P(bf["x_attn"]), None]))
-            gemv(("q", "k", "v"), L, bf["x_attn"], (bf["q"], bf["k"], bf["v"]), S.hidden, bf["sel_attn"])
+            norm(prev, L["attn_norm"], bf["x_attn"], bf["sel_attn"], S.hidden, "norm")
+            gemv(("q", "k", "v"), L, bf["x_attn"], (bf["q"], bf["k"], bf["v"]), S.hidden, bf["sel_attn"], "qkv")
             calls.append((Lb.sf_qk_rope, [P(bf["q"]), P(bf["k"]), B, S.n_q, S.n_kv, P(L.get("q_norm")), P(L.get("k_norm")),
-                                          S.eps, pos, S.theta, P(bf["q16"]), P(bf["k_rot"]), None]))
+                                          S.eps, pos, S.theta, P(bf["q16"]), P(bf["k_rot"]), None], "rope"))
             kv = L["kv"]
             dsc_app = kv.desc(pos)
             # the new token's refinement units: into the device copy, or straight into the
@@ -290,32 +319,47 @@ class DecodeModel:
                 dst = kv.refine.data_ptr() + pos * kv.unit_bytes
             keep.append(dsc_app)
             calls.append((Lb.sf_kv_append, [P(bf["k_rot"]), P(bf["v"]), 1, pos, C.byref(dsc_app), C.c_void_p(dst), kv.t_cap,
-                                            None]))
+                                            None], "append"))
             dsc = kv.desc(pos + 1)
             keep.append(dsc)
             kt = k_select(self.tok_pct, pos + 1) if refined and self.kv_r > 0 else 0
             pool_kv = L.get("pool_kv", -1) if cache is not None else -1
             calls.append((Lb.sf_refined_attn_decode, [P(bf["q16"]), S.n_q, C.byref(dsc), 1.0 / math.sqrt(d), kt, None,
                                                       cache, pool_kv, P(bf["attn"]), P(bf["sel_tok"]), P(bf["hit_tok"]),
-                                                      ws.handle, None]))
-            calls.append((Lb.sf_to_f16, [P(bf["attn"]), B * S.n_q * d, P(bf["a16"]), None]))
-            gemv(("o",), L, bf["a16"], (bf["o"],), S.n_q * d, bf["sel_o"])
-            calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(bf["o"]), P(L["ffn_norm"]), B, S.hidden, S.eps, P(bf["x_ffn"]), None]))
-            gemv(("gate", "up"), L, bf["x_ffn"], (bf["gate"], bf["up"]), S.hidden, bf["sel_ffn"])
-            calls.append((Lb.sf_swiglu, [P(bf["gate"]), P(bf["up"]), B * S.ffn, P(bf["act"]), None]))
-            gemv(("down",), L, bf["act"], (bf["down"],), S.ffn, bf["sel_down"])
-        calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(self.buf[-1]["down"]), P(self.final_norm), B, S.hidden, S.eps,
-                                          P(self.x_final), None]))
-        gemv((self.lm_head,), {}, self.x_final, (self.logits,), S.hidden, self.sel_lm)
-        calls.append((Lb.sf_argmax, [P(self.logits), B, S.vocab, P(self.next_ids), None]))
+                                                      ws.handle, None], "attn"))
+            if ps:
+                calls.append((Lb.sf_to_f16_select, [P(bf["attn"]), B, S.n_q * d, P(bf["a16"]), ksel(S.n_q * d),
+                                                    P(bf["sel_o"]), None], "cast"))
+            else:
+                calls.append((Lb.sf_to_f16, [P(bf["attn"]), B * S.n_q * d, P(bf["a16"]), None], "cast"))
+            gemv(("o",), L, bf["a16"], (bf["o"],), S.n_q * d, bf["sel_o"], "o")
+            norm(bf["o"], L["ffn_norm"], bf["x_ffn"], bf["sel_ffn"], S.hidden, "norm")
+            gemv(("gate", "up"), L, bf["x_ffn"], (bf["gate"], bf["up"]), S.hidden, bf["sel_ffn"], "gateup")
+            if ps:
+                calls.append((Lb.sf_swiglu_select, [P(bf["gate"]), P(bf["up"]), B, S.ffn, P(bf["act"]), ksel(S.ffn),
+                                                    P(bf["sel_down"]), None], "swiglu"))
+            else:
+                calls.append((Lb.sf_swiglu, [P(bf["gate"]), P(bf["up"]), B * S.ffn, P(bf["act"]), None], "swiglu"))
+            gemv(("down",), L, bf["act"], (bf["down"],), S.ffn, bf["sel_down"], "down")
+        if self.head:
+            norm(self.buf[-1]["down"], self.final_norm, self.x_final, self.sel_lm, S.hidden, "norm")
+            gemv((self.lm_head,), {}, self.x_final, (self.logits,), S.hidden, self.sel_lm, "lm_head")
+            calls.append((Lb.sf_argmax, [P(self.logits), B, S.vocab, P(self.next_ids), None], "argmax"))
         return calls, keep
 
-    def enqueue(self, calls, stream):
+    def enqueue(self, calls, stream, timer=None):
+        """Launch the calls on `stream`; timer(tag) -> (start, end) events recorded
+        around each call when given."""
         s = C.c_void_p(stream.cuda_stream)
-        for fn, args in calls:
+        for fn, args, tag in calls:
             a = list(args)
             a[-1] = s
+            ev = timer(tag) if timer is not None else None
+            if ev is not None:
+                ev[0].record(stream)
             st = fn(*a)
+            if ev is not None:
+                ev[1].record(stream)
             if st != 0:
                 binding.check(st)
 

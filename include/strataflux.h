@@ -235,9 +235,15 @@ size_t sf_workspace_bytes_gemv(const sf_gemv_op* ops, int32_t n_ops, int32_t bat
  * (device [k_sel], may be NULL) receives the selection, ascending.  k_sel = 0 is
  * the unrefined low-bit GEMV.  cache may be NULL (every selection misses).
  * A computed selection (sel_in NULL, 0 < k_sel < k_in) needs k_in <= 32768
- * (SF_EUNSUPPORTED otherwise).  Launches: the selection with its lookups (k_sel
- * > 0), then the GEMV: for b in {1, 2, 4, 8} and batch >= 3 the batched MFMA
- * kernel, one launch per 16 batch rows; otherwise one launch per 2 batch rows. */
+ * (SF_EUNSUPPORTED otherwise).  Launches at batch 1-2: one; its first workgroup
+ * computes the selection while the others stream the resident codes, or, with
+ * sel_in given, every workgroup looks up its hits itself.  At batch >= 3: the
+ * selection with its lookups, then for b in {1, 2, 4, 8} the batched MFMA kernel,
+ * one launch per 16 batch rows, otherwise one launch per 2 batch rows.
+ * Test hooks (environment): SF_GEMV_SPLIT=0 / 2 forces the variant where every
+ * workgroup selects / the variant with x staged in LDS; SF_GEMV_ROWS_PER_WAVE=4 / 8;
+ * SF_GEMV_MFMA=0 / 1, SF_GEMV_MFMA_RT, SF_GEMV_MFMA_SLICES force the batched
+ * kernel's use and plan. */
 sf_status sf_refined_gemv(const sf_gemv_op* ops, int32_t n_ops, const uint16_t* x_f16,
                           int32_t batch, int32_t k_sel, const int32_t* sel_in,
                           int32_t* sel_out, sf_refine_cache* cache, sf_workspace* ws,
@@ -304,6 +310,25 @@ sf_status sf_add_rmsnorm(float* h, const float* y, const float* w, int32_t batch
 sf_status sf_qk_rope(const float* q, const float* k, int32_t batch, int32_t n_q, int32_t n_kv,
                      const float* q_norm_w, const float* k_norm_w, float eps, int32_t pos,
                      float theta, uint16_t* q_f16, float* k_out, sf_stream stream);
+
+/* Producers of a refined GEMV's input that also select its channels (rag-lover.com
+ * StrataFlux summary, explainer dialogue: weight refinements are chosen by
+ * input-activation magnitude).  Each is one launch of one workgroup that writes the
+ * fp16 input x [batch][n] exactly as the call named in its comment does and, in the
+ * same launch, the k_sel channels of largest max-over-rows |x| (ties to the lower
+ * channel) in ascending order to sel_out (device [k_sel]; k_sel = 0 selects nothing,
+ * k_sel = n every channel).  Passing sel_out as the GEMV's sel_in lets the GEMV start
+ * with its selection ready.  1 <= batch <= 16, n % 8 == 0, n <= 32768, every tensor
+ * 16-byte aligned (SF_EINVAL otherwise).
+ * sf_add_rmsnorm_select: sf_add_rmsnorm (hidden = n).
+ * sf_swiglu_select: sf_swiglu over gate, up [batch][n].
+ * sf_to_f16_select: sf_to_f16 of x [batch][n]. */
+sf_status sf_add_rmsnorm_select(float* h, const float* y, const float* w, int32_t batch, int32_t hidden, float eps,
+                                uint16_t* x_f16, int32_t k_sel, int32_t* sel_out, sf_stream stream);
+sf_status sf_swiglu_select(const float* gate, const float* up, int32_t batch, int32_t n, uint16_t* act_f16,
+                           int32_t k_sel, int32_t* sel_out, sf_stream stream);
+sf_status sf_to_f16_select(const float* x, int32_t batch, int32_t n, uint16_t* out_f16, int32_t k_sel,
+                           int32_t* sel_out, sf_stream stream);
 
 /* act_f16[i] = fp16(silu(gate[i]) * up[i]), silu(x) = x / (1 + e^-x); n elements. */
 sf_status sf_swiglu(const float* gate, const float* up, int64_t n, uint16_t* act_f16, sf_stream stream);

@@ -33,7 +33,10 @@ def _step_x(cfg, step, k_in, batch=1):
 
 
 @pytest.mark.parametrize("capacity,max_fill", [(24, 0), (24, 5), (0, 0), (512, 0)])
-def test_gemv_lru_over_steps(capacity, max_fill):
+@pytest.mark.parametrize("given", [False, True])
+def test_gemv_lru_over_steps(capacity, max_fill, given):
+    """given: the selection comes in as sel_in (as a producer kernel hands it over),
+    so each tile looks its hits up itself and the first tile logs the lookups."""
     k_in, n_out, ks = 512, 256, 16
     qw, q = _weight(60, n_out, k_in, 2, 2)
     store = qw.host_store()
@@ -41,7 +44,8 @@ def test_gemv_lru_over_steps(capacity, max_fill):
     pool = o_cache.LRUPool(capacity)
     for t in range(8):
         x = _step_x(60 + t % 3, t, k_in)
-        (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, ks, cache=cache)
+        sel_in = np.array(selection.select_channels(x, ks), dtype=np.int32) if given else None
+        (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, ks, cache=cache, sel_in=sel_in)
         torch.cuda.synchronize()
         sel = sel.cpu().numpy().tolist()
         hit = hit.cpu().numpy()

@@ -288,3 +288,43 @@ def test_decode_full_width_llama_w3r1_pools10():
     """The 128K workload's formats at full width: 3-bit weights + 1 refinement bit,
     2+2-bit KV, pools of 10%, 8 steps (short context)."""
     _run_steps(WIDE_LLAMA, 1, 192, 8, 91, b=3, r=1, pool_frac=0.10, output_steps={0, 7})
+
+
+@pytest.mark.parametrize("batch", [1, 3, 16])
+@pytest.mark.parametrize("n,k_sel", [(4096, 123), (14336, 431), (12288, 369), (256, 128), (4096, 0), (1024, 1024),
+                                     (40, 1)])
+def test_producers_select_their_channels(batch, n, k_sel):
+    """sf_add_rmsnorm_select / sf_swiglu_select / sf_to_f16_select: the fp16 output as
+    the oracle forms it (one fp16 rounding: within one ulp; the cast exactly), and the
+    selection exactly the oracle top-k by max-over-rows |x| of that output."""
+    rng = np.random.default_rng(n + batch + k_sel)
+    T = lambda a: torch.as_tensor(a, device="cuda")
+    h = rng.standard_normal((batch, n)).astype(np.float32)
+    y = (rng.standard_normal((batch, n)) * 0.5).astype(np.float32)
+    w = inputs.norm_gain(9, 1, 0, n)
+    ht = T(h)
+    x, sel = binding.add_rmsnorm_select(ht, T(y), T(w), 1e-5, k_sel)
+    assert np.array_equal(ht.cpu().numpy(), h + y)
+    xg = _f16(x)
+    assert_close(xg, o_dec.rmsnorm((h + y).astype(np.float64), w, 1e-5), what="norm", **F16)
+    assert sel.cpu().numpy().tolist() == selection.select_channels(xg.astype(np.float16), k_sel)
+    g = (rng.standard_normal((batch, n)) * 4).astype(np.float32)
+    u = rng.standard_normal((batch, n)).astype(np.float32)
+    act, sel = binding.swiglu_select(T(g), T(u), k_sel)
+    ag = _f16(act)
+    assert_close(ag, o_dec.swiglu(g.astype(np.float64), u.astype(np.float64)), what="swiglu", **F16)
+    assert sel.cpu().numpy().tolist() == selection.select_channels(ag.astype(np.float16), k_sel)
+    v = (rng.standard_normal((batch, n)) * 30).astype(np.float32)
+    c, sel = binding.to_f16_select(T(v), k_sel)
+    cg = _f16(c)
+    assert np.array_equal(cg, v.astype(np.float16).astype(np.float64))
+    assert sel.cpu().numpy().tolist() == selection.select_channels(cg.astype(np.float16), k_sel)
+
+
+def test_producer_ties_go_to_lower_channels():
+    """Equal magnitudes (including signs) at the k-th place: the lower channels win."""
+    v = np.zeros((2, 512), dtype=np.float32)
+    v[0, [7, 100, 300, 301]] = [2.0, -2.0, 2.0, 1.0]
+    v[1, [5, 300]] = [-2.0, 3.0]
+    c, sel = binding.to_f16_select(torch.as_tensor(v, device="cuda"), 3)
+    assert sel.cpu().numpy().tolist() == [5, 7, 300]
