@@ -1,22 +1,18 @@
 #!/usr/bin/env python3
 """Refined low-bit decode-step benchmark on one MI355X.
 
-Default workload: one decode step of a Llama-3.1-8B-shaped model at batch 1 through
-the whole refined path, 32 layers, each:
-  residual add + RMSNorm (which also selects the q/k/v channels),
+Default workload (llama8b-step): the GEMVs and attention of one decode step of a
+Llama-3.1-8B-shaped model at batch 1, 32 layers, each:
+  KV append (the new token quantised into the 2+2-bit cache),
   q/k/v refined GEMV (one fused launch, top 3% input channels refined),
-  rotary embedding, KV append (the new token quantised into the 2+2-bit cache),
   refined GQA attention over the 32768-token context (32 query / 8 KV heads, head
   dim 128, top 2% tokens refined),
-  fp16 cast of the attention output (selecting the o channels), o refined GEMV,
-  residual add + RMSNorm (selecting the gate/up channels), gate/up refined GEMV,
-  SwiGLU (selecting the down channels), down refined GEMV.
-The step starts from a synthetic residual state (in place of the embedding; no
-lm_head, as the GEMV configuration has none).  Weights and KV are 2-bit resident +
-2-bit refinement, group 128.  Every refinement pool holds all of its units on the
-device, so every selected unit hits.  Inputs are seeded synthetic data with the
-pages' shapes and distributions (no trained weights or datasets): W ~ N(0, 0.02),
-K and V ~ N(0, 1) with 4 dims of K x8, RMSNorm gains 1 with 1% of channels x20.
+  o refined GEMV, gate/up refined GEMV (one fused launch), down refined GEMV.
+Every GEMV input is a seeded synthetic fp16 vector, N(0, 1) with 1% of channels
+x20; W ~ N(0, 0.02); K and V ~ N(0, 1) with 4 dims of K x8; q ~ N(0, 1) (no trained
+weights or datasets).  Weights and KV are 2-bit resident + 2-bit refinement, group
+128.  Every refinement pool holds all of its units on the device, so every
+selected unit hits.
 
 Timing: the step is captured once as a HIP graph and replayed; inputs are resident
 in HBM before the timed region.  Every call of the step is also timed on its own
@@ -24,9 +20,12 @@ with HIP events in eager passes over the same step (every layer's own matrices a
 cache, so nothing is timed hot); the call with the largest share of the step gives
 the roofline line.  The CPU baseline is the fp64 oracle on a bounded sample.
 
-Other workloads (--workload): full greedy decode steps with embedding and lm_head of
-a Qwen3-8B-shaped model at context 8192 with 25% LRU pools, or a Llama-3.1-8B-shaped
-model at context 131072 with 3+1-bit weights and 10% pools with asynchronous fills.
+Other workloads (--workload): llama8b-layers runs whole decoder layers (RMSNorm,
+RoPE, SwiGLU and casts between the GEMVs, each GEMV input produced by the layer);
+qwen3-8b-decode and llama8b-128k-decode run full greedy decode steps with embedding
+and lm_head, a Qwen3-8B-shaped model at context 8192 with 25% LRU pools or a
+Llama-3.1-8B-shaped model at context 131072 with 3+1-bit weights and 10% pools with
+asynchronous fills.
 """
 from __future__ import annotations
 
@@ -268,57 +267,167 @@ def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, bat
 
 
 # ---- workloads -------------------------------------------------------------------------
-def layer_step(args):
-    """The default workload: the decoder layers of a Llama-3.1-8B-shaped step."""
+class SyntheticStep:
+    """The default workload: 32 Llama-3.1-8B-shaped layers with synthetic GEMV inputs.
+
+    Per layer, in launch order: KV append of the new token, the q/k/v GEMVs (one fused
+    launch over one input), refined attention over the layer's own cache, o, gate/up
+    (one fused launch), down.  Every GEMV input is its own seeded fp16 vector of
+    N(0, 1) with 1% of channels x20 (the GEMV configuration's activations), so each
+    GEMV selects its own channels; q ~ N(0, 1); K and V ~ N(0, 1) with 4 dims of K x8.
+    Every refinement pool holds all of its units on the device (every selected unit
+    hits)."""
+
+    def __init__(self, layers, T, batch, b=2, r=2, ch_pct=3, tok_pct=2, seed=1234):
+        import torch
+
+        from bit_decode_selective_amd import binding, decode, inputs
+
+        self.torch, self.binding = torch, binding
+        base = decode.LLAMA31_8B
+        self.spec = decode.Spec(base.name, layers, base.hidden, base.n_q, base.n_kv, base.ffn, base.vocab,
+                                base.qk_norm, base.theta, base.eps)
+        S = self.spec
+        self.layers, self.T, self.batch = layers, T, batch
+        self.b, self.r, self.kv_b, self.kv_r, self.ch_pct, self.tok_pct = b, r, b, r, ch_pct, tok_pct
+        dev = torch.device("cuda", 0)
+        self.dev = dev
+        g = torch.Generator(device=dev)
+        H, QD, KD = S.hidden, S.n_q * HD, S.n_kv * HD
+        pools, self.groups, self.kvs = [], [], []
+        for li in range(layers):
+            g.manual_seed(seed + li)
+            mats = {}
+            for name, (n, k) in (("q", (QD, H)), ("k", (KD, H)), ("v", (KD, H)), ("o", (H, QD)),
+                                 ("gate", (S.ffn, H)), ("up", (S.ffn, H)), ("down", (H, S.ffn))):
+                W = inputs.torch_weight(g, n, k, device=dev)
+                mats[name] = binding.QuantWeight.from_device(W, b, r)
+                del W
+            grp = []
+            for tag, names in (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")),
+                               ("down", ("down",))):
+                ops = []
+                for nm in names:
+                    ops.append((mats[nm], len(pools)))
+                    pools.append(mats[nm].resident_pool_desc())
+                grp.append((tag, ops, mats[names[0]].k_in))
+            self.groups.append(grp)
+            kv = binding.QuantKV(batch, S.n_kv, T, b, r, device=dev)
+            for t0 in range(0, T - 1, 8192):
+                K, V = inputs.torch_kv(g, batch, S.n_kv, min(8192, T - 1 - t0), HD, device=dev)
+                kv.append(K, V)
+                del K, V
+            self.kvs.append((kv, len(pools)))
+            pools.append(kv.resident_pool_desc())
+            torch.cuda.synchronize()
+        self.cache = binding.RefineCache(pools, device=dev)
+        self.x, self.y, self.q, self.knew, self.out = [], [], [], [], []
+        for li in range(layers):
+            g.manual_seed(seed + 1000 + li)
+            xs, ys = [], []
+            for tag, ops, k_in in self.groups[li]:
+                outl = torch.randperm(k_in, generator=g, device=dev)[: (k_in + 99) // 100].cpu().numpy()
+                xs.append(binding._f16_bits(inputs.torch_activation(g, batch, k_in, outl, device=dev), dev))
+                ys.append([torch.empty((batch, w.n_out), dtype=torch.float32, device=dev) for w, _ in ops])
+            self.x.append(xs)
+            self.y.append(ys)
+            self.q.append(binding._f16_bits(torch.randn((batch, S.n_q, HD), generator=g, device=dev).half(), dev))
+            K, V = inputs.torch_kv(g, batch, S.n_kv, 1, HD, device=dev)
+            self.knew.append((K.contiguous(), V.contiguous()))
+            self.out.append(torch.empty((batch, S.n_q, HD), dtype=torch.float32, device=dev))
+        L = binding.lib()
+        wsb = [L.sf_workspace_bytes_attn(batch, S.n_q, S.n_kv, T, k_select(tok_pct, T))]
+        for grp in self.groups:
+            for tag, ops, k_in in grp:
+                arr = (binding.sf_gemv_op * len(ops))(*[binding.sf_gemv_op(w.desc(), p, None, None) for w, p in ops])
+                wsb.append(L.sf_workspace_bytes_gemv(arr, len(ops), batch, k_select(ch_pct, k_in)))
+        self.ws = binding.workspace(max(wsb), dev)
+        torch.cuda.synchronize()
+
+    def build_step(self, refined=True):
+        """(function, args, tag) of every launch of one step; `keep` holds the ctypes
+        objects the argument tuples point into."""
+        b, L, S, T = self.binding, self.binding.lib(), self.spec, self.T
+        calls, keep = [], []
+        for li in range(self.layers):
+            kv, kv_pool = self.kvs[li]
+            Kn, Vn = self.knew[li]
+            dsc_app = kv.desc(T - 1)
+            keep.append(dsc_app)
+            dst = kv.refine.data_ptr() + (T - 1) * kv.unit_bytes
+            calls.append((L.sf_kv_append, (C.c_void_p(Kn.data_ptr()), C.c_void_p(Vn.data_ptr()), 1, T - 1,
+                                           C.byref(dsc_app), C.c_void_p(dst), kv.t_cap, None), "append"))
+            for gi, (tag, ops, k_in) in enumerate(self.groups[li]):
+                ks = k_select(self.ch_pct, k_in) if refined else 0
+                arr = (b.sf_gemv_op * len(ops))(*[b.sf_gemv_op(w.desc(), p, self.y[li][gi][i].data_ptr(), None)
+                                                   for i, (w, p) in enumerate(ops)])
+                keep.append(arr)
+                calls.append((L.sf_refined_gemv, (arr, len(ops), C.c_void_p(self.x[li][gi].data_ptr()), self.batch,
+                                                  ks, None, None, self.cache.handle, self.ws.handle, None), tag))
+                if tag == "qkv":
+                    dsc = kv.desc(T)
+                    keep.append(dsc)
+                    kt = k_select(self.tok_pct, T) if refined else 0
+                    calls.append((L.sf_refined_attn_decode,
+                                  (C.c_void_p(self.q[li].data_ptr()), S.n_q, C.byref(dsc), 1.0 / math.sqrt(HD), kt,
+                                   None, self.cache.handle, kv_pool, C.c_void_p(self.out[li].data_ptr()), None, None,
+                                   self.ws.handle, None), "attn"))
+        return calls, keep
+
+    def enqueue(self, calls, stream, timer=None):
+        s = C.c_void_p(stream.cuda_stream)
+        for fn, args, tag in calls:
+            a = list(args)
+            a[-1] = s
+            ev = timer(tag) if timer is not None else None
+            if ev is not None:
+                ev[0].record(stream)
+            st = fn(*a)
+            if ev is not None:
+                ev[1].record(stream)
+            if st != 0:
+                self.binding.check(st)
+
+
+def copy_calibration():
+    """A plain device copy of known size (256 MiB read + 256 MiB written): its HBM
+    counters scale those of the other kernels."""
     import torch
 
-    from bit_decode_selective_amd import binding, decode
+    src_t = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst_t = torch.empty_like(src_t)
+    for _ in range(3):
+        torch.neg(src_t, out=dst_t)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: 3 x torch.neg over {COPY_CALIBRATION_BYTES} bytes", file=sys.stderr, flush=True)
 
-    if args.copy_calibration:
-        src_t = torch.ones(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst_t = torch.empty_like(src_t)
-        for _ in range(3):
-            torch.neg(src_t, out=dst_t)
-        torch.cuda.synchronize()
-        print(f"# copy calibration: 3 x torch.neg over {COPY_CALIBRATION_BYTES} bytes", file=sys.stderr, flush=True)
-        del src_t, dst_t
-    T, B = args.context, args.batch
-    base = decode.LLAMA31_8B
-    spec = decode.Spec(base.name, args.layers, base.hidden, base.n_q, base.n_kv, base.ffn, base.vocab, base.qk_norm,
-                       base.theta, base.eps)
-    t0 = time.time()
-    src = decode.DeviceWeights(1234, "cuda")
-    model = decode.DecodeModel(spec, B, T, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
-                               head=False, producer_select=args.producer_select)
-    model.fill_kv(T - 1, src)
-    pos = T - 1
-    g = torch.Generator(device="cuda")
-    g.manual_seed(99)
-    h0 = torch.randn((B, spec.hidden), generator=g, device="cuda", dtype=torch.float32)
-    print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
-    stream = torch.cuda.Stream()
-    reset = lambda: model.h.copy_(h0)  # the step's input state (in place of the embedding)
-    calls, keep = model.build_step(pos, refined=True)
-    calls0, keep0 = model.build_step(pos, refined=False)
-    torch.cuda.synchronize()
+
+def measure(torch, model, calls, calls0, stream, args, before=None):
+    """Graph-replayed step times (refined, unrefined) and per-call eager timings."""
+    from bit_decode_selective_amd import binding
+
     with torch.cuda.stream(stream):  # first launches outside capture
-        reset()
-        model.enqueue(calls, stream)
-        reset()
-        model.enqueue(calls0, stream)
+        for c in (calls, calls0):
+            if before is not None:
+                before()
+            model.enqueue(c, stream)
     torch.cuda.synchronize()
-    graph = capture(torch, model, calls, stream, reset)
+    graph = capture(torch, model, calls, stream, before)
     ms = time_replays(torch, graph, stream, args.steps, args.warmup)
     print(f"# refined step {ms:.3f} ms", file=sys.stderr, flush=True)
     ws = binding.workspace(0, model.dev)
     ws.check()  # raises if a bounded device wait gave up during the timed steps
     unref_ms = None
     if not args.no_unrefined:
-        graph0 = capture(torch, model, calls0, stream, reset)
+        graph0 = capture(torch, model, calls0, stream, before)
         unref_ms = time_replays(torch, graph0, stream, args.steps, args.warmup)
         print(f"# unrefined step {unref_ms:.3f} ms", file=sys.stderr, flush=True)
-    us = per_call(torch, model, calls, stream, 3, reset)
+    us = per_call(torch, model, calls, stream, 3, before)
     ws.check()
+    return ms, unref_ms, us
+
+
+def report(model, calls, T, B, args, ms, unref_ms, us, workload, extra_config):
     table = call_table(model, calls, T, True, us)
     dom = max(table, key=lambda t: table[t]["avg_us"] * table[t]["per_step"])
     sb = step_bytes(model, calls, T, True)
@@ -338,22 +447,10 @@ def layer_step(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16 x int2 -> fp32",
-        "data": "synthetic (seeded random weights/KV/residual state of the model shapes; no trained weights)",
-        "config": {
-            "workload": (f"Llama-3.1-8B-shape refined decode step, batch {B}: {args.layers} decoder layers x (RMSNorm "
-                         f"selecting channels, q/k/v GEMV, RoPE, KV append, GQA attention 32q/8kv d128 T={T}, o GEMV, "
-                         f"RMSNorm, gate/up GEMV, SwiGLU, down GEMV); weights and KV 2+2-bit, top 3% channels / 2% "
-                         f"tokens refined"),
-            "layers": args.layers,
-            "batch": B,
-            "context": T,
-            "weight_bits": "2+2",
-            "kv_bits": "2+2",
-            "refine_channels_pct": 3,
-            "refine_tokens_pct": 2,
-            "refinement_pools": "all units resident on the device",
-            "hip_graph": True,
-        },
+        "data": "synthetic (seeded random weights, KV and activations of the model shapes; no trained weights)",
+        "config": dict({"workload": workload, "layers": args.layers, "batch": B, "context": T,
+                        "weight_bits": "2+2", "kv_bits": "2+2", "refine_channels_pct": 3, "refine_tokens_pct": 2,
+                        "refinement_pools": "all units resident on the device", "hip_graph": True}, **extra_config),
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": sb,
@@ -378,6 +475,65 @@ def layer_step(args):
         asb = sum(call_bytes(model, t, T, True) for _, _, t in calls if t == "attn")
         res["cpu_baseline"] = cpu_baseline(T, 3, 2, 2, 2, gsb, asb, B)
     print(json.dumps(res), flush=True)
+
+
+def synthetic_step(args):
+    """The default workload (see SyntheticStep)."""
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+    T, B = args.context, args.batch
+    t0 = time.time()
+    model = SyntheticStep(args.layers, T, B)
+    print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    calls, keep = model.build_step(refined=True)
+    calls0, keep0 = model.build_step(refined=False)
+    torch.cuda.synchronize()
+    ms, unref_ms, us = measure(torch, model, calls, calls0, stream, args)
+    workload = (f"Llama-3.1-8B-shape refined decode step, batch {B}: {args.layers} layers x (KV append, q/k/v GEMV, "
+                f"GQA attention 32q/8kv d128 T={T}, o GEMV, gate/up GEMV, down GEMV) with synthetic GEMV inputs "
+                f"(N(0,1), 1% of channels x20) and queries; weights and KV 2+2-bit, top 3% channels / 2% tokens "
+                f"refined")
+    report(model, calls, T, B, args, ms, unref_ms, us, workload, {"channel_selection": "in each GEMV launch"})
+
+
+def layer_chain(args):
+    """Whole decoder layers of a Llama-3.1-8B-shaped model, each GEMV input produced
+    by the layer before it (RMSNorm, RoPE, SwiGLU and casts included)."""
+    import torch
+
+    from bit_decode_selective_amd import decode
+
+    if args.copy_calibration:
+        copy_calibration()
+    T, B = args.context, args.batch
+    base = decode.LLAMA31_8B
+    spec = decode.Spec(base.name, args.layers, base.hidden, base.n_q, base.n_kv, base.ffn, base.vocab, base.qk_norm,
+                       base.theta, base.eps)
+    t0 = time.time()
+    src = decode.DeviceWeights(1234, "cuda")
+    model = decode.DecodeModel(spec, B, T, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
+                               head=False, producer_select=args.producer_select)
+    model.fill_kv(T - 1, src)
+    pos = T - 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    h0 = torch.randn((B, spec.hidden), generator=g, device="cuda", dtype=torch.float32)
+    print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    reset = lambda: model.h.copy_(h0)  # the step's input state (in place of the embedding)
+    calls, keep = model.build_step(pos, refined=True)
+    calls0, keep0 = model.build_step(pos, refined=False)
+    torch.cuda.synchronize()
+    ms, unref_ms, us = measure(torch, model, calls, calls0, stream, args, reset)
+    sel = "by the kernel that produces each GEMV input" if args.producer_select else "in each GEMV launch"
+    workload = (f"Llama-3.1-8B-shape refined decoder layers, batch {B}: {args.layers} layers x (RMSNorm, q/k/v GEMV, "
+                f"RoPE, KV append, GQA attention 32q/8kv d128 T={T}, fp16 cast, o GEMV, RMSNorm, gate/up GEMV, "
+                f"SwiGLU, down GEMV) from a synthetic residual state; weights and KV 2+2-bit, top 3% channels / 2% "
+                f"tokens refined")
+    report(model, calls, T, B, args, ms, unref_ms, us, workload, {"channel_selection": sel})
 
 
 def decode_workload(args):
@@ -481,9 +637,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unrefined", action="store_true")
     ap.add_argument("--workload", default="llama8b-step",
-                    choices=["llama8b-step", "qwen3-8b-decode", "llama8b-128k-decode"],
-                    help="llama8b-step (default): the decoder layers of a Llama-3.1-8B-shaped step; the others run "
-                         "full decode steps with embedding, lm_head and LRU refinement pools")
+                    choices=["llama8b-step", "llama8b-layers", "qwen3-8b-decode", "llama8b-128k-decode"],
+                    help="llama8b-step (default): the GEMVs and attention of a Llama-3.1-8B-shaped step with "
+                         "synthetic inputs; llama8b-layers: whole decoder layers chained through RMSNorm, RoPE and "
+                         "SwiGLU; the others run full decode steps with embedding, lm_head and LRU refinement pools")
     ap.add_argument("--producer-select", action="store_true",
                     help="the kernels that form each GEMV input also select its channels (else each GEMV selects)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -494,14 +651,17 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the refined decode path runs on "
               "a single device; DESIGN.md describes how it would shard)", file=sys.stderr)
         sys.exit(2)
-    if args.workload != "llama8b-step":
-        if args.layers == 32:
-            args.layers = 0  # the model's own depth
-        if args.context == 32768:
-            args.context = 0  # the workload's own context
-        decode_workload(args)
+    if args.workload == "llama8b-step":
+        synthetic_step(args)
         return
-    layer_step(args)
+    if args.workload == "llama8b-layers":
+        layer_chain(args)
+        return
+    if args.layers == 32:
+        args.layers = 0  # the model's own depth
+    if args.context == 32768:
+        args.context = 0  # the workload's own context
+    decode_workload(args)
 
 
 if __name__ == "__main__":

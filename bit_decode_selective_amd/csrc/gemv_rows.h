@@ -255,6 +255,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// One count into a per-wave LDS histogram.  The active lanes whose bin equals the
+// first active lane's bin are added by one lane with their number: a whole wave
+// adding to one address (all-equal keys, as an all-zero input gives) would
+// otherwise serialise on it.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
+  const bool same = bin == b0;
+  const uint64_t m = __ballot(same);
+  const bool leader = same && lanes_below(m) == 0;
+  if (!same || leader) atomicAdd(&h[bin], leader ? (uint32_t)__popcll(m) : 1u);
+}
+
 // Largest bin b of the sum of four per-wave histograms h[w][0..nbin) whose suffix
 // count (bins >= b) reaches `need`; *above = count in bins above b.  Every wave
 // computes it from the histograms itself.  nbin = 256 or 128.
@@ -525,8 +537,8 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
           *(u32x4*)(keys + 4 * m) = kv[i];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            atomicAdd(&whist[wave][(kv[i][q] & 0xFFFFu) >> 7], 1u);
-            atomicAdd(&whist[wave][kv[i][q] >> 23], 1u);
+            hist_add(whist[wave], (kv[i][q] & 0xFFFFu) >> 7);
+            hist_add(whist[wave], kv[i][q] >> 23);
           }
         }
       }
@@ -549,7 +561,7 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
           sure |= (uint32_t)(bin > b1) << e;
           if (bin == b1) {
             bnd |= 1u << e;
-            atomicAdd(&whist2[wave][key & 127u], 1u);
+            hist_add(whist2[wave], key & 127u);
           }
         }
         bs[m] = (uint8_t)sure;
@@ -895,8 +907,8 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
       if (computed && m < n8)  // selection pass 1: top 8 key bits, one histogram per wave
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          atomicAdd(&whist[wave][(kv[q] & 0xFFFFu) >> 7], 1u);
-          atomicAdd(&whist[wave][kv[q] >> 23], 1u);
+          hist_add(whist[wave], (kv[q] & 0xFFFFu) >> 7);
+          hist_add(whist[wave], kv[q] >> 23);
         }
     }
   };
@@ -938,7 +950,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
             sure |= (uint32_t)(bin > b1) << e;
             if (bin == b1) {
               bnd |= 1u << e;
-              atomicAdd(&whist2[wave][key & 127u], 1u);
+              hist_add(whist2[wave], key & 127u);
             }
           }
           bs[m] = (uint8_t)sure;

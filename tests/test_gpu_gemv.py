@@ -68,6 +68,22 @@ def test_selection_ties_go_to_lower_channel():
     assert_close(y, o_gemv.refined_gemv(q, x, [3, 7, 50]))
 
 
+@pytest.mark.parametrize("kind", list(KINDS))
+@pytest.mark.parametrize("fill", [0.0, 0.5])
+def test_all_equal_inputs_select_lowest_channels(kind, fill, monkeypatch):
+    """Every |x| equal (an all-zero input, or one constant): all keys tie, so the
+    selection is the lowest k_sel channels; 14336 input channels (the down
+    projection's width) at batch 1."""
+    monkeypatch.setenv("SF_GEMV_SPLIT", KINDS[kind])
+    W, qw, q = _setup(13, 256, 14336, 2, 2)
+    x = np.full((1, 14336), fill, dtype=np.float16)
+    x[0, 1::2] *= -1  # signs do not change the key
+    ks = selection.k_select(3, 14336)
+    (y,), sel, _ = _run([qw], x, ks)
+    assert sel == list(range(ks))
+    assert_close(y, o_gemv.refined_gemv(q, x, sel), what=f"constant |x| = {fill}")
+
+
 def test_fused_ops_and_external_selection():
     k_in = 1024
     qs = [_setup(13, n, k_in, 2, 2, tensor=i) for i, n in enumerate((256, 64, 64))]
