@@ -556,8 +556,13 @@ def decode_workload(args):
                        spec.theta, spec.eps)
     t0 = time.time()
     src = decode.DeviceWeights(4321, "cuda")
+    store_dir = None
+    if args.store == "ssd":
+        import tempfile
+
+        store_dir = tempfile.mkdtemp(prefix="sf_refine_store_")
     model = decode.DecodeModel(spec, args.batch, T + 1, src, b=wb, r=wr, kv_b=kvb, kv_r=kvr, ch_pct=ch_pct,
-                               tok_pct=tok_pct, pool_frac=frac, cache_mode=mode)
+                               tok_pct=tok_pct, pool_frac=frac, cache_mode=mode, store_dir=store_dir)
     model.fill_kv(T, src)
     print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     calls, keep = model.build_step(T)
@@ -590,6 +595,7 @@ def decode_workload(args):
     ms_kernels = time_replays(torch, g, stream, args.steps, 0)
     binding.workspace(0, model.dev).check()
     d = {k: st1[k] - st0[k] for k in st1}
+    io = model.cache.io_stats()
     sb = step_bytes(model, calls, T + 1, True)
     secs = ms * 1e-3
     res = {
@@ -623,6 +629,14 @@ def decode_workload(args):
         "fill_bytes_per_step": d["h2d_bytes"] / args.steps,
         "units_installed_per_step": d["installed"] / args.steps,
     }
+    if store_dir is not None:
+        res["config"]["weight_refinement_store"] = "files (SSD tier), one per weight pool; KV units in pinned RAM"
+        res["ssd_reads"] = io
+        import shutil
+
+        shutil.rmtree(store_dir, ignore_errors=True)
+    else:
+        res["config"]["weight_refinement_store"] = "pinned host RAM"
     print(json.dumps(res), flush=True)
 
 
@@ -641,6 +655,8 @@ def main():
                     help="llama8b-step (default): the GEMVs and attention of a Llama-3.1-8B-shaped step with "
                          "synthetic inputs; llama8b-layers: whole decoder layers chained through RMSNorm, RoPE and "
                          "SwiGLU; the others run full decode steps with embedding, lm_head and LRU refinement pools")
+    ap.add_argument("--store", default="ram", choices=["ram", "ssd"],
+                    help="decode workloads: weight refinement stores in pinned host RAM or in files (SSD tier)")
     ap.add_argument("--producer-select", action="store_true",
                     help="the kernels that form each GEMV input also select its channels (else each GEMV selects)")
     ap.add_argument("--copy-calibration", action="store_true",

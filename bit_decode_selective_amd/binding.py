@@ -66,6 +66,8 @@ class sf_pool_desc(C.Structure):
         ("host_store", C.c_void_p),
         ("device_store", C.c_void_p),
         ("max_lookup", C.c_int32),
+        ("store_file", C.c_char_p),
+        ("store_offset", C.c_int64),
     ]
 
 
@@ -98,6 +100,8 @@ _PROTOS = {
     "sf_refine_cache_fill": (I32, [VP, VP, VP, C.POINTER(I64)]),
     "sf_refine_cache_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(I64), C.POINTER(I64)]),
     "sf_refine_cache_resident": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64)]),
+    "sf_refine_cache_io_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(C.c_double),
+                                       C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
     "sf_refined_gemv_noalloc": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
@@ -403,11 +407,38 @@ class RefineCache:
         check(lib().sf_refine_cache_stats(self.handle, pool, *[C.byref(x) for x in v]))
         return dict(zip(("lookups", "hits", "installed", "h2d_bytes"), [x.value for x in v]))
 
+    def io_stats(self, pool=-1):
+        """Reads of the pools with a store file: units, bytes, median / p99 read time
+        (us), wall time spent reading (ms)."""
+        n, by = C.c_int64(0), C.c_int64(0)
+        a, b, w = C.c_double(0), C.c_double(0), C.c_double(0)
+        check(lib().sf_refine_cache_io_stats(self.handle, pool, C.byref(n), C.byref(by), C.byref(a), C.byref(b),
+                                             C.byref(w)))
+        return {"reads": n.value, "bytes": by.value, "p50_us": a.value, "p99_us": b.value, "read_ms": w.value}
+
     def resident(self, pool, capacity):
         ids = (C.c_int64 * max(1, capacity))()
         n = C.c_int64(0)
         check(lib().sf_refine_cache_resident(self.handle, pool, ids, C.byref(n)))
         return set(ids[i] for i in range(n.value))
+
+
+def write_store_file(path, store):
+    """Writes a store tensor [n_units][unit_bytes] (any device) to `path`, unit u at
+    byte u * unit_bytes (plain bytes: the file a store-file pool reads)."""
+    arr = store.reshape(store.shape[0], -1).to("cpu").numpy()
+    with open(path, "wb") as f:
+        f.write(arr.tobytes())
+        f.flush()
+        os.fsync(f.fileno())
+
+
+def file_pool_desc(path, unit_bytes, n_units, capacity, max_lookup=0, offset=0):
+    """Pool whose units are read from a file (unit u at offset + u * unit_bytes)."""
+    d = sf_pool_desc(unit_bytes, n_units, capacity, None, None, max_lookup)
+    d.store_file = os.fsencode(path)
+    d.store_offset = offset
+    return d
 
 
 def host_pool_desc(host_store, capacity, max_lookup=0):

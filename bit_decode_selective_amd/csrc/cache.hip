@@ -23,10 +23,25 @@
 // the freed slots, and only after that copy has completed is the map kernel
 // enqueued on the compute stream.  Deterministic mode enqueues the map right away
 // behind a stream wait; async mode enqueues it at the next fill call.
+//
+// A pool whose store is a file (the SSD tier) has pinned staging of its own: the
+// fill reads each installed unit from the file into staging with a positioned
+// read (direct I/O where possible, up to 8 reads in flight), and the scatter
+// kernel copies from staging instead of from a host store.  The staging of one
+// fill is reused by the next only after that fill's copy has completed (the fill
+// waits for the compute stream, which waited for the copy, or for the copy itself).
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
 #include <algorithm>
+#include <cerrno>
+#include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <thread>
 
 #include "sf_internal.h"
 
@@ -41,8 +56,9 @@ struct LogTab {  // where a pool's lookup log sits in the log block
 struct PoolTab {  // what the fill kernels need of a pool
   int32_t* unit2slot;
   uint8_t* slots;
-  const uint8_t* store;  // the pinned host store, device view
+  const uint8_t* store;  // the pinned host store (or the file pool's staging), device view
   int64_t unit_bytes;
+  int64_t staged;        // 1: the unit of a map entry sits at staging position `pad`
 };
 
 struct UnmapEnt {
@@ -71,8 +87,23 @@ struct HostPool {
   int64_t bucket_entries = 0;                       // ids held by all buckets
   std::vector<int64_t> pending;
   std::vector<uint8_t> pending_flag;  // per unit
+  // store file (SSD tier)
+  int fd = -1;
+  bool direct = false;
+  uint8_t* h_fstage = nullptr;  // pinned staging [stage_units][unit_bytes]
+  const uint8_t* fstage_dev = nullptr;
+  std::vector<float> lat_us;    // ring of the last read times
+  size_t lat_next = 0;
+  int64_t io_reads = 0, io_bytes = 0;
+  double io_ms = 0.0;
   // stats
   int64_t n_lookups = 0, n_hits = 0, n_installed = 0, h2d_bytes = 0;
+};
+
+struct FileRead {
+  int32_t pool;
+  int32_t stage;
+  int64_t unit;
 };
 
 }  // namespace
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const PoolTab* tab, const 
   for (int e = blockIdx.x; e < n; e += gridDim.x) {
     const MapEnt m = ents[e];
     const PoolTab p = tab[m.pool];
-    const uint8_t* src = p.store + (int64_t)m.unit * p.unit_bytes;
+    const uint8_t* src = p.store + (int64_t)(p.staged ? m.pad : m.unit) * p.unit_bytes;
     uint8_t* dst = p.slots + (int64_t)m.slot * p.unit_bytes;
     if ((p.unit_bytes & 15) == 0 && (((uintptr_t)p.store | (uintptr_t)p.slots) & 15) == 0) {
       for (int64_t w = threadIdx.x; w < p.unit_bytes / 16; w += 256) ((uint4*)dst)[w] = ((const uint4*)src)[w];
@@ -201,6 +232,8 @@ void destroy_cache(sf_refine_cache* c) {
   for (auto& p : c->pools) {
     if (p.d_unit2slot) hipFree(p.d_unit2slot);
     if (p.d_slots && !p.resident) hipFree(p.d_slots);
+    if (p.h_fstage) hipHostFree(p.h_fstage);
+    if (p.fd >= 0) close(p.fd);
   }
   if (c->d_logs) hipFree(c->d_logs);
   if (c->h_logs) hipHostFree(c->h_logs);
@@ -252,6 +285,90 @@ void compact_buckets(HostPool& p) {
   p.bucket_entries = n;
 }
 
+// Reads n bytes at offset off of a store file into dst.  Direct I/O reads whole
+// 4 KiB blocks into an aligned bounce buffer (at least n + 8 KiB) and copies the
+// unit out of it.
+bool read_unit(int fd, bool direct, int64_t off, int64_t n, uint8_t* dst, uint8_t* bounce) {
+  if (!direct) {
+    int64_t done = 0;
+    while (done < n) {
+      const ssize_t g = pread(fd, dst + done, (size_t)(n - done), (off_t)(off + done));
+      if (g <= 0) {
+        if (g < 0 && errno == EINTR) continue;
+        return false;
+      }
+      done += g;
+    }
+    return true;
+  }
+  const int64_t a0 = off & ~(int64_t)4095, a1 = (off + n + 4095) & ~(int64_t)4095;
+  int64_t got = 0;
+  while (got < off + n - a0) {
+    const ssize_t g = pread(fd, bounce + got, (size_t)(a1 - a0 - got), (off_t)(a0 + got));
+    if (g <= 0) {
+      if (g < 0 && errno == EINTR) continue;
+      return false;
+    }
+    got += g;
+  }
+  std::memcpy(dst, bounce + (off - a0), (size_t)n);
+  return true;
+}
+
+// The file reads of one fill, up to 8 at a time; per-read times go to the pools'
+// rings.  False if a read failed.
+bool run_file_reads(sf_refine_cache* c, const std::vector<FileRead>& reads) {
+  if (reads.empty()) return true;
+  const auto t0 = std::chrono::steady_clock::now();
+  const int nt = (int)std::min<size_t>(8, reads.size());
+  std::vector<float> us(reads.size(), 0.f);
+  std::vector<uint8_t> ok(nt, 1);
+  int64_t max_unit = 0;
+  for (const FileRead& r : reads) max_unit = std::max(max_unit, c->pools[r.pool].d.unit_bytes);
+  const size_t bounce_bytes = (size_t)((max_unit + 8192 + 4095) & ~(int64_t)4095);
+  auto work = [&](int w) {
+    uint8_t* bounce = (uint8_t*)std::aligned_alloc(4096, bounce_bytes);
+    if (!bounce) {
+      ok[w] = 0;
+      return;
+    }
+    for (size_t i = (size_t)w; i < reads.size(); i += (size_t)nt) {
+      const FileRead& r = reads[i];
+      HostPool& p = c->pools[r.pool];
+      const int64_t ub = p.d.unit_bytes;
+      const auto a = std::chrono::steady_clock::now();
+      if (!read_unit(p.fd, p.direct, p.d.store_offset + r.unit * ub, ub, p.h_fstage + (int64_t)r.stage * ub,
+                     bounce)) {
+        ok[w] = 0;
+        break;
+      }
+      us[i] = std::chrono::duration<float, std::micro>(std::chrono::steady_clock::now() - a).count();
+    }
+    std::free(bounce);
+  };
+  if (nt == 1) {
+    work(0);
+  } else {
+    std::vector<std::thread> th;
+    for (int w = 0; w < nt; ++w) th.emplace_back(work, w);
+    for (auto& t : th) t.join();
+  }
+  const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  for (size_t i = 0; i < reads.size(); ++i) {
+    HostPool& p = c->pools[reads[i].pool];
+    if (p.lat_us.size() < 65536) {
+      p.lat_us.push_back(us[i]);
+    } else {
+      p.lat_us[p.lat_next] = us[i];
+      p.lat_next = (p.lat_next + 1) % p.lat_us.size();
+    }
+    ++p.io_reads;
+    p.io_bytes += p.d.unit_bytes;
+  }
+  for (const FileRead& r : reads) c->pools[r.pool].io_ms += ms / (double)reads.size();
+  return std::all_of(ok.begin(), ok.end(), [](uint8_t v) { return v != 0; });
+}
+
 sf_status publish(sf_refine_cache* c, hipStream_t compute) {
   if (!c->in_flight) return SF_OK;
   SF_HIP(hipStreamWaitEvent(compute, c->copy_done, 0));
@@ -300,9 +417,13 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
     SF_REQUIRE(d.capacity >= 0 && d.capacity <= d.n_units, SF_EINVAL, "capacity out of range");
     SF_REQUIRE(d.max_lookup >= 0, SF_EINVAL, "bad max_lookup");
     if (d.device_store)
-      SF_REQUIRE(d.capacity == d.n_units, SF_EINVAL, "a resident pool needs capacity == n_units");
+      SF_REQUIRE(d.capacity == d.n_units && !d.store_file, SF_EINVAL,
+                 "a resident pool needs capacity == n_units and no store file");
     else
-      SF_REQUIRE(d.host_store || d.capacity == 0, SF_EINVAL, "a pool with slots needs a host store");
+      SF_REQUIRE(d.host_store || d.store_file || d.capacity == 0, SF_EINVAL,
+                 "a pool with slots needs a host store or a store file");
+    SF_REQUIRE(!(d.store_file && d.host_store), SF_EINVAL, "give a host store or a store file, not both");
+    SF_REQUIRE(d.store_offset >= 0, SF_EINVAL, "bad store_offset");
   }
   sf_refine_cache* c = new sf_refine_cache();
   c->mode = mode;
@@ -360,7 +481,24 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
       for (int64_t u = 0; u < nu; ++u) p.unit_slot[u] = (int32_t)u;
     } else {
       hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((nu + 255) / 256)), dim3(256), 0, 0, p.d_unit2slot, nu, -1);
-      if (cap > 0) {
+      if (cap > 0 && p.d.store_file) {
+        CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
+        p.fd = open(p.d.store_file, O_RDONLY | O_DIRECT);
+        p.direct = p.fd >= 0;
+        if (p.fd < 0) p.fd = open(p.d.store_file, O_RDONLY);
+        struct stat stt {};
+        if (p.fd < 0 || fstat(p.fd, &stt) != 0 ||
+            (int64_t)stt.st_size < p.d.store_offset + p.d.n_units * p.d.unit_bytes) {
+          sf_set_error("sf_refine_cache_create: store file of pool " + std::to_string(i) +
+                       " cannot be opened or is shorter than its units");
+          destroy_cache(c);
+          return SF_EINVAL;
+        }
+        CK(hipHostMalloc((void**)&p.h_fstage, (size_t)std::max<int64_t>(1, p.stage_units) * p.d.unit_bytes,
+                         hipHostMallocDefault));
+        CK(hipHostGetDevicePointer((void**)&p.fstage_dev, p.h_fstage, 0));
+        p.store_dev = p.fstage_dev;
+      } else if (cap > 0) {
         CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
         // the fill kernels read the store directly: it must be pinned host memory
         hipPointerAttribute_t attr{};
@@ -380,7 +518,7 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
       for (int64_t s = 0; s < cap; ++s) p.free_slots[s] = (int32_t)(cap - 1 - s);
     }
     logtab[i] = LogTab{p.log_off, p.log_cap, 0};
-    pooltab[i] = PoolTab{p.d_unit2slot, p.d_slots, p.store_dev, p.d.unit_bytes};
+    pooltab[i] = PoolTab{p.d_unit2slot, p.d_slots, p.store_dev, p.d.unit_bytes, p.fd >= 0 ? 1 : 0};
   }
   CK(hipMalloc((void**)&c->d_logtab, sizeof(LogTab) * n_pools));
   CK(hipMalloc((void**)&c->d_pooltab, sizeof(PoolTab) * n_pools));
@@ -444,6 +582,7 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
   MapEnt* mp = (MapEnt*)(c->h_stage + c->map_off);
   int32_t n_unmap = 0, n_map = 0;
   bool overflow = false;
+  std::vector<FileRead> file_reads;
   for (int i = 0; i < np; ++i) {
     HostPool& p = c->pools[i];
     if (p.resident) continue;
@@ -494,7 +633,8 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
       if (!now) now = &p.buckets[t];
       now->push_back(u);
       ++p.bucket_entries;
-      mp[n_map] = MapEnt{i, (int32_t)u, slot, 0};
+      mp[n_map] = MapEnt{i, (int32_t)u, slot, (int32_t)n_pool};
+      if (p.fd >= 0) file_reads.push_back(FileRead{i, (int32_t)n_pool, u});
       ++n_map;
       ++n_pool;
       ++p.n_installed;
@@ -502,6 +642,12 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     }
     p.pending.clear();
     compact_buckets(p);
+  }
+  // the SSD tier's units into the pools' staging (the previous fill's copy out of
+  // it has completed: see step 2 and the wait on `compute` in step 1)
+  if (!run_file_reads(c, file_reads)) {
+    sf_set_error(std::string("sf_refine_cache_fill: a store file read failed: ") + std::strerror(errno));
+    return SF_ESTATE;
   }
   if (n_map > 0) {
     // 4. entries and unmaps on the compute stream; the scatter (units read from the
@@ -555,6 +701,35 @@ extern "C" sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int
   if (hits) *hits = b;
   if (installed) *installed = d;
   if (h2d_bytes) *h2d_bytes = e;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_refine_cache_io_stats(sf_refine_cache* c, int32_t pool, int64_t* reads, int64_t* bytes,
+                                              double* p50_us, double* p99_us, double* read_ms) {
+  SF_REQUIRE(c, SF_EINVAL, "null cache");
+  SF_REQUIRE(pool < (int32_t)c->pools.size(), SF_EINVAL, "pool index out of range");
+  int64_t n = 0, by = 0;
+  double ms = 0.0;
+  std::vector<float> lat;
+  for (int i = 0; i < (int)c->pools.size(); ++i) {
+    if (pool >= 0 && i != pool) continue;
+    const HostPool& p = c->pools[i];
+    n += p.io_reads;
+    by += p.io_bytes;
+    ms += p.io_ms;
+    lat.insert(lat.end(), p.lat_us.begin(), p.lat_us.end());
+  }
+  double q50 = 0.0, q99 = 0.0;
+  if (!lat.empty()) {
+    std::sort(lat.begin(), lat.end());
+    q50 = lat[(lat.size() - 1) / 2];
+    q99 = lat[std::min(lat.size() - 1, (size_t)((double)(lat.size() - 1) * 0.99 + 0.5))];
+  }
+  if (reads) *reads = n;
+  if (bytes) *bytes = by;
+  if (p50_us) *p50_us = q50;
+  if (p99_us) *p99_us = q99;
+  if (read_ms) *read_ms = ms;
   return SF_OK;
 }
 

@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes as C
 import math
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -112,7 +113,8 @@ class DecodeModel:
     """
 
     def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
-                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True):
+                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True,
+                 store_dir=None):
         import torch
 
         self.torch, self.spec, self.batch, self.t_cap = torch, spec, batch, t_cap
@@ -126,7 +128,7 @@ class DecodeModel:
         self.host = {}  # fp32 weights kept for the oracle checks (HostWeights only)
         keep_host = isinstance(src, HostWeights)
         pools = []
-        stores = []
+        stores = {}  # pool index -> pinned host store
 
         def quant(layer, tensor, n, k):
             W = src.matrix(layer, tensor, n, k)
@@ -135,13 +137,21 @@ class DecodeModel:
             qw = binding.QuantWeight.from_host(W, b, r) if keep_host else binding.QuantWeight.from_device(W, b, r)
             return qw
 
-        def add_pool(unit_bytes_obj, n_lookup):
-            """n_lookup: unit ids one step looks up in the pool (sizes its lookup log)."""
+        def add_pool(unit_bytes_obj, n_lookup, static=True):
+            """n_lookup: unit ids one step looks up in the pool (sizes its lookup log).
+            With store_dir, a static pool (a weight matrix) reads its units from a
+            file there (the SSD tier); KV units change every step and stay in RAM."""
             if pool_frac is None:
                 pools.append(unit_bytes_obj.resident_pool_desc())
+            elif store_dir is not None and static:
+                path = os.path.join(store_dir, f"refine_pool{len(pools)}.bin")
+                binding.write_store_file(path, unit_bytes_obj.refine)
+                n = unit_bytes_obj.refine.shape[0]
+                pools.append(binding.file_pool_desc(path, unit_bytes_obj.unit_bytes, n, max(0, int(pool_frac * n)),
+                                                    max_lookup=n_lookup))
             else:
                 st = unit_bytes_obj.host_store()
-                stores.append(st)
+                stores[len(pools)] = st
                 cap = max(0, int(pool_frac * st.shape[0]))
                 pools.append(binding.host_pool_desc(st, cap, max_lookup=n_lookup))
             return len(pools) - 1
@@ -169,7 +179,7 @@ class DecodeModel:
             L["kv"] = kv
             if kv_r > 0:
                 # store taken before any token: refilled from the device copy in fill_kv
-                L["pool_kv"] = add_pool(kv, batch * S.n_kv * k_select(tok_pct, t_cap))
+                L["pool_kv"] = add_pool(kv, batch * S.n_kv * k_select(tok_pct, t_cap), static=False)
             self.layers.append(L)
             torch.cuda.synchronize()
         self.final_norm = torch.as_tensor(src.gain(S.layers, FINAL_NORM, H), device=dev)
@@ -183,7 +193,7 @@ class DecodeModel:
             self.pool_lm = add_pool(self.lm_head, k_select(ch_pct, H)) if r > 0 else -1
         self._pool_frac = pool_frac
         self._pools, self._stores = pools, stores
-        self.cache = binding.RefineCache(pools, mode=cache_mode, device=dev, keep=stores) if pools else None
+        self.cache = binding.RefineCache(pools, mode=cache_mode, device=dev, keep=list(stores.values())) if pools else None
         self.side = torch.cuda.Stream(device=dev)
         self._alloc_buffers()
         self.pos = 0

@@ -162,7 +162,16 @@ sf_status sf_kv_append(const float* k_new, const float* v_new, int32_t n_tok, in
  * if a pool with slots has a store that is not pinned.
  * If device_store is non-NULL, the pool is a resident pool: capacity must equal
  * n_units, device_store [n_units][unit_bytes] (caller device memory) already
- * holds every unit, unit u lives in slot u, and the pool never misses. */
+ * holds every unit, unit u lives in slot u, and the pool never misses.
+ * SSD tier (rag-lover.com StrataFlux summary, TL;DR and limitations section: the
+ * extra precision may also sit on an SSD, whose 2 KB random reads are slow; paper
+ * abstract, arXiv 2611.08363: host RAM and solid-state drives): if store_file is
+ * non-NULL (and host_store NULL), the units are read from that file instead, unit
+ * u at byte store_offset + u * unit_bytes.  A fill reads each unit it installs
+ * with its own positioned read (direct I/O, bypassing the page cache, where the
+ * file system allows it; up to 8 reads in flight) into pinned staging the cache
+ * owns, then copies staging to slots as for a host store.  The file must hold
+ * every unit when the cache is created and must not change while it exists. */
 typedef struct {
   int64_t unit_bytes; /* multiple of 4 */
   int64_t n_units;
@@ -170,6 +179,8 @@ typedef struct {
   const uint8_t* host_store;
   uint8_t* device_store;
   int32_t max_lookup; /* most unit ids one step looks up in this pool */
+  const char* store_file; /* NULL: the store is host_store (or device_store) */
+  int64_t store_offset;
 } sf_pool_desc;
 
 #define SF_CACHE_DETERMINISTIC 0 /* fill completes before the next step's lookups */
@@ -207,6 +218,13 @@ sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream 
  * copied host-to-device; per pool if pool >= 0, all pools if pool < 0. */
 sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int64_t* lookups,
                                 int64_t* hits, int64_t* installed, int64_t* h2d_bytes);
+
+/* Reads of a pool with a store file (pool < 0: all such pools) since creation:
+ * units read, bytes read, the median and 99th percentile of one unit's read time
+ * (microseconds, over the last 65536 reads), and the wall time fills spent
+ * reading (milliseconds).  All zero if no pool reads from a file. */
+sf_status sf_refine_cache_io_stats(sf_refine_cache* c, int32_t pool, int64_t* reads, int64_t* bytes,
+                                   double* p50_us, double* p99_us, double* read_ms);
 
 /* Test helper: writes the resident unit ids of `pool` (ascending) to ids (host,
  * room for capacity entries) and their count to *n. */

@@ -62,6 +62,81 @@ def test_gemv_lru_over_steps(capacity, max_fill, given):
     assert st["h2d_bytes"] == st["installed"] * qw.unit_bytes
 
 
+@pytest.mark.parametrize("mode", [binding.SF_CACHE_DETERMINISTIC, binding.SF_CACHE_ASYNC])
+def test_ssd_tier_matches_host_store(tmp_path, mode):
+    """The same weight pool served from a store file (read per unit, direct I/O where
+    the file system allows) and from pinned host memory: identical hit sets, resident
+    sets and outputs (bit for bit) every step; deterministic mode also against the
+    oracle LRU; every installed unit read from the file once."""
+    k_in, n_out, ks, capacity = 512, 256, 16, 24
+    qw, q = _weight(64, n_out, k_in, 2, 2)
+    store = qw.host_store()
+    path = str(tmp_path / "units.bin")
+    binding.write_store_file(path, store)
+    c_ram = binding.RefineCache([binding.host_pool_desc(store, capacity)], mode=mode, keep=[store])
+    c_ssd = binding.RefineCache([binding.file_pool_desc(path, qw.unit_bytes, k_in, capacity)], mode=mode)
+    pool = o_cache.LRUPool(capacity)
+    for t in range(8):
+        x = _step_x(64 + t % 3, t, k_in)
+        outs = []
+        for c in (c_ram, c_ssd):
+            (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, ks, cache=c)
+            torch.cuda.synchronize()
+            outs.append((y.cpu().numpy(), sel.cpu().numpy().tolist(), (hit.cpu().numpy() >= 0).tolist()))
+        assert outs[0][1] == outs[1][1] and outs[0][2] == outs[1][2], t
+        assert np.array_equal(outs[0][0], outs[1][0]), t
+        sel, hits = outs[1][1], outs[1][2]
+        if mode == binding.SF_CACHE_DETERMINISTIC:
+            assert hits == pool.lookup(sel, t), t
+        assert_close(outs[1][0], o_gemv.refined_gemv(q, x, [k for k, h in zip(sel, hits) if h]), what=f"step {t}")
+        c_ram.fill()
+        c_ssd.fill()
+        if mode == binding.SF_CACHE_DETERMINISTIC:
+            pool.fill(t)
+            assert c_ssd.resident(0, capacity) == pool.resident(), t
+    torch.cuda.synchronize()
+    io = c_ssd.io_stats(0)
+    st = c_ssd.stats(0)
+    assert io["reads"] == st["installed"] > 0
+    assert io["bytes"] == st["installed"] * qw.unit_bytes
+    assert io["p99_us"] >= io["p50_us"] > 0
+    assert c_ram.io_stats()["reads"] == 0
+
+
+def test_ssd_tier_kv_pool(tmp_path):
+    """KV refinement units (64 bytes each, far below a disk block) from a store file
+    at an offset: hit sets against the oracle LRU and outputs against the oracle."""
+    batch, n_kv, G, T, b, r, ks = 1, 2, 4, 600, 2, 2, 12
+    K, V = inputs.kv(65, 0, batch, n_kv, T, 128)
+    kv = binding.QuantKV.from_host(K, V, b, r)
+    qk, qv = o_attn.quantize_kv(K, b, r), o_attn.quantize_kv(V, b, r)
+    store = kv.host_store()
+    path = str(tmp_path / "kv_units.bin")
+    with open(path, "wb") as f:
+        f.write(b"\x5a" * 1000)  # the units start at byte 1000
+    with open(path, "ab") as f:
+        f.write(store.numpy().tobytes())
+    capacity = 20
+    cache = binding.RefineCache([binding.file_pool_desc(path, kv.unit_bytes, kv.n_units, capacity, offset=1000)])
+    pool = o_cache.LRUPool(capacity)
+    scale = 1.0 / math.sqrt(128)
+    for t in range(6):
+        q = inputs.query(65, 0, t // 2, batch, n_kv * G, 128)
+        out, sel, hit = binding.refined_attention(q, kv, scale, ks, cache=cache)
+        torch.cuda.synchronize()
+        out, sel, hit = out.cpu().numpy(), sel.cpu().numpy(), hit.cpu().numpy()
+        units = [(bi * n_kv + g) * kv.t_cap + int(tok) for bi in range(batch) for g in range(n_kv) for tok in sel[bi, g]]
+        assert (hit.reshape(-1) >= 0).tolist() == pool.lookup(units, t), t
+        hits = {(bi, g): {int(tok) for tok, h in zip(sel[bi, g], hit[bi, g]) if h >= 0}
+                for bi in range(batch) for g in range(n_kv)}
+        sel_map = {(bi, g): sel[bi, g].tolist() for bi in range(batch) for g in range(n_kv)}
+        ref, _ = o_attn.refined_attention(q, qk, qv, (batch, n_kv, T, 128), scale, ks, sel_in=sel_map, hits=hits)
+        assert_close(out, ref, what=f"attention step {t}")
+        cache.fill()
+        pool.fill(t)
+        assert cache.resident(0, capacity) == pool.resident(), t
+
+
 def test_gemv_fused_ops_have_their_own_pools():
     k_in, ks = 512, 20
     (qa, qa_o), (qb, qb_o) = _weight(61, 256, k_in, 2, 2, 0), _weight(61, 96, k_in, 2, 2, 1)
