@@ -36,3 +36,25 @@ def refined_gemv(q, x_f16, refined_channels):
         x = x[None, :]
     w = effective_weight(q, refined_channels)
     return x @ w.T
+
+
+def lag_delta(q, x_f16, late_channels):
+    """Fetch lag: the contribution of refinements that arrive after their GEMV.
+
+    rag-lover.com StrataFlux summary, explainer dialogue (解説), fetch lead / fetch
+    lag passage: the addition of a refinement to the output may be delayed until a
+    later update, so that its transfer overlaps computation.  Reading: for the
+    channels in ``late_channels`` (selected, missing when the GEMV ran, fetched
+    afterwards) the output misses x_k * (full - resident)[n][k]; that amount is
+    added at a later update of the same output.  Returns it, fp64 [batch][N]:
+      delta[b][n] = sum_{k in late} x[b][k] * (Wfull[n][k] - Wres[n][k]).
+    """
+    x = np.asarray(x_f16, dtype=np.float16).astype(np.float64)
+    if x.ndim == 1:
+        x = x[None, :]
+    late = np.asarray(sorted(set(int(k) for k in late_channels)), dtype=np.int64)
+    n_out = q["codes"].shape[0]
+    if late.size == 0:
+        return np.zeros((x.shape[0], n_out))
+    d = nested.dequant_full(q)[:, late] - nested.dequant_resident(q)[:, late]
+    return x[:, late] @ d.T

@@ -110,3 +110,33 @@ def test_gemv_additive_over_disjoint_sets():
     s = np.repeat(q["scale"].astype(np.float64), 128, axis=1)
     d = gemv.refined_gemv(q, x, [130]) - y0
     np.testing.assert_allclose(d, x.astype(np.float64)[:, [130]] * (s[:, 130] * lo[:, 130])[None, :], atol=1e-13)
+
+
+def test_lag_delta_worked_example(golden):
+    """Channel 1 selected but late: the worked row's output is y_none at the GEMV
+    and y_k1 once the late contribution (x_1 * s * c_lo = 2 * 0.0625 * 3) is added."""
+    ex = golden["nested_2bit"]
+    gx = golden["gemv_row"]
+    q = nested.quantize(np.array([ex["x"]], dtype=np.float32), ex["b"], ex["r"], ex["group"])
+    x = np.array([gx["x"]], dtype=np.float16)
+    d = gemv.lag_delta(q, x, [1])
+    assert d[0, 0] == 0.375
+    assert gemv.refined_gemv(q, x, [])[0, 0] + d[0, 0] == gx["y_k1"]
+    assert gemv.lag_delta(q, x, [])[0, 0] == 0.0
+
+
+def test_lag_delta_completes_the_refined_output():
+    """GEMV on the hits E plus the late contribution of L equals the GEMV refined on
+    E and L together (disjoint sets), element by element against a written-out sum."""
+    q, x = _quantized(5, 20, 384)
+    hits, late = [3, 40, 200], [7, 129, 383]
+    d = gemv.lag_delta(q, x, late)
+    np.testing.assert_allclose(gemv.refined_gemv(q, x, hits) + d, gemv.refined_gemv(q, x, hits + late), rtol=0,
+                               atol=1e-12)
+    _, lo = nested.split(q)
+    s = q["scale"].astype(np.float64)
+    xf = x.astype(np.float64)
+    for bi in range(2):
+        for n in range(20):
+            want = sum(xf[bi, k] * s[n, k // 128] * lo[n, k] for k in late)
+            assert d[bi, n] == pytest.approx(want, rel=1e-12, abs=1e-15)
