@@ -191,7 +191,8 @@ def call_table(model, calls, T, refined, us):
     HBM peak, and the tag's share of the step's summed call time."""
     count = {}
     for _, _, tag in calls:
-        count[tag] = count.get(tag, 0) + 1
+        if tag in us:  # stream-ordering steps are not timed
+            count[tag] = count.get(tag, 0) + 1
     total = sum(np.mean(us[t]) * count[t] for t in count)
     out = {}
     for t in count:
@@ -562,7 +563,8 @@ def decode_workload(args):
 
         store_dir = tempfile.mkdtemp(prefix="sf_refine_store_")
     model = decode.DecodeModel(spec, args.batch, T + 1, src, b=wb, r=wr, kv_b=kvb, kv_r=kvr, ch_pct=ch_pct,
-                               tok_pct=tok_pct, pool_frac=frac, cache_mode=mode, store_dir=store_dir)
+                               tok_pct=tok_pct, pool_frac=frac, cache_mode=mode, store_dir=store_dir,
+                               fetch_lag=args.fetch_lag)
     model.fill_kv(T, src)
     print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     calls, keep = model.build_step(T)
@@ -637,6 +639,7 @@ def decode_workload(args):
         shutil.rmtree(store_dir, ignore_errors=True)
     else:
         res["config"]["weight_refinement_store"] = "pinned host RAM"
+    res["config"]["fetch_lag"] = bool(model.fetch_lag)
     print(json.dumps(res), flush=True)
 
 
@@ -657,6 +660,9 @@ def main():
                          "SwiGLU; the others run full decode steps with embedding, lm_head and LRU refinement pools")
     ap.add_argument("--store", default="ram", choices=["ram", "ssd"],
                     help="decode workloads: weight refinement stores in pinned host RAM or in files (SSD tier)")
+    ap.add_argument("--fetch-lag", action="store_true",
+                    help="decode workloads: missed o / down refinements are fetched on the side stream and added at "
+                         "the residual stream's next update")
     ap.add_argument("--producer-select", action="store_true",
                     help="the kernels that form each GEMV input also select its channels (else each GEMV selects)")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -113,6 +113,8 @@ _PROTOS = {
     "sf_swiglu_select": (I32, [VP, VP, I32, I32, VP, I32, VP, VP]),
     "sf_to_f16_select": (I32, [VP, I32, I32, VP, I32, VP, VP]),
     "sf_to_f16": (I32, [VP, I64, VP, VP]),
+    "sf_residual_add": (I32, [VP, VP, I64, VP]),
+    "sf_refine_lag_delta": (I32, [VP, I32, C.POINTER(sf_qweight), VP, I32, I32, VP, VP, VP, VP]),
     "sf_argmax": (I32, [VP, I32, I64, VP, VP]),
 }
 EXPORTS = tuple(_PROTOS)
@@ -586,3 +588,25 @@ def to_f16_select(x, k_sel, out=None, sel=None, stream=None):
     sel = sel if sel is not None else torch.empty(max(1, k_sel), dtype=torch.int32, device=x.device)
     check(lib().sf_to_f16_select(_ptr(x), batch, n, _ptr(out), k_sel, _ptr(sel), _stream(stream)))
     return out, sel[:k_sel]
+
+
+def residual_add(h, d, stream=None):
+    """h += d in place (fp32 device tensors of equal size)."""
+    check(lib().sf_residual_add(_ptr(h), _ptr(d), h.numel(), _stream(stream)))
+    return h
+
+
+def refine_lag_delta(cache, pool, w, x, sel, hit, out=None, stream=None):
+    """Late contribution of the selected channels that missed (hit < 0) in a GEMV of
+    QuantWeight w on fp16 x [batch][k_in]: fp32 [batch][n_out]."""
+    torch = _torch()
+    dev = w.resident.device
+    xb = _f16_bits(x, dev)
+    if xb.dim() == 1:
+        xb = xb[None]
+    batch = xb.shape[0]
+    o = out if out is not None else torch.empty((batch, w.n_out), dtype=torch.float32, device=dev)
+    d = w.desc()
+    check(lib().sf_refine_lag_delta(cache.handle, pool, C.byref(d), _ptr(xb), batch, sel.numel(), _ptr(sel), _ptr(hit),
+                                    _ptr(o), _stream(stream)))
+    return o

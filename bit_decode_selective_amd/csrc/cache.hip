@@ -77,7 +77,8 @@ struct HostPool {
   int64_t log_off = 0;         // in the cache's log block
   int32_t log_cap = 0;
   int64_t stage_units = 0;     // most units one fill installs
-  const uint8_t* store_dev = nullptr;  // device view of d.host_store
+  const uint8_t* host_dev = nullptr;   // device view of d.host_store
+  const uint8_t* store_dev = nullptr;  // what the scatter reads: host store or file staging (device view)
   std::vector<int64_t> slot_unit;  // -1 free
   std::vector<int64_t> slot_last;
   std::vector<int32_t> unit_slot;  // host view (includes units whose copy is in flight)
@@ -498,19 +499,24 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
                          hipHostMallocDefault));
         CK(hipHostGetDevicePointer((void**)&p.fstage_dev, p.h_fstage, 0));
         p.store_dev = p.fstage_dev;
-      } else if (cap > 0) {
-        CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
-        // the fill kernels read the store directly: it must be pinned host memory
+      } else if (p.d.host_store) {
+        if (cap > 0) CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
+        // the fill and lag kernels read the store directly: it must be pinned host memory
         hipPointerAttribute_t attr{};
-        if (hipPointerGetAttributes(&attr, p.d.host_store) != hipSuccess || attr.type != hipMemoryTypeHost ||
-            attr.devicePointer == nullptr) {
-          (void)hipGetLastError();
+        const bool pinned = hipPointerGetAttributes(&attr, p.d.host_store) == hipSuccess &&
+                            attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr;
+        if (!pinned) (void)hipGetLastError();
+        if (!pinned && cap == 0) {
+          // a pool without slots never fills; only sf_refine_lag_delta would read it
+        } else if (!pinned) {
           sf_set_error("sf_refine_cache_create: host_store of pool " + std::to_string(i) +
                        " is not pinned host memory (hipHostMalloc / pin_memory)");
           destroy_cache(c);
           return SF_EINVAL;
+        } else {
+          p.store_dev = (const uint8_t*)attr.devicePointer;
+          p.host_dev = p.store_dev;
         }
-        p.store_dev = (const uint8_t*)attr.devicePointer;
       }
       p.slot_unit.assign(cap, -1);
       p.slot_last.assign(cap, -1);
@@ -701,6 +707,106 @@ extern "C" sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int
   if (hits) *hits = b;
   if (installed) *installed = d;
   if (h2d_bytes) *h2d_bytes = e;
+  return SF_OK;
+}
+
+namespace {
+
+// Fetch lag: delta[b][n] = sum over the selected channels k that missed of
+// x[b][k] * s[n][k/128] * c_lo[n][k], the refinement words read straight from the
+// pinned host store (channel-major units: unit k holds c_lo[0..N)[k], LSB first).
+// A thread per output row; the late channels are listed in LDS first (in selection
+// order) and their words requested LAG_U at a time.
+constexpr int LAG_T = 256, LAG_LIST = 2048, LAG_U = 8, LAG_MAXB = 16;
+
+__global__ __launch_bounds__(LAG_T) void lag_delta_kernel(const uint8_t* store, int64_t unit_bytes,
+                                                         const uint32_t* sz, int n_out, int k_in, int r,
+                                                         const uint16_t* x, int batch, int k_sel,
+                                                         const int32_t* sel, const int32_t* hit, float* delta) {
+  __shared__ int s_k[LAG_LIST];
+  __shared__ int s_n;
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x * LAG_T + tid;
+  const int ngr = k_in / 128;
+  float acc[LAG_MAXB];
+#pragma unroll
+  for (int b = 0; b < LAG_MAXB; ++b) acc[b] = 0.f;
+  for (int j0 = 0; j0 < k_sel; j0 += LAG_LIST) {
+    const int jn = min(LAG_LIST, k_sel - j0);
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    // late entries of this round, in selection order (one wave compacts by ballot)
+    if (tid < 64) {
+      int base = 0;
+      for (int j = tid; j - tid < jn; j += 64) {
+        const int kq = j < jn ? sel[j0 + j] : -1;
+        const bool late = j < jn && hit[j0 + j] < 0 && kq >= 0 && kq < k_in;
+        const uint64_t m = __ballot(late);
+        const int pos = base + __popcll(m & ((1ull << tid) - 1ull));
+        if (late) s_k[pos] = kq;
+        base += __popcll(m);
+      }
+      if (tid == 0) s_n = base;
+    }
+    __syncthreads();
+    const int nl = s_n;
+    for (int i0 = 0; i0 < nl; i0 += LAG_U) {
+      uint64_t wv[LAG_U];
+      float sv[LAG_U];
+      int kk[LAG_U];
+#pragma unroll
+      for (int u = 0; u < LAG_U; ++u) {
+        kk[u] = i0 + u < nl ? s_k[i0 + u] : -1;
+        wv[u] = 0;
+        sv[u] = 0.f;
+        if (kk[u] >= 0 && n < n_out) {
+          const uint32_t* uw = (const uint32_t*)(store + (int64_t)kk[u] * unit_bytes);
+          const int bit = n * r, wi = bit >> 5;
+          const int nw = (int)(unit_bytes / 4);
+          const uint32_t lo = uw[wi];
+          const uint32_t hi2 = wi + 1 < nw ? uw[wi + 1] : 0u;
+          wv[u] = (((uint64_t)hi2 << 32) | lo) >> (bit & 31);
+          sv[u] = sf_h2f(sz[(int64_t)n * ngr + kk[u] / 128] & 0xFFFFu);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < LAG_U; ++u) {
+        if (kk[u] < 0) break;
+        const float c = (float)(uint32_t)(wv[u] & ((1u << r) - 1u));
+        const float sc = sv[u] * c;
+#pragma unroll
+        for (int b = 0; b < LAG_MAXB; ++b)
+          if (b < batch) acc[b] = fmaf(sf_h2f(x[(int64_t)b * k_in + kk[u]]), sc, acc[b]);
+      }
+    }
+    __syncthreads();  // s_k is rewritten by the next round
+  }
+  if (n < n_out)
+#pragma unroll
+    for (int b = 0; b < LAG_MAXB; ++b)
+      if (b < batch) delta[(int64_t)b * n_out + n] = acc[b];
+}
+
+}  // namespace
+
+extern "C" sf_status sf_refine_lag_delta(sf_refine_cache* c, int32_t pool, const sf_qweight* w, const uint16_t* x_f16,
+                                         int32_t batch, int32_t k_sel, const int32_t* sel, const int32_t* hit,
+                                         float* delta_out, sf_stream stream) {
+  SF_REQUIRE(c && w && x_f16 && delta_out, SF_EINVAL, "null argument");
+  SF_REQUIRE(pool >= 0 && pool < (int32_t)c->pools.size(), SF_EINVAL, "pool index out of range");
+  SF_REQUIRE(batch >= 1 && batch <= LAG_MAXB, SF_EINVAL, "batch must be 1..16");
+  SF_REQUIRE(k_sel >= 0 && k_sel <= w->k_in && (k_sel == 0 || (sel && hit)), SF_EINVAL, "bad k_sel / sel / hit");
+  SF_REQUIRE(w->fmt.r >= 1 && w->fmt.group == 128 && w->k_in % 128 == 0 && w->n_out > 0, SF_EINVAL, "bad weight");
+  const HostPool& p = c->pools[pool];
+  SF_REQUIRE(p.d.n_units == w->k_in && p.d.unit_bytes == (int64_t)w->n_out * w->fmt.r / 8 &&
+                 ((int64_t)w->n_out * w->fmt.r) % 32 == 0,
+             SF_EINVAL, "the pool's units are not this weight's channel-major refinement units");
+  const uint8_t* store = p.resident ? p.d.device_store : (p.d.host_store ? p.host_dev : nullptr);
+  SF_REQUIRE(store, SF_EUNSUPPORTED, "fetch lag needs a pinned host-RAM (or resident) store, not a store file");
+  hipLaunchKernelGGL(lag_delta_kernel, dim3((unsigned)((w->n_out + LAG_T - 1) / LAG_T)), dim3(LAG_T), 0,
+                     (hipStream_t)stream, store, p.d.unit_bytes, w->sz, (int)w->n_out,
+                     (int)w->k_in, (int)w->fmt.r, x_f16, (int)batch, (int)k_sel, sel, hit, delta_out);
+  SF_LAUNCH_CHECK();
   return SF_OK;
 }
 

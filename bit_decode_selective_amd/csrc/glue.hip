@@ -157,6 +157,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* g, const float
   }
 }
 
+__global__ __launch_bounds__(256) void residual_add_kernel(float* h, const float* d, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) h[i] += d[i];
+}
+
 __global__ __launch_bounds__(256) void to_f16_kernel(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = f2h(x[i]);
 }
@@ -397,6 +401,13 @@ extern "C" sf_status sf_qk_rope(const float* q, const float* k, int32_t batch, i
 extern "C" sf_status sf_swiglu(const float* gate, const float* up, int64_t n, uint16_t* act_f16, sf_stream stream) {
   SF_REQUIRE(gate && up && act_f16 && n > 0, SF_EINVAL, "bad arguments");
   hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, gate, up, n, act_f16);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
+extern "C" sf_status sf_residual_add(float* h, const float* d, int64_t n, sf_stream stream) {
+  SF_REQUIRE(h && d && n > 0, SF_EINVAL, "bad arguments");
+  hipLaunchKernelGGL(residual_add_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, h, d, n);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }

@@ -110,16 +110,26 @@ class DecodeModel:
                (sf_add_rmsnorm_select, sf_to_f16_select, sf_swiglu_select) and the
                GEMV takes that selection as sel_in (batch <= 16); otherwise each GEMV
                selects its channels itself
+    store_dir  with pool_frac: weight pools read their units from files in this
+               directory (the SSD tier); KV pools stay in pinned host memory
+    fetch_lag  with pool_frac: the selected channels of the o and down projections
+               that missed are read from the host store on the side stream
+               (sf_refine_lag_delta) and their contribution is added to the
+               residual stream at its next update (the next layer's residual add,
+               or the final norm); the last layer's down has no later update
     """
 
     def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
                  cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True,
-                 store_dir=None):
+                 store_dir=None, fetch_lag=False):
         import torch
 
         self.torch, self.spec, self.batch, self.t_cap = torch, spec, batch, t_cap
         self.head = head
         self.producer_select = producer_select and batch <= 16
+        # fetch lag: the o and down projections' missed refinements are read on the
+        # side stream and added at the residual stream's next update
+        self.fetch_lag = bool(fetch_lag) and pool_frac is not None and r > 0 and store_dir is None
         self.b, self.r, self.kv_b, self.kv_r = b, r, kv_b, kv_r
         self.ch_pct, self.tok_pct = ch_pct, tok_pct
         dev = torch.device(device)
@@ -237,6 +247,8 @@ class DecodeModel:
                 "gate": torch.empty((B, S.ffn), **f32),
                 "up": torch.empty((B, S.ffn), **f32),
                 "act": torch.empty((B, S.ffn), **i16),
+                "lag_o": torch.zeros((B, S.hidden), **f32),
+                "lag_down": torch.zeros((B, S.hidden), **f32),
                 "down": torch.empty((B, S.hidden), **f32),
                 "sel_attn": torch.empty(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32, device=self.dev),
                 "sel_o": torch.empty(max(1, k_select(self.ch_pct, S.n_q * d)), dtype=torch.int32, device=self.dev),
@@ -310,11 +322,44 @@ class DecodeModel:
             else:
                 calls.append((Lb.sf_add_rmsnorm, [P(self.h), P(y), P(w), B, S.hidden, S.eps, P(x), None], tag))
 
+        torch_ = self.torch
+        pending = {}  # update -> late contribution waiting for it
+
+        def lag(li, name, x, sel):
+            """Side stream: the late contribution of this GEMV's missed channels; the
+            returned call adds it to h on the compute stream once it is done."""
+            L, bf = self.layers[li], self.buf[li]
+            ev_in, ev_out = torch_.cuda.Event(), torch_.cuda.Event()
+            dsc = L[name].desc()
+            out = bf["lag_" + name]
+            keep.extend([ev_in, ev_out, dsc])
+            args = (cache, L["pool_" + name], C.byref(dsc), P(x), B, ksel(L[name].k_in), P(sel),
+                    P(self.hits[(li, name)]), P(out), C.c_void_p(self.side.cuda_stream))
+
+            def launch(stream):
+                ev_in.record(stream)
+                self.side.wait_event(ev_in)
+                binding.check(Lb.sf_refine_lag_delta(*args))
+                ev_out.record(self.side)
+
+            def apply(stream):
+                stream.wait_event(ev_out)
+                binding.check(Lb.sf_residual_add(P(self.h), P(out), B * S.hidden, C.c_void_p(stream.cuda_stream)))
+
+            calls.append((launch, None, "lag"))
+            return apply
+
+        def late_into(update):
+            if update in pending:
+                calls.append((pending.pop(update), None, "lag_add"))
+
+        lag_on = self.fetch_lag and refined
         if self.head:
             calls.append((Lb.sf_embed, [P(self.embed), S.vocab, S.hidden, P(self.ids), B, P(self.h), None], "embed"))
         for li, L in enumerate(self.layers):
             bf = self.buf[li]
             prev = self.buf[li - 1]["down"] if li > 0 else None
+            late_into(("attn", li))
             norm(prev, L["attn_norm"], bf["x_attn"], bf["sel_attn"], S.hidden, "norm")
             gemv(("q", "k", "v"), L, bf["x_attn"], (bf["q"], bf["k"], bf["v"]), S.hidden, bf["sel_attn"], "qkv")
             calls.append((Lb.sf_qk_rope, [P(bf["q"]), P(bf["k"]), B, S.n_q, S.n_kv, P(L.get("q_norm")), P(L.get("k_norm")),
@@ -343,6 +388,10 @@ class DecodeModel:
             else:
                 calls.append((Lb.sf_to_f16, [P(bf["attn"]), B * S.n_q * d, P(bf["a16"]), None], "cast"))
             gemv(("o",), L, bf["a16"], (bf["o"],), S.n_q * d, bf["sel_o"], "o")
+            last = li == len(self.layers) - 1
+            if lag_on and (not last or self.head):  # o's next update: the next layer's, or the final norm
+                pending[("attn", li + 1)] = lag(li, "o", bf["a16"], bf["sel_o"])
+            late_into(("ffn", li))
             norm(bf["o"], L["ffn_norm"], bf["x_ffn"], bf["sel_ffn"], S.hidden, "norm")
             gemv(("gate", "up"), L, bf["x_ffn"], (bf["gate"], bf["up"]), S.hidden, bf["sel_ffn"], "gateup")
             if ps:
@@ -351,6 +400,9 @@ class DecodeModel:
             else:
                 calls.append((Lb.sf_swiglu, [P(bf["gate"]), P(bf["up"]), B * S.ffn, P(bf["act"]), None], "swiglu"))
             gemv(("down",), L, bf["act"], (bf["down"],), S.ffn, bf["sel_down"], "down")
+            if lag_on and not last:  # down's next update: the next layer's ffn residual add
+                pending[("ffn", li + 1)] = lag(li, "down", bf["act"], bf["sel_down"])
+        late_into(("attn", len(self.layers)))
         if self.head:
             norm(self.buf[-1]["down"], self.final_norm, self.x_final, self.sel_lm, S.hidden, "norm")
             gemv((self.lm_head,), {}, self.x_final, (self.logits,), S.hidden, self.sel_lm, "lm_head")
@@ -362,6 +414,9 @@ class DecodeModel:
         around each call when given."""
         s = C.c_void_p(stream.cuda_stream)
         for fn, args, tag in calls:
+            if args is None:  # stream-ordering step (events, side-stream work)
+                fn(stream)
+                continue
             a = list(args)
             a[-1] = s
             ev = timer(tag) if timer is not None else None

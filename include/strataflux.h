@@ -219,6 +219,22 @@ sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream 
 sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int64_t* lookups,
                                 int64_t* hits, int64_t* installed, int64_t* h2d_bytes);
 
+/* Fetch lag (rag-lover.com StrataFlux summary, explainer dialogue (解説), fetch lead /
+ * fetch lag passage: a refinement's addition to the output may wait for a later
+ * update, so that its transfer overlaps computation).  For a refined GEMV that
+ * ran with selection sel [k_sel] and per-channel slots hit [k_sel] (its sel_out
+ * and hit_out; -1 = missed), writes the contribution the missed channels would
+ * have made, delta_out[b][n] = sum over j with hit[j] < 0 of
+ * x[b][sel[j]] * s[n][sel[j]/128] * c_lo[n][sel[j]], fp32 [batch][n_out]
+ * (overwritten; zero if nothing missed).  The refinement bits are read straight
+ * from the pool's pinned host store over PCIe (a resident pool reads its device
+ * store); the pool's units must be w's channel-major refinement units.  Run it on
+ * a side stream and add delta_out into the output's next update (sf_residual_add)
+ * once it is done.  batch 1..16; a pool whose store is a file: SF_EUNSUPPORTED. */
+sf_status sf_refine_lag_delta(sf_refine_cache* c, int32_t pool, const sf_qweight* w, const uint16_t* x_f16,
+                              int32_t batch, int32_t k_sel, const int32_t* sel, const int32_t* hit,
+                              float* delta_out, sf_stream stream);
+
 /* Reads of a pool with a store file (pool < 0: all such pools) since creation:
  * units read, bytes read, the median and 99th percentile of one unit's read time
  * (microseconds, over the last 65536 reads), and the wall time fills spent
@@ -353,6 +369,10 @@ sf_status sf_swiglu(const float* gate, const float* up, int64_t n, uint16_t* act
 
 /* out_f16[i] = fp16(x[i]) (nearest even), n elements. */
 sf_status sf_to_f16(const float* x, int64_t n, uint16_t* out_f16, sf_stream stream);
+
+/* h[i] += d[i], n elements (a residual update with a late contribution, see
+ * sf_refine_lag_delta). */
+sf_status sf_residual_add(float* h, const float* d, int64_t n, sf_stream stream);
 
 /* ids[b] = index of the largest logits[b][:] ([batch][vocab] fp32), the lowest index
  * among equal maxima; NaN values are never chosen. */

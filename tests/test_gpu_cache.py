@@ -137,6 +137,46 @@ def test_ssd_tier_kv_pool(tmp_path):
         assert cache.resident(0, capacity) == pool.resident(), t
 
 
+@pytest.mark.parametrize("b,r,batch", [(2, 2, 1), (3, 1, 3), (1, 3, 2)])
+def test_lag_delta_completes_missed_refinements(b, r, batch):
+    """sf_refine_lag_delta after a GEMV whose pool holds 10 of the channels: the late
+    contribution of the channels that missed equals the oracle's, and the GEMV's
+    output plus it equals the oracle GEMV refined on the whole selection."""
+    k_in, n_out, ks, capacity = 640, 224, 40, 10
+    qw, q = _weight(66, n_out, k_in, b, r)
+    store = qw.host_store()
+    cache = binding.RefineCache([binding.host_pool_desc(store, capacity)], keep=[store])
+    x0 = inputs.activation(66, 0, 0, 0, batch, k_in)
+    binding.refined_gemv([(qw, 0)], x0, ks, cache=cache)
+    cache.fill()  # the first selection's top channels are now resident
+    x = inputs.activation(66, 0, 0, 1, batch, k_in)
+    (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, ks, cache=cache)
+    delta = binding.refine_lag_delta(cache, 0, qw, x, sel, hit)
+    torch.cuda.synchronize()
+    sel_l, hit_l = sel.cpu().numpy().tolist(), hit.cpu().numpy().tolist()
+    late = [k for k, h in zip(sel_l, hit_l) if h < 0]
+    assert 0 < len(late) < ks
+    assert_close(delta.cpu().numpy(), o_gemv.lag_delta(q, x, late), what="late contribution")
+    assert_close(y.cpu().numpy() + delta.cpu().numpy(), o_gemv.refined_gemv(q, x, sel_l), what="y + late")
+
+
+def test_lag_delta_edges():
+    """Nothing missed (a resident pool) gives 0; k_sel = 0 gives 0; a store file is
+    not supported; residual_add adds in place."""
+    qw, q = _weight(67, 256, 512, 2, 2)
+    cache = binding.RefineCache([qw.resident_pool_desc()])
+    x = inputs.activation(67, 0, 0, 0, 1, 512)
+    (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, 16, cache=cache)
+    d = binding.refine_lag_delta(cache, 0, qw, x, sel, hit)
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    d0 = binding.refine_lag_delta(cache, 0, qw, x, empty, empty)
+    torch.cuda.synchronize()
+    assert not d.abs().max().item() and not d0.abs().max().item()
+    h = torch.arange(256, dtype=torch.float32, device="cuda")
+    binding.residual_add(h, torch.full_like(h, 0.5))
+    assert torch.equal(h.cpu(), torch.arange(256, dtype=torch.float32) + 0.5)
+
+
 def test_gemv_fused_ops_have_their_own_pools():
     k_in, ks = 512, 20
     (qa, qa_o), (qb, qb_o) = _weight(61, 256, k_in, 2, 2, 0), _weight(61, 96, k_in, 2, 2, 1)

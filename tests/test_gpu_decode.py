@@ -142,7 +142,21 @@ TENSOR = {"q": inputs.Q_PROJ, "k": inputs.K_PROJ, "v": inputs.V_PROJ, "o": input
           "up": inputs.UP, "down": inputs.DOWN}
 
 
-def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None):
+def _lag_check(model, li, name, x16, quants, what):
+    """The late contribution the GPU computed for this GEMV (its lag buffer) against
+    the oracle's on the GEMV's own misses; returns the GPU's (fp64)."""
+    bf = model.buf[li]
+    k_in = model.layers[li][name].k_in
+    ks = decode.k_select(model.ch_pct, k_in)
+    sel = bf["sel_" + name].cpu().numpy()[:ks]
+    hit = model.hits[(li, name)].cpu().numpy()[:ks]
+    late = [int(k) for k, h in zip(sel, hit) if h < 0]
+    got = bf["lag_" + name].cpu().numpy().astype(np.float64)
+    assert_close(got, o_gemv.lag_delta(quants((li, name)), x16.astype(np.float16), late), what=f"{what} late {name}")
+    return got
+
+
+def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None, fetch_lag=False):
     """Teacher-forced decode steps; every operation of every step checked against the
     oracle on the GPU's own inputs.  With pool_frac, the LRU pools of every weight,
     KV cache and lm_head are replayed by the oracle (``cache.LRUPool``): each GEMV's
@@ -151,7 +165,8 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
     outputs are compared (all by default); selections and hit sets are checked at
     every step."""
     src = decode.HostWeights(cfg)
-    model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac)
+    model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac, fetch_lag=fetch_lag)
+    assert model.fetch_lag == fetch_lag
     for li in range(spec.layers):
         for name, t in TENSOR.items():
             model.host[(li, name)] = model.host[(li, t)]
@@ -173,8 +188,11 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
         binding.check_workspaces()
         # rebuild the residual stream in fp64 from the GPU's op outputs
         h = o_dec.embed(model.host["embed"], ids[step])
+        late_o = late_down = None  # the previous layer's late contributions (fetch lag)
         for li, L in enumerate(model.layers):
             bf = {k: v for k, v in model.buf[li].items()}
+            if late_o is not None:
+                h = h + late_o
             x = _f16(bf["x_attn"])
             assert_close(x, o_dec.to_f16(o_dec.rmsnorm(h, L["attn_norm"].cpu().numpy(), S.eps)).astype(np.float64),
                          what=f"layer {li} attn norm", **F16)
@@ -230,6 +248,10 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
             _gemv_check(model, li, ("o",), a16, [o], bf["sel_o"], S.n_q * d, f"step {step} layer {li} o", quants, lru,
                         step, outs)
             h = h + o.astype(np.float64)
+            if late_down is not None:
+                h = h + late_down
+            if fetch_lag:
+                late_o = _lag_check(model, li, "o", a16, quants, f"step {step} layer {li}")
             x2 = _f16(bf["x_ffn"])
             assert_close(x2, o_dec.to_f16(o_dec.rmsnorm(h, L["ffn_norm"].cpu().numpy(), S.eps)).astype(np.float64),
                          what=f"layer {li} ffn norm", **F16)
@@ -242,6 +264,10 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
             _gemv_check(model, li, ("down",), act, [dn], bf["sel_down"], S.ffn, f"step {step} layer {li} down", quants,
                         lru, step, outs)
             h = h + dn.astype(np.float64)
+            if fetch_lag and li < S.layers - 1:
+                late_down = _lag_check(model, li, "down", act, quants, f"step {step} layer {li}")
+        if late_o is not None:
+            h = h + late_o
         xf = _f16(model.x_final)
         assert_close(xf, o_dec.to_f16(o_dec.rmsnorm(h, model.final_norm.cpu().numpy(), S.eps)).astype(np.float64),
                      what="final norm", **F16)
@@ -269,6 +295,15 @@ def test_decode_steps(spec, batch):
 def test_decode_steps_lru_pools(spec):
     """Small decoders with LRU pools holding 25% of every tensor's units over 8 steps."""
     _run_steps(spec, 2, 60, 8, 80, pool_frac=0.25)
+
+
+@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
+def test_decode_steps_fetch_lag(spec):
+    """Fetch lag with 25% LRU pools over 6 steps: each o / down projection's late
+    contribution (its missed channels, read from the host store on the side stream)
+    against the oracle, and every later operation against the oracle on a residual
+    stream that carries it from the next update on."""
+    _run_steps(spec, 2, 60, 6, 85, pool_frac=0.25, fetch_lag=True)
 
 
 # full hidden width, two layers, a 4096-token vocabulary (the lm_head's shape aside,
