@@ -8,7 +8,7 @@ stamps, linear scan) on random traces.
 import numpy as np
 import pytest
 
-from oracle.cache import LRUPool
+from oracle.cache import LeadPool, LRUPool
 
 
 def test_hand_trace():
@@ -105,3 +105,72 @@ def test_warm_full_capacity_all_hits():
     p.lookup(list(range(100)), 6)
     p.fill(6)
     assert all(p.lookup(list(range(100)), 7))
+
+
+def test_lead_hand_trace():
+    """Capacity 2, 2 ring slots: prefetched units hit without an LRU mark; the ring
+    keeps what the new prediction names and empties the rest; fills go to the LRU."""
+    p = LeadPool(2, 2)
+    assert p.prefetch([4, 7, 9]) == [4, 7]  # 9 finds no empty ring slot
+    assert p.ring == [4, 7]
+    assert p.lookup([7, 9, 4], 0) == [True, False, True]
+    assert p.fill(0) == [9]
+    assert p.resident() == {9} and p.ring_units() == {4, 7}
+    assert p.prefetch([7, 9, 1]) == [1]  # 7 stays in slot 1, 4 leaves slot 0 for 1; 9 is in the LRU
+    assert p.ring == [1, 7]
+    assert p.lookup([4, 1, 9, 7], 1) == [False, True, True, True]
+    assert p.fill(1) == [4]  # a free LRU slot
+    assert p.resident() == {9, 4}
+    assert p.prefetch([5]) == [5]  # both ring slots emptied, 5 takes slot 0
+    assert p.ring == [5, None]
+    assert p.lookup([1, 7, 5, 4], 2) == [False, False, True, True]
+    # queued 1 then 7; LRU: 4 used at 2, 9 last at 1 -> 9 goes for 1; then 7 finds
+    # only 4 and 1, both used or installed at 2 -> dropped
+    assert p.fill(2) == [1]
+    assert p.resident() == {4, 1} and p.ring_units() == {5}
+    assert p.lookup([9], 3) == [False]
+
+
+def test_lead_ring_loses_to_a_later_lru_install():
+    """A unit queued as a miss and prefetched before the fill ends up in its LRU slot;
+    emptying its ring slot later leaves it on the device, an LRU eviction does not."""
+    p = LeadPool(1, 1)
+    assert p.lookup([3], 0) == [False]
+    assert p.prefetch([3]) == [3]
+    assert p.fill(0) == [3]
+    assert p.where[3] == "lru"
+    assert p.prefetch([8]) == [8]  # ring slot 0 no longer serves 3
+    assert p.lookup([3, 8], 1) == [True, True]
+    assert p.lookup([6], 2) == [False]
+    assert p.fill(2) == [6]  # 3 (last used 1) evicted
+    assert p.lookup([3, 8, 6], 3) == [False, True, True]
+    with pytest.raises(ValueError):
+        p.prefetch([1, 1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lead_zero_is_the_lru(seed):
+    """Without ring slots (and without prefetches) the policy is LRUPool's."""
+    g = np.random.default_rng(seed)
+    a, b = LRUPool(7), LeadPool(7, 0)
+    for t in range(30):
+        units = g.integers(0, 20, size=g.integers(1, 9)).tolist()
+        assert a.lookup(units, t) == b.lookup(units, t)
+        assert a.fill(t) == b.fill(t)
+        assert a.resident() == b.resident()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lead_prefetched_units_hit(seed):
+    """Right after a prefetch of at most `lead` new units, every unit asked for is on
+    the device; the LRU state is untouched by the prefetch itself."""
+    g = np.random.default_rng(100 + seed)
+    p = LeadPool(5, 6)
+    for t in range(20):
+        want = [int(u) for u in g.choice(40, size=6, replace=False)]
+        lru_before = dict(p.last_use)
+        p.prefetch(want)
+        assert p.last_use == lru_before
+        assert all(p.lookup(want, t))
+        p.lookup(g.integers(0, 40, size=4).tolist(), t)
+        p.fill(t)
