@@ -564,7 +564,7 @@ def decode_workload(args):
         store_dir = tempfile.mkdtemp(prefix="sf_refine_store_")
     model = decode.DecodeModel(spec, args.batch, T + 1, src, b=wb, r=wr, kv_b=kvb, kv_r=kvr, ch_pct=ch_pct,
                                tok_pct=tok_pct, pool_frac=frac, cache_mode=mode, store_dir=store_dir,
-                               fetch_lag=args.fetch_lag)
+                               fetch_lag=args.fetch_lag, fetch_lead=args.fetch_lead)
     model.fill_kv(T, src)
     print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     calls, keep = model.build_step(T)
@@ -640,6 +640,7 @@ def decode_workload(args):
     else:
         res["config"]["weight_refinement_store"] = "pinned host RAM"
     res["config"]["fetch_lag"] = bool(model.fetch_lag)
+    res["config"]["fetch_lead"] = bool(model.fetch_lead)
     print(json.dumps(res), flush=True)
 
 
@@ -660,6 +661,9 @@ def main():
                          "SwiGLU; the others run full decode steps with embedding, lm_head and LRU refinement pools")
     ap.add_argument("--store", default="ram", choices=["ram", "ssd"],
                     help="decode workloads: weight refinement stores in pinned host RAM or in files (SSD tier)")
+    ap.add_argument("--fetch-lead", action="store_true",
+                    help="decode workloads: each layer predicts the next layer's q/k/v and gate/up channels from its "
+                         "residual stream and prefetches them on the side stream")
     ap.add_argument("--fetch-lag", action="store_true",
                     help="decode workloads: missed o / down refinements are fetched on the side stream and added at "
                          "the residual stream's next update")

@@ -68,6 +68,7 @@ class sf_pool_desc(C.Structure):
         ("max_lookup", C.c_int32),
         ("store_file", C.c_char_p),
         ("store_offset", C.c_int64),
+        ("lead_slots", C.c_int32),
     ]
 
 
@@ -100,6 +101,7 @@ _PROTOS = {
     "sf_refine_cache_fill": (I32, [VP, VP, VP, C.POINTER(I64)]),
     "sf_refine_cache_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(I64), C.POINTER(I64)]),
     "sf_refine_cache_resident": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64)]),
+    "sf_refine_cache_prefetch": (I32, [VP, I32, VP, I32, VP]),
     "sf_refine_cache_io_stats": (I32, [VP, I32, C.POINTER(I64), C.POINTER(I64), C.POINTER(C.c_double),
                                        C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
@@ -409,6 +411,13 @@ class RefineCache:
         check(lib().sf_refine_cache_stats(self.handle, pool, *[C.byref(x) for x in v]))
         return dict(zip(("lookups", "hits", "installed", "h2d_bytes"), [x.value for x in v]))
 
+    def prefetch(self, pool, ids, stream=None):
+        """Fetch lead: the pool's lead slots come to hold the units `ids` (device int32)."""
+        torch = _torch()
+        ids = ids.to(torch.int32).contiguous()
+        check(lib().sf_refine_cache_prefetch(self.handle, pool, _ptr(ids), ids.numel(), _stream(stream)))
+        return ids
+
     def io_stats(self, pool=-1):
         """Reads of the pools with a store file: units, bytes, median / p99 read time
         (us), wall time spent reading (ms)."""
@@ -443,10 +452,13 @@ def file_pool_desc(path, unit_bytes, n_units, capacity, max_lookup=0, offset=0):
     return d
 
 
-def host_pool_desc(host_store, capacity, max_lookup=0):
-    """Pool over a pinned host store tensor [n_units][unit_bytes] with `capacity` slots."""
+def host_pool_desc(host_store, capacity, max_lookup=0, lead_slots=0):
+    """Pool over a pinned host store tensor [n_units][unit_bytes] with `capacity` LRU
+    slots and `lead_slots` slots for prefetches (fetch lead)."""
     n, ub = host_store.shape
-    return sf_pool_desc(ub, n, capacity, host_store.data_ptr(), None, max_lookup)
+    d = sf_pool_desc(ub, n, capacity, host_store.data_ptr(), None, max_lookup)
+    d.lead_slots = lead_slots
+    return d
 
 
 # ---- refined GEMV -------------------------------------------------------------------

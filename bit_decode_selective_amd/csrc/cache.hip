@@ -88,6 +88,10 @@ struct HostPool {
   int64_t bucket_entries = 0;                       // ids held by all buckets
   std::vector<int64_t> pending;
   std::vector<uint8_t> pending_flag;  // per unit
+  // fetch lead: ring slots [capacity, capacity + lead) of d_slots
+  int32_t lead = 0;
+  int32_t* d_ring = nullptr;  // [lead] unit held by each ring slot, -1 = empty
+  int32_t* d_plan = nullptr;  // [2 * lead] (unit, slot) fetched by a prefetch | [1] count
   // store file (SSD tier)
   int fd = -1;
   bool direct = false;
@@ -234,6 +238,8 @@ void destroy_cache(sf_refine_cache* c) {
     if (p.d_unit2slot) hipFree(p.d_unit2slot);
     if (p.d_slots && !p.resident) hipFree(p.d_slots);
     if (p.h_fstage) hipHostFree(p.h_fstage);
+    if (p.d_ring) hipFree(p.d_ring);
+    if (p.d_plan) hipFree(p.d_plan);
     if (p.fd >= 0) close(p.fd);
   }
   if (c->d_logs) hipFree(c->d_logs);
@@ -425,6 +431,10 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
                  "a pool with slots needs a host store or a store file");
     SF_REQUIRE(!(d.store_file && d.host_store), SF_EINVAL, "give a host store or a store file, not both");
     SF_REQUIRE(d.store_offset >= 0, SF_EINVAL, "bad store_offset");
+    SF_REQUIRE(d.lead_slots >= 0 && d.lead_slots <= 16384 && d.lead_slots <= d.n_units, SF_EINVAL,
+               "lead_slots must be in [0, min(n_units, 16384)]");
+    SF_REQUIRE(d.lead_slots == 0 || (d.host_store && !d.device_store), SF_EINVAL,
+               "lead slots need a pinned host store");
   }
   sf_refine_cache* c = new sf_refine_cache();
   c->mode = mode;
@@ -500,13 +510,20 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
         CK(hipHostGetDevicePointer((void**)&p.fstage_dev, p.h_fstage, 0));
         p.store_dev = p.fstage_dev;
       } else if (p.d.host_store) {
-        if (cap > 0) CK(hipMalloc((void**)&p.d_slots, (size_t)cap * p.d.unit_bytes));
+        p.lead = p.d.lead_slots;
+        if (cap + p.lead > 0) CK(hipMalloc((void**)&p.d_slots, (size_t)(cap + p.lead) * p.d.unit_bytes));
+        if (p.lead > 0) {
+          CK(hipMalloc((void**)&p.d_ring, sizeof(int32_t) * p.lead));
+          CK(hipMalloc((void**)&p.d_plan, sizeof(int32_t) * (2 * (size_t)p.lead + 1)));
+          hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((p.lead + 255) / 256)), dim3(256), 0, 0, p.d_ring,
+                             (int64_t)p.lead, -1);
+        }
         // the fill and lag kernels read the store directly: it must be pinned host memory
         hipPointerAttribute_t attr{};
         const bool pinned = hipPointerGetAttributes(&attr, p.d.host_store) == hipSuccess &&
                             attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr;
         if (!pinned) (void)hipGetLastError();
-        if (!pinned && cap == 0) {
+        if (!pinned && cap == 0 && p.lead == 0) {
           // a pool without slots never fills; only sf_refine_lag_delta would read it
         } else if (!pinned) {
           sf_set_error("sf_refine_cache_create: host_store of pool " + std::to_string(i) +
@@ -605,7 +622,9 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
       const int32_t s = log_s[e];
       ++p.n_lookups;
       if (u < 0 || u >= p.d.n_units) continue;
-      if (s >= 0 && s < cap) {
+      if (s >= cap) {  // a ring slot (fetch lead): a hit that is not an LRU use
+        ++p.n_hits;
+      } else if (s >= 0) {
         ++p.n_hits;
         p.slot_last[s] = t;
         if (!now) now = &p.buckets[t];
@@ -707,6 +726,129 @@ extern "C" sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int
   if (hits) *hits = b;
   if (installed) *installed = d;
   if (h2d_bytes) *h2d_bytes = e;
+  return SF_OK;
+}
+
+namespace {
+
+// Exclusive prefix of a per-thread flag over a 1024-thread workgroup (in thread
+// order); *total = the number of set flags.  Uses wsum[16]; ends with a barrier.
+__device__ __forceinline__ int block_rank(bool f, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const int below = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+  __syncthreads();
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int v = wsum[w];
+    base += w < wave ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  __syncthreads();
+  return base + below;
+}
+
+// Fetch lead, planning: one 1024-thread workgroup.  Ring slots whose unit is named
+// again are kept; the others are emptied (their unit unmapped if the slot still
+// serves it); the named units mapped nowhere take the empty slots in ascending
+// order.  The plan lists (unit, slot) pairs; the count follows them.
+constexpr int LEAD_T = 1024, LEAD_MAX = 16384;
+__global__ __launch_bounds__(LEAD_T) void lead_plan_kernel(int32_t* unit2slot, int64_t n_units, int32_t cap,
+                                                           int32_t lead, int32_t* ring, const int32_t* ids, int32_t n,
+                                                           int32_t* plan) {
+  __shared__ uint8_t keep[LEAD_MAX];
+  __shared__ uint16_t free_slot[LEAD_MAX];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  for (int j = tid; j < lead; j += LEAD_T) keep[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += LEAD_T) {
+    const int32_t u = ids[i];
+    if (u >= 0 && u < n_units) {
+      const int32_t sl = unit2slot[u];
+      if (sl >= cap && sl < cap + lead) keep[sl - cap] = 1;
+    }
+  }
+  __syncthreads();
+  int n_free = 0;
+  for (int j0 = 0; j0 < lead; j0 += LEAD_T) {
+    const int j = j0 + tid;
+    const bool fr = j < lead && !keep[j];
+    int tot;
+    const int rk = block_rank(fr, wsum, &tot);
+    if (fr) {
+      free_slot[n_free + rk] = (uint16_t)j;
+      const int32_t o = ring[j];
+      if (o >= 0 && unit2slot[o] == cap + j) unit2slot[o] = -1;
+      ring[j] = -1;
+    }
+    n_free += tot;
+  }
+  // (a named unit is never one emptied here: its ring slot was kept)
+  int n_new = 0;
+  for (int i0 = 0; i0 < n; i0 += LEAD_T) {
+    const int i = i0 + tid;
+    int32_t u = -1;
+    bool miss = false;
+    if (i < n) {
+      u = ids[i];
+      miss = u >= 0 && u < n_units && unit2slot[u] < 0;
+    }
+    int tot;
+    const int rk = n_new + block_rank(miss, wsum, &tot);
+    if (miss && rk < n_free) {
+      const int j = free_slot[rk];
+      ring[j] = u;
+      plan[2 * rk] = u;
+      plan[2 * rk + 1] = cap + j;
+    }
+    n_new += tot;
+  }
+  if (tid == 0) plan[2 * lead] = min(n_new, n_free);
+}
+
+// Copies the planned units from the pinned host store (over PCIe) into their slots.
+__global__ __launch_bounds__(256) void lead_copy_kernel(const uint8_t* store, uint8_t* slots, int64_t unit_bytes,
+                                                        const int32_t* plan, int32_t lead) {
+  const int cnt = plan[2 * lead];
+  for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
+    const uint8_t* src = store + (int64_t)plan[2 * e] * unit_bytes;
+    uint8_t* dst = slots + (int64_t)plan[2 * e + 1] * unit_bytes;
+    if ((unit_bytes & 15) == 0 && (((uintptr_t)store | (uintptr_t)slots) & 15) == 0) {
+      for (int64_t w = threadIdx.x; w < unit_bytes / 16; w += 256) ((uint4*)dst)[w] = ((const uint4*)src)[w];
+    } else {
+      for (int64_t w = threadIdx.x; w < unit_bytes / 4; w += 256) ((uint32_t*)dst)[w] = ((const uint32_t*)src)[w];
+    }
+  }
+}
+
+// Maps the planned units once their bytes are in place (a launch after the copy).
+__global__ __launch_bounds__(256) void lead_map_kernel(int32_t* unit2slot, const int32_t* plan, int32_t lead) {
+  const int cnt = plan[2 * lead];
+  for (int e = threadIdx.x; e < cnt; e += 256) unit2slot[plan[2 * e]] = plan[2 * e + 1];
+}
+
+}  // namespace
+
+extern "C" sf_status sf_refine_cache_prefetch(sf_refine_cache* c, int32_t pool, const int32_t* unit_ids, int32_t n,
+                                              sf_stream stream_) {
+  SF_REQUIRE(c, SF_EINVAL, "null cache");
+  SF_REQUIRE(pool >= 0 && pool < (int32_t)c->pools.size(), SF_EINVAL, "pool index out of range");
+  HostPool& p = c->pools[pool];
+  SF_REQUIRE(p.lead > 0, SF_EINVAL, "the pool has no lead slots");
+  SF_REQUIRE(n >= 0 && (n == 0 || unit_ids), SF_EINVAL, "bad ids");
+  hipStream_t s = (hipStream_t)stream_;
+  hipLaunchKernelGGL(lead_plan_kernel, dim3(1), dim3(LEAD_T), 0, s, p.d_unit2slot, p.d.n_units,
+                     (int32_t)p.d.capacity, p.lead, p.d_ring, unit_ids, n, p.d_plan);
+  SF_LAUNCH_CHECK();
+  hipLaunchKernelGGL(lead_copy_kernel, dim3((unsigned)std::max(1, std::min(p.lead, 1024))), dim3(256), 0, s,
+                     p.host_dev, p.d_slots, p.d.unit_bytes, (const int32_t*)p.d_plan, p.lead);
+  SF_LAUNCH_CHECK();
+  hipLaunchKernelGGL(lead_map_kernel, dim3(1), dim3(256), 0, s, p.d_unit2slot, (const int32_t*)p.d_plan, p.lead);
+  SF_LAUNCH_CHECK();
   return SF_OK;
 }
 

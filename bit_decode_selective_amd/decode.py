@@ -112,6 +112,11 @@ class DecodeModel:
                selects its channels itself
     store_dir  with pool_frac: weight pools read their units from files in this
                directory (the SSD tier); KV pools stay in pinned host memory
+    fetch_lead with pool_frac: at each layer l but the last, layer l + 1's q/k/v and
+               gate/up channels are predicted from the residual stream entering
+               layer l (its RMSNorms with layer l + 1's gains, then top-k) and
+               prefetched on the side stream into lead slots of those pools
+               (sf_refine_cache_prefetch); layer l + 1's q/k/v GEMV waits for them
     fetch_lag  with pool_frac: the selected channels of the o and down projections
                that missed are read from the host store on the side stream
                (sf_refine_lag_delta) and their contribution is added to the
@@ -121,7 +126,7 @@ class DecodeModel:
 
     def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
                  cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True,
-                 store_dir=None, fetch_lag=False):
+                 store_dir=None, fetch_lag=False, fetch_lead=False):
         import torch
 
         self.torch, self.spec, self.batch, self.t_cap = torch, spec, batch, t_cap
@@ -130,6 +135,9 @@ class DecodeModel:
         # fetch lag: the o and down projections' missed refinements are read on the
         # side stream and added at the residual stream's next update
         self.fetch_lag = bool(fetch_lag) and pool_frac is not None and r > 0 and store_dir is None
+        # fetch lead: layer l + 1's q/k/v and gate/up channels are predicted from the
+        # residual stream entering layer l and prefetched into lead slots meanwhile
+        self.fetch_lead = bool(fetch_lead) and pool_frac is not None and r > 0 and store_dir is None
         self.b, self.r, self.kv_b, self.kv_r = b, r, kv_b, kv_r
         self.ch_pct, self.tok_pct = ch_pct, tok_pct
         dev = torch.device(device)
@@ -147,7 +155,9 @@ class DecodeModel:
             qw = binding.QuantWeight.from_host(W, b, r) if keep_host else binding.QuantWeight.from_device(W, b, r)
             return qw
 
-        def add_pool(unit_bytes_obj, n_lookup, static=True):
+        lead_of = lambda n_lookup: n_lookup if self.fetch_lead else 0
+
+        def add_pool(unit_bytes_obj, n_lookup, static=True, lead=0):
             """n_lookup: unit ids one step looks up in the pool (sizes its lookup log).
             With store_dir, a static pool (a weight matrix) reads its units from a
             file there (the SSD tier); KV units change every step and stay in RAM."""
@@ -163,7 +173,7 @@ class DecodeModel:
                 st = unit_bytes_obj.host_store()
                 stores[len(pools)] = st
                 cap = max(0, int(pool_frac * st.shape[0]))
-                pools.append(binding.host_pool_desc(st, cap, max_lookup=n_lookup))
+                pools.append(binding.host_pool_desc(st, cap, max_lookup=n_lookup, lead_slots=lead))
             return len(pools) - 1
 
         self.layers = []
@@ -178,7 +188,9 @@ class DecodeModel:
             L["down"] = quant(li, inputs.DOWN, H, S.ffn)
             if r > 0:
                 for name in ("q", "k", "v", "o", "gate", "up", "down"):
-                    L["pool_" + name] = add_pool(L[name], k_select(ch_pct, L[name].k_in))
+                    n_look = k_select(ch_pct, L[name].k_in)
+                    lead = lead_of(n_look) if name in ("q", "k", "v", "gate", "up") and li > 0 else 0
+                    L["pool_" + name] = add_pool(L[name], n_look, lead=lead)
             L["attn_norm"] = torch.as_tensor(src.gain(li, ATTN_NORM, H), device=dev)
             L["ffn_norm"] = torch.as_tensor(src.gain(li, FFN_NORM, H), device=dev)
             if S.qk_norm:
@@ -247,6 +259,12 @@ class DecodeModel:
                 "gate": torch.empty((B, S.ffn), **f32),
                 "up": torch.empty((B, S.ffn), **f32),
                 "act": torch.empty((B, S.ffn), **i16),
+                "x_pred_attn": torch.zeros((B, S.hidden), **i16),
+                "x_pred_ffn": torch.zeros((B, S.hidden), **i16),
+                "sel_pred_attn": torch.zeros(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32,
+                                             device=self.dev),
+                "sel_pred_ffn": torch.zeros(max(1, k_select(self.ch_pct, S.hidden)), dtype=torch.int32,
+                                            device=self.dev),
                 "lag_o": torch.zeros((B, S.hidden), **f32),
                 "lag_down": torch.zeros((B, S.hidden), **f32),
                 "down": torch.empty((B, S.hidden), **f32),
@@ -354,6 +372,38 @@ class DecodeModel:
                 calls.append((pending.pop(update), None, "lag_add"))
 
         lag_on = self.fetch_lag and refined
+        lead_on = self.fetch_lead and refined
+        lead_wait = {}  # ("qkv" | "ffn-write", layer) -> call that makes the compute stream wait
+
+        def lead(li):
+            """Predict layer li + 1's channels from the residual stream entering layer li
+            (side stream: the two norms' selections, then the prefetches) and register
+            the waits: the compute stream's next write of h waits for the prediction,
+            layer li + 1's q/k/v GEMV for the prefetches."""
+            nx, bn = self.layers[li + 1], self.buf[li + 1]
+            ks = ksel(S.hidden)
+            ev_in, ev_pred, ev_done = torch_.cuda.Event(), torch_.cuda.Event(), torch_.cuda.Event()
+            keep.extend([ev_in, ev_pred, ev_done])
+            side = C.c_void_p(self.side.cuda_stream)
+            preds = [(nx["attn_norm"], bn["x_pred_attn"], bn["sel_pred_attn"]),
+                     (nx["ffn_norm"], bn["x_pred_ffn"], bn["sel_pred_ffn"])]
+            fetch = [(nx["pool_" + n], bn["sel_pred_attn"] if n in ("q", "k", "v") else bn["sel_pred_ffn"])
+                     for n in ("q", "k", "v", "gate", "up")]
+
+            def launch(stream):
+                ev_in.record(stream)
+                self.side.wait_event(ev_in)
+                for gain, xp, sp in preds:
+                    binding.check(Lb.sf_add_rmsnorm_select(P(self.h), None, P(gain), B, S.hidden, S.eps, P(xp), ks,
+                                                           P(sp), side))
+                ev_pred.record(self.side)
+                for pool, sp in fetch:
+                    binding.check(Lb.sf_refine_cache_prefetch(cache, pool, P(sp), ks, side))
+                ev_done.record(self.side)
+
+            calls.append((launch, None, "lead"))
+            lead_wait[("ffn-write", li)] = lambda stream: stream.wait_event(ev_pred)
+            lead_wait[("qkv", li + 1)] = lambda stream: stream.wait_event(ev_done)
         if self.head:
             calls.append((Lb.sf_embed, [P(self.embed), S.vocab, S.hidden, P(self.ids), B, P(self.h), None], "embed"))
         for li, L in enumerate(self.layers):
@@ -361,6 +411,10 @@ class DecodeModel:
             prev = self.buf[li - 1]["down"] if li > 0 else None
             late_into(("attn", li))
             norm(prev, L["attn_norm"], bf["x_attn"], bf["sel_attn"], S.hidden, "norm")
+            if lead_on and li + 1 < len(self.layers):
+                lead(li)
+            if ("qkv", li) in lead_wait:
+                calls.append((lead_wait.pop(("qkv", li)), None, "lead_wait"))
             gemv(("q", "k", "v"), L, bf["x_attn"], (bf["q"], bf["k"], bf["v"]), S.hidden, bf["sel_attn"], "qkv")
             calls.append((Lb.sf_qk_rope, [P(bf["q"]), P(bf["k"]), B, S.n_q, S.n_kv, P(L.get("q_norm")), P(L.get("k_norm")),
                                           S.eps, pos, S.theta, P(bf["q16"]), P(bf["k_rot"]), None], "rope"))
@@ -391,6 +445,8 @@ class DecodeModel:
             last = li == len(self.layers) - 1
             if lag_on and (not last or self.head):  # o's next update: the next layer's, or the final norm
                 pending[("attn", li + 1)] = lag(li, "o", bf["a16"], bf["sel_o"])
+            if ("ffn-write", li) in lead_wait:  # the prediction read h: its next write waits
+                calls.append((lead_wait.pop(("ffn-write", li)), None, "lead_wait"))
             late_into(("ffn", li))
             norm(bf["o"], L["ffn_norm"], bf["x_ffn"], bf["sel_ffn"], S.hidden, "norm")
             gemv(("gate", "up"), L, bf["x_ffn"], (bf["gate"], bf["up"]), S.hidden, bf["sel_ffn"], "gateup")

@@ -181,6 +181,7 @@ typedef struct {
   int32_t max_lookup; /* most unit ids one step looks up in this pool */
   const char* store_file; /* NULL: the store is host_store (or device_store) */
   int64_t store_offset;
+  int32_t lead_slots; /* device slots beyond capacity that sf_refine_cache_prefetch fills */
 } sf_pool_desc;
 
 #define SF_CACHE_DETERMINISTIC 0 /* fill completes before the next step's lookups */
@@ -218,6 +219,21 @@ sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream 
  * copied host-to-device; per pool if pool >= 0, all pools if pool < 0. */
 sf_status sf_refine_cache_stats(sf_refine_cache* c, int32_t pool, int64_t* lookups,
                                 int64_t* hits, int64_t* installed, int64_t* h2d_bytes);
+
+/* Fetch lead (rag-lover.com StrataFlux summary, explainer dialogue (解説), fetch lead /
+ * fetch lag passage: the channels a block will need are predicted from the
+ * previous block's residual stream and fetched ahead of it).  The pool's
+ * lead_slots ring slots come to hold the units named by unit_ids (device [n],
+ * distinct): ring units named again stay; every other ring slot is emptied (its
+ * unit unmapped unless an LRU slot serves it); the named units found in no slot,
+ * in the order given, are copied from the pinned host store into the empty ring
+ * slots (ascending) and mapped, as many as there are empty slots.  Three kernels
+ * on `stream` (a side stream: work on the compute stream that looks these units
+ * up must wait for it; nothing else may look up or fill this pool meanwhile).
+ * Lookups that find a unit in a ring slot are hits that do not count as LRU use;
+ * fills never evict ring slots.  SF_EINVAL if the pool has no lead slots. */
+sf_status sf_refine_cache_prefetch(sf_refine_cache* c, int32_t pool, const int32_t* unit_ids, int32_t n,
+                                   sf_stream stream);
 
 /* Fetch lag (rag-lover.com StrataFlux summary, explainer dialogue (解説), fetch lead /
  * fetch lag passage: a refinement's addition to the output may wait for a later

@@ -177,6 +177,68 @@ def test_lag_delta_edges():
     assert torch.equal(h.cpu(), torch.arange(256, dtype=torch.float32) + 0.5)
 
 
+@pytest.mark.parametrize("lead,capacity", [(16, 12), (10, 0), (40, 30)])
+def test_lead_prefetch_over_steps(lead, capacity):
+    """Fetch lead on one weight pool over 10 steps: a prefetch of a predicted
+    selection (every other step the GEMV's own, otherwise another step's) on a side
+    stream, then the GEMV: hit sets, outputs and LRU resident sets against the
+    oracle policy (LRU slots plus lead slots)."""
+    k_in, n_out, ks = 512, 256, 16
+    qw, q = _weight(68, n_out, k_in, 2, 2)
+    store = qw.host_store()
+    cache = binding.RefineCache([binding.host_pool_desc(store, capacity, lead_slots=lead)], keep=[store])
+    pool = o_cache.LeadPool(capacity, lead)
+    side = torch.cuda.Stream()
+    for t in range(10):
+        x = _step_x(68, t, k_in)
+        pred = selection.select_channels(_step_x(68, t + 1, k_in), ks)
+        ev = torch.cuda.Event()
+        with torch.cuda.stream(side):
+            cache.prefetch(0, torch.as_tensor(pred, dtype=torch.int32, device="cuda"), stream=side)
+            ev.record(side)
+        torch.cuda.current_stream().wait_event(ev)
+        pool.prefetch(pred)
+        (y,), sel, (hit,) = binding.refined_gemv([(qw, 0)], x, ks, cache=cache)
+        torch.cuda.synchronize()
+        sel = sel.cpu().numpy().tolist()
+        hits = (hit.cpu().numpy() >= 0).tolist()
+        assert hits == pool.lookup(sel, t), t
+        assert_close(y.cpu().numpy(), o_gemv.refined_gemv(q, x, [k for k, h in zip(sel, hits) if h]),
+                     what=f"step {t}")
+        cache.fill()
+        pool.fill(t)
+        assert cache.resident(0, max(1, capacity)) == pool.resident(), t
+    st = cache.stats(0)
+    assert st["lookups"] == 10 * ks and st["hits"] > 0
+
+
+def test_lead_prefetch_edges():
+    """A pool without lead slots refuses prefetches; an empty prefetch empties the
+    ring; prefetched units that the LRU already holds are not fetched again."""
+    qw, q = _weight(69, 256, 512, 2, 2)
+    store = qw.host_store()
+    with pytest.raises(binding.SFError):
+        c0 = binding.RefineCache([binding.host_pool_desc(store, 8)], keep=[store])
+        c0.prefetch(0, torch.arange(4, dtype=torch.int32, device="cuda"))
+    cache = binding.RefineCache([binding.host_pool_desc(store, 8, lead_slots=8)], keep=[store])
+    pool = o_cache.LeadPool(8, 8)
+    ids = torch.arange(8, dtype=torch.int32, device="cuda")
+    slots = cache.lookup(0, ids)
+    pool.lookup(list(range(8)), 0)
+    cache.fill()
+    pool.fill(0)  # units 0..7 in LRU slots
+    cache.prefetch(0, torch.arange(4, 12, dtype=torch.int32, device="cuda"))
+    assert pool.prefetch(list(range(4, 12))) == [8, 9, 10, 11]
+    slots = cache.lookup(0, torch.arange(16, dtype=torch.int32, device="cuda")).cpu().numpy()
+    assert (slots >= 0).tolist() == pool.lookup(list(range(16)), 1)
+    assert set(slots[8:12].tolist()) <= set(range(8, 16)) and slots[:8].max() < 8  # ring slots follow the LRU's
+    cache.prefetch(0, torch.empty(0, dtype=torch.int32, device="cuda"))
+    pool.prefetch([])
+    slots = cache.lookup(0, torch.arange(16, dtype=torch.int32, device="cuda")).cpu().numpy()
+    assert (slots >= 0).tolist() == pool.lookup(list(range(16)), 2)
+    torch.cuda.synchronize()
+
+
 def test_gemv_fused_ops_have_their_own_pools():
     k_in, ks = 512, 20
     (qa, qa_o), (qb, qb_o) = _weight(61, 256, k_in, 2, 2, 0), _weight(61, 96, k_in, 2, 2, 1)

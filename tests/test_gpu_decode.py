@@ -156,7 +156,8 @@ def _lag_check(model, li, name, x16, quants, what):
     return got
 
 
-def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None, fetch_lag=False):
+def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None, fetch_lag=False,
+               fetch_lead=False):
     """Teacher-forced decode steps; every operation of every step checked against the
     oracle on the GPU's own inputs.  With pool_frac, the LRU pools of every weight,
     KV cache and lm_head are replayed by the oracle (``cache.LRUPool``): each GEMV's
@@ -165,8 +166,9 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
     outputs are compared (all by default); selections and hit sets are checked at
     every step."""
     src = decode.HostWeights(cfg)
-    model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac, fetch_lag=fetch_lag)
-    assert model.fetch_lag == fetch_lag
+    model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac, fetch_lag=fetch_lag,
+                               fetch_lead=fetch_lead)
+    assert model.fetch_lag == fetch_lag and model.fetch_lead == fetch_lead
     for li in range(spec.layers):
         for name, t in TENSOR.items():
             model.host[(li, name)] = model.host[(li, t)]
@@ -175,7 +177,7 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
     quants = Quants(model)
     lru = None
     if pool_frac is not None:
-        lru = {i: o_cache.LRUPool(int(p.capacity)) for i, p in enumerate(model._pools)}
+        lru = {i: o_cache.LeadPool(int(p.capacity), int(p.lead_slots)) for i, p in enumerate(model._pools)}
     S, d = spec, spec.head_dim
     kv_host = {li: model.host[("kv", li)] for li in range(S.layers)}
     appended = {li: ([], []) for li in range(S.layers)}
@@ -196,6 +198,19 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
             x = _f16(bf["x_attn"])
             assert_close(x, o_dec.to_f16(o_dec.rmsnorm(h, L["attn_norm"].cpu().numpy(), S.eps)).astype(np.float64),
                          what=f"layer {li} attn norm", **F16)
+            if fetch_lead and li + 1 < S.layers:
+                # layer li + 1's channels predicted from this residual stream, then
+                # prefetched into its pools' lead slots (in the GPU's order)
+                nx, bn = model.layers[li + 1], model.buf[li + 1]
+                ks_h = decode.k_select(model.ch_pct, S.hidden)
+                for norm_key, sfx, names in (("attn_norm", "attn", ("q", "k", "v")), ("ffn_norm", "ffn", ("gate", "up"))):
+                    xp = _f16(bn["x_pred_" + sfx])
+                    assert_close(xp, o_dec.to_f16(o_dec.rmsnorm(h, nx[norm_key].cpu().numpy(), S.eps)).astype(np.float64),
+                                 what=f"layer {li} prediction for {li + 1} ({sfx})", **F16)
+                    sp = bn["sel_pred_" + sfx].cpu().numpy()[:ks_h].tolist()
+                    assert sp == selection.select_channels(xp.astype(np.float16), ks_h), (step, li, sfx)
+                    for n in names:
+                        lru[nx["pool_" + n]].prefetch(sp)
             ys = [bf[n].cpu().numpy() for n in ("q", "k", "v")]
             _gemv_check(model, li, ("q", "k", "v"), x, ys, bf["sel_attn"], S.hidden, f"step {step} layer {li} qkv",
                         quants, lru, step, outs)
@@ -304,6 +319,23 @@ def test_decode_steps_fetch_lag(spec):
     against the oracle, and every later operation against the oracle on a residual
     stream that carries it from the next update on."""
     _run_steps(spec, 2, 60, 6, 85, pool_frac=0.25, fetch_lag=True)
+
+
+@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
+def test_decode_steps_fetch_lead(spec):
+    """Fetch lead with 25% LRU pools over 6 steps (3 layers): each layer's q/k/v and
+    gate/up channels for the next layer predicted from its residual stream (checked
+    against the oracle), prefetched into lead slots, and every later lookup's hit set
+    equal to the oracle policy's (LRU slots plus lead slots)."""
+    spec3 = decode.Spec(spec.name, 3, spec.hidden, spec.n_q, spec.n_kv, spec.ffn, spec.vocab, spec.qk_norm,
+                        spec.theta, spec.eps)
+    _run_steps(spec3, 2, 60, 6, 86, pool_frac=0.25, fetch_lead=True)
+
+
+def test_decode_full_width_llama_fetch_lead_and_lag():
+    """Full-width Llama layers (2+2 bits, 10% pools) with fetch lead and fetch lag
+    together, 4 steps; outputs checked on the last."""
+    _run_steps(WIDE_LLAMA, 1, 128, 4, 87, pool_frac=0.10, output_steps={3}, fetch_lag=True, fetch_lead=True)
 
 
 # full hidden width, two layers, a 4096-token vocabulary (the lm_head's shape aside,
