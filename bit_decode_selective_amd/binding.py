@@ -107,6 +107,9 @@ _PROTOS = {
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
     "sf_refined_gemv_noalloc": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
+    "sf_attn_decode_variant": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP,
+                                     I32]),
+    "sf_fp16_fetch_delta": (I32, [VP, I32, C.POINTER(sf_qweight), VP, I32, I32, VP, VP, VP, VP]),
     "sf_embed": (I32, [VP, I64, I32, VP, I32, VP, VP]),
     "sf_add_rmsnorm": (I32, [VP, VP, VP, I32, I32, C.c_float, VP, VP]),
     "sf_qk_rope": (I32, [VP, VP, I32, I32, I32, VP, VP, C.c_float, I32, C.c_float, VP, VP, VP]),
@@ -494,7 +497,11 @@ def refined_gemv(ops, x, k_sel, cache=None, sel_in=None, stream=None, ys=None, w
 
 
 # ---- refined attention ----------------------------------------------------------------
-def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stream=None, out=None, t_len=None):
+SF_ATTN_NESTED, SF_ATTN_FP16_TOKENS, SF_ATTN_DROP_UNSELECTED = 0, 1, 2
+
+
+def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stream=None, out=None, t_len=None,
+                      variant=SF_ATTN_NESTED):
     """q fp16 [batch][n_q][d].  Returns (out fp32 [batch][n_q][d], sel [batch][n_kv][k_sel],
     hits [batch][n_kv][k_sel])."""
     torch = _torch()
@@ -510,9 +517,9 @@ def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stre
     ws = workspace(lib().sf_workspace_bytes_attn(batch, n_q, kv.n_kv, tl, k_sel), dev)
     d_ = kv.desc(tl)
     check(
-        lib().sf_refined_attn_decode(
+        lib().sf_attn_decode_variant(
             _ptr(qb), n_q, C.byref(d_), float(scale), k_sel, _ptr(sin), cache.handle if cache else None, pool,
-            _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream),
+            _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream), variant,
         )
     )
     return o, sel[:, :, :k_sel], hit[:, :, :k_sel]
@@ -622,3 +629,43 @@ def refine_lag_delta(cache, pool, w, x, sel, hit, out=None, stream=None):
     check(lib().sf_refine_lag_delta(cache.handle, pool, C.byref(d), _ptr(xb), batch, sel.numel(), _ptr(sel), _ptr(hit),
                                     _ptr(o), _stream(stream)))
     return o
+
+
+def fp16_fetch_gemv(w, x, k_sel, cache, pool, sel_in=None, stream=None):
+    """FP16 fetch (comparison variant) for one QuantWeight: the resident GEMV with the
+    channel selection, a lookup of the selection in `pool` (fp16 columns), and the
+    fetched columns' correction to their fp16 value.  Returns (y, sel, slots)."""
+    (y,), sel, _ = refined_gemv([(w, -1)], x, k_sel, cache=None, sel_in=sel_in, stream=stream, want_hits=False)
+    if k_sel == 0:
+        return y, sel, sel
+    slots = cache.lookup(pool, sel, stream=stream)
+    xb = _f16_bits(x, w.resident.device)
+    if xb.dim() == 1:
+        xb = xb[None]
+    d = w.desc()
+    check(lib().sf_fp16_fetch_delta(cache.handle, pool, C.byref(d), _ptr(xb), xb.shape[0], k_sel, _ptr(sel),
+                                    _ptr(slots), _ptr(y), _stream(stream)))
+    return y, sel, slots
+
+
+def fp16_weight_units(W, device="cuda"):
+    """fp16 columns of W [n_out][k_in] as units [k_in][2 * n_out] bytes (unit k =
+    fp16(W[:, k]), nearest even), on `device`."""
+    torch = _torch()
+    Wt = torch.as_tensor(np.asarray(W, dtype=np.float32)).t().contiguous().to(torch.float16)
+    return Wt.view(torch.uint8).reshape(Wt.shape[0], -1).to(device)
+
+
+def fp16_kv_units(K, V, device="cuda"):
+    """fp16 K and V of every token-head as units [batch*n_kv*T][512] bytes (K's 128
+    values, then V's; unit (b, h, t) at (b * n_kv + h) * T + t)."""
+    torch = _torch()
+    KV = torch.cat([torch.as_tensor(np.asarray(K, dtype=np.float32)), torch.as_tensor(np.asarray(V, dtype=np.float32))],
+                   dim=-1).to(torch.float16)
+    return KV.view(torch.uint8).reshape(-1, 4 * KV.shape[-1] // 2).to(device)
+
+
+def device_pool_desc(units):
+    """A resident pool over device units [n_units][unit_bytes] (every unit present)."""
+    n, ub = units.shape
+    return sf_pool_desc(ub, n, n, None, units.data_ptr(), 0)

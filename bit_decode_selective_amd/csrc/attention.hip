@@ -72,6 +72,7 @@ struct AttnArgs {
   const uint8_t* v_res;
   const uint32_t* v_sz;
   int batch, n_q, n_kv, G, T, LT, t_cap, b, r, k_sel, nsa, s2, nsp;
+  int variant;  // SF_ATTN_NESTED, SF_ATTN_FP16_TOKENS or SF_ATTN_DROP_UNSELECTED
   float scale;
   float* logits;    // [batch*n_q][LT] (rows padded to 4 floats)
   float* part_a;    // [bh][nsa][G][PW]: split max / sum (+ value sums without refinement)
@@ -476,6 +477,22 @@ __device__ __forceinline__ float kref_dot(const uint8_t* unit, int r, const floa
   return dot;
 }
 
+// q . K16 over a unit that holds the key as HD fp16 values (then the value's).
+__device__ __forceinline__ float k16_dot(const uint8_t* unit, const float* qh) {
+  const u32x4* u4 = (const u32x4*)unit;
+  float dot = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < HD / 8; ++i) {
+    const u32x4 v = u4[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(qh[8 * i + 2 * e], h2f16((uint16_t)(v[e] & 0xFFFFu)), dot);
+      dot = fmaf(qh[8 * i + 2 * e + 1], h2f16((uint16_t)(v[e] >> 16)), dot);
+    }
+  }
+  return dot;
+}
+
 template <int G>
 __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   __shared__ uint32_t lh[NBIN];
@@ -754,9 +771,10 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   const size_t unit0 = (size_t)bh * a.t_cap;
   const int base = a.pool.log_count ? (int)sf_get(a.ctl + 5) : -1;
   // max after replacement: unselected tokens, selected misses (old logit), hits (new)
+  // (dropping the unselected tokens: the max over the selected ones only)
   float mloc[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mloc[h] = mx_uns[h];
+  for (int h = 0; h < G; ++h) mloc[h] = a.variant == SF_ATTN_DROP_UNSELECTED ? -INFINITY : mx_uns[h];
 #pragma nounroll
   for (int m = tid; m < cnt * G; m += SEL_T) {
     const int j = m / G, hh = m - j * G;
@@ -783,8 +801,10 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
         if (h == hh && ok) mloc[h] = fmaxf(mloc[h], l);
       continue;
     }
-    const float dot = kref_dot(a.pool.slots + (size_t)slot * a.pool.unit_bytes, a.r, qf[hh]);
-    const float l2 = l + a.scale * (s * dot);
+    const uint8_t* unit = a.pool.slots + (size_t)slot * a.pool.unit_bytes;
+    // nested: l + scale * s_K * (q . cK_lo); fp16 tokens: scale * (q . K16)
+    const float l2 = a.variant == SF_ATTN_FP16_TOKENS ? a.scale * k16_dot(unit, qf[hh])
+                                                       : l + a.scale * (s * kref_dot(unit, a.r, qf[hh]));
     *lp = l2;
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -855,6 +875,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __shared__ float s_st[3 * G + 1];
   __shared__ int s_rng[4][2];
   __shared__ int s_flag;
+  __shared__ uint32_t s_selm[SP / 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
@@ -948,6 +969,40 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     ht[i] = j < nh ? sel[hit_lo + j] - t_begin : -1;
     hsl[i] = j < nh ? slots[hit_lo + j] : -1;
   }
+  if (a.variant == SF_ATTN_DROP_UNSELECTED) {
+    // only the selected tokens are attended: the others get no weight, and the
+    // split's reference max is taken over the selected ones
+    if (tid < SP / 32) s_selm[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      if (tid + 256 * i < nh && ht[i] >= 0 && ht[i] < n_here) atomicOr(&s_selm[ht[i] >> 5], 1u << (ht[i] & 31));
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) lmx[h] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = tl0 + i;
+      const bool on = t < n_here && ((s_selm[t >> 5] >> (t & 31)) & 1u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (!on) lg[h][i] = -INFINITY;
+        lmx[h] = fmaxf(lmx[h], lg[h][i]);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int h = 0; h < G; ++h) lmx[h] = fmaxf(lmx[h], __shfl_xor(lmx[h], o, 64));
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s_red[wave][1 + h] = lmx[h];
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
+    __syncthreads();
+  }
   const float smax = smx * (float)(1u << a.r);
   int e2 = 0;
   if (smax > 0.f) (void)frexpf(smax, &e2);
@@ -960,7 +1015,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const float w = __expf(lg[h][i] - msp[h]);
+      const float w = lg[h][i] == -INFINITY ? 0.f : __expf(lg[h][i] - msp[h]);
       s_w[h][tl0 + i] = w;
       const float u = w * sf_h2f(vsz[i]) * uscale;
       const _Float16 hi = (_Float16)u;
@@ -1035,9 +1090,14 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   float hacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) hacc[h][0] = hacc[h][1] = 0.f;
-  const int RW = HD * r / 32;  // value refinement words of a unit (after the key's)
-  for (int j0 = 0; j0 < nh; j0 += PV_HB) {
-    const int nb = min(PV_HB, nh - j0);
+  // nested units: the value's refinement words follow the key's (RW each); fp16
+  // units: the value's HD fp16 values follow the key's (64 words each), and a hit
+  // adds w * (V16 - V_b), V_b rebuilt from the staged resident codes
+  const bool f16u = a.variant == SF_ATTN_FP16_TOKENS;
+  const int RW = f16u ? HD / 2 : HD * r / 32;
+  const int HB = (PV_HB * PV_RWM) / RW;  // hits staged together
+  for (int j0 = 0; j0 < nh; j0 += HB) {
+    const int nb = min(HB, nh - j0);
     constexpr int NPT = (PV_HB * PV_RWM + 255) / 256;  // words a thread stages at most
     uint32_t v[NPT];
 #pragma unroll
@@ -1054,19 +1114,27 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int q = 0; q < NPT; ++q) {
       const int i = tid + 256 * q;
-      if (i < nb * RW) {
-        const int jj = i / RW;
-        s_hr[jj * PV_RWM + (i - jj * RW)] = v[q];
-      }
+      if (i < nb * RW) s_hr[i] = v[q];
     }
     __syncthreads();
     for (int jj = wave; jj < nb; jj += 4) {
       const int t = s_hit[j0 + jj][0], slot = s_hit[j0 + jj][1];
       if (slot < 0 || t < 0 || t >= n_here) continue;
-      const uint32_t* vr = s_hr + jj * PV_RWM;
+      const uint32_t* vr = s_hr + jj * RW;
       const float sv = sf_h2f(s_vsz[t]);
-      const float c0 = sv * (float)field(vr, 2 * lane * r, r);
-      const float c1 = sv * (float)field(vr, (2 * lane + 1) * r, r);
+      float c0, c1;
+      if (f16u) {
+        constexpr uint32_t cm = (1u << B) - 1u;
+        const float st = sv * (float)(1u << r), zv = sf_h2f(s_vsz[t] >> 16);
+        const int d0 = 2 * lane, d1 = 2 * lane + 1;
+        const uint32_t q0 = (s_vc[((d0 * B) >> 5) * CST + t] >> ((d0 * B) & 31)) & cm;
+        const uint32_t q1 = (s_vc[((d1 * B) >> 5) * CST + t] >> ((d1 * B) & 31)) & cm;
+        c0 = h2f16((uint16_t)(vr[lane] & 0xFFFFu)) - fmaf(st, (float)q0, zv);
+        c1 = h2f16((uint16_t)(vr[lane] >> 16)) - fmaf(st, (float)q1, zv);
+      } else {
+        c0 = sv * (float)field(vr, 2 * lane * r, r);
+        c1 = sv * (float)field(vr, (2 * lane + 1) * r, r);
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
@@ -1223,7 +1291,20 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
                                             sf_refine_cache* cache, int32_t pool, float* out,
                                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                             sf_stream stream) {
+  return sf_attn_decode_variant(q_f16, n_q_heads, kv, softmax_scale, k_sel, sel_in, cache, pool, out, sel_out,
+                                hit_out, ws, stream, SF_ATTN_NESTED);
+}
+
+extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
+                                            float softmax_scale, int32_t k_sel, const int32_t* sel_in,
+                                            sf_refine_cache* cache, int32_t pool, float* out,
+                                            int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
+                                            sf_stream stream, int32_t variant) {
   SF_REQUIRE(q_f16 && kv && out && ws, SF_EINVAL, "null argument");
+  SF_REQUIRE(variant == SF_ATTN_NESTED || variant == SF_ATTN_FP16_TOKENS || variant == SF_ATTN_DROP_UNSELECTED,
+             SF_EINVAL, "unknown attention variant");
+  SF_REQUIRE(variant != SF_ATTN_DROP_UNSELECTED || k_sel >= 1, SF_EINVAL,
+             "dropping the unselected tokens needs k_sel >= 1");
   SF_REQUIRE(kv->head_dim == HD, SF_EUNSUPPORTED, "head_dim must be 128");
   SF_REQUIRE(kv->fmt.group == 128 && kv->fmt.b >= 1 && kv->fmt.r >= 0 && kv->fmt.b + kv->fmt.r <= 8,
              SF_EUNSUPPORTED, "bad format");
@@ -1232,7 +1313,7 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
   SF_REQUIRE(kv->t_len >= 1 && kv->t_len <= kv->t_cap, SF_EINVAL, "need 1 <= t_len <= t_cap");
   SF_REQUIRE((int64_t)kv->t_len <= (int64_t)MAX_CHUNKS * CB, SF_EUNSUPPORTED, "t_len above 1048576");
   SF_REQUIRE(k_sel >= 0 && k_sel <= kv->t_len, SF_EINVAL, "k_sel out of range");
-  SF_REQUIRE(k_sel == 0 || kv->fmt.r > 0, SF_EINVAL, "k_sel > 0 needs r > 0");
+  SF_REQUIRE(k_sel == 0 || kv->fmt.r > 0 || variant != SF_ATTN_NESTED, SF_EINVAL, "k_sel > 0 needs r > 0");
   AttnArgs a = {};
   a.q = q_f16;
   a.k_res = kv->k_res;
@@ -1249,6 +1330,7 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
   a.b = kv->fmt.b;
   a.r = kv->fmt.r;
   a.k_sel = k_sel;
+  a.variant = variant;
   a.scale = softmax_scale;
   a.nsa = (a.T + SA - 1) / SA;
   a.s2 = (a.T + CB - 1) / CB;
@@ -1277,7 +1359,9 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
     sf_status st = sf_cache_pool_view(cache, cache ? pool : -1, &a.pool);
     if (st != SF_OK) return st;
     if (a.pool.unit2slot) {
-      SF_REQUIRE(a.pool.unit_bytes == 2 * HD * a.r / 8, SF_EINVAL, "pool unit size is not a KV unit");
+      const int want = variant == SF_ATTN_FP16_TOKENS ? 2 * HD * 2 : 2 * HD * a.r / 8;
+      SF_REQUIRE(a.pool.unit_bytes == want, SF_EINVAL,
+                 "pool unit size is not a KV unit of this variant (nested: 2*128*r/8, fp16 tokens: 512 bytes)");
       SF_REQUIRE(a.pool.n_units >= (int64_t)a.batch * a.n_kv * a.t_cap, SF_EINVAL,
                  "pool has fewer units than batch * n_kv * t_cap");
     }

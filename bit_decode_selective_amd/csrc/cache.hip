@@ -952,6 +952,104 @@ extern "C" sf_status sf_refine_lag_delta(sf_refine_cache* c, int32_t pool, const
   return SF_OK;
 }
 
+namespace {
+
+// FP16 fetch: y[b][n] += sum over the selected channels k whose fp16 column is in a
+// slot of x[b][k] * (w16[n][k] - resident[n][k]).  A thread per output row; the
+// resident code of (n, k) is read from row n of the packed codes.
+__global__ __launch_bounds__(LAG_T) void fp16_fetch_kernel(const uint8_t* slots, int64_t unit_bytes,
+                                                          const uint8_t* res, const uint32_t* sz, int n_out, int k_in,
+                                                          int b, int r, const uint16_t* x, int batch, int k_sel,
+                                                          const int32_t* sel, const int32_t* slot, float* y) {
+  __shared__ int s_k[LAG_LIST], s_s[LAG_LIST];
+  __shared__ int s_n;
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x * LAG_T + tid;
+  const int ngr = k_in / 128;
+  const int64_t row_bytes = (int64_t)k_in * b / 8;
+  const uint32_t cmask = (1u << b) - 1u;
+  float acc[LAG_MAXB];
+#pragma unroll
+  for (int q = 0; q < LAG_MAXB; ++q) acc[q] = 0.f;
+  for (int j0 = 0; j0 < k_sel; j0 += LAG_LIST) {
+    const int jn = min(LAG_LIST, k_sel - j0);
+    __syncthreads();
+    if (tid < 64) {
+      int base = 0;
+      for (int j = tid; j - tid < jn; j += 64) {
+        const int kq = j < jn ? sel[j0 + j] : -1;
+        const int sq = j < jn ? slot[j0 + j] : -1;
+        const bool on = sq >= 0 && kq >= 0 && kq < k_in;
+        const uint64_t m = __ballot(on);
+        const int pos = base + __popcll(m & ((1ull << tid) - 1ull));
+        if (on) {
+          s_k[pos] = kq;
+          s_s[pos] = sq;
+        }
+        base += __popcll(m);
+      }
+      if (tid == 0) s_n = base;
+    }
+    __syncthreads();
+    const int nl = s_n;
+    for (int i0 = 0; i0 < nl; i0 += LAG_U) {
+      float dv[LAG_U];
+      int kk[LAG_U];
+#pragma unroll
+      for (int u = 0; u < LAG_U; ++u) {
+        kk[u] = i0 + u < nl ? s_k[i0 + u] : -1;
+        dv[u] = 0.f;
+        if (kk[u] >= 0 && n < n_out) {
+          const int k = kk[u];
+          const uint16_t w16 = ((const uint16_t*)(slots + (int64_t)s_s[i0 + u] * unit_bytes))[n];
+          const int64_t bit = (int64_t)k * b;
+          const uint8_t* cp = res + (int64_t)n * row_bytes + (bit >> 3);
+          uint32_t cv = cp[0];
+          if ((int)(bit & 7) + b > 8) cv |= (uint32_t)cp[1] << 8;
+          const uint32_t c = (cv >> (bit & 7)) & cmask;
+          const uint32_t w = sz[(int64_t)n * ngr + k / 128];
+          const float st = sf_h2f(w & 0xFFFFu) * (float)(1u << r);
+          dv[u] = sf_h2f(w16) - fmaf(st, (float)c, sf_h2f(w >> 16));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < LAG_U; ++u) {
+        if (kk[u] < 0) break;
+#pragma unroll
+        for (int q = 0; q < LAG_MAXB; ++q)
+          if (q < batch) acc[q] = fmaf(sf_h2f(x[(int64_t)q * k_in + kk[u]]), dv[u], acc[q]);
+      }
+    }
+  }
+  if (n < n_out)
+#pragma unroll
+    for (int q = 0; q < LAG_MAXB; ++q)
+      if (q < batch) y[(int64_t)q * n_out + n] += acc[q];
+}
+
+}  // namespace
+
+extern "C" sf_status sf_fp16_fetch_delta(sf_refine_cache* c, int32_t pool, const sf_qweight* w, const uint16_t* x_f16,
+                                         int32_t batch, int32_t k_sel, const int32_t* sel, const int32_t* slot,
+                                         float* y, sf_stream stream) {
+  SF_REQUIRE(c && w && x_f16 && y, SF_EINVAL, "null argument");
+  SF_REQUIRE(pool >= 0 && pool < (int32_t)c->pools.size(), SF_EINVAL, "pool index out of range");
+  SF_REQUIRE(batch >= 1 && batch <= LAG_MAXB, SF_EINVAL, "batch must be 1..16");
+  SF_REQUIRE(k_sel >= 0 && k_sel <= w->k_in && (k_sel == 0 || (sel && slot)), SF_EINVAL, "bad k_sel / sel / slot");
+  SF_REQUIRE(w->fmt.group == 128 && w->k_in % 128 == 0 && w->n_out > 0 && w->fmt.b >= 1 && w->fmt.b <= 8 &&
+                 w->resident && w->sz,
+             SF_EINVAL, "bad weight");
+  const HostPool& p = c->pools[pool];
+  SF_REQUIRE(p.d.n_units == w->k_in && p.d.unit_bytes == 2 * w->n_out, SF_EINVAL,
+             "the pool's units are not this weight's fp16 columns (n_units = k_in, unit_bytes = 2 * n_out)");
+  if (k_sel == 0 || !p.d_slots) return SF_OK;
+  hipLaunchKernelGGL(fp16_fetch_kernel, dim3((unsigned)((w->n_out + LAG_T - 1) / LAG_T)), dim3(LAG_T), 0,
+                     (hipStream_t)stream, p.d_slots, p.d.unit_bytes, w->resident, w->sz, (int)w->n_out, (int)w->k_in,
+                     (int)w->fmt.b, (int)w->fmt.r, x_f16, (int)batch, (int)k_sel, sel, slot, y);
+  SF_LAUNCH_CHECK();
+  return SF_OK;
+}
+
 extern "C" sf_status sf_refine_cache_io_stats(sf_refine_cache* c, int32_t pool, int64_t* reads, int64_t* bytes,
                                               double* p50_us, double* p99_us, double* read_ms) {
   SF_REQUIRE(c, SF_EINVAL, "null cache");

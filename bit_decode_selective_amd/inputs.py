@@ -23,7 +23,7 @@ import numpy as np
 
 # tensor ids used in seed keys
 Q_PROJ, K_PROJ, V_PROJ, O_PROJ, GATE, UP, DOWN = range(7)
-KV_CACHE, QUERY, OUTLIERS, HIDDEN, TOKENS, EMBED, LM_HEAD, NORM = range(7, 15)
+KV_CACHE, QUERY, OUTLIERS, HIDDEN, TOKENS, EMBED, LM_HEAD, NORM, RANDOM_SEL = range(7, 16)
 KV_HOT_DIMS = 16
 
 
@@ -121,3 +121,20 @@ def torch_kv(gen, batch, n_kv, T, d, hot_dims=4, hot_scale=8.0, device="cuda"):
         dims = torch.randperm(d, generator=gen, device=device)[:hot_dims]
         K[:, h, :, dims] *= hot_scale
     return K, V
+
+
+def random_selection(cfg, layer, tensor, step, n, k):
+    """Random selection (the pages' ablation): k of n unit ids, uniform without
+    replacement, ascending, int32."""
+    g = rng(cfg, layer, tensor, RANDOM_SEL, step)
+    return np.sort(g.choice(n, size=k, replace=False)).astype(np.int32)
+
+
+def random_token_selection(cfg, layer, step, batch, n_kv, T, k):
+    """Random token selection per (batch, kv head): int32 [batch][n_kv][k], each row
+    k of T tokens, uniform without replacement, ascending."""
+    out = np.zeros((batch, n_kv, k), dtype=np.int32)
+    for bi in range(batch):
+        for h in range(n_kv):
+            out[bi, h] = random_selection(cfg, layer, KV_CACHE, step * 1000003 + bi * 4096 + h, T, k)
+    return out

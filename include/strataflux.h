@@ -251,6 +251,18 @@ sf_status sf_refine_lag_delta(sf_refine_cache* c, int32_t pool, const sf_qweight
                               int32_t batch, int32_t k_sel, const int32_t* sel, const int32_t* hit,
                               float* delta_out, sf_stream stream);
 
+/* FP16 fetch, a comparison variant (rag-lover.com StrataFlux summary, "既存手法との
+ * 違い": fetching FP16 values instead of refinement bits).  The pool's units are
+ * w's columns as fp16 (unit k = fp16(W[0..n_out)[k]), 2 * n_out bytes).  After a
+ * resident GEMV that selected sel [k_sel] (sf_refined_gemv with cache NULL and
+ * sel_out) and a lookup of sel in this pool (sf_refine_cache_lookup -> slot), adds
+ * y[b][n] += sum over j with slot[j] >= 0 of x[b][sel[j]] * (w16[n][sel[j]] -
+ * resident[n][sel[j]]), so that the fetched columns hold their fp16 value.
+ * batch 1..16. */
+sf_status sf_fp16_fetch_delta(sf_refine_cache* c, int32_t pool, const sf_qweight* w, const uint16_t* x_f16,
+                              int32_t batch, int32_t k_sel, const int32_t* sel, const int32_t* slot, float* y,
+                              sf_stream stream);
+
 /* Reads of a pool with a store file (pool < 0: all such pools) since creation:
  * units read, bytes read, the median and 99th percentile of one unit's read time
  * (microseconds, over the last 65536 reads), and the wall time fills spent
@@ -332,6 +344,29 @@ sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const
                                  sf_refine_cache* cache, int32_t pool, float* out,
                                  int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                  sf_stream stream);
+
+/* Comparison variants of the refined attention (rag-lover.com StrataFlux summary,
+ * "既存手法との違い": the paper compares nested refinement with SpeCache, which
+ * replaces selected tokens by their FP16 values, and with sparse attention, which
+ * drops the unselected tokens).  Same arguments, selection and cache semantics as
+ * sf_refined_attn_decode; `variant`:
+ *   SF_ATTN_NESTED           sf_refined_attn_decode itself;
+ *   SF_ATTN_FP16_TOKENS      a selected token that hits uses fp16 K and V from its
+ *                            unit (512 bytes: K[0..128) fp16, then V[0..128) fp16)
+ *                            in place of its resident vectors, for its logit and its
+ *                            value; the softmax runs over all tokens (fmt.r may be 0);
+ *   SF_ATTN_DROP_UNSELECTED  only the selected tokens are attended (softmax over
+ *                            them), each at (b+r) bits if it hits, else resident;
+ *                            needs k_sel >= 1.
+ * The pool's units must be of the variant's kind (SF_EINVAL otherwise). */
+#define SF_ATTN_NESTED 0
+#define SF_ATTN_FP16_TOKENS 1
+#define SF_ATTN_DROP_UNSELECTED 2
+sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
+                                 float softmax_scale, int32_t k_sel, const int32_t* sel_in,
+                                 sf_refine_cache* cache, int32_t pool, float* out,
+                                 int32_t* sel_out, int32_t* hit_out, sf_workspace* ws, sf_stream stream,
+                                 int32_t variant);
 
 /* ---- a14: decode-step glue ------------------------------------------------- */
 /* A decoder step around the refined GEMV and attention, after the public
