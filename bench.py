@@ -537,6 +537,85 @@ def layer_chain(args):
     report(model, calls, T, B, args, ms, unref_ms, us, workload, {"channel_selection": sel})
 
 
+def variants_workload(args):
+    """The pages' comparison variants beside nested refinement, per call, each over
+    distinct matrices / layer caches (more bytes than the 256 MB last-level cache):
+    a 4096 -> 14336 2+2-bit GEMV refined on 123 channels (3%) -- nested refinement,
+    random selection, FP16 fetch of the columns -- and attention over 32768 tokens,
+    32 query / 8 KV heads, 656 tokens per KV head (2%) -- nested refinement, random
+    selection, SpeCache-style FP16 tokens, sparse attention over the selected
+    tokens.  Every unit is resident on the device; each variant's calls are captured
+    in a HIP graph and replayed."""
+    import torch
+
+    from bit_decode_selective_amd import binding, inputs
+
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    n_mat, n_kv_layers, T, H, F = 24, 16, args.context, 4096, 14336
+    ks_c, ks_t = k_select(3, H), k_select(2, T)
+    mats = []
+    for i in range(n_mat):
+        W = inputs.torch_weight(g, F, H, device=dev)
+        qw = binding.QuantWeight.from_device(W, 2, 2)
+        u16 = W.t().contiguous().half().view(torch.uint8).reshape(H, -1)
+        del W
+        mats.append((qw, binding.RefineCache([qw.resident_pool_desc()]), binding.RefineCache([binding.device_pool_desc(u16)]),
+                     u16))
+    x = binding._f16_bits(inputs.torch_activation(g, 1, H, torch.randperm(H, generator=g, device=dev)[:41].cpu().numpy(),
+                                                  device=dev), dev)
+    rsel = torch.as_tensor(inputs.random_selection(77, 0, 0, 0, H, ks_c), device=dev)
+    layers = []
+    for i in range(n_kv_layers):
+        K, V = inputs.torch_kv(g, 1, 8, T, HD, device=dev)
+        kv = binding.QuantKV.from_host(K, V, 2, 2)
+        u16 = torch.cat([K, V], dim=-1).half().view(torch.uint8).reshape(-1, 4 * HD)
+        del K, V
+        layers.append((kv, binding.RefineCache([kv.resident_pool_desc()]), binding.RefineCache([binding.device_pool_desc(u16)]),
+                       u16))
+    q = binding._f16_bits(torch.randn((1, 32, HD), generator=g, device=dev).half(), dev)
+    tsel = torch.as_tensor(inputs.random_token_selection(77, 0, 0, 1, 8, T, ks_t), device=dev)
+    sc = 1.0 / math.sqrt(HD)
+    V_ = binding
+    cases = {
+        "gemv_nested": lambda: [V_.refined_gemv([(m[0], 0)], x, ks_c, cache=m[1], want_hits=False) for m in mats],
+        "gemv_random_selection": lambda: [V_.refined_gemv([(m[0], 0)], x, ks_c, cache=m[1], sel_in=rsel, want_hits=False)
+                                          for m in mats],
+        "gemv_fp16_fetch": lambda: [V_.fp16_fetch_gemv(m[0], x, ks_c, m[2], 0) for m in mats],
+        "attn_nested": lambda: [V_.refined_attention(q, L[0], sc, ks_t, cache=L[1]) for L in layers],
+        "attn_random_selection": lambda: [V_.refined_attention(q, L[0], sc, ks_t, cache=L[1], sel_in=tsel) for L in layers],
+        "attn_fp16_tokens": lambda: [V_.refined_attention(q, L[0], sc, ks_t, cache=L[2], variant=V_.SF_ATTN_FP16_TOKENS)
+                                     for L in layers],
+        "attn_sparse": lambda: [V_.refined_attention(q, L[0], sc, ks_t, cache=L[1], variant=V_.SF_ATTN_DROP_UNSELECTED)
+                                for L in layers],
+    }
+    unit = {"gemv_nested": F * 2 // 8, "gemv_random_selection": F * 2 // 8, "gemv_fp16_fetch": F * 2,
+            "attn_nested": 2 * HD * 2 // 8, "attn_random_selection": 2 * HD * 2 // 8, "attn_fp16_tokens": 4 * HD,
+            "attn_sparse": 2 * HD * 2 // 8}
+    stream = torch.cuda.Stream()
+    res = {}
+    for name, fn in cases.items():
+        with torch.cuda.stream(stream):
+            keep = fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            keep = fn()
+        n_calls = n_mat if name.startswith("gemv") else n_kv_layers
+        ms = time_replays(torch, graph, stream, args.steps, args.warmup)
+        per = ms * 1e3 / n_calls
+        sel_units = ks_c if name.startswith("gemv") else 8 * ks_t
+        res[name] = {"us_per_call": round(per, 2), "selected_units": sel_units, "unit_bytes": unit[name],
+                     "selected_bytes": sel_units * unit[name]}
+        print(f"# {name}: {per:.2f} us per call", file=sys.stderr, flush=True)
+        del graph, keep
+    binding.workspace(0, dev).check()
+    print(json.dumps({"workload": "comparison variants (per call, every unit resident)", "context": T,
+                      "gemv": f"{H} -> {F}, 2+2-bit, {ks_c} channels", "attention": f"32q/8kv d128, {ks_t} tokens per "
+                      "KV head", "variants": res}), flush=True)
+
+
 def decode_workload(args):
     """Full greedy decode steps (embedding .. argmax) of a Qwen3-8B-shaped model at
     context 8192 with pools holding 25% of every tensor's refinement units (LRU,
@@ -655,7 +734,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unrefined", action="store_true")
     ap.add_argument("--workload", default="llama8b-step",
-                    choices=["llama8b-step", "llama8b-layers", "qwen3-8b-decode", "llama8b-128k-decode"],
+                    choices=["llama8b-step", "llama8b-layers", "qwen3-8b-decode", "llama8b-128k-decode", "variants"],
                     help="llama8b-step (default): the GEMVs and attention of a Llama-3.1-8B-shaped step with "
                          "synthetic inputs; llama8b-layers: whole decoder layers chained through RMSNorm, RoPE and "
                          "SwiGLU; the others run full decode steps with embedding, lm_head and LRU refinement pools")
@@ -682,6 +761,9 @@ def main():
         return
     if args.workload == "llama8b-layers":
         layer_chain(args)
+        return
+    if args.workload == "variants":
+        variants_workload(args)
         return
     if args.layers == 32:
         args.layers = 0  # the model's own depth
