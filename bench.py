@@ -175,14 +175,23 @@ def time_replays(torch, g, stream, steps, warmup, after=None):
 
 
 def per_call(torch, model, calls, stream, passes, before=None):
-    """Per-tag call durations (us) over `passes` eager passes of the step."""
+    """Per-tag call durations (us) over `passes` eager passes of the step.  Each pass
+    is queued behind a GPU sleep longer than the host needs to enqueue the whole
+    pass, so the events around a call time its kernels, not the host's launches."""
     timer = CallTimer(torch)
     with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        if before is not None:
+            before()
+        model.enqueue(calls, stream)  # untimed: the host's enqueue time of one pass
+        host_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
         for _ in range(passes):
+            torch.cuda._sleep(int(max(host_s, 1e-3) * 4 * 2.4e9))
             if before is not None:
                 before()
             model.enqueue(calls, stream, timer)
-    torch.cuda.synchronize()
+            torch.cuda.synchronize()
     return timer.us()
 
 

@@ -1,6 +1,10 @@
 // Error reporting, version and workspace management of libstrataflux.
 #include <string>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "sf_internal.h"
 
 namespace {
@@ -86,4 +90,25 @@ extern "C" sf_status sf_workspace_set_spin_limit(sf_workspace* ws, uint32_t poll
   SF_HIP(hipDeviceSynchronize());
   SF_HIP(hipMemcpy(ws->base + offsetof(WsControl, spin_limit), &polls, 4, hipMemcpyHostToDevice));
   return SF_OK;
+}
+
+int sf_occupancy(const void* kernel, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int, size_t>, int> memo;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const auto key = std::make_tuple(dev, kernel, threads, lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess || occ < 1) {
+    (void)hipGetLastError();
+    occ = 1;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  memo[key] = occ;
+  return occ;
 }

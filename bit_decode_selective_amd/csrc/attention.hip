@@ -780,7 +780,8 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     const int j = m / G, hh = m - j * G;
     const int t = s_tok[j];
     const bool ok = t >= 0 && t < T;
-    const int slot = (a.pool.unit2slot && ok) ? a.pool.unit2slot[unit0 + t] : -1;
+    // (a resident pool holds unit u in slot u)
+    const int slot = !ok ? -1 : (a.pool.resident ? (int)(unit0 + t) : (a.pool.unit2slot ? a.pool.unit2slot[unit0 + t] : -1));
     float* lp = a.logits + ((size_t)bi * a.n_q + kvh * G + hh) * a.LT + (ok ? t : 0);
     const float l = *lp;
     const float s = sf_h2f(a.k_sz[unit0 + (ok ? t : 0)]);

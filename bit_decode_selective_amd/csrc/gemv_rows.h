@@ -1374,21 +1374,16 @@ sf_status launch_split(GemvArgs a, hipStream_t s) {
   // the tiles wait for workgroup 0 only at their end, but a tile that has to wait
   // for a free slot adds a whole tile time: when the grid does not fit the device
   // at once, the fused kernel (selection in every workgroup) is used instead
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)gemv_split_kernel<C, B, R, NB, D>, 256, lds) !=
-          hipSuccess ||
-      occ < 1)
-    occ = 1;
+  const int occ = sf_occupancy((const void*)gemv_split_kernel<C, B, R, NB, D>, 256, lds);
   // SF_GEMV_SPLIT=2 always takes the staged variant (x in LDS, workgroup 0 selecting)
   const bool staged = env_int("SF_GEMV_SPLIT", 1) == 2;
   if (a.sel_wg && (staged || (long)occ * device_cus() < (long)a.total_tiles + a.sel_wg)) {
     // the staged variant needs fewer registers; else the fused kernel
     constexpr int D2 = R >= 8 ? 1 : (R >= 4 ? 2 : 4);
     const size_t lds2 = fused_sw_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R);
-    int occ2 = 0;
     const void* k2 = a.k_in <= 256 * 8 * 2 ? (const void*)gemv_fused_kernel<C, B, R, NB, D2, 2, true>
                                            : (const void*)gemv_fused_kernel<C, B, R, NB, D2, 8, true>;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ2, k2, 256, lds2) != hipSuccess || occ2 < 1) occ2 = 1;
+    const int occ2 = sf_occupancy(k2, 256, lds2);
     if (a.sel_wg && lds2 <= MAX_DYN_LDS && (staged || (long)occ2 * device_cus() >= (long)a.total_tiles + 1))
       return launch_fused<C, B, R, NB, true>(a, s);
     if (fused_lds_bytes(a.k_in, C::CODES, NB, a.k_sel, R) <= MAX_DYN_LDS) {

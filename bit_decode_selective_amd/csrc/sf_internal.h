@@ -71,6 +71,11 @@ struct PoolDev {
   int64_t n_units;
 };
 
+// Resident workgroups per CU of `kernel` at `threads` threads and `lds` bytes of
+// dynamic LDS on the current device (at least 1), cached per (device, kernel,
+// threads, lds): the query costs microseconds of host time per launch otherwise.
+int sf_occupancy(const void* kernel, int threads, size_t lds);
+
 // Returns the device view of a pool, or a pool that misses everything if c is
 // NULL or pool < 0.  Fails with SF_EINVAL for a bad pool index.
 sf_status sf_cache_pool_view(sf_refine_cache* c, int32_t pool, PoolDev* out);
