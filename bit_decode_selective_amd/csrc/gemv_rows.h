@@ -267,6 +267,25 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
   if (!same || leader) atomicAdd(&h[bin], leader ? (uint32_t)__popcll(m) : 1u);
 }
 
+// Pass 1 of the selection: the top 8 bits of the 8 keys of each active lane into the
+// wave's histogram.  When every active lane holds 8 copies of one key (an all-equal
+// input, e.g. all zeros), one lane adds them all: a wave of same-address LDS atomics
+// serialises; otherwise plain per-key atomics (cheaper than aggregating every key).
+__device__ __forceinline__ void hist_add8(uint32_t* h, const u32x4& kv) {
+  const uint32_t k0 = __builtin_amdgcn_readfirstlane(kv[0]);
+  const bool same = kv[0] == k0 && kv[1] == k0 && kv[2] == k0 && kv[3] == k0 && (k0 & 0xFFFFu) == (k0 >> 16);
+  const uint64_t act = __ballot(true);
+  if (__ballot(same) == act) {
+    if (lanes_below(act) == 0) atomicAdd(&h[(k0 & 0xFFFFu) >> 7], 8u * (uint32_t)__popcll(act));
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    atomicAdd(&h[(kv[q] & 0xFFFFu) >> 7], 1u);
+    atomicAdd(&h[kv[q] >> 23], 1u);
+  }
+}
+
 // Largest bin b of the sum of four per-wave histograms h[w][0..nbin) whose suffix
 // count (bins >= b) reaches `need`; *above = count in bins above b.  Every wave
 // computes it from the histograms itself.  nbin = 256 or 128.
@@ -535,17 +554,15 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
         const int m = m0 + 256 * i + tid;
         if (m < n8) {
           *(u32x4*)(keys + 4 * m) = kv[i];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            hist_add(whist[wave], (kv[i][q] & 0xFFFFu) >> 7);
-            hist_add(whist[wave], kv[i][q] >> 23);
-          }
+          hist_add8(whist[wave], kv[i]);
         }
       }
     }
     lds_barrier();
     int b1, above1;
     wave_threshold4(whist, 256, ks, &b1, &above1);
+    // a crowded boundary bin (all-equal inputs) takes wave-aggregated counts below
+    const bool crowd = (whist[0][b1] + whist[1][b1]) + (whist[2][b1] + whist[3][b1]) > 2048u;
     // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
     // (all taken) and in bin b1
     {
@@ -556,16 +573,22 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
         uint32_t sure = 0u, bnd = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          const int bin = (int)(key >> 7);
-          sure |= (uint32_t)(bin > b1) << e;
-          if (bin == b1) {
-            bnd |= 1u << e;
-            hist_add(whist2[wave], key & 127u);
-          }
+          const uint32_t bin = ((kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 7;
+          sure |= (uint32_t)(bin > (uint32_t)b1) << e;
+          bnd |= (uint32_t)(bin == (uint32_t)b1) << e;
         }
         bs[m] = (uint8_t)sure;
         bb[m] = (uint8_t)bnd;
+        if (crowd) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if ((bnd >> e) & 1u) hist_add(whist2[wave], (kv[e >> 1] >> (16 * (e & 1))) & 127u);
+        } else {
+          for (uint32_t r = bnd; r; r &= r - 1u) {  // the boundary bin's keys (few)
+            const int e = __builtin_ctz(r);
+            atomicAdd(&whist2[wave][(kv[e >> 1] >> (16 * (e & 1))) & 127u], 1u);
+          }
+        }
       }
     }
     lds_barrier();
@@ -905,11 +928,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
       }
       if (!SW && refine && m < n8) *(u32x4*)(keys + 4 * m) = kv;
       if (computed && m < n8)  // selection pass 1: top 8 key bits, one histogram per wave
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          hist_add(whist[wave], (kv[q] & 0xFFFFu) >> 7);
-          hist_add(whist[wave], kv[q] >> 23);
-        }
+        hist_add8(whist[wave], kv);
     }
   };
   stage(xv0, 0);
@@ -935,6 +954,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
       // every wave finds the boundary bin itself (no further barrier)
       int b1, above1;
       wave_threshold4(whist, 256, ks, &b1, &above1);
+      const bool crowd = (whist[0][b1] + whist[1][b1]) + (whist[2][b1] + whist[3][b1]) > 2048u;
       // pass 2: low 7 bits of the keys in bin b1; bitmaps of the keys above bin b1
       // (all taken) and in bin b1 (decided by the low bits)
       {
@@ -945,16 +965,22 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(GemvArgs a) {
           uint32_t sure = 0u, bnd = 0u;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t key = (kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const int bin = (int)(key >> 7);
-            sure |= (uint32_t)(bin > b1) << e;
-            if (bin == b1) {
-              bnd |= 1u << e;
-              hist_add(whist2[wave], key & 127u);
-            }
+            const uint32_t bin = ((kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 7;
+            sure |= (uint32_t)(bin > (uint32_t)b1) << e;
+            bnd |= (uint32_t)(bin == (uint32_t)b1) << e;
           }
           bs[m] = (uint8_t)sure;
           bb[m] = (uint8_t)bnd;
+          if (crowd) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if ((bnd >> e) & 1u) hist_add(whist2[wave], (kv[e >> 1] >> (16 * (e & 1))) & 127u);
+          } else {
+            for (uint32_t r = bnd; r; r &= r - 1u) {  // the boundary bin's keys (few)
+              const int e = __builtin_ctz(r);
+              atomicAdd(&whist2[wave][(kv[e >> 1] >> (16 * (e & 1))) & 127u], 1u);
+            }
+          }
         }
       }
       lds_barrier();
