@@ -125,14 +125,16 @@ struct sf_refine_cache {
   // lookup logs: [u32 count per pool, 256-aligned][per pool: units[cap] | slots[cap]],
   // on the device and mirrored in pinned host memory at the same offsets
   uint8_t* d_logs = nullptr;
-  uint8_t* h_logs = nullptr;
-  uint8_t* h_logs_dev = nullptr;  // the mirror's device address
+  uint8_t* h_logs[2] = {nullptr, nullptr};      // two mirrors (async mode alternates)
+  uint8_t* h_logs_dev[2] = {nullptr, nullptr};  // their device addresses
+  hipEvent_t ev_logs[2] = {nullptr, nullptr};   // a mirror's copy has landed
   size_t logs_bytes = 0;
   LogTab* d_logtab = nullptr;
   PoolTab* d_pooltab = nullptr;
   // fill entries, device and pinned host: [unmaps | maps]
-  uint8_t* d_stage = nullptr;
-  uint8_t* h_stage = nullptr;
+  uint8_t* d_stage[2] = {nullptr, nullptr};  // async mode alternates between the two
+  uint8_t* h_stage[2] = {nullptr, nullptr};
+  int flight_buf = 0;                         // the staging of the fill in flight
   size_t stage_bytes = 0;
   int64_t map_off = 0;
   bool in_flight = false;  // a copy whose map has not been enqueued
@@ -243,11 +245,14 @@ void destroy_cache(sf_refine_cache* c) {
     if (p.fd >= 0) close(p.fd);
   }
   if (c->d_logs) hipFree(c->d_logs);
-  if (c->h_logs) hipHostFree(c->h_logs);
+  for (int i = 0; i < 2; ++i) {
+    if (c->h_logs[i]) hipHostFree(c->h_logs[i]);
+    if (c->d_stage[i]) hipFree(c->d_stage[i]);
+    if (c->h_stage[i]) hipHostFree(c->h_stage[i]);
+    if (c->ev_logs[i]) hipEventDestroy(c->ev_logs[i]);
+  }
   if (c->d_logtab) hipFree(c->d_logtab);
   if (c->d_pooltab) hipFree(c->d_pooltab);
-  if (c->d_stage) hipFree(c->d_stage);
-  if (c->h_stage) hipHostFree(c->h_stage);
   if (c->ev_compute) hipEventDestroy(c->ev_compute);
   if (c->copy_done) hipEventDestroy(c->copy_done);
   delete c;
@@ -381,7 +386,7 @@ sf_status publish(sf_refine_cache* c, hipStream_t compute) {
   SF_HIP(hipStreamWaitEvent(compute, c->copy_done, 0));
   if (c->flight_maps > 0) {
     hipLaunchKernelGGL(map_kernel, dim3((c->flight_maps + 255) / 256), dim3(256), 0, compute, c->d_pooltab,
-                       (const MapEnt*)(c->d_stage + c->map_off), c->flight_maps);
+                       (const MapEnt*)(c->d_stage[c->flight_buf] + c->map_off), c->flight_maps);
     SF_LAUNCH_CHECK();
   }
   c->in_flight = false;
@@ -471,12 +476,17 @@ extern "C" sf_status sf_refine_cache_create(const sf_pool_desc* pools, int32_t n
   CK(hipEventCreateWithFlags(&c->ev_compute, hipEventDisableTiming));
   CK(hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming));
   CK(hipMalloc((void**)&c->d_logs, c->logs_bytes));
-  CK(hipHostMalloc((void**)&c->h_logs, c->logs_bytes, hipHostMallocDefault));
-  CK(hipHostGetDevicePointer((void**)&c->h_logs_dev, c->h_logs, 0));
+  for (int i = 0; i < 2; ++i) {
+    CK(hipHostMalloc((void**)&c->h_logs[i], c->logs_bytes, hipHostMallocDefault));
+    CK(hipHostGetDevicePointer((void**)&c->h_logs_dev[i], c->h_logs[i], 0));
+    CK(hipEventCreateWithFlags(&c->ev_logs[i], hipEventDisableTiming));
+  }
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, 0, (uint32_t*)c->d_logs, n_pools);
   if (stage_ents > 0) {
-    CK(hipMalloc((void**)&c->d_stage, c->stage_bytes));
-    CK(hipHostMalloc((void**)&c->h_stage, c->stage_bytes, hipHostMallocDefault));
+    for (int i = 0; i < 2; ++i) {
+      CK(hipMalloc((void**)&c->d_stage[i], c->stage_bytes));
+      CK(hipHostMalloc((void**)&c->h_stage[i], c->stage_bytes, hipHostMallocDefault));
+    }
   }
   std::vector<LogTab> logtab(n_pools);
   std::vector<PoolTab> pooltab(n_pools);
@@ -587,22 +597,47 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     return SF_OK;
   }
   const int np = (int)c->pools.size();
-  // 1. every pool's lookup log into the pinned mirror (device counts cleared)
-  hipLaunchKernelGGL(logs_to_host_kernel, dim3(np), dim3(256), 0, compute, c->d_logs, c->h_logs_dev,
+  // Async mode lags the policy by one step so that the host never waits for the
+  // step in flight: this call copies step t's logs into one mirror and runs the
+  // policy on step t-1's logs (copied by the previous call, complete once step t-1
+  // has finished); its installs are copied while step t+1 runs and mapped by the
+  // next call, so they serve lookups from step t+2.  Deterministic mode runs the
+  // policy on step t's logs after one wait for the compute stream.
+  const bool lag = c->mode == SF_CACHE_ASYNC;
+  const int cur = lag ? (int)(t & 1) : 0;
+  // 1. every pool's lookup log into a pinned mirror (device counts cleared)
+  hipLaunchKernelGGL(logs_to_host_kernel, dim3(np), dim3(256), 0, compute, c->d_logs, c->h_logs_dev[cur],
                      (const LogTab*)c->d_logtab);
   SF_LAUNCH_CHECK();
-  SF_HIP(hipStreamSynchronize(compute));
-  // 2. async mode: publish the previous fill (its copy must be complete by now,
-  //    and the staging is free again after this wait)
+  if (lag)
+    SF_HIP(hipEventRecord(c->ev_logs[cur], compute));
+  else
+    SF_HIP(hipStreamSynchronize(compute));
+  // 2. async mode: map the previous call's installs behind their copy (a wait of the
+  //    compute stream, not of the host)
   if (c->in_flight) {
-    SF_HIP(hipEventSynchronize(c->copy_done));
     sf_status st = publish(c, compute);
     if (st != SF_OK) return st;
   }
+  int src = cur;  // the mirror the policy reads
+  int64_t tl = t;  // the step whose logs they are
+  if (lag) {
+    if (t == 0) {  // no earlier step to act on yet
+      c->step = 1;
+      if (n_filled) *n_filled = 0;
+      return SF_OK;
+    }
+    src = cur ^ 1;
+    tl = t - 1;
+    // step t-1's logs have landed; so have the entry copies of the call before the
+    // previous one, which used the staging this call writes
+    SF_HIP(hipEventSynchronize(c->ev_logs[src]));
+  }
+  const int sb = cur;  // staging of this call's installs
   // 3. policy of every pool; installs listed in the pinned entry buffer
-  const uint32_t* counts = (const uint32_t*)c->h_logs;
-  UnmapEnt* unm = (UnmapEnt*)c->h_stage;
-  MapEnt* mp = (MapEnt*)(c->h_stage + c->map_off);
+  const uint32_t* counts = (const uint32_t*)c->h_logs[src];
+  UnmapEnt* unm = (UnmapEnt*)c->h_stage[sb];
+  MapEnt* mp = (MapEnt*)(c->h_stage[sb] + c->map_off);
   int32_t n_unmap = 0, n_map = 0;
   bool overflow = false;
   std::vector<FileRead> file_reads;
@@ -613,10 +648,10 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     uint32_t cnt = counts[i] & 0x7FFFFFFFu;
     if (counts[i] & 0x80000000u) overflow = true;
     if (cnt > (uint32_t)p.log_cap) cnt = (uint32_t)p.log_cap;
-    const int32_t* log_u = (const int32_t*)(c->h_logs + p.log_off);
+    const int32_t* log_u = (const int32_t*)(c->h_logs[src] + p.log_off);
     const int32_t* log_s = log_u + p.log_cap;
     const int64_t cap = p.d.capacity;
-    std::vector<int64_t>* now = nullptr;  // bucket of step t
+    std::vector<int64_t>* now = nullptr;  // bucket of step tl
     for (uint32_t e = 0; e < cnt; ++e) {
       const int64_t u = log_u[e];
       const int32_t s = log_s[e];
@@ -626,8 +661,8 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
         ++p.n_hits;
       } else if (s >= 0) {
         ++p.n_hits;
-        p.slot_last[s] = t;
-        if (!now) now = &p.buckets[t];
+        p.slot_last[s] = tl;
+        if (!now) now = &p.buckets[tl];
         now->push_back(u);
         ++p.bucket_entries;
       } else if (p.unit_slot[u] < 0 && !p.pending_flag[u]) {
@@ -646,7 +681,7 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
         slot = p.free_slots.back();
         p.free_slots.pop_back();
       } else {
-        const int64_t victim = pick_victim(p, t);
+        const int64_t victim = pick_victim(p, tl);
         if (victim < 0) continue;
         slot = p.unit_slot[victim];
         p.unit_slot[victim] = -1;
@@ -654,8 +689,8 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
       }
       p.slot_unit[slot] = u;
       p.unit_slot[u] = slot;
-      p.slot_last[slot] = t;
-      if (!now) now = &p.buckets[t];
+      p.slot_last[slot] = tl;
+      if (!now) now = &p.buckets[tl];
       now->push_back(u);
       ++p.bucket_entries;
       mp[n_map] = MapEnt{i, (int32_t)u, slot, (int32_t)n_pool};
@@ -678,23 +713,24 @@ extern "C" sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute_
     // 4. entries and unmaps on the compute stream; the scatter (units read from the
     //    pinned stores) on the side stream once the unmaps are done there
     if (n_unmap > 0)
-      SF_HIP(hipMemcpyAsync(c->d_stage, c->h_stage, sizeof(UnmapEnt) * (size_t)n_unmap, hipMemcpyHostToDevice,
+      SF_HIP(hipMemcpyAsync(c->d_stage[sb], c->h_stage[sb], sizeof(UnmapEnt) * (size_t)n_unmap, hipMemcpyHostToDevice,
                             compute));
-    SF_HIP(hipMemcpyAsync(c->d_stage + c->map_off, c->h_stage + c->map_off, sizeof(MapEnt) * (size_t)n_map,
+    SF_HIP(hipMemcpyAsync(c->d_stage[sb] + c->map_off, c->h_stage[sb] + c->map_off, sizeof(MapEnt) * (size_t)n_map,
                           hipMemcpyHostToDevice, compute));
     if (n_unmap > 0) {
       hipLaunchKernelGGL(unmap_kernel, dim3((n_unmap + 255) / 256), dim3(256), 0, compute, c->d_pooltab,
-                         (const UnmapEnt*)c->d_stage, n_unmap);
+                         (const UnmapEnt*)c->d_stage[sb], n_unmap);
       SF_LAUNCH_CHECK();
     }
     SF_HIP(hipEventRecord(c->ev_compute, compute));
     SF_HIP(hipStreamWaitEvent(side, c->ev_compute, 0));
     hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)std::min(n_map, 4096)), dim3(256), 0, side, c->d_pooltab,
-                       (const MapEnt*)(c->d_stage + c->map_off), n_map);
+                       (const MapEnt*)(c->d_stage[sb] + c->map_off), n_map);
     SF_LAUNCH_CHECK();
     SF_HIP(hipEventRecord(c->copy_done, side));
     c->in_flight = true;
     c->flight_maps = n_map;
+    c->flight_buf = sb;
     if (c->mode == SF_CACHE_DETERMINISTIC) {
       sf_status st = publish(c, compute);
       if (st != SF_OK) return st;

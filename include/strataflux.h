@@ -208,8 +208,11 @@ sf_status sf_refine_cache_lookup(sf_refine_cache* c, int32_t pool, const int32_t
  * one kernel on `side` copies the new units from the pinned host stores into
  * their slots, and they are mapped on `compute` behind that copy.
  * Deterministic mode: returns after the new units are visible to work enqueued
- * later on `compute`.  Async mode: returns after enqueueing; units whose copy
- * finished are published at a later fill call.  n_filled (host, may be NULL):
+ * later on `compute`.  Async mode (the host never waits for the step in flight):
+ * the call at the end of step t copies step t's lookups to the host and runs the
+ * policy on step t-1's (replacement decisions as of step t-1); their copy runs on
+ * `side` behind step t's work and the next call maps them, so they serve lookups
+ * from step t+2 on.  n_filled (host, may be NULL):
  * units installed or queued for install by this call.  SF_ESTATE if a pool's
  * lookups of the step exceeded its max_lookup (the excess was not recorded). */
 sf_status sf_refine_cache_fill(sf_refine_cache* c, sf_stream compute, sf_stream side,
