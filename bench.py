@@ -663,8 +663,15 @@ def decode_workload(args):
         binding.check(binding.lib().sf_refine_cache_fill(model.cache.handle, C.c_void_p(stream.cuda_stream),
                                                          C.c_void_p(model.side.cuda_stream), None))
 
+    # token ids of every step staged on the device up front: a step's copy is device to
+    # device and never waits for the step in flight (a pageable host copy would)
+    n_ids = 2 + args.warmup + 2 * args.steps
+    ids_all = torch.as_tensor(rng.integers(0, spec.vocab, size=(n_ids, args.batch)), dtype=torch.int32).to(model.dev)
+    ids_next = [0]
+
     def new_ids():
-        model.ids.copy_(torch.as_tensor(rng.integers(0, spec.vocab, size=args.batch), dtype=torch.int32))
+        model.ids.copy_(ids_all[ids_next[0] % n_ids], non_blocking=True)
+        ids_next[0] += 1
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
