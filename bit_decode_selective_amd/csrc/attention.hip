@@ -451,9 +451,10 @@ __device__ __forceinline__ void chunk_barrier(uint32_t* ctr, uint32_t n, uint32_
   __syncthreads();
 }
 
-// q_h . cK_lo for the HD r-bit key refinement codes at the start of a unit
-template <int R>
-__device__ __forceinline__ float kref_dot_r(const uint8_t* unit, const float* qh) {
+// q_h . cK_lo for the G heads h, over the HD r-bit key refinement codes at the start
+// of a unit (each code extracted once; dims summed in order)
+template <int G, int R>
+__device__ __forceinline__ void kref_dots_r(const uint8_t* unit, const float (*qf)[HD], float (&dot)[G]) {
   constexpr int NW = HD * R / 32;
   uint32_t w[NW];
   const u32x4* u4 = (const u32x4*)unit;
@@ -462,41 +463,65 @@ __device__ __forceinline__ float kref_dot_r(const uint8_t* unit, const float* qh
     const u32x4 v = u4[i];
     w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
-  float dot = 0.f;
 #pragma unroll
-  for (int i = 0; i < HD; ++i) dot = fmaf(qh[i], (float)((w[(i * R) >> 5] >> ((i * R) & 31)) & ((1u << R) - 1u)), dot);
-  return dot;
+  for (int h = 0; h < G; ++h) dot[h] = 0.f;
+  // one code word per step (the words shift down, so every index is static)
+#pragma unroll 1
+  for (int wi = 0; wi < NW; ++wi) {
+    const uint32_t wv = w[0];
+#pragma unroll
+    for (int k = 0; k + 1 < NW; ++k) w[k] = w[k + 1];
+#pragma unroll
+    for (int e = 0; e < 32 / R; ++e) {
+      const float c = (float)((wv >> (e * R)) & ((1u << R) - 1u));
+      const int i = wi * (32 / R) + e;
+#pragma unroll
+      for (int h = 0; h < G; ++h) dot[h] = fmaf(qf[h][i], c, dot[h]);
+    }
+  }
 }
 
-__device__ __forceinline__ float kref_dot(const uint8_t* unit, int r, const float* qh) {
-  if (r == 2) return kref_dot_r<2>(unit, qh);
-  if (r == 1) return kref_dot_r<1>(unit, qh);
+template <int G>
+__device__ __forceinline__ void kref_dots(const uint8_t* unit, int r, const float (*qf)[HD], float (&dot)[G]) {
+  if (r == 2) return kref_dots_r<G, 2>(unit, qf, dot);
+  if (r == 1) return kref_dots_r<G, 1>(unit, qf, dot);
   const uint32_t* w = (const uint32_t*)unit;
-  float dot = 0.f;
-  for (int i = 0; i < HD; ++i) dot = fmaf(qh[i], (float)field(w, i * r, r), dot);
-  return dot;
+#pragma unroll
+  for (int h = 0; h < G; ++h) dot[h] = 0.f;
+  for (int i = 0; i < HD; ++i) {
+    const float c = (float)field(w, i * r, r);
+#pragma unroll
+    for (int h = 0; h < G; ++h) dot[h] = fmaf(qf[h][i], c, dot[h]);
+  }
 }
 
-// q . K16 over a unit that holds the key as HD fp16 values (then the value's).
-__device__ __forceinline__ float k16_dot(const uint8_t* unit, const float* qh) {
+// q_h . K16 for the G heads h, over a unit that holds the key as HD fp16 values
+// (then the value's)
+template <int G>
+__device__ __forceinline__ void k16_dots(const uint8_t* unit, const float (*qf)[HD], float (&dot)[G]) {
   const u32x4* u4 = (const u32x4*)unit;
-  float dot = 0.f;
-#pragma unroll 4
+#pragma unroll
+  for (int h = 0; h < G; ++h) dot[h] = 0.f;
+#pragma unroll 2
   for (int i = 0; i < HD / 8; ++i) {
     const u32x4 v = u4[i];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dot = fmaf(qh[8 * i + 2 * e], h2f16((uint16_t)(v[e] & 0xFFFFu)), dot);
-      dot = fmaf(qh[8 * i + 2 * e + 1], h2f16((uint16_t)(v[e] >> 16)), dot);
+      const float k0 = h2f16((uint16_t)(v[e] & 0xFFFFu)), k1 = h2f16((uint16_t)(v[e] >> 16));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        dot[h] = fmaf(qf[h][8 * i + 2 * e], k0, dot[h]);
+        dot[h] = fmaf(qf[h][8 * i + 2 * e + 1], k1, dot[h]);
+      }
     }
   }
-  return dot;
 }
 
 template <int G>
 __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   __shared__ uint32_t lh[NBIN];
   __shared__ int s_tok[CB];
+  __shared__ int s_slot[CB];
   __shared__ float qf[G][HD];
   __shared__ float s_m[G], s_iz[G];
   __shared__ float s_wm[SEL_T / 64][G][2];
@@ -766,50 +791,79 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
   cnt = min(max(cnt, 0), min(CB, ks - off));
   __syncthreads();
 
-  // ---- lookups (in selection order) and, for the hits, the logits become
-  //      l' = l + scale * s_K * (q . cK_lo); item m = (selected j, head m % G) ----
+  // ---- lookups, in selection order: every selected token's slot into LDS (all of a
+  //      thread's lookups requested at once) ----
   const size_t unit0 = (size_t)bh * a.t_cap;
   const int base = a.pool.log_count ? (int)sf_get(a.ctl + 5) : -1;
+  {
+    constexpr int NR = CB / SEL_T;  // cnt <= CB: one pass
+    int tk[NR], sl[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int j = tid + SEL_T * i;
+      tk[i] = j < cnt ? s_tok[j] : -1;
+      const bool ok = tk[i] >= 0 && tk[i] < T;
+      // (a resident pool holds unit u in slot u)
+      sl[i] = !ok ? -1
+                  : (a.pool.resident ? (int)(unit0 + tk[i])
+                                     : (a.pool.unit2slot ? a.pool.unit2slot[unit0 + tk[i]] : -1));
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int j = tid + SEL_T * i;
+      if (j >= cnt) continue;
+      const bool ok = tk[i] >= 0 && tk[i] < T;
+      const size_t p = (size_t)bh * ks + off + j;
+      s_slot[j] = sl[i];
+      a.sel_ws[(size_t)bh * KS + off + j] = tk[i];
+      a.slot_ws[(size_t)bh * KS + off + j] = sl[i];
+      if (a.sel_out) a.sel_out[p] = tk[i];
+      if (a.hit_out) a.hit_out[p] = sl[i];
+      if (base >= 0) {
+        a.pool.log_units[base + p] = ok ? (int)(unit0 + tk[i]) : -1;
+        a.pool.log_slots[base + p] = sl[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- for the hits the logits of all G heads become l' = l + scale * s_K *
+  //      (q_h . cK_lo) (one token a thread, its unit read once) ----
   // max after replacement: unselected tokens, selected misses (old logit), hits (new)
   // (dropping the unselected tokens: the max over the selected ones only)
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = a.variant == SF_ATTN_DROP_UNSELECTED ? -INFINITY : mx_uns[h];
 #pragma nounroll
-  for (int m = tid; m < cnt * G; m += SEL_T) {
-    const int j = m / G, hh = m - j * G;
-    const int t = s_tok[j];
-    const bool ok = t >= 0 && t < T;
-    // (a resident pool holds unit u in slot u)
-    const int slot = !ok ? -1 : (a.pool.resident ? (int)(unit0 + t) : (a.pool.unit2slot ? a.pool.unit2slot[unit0 + t] : -1));
-    float* lp = a.logits + ((size_t)bi * a.n_q + kvh * G + hh) * a.LT + (ok ? t : 0);
-    const float l = *lp;
-    const float s = sf_h2f(a.k_sz[unit0 + (ok ? t : 0)]);
-    if (hh == 0) {
-      const size_t p = (size_t)bh * ks + off + j;
-      a.sel_ws[(size_t)bh * KS + off + j] = t;
-      a.slot_ws[(size_t)bh * KS + off + j] = slot;
-      if (a.sel_out) a.sel_out[p] = t;
-      if (a.hit_out) a.hit_out[p] = slot;
-      if (base >= 0) {
-        a.pool.log_units[base + p] = ok ? (int)(unit0 + t) : -1;
-        a.pool.log_slots[base + p] = slot;
-      }
+  for (int j = tid; j < cnt; j += SEL_T) {
+    const int t = s_tok[j], slot = s_slot[j];
+    if (t < 0 || t >= T) continue;
+    float* lp[G];
+    float l[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lp[h] = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + t;
+      l[h] = *lp[h];
     }
     if (slot < 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (h == hh && ok) mloc[h] = fmaxf(mloc[h], l);
+      for (int h = 0; h < G; ++h) mloc[h] = fmaxf(mloc[h], l[h]);
       continue;
     }
+    const float s = sf_h2f(a.k_sz[unit0 + t]);
     const uint8_t* unit = a.pool.slots + (size_t)slot * a.pool.unit_bytes;
+    float dot[G];
     // nested: l + scale * s_K * (q . cK_lo); fp16 tokens: scale * (q . K16)
-    const float l2 = a.variant == SF_ATTN_FP16_TOKENS ? a.scale * k16_dot(unit, qf[hh])
-                                                       : l + a.scale * (s * kref_dot(unit, a.r, qf[hh]));
-    *lp = l2;
+    if (a.variant == SF_ATTN_FP16_TOKENS)
+      k16_dots<G>(unit, qf, dot);
+    else
+      kref_dots<G>(unit, a.r, qf, dot);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      if (h == hh) mloc[h] = fmaxf(mloc[h], l2);
+    for (int h = 0; h < G; ++h) {
+      const float l2 = a.variant == SF_ATTN_FP16_TOKENS ? a.scale * dot[h] : l[h] + a.scale * (s * dot[h]);
+      *lp[h] = l2;
+      mloc[h] = fmaxf(mloc[h], l2);
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
