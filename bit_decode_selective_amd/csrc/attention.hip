@@ -901,15 +901,18 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 
 // ---- pv: final weights, value sums, hit refinements, merge ---------------------------
 // Every load of the workgroup is issued first: its V codes (16 bytes a thread per
-// step), scale words, final logits, the KV head's max, and the selection words that
-// locate this split's hits.  V codes are staged column-major ([code word][token],
-// padded), so a lane's B operand -- one dim of 8 consecutive tokens -- is two
-// 16-byte LDS reads.  The split's hits (token, slot) are gathered into LDS while
-// the weights are formed, and each wave requests the refinement words of all its
-// hits at once.  All splits of a KV head use the same max, so their sums are added
-// into one fp32 record per head (atomically); the last split divides.
-constexpr int PV_HB = 128;  // hits whose value refinement words are staged in LDS together
-constexpr int PV_RWM = 28;  // value refinement words of a unit at most (HD * r / 32, r <= 7)
+// step), scale words, final logits and the KV head's max.  V codes are staged
+// column-major ([code word][token], padded), so a lane's B operand -- one dim of 8
+// consecutive tokens -- is two 16-byte LDS reads.  The refinement of the hits is
+// not done by the split that holds the token: in peaked attention the selection
+// crowds into a few splits, so workgroup s of a KV head takes the equal share
+// [s k / nsp, (s + 1) k / nsp) of the selection positions instead, with weights
+// relative to the KV head's common max; the words of a batch of hits are requested
+// at once.  All splits of a KV head use the same max, so their sums are added into
+// one fp32 record per head (atomically); the last split divides.
+constexpr int PV_HB = 256;   // hits staged in LDS together at most (one a thread)
+constexpr int PV_HW = 1792;  // words of their staging (a batch holds fewer hits when a hit has more)
+constexpr int PV_RWM = 28;   // value refinement words of a nested unit at most (HD * r / 32, r <= 7)
 
 template <int B, int G>
 __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
@@ -919,13 +922,21 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   constexpr int UP = SP + 8;
   constexpr int TPW = SP / 256;          // tokens per thread in the weight phase
   constexpr int NV = SP * WPT / 4 / 256; // 16-byte code loads per thread
-  __shared__ uint32_t s_vc[WPT * CST];
-  __shared__ _Float16 s_u[2 * G][UP];
+  // The V codes and the fp16 weights are dead once the value sums are formed; the
+  // hit staging then reuses the codes' space and the per-wave sums the weights'.
+  constexpr int VC_BYTES = WPT * CST * 4;
+  constexpr int HIT_BYTES = PV_HW * 4 + PV_HB * (G + 2) * 4;
+  constexpr int U_BYTES = 2 * G * UP * 2, ACC_BYTES = 4 * G * HD * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t s_big[VC_BYTES > HIT_BYTES ? VC_BYTES : HIT_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_big2[U_BYTES > ACC_BYTES ? U_BYTES : ACC_BYTES];
+  uint32_t* const s_vc = (uint32_t*)s_big;                                 // [WPT][CST]
+  uint32_t* const s_hr = (uint32_t*)s_big;                                 // [PV_HW] hit words
+  float(*const s_hw)[G] = (float(*)[G])(s_big + PV_HW * 4);                // [PV_HB][G] hit weights
+  int* const s_hslot = (int*)(s_big + PV_HW * 4 + PV_HB * G * 4);          // [PV_HB] slot, -1 = none
+  uint32_t* const s_hsz = (uint32_t*)(s_big + PV_HW * 4 + PV_HB * (G + 1) * 4);  // [PV_HB] scale words
+  _Float16(*const s_u)[UP] = (_Float16(*)[UP])s_big2;                      // [2G][UP]
+  float(*const s_acc)[G][HD] = (float(*)[G][HD])s_big2;                    // [4][G][HD]
   __shared__ uint32_t s_vsz[SP];
-  __shared__ float s_w[G][SP];
-  __shared__ float s_acc[4][G][HD];
-  __shared__ int s_hit[SP][2];
-  __shared__ uint32_t s_hr[PV_HB * PV_RWM];
   __shared__ float s_red[4][3 * G + 1];
   __shared__ float s_st[3 * G + 1];
   __shared__ int s_rng[4][2];
@@ -938,6 +949,20 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   const int t_begin = split * SP, n_here = min(SP, T - t_begin);
   const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
   // ---- loads ----
+  // this workgroup's share of the hits (see the hit section): the first batch's
+  // positions and slots, one a thread, before anything else
+  const int* sel = a.sel_ws + (size_t)bh * a.k_sel;
+  const int* slots = a.slot_ws + (size_t)bh * a.k_sel;
+  const bool f16u = a.variant == SF_ATTN_FP16_TOKENS;
+  const int RW = f16u ? HD / 2 : HD * a.r / 32;  // value words of a unit
+  const int RS = RW + (f16u ? WPT : 0);          // words staged per hit
+  const int HB = min(PV_HB, PV_HW / RS);
+  const int p0 = (int)((long long)split * a.k_sel / a.nsp), p1 = (int)((long long)(split + 1) * a.k_sel / a.nsp);
+  int h_t = -1, h_slot = -1;
+  if (tid < min(HB, p1 - p0)) {
+    h_t = sel[p0 + tid];
+    h_slot = slots[p0 + tid];
+  }
   u32x4 vc[NV];
   {
     const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
@@ -961,15 +986,31 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   float mh[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mh[h] = a.mref[bh * G + h];
-  // selected positions of this split's tokens: [#sel < t_begin, #sel < t_end)
-  const int* sel = a.sel_ws + (size_t)bh * a.k_sel;
-  const int* slots = a.slot_ws + (size_t)bh * a.k_sel;
+  // the first batch's logits, scale words and (nested) refinement words: they land
+  // while the split's own sums are formed
+  float h_l[G];
+  uint32_t h_sz = 0u;
+  u32x4 h_w[PV_RWM / 4];
+  const auto load_hit = [&]() {
+    const bool ok = h_slot >= 0 && h_t >= 0 && h_t < T;
+#pragma unroll
+    for (int h = 0; h < G; ++h) h_l[h] = ok ? a.logits[((size_t)bi * a.n_q + kvh * G + h) * a.LT + h_t] : -INFINITY;
+    h_sz = ok ? a.v_sz[(size_t)bh * a.t_cap + h_t] : 0u;
+    const u32x4* uw = (const u32x4*)(a.pool.slots + (size_t)(ok ? h_slot : 0) * a.pool.unit_bytes) + RW / 4;
+#pragma unroll
+    for (int k = 0; k < PV_RWM / 4; ++k) h_w[k] = ok && !f16u && 4 * k < RW ? uw[k] : u32x4{0u, 0u, 0u, 0u};
+  };
+  load_hit();
+  const bool drop = a.variant == SF_ATTN_DROP_UNSELECTED;
+  // dropping the unselected tokens: the selected positions of this split's tokens,
+  // [#sel < t_begin, #sel < t_end)
   int below0 = 0, below1 = 0;
-  for (int j = tid; j < a.k_sel; j += 256) {
-    const int t = sel[j];
-    below0 += t < t_begin;
-    below1 += t < t_begin + n_here;
-  }
+  if (drop)
+    for (int j = tid; j < a.k_sel; j += 256) {
+      const int t = sel[j];
+      below0 += t < t_begin;
+      below1 += t < t_begin + n_here;
+    }
   // ---- V codes into LDS, column-major ----
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -1013,25 +1054,17 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
   for (int h = 0; h < G; ++h)
     msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
-  const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
-  const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
-  // this split's selected tokens and their slots (the selection ascends): loads now,
-  // LDS writes after the weights
-  int ht[TPW], hsl[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int j = tid + 256 * i;
-    ht[i] = j < nh ? sel[hit_lo + j] - t_begin : -1;
-    hsl[i] = j < nh ? slots[hit_lo + j] : -1;
-  }
-  if (a.variant == SF_ATTN_DROP_UNSELECTED) {
+  if (drop) {
     // only the selected tokens are attended: the others get no weight, and the
-    // split's reference max is taken over the selected ones
+    // split's reference max is taken over the selected ones (the selection ascends)
+    const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
+    const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
     if (tid < SP / 32) s_selm[tid] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      if (tid + 256 * i < nh && ht[i] >= 0 && ht[i] < n_here) atomicOr(&s_selm[ht[i] >> 5], 1u << (ht[i] & 31));
+    for (int j = tid; j < nh; j += 256) {
+      const int t = sel[hit_lo + j] - t_begin;
+      if (t >= 0 && t < n_here) atomicOr(&s_selm[t >> 5], 1u << (t & 31));
+    }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h) lmx[h] = -INFINITY;
@@ -1071,7 +1104,6 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const float w = lg[h][i] == -INFINITY ? 0.f : __expf(lg[h][i] - msp[h]);
-      s_w[h][tl0 + i] = w;
       const float u = w * sf_h2f(vsz[i]) * uscale;
       const _Float16 hi = (_Float16)u;
       const _Float16 lo = (_Float16)((u - (float)hi) * 2048.f);
@@ -1080,13 +1112,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       acc3[3 * h] += w;
       acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
     }
-#pragma unroll
-  for (int i = 0; i < TPW; ++i)
-    if (tid + 256 * i < nh) {
-      s_hit[tid + 256 * i][0] = ht[i];
-      s_hit[tid + 256 * i][1] = hsl[i];
-    }
-  __syncthreads();  // s_u, s_vc, s_vsz, s_w, s_hit written; s_red free
+  __syncthreads();  // s_u, s_vc, s_vsz written; s_red free
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1)
 #pragma unroll
@@ -1095,18 +1121,10 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
 
-  // e^(split max - common max) per head; a hit whose weight times this is 0 in fp32
-  // for every head adds nothing above fp32's smallest value, and its refinement is not
-  // fetched (in very peaked attention the selection ends in tokens of no weight)
+  // e^(split max - common max) per head
   float fsc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
-  const auto live = [&](int t) {
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) any = any || s_w[h][t] * fsc[h] != 0.f;
-    return any;
-  };
 
   const int r = a.r;
   // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
@@ -1138,52 +1156,65 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     }
   }
 
-  // ---- hits in this split: + w * s_V * cV_lo; lane: dims 2l, 2l+1 ----
-  // In batches of PV_HB hits: every thread requests its share of the batch's value
-  // refinement words into LDS at once (one memory latency per batch, however the
-  // hits crowd into this split), then each wave adds the hits w, w + 4, ..
+  // ---- this workgroup's share of the hits: + w * s_V * cV_lo; lane: dims 2l, 2l+1 ----
+  // Positions [p0, p1) of the KV head's selection, in batches of HB (one a thread
+  // while staged).  A hit whose weight is 0 in fp32 for every head adds nothing.
+  // Nested units: the value's refinement words follow the key's (RW each); fp16
+  // units: the value's HD fp16 values follow the key's (64 words), and a hit adds
+  // w * (V16 - V_b), V_b from the token's resident codes (staged after the words).
   float hacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) hacc[h][0] = hacc[h][1] = 0.f;
-  // nested units: the value's refinement words follow the key's (RW each); fp16
-  // units: the value's HD fp16 values follow the key's (64 words each), and a hit
-  // adds w * (V16 - V_b), V_b rebuilt from the staged resident codes
-  const bool f16u = a.variant == SF_ATTN_FP16_TOKENS;
-  const int RW = f16u ? HD / 2 : HD * r / 32;
-  const int HB = (PV_HB * PV_RWM) / RW;  // hits staged together
-  for (int j0 = 0; j0 < nh; j0 += HB) {
-    const int nb = min(HB, nh - j0);
-    constexpr int NPT = (PV_HB * PV_RWM + 255) / 256;  // words a thread stages at most
-    uint32_t v[NPT];
-#pragma unroll
-    for (int q = 0; q < NPT; ++q) {  // every load first, then the LDS writes
-      const int i = tid + 256 * q;
-      v[q] = 0u;
-      if (i < nb * RW) {
-        const int jj = i / RW, w = i - jj * RW;
-        const int t = s_hit[j0 + jj][0], slot = s_hit[j0 + jj][1];
-        if (slot >= 0 && t >= 0 && t < n_here && live(t))
-          v[q] = ((const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes))[RW + w];
+  for (int j0 = p0; j0 < p1; j0 += HB) {
+    const int nb = min(HB, p1 - j0);
+    if (j0 > p0) {  // later batches: requested now
+      h_t = h_slot = -1;
+      if (tid < nb) {
+        h_t = sel[j0 + tid];
+        h_slot = slots[j0 + tid];
       }
+      load_hit();
     }
+    __syncthreads();  // the previous batch's staging has been read
+    if (tid < nb) {
+      bool any = false;
 #pragma unroll
-    for (int q = 0; q < NPT; ++q) {
-      const int i = tid + 256 * q;
-      if (i < nb * RW) s_hr[i] = v[q];
+      for (int h = 0; h < G; ++h) {
+        const float w = h_l[h] == -INFINITY ? 0.f : __expf(h_l[h] - mh[h]);
+        any = any || w != 0.f;
+        s_hw[tid][h] = w;
+      }
+      s_hslot[tid] = any ? h_slot : -1;
+      s_hsz[tid] = h_sz;
+      if (!f16u)
+#pragma unroll
+        for (int k = 0; k < PV_RWM / 4; ++k)
+          if (4 * k < RW) *(u32x4*)(s_hr + tid * RS + 4 * k) = h_w[k];
+    }
+    if (f16u) {
+      __syncthreads();
+      // the value's fp16 words and the token's resident codes of each live hit
+      for (int i = tid; i < nb * RS; i += 256) {
+        const int jj = i / RS, w2 = i - jj * RS;
+        const int slot = s_hslot[jj];
+        if (slot < 0) continue;
+        const int t = sel[j0 + jj];
+        s_hr[i] = w2 < RW ? ((const uint32_t*)(a.pool.slots + (size_t)slot * a.pool.unit_bytes))[RW + w2]
+                          : ((const uint32_t*)(a.v_res + ((size_t)bh * a.t_cap + t) * (HD * B / 8)))[w2 - RW];
+      }
     }
     __syncthreads();
     for (int jj = wave; jj < nb; jj += 4) {
-      const int t = s_hit[j0 + jj][0], slot = s_hit[j0 + jj][1];
-      if (slot < 0 || t < 0 || t >= n_here) continue;
-      const uint32_t* vr = s_hr + jj * RW;
-      const float sv = sf_h2f(s_vsz[t]);
+      if (s_hslot[jj] < 0) continue;
+      const uint32_t* vr = s_hr + jj * RS;
+      const float sv = sf_h2f(s_hsz[jj]);
       float c0, c1;
       if (f16u) {
         constexpr uint32_t cm = (1u << B) - 1u;
-        const float st = sv * (float)(1u << r), zv = sf_h2f(s_vsz[t] >> 16);
+        const float st = sv * (float)(1u << r), zv = sf_h2f(s_hsz[jj] >> 16);
         const int d0 = 2 * lane, d1 = 2 * lane + 1;
-        const uint32_t q0 = (s_vc[((d0 * B) >> 5) * CST + t] >> ((d0 * B) & 31)) & cm;
-        const uint32_t q1 = (s_vc[((d1 * B) >> 5) * CST + t] >> ((d1 * B) & 31)) & cm;
+        const uint32_t q0 = (vr[RW + ((d0 * B) >> 5)] >> ((d0 * B) & 31)) & cm;
+        const uint32_t q1 = (vr[RW + ((d1 * B) >> 5)] >> ((d1 * B) & 31)) & cm;
         c0 = h2f16((uint16_t)(vr[lane] & 0xFFFFu)) - fmaf(st, (float)q0, zv);
         c1 = h2f16((uint16_t)(vr[lane] >> 16)) - fmaf(st, (float)q1, zv);
       } else {
@@ -1192,12 +1223,12 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        hacc[h][0] = fmaf(s_w[h][t], c0, hacc[h][0]);
-        hacc[h][1] = fmaf(s_w[h][t], c1, hacc[h][1]);
+        hacc[h][0] = fmaf(s_hw[jj][h], c0, hacc[h][0]);
+        hacc[h][1] = fmaf(s_hw[jj][h], c1, hacc[h][1]);
       }
     }
-    __syncthreads();
   }
+  __syncthreads();  // every wave is past its reads of s_u and s_hr
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     s_acc[wave][h][2 * lane] = hacc[h][0];
@@ -1220,7 +1251,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       if (h < G) {
         const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1] * (1.f / 2048.f);
         const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
-        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * D + corr),
+        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * D) + corr,
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
