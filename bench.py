@@ -652,7 +652,8 @@ def decode_workload(args):
         store_dir = tempfile.mkdtemp(prefix="sf_refine_store_")
     model = decode.DecodeModel(spec, args.batch, T + 1, src, b=wb, r=wr, kv_b=kvb, kv_r=kvr, ch_pct=ch_pct,
                                tok_pct=tok_pct, pool_frac=frac, cache_mode=mode, store_dir=store_dir,
-                               fetch_lag=args.fetch_lag, fetch_lead=args.fetch_lead)
+                               fetch_lag=args.fetch_lag, fetch_lead=args.fetch_lead,
+                               producer_select=args.producer_select)
     model.fill_kv(T, src)
     print(f"# setup {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     calls, keep = model.build_step(T)
@@ -734,6 +735,8 @@ def decode_workload(args):
         shutil.rmtree(store_dir, ignore_errors=True)
     else:
         res["config"]["weight_refinement_store"] = "pinned host RAM"
+    res["config"]["channel_selection"] = ("by the kernel that produces each GEMV input" if model.producer_select
+                                          else "in each GEMV launch")
     res["config"]["fetch_lag"] = bool(model.fetch_lag)
     res["config"]["fetch_lead"] = bool(model.fetch_lead)
     print(json.dumps(res), flush=True)

@@ -165,43 +165,63 @@ __global__ __launch_bounds__(256) void to_f16_kernel(const float* x, int64_t n, 
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = f2h(x[i]);
 }
 
-// ids[b] = argmax over logits[b] (lowest index among equal maxima; NaN never wins)
-constexpr int AMAX_T = 1024;
+// ids[b] = argmax over logits[b] (lowest index among equal maxima; NaN never wins).
+// One workgroup per row; the row is read as 16-byte vectors, AMAX_U of them in
+// flight per thread, so that a long vocabulary costs a few memory latencies.
+constexpr int AMAX_T = 1024, AMAX_U = 8;
+
+__device__ __forceinline__ void amax_take(float v, int64_t i, float& best, int64_t& bi) {
+  if (v > best || (v == best && (bi < 0 || i < bi))) {
+    best = v;
+    bi = i;
+  }
+}
+
 __global__ __launch_bounds__(AMAX_T) void argmax_kernel(const float* logits, int64_t vocab, int32_t* ids) {
   __shared__ float sv[AMAX_T / 64];
   __shared__ int64_t si[AMAX_T / 64];
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const float* row = logits + (size_t)b * vocab;
   float best = -INFINITY;
   int64_t bi = -1;
-  for (int64_t i = threadIdx.x; i < vocab; i += AMAX_T) {
-    const float v = row[i];
-    if (v > best || (bi < 0 && v == best)) {  // strided ascending: the first of equals stays
-      best = v;
-      bi = i;
+  // scalar head up to 16-byte alignment, then vectors, then the scalar tail
+  const int64_t head = std::min<int64_t>(vocab, (int64_t)((16 - ((uintptr_t)row & 15)) & 15) / 4);
+  if (tid < head) amax_take(row[tid], tid, best, bi);
+  const int64_t nv = (vocab - head) / 4;
+  const float4* rv = (const float4*)(row + head);
+  for (int64_t v0 = 0; v0 < nv; v0 += (int64_t)AMAX_T * AMAX_U) {
+    float4 x[AMAX_U];
+#pragma unroll
+    for (int u = 0; u < AMAX_U; ++u) {
+      const int64_t j = v0 + tid + (int64_t)AMAX_T * u;
+      x[u] = j < nv ? rv[j] : make_float4(NAN, NAN, NAN, NAN);
+    }
+#pragma unroll
+    for (int u = 0; u < AMAX_U; ++u) {
+      const int64_t i0 = head + 4 * (v0 + tid + (int64_t)AMAX_T * u);
+      amax_take(x[u].x, i0, best, bi);
+      amax_take(x[u].y, i0 + 1, best, bi);
+      amax_take(x[u].z, i0 + 2, best, bi);
+      amax_take(x[u].w, i0 + 3, best, bi);
     }
   }
+  const int64_t tail0 = head + 4 * nv;
+  if (tail0 + tid < vocab) amax_take(row[tail0 + tid], tail0 + tid, best, bi);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(best, o, 64);
     const int64_t oi = __shfl_xor(bi, o, 64);
-    if (oi >= 0 && (bi < 0 || ov > best || (ov == best && oi < bi))) {
-      best = ov;
-      bi = oi;
-    }
+    if (oi >= 0) amax_take(ov, oi, best, bi);
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   if (lane == 0) {
     sv[wave] = best;
     si[wave] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     for (int w = 1; w < AMAX_T / 64; ++w)
-      if (si[w] >= 0 && (bi < 0 || sv[w] > best || (sv[w] == best && si[w] < bi))) {
-        best = sv[w];
-        bi = si[w];
-      }
+      if (si[w] >= 0) amax_take(sv[w], si[w], best, bi);
     ids[b] = (int32_t)(bi < 0 ? 0 : bi);
   }
 }

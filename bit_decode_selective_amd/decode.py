@@ -108,8 +108,10 @@ class DecodeModel:
     producer_select
                the kernel that forms each GEMV input also selects its channels
                (sf_add_rmsnorm_select, sf_to_f16_select, sf_swiglu_select) and the
-               GEMV takes that selection as sel_in (batch <= 16); otherwise each GEMV
-               selects its channels itself
+               GEMV takes that selection as sel_in (batch <= 16).  Off by default:
+               each GEMV then selects its channels itself, in one workgroup while
+               the others stream the resident codes, which hides the selection
+               (a producer's selection runs on one workgroup before the GEMV starts)
     store_dir  with pool_frac: weight pools read their units from files in this
                directory (the SSD tier); KV pools stay in pinned host memory
     fetch_lead with pool_frac: at each layer l but the last, layer l + 1's q/k/v and
@@ -125,7 +127,7 @@ class DecodeModel:
     """
 
     def __init__(self, spec, batch, t_cap, src, b=2, r=2, kv_b=2, kv_r=2, ch_pct=3, tok_pct=2, pool_frac=None,
-                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=True,
+                 cache_mode=binding.SF_CACHE_DETERMINISTIC, device="cuda", head=True, producer_select=False,
                  store_dir=None, fetch_lag=False, fetch_lead=False):
         import torch
 

@@ -157,7 +157,7 @@ def _lag_check(model, li, name, x16, quants, what):
 
 
 def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_steps=None, fetch_lag=False,
-               fetch_lead=False):
+               fetch_lead=False, producer_select=False):
     """Teacher-forced decode steps; every operation of every step checked against the
     oracle on the GPU's own inputs.  With pool_frac, the LRU pools of every weight,
     KV cache and lm_head are replayed by the oracle (``cache.LRUPool``): each GEMV's
@@ -167,7 +167,7 @@ def _run_steps(spec, batch, T0, steps, cfg, b=2, r=2, pool_frac=None, output_ste
     every step."""
     src = decode.HostWeights(cfg)
     model = decode.DecodeModel(spec, batch, T0 + steps, src, b=b, r=r, pool_frac=pool_frac, fetch_lag=fetch_lag,
-                               fetch_lead=fetch_lead)
+                               fetch_lead=fetch_lead, producer_select=producer_select)
     assert model.fetch_lag == fetch_lag and model.fetch_lead == fetch_lead
     for li in range(spec.layers):
         for name, t in TENSOR.items():
@@ -302,14 +302,16 @@ TINY_QWEN = decode.Spec("tiny-qwen", 2, 256, 4, 2, 384, 1280, True, 1000000.0, 1
 
 @pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
 @pytest.mark.parametrize("batch", [1, 2])
-def test_decode_steps(spec, batch):
-    _run_steps(spec, batch, 40, 2, 70 + batch)
+@pytest.mark.parametrize("producer_select", [False, True], ids=["gemv-selects", "producer-selects"])
+def test_decode_steps(spec, batch, producer_select):
+    _run_steps(spec, batch, 40, 2, 70 + batch, producer_select=producer_select)
 
 
 @pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
-def test_decode_steps_lru_pools(spec):
+@pytest.mark.parametrize("producer_select", [False, True], ids=["gemv-selects", "producer-selects"])
+def test_decode_steps_lru_pools(spec, producer_select):
     """Small decoders with LRU pools holding 25% of every tensor's units over 8 steps."""
-    _run_steps(spec, 2, 60, 8, 80, pool_frac=0.25)
+    _run_steps(spec, 2, 60, 8, 80, pool_frac=0.25, producer_select=producer_select)
 
 
 @pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
