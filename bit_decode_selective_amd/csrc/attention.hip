@@ -76,6 +76,7 @@ struct AttnArgs {
   float scale;
   float* logits;    // [batch*n_q][LT] (rows padded to 4 floats)
   float* part_a;    // [bh][nsa][G][PW]: split max / sum (+ value sums without refinement)
+  float2* part_ms;  // [bh][nsa][G]: split max / sum again, packed (the select kernel's merge reads these)
   float* part_c;    // [bh][s2][G][PW]: chunk sums (without refinement)
   float* part_p;    // [bh][PV_NR][G][PW]: value sums of the splits (with refinement)
   float* cmax;      // [bh][s2][G]: chunk max of the replaced logits
@@ -383,6 +384,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   if (tid < G) {
     PS[tid * PW + HD] = ms[tid];
     PS[tid * PW + HD + 1] = s_st[3 * tid];
+    a.part_ms[((size_t)bh * a.nsa + split) * G + tid] = make_float2(ms[tid], s_st[3 * tid]);
   }
 }
 
@@ -563,8 +565,14 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
     constexpr int NJ = SEL_T / G;
     const int h = tid % G, j = tid / G;
     float m = -INFINITY, z = 0.f;
-    const float* PA = a.part_a + (size_t)bh * a.nsa * G * PW;
-    for (int s = j; s < a.nsa; s += NJ) merge_ms(m, z, PA[(s * G + h) * PW + HD], PA[(s * G + h) * PW + HD + 1]);
+    const float2* PM = a.part_ms + (size_t)bh * a.nsa * G;
+    for (int s0 = j; s0 < a.nsa; s0 += 4 * NJ) {  // four records requested at once
+      float2 r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r[u] = s0 + u * NJ < a.nsa ? PM[(s0 + u * NJ) * G + h] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) merge_ms(m, z, r[u].x, r[u].y);
+    }
 #pragma unroll
     for (int o = G; o < 64; o <<= 1) merge_ms(m, z, __shfl_xor(m, o, 64), __shfl_xor(z, o, 64));
     if (lane < G) {
@@ -1303,7 +1311,7 @@ size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12
       bh * 3 * NBIN * 4,             // histograms
       bh * 8 * 4,                    // control words
       bh * s2 * 2 * 4,               // chunk counts
-      0};
+      bh * nsa * G * 8};             // split max / sum, compact
   size_t o = sf_align256(sizeof(WsControl));
   for (int i = 0; i < 12; ++i) {
     off[i] = o;
@@ -1436,6 +1444,7 @@ extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_h
   a.hist = (uint32_t*)(w + off[8]);
   a.ctl = (uint32_t*)(w + off[9]);
   a.cnts = (uint32_t*)(w + off[10]);
+  a.part_ms = (float2*)(w + off[11]);
   a.timeout = (uint32_t*)(w + offsetof(WsControl, timeout));
   a.sel_in = sel_in;
   a.sel_out = sel_out;
