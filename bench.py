@@ -53,7 +53,14 @@ SOURCES = ("bit_decode_selective_amd/csrc/gemv_rows.h", "bit_decode_selective_am
 # --pmc runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain copy
 # of known size (--copy-calibration); reported only while the kernel sources have
 # the hash they were measured on, and only for the call they were measured for.
-TRAFFIC = None
+TRAFFIC = {
+    # attn call, T = 32768, 8 KV heads: split + select + pv, medians over 32 calls each
+    # (profiles/decode_step_llama8b_2bit_t32k_hbm_counters.md)
+    "call": "attn",
+    "sources_sha256": "336f8c43eddf9014f3c96b5968a2e1ce8507d0fba357980e111a42932617b8ee",
+    "fetch_bytes": 9620920 + 6849056 + 16890814,
+    "write_bytes": 4690176 + 740656 + 1409024,
+}
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
