@@ -73,6 +73,7 @@ struct AttnArgs {
   const uint32_t* v_sz;
   int batch, n_q, n_kv, G, T, LT, t_cap, b, r, k_sel, nsa, s2, nsp;
   int variant;  // SF_ATTN_NESTED, SF_ATTN_FP16_TOKENS or SF_ATTN_DROP_UNSELECTED
+  int spw;      // pv splits per workgroup
   float scale;
   float* logits;    // [batch*n_q][LT] (rows padded to 4 floats)
   float* part_a;    // [bh][nsa][G][PW]: split max / sum (+ value sums without refinement)
@@ -951,11 +952,11 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   __shared__ int s_flag;
   __shared__ uint32_t s_selm[SP / 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, bh = blockIdx.y;
+  const int bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
   const int T = a.T;
-  const int t_begin = split * SP, n_here = min(SP, T - t_begin);
-  const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
+  // this workgroup's splits [sp0, sp1) (one, unless the grid would not fit at once)
+  const int sp0 = blockIdx.x * a.spw, sp1 = min(a.nsp, sp0 + a.spw);
   // ---- loads ----
   // this workgroup's share of the hits (see the hit section): the first batch's
   // positions and slots, one a thread, before anything else
@@ -965,37 +966,41 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   const int RW = f16u ? HD / 2 : HD * a.r / 32;  // value words of a unit
   const int RS = RW + (f16u ? WPT : 0);          // words staged per hit
   const int HB = min(PV_HB, PV_HW / RS);
-  const int p0 = (int)((long long)split * a.k_sel / a.nsp), p1 = (int)((long long)(split + 1) * a.k_sel / a.nsp);
+  const int p0 = (int)((long long)sp0 * a.k_sel / a.nsp), p1 = (int)((long long)sp1 * a.k_sel / a.nsp);
   int h_t = -1, h_slot = -1;
   if (tid < min(HB, p1 - p0)) {
     h_t = sel[p0 + tid];
     h_slot = slots[p0 + tid];
   }
+  // one split's V codes (16 bytes a thread per step), scale words and final logits
+  const int tl0 = TPW * tid;  // this thread's first token within a split
   u32x4 vc[NV];
-  {
+  uint32_t vsz[TPW];
+  float lg[G][TPW];
+  const auto load_split = [&](int split) {
+    const int t_begin = split * SP, n_here = min(SP, T - t_begin);
+    const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
     const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = tid + 256 * i;
       vc[i] = idx < n_here * WPT / 4 ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  const int tl0 = TPW * tid;  // this thread's first token within the split
-  uint32_t vsz[TPW];
-  float lg[G][TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) vsz[i] = tl0 + i < n_here ? a.v_sz[tok0 + tl0 + i] : 0u;
+    for (int i = 0; i < TPW; ++i) vsz[i] = tl0 + i < n_here ? a.v_sz[tok0 + tl0 + i] : 0u;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + t_begin + tl0;
+    for (int h = 0; h < G; ++h) {
+      const float* lr = a.logits + ((size_t)bi * a.n_q + kvh * G + h) * a.LT + t_begin + tl0;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) lg[h][i] = tl0 + i < n_here ? lr[i] : -INFINITY;
-  }
+      for (int i = 0; i < TPW; ++i) lg[h][i] = tl0 + i < n_here ? lr[i] : -INFINITY;
+    }
+  };
+  load_split(sp0);
   float mh[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mh[h] = a.mref[bh * G + h];
   // the first batch's logits, scale words and (nested) refinement words: they land
-  // while the split's own sums are formed
+  // while the splits' own sums are formed
   float h_l[G];
   uint32_t h_sz = 0u;
   u32x4 h_w[PV_RWM / 4];
@@ -1010,157 +1015,196 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
   };
   load_hit();
   const bool drop = a.variant == SF_ATTN_DROP_UNSELECTED;
-  // dropping the unselected tokens: the selected positions of this split's tokens,
-  // [#sel < t_begin, #sel < t_end)
-  int below0 = 0, below1 = 0;
-  if (drop)
-    for (int j = tid; j < a.k_sel; j += 256) {
-      const int t = sel[j];
-      below0 += t < t_begin;
-      below1 += t < t_begin + n_here;
+  const int r = a.r;
+  const int n = lane & 15, qg = lane >> 4;
+  constexpr uint32_t cmask = (1u << B) - 1u;
+  // this workgroup's value sums (lane: dims 32 wave + 16 db + n of heads 2 qg + hh)
+  // and weight sums (thread h < G), each split's rescaled to the common max
+  float accv[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, accz = 0.f;
+  for (int split = sp0; split < sp1; ++split) {
+    const int t_begin = split * SP, n_here = min(SP, T - t_begin);
+    if (split > sp0) __syncthreads();  // the previous split's LDS reads are done
+    // dropping the unselected tokens: the selected positions of this split's
+    // tokens, [#sel < t_begin, #sel < t_end)
+    int below0 = 0, below1 = 0;
+    if (drop)
+      for (int j = tid; j < a.k_sel; j += 256) {
+        const int t = sel[j];
+        below0 += t < t_begin;
+        below1 += t < t_begin + n_here;
+      }
+    // ---- V codes into LDS, column-major ----
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int w = 4 * (tid + 256 * i), tk = w / WPT, c = w - tk * WPT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_vc[(c + e) * CST + tk] = vc[i][e];
     }
-  // ---- V codes into LDS, column-major ----
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int w = 4 * (tid + 256 * i), tk = w / WPT, c = w - tk * WPT;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s_vc[(c + e) * CST + tk] = vc[i][e];
-  }
-  // largest value scale of the split, the split's max logit per head, the hit range
-  float smx = 0.f, lmx[G];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    s_vsz[tl0 + i] = vsz[i];
-    smx = fmaxf(smx, sf_h2f(vsz[i]));
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lmx[h] = lg[h][0];
-#pragma unroll
-    for (int i = 1; i < TPW; ++i) lmx[h] = fmaxf(lmx[h], lg[h][i]);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    smx = fmaxf(smx, __shfl_xor(smx, o, 64));
-#pragma unroll
-    for (int h = 0; h < G; ++h) lmx[h] = fmaxf(lmx[h], __shfl_xor(lmx[h], o, 64));
-    below0 += __shfl_xor(below0, o, 64);
-    below1 += __shfl_xor(below1, o, 64);
-  }
-  if (lane == 0) {
-    s_red[wave][0] = smx;
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_red[wave][1 + h] = lmx[h];
-    s_rng[wave][0] = below0;
-    s_rng[wave][1] = below1;
-  }
-  __syncthreads();
-  smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
-  // weights relative to the split's own max (full fp16 precision in the value sums);
-  // the sums are rescaled to the KV head's common max before they are added
-  float msp[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
-  if (drop) {
-    // only the selected tokens are attended: the others get no weight, and the
-    // split's reference max is taken over the selected ones (the selection ascends)
-    const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
-    const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
-    if (tid < SP / 32) s_selm[tid] = 0u;
-    __syncthreads();
-    for (int j = tid; j < nh; j += 256) {
-      const int t = sel[hit_lo + j] - t_begin;
-      if (t >= 0 && t < n_here) atomicOr(&s_selm[t >> 5], 1u << (t & 31));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) lmx[h] = -INFINITY;
+    // largest value scale of the split, the split's max logit per head, the hit range
+    float smx = 0.f, lmx[G];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int t = tl0 + i;
-      const bool on = t < n_here && ((s_selm[t >> 5] >> (t & 31)) & 1u);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (!on) lg[h][i] = -INFINITY;
-        lmx[h] = fmaxf(lmx[h], lg[h][i]);
-      }
+      s_vsz[tl0 + i] = vsz[i];
+      smx = fmaxf(smx, sf_h2f(vsz[i]));
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int h = 0; h < G; ++h) {
+      lmx[h] = lg[h][0];
+#pragma unroll
+      for (int i = 1; i < TPW; ++i) lmx[h] = fmaxf(lmx[h], lg[h][i]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      smx = fmaxf(smx, __shfl_xor(smx, o, 64));
 #pragma unroll
       for (int h = 0; h < G; ++h) lmx[h] = fmaxf(lmx[h], __shfl_xor(lmx[h], o, 64));
-    if (lane == 0)
+      below0 += __shfl_xor(below0, o, 64);
+      below1 += __shfl_xor(below1, o, 64);
+    }
+    if (lane == 0) {
+      s_red[wave][0] = smx;
 #pragma unroll
       for (int h = 0; h < G; ++h) s_red[wave][1 + h] = lmx[h];
+      s_rng[wave][0] = below0;
+      s_rng[wave][1] = below1;
+    }
     __syncthreads();
+    smx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
+    // weights relative to the split's own max (full fp16 precision in the value
+    // sums); the sums are rescaled to the KV head's common max before they are added
+    float msp[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
       msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
-    __syncthreads();
-  }
-  const float smax = smx * (float)(1u << a.r);
-  int e2 = 0;
-  if (smax > 0.f) (void)frexpf(smax, &e2);
-  const int shift = smax > 0.f ? 14 - e2 : 0;
-  const float uscale = ldexpf((float)(1u << a.r), shift);
-  float acc3[3 * G];
+    if (drop) {
+      // only the selected tokens are attended: the others get no weight, and the
+      // split's reference max is taken over the selected ones (the selection ascends)
+      const int hit_lo = (s_rng[0][0] + s_rng[1][0]) + (s_rng[2][0] + s_rng[3][0]);
+      const int nh = min((s_rng[0][1] + s_rng[1][1]) + (s_rng[2][1] + s_rng[3][1]) - hit_lo, SP);
+      if (tid < SP / 32) s_selm[tid] = 0u;
+      __syncthreads();
+      for (int j = tid; j < nh; j += 256) {
+        const int t = sel[hit_lo + j] - t_begin;
+        if (t >= 0 && t < n_here) atomicOr(&s_selm[t >> 5], 1u << (t & 31));
+      }
+      __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 3 * G; ++i) acc3[i] = 0.f;
+      for (int h = 0; h < G; ++h) lmx[h] = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+      for (int i = 0; i < TPW; ++i) {
+        const int t = tl0 + i;
+        const bool on = t < n_here && ((s_selm[t >> 5] >> (t & 31)) & 1u);
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const float w = lg[h][i] == -INFINITY ? 0.f : __expf(lg[h][i] - msp[h]);
-      const float u = w * sf_h2f(vsz[i]) * uscale;
-      const _Float16 hi = (_Float16)u;
-      const _Float16 lo = (_Float16)((u - (float)hi) * 2048.f);
-      s_u[2 * h][tl0 + i] = hi;
-      s_u[2 * h + 1][tl0 + i] = lo;
-      acc3[3 * h] += w;
-      acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
+        for (int h = 0; h < G; ++h) {
+          if (!on) lg[h][i] = -INFINITY;
+          lmx[h] = fmaxf(lmx[h], lg[h][i]);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h) lmx[h] = fmaxf(lmx[h], __shfl_xor(lmx[h], o, 64));
+      if (lane == 0)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_red[wave][1 + h] = lmx[h];
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        msp[h] = fmaxf(fmaxf(s_red[0][1 + h], s_red[1][1 + h]), fmaxf(s_red[2][1 + h], s_red[3][1 + h]));
+      __syncthreads();
     }
-  __syncthreads();  // s_u, s_vc, s_vsz written; s_red free
+    const float smax = smx * (float)(1u << r);
+    int e2 = 0;
+    if (smax > 0.f) (void)frexpf(smax, &e2);
+    const int shift = smax > 0.f ? 14 - e2 : 0;
+    const float uscale = ldexpf((float)(1u << r), shift);
+    float acc3[3 * G];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
+    for (int i = 0; i < 3 * G; ++i) acc3[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 3 * G; ++i) acc3[i] += __shfl_xor(acc3[i], o, 64);
-  if (lane == 0)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
+      for (int i = 0; i < TPW; ++i) {
+        const float w = lg[h][i] == -INFINITY ? 0.f : __expf(lg[h][i] - msp[h]);
+        const float u = w * sf_h2f(vsz[i]) * uscale;
+        const _Float16 hi = (_Float16)u;
+        const _Float16 lo = (_Float16)((u - (float)hi) * 2048.f);
+        s_u[2 * h][tl0 + i] = hi;
+        s_u[2 * h + 1][tl0 + i] = lo;
+        acc3[3 * h] += w;
+        acc3[3 * h + 1] = fmaf(w, sf_h2f(vsz[i] >> 16), acc3[3 * h + 1]);
+      }
+    // the next split's loads go out now and land during this split's value sums
+    if (split + 1 < sp1) load_split(split + 1);
+    __syncthreads();  // s_u, s_vc, s_vsz written; s_red free
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int i = 0; i < 3 * G; ++i) acc3[i] += __shfl_xor(acc3[i], o, 64);
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < 3 * G; ++i) s_red[wave][i] = acc3[i];
 
-  // e^(split max - common max) per head
-  float fsc[G];
+    // e^(split max - common max) per head
+    float fsc[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
+    for (int h = 0; h < G; ++h) fsc[h] = msp[h] > -INFINITY ? __expf(msp[h] - mh[h]) : 0.f;
 
-  const int r = a.r;
-  // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
-  const int n = lane & 15, qg = lane >> 4;
-  constexpr uint32_t cmask = (1u << B) - 1u;
-  f4_t pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // ---- value sums on MFMA; wave w: dims [32w, 32w+32) as two 16-dim blocks ----
+    f4_t pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
-  for (int kb = 0; kb < SP / 32; ++kb) {
-    const int tk0 = 32 * kb + 8 * qg;
-    h8_t av;
-    if (n < 2 * G) {
-      av = *(const h8_t*)(&s_u[n][tk0]);
-    } else {
+    for (int kb = 0; kb < SP / 32; ++kb) {
+      const int tk0 = 32 * kb + 8 * qg;
+      h8_t av;
+      if (n < 2 * G) {
+        av = *(const h8_t*)(&s_u[n][tk0]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = (_Float16)0.f;
+        for (int e = 0; e < 8; ++e) av[e] = (_Float16)0.f;
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int d = 32 * wave + 16 * db + n;
+        const int bit = d * B, wi = bit >> 5, sh = bit & 31;
+        const u32x4 w0 = *(const u32x4*)(s_vc + wi * CST + tk0);
+        const u32x4 w1 = *(const u32x4*)(s_vc + wi * CST + tk0 + 4);
+        const uint32_t c[8] = {(w0.x >> sh) & cmask, (w0.y >> sh) & cmask, (w0.z >> sh) & cmask,
+                               (w0.w >> sh) & cmask, (w1.x >> sh) & cmask, (w1.y >> sh) & cmask,
+                               (w1.z >> sh) & cmask, (w1.w >> sh) & cmask};
+        u32x4 bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = code_pair<B>(c[2 * e], c[2 * e + 1]);
+        pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
+      }
     }
+    __syncthreads();  // s_red
+    if (tid < 3 * G) s_st[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
+    __syncthreads();
+    // lane group qg holds rows 4qg..4qg+3 = head 2qg (rows 0, 1) and head 2qg+1 (rows 2, 3)
+    const float back = ldexpf(1.f, B - shift);  // 2^B undoes the c/2^B form, 2^-shift the scaling
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int d = 32 * wave + 16 * db + n;
-      const int bit = d * B, wi = bit >> 5, sh = bit & 31;
-      const u32x4 w0 = *(const u32x4*)(s_vc + wi * CST + tk0);
-      const u32x4 w1 = *(const u32x4*)(s_vc + wi * CST + tk0 + 4);
-      const uint32_t c[8] = {(w0.x >> sh) & cmask, (w0.y >> sh) & cmask, (w0.z >> sh) & cmask, (w0.w >> sh) & cmask,
-                             (w1.x >> sh) & cmask, (w1.y >> sh) & cmask, (w1.z >> sh) & cmask, (w1.w >> sh) & cmask};
-      u32x4 bv;
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = code_pair<B>(c[2 * e], c[2 * e + 1]);
-      pacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8_t, bv), pacc[db], 0, 0, 0);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * qg + hh;
+        if (h < G) {
+          float fh = fsc[0], sth = s_st[1];
+#pragma unroll
+          for (int h2 = 1; h2 < G; ++h2)
+            if (h2 == h) {
+              fh = fsc[h2];
+              sth = s_st[3 * h2 + 1];
+            }
+          const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1] * (1.f / 2048.f);
+          accv[db][hh] = fmaf(fh, sth + back * D, accv[db][hh]);
+        }
+      }
+    if (tid < G) {
+      float ft = fsc[0];
+#pragma unroll
+      for (int h2 = 1; h2 < G; ++h2)
+        if (h2 == tid) ft = fsc[h2];
+      accz = fmaf(ft, s_st[3 * tid], accz);
     }
   }
 
@@ -1242,14 +1286,11 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     s_acc[wave][h][2 * lane] = hacc[h][0];
     s_acc[wave][h][2 * lane + 1] = hacc[h][1];
   }
-  __syncthreads();  // s_red, s_acc
-  if (tid < 3 * G) s_st[tid] = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
-  __syncthreads();
-  // this split's sums, added into one of the KV head's records [PV_NR][G][PW] (zeroed
-  // by the split launch; several records keep the number of adds per address small)
+  __syncthreads();  // s_acc
+  // this workgroup's sums, added into one of the KV head's records [PV_NR][G][PW]
+  // (zeroed by the split launch; several records keep the adds per address few)
   float* PB = a.part_p + (size_t)bh * PV_NR * G * PW;
-  float* PP = PB + (size_t)(split % PV_NR) * G * PW;
-  const float back = ldexpf(1.f, B - shift);
+  float* PP = PB + (size_t)(blockIdx.x % PV_NR) * G * PW;
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = 32 * wave + 16 * db + n;
@@ -1257,24 +1298,22 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int h = 2 * qg + hh;
       if (h < G) {
-        const float D = pacc[db][2 * hh] + pacc[db][2 * hh + 1] * (1.f / 2048.f);
         const float corr = (s_acc[0][h][d] + s_acc[1][h][d]) + (s_acc[2][h][d] + s_acc[3][h][d]);
-        (void)__hip_atomic_fetch_add(PP + h * PW + d, fsc[h] * (s_st[3 * h + 1] + back * D) + corr,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        (void)__hip_atomic_fetch_add(PP + h * PW + d, accv[db][hh] + corr, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (tid < G)
-    (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, fsc[tid] * s_st[3 * tid], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    (void)__hip_atomic_fetch_add(PP + tid * PW + HD + 1, accz, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   sf_drain();
   __syncthreads();
   if (tid == 0)
     s_flag = sf_add_acq_rel(a.ctl + bh * 8 + 6, 1u) ==
-             (uint32_t)(a.nsp - 1);
+             (uint32_t)(gridDim.x - 1);
   __syncthreads();
   if (!s_flag) return;
-  // last split of this KV head: out = N / z over the records
+  // last workgroup of this KV head: out = N / z over the records
   for (int i = tid; i < G * HD; i += 256) {
     const int h = i / HD, d = i - h * HD;
     float vn[PV_NR], vz[PV_NR];
@@ -1354,7 +1393,12 @@ sf_status launch_attn(AttnArgs& a, hipStream_t s) {
   SF_LAUNCH_CHECK();
   hipLaunchKernelGGL((attn_select_kernel<G>), dim3(a.s2, bh), dim3(SEL_T), 0, s, a);
   SF_LAUNCH_CHECK();
-  hipLaunchKernelGGL((attn_pv_kernel<B, G>), dim3(a.nsp, bh), dim3(256), 0, s, a);
+  // pv: one split a workgroup, unless the grid would not fit the device at once;
+  // then each workgroup takes consecutive splits (their loads overlap the previous
+  // split's value sums)
+  const long pv_cap = (long)std::max(1, sf_occupancy((const void*)attn_pv_kernel<B, G>, 256, 0)) * attn_device_cus();
+  a.spw = (int)std::max<long>(1, ((long)a.nsp * bh + pv_cap - 1) / pv_cap);
+  hipLaunchKernelGGL((attn_pv_kernel<B, G>), dim3((a.nsp + a.spw - 1) / a.spw, bh), dim3(256), 0, s, a);
   SF_LAUNCH_CHECK();
   return SF_OK;
 }
