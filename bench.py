@@ -3,10 +3,10 @@
 
 Default workload (llama8b-step): the GEMVs and attention of one decode step of a
 Llama-3.1-8B-shaped model at batch 1, 32 layers, each:
-  KV append (the new token quantised into the 2+2-bit cache),
   q/k/v refined GEMV (one fused launch, top 3% input channels refined),
-  refined GQA attention over the 32768-token context (32 query / 8 KV heads, head
-  dim 128, top 2% tokens refined),
+  KV append (the new token quantised into the 2+2-bit cache) and refined GQA
+  attention over the 32768-token context (32 query / 8 KV heads, head dim 128, top
+  2% tokens refined) in one call,
   o refined GEMV, gate/up refined GEMV (one fused launch), down refined GEMV.
 Every GEMV input is a seeded synthetic fp16 vector, N(0, 1) with 1% of channels
 x20; W ~ N(0, 0.02); K and V ~ N(0, 1) with 4 dims of K x8; q ~ N(0, 1) (no trained
@@ -114,8 +114,9 @@ def call_bytes(model, tag, T, refined):
         return gemv_bytes([H], S.ffn, ks(S.ffn), model.b, model.r, B)
     if tag == "lm_head":
         return gemv_bytes([S.vocab], H, ks(H), model.b, model.r, B)
-    if tag == "attn":
-        return attn_bytes(T, kt, model.kv_b, model.kv_r, B, S.n_q, S.n_kv)
+    if tag == "attn":  # with the new token's append (one call)
+        return attn_bytes(T, kt, model.kv_b, model.kv_r, B, S.n_q, S.n_kv) + append_bytes(model.kv_b, model.kv_r, B,
+                                                                                           S.n_kv)
     if tag == "append":
         return append_bytes(model.kv_b, model.kv_r, B, S.n_kv)
     if tag == "norm":  # h (+ y) read, h written, gains, x written, selection
@@ -222,7 +223,7 @@ def call_table(model, calls, T, refined, us):
 KERNELS = {  # the kernels one call of a tag launches (batch 1-2)
     "qkv": "gemv_split_kernel", "o": "gemv_split_kernel", "down": "gemv_split_kernel",
     "gateup": "gemv_split_kernel", "lm_head": "gemv_split_kernel",
-    "attn": "attn_split_kernel + attn_select_kernel + attn_pv_kernel",
+    "attn": "attn_split_kernel (appending the new token) + attn_select_kernel + attn_pv_kernel",
     "norm": "produce_select_kernel<PROD_NORM>", "cast": "produce_select_kernel<PROD_CAST>",
     "swiglu": "produce_select_kernel<PROD_SWIGLU>", "rope": "qk_rope_kernel", "append": "kv_append_kernel",
 }
@@ -287,8 +288,9 @@ def cpu_baseline(T, ch_pct, tok_pct, b, r, gemv_step_bytes, attn_step_bytes, bat
 class SyntheticStep:
     """The default workload: 32 Llama-3.1-8B-shaped layers with synthetic GEMV inputs.
 
-    Per layer, in launch order: KV append of the new token, the q/k/v GEMVs (one fused
-    launch over one input), refined attention over the layer's own cache, o, gate/up
+    Per layer, in launch order: the q/k/v GEMVs (one fused launch over one input),
+    the new token's KV append and refined attention over the layer's own cache (one
+    call), o, gate/up
     (one fused launch), down.  Every GEMV input is its own seeded fp16 vector of
     N(0, 1) with 1% of channels x20 (the GEMV configuration's activations), so each
     GEMV selects its own channels; q ~ N(0, 1); K and V ~ N(0, 1) with 4 dims of K x8.
@@ -369,11 +371,7 @@ class SyntheticStep:
         for li in range(self.layers):
             kv, kv_pool = self.kvs[li]
             Kn, Vn = self.knew[li]
-            dsc_app = kv.desc(T - 1)
-            keep.append(dsc_app)
             dst = kv.refine.data_ptr() + (T - 1) * kv.unit_bytes
-            calls.append((L.sf_kv_append, (C.c_void_p(Kn.data_ptr()), C.c_void_p(Vn.data_ptr()), 1, T - 1,
-                                           C.byref(dsc_app), C.c_void_p(dst), kv.t_cap, None), "append"))
             for gi, (tag, ops, k_in) in enumerate(self.groups[li]):
                 ks = k_select(self.ch_pct, k_in) if refined else 0
                 arr = (b.sf_gemv_op * len(ops))(*[b.sf_gemv_op(w.desc(), p, self.y[li][gi][i].data_ptr(), None)
@@ -385,8 +383,10 @@ class SyntheticStep:
                     dsc = kv.desc(T)
                     keep.append(dsc)
                     kt = k_select(self.tok_pct, T) if refined else 0
-                    calls.append((L.sf_refined_attn_decode,
-                                  (C.c_void_p(self.q[li].data_ptr()), S.n_q, C.byref(dsc), 1.0 / math.sqrt(HD), kt,
+                    # the new token's KV append and the attention in one call
+                    calls.append((L.sf_refined_attn_decode_append,
+                                  (C.c_void_p(self.q[li].data_ptr()), S.n_q, C.byref(dsc), C.c_void_p(Kn.data_ptr()),
+                                   C.c_void_p(Vn.data_ptr()), C.c_void_p(dst), kv.t_cap, 1.0 / math.sqrt(HD), kt,
                                    None, self.cache.handle, kv_pool, C.c_void_p(self.out[li].data_ptr()), None, None,
                                    self.ws.handle, None), "attn"))
         return calls, keep
@@ -509,8 +509,8 @@ def synthetic_step(args):
     calls0, keep0 = model.build_step(refined=False)
     torch.cuda.synchronize()
     ms, unref_ms, us = measure(torch, model, calls, calls0, stream, args)
-    workload = (f"Llama-3.1-8B-shape refined decode step, batch {B}: {args.layers} layers x (KV append, q/k/v GEMV, "
-                f"GQA attention 32q/8kv d128 T={T}, o GEMV, gate/up GEMV, down GEMV) with synthetic GEMV inputs "
+    workload = (f"Llama-3.1-8B-shape refined decode step, batch {B}: {args.layers} layers x (q/k/v GEMV, "
+                f"KV append + GQA attention 32q/8kv d128 T={T} in one call, o GEMV, gate/up GEMV, down GEMV) with synthetic GEMV inputs "
                 f"(N(0,1), 1% of channels x20) and queries; weights and KV 2+2-bit, top 3% channels / 2% tokens "
                 f"refined")
     report(model, calls, T, B, args, ms, unref_ms, us, workload, {"channel_selection": "in each GEMV launch"})
@@ -547,7 +547,7 @@ def layer_chain(args):
     ms, unref_ms, us = measure(torch, model, calls, calls0, stream, args, reset)
     sel = "by the kernel that produces each GEMV input" if args.producer_select else "in each GEMV launch"
     workload = (f"Llama-3.1-8B-shape refined decoder layers, batch {B}: {args.layers} layers x (RMSNorm, q/k/v GEMV, "
-                f"RoPE, KV append, GQA attention 32q/8kv d128 T={T}, fp16 cast, o GEMV, RMSNorm, gate/up GEMV, "
+                f"RoPE, KV append + GQA attention 32q/8kv d128 T={T} in one call, fp16 cast, o GEMV, RMSNorm, gate/up GEMV, "
                 f"SwiGLU, down GEMV) from a synthetic residual state; weights and KV 2+2-bit, top 3% channels / 2% "
                 f"tokens refined")
     report(model, calls, T, B, args, ms, unref_ms, us, workload, {"channel_selection": sel})

@@ -107,6 +107,8 @@ _PROTOS = {
     "sf_refined_gemv": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP, VP]),
     "sf_refined_gemv_noalloc": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
+    "sf_refined_attn_decode_append": (I32, [VP, I32, C.POINTER(sf_qkv), VP, VP, VP, I64, C.c_float, I32, VP, VP, I32,
+                                            VP, VP, VP, VP, VP]),
     "sf_attn_decode_variant": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP,
                                      I32]),
     "sf_fp16_fetch_delta": (I32, [VP, I32, C.POINTER(sf_qweight), VP, I32, I32, VP, VP, VP, VP]),
@@ -522,6 +524,35 @@ def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stre
             _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream), variant,
         )
     )
+    return o, sel[:, :, :k_sel], hit[:, :, :k_sel]
+
+
+def refined_attention_append(q, kv, K_new, V_new, scale, k_sel, cache=None, pool=0, stream=None, out=None):
+    """Appends one token (K_new, V_new fp32 [batch][n_kv][d]) at position kv.t_len and
+    attends over kv.t_len + 1 tokens in one call (sf_refined_attn_decode_append); the
+    token's refinement units land in place in kv.refine.  Returns (out, sel, hits) as
+    refined_attention."""
+    torch = _torch()
+    dev = kv.k_res.device
+    qb = _f16_bits(q, dev)
+    batch, n_q, d = qb.shape
+    K_new = _dev_tensor(K_new, torch.float32, dev).reshape(batch, kv.n_kv, d).contiguous()
+    V_new = _dev_tensor(V_new, torch.float32, dev).reshape(batch, kv.n_kv, d).contiguous()
+    o = out if out is not None else torch.empty((batch, n_q, d), dtype=torch.float32, device=dev)
+    ks = max(1, k_sel)
+    sel = torch.empty((batch, kv.n_kv, ks), dtype=torch.int32, device=dev)
+    hit = torch.empty((batch, kv.n_kv, ks), dtype=torch.int32, device=dev)
+    tl = kv.t_len + 1
+    ws = workspace(lib().sf_workspace_bytes_attn(batch, n_q, kv.n_kv, tl, k_sel), dev)
+    d_ = kv.desc(tl)
+    dst = kv.refine.data_ptr() + kv.t_len * kv.unit_bytes
+    check(
+        lib().sf_refined_attn_decode_append(
+            _ptr(qb), n_q, C.byref(d_), _ptr(K_new), _ptr(V_new), C.c_void_p(dst), kv.t_cap, float(scale), k_sel,
+            None, cache.handle if cache else None, pool, _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream),
+        )
+    )
+    kv.t_len = tl
     return o, sel[:, :, :k_sel], hit[:, :, :k_sel]
 
 

@@ -34,6 +34,7 @@
 // The chunks of one KV head in `select` wait for each other at up to four points
 // (bounded spins).  Workgroups are dispatched in order and a KV head has at most
 // 256 chunks, so the chunks of a KV head are resident together.
+#include "group_quant.h"
 #include "sf_internal.h"
 
 namespace {
@@ -93,6 +94,13 @@ struct AttnArgs {
   float* out;       // [batch][n_q][HD]
   uint32_t* timeout;
   PoolDev pool;
+  // appending the new token at position T - 1 in the split pass (k_new non-null):
+  // its K and V rows [bh][HD] fp32, and where its refinement units go (the unit of
+  // KV head bh at ap_refine + bh * ap_refine_ld * unit_bytes; may be null)
+  const float* k_new;
+  const float* v_new;
+  uint8_t* ap_refine;
+  int64_t ap_refine_ld;
 };
 
 __device__ __forceinline__ void merge_ms(float& m, float& z, float om, float oz) {
@@ -142,12 +150,35 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   __shared__ _Float16 s_u[PV ? 2 * G : 1][UP];
   __shared__ float s_red[4][3 * G + 1];
   __shared__ float s_st[3 * G + 1];
+  __shared__ uint8_t s_aq[2][256];       // the appended token's codes (quantiser scratch)
+  __shared__ uint32_t s_nk[2][4 * B];    // its resident words, K and V
+  __shared__ uint32_t s_nsz[2];          // its sz words
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, bh = blockIdx.y;
   const int bi = bh / a.n_kv, kvh = bh - bi * a.n_kv;
   const int T = a.T;
   const int t_begin = split * SA, n_here = min(SA, T - t_begin);
   const size_t tok0 = (size_t)bh * a.t_cap + t_begin;
+
+  // the new token, when this call appends it and this split holds position T - 1:
+  // waves 0 and 1 quantise its K and V rows exactly as the KV append does (codes,
+  // sz words and refinement units into the cache), and this workgroup takes the
+  // token's words from LDS rather than reading back what it has just written
+  const int tnew = a.k_new ? T - 1 - t_begin : -1;
+  const bool app = tnew >= 0 && tnew < SA;
+  if (app) {
+    if (wave < 2) {
+      const size_t pos = (size_t)bh * a.t_cap + (T - 1);
+      uint8_t* res = const_cast<uint8_t*>(wave ? a.v_res : a.k_res);
+      uint32_t* szp = const_cast<uint32_t*>(wave ? a.v_sz : a.k_sz);
+      uint32_t* ref = a.ap_refine && a.r > 0
+                          ? (uint32_t*)(a.ap_refine + (size_t)bh * a.ap_refine_ld * (2 * 16 * a.r) + wave * 16 * a.r)
+                          : nullptr;
+      sfq::quantize_group_wave((wave ? a.v_new : a.k_new) + (size_t)bh * HD, B, a.r, s_aq[wave], s_aq[wave] + 128,
+                               (uint32_t*)(res + pos * 16 * B), szp + pos, ref, s_nk[wave], &s_nsz[wave]);
+    }
+    __syncthreads();
+  }
 
   // this call's selection histograms, counters and lookup-log base
   if (a.k_sel > 0) {
@@ -176,20 +207,25 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     const u32x4* src = (const u32x4*)(a.v_res + tok0 * (HD * B / 8));
     const int nv = n_here * WPT / 4;
     for (int i = tid; i < nv; i += 256) {
-      const u32x4 v = __builtin_nontemporal_load(src + i);
       const int w = 4 * i, tk = w / WPT, c = w - tk * WPT;
+      if (tk == tnew) continue;
+      const u32x4 v = __builtin_nontemporal_load(src + i);
       uint32_t* d = s_vc + tk * WPTP + c;
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
-    s_vsz[tid] = tid < n_here ? a.v_sz[tok0 + tid] : 0u;
+    if (app && tid < WPT) s_vc[tnew * WPTP + tid] = s_nk[1][tid];
+    s_vsz[tid] = tid == tnew ? s_nsz[1] : (tid < n_here ? a.v_sz[tok0 + tid] : 0u);
   }
-  s_ksz[tid] = tid < n_here ? a.k_sz[tok0 + tid] : 0u;
+  s_ksz[tid] = tid == tnew ? s_nsz[0] : (tid < n_here ? a.k_sz[tok0 + tid] : 0u);
   const int n = lane & 15, qg = lane >> 4;
   uint32_t kw[4][B];  // wave: 4 tiles of 16 tokens; lane: token n of each tile, dims 32qg..
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int tl = wave * 64 + 16 * u + n;
-    if (tl < n_here) {
+    if (tl == tnew) {
+#pragma unroll
+      for (int w = 0; w < B; ++w) kw[u][w] = s_nk[0][qg * B + w];
+    } else if (tl < n_here) {
       const uint32_t* src = (const uint32_t*)(a.k_res + (tok0 + tl) * (HD * B / 8)) + qg * B;
       if constexpr (B == 1) {
         kw[u][0] = __builtin_nontemporal_load(src);
@@ -1424,20 +1460,26 @@ extern "C" size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int3
   return attn_layout(batch, n_q_heads, n_kv_heads, t_len, k_sel, off);
 }
 
+static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv, const float* k_new,
+                             const float* v_new, uint8_t* refine_out, int64_t refine_ld, float softmax_scale,
+                             int32_t k_sel, const int32_t* sel_in, sf_refine_cache* cache, int32_t pool, float* out,
+                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws, sf_stream stream,
+                             int32_t variant);
+
 extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
                                             float softmax_scale, int32_t k_sel, const int32_t* sel_in,
                                             sf_refine_cache* cache, int32_t pool, float* out,
                                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                             sf_stream stream) {
-  return sf_attn_decode_variant(q_f16, n_q_heads, kv, softmax_scale, k_sel, sel_in, cache, pool, out, sel_out,
-                                hit_out, ws, stream, SF_ATTN_NESTED);
+  return attn_decode(q_f16, n_q_heads, kv, nullptr, nullptr, nullptr, 0, softmax_scale, k_sel, sel_in, cache, pool,
+                     out, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
 }
 
-extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
-                                            float softmax_scale, int32_t k_sel, const int32_t* sel_in,
-                                            sf_refine_cache* cache, int32_t pool, float* out,
-                                            int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
-                                            sf_stream stream, int32_t variant) {
+static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv, const float* k_new,
+                             const float* v_new, uint8_t* refine_out, int64_t refine_ld, float softmax_scale,
+                             int32_t k_sel, const int32_t* sel_in, sf_refine_cache* cache, int32_t pool, float* out,
+                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws, sf_stream stream,
+                             int32_t variant) {
   SF_REQUIRE(q_f16 && kv && out && ws, SF_EINVAL, "null argument");
   SF_REQUIRE(variant == SF_ATTN_NESTED || variant == SF_ATTN_FP16_TOKENS || variant == SF_ATTN_DROP_UNSELECTED,
              SF_EINVAL, "unknown attention variant");
@@ -1494,6 +1536,10 @@ extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_h
   a.sel_out = sel_out;
   a.hit_out = hit_out;
   a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.ap_refine = refine_out;
+  a.ap_refine_ld = refine_ld;
   if (k_sel > 0) {
     sf_status st = sf_cache_pool_view(cache, cache ? pool : -1, &a.pool);
     if (st != SF_OK) return st;
@@ -1515,4 +1561,25 @@ extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_h
       sf_set_error("sf_refined_attn_decode: resident KV width b must be 1, 2, 4 or 8");
       return SF_EUNSUPPORTED;
   }
+}
+
+extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
+                                            float softmax_scale, int32_t k_sel, const int32_t* sel_in,
+                                            sf_refine_cache* cache, int32_t pool, float* out,
+                                            int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
+                                            sf_stream stream, int32_t variant) {
+  return attn_decode(q_f16, n_q_heads, kv, nullptr, nullptr, nullptr, 0, softmax_scale, k_sel, sel_in, cache, pool,
+                     out, sel_out, hit_out, ws, stream, variant);
+}
+
+extern "C" sf_status sf_refined_attn_decode_append(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
+                                                   const float* k_new, const float* v_new, uint8_t* refine_out,
+                                                   int64_t refine_ld, float softmax_scale, int32_t k_sel,
+                                                   const int32_t* sel_in, sf_refine_cache* cache, int32_t pool,
+                                                   float* out, int32_t* sel_out, int32_t* hit_out,
+                                                   sf_workspace* ws, sf_stream stream) {
+  SF_REQUIRE(k_new && v_new, SF_EINVAL, "null k_new / v_new");
+  SF_REQUIRE(refine_out == nullptr || refine_ld >= 1, SF_EINVAL, "refine_ld must be >= 1");
+  return attn_decode(q_f16, n_q_heads, kv, k_new, v_new, refine_out, refine_ld, softmax_scale, k_sel, sel_in, cache,
+                     pool, out, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
 }

@@ -421,23 +421,22 @@ class DecodeModel:
             calls.append((Lb.sf_qk_rope, [P(bf["q"]), P(bf["k"]), B, S.n_q, S.n_kv, P(L.get("q_norm")), P(L.get("k_norm")),
                                           S.eps, pos, S.theta, P(bf["q16"]), P(bf["k_rot"]), None], "rope"))
             kv = L["kv"]
-            dsc_app = kv.desc(pos)
             # the new token's refinement units: into the device copy, or straight into the
             # pinned host store the cache fills from (device-visible memory)
             if self._pool_frac is not None and self.kv_r > 0:
                 dst = self._stores[L["pool_kv"]].data_ptr() + pos * kv.unit_bytes
             else:
                 dst = kv.refine.data_ptr() + pos * kv.unit_bytes
-            keep.append(dsc_app)
-            calls.append((Lb.sf_kv_append, [P(bf["k_rot"]), P(bf["v"]), 1, pos, C.byref(dsc_app), C.c_void_p(dst), kv.t_cap,
-                                            None], "append"))
             dsc = kv.desc(pos + 1)
             keep.append(dsc)
             kt = k_select(self.tok_pct, pos + 1) if refined and self.kv_r > 0 else 0
             pool_kv = L.get("pool_kv", -1) if cache is not None else -1
-            calls.append((Lb.sf_refined_attn_decode, [P(bf["q16"]), S.n_q, C.byref(dsc), 1.0 / math.sqrt(d), kt, None,
-                                                      cache, pool_kv, P(bf["attn"]), P(bf["sel_tok"]), P(bf["hit_tok"]),
-                                                      ws.handle, None], "attn"))
+            # the append and the attention in one call (the attention's first pass
+            # quantises the new token)
+            calls.append((Lb.sf_refined_attn_decode_append,
+                          [P(bf["q16"]), S.n_q, C.byref(dsc), P(bf["k_rot"]), P(bf["v"]), C.c_void_p(dst), kv.t_cap,
+                           1.0 / math.sqrt(d), kt, None, cache, pool_kv, P(bf["attn"]), P(bf["sel_tok"]),
+                           P(bf["hit_tok"]), ws.handle, None], "attn"))
             if ps:
                 calls.append((Lb.sf_to_f16_select, [P(bf["attn"]), B, S.n_q * d, P(bf["a16"]), ksel(S.n_q * d),
                                                     P(bf["sel_o"]), None], "cast"))

@@ -203,3 +203,37 @@ def test_refinement_that_removes_the_dominant_token():
     ref, chosen = o_attn.refined_attention(q, qk, qv, (1, n_kv, T, D), SCALE, ks)
     assert sel.cpu().numpy()[0, 0].tolist() == chosen[(0, 0)] and 0 in chosen[(0, 0)]
     assert_close(out.cpu().numpy(), ref, what="dominant token refined away")
+
+
+@pytest.mark.parametrize("b,r,G,T0", [(2, 2, 4, 300), (1, 1, 2, 40), (4, 4, 8, 700), (2, 2, 4, 4096 + 255), (2, 1, 1, 0)])
+def test_fused_append_matches_append_then_attention(b, r, G, T0):
+    """sf_refined_attn_decode_append against sf_kv_append of the same token followed by
+    sf_refined_attn_decode: the cache (codes, sz words, refinement units), the
+    selection and the hits bit for bit; the outputs to fp32 rounding (the value-sum
+    records are added atomically, in no fixed order).  T0 = 0: the new token is the
+    whole cache."""
+    batch, n_kv = 2, 2
+    K, V = inputs.kv(60 + b + G, 0, batch, n_kv, T0 + 1, D)
+    q = inputs.query(60 + b + G, 0, 0, batch, n_kv * G, D)
+    ks = max(1, selection.k_select(2, T0 + 1))
+    res = []
+    for fused in (False, True):
+        kv = binding.QuantKV(batch, n_kv, T0 + 8, b, r)
+        if T0 > 0:
+            kv.append(K[:, :, :T0], V[:, :, :T0])
+        cache = binding.RefineCache([kv.resident_pool_desc()])
+        kn, vn = K[:, :, T0], V[:, :, T0]
+        if fused:
+            out, sel, hit = binding.refined_attention_append(q, kv, kn, vn, SCALE, ks, cache=cache)
+        else:
+            kv.append(kn[:, :, None], vn[:, :, None])
+            out, sel, hit = binding.refined_attention(q, kv, SCALE, ks, cache=cache)
+        torch.cuda.synchronize()
+        assert kv.t_len == T0 + 1
+        res.append(([t.cpu().numpy() for t in (kv.k_res, kv.k_sz, kv.v_res, kv.v_sz, kv.refine)],
+                    out.cpu().numpy(), sel.cpu().numpy(), hit.cpu().numpy()))
+    (bufs_a, out_a, sel_a, hit_a), (bufs_b, out_b, sel_b, hit_b) = res
+    for x, y in zip(bufs_a, bufs_b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(sel_a, sel_b) and np.array_equal(hit_a, hit_b)
+    assert_close(out_b, out_a, rtol=1e-6, atol=1e-7, what="fused append")
