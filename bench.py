@@ -54,12 +54,13 @@ SOURCES = ("bit_decode_selective_amd/csrc/gemv_rows.h", "bit_decode_selective_am
 # of known size (--copy-calibration); reported only while the kernel sources have
 # the hash they were measured on, and only for the call they were measured for.
 TRAFFIC = {
-    # attn call, T = 32768, 8 KV heads: split + select + pv, medians over 32 calls each
+    # attn call (with the new token's append), T = 32768, 8 KV heads: split + select + pv,
+    # medians over 32 calls each
     # (profiles/decode_step_llama8b_2bit_t32k_hbm_counters.md)
     "call": "attn",
-    "sources_sha256": "336f8c43eddf9014f3c96b5968a2e1ce8507d0fba357980e111a42932617b8ee",
-    "fetch_bytes": 9620920 + 6849056 + 16890814,
-    "write_bytes": 4690176 + 740656 + 1409024,
+    "sources_sha256": "bf7a0b8b23883769ecf47fe4509c1e9a74419e3febf68b865b81a6b2f4cb4dd0",
+    "fetch_bytes": 9670323 + 6840928 + 16886716,
+    "write_bytes": 4691712 + 740640 + 1409024,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
 
