@@ -389,7 +389,7 @@ class SyntheticStep:
                                   (C.c_void_p(self.q[li].data_ptr()), S.n_q, C.byref(dsc), C.c_void_p(Kn.data_ptr()),
                                    C.c_void_p(Vn.data_ptr()), C.c_void_p(dst), kv.t_cap, 1.0 / math.sqrt(HD), kt,
                                    None, self.cache.handle, kv_pool, C.c_void_p(self.out[li].data_ptr()), None, None,
-                                   self.ws.handle, None), "attn"))
+                                   None, self.ws.handle, None), "attn"))
         return calls, keep
 
     def enqueue(self, calls, stream, timer=None):

@@ -108,7 +108,7 @@ _PROTOS = {
     "sf_refined_gemv_noalloc": (I32, [C.POINTER(sf_gemv_op), I32, VP, I32, I32, VP, VP, VP, VP]),
     "sf_refined_attn_decode": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP]),
     "sf_refined_attn_decode_append": (I32, [VP, I32, C.POINTER(sf_qkv), VP, VP, VP, I64, C.c_float, I32, VP, VP, I32,
-                                            VP, VP, VP, VP, VP]),
+                                            VP, VP, VP, VP, VP, VP]),
     "sf_attn_decode_variant": (I32, [VP, I32, C.POINTER(sf_qkv), C.c_float, I32, VP, VP, I32, VP, VP, VP, VP, VP,
                                      I32]),
     "sf_fp16_fetch_delta": (I32, [VP, I32, C.POINTER(sf_qweight), VP, I32, I32, VP, VP, VP, VP]),
@@ -527,10 +527,12 @@ def refined_attention(q, kv, scale, k_sel, cache=None, pool=0, sel_in=None, stre
     return o, sel[:, :, :k_sel], hit[:, :, :k_sel]
 
 
-def refined_attention_append(q, kv, K_new, V_new, scale, k_sel, cache=None, pool=0, stream=None, out=None):
+def refined_attention_append(q, kv, K_new, V_new, scale, k_sel, cache=None, pool=0, stream=None, out=None,
+                             out_f16=None):
     """Appends one token (K_new, V_new fp32 [batch][n_kv][d]) at position kv.t_len and
     attends over kv.t_len + 1 tokens in one call (sf_refined_attn_decode_append); the
-    token's refinement units land in place in kv.refine.  Returns (out, sel, hits) as
+    token's refinement units land in place in kv.refine; out_f16 (int16 [batch][n_q][d],
+    optional) receives the output as fp16 bits.  Returns (out, sel, hits) as
     refined_attention."""
     torch = _torch()
     dev = kv.k_res.device
@@ -549,7 +551,8 @@ def refined_attention_append(q, kv, K_new, V_new, scale, k_sel, cache=None, pool
     check(
         lib().sf_refined_attn_decode_append(
             _ptr(qb), n_q, C.byref(d_), _ptr(K_new), _ptr(V_new), C.c_void_p(dst), kv.t_cap, float(scale), k_sel,
-            None, cache.handle if cache else None, pool, _ptr(o), _ptr(sel), _ptr(hit), ws.handle, _stream(stream),
+            None, cache.handle if cache else None, pool, _ptr(o), _ptr(out_f16), _ptr(sel), _ptr(hit), ws.handle,
+            _stream(stream),
         )
     )
     kv.t_len = tl

@@ -92,6 +92,7 @@ struct AttnArgs {
   int32_t* sel_out;
   int32_t* hit_out;
   float* out;       // [batch][n_q][HD]
+  uint16_t* out16;  // the same as fp16 bits (round to nearest even), or null
   uint32_t* timeout;
   PoolDev pool;
   // appending the new token at position T - 1 in the split pass (k_new non-null):
@@ -670,7 +671,9 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
             den += vd[k];
           }
       }
-      a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
+      const size_t oi = ((size_t)bi * a.n_q + kvh * G + h) * HD + d;
+      a.out[oi] = num / den;
+      if (a.out16) a.out16[oi] = __builtin_bit_cast(uint16_t, (_Float16)(num / den));
     }
     return;
   }
@@ -1364,7 +1367,9 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
       num += vn[k];
       den += vz[k];
     }
-    a.out[((size_t)bi * a.n_q + kvh * G + h) * HD + d] = num / den;
+    const size_t oi = ((size_t)bi * a.n_q + kvh * G + h) * HD + d;
+    a.out[oi] = num / den;
+    if (a.out16) a.out16[oi] = __builtin_bit_cast(uint16_t, (_Float16)(num / den));
   }
 }
 
@@ -1463,8 +1468,8 @@ extern "C" size_t sf_workspace_bytes_attn(int32_t batch, int32_t n_q_heads, int3
 static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv, const float* k_new,
                              const float* v_new, uint8_t* refine_out, int64_t refine_ld, float softmax_scale,
                              int32_t k_sel, const int32_t* sel_in, sf_refine_cache* cache, int32_t pool, float* out,
-                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws, sf_stream stream,
-                             int32_t variant);
+                             uint16_t* out_f16, int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
+                             sf_stream stream, int32_t variant);
 
 extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
                                             float softmax_scale, int32_t k_sel, const int32_t* sel_in,
@@ -1472,14 +1477,14 @@ extern "C" sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_h
                                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                             sf_stream stream) {
   return attn_decode(q_f16, n_q_heads, kv, nullptr, nullptr, nullptr, 0, softmax_scale, k_sel, sel_in, cache, pool,
-                     out, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
+                     out, nullptr, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
 }
 
 static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv, const float* k_new,
                              const float* v_new, uint8_t* refine_out, int64_t refine_ld, float softmax_scale,
                              int32_t k_sel, const int32_t* sel_in, sf_refine_cache* cache, int32_t pool, float* out,
-                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws, sf_stream stream,
-                             int32_t variant) {
+                             uint16_t* out_f16, int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
+                             sf_stream stream, int32_t variant) {
   SF_REQUIRE(q_f16 && kv && out && ws, SF_EINVAL, "null argument");
   SF_REQUIRE(variant == SF_ATTN_NESTED || variant == SF_ATTN_FP16_TOKENS || variant == SF_ATTN_DROP_UNSELECTED,
              SF_EINVAL, "unknown attention variant");
@@ -1536,6 +1541,7 @@ static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_
   a.sel_out = sel_out;
   a.hit_out = hit_out;
   a.out = out;
+  a.out16 = out_f16;
   a.k_new = k_new;
   a.v_new = v_new;
   a.ap_refine = refine_out;
@@ -1569,17 +1575,17 @@ extern "C" sf_status sf_attn_decode_variant(const uint16_t* q_f16, int32_t n_q_h
                                             int32_t* sel_out, int32_t* hit_out, sf_workspace* ws,
                                             sf_stream stream, int32_t variant) {
   return attn_decode(q_f16, n_q_heads, kv, nullptr, nullptr, nullptr, 0, softmax_scale, k_sel, sel_in, cache, pool,
-                     out, sel_out, hit_out, ws, stream, variant);
+                     out, nullptr, sel_out, hit_out, ws, stream, variant);
 }
 
 extern "C" sf_status sf_refined_attn_decode_append(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
                                                    const float* k_new, const float* v_new, uint8_t* refine_out,
                                                    int64_t refine_ld, float softmax_scale, int32_t k_sel,
                                                    const int32_t* sel_in, sf_refine_cache* cache, int32_t pool,
-                                                   float* out, int32_t* sel_out, int32_t* hit_out,
-                                                   sf_workspace* ws, sf_stream stream) {
+                                                   float* out, uint16_t* out_f16, int32_t* sel_out,
+                                                   int32_t* hit_out, sf_workspace* ws, sf_stream stream) {
   SF_REQUIRE(k_new && v_new, SF_EINVAL, "null k_new / v_new");
   SF_REQUIRE(refine_out == nullptr || refine_ld >= 1, SF_EINVAL, "refine_ld must be >= 1");
   return attn_decode(q_f16, n_q_heads, kv, k_new, v_new, refine_out, refine_ld, softmax_scale, k_sel, sel_in, cache,
-                     pool, out, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
+                     pool, out, out_f16, sel_out, hit_out, ws, stream, SF_ATTN_NESTED);
 }

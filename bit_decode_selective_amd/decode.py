@@ -432,16 +432,15 @@ class DecodeModel:
             kt = k_select(self.tok_pct, pos + 1) if refined and self.kv_r > 0 else 0
             pool_kv = L.get("pool_kv", -1) if cache is not None else -1
             # the append and the attention in one call (the attention's first pass
-            # quantises the new token)
+            # quantises the new token); without producer selection the attention also
+            # writes the o projection's fp16 input
             calls.append((Lb.sf_refined_attn_decode_append,
                           [P(bf["q16"]), S.n_q, C.byref(dsc), P(bf["k_rot"]), P(bf["v"]), C.c_void_p(dst), kv.t_cap,
-                           1.0 / math.sqrt(d), kt, None, cache, pool_kv, P(bf["attn"]), P(bf["sel_tok"]),
-                           P(bf["hit_tok"]), ws.handle, None], "attn"))
+                           1.0 / math.sqrt(d), kt, None, cache, pool_kv, P(bf["attn"]), None if ps else P(bf["a16"]),
+                           P(bf["sel_tok"]), P(bf["hit_tok"]), ws.handle, None], "attn"))
             if ps:
                 calls.append((Lb.sf_to_f16_select, [P(bf["attn"]), B, S.n_q * d, P(bf["a16"]), ksel(S.n_q * d),
                                                     P(bf["sel_o"]), None], "cast"))
-            else:
-                calls.append((Lb.sf_to_f16, [P(bf["attn"]), B * S.n_q * d, P(bf["a16"]), None], "cast"))
             gemv(("o",), L, bf["a16"], (bf["o"],), S.n_q * d, bf["sel_o"], "o")
             last = li == len(self.layers) - 1
             if lag_on and (not last or self.head):  # o's next update: the next layer's, or the final norm

@@ -357,14 +357,17 @@ sf_status sf_refined_attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const
  * and, when refine_out is non-NULL, its refinement units at refine_out + (i *
  * n_kv_heads + h) * refine_ld * unit_bytes for batch i, head h) by the attention's
  * own first pass, saving a launch.  k_new, v_new: device fp32 [batch][n_kv_heads]
- * [head_dim].  The nested variant only; errors as sf_refined_attn_decode, and
- * SF_EINVAL for null k_new / v_new or refine_ld < 1 with refine_out. */
+ * [head_dim].  out_f16 (device, may be NULL): out again as fp16 bits (round to
+ * nearest even, as sf_to_f16), the input of the o projection, written by the same
+ * kernel that writes out.  The nested variant only; errors as
+ * sf_refined_attn_decode, and SF_EINVAL for null k_new / v_new or refine_ld < 1
+ * with refine_out. */
 sf_status sf_refined_attn_decode_append(const uint16_t* q_f16, int32_t n_q_heads, const sf_qkv* kv,
                                         const float* k_new, const float* v_new, uint8_t* refine_out,
                                         int64_t refine_ld, float softmax_scale, int32_t k_sel,
                                         const int32_t* sel_in, sf_refine_cache* cache, int32_t pool,
-                                        float* out, int32_t* sel_out, int32_t* hit_out,
-                                        sf_workspace* ws, sf_stream stream);
+                                        float* out, uint16_t* out_f16, int32_t* sel_out,
+                                        int32_t* hit_out, sf_workspace* ws, sf_stream stream);
 
 /* Comparison variants of the refined attention (rag-lover.com StrataFlux summary,
  * "既存手法との違い": the paper compares nested refinement with SpeCache, which

@@ -210,8 +210,8 @@ def test_fused_append_matches_append_then_attention(b, r, G, T0):
     """sf_refined_attn_decode_append against sf_kv_append of the same token followed by
     sf_refined_attn_decode: the cache (codes, sz words, refinement units), the
     selection and the hits bit for bit; the outputs to fp32 rounding (the value-sum
-    records are added atomically, in no fixed order).  T0 = 0: the new token is the
-    whole cache."""
+    records are added atomically, in no fixed order), and the fp16 output as the fp32
+    one rounded to nearest even.  T0 = 0: the new token is the whole cache."""
     batch, n_kv = 2, 2
     K, V = inputs.kv(60 + b + G, 0, batch, n_kv, T0 + 1, D)
     q = inputs.query(60 + b + G, 0, 0, batch, n_kv * G, D)
@@ -224,7 +224,8 @@ def test_fused_append_matches_append_then_attention(b, r, G, T0):
         cache = binding.RefineCache([kv.resident_pool_desc()])
         kn, vn = K[:, :, T0], V[:, :, T0]
         if fused:
-            out, sel, hit = binding.refined_attention_append(q, kv, kn, vn, SCALE, ks, cache=cache)
+            o16 = torch.empty((batch, n_kv * G, D), dtype=torch.int16, device="cuda")
+            out, sel, hit = binding.refined_attention_append(q, kv, kn, vn, SCALE, ks, cache=cache, out_f16=o16)
         else:
             kv.append(kn[:, :, None], vn[:, :, None])
             out, sel, hit = binding.refined_attention(q, kv, SCALE, ks, cache=cache)
@@ -237,3 +238,5 @@ def test_fused_append_matches_append_then_attention(b, r, G, T0):
         assert np.array_equal(x, y)
     assert np.array_equal(sel_a, sel_b) and np.array_equal(hit_a, hit_b)
     assert_close(out_b, out_a, rtol=1e-6, atol=1e-7, what="fused append")
+    # the fp16 copy: the fp32 output rounded to nearest even
+    assert np.array_equal(o16.cpu().numpy().view(np.float16), out_b.astype(np.float16))
