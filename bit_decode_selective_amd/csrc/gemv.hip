@@ -26,39 +26,19 @@
 #include <string>
 
 #include "gemv_rows.h"
-#include "select_core.h"
 
 namespace sfg {
-// The channel selection (select_core.h) over x read from memory, then the lookups
-// and reports of every matrix of the call.
-__global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
+// The channel selection over x read from memory (split_select: one 256-thread
+// workgroup, two-pass radix select), then the lookups and reports of every matrix
+// of the call.
+__global__ __launch_bounds__(256) void gemv_select_kernel(GemvArgs a) {
+  extern __shared__ uint32_t smem[];
   __shared__ int lds[24];
   const int tid = threadIdx.x;
   const int K = a.k_in, ks = a.k_sel;
   int32_t* sel = a.ws_sel;
-  if (a.sel_in) {
-    for (int j = tid; j < ks; j += SEL_NT) sel[j] = a.sel_in[j];
-  } else if (ks >= K) {
-    for (int j = tid; j < ks; j += SEL_NT) sel[j] = j;
-  } else {
-    constexpr int MI = 4;
-    uint32_t kw[4 * MI];
-#pragma unroll
-    for (int i = 0; i < 4 * MI; ++i) kw[i] = 0;
-    for (int bb = 0; bb < a.batch; ++bb) {
-      const u32x4* xr = (const u32x4*)(a.x + (size_t)bb * K);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int m = tid + SEL_NT * i;
-        if (m < K / 8) {
-          const u32x4 v = xr[m];
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-          sfsel::key_max8(kw + 4 * i, wv);
-        }
-      }
-    }
-    sfsel::topk_keys<SEL_NT, MI>(kw, K, ks, sel);
-  }
+  const int32_t* l_sel = split_select(a, smem);
+  for (int j = tid; j < ks; j += 256) sel[j] = l_sel[j];
   // sel[] is read back below by other threads of this workgroup
   __syncthreads();
   // lookups, per op, in selection order (with the report and the lookup log)
@@ -71,8 +51,8 @@ __global__ __launch_bounds__(SEL_NT) void gemv_select_kernel(GemvArgs a) {
     lds[tid] = base;
   }
   __syncthreads();
-  for (int j = tid; j < ks; j += SEL_NT) {
-    const int k = sel[j];
+  for (int j = tid; j < ks; j += 256) {
+    const int k = l_sel[j];
     if (a.sel_out) a.sel_out[j] = k;
     int slot[SF_MAX_OPS];
 #pragma unroll
@@ -637,7 +617,7 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
   const int max_nb = lds2 <= 64 * 1024 ? 2 : 1;
   const bool one_launch = !mfma && batch <= max_nb;
   if (k_sel > 0 && !one_launch) {
-    hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(SEL_NT), 0, s, a);
+    hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(256), select_lds_bytes((int)K, k_sel), s, a);
     SF_LAUNCH_CHECK();
   }
   if (mfma) {

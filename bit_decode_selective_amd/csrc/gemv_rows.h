@@ -431,6 +431,12 @@ inline size_t split_lds_bytes(int k_in, int pairs, int codes, int nb, int k_sel,
   return std::max(tile, sel) * 4;
 }
 
+// LDS of split_select alone (the selection launch of batches the row kernels do
+// not take in one launch).
+inline size_t select_lds_bytes(int k_in, int k_sel) {
+  return ((size_t)(k_in / 2) + 2 * (size_t)(k_in / 32) + (((size_t)k_sel + 3) & ~(size_t)3) + 4 * 256 + 4 * 128 + 16) * 4;
+}
+
 // Copies of the published words (tile t reads copy t mod SPLIT_COPIES), and the
 // stride of one copy in words.
 constexpr int SPLIT_COPIES = 8;
@@ -511,9 +517,11 @@ __device__ __forceinline__ void split_retire(const GemvArgs& a) {
   }
 }
 
-// Workgroup 0: selection into l_sel (LDS), then the lookups, the published copy in
-// the workspace and the reports.
-__device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint32_t* smem) {
+// The channel selection of one 256-thread workgroup into LDS (returned: k_sel
+// channels, ascending; every thread returns after a barrier), by a two-pass radix
+// select over per-wave LDS histograms of the 15-bit |x| keys (max over the batch
+// rows).  smem: the selector layout of split_lds_bytes / select_lds_bytes.
+__device__ __forceinline__ int32_t* split_select(const GemvArgs& a, uint32_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.k_in, ks = a.k_sel, n8 = K / 8;
   uint32_t* keys = smem;                       // [K/2]
@@ -644,6 +652,16 @@ __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint
     }
   }
   lds_barrier();
+  return l_sel;
+}
+
+// Workgroup 0: selection into LDS, then the lookups, the published copy in the
+// workspace and the reports.
+__device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint32_t* smem) {
+  const int tid = threadIdx.x;
+  const int ks = a.k_sel;
+  const int32_t* l_sel = split_select(a, smem);
+  int* sc = (int*)(l_sel + ((ks + 3) & ~3) + 4 * 256 + 4 * 128);  // [16] (after the histograms)
   // the published words first: the channels and, per matrix without resident
   // units, the slots, in SPLIT_COPIES copies
   uint32_t* hw = a.ctl + offsetof(WsControl, hit) / 4;
