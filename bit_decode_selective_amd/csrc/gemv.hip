@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void gemv_select_kernel(GemvArgs a) {
   const int tid = threadIdx.x;
   const int K = a.k_in, ks = a.k_sel;
   int32_t* sel = a.ws_sel;
-  const int32_t* l_sel = split_select(a, smem);
+  const int32_t* l_sel = split_select<true>(a, smem);
   for (int j = tid; j < ks; j += 256) sel[j] = l_sel[j];
   // sel[] is read back below by other threads of this workgroup
   __syncthreads();

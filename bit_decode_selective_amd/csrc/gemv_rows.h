@@ -517,10 +517,42 @@ __device__ __forceinline__ void split_retire(const GemvArgs& a) {
   }
 }
 
+// key words of NI u32x4 slots a thread (channels 8m .. 8m+7, m = m0 + 256 i + tid):
+// the running max over the batch rows of |x|, RG = 16 / NI rows' loads in flight at
+// once (rows past the batch re-read the last row, which leaves the max unchanged)
+__device__ __forceinline__ void key_max8x(u32x4& kv, const u32x4& v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t x2 = v[q] & 0x7FFF7FFFu;
+    kv[q] = max(kv[q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[q] >> 16, x2 >> 16) << 16);
+  }
+}
+template <int NI>
+__device__ __forceinline__ void key_rows(const GemvArgs& a, int m0, int n8, int tid, u32x4 (&kv)[8]) {
+  constexpr int RG = 16 / NI;
+  const int K = a.k_in;
+  for (int b0 = 0; b0 < a.batch; b0 += RG) {
+    u32x4 v[RG][NI];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const u32x4* xr = (const u32x4*)(a.x + (size_t)min(b0 + r, a.batch - 1) * K);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) v[r][i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) key_max8x(kv[i], v[r][i]);
+  }
+}
+
 // The channel selection of one 256-thread workgroup into LDS (returned: k_sel
 // channels, ascending; every thread returns after a barrier), by a two-pass radix
 // select over per-wave LDS histograms of the 15-bit |x| keys (max over the batch
-// rows).  smem: the selector layout of split_lds_bytes / select_lds_bytes.
+// rows).  smem: the selector layout of split_lds_bytes / select_lds_bytes.  ROWS:
+// the key loads of several batch rows are issued together (the batched selection
+// launch); otherwise row by row, 8 slots a thread (the split kernel, batch 1 or 2).
+template <bool ROWS = false>
 __device__ __forceinline__ int32_t* split_select(const GemvArgs& a, uint32_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.k_in, ks = a.k_sel, n8 = K / 8;
@@ -544,18 +576,26 @@ __device__ __forceinline__ int32_t* split_select(const GemvArgs& a, uint32_t* sm
       u32x4 kv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) kv[i] = u32x4{0u, 0u, 0u, 0u};
-      for (int bb = 0; bb < a.batch; ++bb) {
-        const u32x4* xr = (const u32x4*)(a.x + (size_t)bb * K);
-        u32x4 v[8];
+      if constexpr (ROWS) {
+        switch (min(8, (n8 - m0 + 255) / 256)) {
+          case 1: key_rows<1>(a, m0, n8, tid, kv); break;
+          case 2: key_rows<2>(a, m0, n8, tid, kv); break;
+          case 3: key_rows<3>(a, m0, n8, tid, kv); break;
+          case 4: key_rows<4>(a, m0, n8, tid, kv); break;
+          case 5: key_rows<5>(a, m0, n8, tid, kv); break;
+          case 6: key_rows<6>(a, m0, n8, tid, kv); break;
+          case 7: key_rows<7>(a, m0, n8, tid, kv); break;
+          default: key_rows<8>(a, m0, n8, tid, kv); break;
+        }
+      } else {
+        for (int bb = 0; bb < a.batch; ++bb) {
+          const u32x4* xr = (const u32x4*)(a.x + (size_t)bb * K);
+          u32x4 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
+          for (int i = 0; i < 8; ++i) v[i] = xr[min(m0 + 256 * i + tid, n8 - 1)];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x2 = v[i][q] & 0x7FFF7FFFu;
-            kv[i][q] = max(kv[i][q] & 0xFFFFu, x2 & 0xFFFFu) | (max(kv[i][q] >> 16, x2 >> 16) << 16);
-          }
+          for (int i = 0; i < 8; ++i) key_max8x(kv[i], v[i]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
