@@ -85,41 +85,58 @@ __global__ __launch_bounds__(256) void gemv_select_kernel(GemvArgs a) {
 // the fp32 sum sees the full-precision value on hits.  A workgroup covers 64*RT
 // rows (RT 16-row tiles per wave) by one channel slice; the slices of a row block
 // are summed in slice order by the workgroup that finishes last.
-constexpr int MPFG = 4;         // groups of codes in flight per tile
 constexpr int MAX_ROW_BLOCKS = 1024;  // counters in the workspace control block
 
+// (plain loads: the lanes of one load take 32 of a line's 128 bytes and the next
+// groups' loads the rest; with nontemporal loads the lines were fetched again)
 template <int W>
 __device__ __forceinline__ void load_words(const uint8_t* src, uint32_t (&w)[W]) {
   if constexpr (W == 1) {
-    w[0] = __builtin_nontemporal_load((const uint32_t*)src);
+    w[0] = *(const uint32_t*)src;
   } else if constexpr (W == 2) {
-    const u32x2 v = __builtin_nontemporal_load((const u32x2*)src);
+    const u32x2 v = *(const u32x2*)src;
     w[0] = v.x; w[1] = v.y;
   } else {
 #pragma unroll
     for (int i = 0; i < W / 4; ++i) {
-      const u32x4 v = __builtin_nontemporal_load((const u32x4*)src + i);
+      const u32x4 v = *((const u32x4*)src + i);
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
   }
 }
 
-__host__ __device__ constexpr size_t mfma_lds_words(int nb, int gs, int rows_wg, int nhp) {
+// uw: words of a refinement unit that hold the workgroup's rows (rows_wg r / 32;
+// 0 without a selection)
+__host__ __device__ constexpr size_t mfma_lds_words(int nb, int gs, int rows_wg, int nhp, int uw) {
   return (size_t)nb * (gs * 64 + 4) + (size_t)gs * 16 + (size_t)rows_wg * (gs + 1) * 2 +
-         ((size_t)nb * (nhp + 8) + 1) / 2 + (size_t)nhp * 2;
+         ((size_t)nb * (nhp + 8) + 1) / 2 + (size_t)nhp * 2 + (size_t)32 * uw;
 }
 
-template <int B, int RT>
+// PAIR (b = 1, 2 and an even group count per slice): the 4 lanes of a row load
+// two groups' codes together (8 b bytes a lane, 16 at b = 2, instead of 4 b) and
+// swap one half with the lane 32 away, so that each lane holds one chunk of 32
+// codes of each group (lanes q = 0, 1, 2, 3 chunks 0, 2, 1, 3); x is read in the
+// same chunk order.  Measured on a streaming probe of the gate/up shape: 16-byte
+// loads over 64-byte spans of a row move the bytes in 6.7 us against 9.1 us for
+// 8-byte loads over 32-byte spans.
+template <int B, int RT, bool PAIR>
 __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   using C = CodecPow2<B>;
   constexpr int WQ = B;  // words holding one lane's 32 codes of a group
+  static_assert(!PAIR || B <= 2, "paired loads serve b = 1 and 2");
+  constexpr int MPFG = 4;  // groups of codes in flight per tile
   extern __shared__ uint32_t smem[];
   __shared__ int s_cnt[4][2];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int ns = a.ns, GS = a.gs;
-  const int slice = blockIdx.x % ns, tile_g = blockIdx.x / ns;
+  // workgroups go to the 8 XCDs in turn: the slices of a row block are given
+  // workgroups of one XCD, so that the row block's scale lines are fetched into one
+  // L2 (slices on different XCDs fetched each line once per XCD: 1.8x the bytes)
+  int wl = blockIdx.x;
+  if ((gridDim.x & 7) == 0) wl = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int slice = wl % ns, tile_g = wl / ns;
   const int op = op_of_tile(a, tile_g);
   const GemvOpDev& o = a.ops[op];
   constexpr int rows_wg = 64 * RT;
@@ -135,82 +152,131 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   float* xsum = (float*)(xs + nb * XSTR);               // [GS][16]
   float2* sp = (float2*)(xsum + GS * 16);               // [rows_wg][SSTR]: (s', z - s')
   _Float16* hx = (_Float16*)(sp + rows_wg * SSTR);      // [nb][HSTR]
-  int32_t* hk = (int32_t*)(xs + (mfma_lds_words(nb, GS, rows_wg, a.nhp) - 2 * a.nhp));  // [nhp]
-  int32_t* hs = hk + a.nhp;                                                            // [nhp]
+  const int UW = a.nhp > 0 ? rows_wg * a.r / 32 : 0;  // unit words of the block's rows
+  int32_t* hk = (int32_t*)(xs + (mfma_lds_words(nb, GS, rows_wg, a.nhp, UW) - 2 * a.nhp - 32 * UW));  // [nhp]
+  int32_t* hs = hk + a.nhp;                                                                         // [nhp]
+  uint32_t* hu = (uint32_t*)(hs + a.nhp);  // [32][UW]: one block of hits' unit words
   const int wrow0 = wave * 16 * RT;  // this wave's first row within the block
 
-  // codes of the first MPFG groups of every tile
+  // codes of the first MPFG groups of every tile (PAIR: unit u even and u + 1 hold
+  // groups gl and gl + 1 as loaded until they are exchanged)
+  const int cq = PAIR ? (((q & 1) << 1) | (q >> 1)) : q;  // the chunk of a group this lane holds
   uint32_t cw[MPFG][RT][WQ];
   auto issue = [&](int u, int gl) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int row = row_wg0 + wrow0 + 16 * t + n;
       if (gl < GS && row < o.n_out) {
-        load_words<WQ>(o.res + (size_t)row * rowbytes + (size_t)(g0 + gl) * (16 * B) + q * (4 * B), cw[u][t]);
+        const uint8_t* src = o.res + (size_t)row * rowbytes + (size_t)(g0 + gl) * (16 * B);
+        if constexpr (PAIR) {
+          uint32_t v[2 * WQ];
+          load_words<2 * WQ>(src + q * (8 * B), v);
+#pragma unroll
+          for (int w = 0; w < WQ; ++w) {
+            cw[u][t][w] = v[w];
+            cw[u + 1][t][w] = v[WQ + w];
+          }
+        } else {
+          load_words<WQ>(src + q * (4 * B), cw[u][t]);
+        }
       } else {
 #pragma unroll
-        for (int w = 0; w < WQ; ++w) cw[u][t][w] = 0u;
+        for (int w = 0; w < WQ; ++w) {
+          cw[u][t][w] = 0u;
+          if constexpr (PAIR) cw[u + 1][t][w] = 0u;
+        }
       }
     }
   };
 #pragma unroll
-  for (int u = 0; u < MPFG; ++u) issue(u, u);
-
-  // x slice -> LDS in half-pair order, with its group sums
-  {
-    const int per_row = KS / 8;  // 16-byte loads per batch row (a multiple of 16)
-    const int items = nb * per_row;
-    constexpr int XB = 4;
-    for (int i0 = 0; i0 < items; i0 += 256 * XB) {
-      u32x4 xv[XB];
+  for (int u = 0; u < MPFG; u += PAIR ? 2 : 1) issue(u, u);
+  // PAIR: lanes q < 2 hold chunks 2q, 2q + 1 of group gl, lanes q >= 2 chunks
+  // 2(q-2), 2(q-2) + 1 of group gl + 1; each passes one chunk to the lane 32 away
+  auto exchange = [&](int u) {
 #pragma unroll
-      for (int it = 0; it < XB; ++it) {
-        const int i = i0 + 256 * it + tid;
-        if (i < items) {
-          const int bc = i / per_row, c8 = i - bc * per_row;
-          xv[it] = *(const u32x4*)(a.x + (size_t)(a.batch_off + bc) * K + k0 + 8 * c8);
-        }
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int w = 0; w < WQ; ++w) {
+        const uint32_t give = q < 2 ? cw[u + 1][t][w] : cw[u][t][w];
+        const uint32_t got = (uint32_t)__shfl_xor((int)give, 32, 64);
+        if (q < 2) cw[u + 1][t][w] = got;
+        else cw[u][t][w] = got;
       }
+  };
+
+  // The first batch of every prologue load is requested before any of them is
+  // used: the x slice, the scale words of the block's rows and the selection with
+  // its slots (one round trip instead of four).
+  const int per_row = KS / 8;  // 16-byte x loads per batch row (a multiple of 16)
+  const int items = nb * per_row;
+  constexpr int XB = 4, SB = 8, SU = 2;
+  const int ks = a.k_sel;
+  const int32_t* slots = a.ws_slot + (size_t)op * ks;
+  u32x4 xv[XB];
+  auto load_x = [&](int i0) {
 #pragma unroll
-      for (int it = 0; it < XB; ++it) {
-        const int i = i0 + 256 * it + tid;
-        float part = 0.f;
-        int bc = 0, c8 = 0;
-        if (i < items) {
-          bc = i / per_row;
-          c8 = i - bc * per_row;
-          const uint32_t wds[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
-          uint16_t* xh = (uint16_t*)(xs + bc * XSTR);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kl = 8 * c8 + e, gl = kl >> 7, kg = kl & 127;
-            int j, hi;
-            C::locate(kg & 31, &j, &hi);
-            const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
-            xh[2 * ((gl * 4 + (kg >> 5)) * 16 + j) + hi] = hb;
-            part += (float)__builtin_bit_cast(_Float16, hb);
-          }
-        }
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) part += __shfl_xor(part, off, 16);
-        if (i < items && (c8 & 15) == 0) xsum[(c8 >> 4) * 16 + bc] = part;
+    for (int it = 0; it < XB; ++it) {
+      const int i = i0 + 256 * it + tid;
+      if (i < items) {
+        const int bc = i / per_row, c8 = i - bc * per_row;
+        xv[it] = *(const u32x4*)(a.x + (size_t)(a.batch_off + bc) * K + k0 + 8 * c8);
       }
     }
-    for (int i = tid; i < GS * 16; i += 256)
-      if ((i & 15) >= nb) xsum[i] = 0.f;
+  };
+  uint32_t w[SB];
+  auto load_sz = [&](int i0) {
+#pragma unroll
+    for (int it = 0; it < SB; ++it) {
+      const int i = i0 + 256 * it + tid;
+      const int rl = i / GS, gl = i - rl * GS, row = row_wg0 + rl;
+      w[it] = (i < rows_wg * GS && row < o.n_out) ? o.sz[(size_t)row * ngr + g0 + gl] : 0u;
+    }
+  };
+  int selk[SU], sels[SU];
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const int j = tid + 256 * u;
+    selk[u] = j < ks ? a.ws_sel[j] : INT32_MAX;
+    sels[u] = j < ks ? slots[j] : -1;
   }
+  load_x(0);
+  load_sz(0);
+
+  // x slice -> LDS in half-pair order, with its group sums
+  for (int i0 = 0; i0 < items; i0 += 256 * XB) {
+    if (i0 > 0) load_x(i0);
+#pragma unroll
+    for (int it = 0; it < XB; ++it) {
+      const int i = i0 + 256 * it + tid;
+      float part = 0.f;
+      int bc = 0, c8 = 0;
+      if (i < items) {
+        bc = i / per_row;
+        c8 = i - bc * per_row;
+        const uint32_t wds[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
+        uint16_t* xh = (uint16_t*)(xs + bc * XSTR);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kl = 8 * c8 + e, gl = kl >> 7, kg = kl & 127;
+          int j, hi;
+          C::locate(kg & 31, &j, &hi);
+          const uint16_t hb = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+          xh[2 * ((gl * 4 + (kg >> 5)) * 16 + j) + hi] = hb;
+          part += (float)__builtin_bit_cast(_Float16, hb);
+        }
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) part += __shfl_xor(part, off, 16);
+      if (i < items && (c8 & 15) == 0) xsum[(c8 >> 4) * 16 + bc] = part;
+    }
+  }
+  for (int i = tid; i < GS * 16; i += 256)
+    if ((i & 15) >= nb) xsum[i] = 0.f;
   // scale words of the block's rows in the slice -> (s 2^(r+b), z - s 2^(r+b))
   {
     const float scl = (float)(1u << (a.r + B));
-    constexpr int SB = 8;
     for (int i0 = 0; i0 < rows_wg * GS; i0 += 256 * SB) {
-      uint32_t w[SB];
-#pragma unroll
-      for (int it = 0; it < SB; ++it) {
-        const int i = i0 + 256 * it + tid;
-        const int rl = i / GS, gl = i - rl * GS, row = row_wg0 + rl;
-        w[it] = (i < rows_wg * GS && row < o.n_out) ? o.sz[(size_t)row * ngr + g0 + gl] : 0u;
-      }
+      if (i0 > 0) load_sz(i0);
 #pragma unroll
       for (int it = 0; it < SB; ++it) {
         const int i = i0 + 256 * it + tid;
@@ -223,11 +289,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
     }
   }
   // selected channels inside the slice: positions [h0, h1) of the ascending list
-  const int ks = a.k_sel;
   int h0 = 0, nh = 0;
   if (ks > 0) {
     int c0 = 0, c1 = 0;
-    for (int j = tid; j < ks; j += 256) {
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      c0 += selk[u] < k0;
+      c1 += selk[u] < k0 + KS;
+    }
+    for (int j = tid + 256 * SU; j < ks; j += 256) {
       const int k = a.ws_sel[j];
       c0 += k < k0;
       c1 += k < k0 + KS;
@@ -242,21 +312,54 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       s_cnt[wave][1] = c1;
     }
   }
-  lds_barrier();
+  lds_barrier();  // x staged, counts
   if (ks > 0) {
     h0 = (s_cnt[0][0] + s_cnt[1][0]) + (s_cnt[2][0] + s_cnt[3][0]);
     nh = (s_cnt[0][1] + s_cnt[1][1]) + (s_cnt[2][1] + s_cnt[3][1]) - h0;
     const int nhp = (nh + 31) & ~31;
-    const int32_t* slots = a.ws_slot + (size_t)op * ks;
-    for (int j = tid; j < nhp; j += 256) {
-      const bool valid = j < nh;
-      const int k = valid ? a.ws_sel[h0 + j] : k0;
-      hk[j] = k;
-      hs[j] = valid ? slots[h0 + j] : -1;
+    // the hit list of the slice, with x at each hit read from the staged slice
+    auto stage = [&](int pos, int k, int slot) {
+      hk[pos] = k;
+      hs[pos] = slot;
+      const int kl = k - k0, kg = kl & 127;
+      int j, hi;
+      C::locate(kg & 31, &j, &hi);
+      const int hoff = 2 * (((kl >> 7) * 4 + (kg >> 5)) * 16 + j) + hi;
       for (int bc = 0; bc < nb; ++bc)
-        hx[bc * HSTR + j] = valid ? __builtin_bit_cast(_Float16, a.x[(size_t)(a.batch_off + bc) * K + k])
-                                  : (_Float16)0.f;
+        hx[bc * HSTR + pos] = __builtin_bit_cast(_Float16, ((const uint16_t*)(xs + bc * XSTR))[hoff]);
+    };
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int j = tid + 256 * u;
+      if (j >= h0 && j < h0 + nh) stage(j - h0, selk[u], sels[u]);
     }
+    for (int j = tid + 256 * SU; j < h0 + nh; j += 256)
+      if (j >= h0) stage(j - h0, a.ws_sel[j], slots[j]);
+    for (int p = nh + tid; p < nhp; p += 256) {
+      hk[p] = k0;
+      hs[p] = -1;
+      for (int bc = 0; bc < nb; ++bc) hx[bc * HSTR + p] = (_Float16)0.f;
+    }
+  }
+
+  // the unit words of the first 32 hits (the block's rows only) are requested
+  // now and land during the resident pass
+  const uint32_t* units = (const uint32_t*)o.pool.slots;
+  const int wpu = o.pool.unit_bytes >> 2;
+  const int wbase = row_wg0 / 32 * a.r;  // row_wg0 is a multiple of 64
+  const int n_hw = 32 * UW;
+  auto load_hw = [&](int blk, int idx) -> uint32_t {
+    if (idx >= n_hw) return 0u;
+    const int h = idx / UW, w = idx - h * UW, sl = hs[blk * 32 + h], wi = wbase + w;
+    return (sl >= 0 && wi < wpu) ? units[(size_t)sl * wpu + wi] : 0u;
+  };
+  constexpr int HV = 4;  // prefetched words a thread (blocks of up to 1024 words)
+  uint32_t hpre[HV];
+  const bool pre = ks > 0 && nh > 0 && n_hw <= 256 * HV;
+  if (ks > 0 && nh > 0) lds_barrier();  // hit lists staged
+  if (pre) {
+#pragma unroll
+    for (int v = 0; v < HV; ++v) hpre[v] = load_hw(0, tid + 256 * v);
   }
 
   // resident GEMV
@@ -269,12 +372,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
     for (int u = 0; u < MPFG; ++u) {
       const int gl = gb + u;
+      if constexpr (PAIR) {
+        if ((u & 1) == 0 && gl < GS) exchange(u);
+      }
       if (gl < GS) {
         h8_t ax[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if (arow) {
-            ax[m] = *(const h8_t*)(xs + n * XSTR + (gl * 4 + q) * 16 + 4 * m);
+            ax[m] = *(const h8_t*)(xs + n * XSTR + (gl * 4 + cq) * 16 + 4 * m);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) ax[m][e] = (_Float16)0.f;
@@ -295,18 +401,36 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
           for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc.x, d[v], fmaf(sc.y, X4[v], acc[t][v]));
         }
       }
-      issue(u, gl + MPFG);
+      if constexpr (PAIR) {
+        if (u & 1) issue(u - 1, gl - 1 + MPFG);
+      } else {
+        issue(u, gl + MPFG);
+      }
     }
   }
 
   // refinements of the hit channels in the slice, 32 channels per MFMA
   if (ks > 0 && nh > 0) {
-    lds_barrier();  // hit lists staged
-    const uint32_t* units = (const uint32_t*)o.pool.slots;
-    const int wpu = o.pool.unit_bytes >> 2;
     const int r = a.r;
     const float sdown = 1.f / (float)(1u << (r + B));
     for (int blk = 0; blk * 32 < nh; ++blk) {
+      // this block's unit words -> LDS
+      if (blk > 0) lds_barrier();  // the previous block's words are consumed
+      if (blk == 0 && pre) {
+#pragma unroll
+        for (int v = 0; v < HV; ++v)
+          if (tid + 256 * v < n_hw) hu[tid + 256 * v] = hpre[v];
+      } else {
+        for (int i0 = 0; i0 < n_hw; i0 += 256 * HV) {
+          uint32_t v4[HV];
+#pragma unroll
+          for (int v = 0; v < HV; ++v) v4[v] = load_hw(blk, i0 + tid + 256 * v);
+#pragma unroll
+          for (int v = 0; v < HV; ++v)
+            if (i0 + tid + 256 * v < n_hw) hu[i0 + tid + 256 * v] = v4[v];
+        }
+      }
+      lds_barrier();
       h8_t ah;
       if (arow) {
         ah = *(const h8_t*)(hx + n * HSTR + blk * 32 + 8 * q);
@@ -329,9 +453,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
         for (int e = 0; e < 8; ++e) {
           w0[e] = w1[e] = 0u;
           if (sl[e] >= 0 && row < o.n_out) {
-            const uint32_t* u = units + (size_t)sl[e] * wpu;
+            // a row's bits end inside the block's span, which ends on a word boundary
+            const uint32_t* u = hu + (8 * q + e) * UW - wbase;
             w0[e] = u[wi];
-            if (off + r > 32 && wi + 1 < wpu) w1[e] = u[wi + 1];
+            if (off + r > 32) w1[e] = u[wi + 1];
           }
         }
         u32x4 hb, lb;
@@ -385,21 +510,35 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
              (uint32_t)(ns - 1);
   __syncthreads();
   if (!s_last) return;
-  // last slice of this row block: y = sum of the slices' partials, in slice order
-  for (int i = tid; i < nb * rows_wg; i += 256) {
-    const int bc = i / rows_wg, rl = i - bc * rows_wg, row = row_wg0 + rl;
-    if (row >= o.n_out) continue;
-    const float* pp = a.part + (size_t)bc * a.rows_pad + tile_g * rows_wg + rl;
-    const size_t sstride = (size_t)nb * a.rows_pad;
-    float sum = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 16) {
-      float v[16];
+  // last slice of this row block: y = sum of the slices' partials, in slice order;
+  // 32 partials of the thread's items (at most 16 batch rows x rows_wg / 256 of
+  // them) and consecutive slices are requested at once
+  constexpr int MI = 4 * RT, SS = 32 / MI;
+  const int n_items = nb * rows_wg;
+  const size_t sstride = (size_t)nb * a.rows_pad;
+  float sum[MI];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = s0 + k < ns ? sf_get(pp + (size_t)(s0 + k) * sstride) : 0.f;
+  for (int m = 0; m < MI; ++m) sum[m] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += SS) {
+    float v[SS][MI];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) sum += v[k];
-    }
-    o.y[(size_t)(a.batch_off + bc) * o.n_out + row] = sum;
+    for (int ss = 0; ss < SS; ++ss)
+#pragma unroll
+      for (int m = 0; m < MI; ++m) {
+        const int i = tid + 256 * m, bc = i / rows_wg, rl = i - bc * rows_wg;
+        const bool ok = s0 + ss < ns && i < n_items && row_wg0 + rl < o.n_out;
+        v[ss][m] = ok ? sf_get(a.part + (size_t)bc * a.rows_pad + tile_g * rows_wg + rl + (size_t)(s0 + ss) * sstride)
+                      : 0.f;
+      }
+#pragma unroll
+    for (int ss = 0; ss < SS; ++ss)
+#pragma unroll
+      for (int m = 0; m < MI; ++m) sum[m] += v[ss][m];
+  }
+#pragma unroll
+  for (int m = 0; m < MI; ++m) {
+    const int i = tid + 256 * m, bc = i / rows_wg, rl = i - bc * rows_wg, row = row_wg0 + rl;
+    if (i < n_items && row < o.n_out) o.y[(size_t)(a.batch_off + bc) * o.n_out + row] = sum[m];
   }
 }
 
@@ -452,7 +591,7 @@ struct MfmaPlan {
 // else 128, else 64.  Channel slices: the fewest (a divisor of the group count,
 // at most 16 groups each, LDS within 64 KB) that give 1.5 workgroups per CU.
 // SF_GEMV_MFMA_RT and SF_GEMV_MFMA_SLICES override the choices.
-MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel) {
+MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel, int r) {
   MfmaPlan p;
   const int n_cu = device_cus();
   const int nb = batch < 16 ? batch : 16;
@@ -471,7 +610,7 @@ MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel)
     const int gs = ngr / ns;
     if (gs > 16 || (ns > 1 && tiles > MAX_ROW_BLOCKS)) continue;
     const int nhp = k_sel > 0 ? ((std::min(k_sel, gs * 128) + 31) & ~31) : 0;
-    if (mfma_lds_words(nb, gs, rows_wg, nhp) * 4 > MAX_MFMA_LDS) continue;
+    if (mfma_lds_words(nb, gs, rows_wg, nhp, k_sel > 0 ? rows_wg * r / 32 : 0) * 4 > MAX_MFMA_LDS) continue;
     best = ns;
     if (want_ns > 0 ? ns >= want_ns : (long)tiles * ns >= 3L * n_cu / 2) break;
   }
@@ -485,13 +624,13 @@ MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel)
   return p;
 }
 
-template <int B>
+template <int B, bool PAIR>
 sf_status launch_mfma_rt(GemvArgs& a, int rt, size_t lds, hipStream_t s) {
   const dim3 grid((unsigned)(a.total_tiles * a.ns));
   switch (rt) {
-    case 1: hipLaunchKernelGGL((gemv_mfma_kernel<B, 1>), grid, dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<B, 2>), grid, dim3(256), lds, s, a); break;
-    default: hipLaunchKernelGGL((gemv_mfma_kernel<B, 4>), grid, dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((gemv_mfma_kernel<B, 1, PAIR>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<B, 2, PAIR>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((gemv_mfma_kernel<B, 4, PAIR>), grid, dim3(256), lds, s, a); break;
   }
   SF_LAUNCH_CHECK();
   return SF_OK;
@@ -499,10 +638,10 @@ sf_status launch_mfma_rt(GemvArgs& a, int rt, size_t lds, hipStream_t s) {
 
 sf_status launch_mfma(GemvArgs& a, int b, int rt, size_t lds, hipStream_t s) {
   switch (b) {
-    case 1: return launch_mfma_rt<1>(a, rt, lds, s);
-    case 2: return launch_mfma_rt<2>(a, rt, lds, s);
-    case 4: return launch_mfma_rt<4>(a, rt, lds, s);
-    default: return launch_mfma_rt<8>(a, rt, lds, s);
+    case 1: return a.gs % 2 == 0 ? launch_mfma_rt<1, true>(a, rt, lds, s) : launch_mfma_rt<1, false>(a, rt, lds, s);
+    case 2: return a.gs % 2 == 0 ? launch_mfma_rt<2, true>(a, rt, lds, s) : launch_mfma_rt<2, false>(a, rt, lds, s);
+    case 4: return launch_mfma_rt<4, false>(a, rt, lds, s);
+    default: return launch_mfma_rt<8, false>(a, rt, lds, s);
   }
 }
 
@@ -512,7 +651,7 @@ MfmaPlan plan_for(const sf_gemv_op* ops, int n_ops, int batch, int k_sel) {
   if (!mfma_wanted(ops[0].w.fmt.b, batch)) return p;
   int64_t no[SF_MAX_OPS];
   for (int i = 0; i < n_ops; ++i) no[i] = ops[i].w.n_out;
-  return mfma_plan(no, n_ops, (int)ops[0].w.k_in, batch, k_sel);
+  return mfma_plan(no, n_ops, (int)ops[0].w.k_in, batch, k_sel, ops[0].w.fmt.r);
 }
 
 }  // namespace sfg
@@ -630,7 +769,7 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
     for (int b0 = 0; b0 < batch; b0 += 16) {
       const int nb = batch - b0 < 16 ? batch - b0 : 16;
       a.batch_off = b0;
-      sf_status st = launch_mfma(a, f.b, mp.rt, mfma_lds_words(nb, mp.gs, rows_wg, mp.nhp) * 4, s);
+      sf_status st = launch_mfma(a, f.b, mp.rt, mfma_lds_words(nb, mp.gs, rows_wg, mp.nhp, mp.nhp > 0 ? rows_wg * f.r / 32 : 0) * 4, s);
       if (st != SF_OK) return st;
     }
     return SF_OK;
