@@ -22,8 +22,8 @@
 //            score by a radix select over shared histograms (ties to the lower
 //            token); each chunk writes its part of the ascending selection, looks it
 //            up in the refinement cache and replaces the logits of its hits by
-//            l' = l + scale * s_K * (q . cK_lo); the last chunk records the max
-//            logit after replacement.
+//            l' = l + scale * s_K * (q . cK_lo) and records its max logit after
+//            replacement.
 //   pv     : (refinement only) a workgroup per 512 tokens (256 for b = 8) forms
 //            the final weights e^(l - max), sums weight * V_b on MFMA
 //            and adds weight * s_V * cV_lo for its hits; the last workgroup of the
@@ -52,8 +52,8 @@ constexpr int TPT = CB / SEL_T;  // tokens per select thread
 constexpr int PW = HD + 4;       // partial record: N[HD], max, sum, pad
 constexpr int NBIN = 2048;       // histogram bins (levels: key bits 30..20, 19..10, 9..0)
 constexpr int MAX_CHUNKS = 256;
-constexpr int PV_NR = 8;
-constexpr float SCORE_CUTOFF = -64.f;  // logit below the head's max past which a weight scores 0         // value-sum records per KV head (pv split s adds into record s % PV_NR)
+constexpr int PV_NR = 8;                // value-sum records per KV head (pv split s adds into record s % PV_NR)
+constexpr float SCORE_CUTOFF = -64.f;  // logit below the head's max past which a weight scores 0
 
 __host__ __device__ constexpr int pv_tokens(int b) { return b <= 4 ? 512 : 256; }
 
@@ -82,7 +82,6 @@ struct AttnArgs {
   float* part_c;    // [bh][s2][G][PW]: chunk sums (without refinement)
   float* part_p;    // [bh][PV_NR][G][PW]: value sums of the splits (with refinement)
   float* cmax;      // [bh][s2][G]: chunk max of the replaced logits
-  float* mref;      // [bh][G]: max logit after replacement
   int32_t* sel_ws;  // [bh][KS]: selection
   int32_t* slot_ws; // [bh][KS]: slot of each selected token, -1 = miss
   uint32_t* hist;   // [bh][3][NBIN]
@@ -922,28 +921,11 @@ __global__ __launch_bounds__(SEL_T) void attn_select_kernel(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) s_wm[wave][h][0] = mloc[h];
   __syncthreads();
+  // this chunk's max after replacement; pv takes the max over the chunks
   if (tid < G) {
     float mm = -INFINITY;
     for (int w = 0; w < SEL_T / 64; ++w) mm = fmaxf(mm, s_wm[w][tid][0]);
-    sf_put(a.cmax + ((size_t)bh * s2 + chunk) * G + tid, mm);
-  }
-  sf_drain();
-  __syncthreads();
-  if (tid == 0)
-    lds[36] = sf_add_acq_rel(ctl + 4, 1u) == (uint32_t)(s2 - 1);
-  __syncthreads();
-  if (!lds[36]) return;
-  // last chunk: the max logit after replacement
-  if (tid < G) {
-    float mm = -INFINITY;
-    for (int c0_ = 0; c0_ < s2; c0_ += 8) {
-      float v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = sf_get(a.cmax + ((size_t)bh * s2 + min(c0_ + k, s2 - 1)) * G + tid);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) mm = fmaxf(mm, v[k]);
-    }
-    a.mref[bh * G + tid] = mm;
+    a.cmax[((size_t)bh * s2 + chunk) * G + tid] = mm;
   }
 }
 
@@ -1035,9 +1017,18 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(AttnArgs a) {
     }
   };
   load_split(sp0);
+  // the KV head's max logit after replacement: the max over its chunks' maxima
+  // (every wave forms it, lanes over chunks)
   float mh[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) mh[h] = a.mref[bh * G + h];
+  for (int h = 0; h < G; ++h) mh[h] = -INFINITY;
+  for (int c = lane; c < a.s2; c += 64)
+#pragma unroll
+    for (int h = 0; h < G; ++h) mh[h] = fmaxf(mh[h], a.cmax[((size_t)bh * a.s2 + c) * G + h]);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mh[h] = fmaxf(mh[h], __shfl_xor(mh[h], o, 64));
   // the first batch's logits, scale words and (nested) refinement words: they land
   // while the splits' own sums are formed
   float h_l[G];
@@ -1385,7 +1376,7 @@ size_t attn_layout(int batch, int n_q, int n_kv, int T, int k_sel, size_t off[12
       bh * s2 * G * PW * 4,          // chunk partials
       bh * PV_NR * G * PW * 4,       // value-sum records
       bh * s2 * G * 4,               // chunk max
-      bh * G * 4,                    // max after replacement
+      0,                             // (unused)
       bh * KS * 4,                   // selection
       bh * KS * 4,                   // slots
       bh * 3 * NBIN * 4,             // histograms
@@ -1417,10 +1408,7 @@ sf_status launch_attn(AttnArgs& a, hipStream_t s) {
   // the chunks of one KV head wait for each other: all of them must be resident at
   // once (workgroups are dispatched in order, so the chunks of earlier KV heads
   // finish and make room for later ones)
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)attn_select_kernel<G>, SEL_T, 0) != hipSuccess ||
-      occ < 1)
-    occ = 1;
+  const int occ = std::max(1, sf_occupancy((const void*)attn_select_kernel<G>, SEL_T, 0));
   SF_REQUIRE((long)a.s2 <= (long)occ * attn_device_cus(), SF_EUNSUPPORTED,
              "t_len too long: the selection chunks of one KV head do not fit the device at once");
   if (a.k_sel == 0) {
@@ -1529,7 +1517,6 @@ static sf_status attn_decode(const uint16_t* q_f16, int32_t n_q_heads, const sf_
   a.part_c = (float*)(w + off[2]);
   a.part_p = (float*)(w + off[3]);
   a.cmax = (float*)(w + off[4]);
-  a.mref = (float*)(w + off[5]);
   a.sel_ws = (int32_t*)(w + off[6]);
   a.slot_ws = (int32_t*)(w + off[7]);
   a.hist = (uint32_t*)(w + off[8]);

@@ -102,6 +102,16 @@ def test_uniform_query_selects_first_tokens():
     assert sel[0, 0].tolist() == sel[0, 1].tolist() == [0, 1, 2, 3, 4]
 
 
+@pytest.mark.parametrize("T,k", [(12000, 700), (9000, 4100), (4097, 2)])
+def test_uniform_query_ties_across_chunks(T, k):
+    """q = 0 over several 4096-token chunks: every score is equal, so the first k
+    tokens win, taken across chunk boundaries in token order."""
+    case = Case(53, 1, 2, 4, T)
+    q = np.zeros((1, 8, D), dtype=np.float16)
+    out, sel, _ = _check(case, q, k)
+    assert sel[0, 0].tolist() == sel[0, 1].tolist() == list(range(k))
+
+
 def test_misses_fall_back_to_resident():
     case = Case(51, 1, 2, 4, 500)
     _, sel, hit = _check(case, case.query(10), 10, cache=None)
