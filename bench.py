@@ -52,15 +52,19 @@ SOURCES = ("bit_decode_selective_amd/csrc/gemv_rows.h", "bit_decode_selective_am
 # HBM bytes per call of the dominant call of the default workload, from two rocprofv3
 # --pmc runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain copy
 # of known size (--copy-calibration); reported only while the kernel sources have
-# the hash they were measured on, and only for the call they were measured for.
+# the hash they were measured on, and only for the call and workload (batch, context)
+# they were measured for.
 TRAFFIC = {
     # attn call (with the new token's append), T = 32768, 8 KV heads: split + select + pv,
     # medians over 32 calls each
     # (profiles/decode_step_llama8b_2bit_t32k_hbm_counters.md)
     "call": "attn",
-    "sources_sha256": "bf7a0b8b23883769ecf47fe4509c1e9a74419e3febf68b865b81a6b2f4cb4dd0",
-    "fetch_bytes": 9670323 + 6840928 + 16886716,
-    "write_bytes": 4691712 + 740640 + 1409024,
+    "workload": "llama8b-step",
+    "batch": 1,
+    "context": 32768,
+    "sources_sha256": "1f6e286aebba572ad16391aa406ee28aa6eb6a576bf61a08d62757459de741dc",
+    "fetch_bytes": 9655022 + 6832404 + 16914617,
+    "write_bytes": 4691763 + 738406 + 1409024,
 }
 COPY_CALIBRATION_BYTES = 256 << 20
 
@@ -451,7 +455,9 @@ def report(model, calls, T, B, args, ms, unref_ms, us, workload, extra_config):
     sb = step_bytes(model, calls, T, True)
     gbps = sb / (ms * 1e-3) / 1e9
     traffic = None
-    if TRAFFIC is not None and TRAFFIC.get("call") == dom and TRAFFIC.get("sources_sha256") == sources_hash():
+    if (TRAFFIC is not None and TRAFFIC.get("call") == dom and TRAFFIC.get("workload") == args.workload
+            and TRAFFIC.get("batch") == B and TRAFFIC.get("context") == T
+            and TRAFFIC.get("sources_sha256") == sources_hash()):
         traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     res = {
         "metric": "refined decode tokens/s + achieved HBM GB/s (% peak), Llama-8B-shape 2-bit",
