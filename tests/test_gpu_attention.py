@@ -179,6 +179,28 @@ def test_full_size_128k():
         assert_close(out[:, g * G:(g + 1) * G], ref, what=f"128K kv head {g}")
 
 
+def test_max_context_1m():
+    """The largest context the call accepts, T = 1,048,576 (256 selection chunks, one
+    per CU, all resident together): one KV head, top 2% (20,972 tokens), exact
+    selection and the output against the oracle."""
+    T, n_kv, G = 1 << 20, 1, 4
+    K, V = inputs.kv(6, 0, 1, n_kv, T, D)
+    kv = binding.QuantKV.from_host(K, V, 2, 2)
+    ks = selection.k_select(2, T)
+    qk = o_attn.quantize_kv(K, 2, 2)
+    qv = o_attn.quantize_kv(V, 2, 2)
+    del K, V
+    k_res = nested.dequant_resident(qk).reshape(1, n_kv, T, D)
+    q, _ = separated_query(6, 0, 1, n_kv, G, D, lambda bi, g: k_res[bi, g], SCALE, ks)
+    cache = binding.RefineCache([kv.resident_pool_desc()])
+    out, sel, hit = binding.refined_attention(q, kv, SCALE, ks, cache=cache)
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    assert sel[0, 0].tolist() == selection.top_k(o_attn.token_scores(q[0], k_res[0, 0], SCALE), ks)
+    ref, _ = o_attn.refined_attention(q, qk, qv, (1, n_kv, T, D), SCALE, ks)
+    assert_close(out, ref, what="attention T=1048576")
+
+
 def test_refinement_that_removes_the_dominant_token():
     """KV head 0's token 0 holds nearly all of the softmax mass at resident precision
     and loses it once refined (its refinement bits sit where the query is negative),
