@@ -128,14 +128,26 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   extern __shared__ uint32_t smem[];
   __shared__ int s_cnt[4][2];
   __shared__ int s_last;
+  __shared__ int s_pub;
+  // with sel_wg, workgroup 0 selects the channels over all batch rows and publishes
+  // them (as the batch-1/2 split kernel's selecting workgroup); the others take the
+  // selection after their resident pass
+  if (a.sel_wg && blockIdx.x == 0) {
+    __builtin_amdgcn_s_setprio(3);
+    split_select_and_publish<false>(a, smem);
+    __builtin_amdgcn_s_setprio(0);
+    split_retire(a);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, q = lane >> 4;
   const int ns = a.ns, GS = a.gs;
   // workgroups go to the 8 XCDs in turn: the slices of a row block are given
   // workgroups of one XCD, so that the row block's scale lines are fetched into one
   // L2 (slices on different XCDs fetched each line once per XCD: 1.8x the bytes)
-  int wl = blockIdx.x;
-  if ((gridDim.x & 7) == 0) wl = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int wid = blockIdx.x - a.sel_wg, nwg = gridDim.x - a.sel_wg;  // this reader's index
+  int wl = wid;
+  if ((nwg & 7) == 0) wl = (wid & 7) * (nwg >> 3) + (wid >> 3);
   const int slice = wl % ns, tile_g = wl / ns;
   const int op = op_of_tile(a, tile_g);
   const GemvOpDev& o = a.ops[op];
@@ -232,12 +244,21 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       w[it] = (i < rows_wg * GS && row < o.n_out) ? o.sz[(size_t)row * ngr + g0 + gl] : 0u;
     }
   };
+  // the selection and its slots: from the selection launch (complete before this
+  // one), or published by workgroup 0 (read after the resident pass)
+  const bool pub = a.sel_wg != 0;
+  const uint32_t* hc = a.ctl + offsetof(WsControl, hit) / 4 + (wid % SPLIT_COPIES) * split_copy_words(ks, a.n_ops);
+  const bool resident = o.pool.resident != 0;
+  auto sel_k = [&](int j) { return pub ? read_published(hc + j, a) : a.ws_sel[j]; };
+  auto sel_slot = [&](int j, int k) {
+    return pub ? (resident ? k : read_published(hc + ks * (1 + op) + j, a)) : slots[j];
+  };
   int selk[SU], sels[SU];
 #pragma unroll
   for (int u = 0; u < SU; ++u) {
     const int j = tid + 256 * u;
-    selk[u] = j < ks ? a.ws_sel[j] : INT32_MAX;
-    sels[u] = j < ks ? slots[j] : -1;
+    selk[u] = !pub && j < ks ? a.ws_sel[j] : INT32_MAX;
+    sels[u] = !pub && j < ks ? slots[j] : -1;
   }
   load_x(0);
   load_sz(0);
@@ -288,9 +309,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       }
     }
   }
-  // selected channels inside the slice: positions [h0, h1) of the ascending list
+  // selected channels inside the slice: positions [h0, h1) of the ascending list,
+  // then the slice's hit list (channel, slot, x at each batch row) from the staged x
   int h0 = 0, nh = 0;
-  if (ks > 0) {
+  auto find_hits = [&]() {
     int c0 = 0, c1 = 0;
 #pragma unroll
     for (int u = 0; u < SU; ++u) {
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       c1 += selk[u] < k0 + KS;
     }
     for (int j = tid + 256 * SU; j < ks; j += 256) {
-      const int k = a.ws_sel[j];
+      const int k = sel_k(j);
       c0 += k < k0;
       c1 += k < k0 + KS;
     }
@@ -311,13 +333,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       s_cnt[wave][0] = c0;
       s_cnt[wave][1] = c1;
     }
-  }
-  lds_barrier();  // x staged, counts
-  if (ks > 0) {
+    lds_barrier();  // (x staged,) counts
     h0 = (s_cnt[0][0] + s_cnt[1][0]) + (s_cnt[2][0] + s_cnt[3][0]);
     nh = (s_cnt[0][1] + s_cnt[1][1]) + (s_cnt[2][1] + s_cnt[3][1]) - h0;
     const int nhp = (nh + 31) & ~31;
-    // the hit list of the slice, with x at each hit read from the staged slice
     auto stage = [&](int pos, int k, int slot) {
       hk[pos] = k;
       hs[pos] = slot;
@@ -334,13 +353,20 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
       if (j >= h0 && j < h0 + nh) stage(j - h0, selk[u], sels[u]);
     }
     for (int j = tid + 256 * SU; j < h0 + nh; j += 256)
-      if (j >= h0) stage(j - h0, a.ws_sel[j], slots[j]);
+      if (j >= h0) {
+        const int k = sel_k(j);
+        stage(j - h0, k, sel_slot(j, k));
+      }
     for (int p = nh + tid; p < nhp; p += 256) {
       hk[p] = k0;
       hs[p] = -1;
       for (int bc = 0; bc < nb; ++bc) hx[bc * HSTR + p] = (_Float16)0.f;
     }
-  }
+  };
+  if (ks > 0 && !pub)
+    find_hits();
+  else
+    lds_barrier();  // x staged
 
   // the unit words of the first 32 hits (the block's rows only) are requested
   // now and land during the resident pass
@@ -355,8 +381,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
   };
   constexpr int HV = 4;  // prefetched words a thread (blocks of up to 1024 words)
   uint32_t hpre[HV];
-  const bool pre = ks > 0 && nh > 0 && n_hw <= 256 * HV;
-  if (ks > 0 && nh > 0) lds_barrier();  // hit lists staged
+  const bool pre = !pub && ks > 0 && nh > 0 && n_hw <= 256 * HV;
+  if (!pub && ks > 0 && nh > 0) lds_barrier();  // hit lists staged
   if (pre) {
 #pragma unroll
     for (int v = 0; v < HV; ++v) hpre[v] = load_hw(0, tid + 256 * v);
@@ -407,6 +433,28 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(GemvArgs a) {
         issue(u, gl + MPFG);
       }
     }
+  }
+
+  // the published selection, after the resident pass: wave 0 waits for its flag group,
+  // every thread reads its words, the hit list is staged, and once every read has
+  // completed the workgroup counts itself for workgroup 0
+  if (pub && ks > 0) {
+    if (wave == 0) {
+      const bool ok0 = wait_published(a, wid & 63);
+      if (lane == 0) s_pub = ok0 ? 1 : 0;
+    }
+    lds_barrier();
+    if (s_pub) {
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int j = tid + 256 * u;
+        selk[u] = j < ks ? sel_k(j) : INT32_MAX;
+        sels[u] = j < ks ? sel_slot(j, selk[u]) : -1;
+      }
+      find_hits();
+      lds_barrier();  // hit lists staged
+    }
+    if (tid == 0) count_reader(a, wid & 63);
   }
 
   // refinements of the hit channels in the slice, 32 channels per MFMA
@@ -626,7 +674,7 @@ MfmaPlan mfma_plan(const int64_t* n_out, int n_ops, int K, int batch, int k_sel,
 
 template <int B, bool PAIR>
 sf_status launch_mfma_rt(GemvArgs& a, int rt, size_t lds, hipStream_t s) {
-  const dim3 grid((unsigned)(a.total_tiles * a.ns));
+  const dim3 grid((unsigned)(a.total_tiles * a.ns + a.sel_wg));
   switch (rt) {
     case 1: hipLaunchKernelGGL((gemv_mfma_kernel<B, 1, PAIR>), grid, dim3(256), lds, s, a); break;
     case 2: hipLaunchKernelGGL((gemv_mfma_kernel<B, 2, PAIR>), grid, dim3(256), lds, s, a); break;
@@ -755,7 +803,12 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
                                          : fused_lds_bytes((int)K, cpc, 2, k_sel, rpw);
   const int max_nb = lds2 <= 64 * 1024 ? 2 : 1;
   const bool one_launch = !mfma && batch <= max_nb;
-  if (k_sel > 0 && !one_launch) {
+  // the batched kernel selects in its own workgroup 0 when one launch takes every
+  // batch row and the published copies fit the control block; else a selection
+  // launch comes first
+  const bool mfma_sw = mfma && !given && batch <= 16 &&
+                       (size_t)SPLIT_COPIES * split_copy_words(k_sel, n_ops) <= sizeof(((WsControl*)nullptr)->hit) / 4;
+  if (k_sel > 0 && !one_launch && !mfma_sw) {
     hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(256), select_lds_bytes((int)K, k_sel), s, a);
     SF_LAUNCH_CHECK();
   }
@@ -766,10 +819,16 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
     a.rows_pad = tiles * rows_wg;
     a.part = (float*)(ws_base + o_part);
     a.ctr = (uint32_t*)(ws_base + offsetof(WsControl, row_ctr));
+    a.ctl = (uint32_t*)ws_base;
+    a.sel_wg = mfma_sw ? 1 : 0;
+    a.report = mfma_sw ? 1 : 0;
+    a.n_readers = tiles * mp.ns;
     for (int b0 = 0; b0 < batch; b0 += 16) {
       const int nb = batch - b0 < 16 ? batch - b0 : 16;
       a.batch_off = b0;
-      sf_status st = launch_mfma(a, f.b, mp.rt, mfma_lds_words(nb, mp.gs, rows_wg, mp.nhp, mp.nhp > 0 ? rows_wg * f.r / 32 : 0) * 4, s);
+      size_t lds = mfma_lds_words(nb, mp.gs, rows_wg, mp.nhp, mp.nhp > 0 ? rows_wg * f.r / 32 : 0) * 4;
+      if (mfma_sw) lds = std::max(lds, select_lds_bytes((int)K, k_sel));
+      sf_status st = launch_mfma(a, f.b, mp.rt, lds, s);
       if (st != SF_OK) return st;
     }
     return SF_OK;
@@ -780,6 +839,7 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
   // the selecting workgroup only where the selection is computed in this launch
   a.sel_wg = (kind == KIND_SPLIT && k_sel > 0 && a.sel_in == nullptr && k_sel < K) ? 1 : 0;
   a.ctl = (uint32_t*)ws_base;
+  a.n_readers = tiles;
   for (int b0 = 0; b0 < batch; b0 += max_nb) {
     const int nb = (batch - b0) >= max_nb ? max_nb : 1;
     a.batch_off = b0;

@@ -52,8 +52,10 @@ struct GemvArgs {
   float* part;
   uint32_t* ctr;
   // overlapped kernel: workgroup 0 selects (sel_wg = 1) and publishes through the
-  // workspace control words ctl (WsControl: sel_state, done, timeout)
+  // workspace control words ctl (WsControl: sel_state, done, timeout); n_readers:
+  // the workgroups that read the published words (every other workgroup)
   int32_t sel_wg;
+  int32_t n_readers;
   uint32_t* ctl;
 };
 
@@ -495,7 +497,7 @@ __device__ __forceinline__ void split_retire(const GemvArgs& a) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     uint32_t* ctr = a.ctl + offsetof(WsControl, rd_ctr) / 4 + 32 * tid;
-    const uint32_t tiles = (uint32_t)a.total_tiles;
+    const uint32_t tiles = (uint32_t)a.n_readers;
     const uint32_t want = (uint32_t)tid < tiles ? (tiles - (uint32_t)tid + 63u) / 64u : 0u;
     const uint32_t lim = sf_spin_limit(a.ctl + 2);
     for (uint32_t it = 0;; ++it) {
@@ -697,10 +699,11 @@ __device__ __forceinline__ int32_t* split_select(const GemvArgs& a, uint32_t* sm
 
 // Workgroup 0: selection into LDS, then the lookups, the published copy in the
 // workspace and the reports.
+template <bool ROWS = false>
 __device__ __forceinline__ void split_select_and_publish(const GemvArgs& a, uint32_t* smem) {
   const int tid = threadIdx.x;
   const int ks = a.k_sel;
-  const int32_t* l_sel = split_select(a, smem);
+  const int32_t* l_sel = split_select<ROWS>(a, smem);
   int* sc = (int*)(l_sel + ((ks + 3) & ~3) + 4 * 256 + 4 * 128);  // [16] (after the histograms)
   // the published words first: the channels and, per matrix without resident
   // units, the slots, in SPLIT_COPIES copies
