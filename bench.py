@@ -46,9 +46,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 HD = 128
-SOURCES = ("bit_decode_selective_amd/csrc/gemv_rows.h", "bit_decode_selective_amd/csrc/gemv.hip",
-           "bit_decode_selective_amd/csrc/attention.hip", "bit_decode_selective_amd/csrc/glue.hip",
-           "bit_decode_selective_amd/csrc/sf_internal.h", "bit_decode_selective_amd/csrc/select_core.h")
+# kernel sources of the attention call (its kernels and the headers they include)
+ATTN_SOURCES = ("bit_decode_selective_amd/csrc/attention.hip", "bit_decode_selective_amd/csrc/group_quant.h",
+                "bit_decode_selective_amd/csrc/sf_internal.h")
 # HBM bytes per call of the dominant call of the default workload, from two rocprofv3
 # --pmc runs (FETCH_SIZE, then WRITE_SIZE) scaled by the same counters on a plain copy
 # of known size (--copy-calibration); reported only while the kernel sources have
@@ -62,7 +62,7 @@ TRAFFIC = {
     "workload": "llama8b-step",
     "batch": 1,
     "context": 32768,
-    "sources_sha256": "1f6e286aebba572ad16391aa406ee28aa6eb6a576bf61a08d62757459de741dc",
+    "sources_sha256": "1409320ba4786b1569199114f7d3b8b6eb576b7237270215564f0b370c3b8ae3",
     "fetch_bytes": 9655022 + 6832404 + 16914617,
     "write_bytes": 4691763 + 738406 + 1409024,
 }
@@ -73,9 +73,9 @@ def k_select(percent, n):
     return (percent * n + 99) // 100
 
 
-def sources_hash():
+def sources_hash(files=ATTN_SOURCES):
     h = hashlib.sha256()
-    for s in SOURCES:
+    for s in files:
         with open(os.path.join(ROOT, s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
