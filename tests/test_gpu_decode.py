@@ -308,6 +308,13 @@ def test_decode_steps(spec, batch, producer_select):
 
 
 @pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
+def test_decode_steps_batch8(spec):
+    """Batch 8: every GEMV on the batched MFMA kernel, its channels selected by the
+    launch's own first workgroup over all eight rows."""
+    _run_steps(spec, 8, 40, 2, 78)
+
+
+@pytest.mark.parametrize("spec", [TINY_LLAMA, TINY_QWEN], ids=lambda s: s.name)
 @pytest.mark.parametrize("producer_select", [False, True], ids=["gemv-selects", "producer-selects"])
 def test_decode_steps_lru_pools(spec, producer_select):
     """Small decoders with LRU pools holding 25% of every tensor's units over 8 steps."""
@@ -351,6 +358,13 @@ def test_decode_full_width_qwen3_pools25():
     with LRU replacement and deterministic fills, 8 steps; every operation's output
     checked on the first and last step, selections and hit sets on all."""
     _run_steps(WIDE_QWEN, 1, 192, 8, 90, pool_frac=0.25, output_steps={0, 7})
+
+
+def test_decode_full_width_qwen3_batch8_pools25():
+    """The Qwen3-8B workload's step at full width and batch 8 (the batched MFMA GEMVs,
+    64 token selections per layer), pools of 25%, 4 steps; outputs checked on the first
+    and last step, selections and hit sets on all."""
+    _run_steps(WIDE_QWEN, 8, 160, 4, 92, pool_frac=0.25, output_steps={0, 3})
 
 
 def test_decode_full_width_llama_w3r1_pools10():
