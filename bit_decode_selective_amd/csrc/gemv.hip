@@ -804,9 +804,9 @@ static sf_status refined_gemv_on(const sf_gemv_op* ops, int32_t n_ops, const uin
   const int max_nb = lds2 <= 64 * 1024 ? 2 : 1;
   const bool one_launch = !mfma && batch <= max_nb;
   // the batched kernel selects in its own workgroup 0 when one launch takes every
-  // batch row and the published copies fit the control block; else a selection
+  // batch row and the selector's LDS and the published copies fit; else a selection
   // launch comes first
-  const bool mfma_sw = mfma && !given && batch <= 16 &&
+  const bool mfma_sw = mfma && !given && batch <= 16 && select_lds_bytes((int)K, k_sel) <= MAX_MFMA_LDS &&
                        (size_t)SPLIT_COPIES * split_copy_words(k_sel, n_ops) <= sizeof(((WsControl*)nullptr)->hit) / 4;
   if (k_sel > 0 && !one_launch && !mfma_sw) {
     hipLaunchKernelGGL(gemv_select_kernel, dim3(1), dim3(256), select_lds_bytes((int)K, k_sel), s, a);

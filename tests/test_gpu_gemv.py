@@ -204,6 +204,18 @@ def test_batched_mfma_fused_ragged_ops(slices, monkeypatch):
         assert_close(y, o_gemv.refined_gemv(q, x, []))
 
 
+def test_batched_mfma_wide_input_takes_the_selection_launch():
+    """k_in = 32768 at batch 4: the selector's LDS would not fit the batched launch,
+    so the channels come from the selection launch before it (984 of 32768)."""
+    W, qw, q = _setup(19, 256, 32768, 2, 2)
+    x = inputs.activation(19, 0, 0, 0, 4, 32768)
+    ks = selection.k_select(3, 32768)
+    (y,), sel, _ = _run([qw], x, ks)
+    want = selection.select_channels(x, ks)
+    assert sel == want
+    assert_close(y, o_gemv.refined_gemv(q, x, want))
+
+
 def test_batched_mfma_repeated_calls():
     """Slice counters return to zero after every call: alternate shapes and batch
     sizes on one workspace."""
